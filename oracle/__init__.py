@@ -1,0 +1,178 @@
+"""CPU oracle for the shortlisted draft head (TEST INFRASTRUCTURE ONLY).
+
+Thin ctypes wrappers over ``dynaspec_oracle.c`` (plain single-threaded C,
+fp64 accumulation).  Only the tests, the smoke check and the benchmark's CPU
+baseline import this package; the HIP library never does.
+
+Every wrapper takes and returns numpy arrays with the layouts of the library's
+C-ABI: bf16 tensors are uint16 bit patterns, shortlist offsets are absolute
+(``sl_off[0]`` is the base), verification rows are position-major.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dynaspec_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OK, EINVAL, ECAPACITY = 0, 1, 4
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, one thread)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall",
+                               "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = C.CDLL(_LIB)
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return 1
+    if a.dtype == np.float32:
+        return 0
+    raise TypeError("expected float32 or bf16 bits (uint16), got %s" % a.dtype)
+
+
+def _c(a, dt=None):
+    return None if a is None else np.ascontiguousarray(a, dtype=dt or a.dtype)
+
+
+def router_score(h, W1, b1, W2, b2, act: int) -> np.ndarray:
+    """scores[n][M]; h[n][d], W1[r][d], W2[M][r] (fp32 or bf16 bits)."""
+    lib = _load()
+    h, W1, W2 = _c(h), _c(W1), _c(W2)
+    b1, b2 = _c(b1), _c(b2)
+    n, d = h.shape
+    r, M = W1.shape[0], W2.shape[0]
+    dt = _dtype_code(W1)
+    for a in (h, W2) + tuple(x for x in (b1, b2) if x is not None):
+        assert _dtype_code(a) == dt
+    out = np.empty((n, M), np.float32)
+    lib.oracle_router_score(C.c_int(dt), C.c_int(n), C.c_int(d), C.c_int(r), C.c_int(M),
+                            C.c_int(act), _p(h), C.c_int64(d), _p(W1), _p(b1), _p(W2), _p(b2),
+                            _p(out))
+    return out
+
+
+def select_clusters(scores, cluster_size, kind: int, budget):
+    """Returns (sel[n][M] ranked ids padded with -1, n_sel[n], sl_len[n])."""
+    lib = _load()
+    scores = _c(scores, np.float32)
+    n, M = scores.shape
+    cs, bud = _c(cluster_size, np.int32), _c(budget, np.int32).reshape(n)
+    sel = np.empty((n, M), np.int32)
+    n_sel = np.empty(n, np.int32)
+    sl_len = np.empty(n, np.int32)
+    lib.oracle_select_clusters(C.c_int(n), C.c_int(M), _p(scores), _p(cs), C.c_int(kind),
+                               _p(bud), _p(sel), _p(n_sel), _p(sl_len))
+    return sel, n_sel, sl_len
+
+
+def build_shortlist(sel, n_sel, cluster_of, capacity: int | None = None, base: int = 0):
+    """Returns (status, sl_off[n+1] int64, sl_ids[capacity] int32)."""
+    lib = _load()
+    sel = _c(sel, np.int32)
+    n, M = sel.shape
+    n_sel, cluster_of = _c(n_sel, np.int32), _c(cluster_of, np.int32)
+    V = cluster_of.shape[0]
+    if capacity is None:
+        capacity = base + n * V
+    sl_off = np.zeros(n + 1, np.int64)
+    sl_off[0] = base
+    sl_ids = np.full(max(capacity, 1), -1, np.int32)
+    st = lib.oracle_build_shortlist(C.c_int(n), C.c_int(M), C.c_int(V), _p(sel), _p(n_sel),
+                                    _p(cluster_of), C.c_int64(capacity), _p(sl_off), _p(sl_ids))
+    return int(st), sl_off, sl_ids[:capacity]
+
+
+def gathered_lm_head(W, h, sl_off, sl_ids):
+    """h[G][m][d]; returns the logits buffer (length m*sl_off[G]) in the
+    library's layout (group g at m*sl_off[g], [m][len_g])."""
+    lib = _load()
+    W, h = _c(W), _c(h)
+    V, d = W.shape
+    G, m, _ = h.shape
+    sl_off, sl_ids = _c(sl_off, np.int64), _c(sl_ids, np.int32)
+    out = np.full(int(m * sl_off[G]), np.nan, np.float32)
+    lib.oracle_gathered_lm_head(C.c_int(_dtype_code(W)), C.c_int(V), C.c_int(d), _p(W),
+                                C.c_int(G), C.c_int(m), _p(h), C.c_int64(m * d),
+                                _p(sl_off), _p(sl_ids), _p(out))
+    return out
+
+
+def dense_lm_head(W, h):
+    """logits[n][V] for h[n][d] over every row of W."""
+    lib = _load()
+    W, h = _c(W), _c(h)
+    V, d = W.shape
+    n = h.shape[0]
+    out = np.empty((n, V), np.float32)
+    lib.oracle_dense_lm_head(C.c_int(_dtype_code(W)), C.c_int(V), C.c_int(d), _p(W), C.c_int(n),
+                             _p(h), C.c_int64(d), _p(out))
+    return out
+
+
+def shortlist_sample(sl_off, sl_ids, logits, u, m: int = 1, temperature: float = 1.0):
+    """Returns (token[G*m], q (same layout as logits), tie[G*m] bool)."""
+    lib = _load()
+    sl_off, sl_ids = _c(sl_off, np.int64), _c(sl_ids, np.int32)
+    logits, u = _c(logits, np.float32), _c(u, np.float32).reshape(-1)
+    G = sl_off.shape[0] - 1
+    assert u.shape[0] == G * m
+    token = np.empty(G * m, np.int32)
+    q = np.full(logits.shape[0], np.nan, np.float32)
+    tie = np.zeros(G * m, np.uint8)
+    lib.oracle_shortlist_sample(C.c_int(G), C.c_int(m), _p(sl_off), _p(sl_ids), _p(logits),
+                                C.c_float(temperature), _p(u), _p(token), _p(q), _p(tie))
+    return token, q, tie.astype(bool)
+
+
+def target_softmax(logits):
+    lib = _load()
+    logits = _c(logits, np.float32)
+    V = logits.shape[-1]
+    rows = logits.size // V
+    p = np.empty_like(logits)
+    lib.oracle_target_softmax(C.c_int(rows), C.c_int(V), _p(logits), _p(p))
+    return p
+
+
+def verify_reject(draft, sl_off, sl_ids, q, p, u_acc, u_fin):
+    """draft[T][B], sl_off[T*B+1] (row t*B+b), p[B][T+1][V], u_acc[T][B],
+    u_fin[B].  Returns (n_acc[B], out[B][T+1], tie[B] bool)."""
+    lib = _load()
+    draft = _c(draft, np.int32)
+    T, B = draft.shape
+    p = _c(p, np.float32)
+    V = p.shape[-1]
+    assert p.shape == (B, T + 1, V)
+    sl_off, sl_ids, q = _c(sl_off, np.int64), _c(sl_ids, np.int32), _c(q, np.float32)
+    u_acc, u_fin = _c(u_acc, np.float32).reshape(T, B), _c(u_fin, np.float32).reshape(B)
+    n_acc = np.empty(B, np.int32)
+    out = np.empty((B, T + 1), np.int32)
+    tie = np.zeros(B, np.uint8)
+    lib.oracle_verify_reject(C.c_int(B), C.c_int(T), C.c_int(V), _p(draft), _p(sl_off),
+                             _p(sl_ids), _p(q), _p(p), _p(u_acc), _p(u_fin), _p(n_acc),
+                             _p(out), _p(tie))
+    return n_acc, out, tie.astype(bool)

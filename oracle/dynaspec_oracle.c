@@ -1,0 +1,453 @@
+/*
+ * CPU oracle for the DynaSpec draft-side shortlisted LM head.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, single-threaded
+ * definition that the HIP library is checked against.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark load it; the
+ * product path never does, and the two share no code.
+ *
+ * Sources (the pages are cited by title and section):
+ *   [A]  "DynaSpec: Context-aware Dynamic Speculative Sampling for
+ *        Large-Vocabulary Language Models", arXiv abstract page, Abstract.
+ *   [S]  papers.lunadong.com summary of DynaSpec: sections "Problem
+ *        Definition", "Pipeline Flow", "System Modules", "Novel
+ *        Architectural Elements", "Modeling / Key Hyperparameters",
+ *        "Comparison to Prior Work".
+ *   Speculative sampling itself (accept with min(1, p/q), resample from the
+ *   normalised residual max(0, p - q), bonus token from the last target
+ *   position) is the textbook algorithm of the two speculative-decoding
+ *   works that [A] builds on ("Fast Inference from Transformers via
+ *   Speculative Decoding"; "Accelerating Large Language Model Decoding with
+ *   Speculative Sampling").
+ *
+ * Arithmetic: bf16 inputs are widened to fp32 exactly and then to double;
+ * every sum runs in double, in ascending index order; exp is libm's double
+ * exp.  Results that the pages store as fp32 are rounded once at the end.
+ *
+ * Index conventions (shared with the library's C-ABI, restated here):
+ *   - shortlist offsets sl_off are ABSOLUTE element offsets into sl_ids;
+ *     sl_off[0] is an input (the base), build writes sl_off[1..n].
+ *   - logits/q for group g, row i, entry j live at m*sl_off[g] + i*len_g + j.
+ *   - verification rows are position-major: row = t*B + b.
+ *
+ * Parity status: every function is pinned by tests that do not retype its
+ * formula (library GEMV in float64, brute force, closed forms, quadrature,
+ * exact enumeration); see the oracle test module.  The pages print no
+ * numeric example for any step.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL 1
+#define OR_ECAPACITY 4
+
+#define TIE_REL 1e-12 /* a CDF boundary closer than this (relative) is a tie */
+
+static double bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* element idx of an array that holds fp32 (dtype 0) or bf16 bits (dtype 1) */
+static double load_elem(int dtype, const void *base, int64_t idx)
+{
+    if (dtype == 1)
+        return bf16_to_double(((const uint16_t *)base)[idx]);
+    return (double)((const float *)base)[idx];
+}
+
+static double activation(int act, double x)
+{
+    if (act == 0)
+        return x > 0.0 ? x : 0.0;          /* ReLU */
+    return x / (1.0 + exp(-x));             /* SiLU */
+}
+
+/*
+ * Router / meta-classifier [S "System Modules: Router"; "Key
+ * Hyperparameters: 2-layer MLP with ReLU"; "Problem Definition": input is the
+ * draft hidden state H_{t-1}].  Two-layer MLP, one score per cluster:
+ *   z_i = act(sum_k W1[i][k] h[k] + b1[i]),  s_c = sum_i W2[c][i] z_i + b2[c].
+ * h row `row` starts at h + row*ldh (elements).  b1/b2 may be NULL.
+ */
+void oracle_router_score(int dtype, int n, int d, int r, int M, int act,
+                         const void *h, int64_t ldh, const void *W1,
+                         const void *b1, const void *W2, const void *b2,
+                         float *scores)
+{
+    double *z = (double *)malloc(sizeof(double) * (size_t)r);
+    for (int row = 0; row < n; ++row) {
+        for (int i = 0; i < r; ++i) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k)
+                acc += load_elem(dtype, W1, (int64_t)i * d + k) *
+                       load_elem(dtype, h, (int64_t)row * ldh + k);
+            if (b1)
+                acc += load_elem(dtype, b1, i);
+            z[i] = activation(act, acc);
+        }
+        for (int c = 0; c < M; ++c) {
+            double acc = 0.0;
+            for (int i = 0; i < r; ++i)
+                acc += load_elem(dtype, W2, (int64_t)c * r + i) * z[i];
+            if (b2)
+                acc += load_elem(dtype, b2, c);
+            scores[(int64_t)row * M + c] = (float)acc;
+        }
+    }
+    free(z);
+}
+
+/* ranking used by selection: score descending, then cluster id ascending */
+static const float *g_rank_scores;
+static int rank_cmp(const void *a, const void *b)
+{
+    int ia = *(const int *)a, ib = *(const int *)b;
+    float sa = g_rank_scores[ia], sb = g_rank_scores[ib];
+    if (sa > sb)
+        return -1;
+    if (sa < sb)
+        return 1;
+    return ia < ib ? -1 : (ia > ib ? 1 : 0);
+}
+
+/*
+ * Top-cluster selection under a position-aware budget [A "the union of the
+ * top-selected clusters"; S "Key Novelty": position-aware budget, larger
+ * shortlists for early tokens; "Key Hyperparameters": k_c(t) decays from k_0
+ * to k_1].  Clusters are ranked by (score desc, id asc).
+ *   kind 0 (cluster budget): the first k = clamp(budget, 1, M) clusters.
+ *   kind 1 (token budget):   the shortest prefix whose total size reaches the
+ *                            budget (every cluster whose exclusive prefix size
+ *                            is below it); budget <= 0 counts as 1.
+ * Outputs: sel[row][0..n_sel) ranked ids, n_sel[row], sl_len[row] = sum of
+ * the selected sizes.  NaN scores are invalid input.
+ */
+void oracle_select_clusters(int n, int M, const float *scores,
+                            const int32_t *cluster_size, int kind,
+                            const int32_t *budget, int32_t *sel,
+                            int32_t *n_sel, int32_t *sl_len)
+{
+    int *order = (int *)malloc(sizeof(int) * (size_t)M);
+    for (int row = 0; row < n; ++row) {
+        const float *s = scores + (int64_t)row * M;
+        for (int c = 0; c < M; ++c)
+            order[c] = c;
+        g_rank_scores = s;
+        qsort(order, (size_t)M, sizeof(int), rank_cmp);
+        int take = 0;
+        int64_t total = 0;
+        if (kind == 0) {
+            int k = budget[row];
+            if (k < 1)
+                k = 1;
+            if (k > M)
+                k = M;
+            for (take = 0; take < k; ++take)
+                total += cluster_size[order[take]];
+        } else {
+            int64_t b = budget[row] < 1 ? 1 : budget[row];
+            while (take < M && total < b)
+                total += cluster_size[order[take++]];
+        }
+        for (int j = 0; j < M; ++j)
+            sel[(int64_t)row * M + j] = j < take ? order[j] : -1;
+        n_sel[row] = take;
+        sl_len[row] = (int32_t)total;
+    }
+    free(order);
+}
+
+/*
+ * Shortlist = union of the selected clusters' members [A "the union of the
+ * top-selected clusters defines the drafter's shortlist"; S "Problem
+ * Definition": output V_S].  Listed in ascending token id.
+ * sl_off[0] is read (base offset); sl_off[1..n] are written; offsets never
+ * exceed `capacity` (entries past it are dropped and OR_ECAPACITY returned).
+ * Cluster ids outside [0, M) are skipped and OR_EINVAL returned.
+ */
+int oracle_build_shortlist(int n, int M, int V, const int32_t *sel,
+                           const int32_t *n_sel, const int32_t *cluster_of,
+                           int64_t capacity, int64_t *sl_off, int32_t *sl_ids)
+{
+    int status = OR_OK;
+    unsigned char *mark = (unsigned char *)malloc((size_t)(M > 0 ? M : 1));
+    int64_t pos = sl_off[0];
+    for (int row = 0; row < n; ++row) {
+        memset(mark, 0, (size_t)M);
+        int k = n_sel[row];
+        if (k < 0 || k > M) {
+            status = status ? status : OR_EINVAL;
+            k = k < 0 ? 0 : M;
+        }
+        for (int j = 0; j < k; ++j) {
+            int c = sel[(int64_t)row * M + j];
+            if (c < 0 || c >= M) {
+                status = status ? status : OR_EINVAL;
+                continue;
+            }
+            mark[c] = 1;
+        }
+        for (int y = 0; y < V; ++y) {
+            int c = cluster_of[y];
+            if (c < 0 || c >= M) {
+                status = status ? status : OR_EINVAL;
+                continue;
+            }
+            if (!mark[c])
+                continue;
+            if (pos < capacity)
+                sl_ids[pos] = y;
+            else
+                status = OR_ECAPACITY;
+            ++pos;
+        }
+        sl_off[row + 1] = pos < capacity ? pos : capacity;
+    }
+    free(mark);
+    return status;
+}
+
+/*
+ * Gathered LM head [S "System Modules: Gathered LM Head" (projects hidden
+ * states onto the shortlist rows only); "Novel Architectural Elements"
+ * (index-select + GEMM); "Comparison to Prior Work" (O(|V_S| d) instead of
+ * O(|V| d))]:
+ *   logit[g][i][j] = sum_k W[S_g[j]][k] * h[g][i][k].
+ * h row (g, i) starts at h + g*ldh_g + i*d.  Output for (g, i, j) at
+ * m*sl_off[g] + i*len_g + j.  A token id outside [0, V) yields NaN.
+ */
+void oracle_gathered_lm_head(int dtype, int V, int d, const void *W, int G,
+                             int m, const void *h, int64_t ldh_g,
+                             const int64_t *sl_off, const int32_t *sl_ids,
+                             float *logits)
+{
+    for (int g = 0; g < G; ++g) {
+        int64_t len = sl_off[g + 1] - sl_off[g];
+        for (int i = 0; i < m; ++i) {
+            int64_t hrow = (int64_t)g * ldh_g + (int64_t)i * d;
+            float *out = logits + (int64_t)m * sl_off[g] + (int64_t)i * len;
+            for (int64_t j = 0; j < len; ++j) {
+                int32_t y = sl_ids[sl_off[g] + j];
+                if (y < 0 || y >= V) {
+                    out[j] = NAN;
+                    continue;
+                }
+                double acc = 0.0;
+                for (int k = 0; k < d; ++k)
+                    acc += load_elem(dtype, W, (int64_t)y * d + k) *
+                           load_elem(dtype, h, hrow + k);
+                out[j] = (float)acc;
+            }
+        }
+    }
+}
+
+/*
+ * Dense (full-vocabulary) head, the O(|V| d) projection the method replaces
+ * [A; S "Core Problem"]: logits[row][y] = sum_k W[y][k] h_row[k].
+ * Same summation as the gathered head, so the two agree bit for bit.
+ */
+void oracle_dense_lm_head(int dtype, int V, int d, const void *W, int n,
+                          const void *h, int64_t ldh, float *logits)
+{
+    for (int row = 0; row < n; ++row)
+        for (int y = 0; y < V; ++y) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k)
+                acc += load_elem(dtype, W, (int64_t)y * d + k) *
+                       load_elem(dtype, h, (int64_t)row * ldh + k);
+            logits[(int64_t)row * V + y] = (float)acc;
+        }
+}
+
+/*
+ * Inverse-CDF draw over non-negative weights w[0..n): total = sum w; the
+ * first j whose inclusive running sum exceeds u*total; if rounding leaves
+ * none, the last j with w_j > 0 (or -1 when all are zero).  *tie is set when
+ * a CDF boundary next to the threshold lies within TIE_REL*total of it.
+ */
+static int64_t inverse_cdf(const double *w, int64_t n, double u, int *tie,
+                           double *total_out)
+{
+    double total = 0.0;
+    for (int64_t j = 0; j < n; ++j)
+        total += w[j];
+    if (total_out)
+        *total_out = total;
+    double thr = u * total, run = 0.0, eps = TIE_REL * total;
+    int64_t pick = -1, last_pos = -1;
+    for (int64_t j = 0; j < n; ++j) {
+        double before = run;
+        run += w[j];
+        if (w[j] > 0.0)
+            last_pos = j;
+        if (pick < 0 && run > thr) {
+            pick = j;
+            if (fabs(run - thr) < eps || (j > 0 && fabs(before - thr) < eps))
+                *tie = 1;
+        }
+    }
+    if (pick < 0) {
+        pick = last_pos;
+        *tie = 1;
+    }
+    return pick;
+}
+
+/*
+ * Draft proposal from the shortlist distribution [A: the drafter proposes
+ * from its shortlist; S "Pipeline Flow": gathered projection, then
+ * sampling].  Per row (g, i): q = softmax(logits / tau) over S_g, token =
+ * S_g[inverse_cdf(q, u)].  tau == 0 means argmax (ties to the lowest token
+ * id) with a one-hot q.  Empty rows give token -1.  tie[row] marks draws
+ * whose threshold sits within 1e-12 (relative) of a CDF boundary.
+ */
+void oracle_shortlist_sample(int G, int m, const int64_t *sl_off,
+                             const int32_t *sl_ids, const float *logits,
+                             float temperature, const float *u,
+                             int32_t *token, float *q, unsigned char *tie)
+{
+    for (int g = 0; g < G; ++g) {
+        int64_t len = sl_off[g + 1] - sl_off[g];
+        double *e = (double *)malloc(sizeof(double) * (size_t)(len > 0 ? len : 1));
+        for (int i = 0; i < m; ++i) {
+            int64_t row = (int64_t)g * m + i;
+            const float *l = logits + (int64_t)m * sl_off[g] + (int64_t)i * len;
+            float *qr = q + (int64_t)m * sl_off[g] + (int64_t)i * len;
+            int t = 0;
+            if (len == 0) {
+                token[row] = -1;
+                if (tie)
+                    tie[row] = 0;
+                continue;
+            }
+            int64_t jmax = 0;
+            for (int64_t j = 1; j < len; ++j)
+                if (l[j] > l[jmax])
+                    jmax = j;
+            int64_t pick;
+            if (temperature == 0.0f) {
+                pick = jmax;
+                for (int64_t j = 0; j < len; ++j)
+                    qr[j] = j == jmax ? 1.0f : 0.0f;
+            } else {
+                double mx = (double)l[jmax], Z = 0.0;
+                for (int64_t j = 0; j < len; ++j)
+                    e[j] = exp(((double)l[j] - mx) / (double)temperature);
+                pick = inverse_cdf(e, len, (double)u[row], &t, &Z);
+                for (int64_t j = 0; j < len; ++j)
+                    qr[j] = (float)(e[j] / Z);
+            }
+            token[row] = sl_ids[sl_off[g] + pick];
+            if (tie)
+                tie[row] = (unsigned char)t;
+        }
+        free(e);
+    }
+}
+
+/*
+ * Full-vocabulary target distribution from target logits (softmax per row):
+ * p[y] = exp(l[y] - max) / sum_y' exp(l[y'] - max), rounded to fp32.  The
+ * target verifies over the full vocabulary [A; S "System Modules: Target
+ * Model"].
+ */
+void oracle_target_softmax(int rows, int V, const float *logits, float *p)
+{
+    double *e = (double *)malloc(sizeof(double) * (size_t)V);
+    for (int r = 0; r < rows; ++r) {
+        const float *l = logits + (int64_t)r * V;
+        float mx = l[0];
+        for (int y = 1; y < V; ++y)
+            if (l[y] > mx)
+                mx = l[y];
+        double Z = 0.0;
+        for (int y = 0; y < V; ++y) {
+            e[y] = exp((double)l[y] - (double)mx);
+            Z += e[y];
+        }
+        for (int y = 0; y < V; ++y)
+            p[(int64_t)r * V + y] = (float)(e[y] / Z);
+    }
+    free(e);
+}
+
+/*
+ * Rejection-sampling verification over the full vocabulary, which keeps the
+ * output distributed exactly as the target [A "the target model still
+ * verifies over the full vocabulary, preserving exactness"; S "Pipeline
+ * Flow: Rejection Sampling Verification"; textbook speculative sampling].
+ * For sequence b and positions t = 0..T-1 (draft[t][b], row t*B + b of the
+ * shortlist arrays, q in the sampler's layout with m = 1):
+ *   accept x iff u_acc * q_t(x) < p_t(x)   (q_t(x) = 0 off the shortlist);
+ *   on the first rejection draw from max(0, p_t - q_t) over all of V (from
+ *   p_t itself if that residual has no mass) with u_fin and stop;
+ *   if all T are accepted draw the bonus token from p_T with u_fin.
+ * out[b][0..n_acc] holds the emitted tokens, the rest is -1.
+ */
+void oracle_verify_reject(int B, int T, int V, const int32_t *draft,
+                          const int64_t *sl_off, const int32_t *sl_ids,
+                          const float *q, const float *p, const float *u_acc,
+                          const float *u_fin, int32_t *n_acc, int32_t *out,
+                          unsigned char *tie)
+{
+    double *w = (double *)malloc(sizeof(double) * (size_t)V);
+    double *qd = (double *)malloc(sizeof(double) * (size_t)V);
+    for (int b = 0; b < B; ++b) {
+        int t_flag = 0, t;
+        for (int k = 0; k <= T; ++k)
+            out[(int64_t)b * (T + 1) + k] = -1;
+        for (t = 0; t < T; ++t) {
+            int64_t row = (int64_t)t * B + b;
+            const float *pt = p + ((int64_t)b * (T + 1) + t) * V;
+            /* q_t as a dense vector over V */
+            for (int y = 0; y < V; ++y)
+                qd[y] = 0.0;
+            for (int64_t j = sl_off[row]; j < sl_off[row + 1]; ++j) {
+                int32_t y = sl_ids[j];
+                if (y >= 0 && y < V)
+                    qd[y] = (double)q[j];
+            }
+            int32_t x = draft[row];
+            double qx = (x >= 0 && x < V) ? qd[x] : 0.0;
+            double px = (x >= 0 && x < V) ? (double)pt[x] : 0.0;
+            if ((double)u_acc[row] * qx < px) {
+                out[(int64_t)b * (T + 1) + t] = x;
+                continue;
+            }
+            double R;
+            for (int y = 0; y < V; ++y) {
+                double r = (double)pt[y] - qd[y];
+                w[y] = r > 0.0 ? r : 0.0;
+            }
+            int64_t pick = inverse_cdf(w, V, (double)u_fin[b], &t_flag, &R);
+            if (!(R > 0.0)) {
+                t_flag = 0;
+                for (int y = 0; y < V; ++y)
+                    w[y] = (double)pt[y];
+                pick = inverse_cdf(w, V, (double)u_fin[b], &t_flag, NULL);
+            }
+            out[(int64_t)b * (T + 1) + t] = (int32_t)pick;
+            break;
+        }
+        if (t == T) {
+            const float *pT = p + ((int64_t)b * (T + 1) + T) * V;
+            for (int y = 0; y < V; ++y)
+                w[y] = (double)pT[y];
+            out[(int64_t)b * (T + 1) + T] =
+                (int32_t)inverse_cdf(w, V, (double)u_fin[b], &t_flag, NULL);
+        }
+        n_acc[b] = t;
+        if (tie)
+            tie[b] = (unsigned char)t_flag;
+    }
+    free(w);
+    free(qd);
+}
