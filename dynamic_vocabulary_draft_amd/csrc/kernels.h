@@ -1,0 +1,40 @@
+// Internal launchers, one per kernel family (each defined next to its
+// kernels).  Arguments are validated by the C-ABI layer before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ds {
+
+hipError_t router_launch(hipStream_t s, bool bf16, int n, int d, int r, int M, int act,
+                         const void *h, int64_t ldh, const void *W1, const void *b1,
+                         const void *W2, const void *b2, float *scores, float *z);
+
+hipError_t select_launch(hipStream_t s, int n, int M, const float *scores,
+                         const int32_t *cluster_size, int kind, const int32_t *budget,
+                         int32_t *sel, int32_t *n_sel, int32_t *sl_len);
+
+// build: chunk counts + last-block scan, then compaction
+constexpr int kBuildChunk = 4096;  // tokens per workgroup
+size_t build_ws_bytes(int n, int V);
+hipError_t build_launch(hipStream_t s, int n, int M, int V, const int32_t *sel,
+                        const int32_t *n_sel, const int32_t *cluster_of, int64_t capacity,
+                        int64_t *sl_off, int32_t *sl_ids, int32_t *err_flag, void *ws);
+
+hipError_t head_launch(hipStream_t s, bool bf16, int V, int d, const void *W, int G, int m,
+                       const void *h, int64_t ldh_g, const int64_t *sl_off,
+                       const int32_t *sl_ids, int64_t max_rows, float *logits);
+
+hipError_t sample_launch(hipStream_t s, int G, int m, const int64_t *sl_off,
+                         const int32_t *sl_ids, const float *logits, float temperature,
+                         const float *u, int32_t *token, float *q);
+
+hipError_t softmax_launch(hipStream_t s, int rows, int V, const float *logits, float *p);
+
+hipError_t verify_launch(hipStream_t s, int B, int T, int V, const int32_t *draft,
+                         const int64_t *sl_off, const int32_t *sl_ids, const float *q,
+                         const float *p, const float *u_acc, const float *u_fin, int32_t *n_acc,
+                         int32_t *out);
+
+}  // namespace ds

@@ -1,0 +1,190 @@
+"""ctypes binding of libdynaspec.so (the C-ABI in include/dynaspec.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, passes their device pointers and sizes to the library, and
+raises DynaspecError on a non-zero status.  No computation happens here, and
+there is no fallback: if the library is missing the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdynaspec.so")
+
+F32, BF16 = 0, 1
+RELU, SILU = 0, 1
+BUDGET_CLUSTERS, BUDGET_TOKENS = 0, 1
+STATUS = {0: "DS_OK", 1: "DS_EINVAL", 2: "DS_EDTYPE", 3: "DS_ESHAPE", 4: "DS_ECAPACITY",
+          5: "DS_EHIP"}
+
+_vp, _i, _i64, _f, _sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
+
+
+class DynaspecError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__("%s failed: %s (%d)" % (fn, STATUS.get(code, "?"), code))
+        self.code = code
+
+
+class ChainArgs(C.Structure):
+    """Mirror of ds_draft_chain_args."""
+    _fields_ = [("B", _i), ("T", _i), ("V", _i), ("d", _i), ("r", _i), ("M", _i),
+                ("dtype", _i), ("act", _i), ("budget_kind", _i), ("temperature", _f),
+                ("W", _vp), ("W1", _vp), ("b1", _vp), ("W2", _vp), ("b2", _vp),
+                ("cluster_of", _vp), ("cluster_size", _vp), ("h", _vp), ("budget", _vp),
+                ("u_draft", _vp), ("capacity", _i64), ("max_rows", _vp),
+                ("scores", _vp), ("sel", _vp), ("n_sel", _vp), ("sl_len", _vp),
+                ("sl_off", _vp), ("sl_ids", _vp), ("logits", _vp), ("q", _vp),
+                ("token", _vp), ("err_flag", _vp), ("ws", _vp), ("ws_bytes", _sz)]
+
+
+_SIGS = {
+    "ds_status_string": (C.c_char_p, [_i]),
+    "ds_version": (C.c_char_p, []),
+    "ds_router_workspace_bytes": (_sz, [_i, _i]),
+    "ds_router_score": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _sz]),
+    "ds_select_clusters": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp]),
+    "ds_build_workspace_bytes": (_sz, [_i, _i]),
+    "ds_build_shortlist": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz]),
+    "ds_gathered_lm_head": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i64, _vp, _vp, _i64, _vp]),
+    "ds_shortlist_sample": (_i, [_vp, _i, _i, _vp, _vp, _vp, _f, _vp, _vp, _vp]),
+    "ds_target_softmax": (_i, [_vp, _i, _i, _vp, _vp]),
+    "ds_verify_reject": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "ds_draft_chain_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "ds_draft_chain": (_i, [_vp, _vp, C.POINTER(ChainArgs)]),
+}
+
+SYMBOLS = tuple(_SIGS)
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libdynaspec.so is not built (run python -m "
+                          "dynamic_vocabulary_draft_amd.build); there is no fallback path")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _s(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError("expected bf16 or fp32, got %s" % t.dtype)
+
+
+def _ld(t: torch.Tensor, dim: int = 0) -> int:
+    """Leading dimension (elements between consecutive indices of `dim`); a
+    size-1 dimension may carry any stride, so it is taken from the shape."""
+    if t.shape[dim] > 1:
+        return t.stride(dim)
+    n = 1
+    for s in t.shape[dim + 1:]:
+        n *= s
+    return n
+
+
+def _check(name: str, code: int) -> None:
+    if code != 0:
+        raise DynaspecError(name, code)
+
+
+def version() -> str:
+    return lib.ds_version().decode()
+
+
+def router_workspace_bytes(n: int, r: int) -> int:
+    return int(lib.ds_router_workspace_bytes(n, r))
+
+
+def build_workspace_bytes(n: int, V: int) -> int:
+    return int(lib.ds_build_workspace_bytes(n, V))
+
+
+def draft_chain_workspace_bytes(B: int, T: int, V: int, r: int) -> int:
+    return int(lib.ds_draft_chain_workspace_bytes(B, T, V, r))
+
+
+def router_score(h, W1, b1, W2, b2, act, scores, ws, *, n=None, ldh=None, stream=None):
+    """scores[n][M] <- router(h rows); h row i at h + i*ldh elements."""
+    n = h.shape[0] if n is None else n
+    ldh = _ld(h) if ldh is None else ldh
+    r, d = W1.shape
+    M = W2.shape[0]
+    _check("ds_router_score", lib.ds_router_score(
+        _s(stream), _dt(W1), n, d, r, M, act, _p(h), ldh, _p(W1), _p(b1), _p(W2), _p(b2),
+        _p(scores), _p(ws), ws.numel() * ws.element_size()))
+
+
+def select_clusters(scores, cluster_size, kind, budget, sel, n_sel, sl_len, *, stream=None):
+    n, M = scores.shape
+    _check("ds_select_clusters", lib.ds_select_clusters(
+        _s(stream), n, M, _p(scores), _p(cluster_size), kind, _p(budget), _p(sel), _p(n_sel),
+        _p(sl_len)))
+
+
+def build_shortlist(sel, n_sel, cluster_of, capacity, sl_off, sl_ids, err_flag, ws, *,
+                    stream=None):
+    n, M = sel.shape
+    _check("ds_build_shortlist", lib.ds_build_shortlist(
+        _s(stream), n, M, cluster_of.shape[0], _p(sel), _p(n_sel), _p(cluster_of), int(capacity),
+        _p(sl_off), _p(sl_ids), _p(err_flag), _p(ws), ws.numel() * ws.element_size()))
+
+
+def gathered_lm_head(W, h, sl_off, sl_ids, max_rows, logits, *, G=None, m=None, ldh_g=None,
+                     stream=None):
+    """h is [G][m][d] (or pass G, m, ldh_g for a strided view)."""
+    V, d = W.shape
+    if G is None:
+        G, m = h.shape[0], h.shape[1]
+        ldh_g = _ld(h)
+    _check("ds_gathered_lm_head", lib.ds_gathered_lm_head(
+        _s(stream), _dt(W), V, d, _p(W), G, m, _p(h), ldh_g, _p(sl_off), _p(sl_ids),
+        int(max_rows), _p(logits)))
+
+
+def shortlist_sample(sl_off, sl_ids, logits, temperature, u, token, q, *, m=1, stream=None):
+    G = sl_off.shape[0] - 1
+    _check("ds_shortlist_sample", lib.ds_shortlist_sample(
+        _s(stream), G, m, _p(sl_off), _p(sl_ids), _p(logits), float(temperature), _p(u),
+        _p(token), _p(q)))
+
+
+def target_softmax(logits, p, *, stream=None):
+    V = logits.shape[-1]
+    _check("ds_target_softmax", lib.ds_target_softmax(
+        _s(stream), logits.numel() // V, V, _p(logits), _p(p)))
+
+
+def verify_reject(draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out, *, stream=None):
+    T, B = draft.shape
+    V = p.shape[-1]
+    _check("ds_verify_reject", lib.ds_verify_reject(
+        _s(stream), B, T, V, _p(draft), _p(sl_off), _p(sl_ids), _p(q), _p(p), _p(u_acc),
+        _p(u_fin), _p(n_acc), _p(out)))
+
+
+def draft_chain(args: ChainArgs, head_stream=None, router_stream=None):
+    _check("ds_draft_chain", lib.ds_draft_chain(_s(head_stream), _s(router_stream),
+                                                C.byref(args)))

@@ -1,0 +1,160 @@
+"""One speculative draft step on the GPU, through the C-ABI only.
+
+``DraftStep`` owns the device buffers for one workload and enqueues:
+  chains (batch B, depth T): ds_draft_chain (router/select/build of position
+      t+1 on a second stream, overlapped with head + sample of position t),
+      then ds_target_softmax and ds_verify_reject on the head stream;
+  trees (B sequences x m nodes sharing one shortlist): router, select and
+      build for the B roots, then one gathered head with m rows per group and
+      one sample per node.
+PyTorch only allocates memory and provides the streams.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import native as N
+from . import synthetic as syn
+
+
+def to_dev(a: np.ndarray | None, device="cuda") -> torch.Tensor | None:
+    if a is None:
+        return None
+    src = np.ascontiguousarray(a)
+    if src.dtype == np.uint16:  # bf16 bit patterns
+        src = src.view(np.int16)
+    host = torch.from_numpy(src)
+    # a fresh tensor has canonical strides (numpy may give size-1 dims any stride)
+    out = torch.empty(host.shape, dtype=host.dtype, device=device).copy_(host)
+    return out.view(torch.bfloat16) if a.dtype == np.uint16 else out
+
+
+def shortlist_bounds(cfg: syn.Config, cluster_size: np.ndarray) -> np.ndarray:
+    """Host-side upper bound of the shortlist rows of each position-call."""
+    srt = np.sort(cluster_size)[::-1].astype(np.int64)
+    out = []
+    for b in cfg.budget:
+        if cfg.budget_kind == syn.BUDGET_TOKENS:
+            per_row = min(int(cfg.V), max(int(b), 1) + int(srt[0]))
+        else:
+            k = min(max(int(b), 1), cfg.M)
+            per_row = int(srt[:k].sum())
+        out.append(per_row * cfg.B)
+    return np.asarray(out, dtype=np.int64)
+
+
+class DraftStep:
+    def __init__(self, wl: syn.Workload, device="cuda", W: torch.Tensor | None = None,
+                 temperature: float = 1.0):
+        cfg = self.cfg = wl.cfg
+        self.device = device
+        self.temperature = float(temperature)
+        dev = lambda a: to_dev(a, device)  # noqa: E731
+        self.W = W if W is not None else dev(wl.W)
+        R = wl.router
+        self.W1, self.b1, self.W2, self.b2 = (dev(R[k]) for k in ("W1", "b1", "W2", "b2"))
+        self.cluster_of = dev(wl.cluster_of)
+        self.cluster_size = dev(wl.cluster_size)
+        self.h = dev(wl.h)
+        self.budget = dev(wl.budget)
+        self.u_draft = dev(wl.u_draft)
+        self.u_acc = dev(wl.u_acc)
+        self.u_fin = dev(wl.u_fin)
+        self.target_logits = dev(wl.target_logits)
+        B, T, M, V = cfg.B, cfg.T, cfg.M, cfg.V
+        self.max_rows = shortlist_bounds(cfg, wl.cluster_size)
+        self.capacity = int(self.max_rows.sum())
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.scores = torch.empty(T, B, M, **f32)
+        self.sel = torch.empty(T, B, M, **i32)
+        self.n_sel = torch.empty(T, B, **i32)
+        self.sl_len = torch.empty(T, B, **i32)
+        self.sl_off = torch.zeros(T * B + 1, dtype=torch.int64, device=device)
+        self.sl_ids = torch.empty(max(self.capacity, 1), **i32)
+        m = cfg.tree_nodes
+        self.logits = torch.empty(max(self.capacity * m, 1), **f32)
+        self.q = torch.empty(max(self.capacity * m, 1), **f32)
+        self.token = torch.empty((B, m) if cfg.is_tree else (T, B), **i32)
+        self.err_flag = torch.zeros(1, **i32)
+        nbytes = N.draft_chain_workspace_bytes(B, T, V, cfg.r)
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.router_stream = torch.cuda.Stream(device=device)
+        if self.target_logits is not None:
+            self.p = torch.empty(B, T + 1, V, **f32)
+            self.n_acc = torch.empty(B, **i32)
+            self.out = torch.empty(B, T + 1, **i32)
+        self._args = self._chain_args() if not cfg.is_tree else None
+
+    # ------------------------------------------------------------------ chains
+    def _chain_args(self) -> N.ChainArgs:
+        cfg = self.cfg
+        p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        return N.ChainArgs(
+            B=cfg.B, T=cfg.T, V=cfg.V, d=cfg.d, r=cfg.r, M=cfg.M,
+            dtype=N.BF16 if cfg.dtype == syn.DT_BF16 else N.F32, act=cfg.act,
+            budget_kind=cfg.budget_kind, temperature=self.temperature,
+            W=p(self.W), W1=p(self.W1), b1=p(self.b1), W2=p(self.W2), b2=p(self.b2),
+            cluster_of=p(self.cluster_of), cluster_size=p(self.cluster_size), h=p(self.h),
+            budget=p(self.budget), u_draft=p(self.u_draft), capacity=self.capacity,
+            max_rows=self.max_rows.ctypes.data, scores=p(self.scores), sel=p(self.sel),
+            n_sel=p(self.n_sel), sl_len=p(self.sl_len), sl_off=p(self.sl_off),
+            sl_ids=p(self.sl_ids), logits=p(self.logits), q=p(self.q), token=p(self.token),
+            err_flag=p(self.err_flag), ws=p(self.ws), ws_bytes=self.ws.numel())
+
+    def set_W(self, W: torch.Tensor) -> None:
+        """Point the head at another (identical) copy of W."""
+        self.W = W
+        if self._args is not None:
+            self._args.W = W.data_ptr()
+
+    def draft(self, stream=None) -> None:
+        stream = stream or torch.cuda.current_stream()
+        if self.cfg.is_tree:
+            return self._draft_tree(stream)
+        N.draft_chain(self._args, stream, self.router_stream)
+
+    def verify(self, stream=None) -> None:
+        N.target_softmax(self.target_logits, self.p, stream=stream)
+        N.verify_reject(self.token, self.sl_off, self.sl_ids, self.q, self.p, self.u_acc,
+                        self.u_fin, self.n_acc, self.out, stream=stream)
+
+    def step(self, stream=None) -> None:
+        self.draft(stream)
+        if self.target_logits is not None:
+            self.verify(stream)
+
+    # ------------------------------------------------------------------- trees
+    def _draft_tree(self, stream) -> None:
+        cfg = self.cfg
+        B, M, m = cfg.B, cfg.M, cfg.tree_nodes
+        z = self.ws  # router z and build workspace share the chain workspace
+        zbytes = (N.router_workspace_bytes(B, cfg.r) + 255) // 256 * 256
+        N.router_score(self.h, self.W1, self.b1, self.W2, self.b2, cfg.act, self.scores[0],
+                       z[:zbytes], n=B, ldh=(1 + cfg.tree_nodes) * cfg.d, stream=stream)
+        N.select_clusters(self.scores[0], self.cluster_size, cfg.budget_kind, self.budget[0],
+                          self.sel[0], self.n_sel[0], self.sl_len[0], stream=stream)
+        N.build_shortlist(self.sel[0], self.n_sel[0], self.cluster_of, self.capacity,
+                          self.sl_off, self.sl_ids, self.err_flag, z[zbytes:], stream=stream)
+        d = cfg.d
+        N.gathered_lm_head(self.W, self.h[:, 1:], self.sl_off, self.sl_ids, self.max_rows[0],
+                           self.logits, G=B, m=m, ldh_g=(1 + m) * d, stream=stream)
+        N.shortlist_sample(self.sl_off, self.sl_ids, self.logits, self.temperature,
+                           self.u_draft, self.token, self.q, m=m, stream=stream)
+        del d
+
+    # ----------------------------------------------------------------- results
+    def host(self) -> dict:
+        torch.cuda.synchronize(self.device)
+        n = int(self.sl_off[-1].item())
+        r = {k: getattr(self, k).cpu().numpy() for k in
+             ("scores", "sel", "n_sel", "sl_len", "sl_off", "token", "err_flag")}
+        r["sl_ids"] = self.sl_ids[:n].cpu().numpy()
+        mm = self.cfg.tree_nodes
+        r["logits"] = self.logits[: n * mm].cpu().numpy()
+        r["q"] = self.q[: n * mm].cpu().numpy()
+        if self.target_logits is not None:
+            r.update(p=self.p.cpu().numpy(), n_acc=self.n_acc.cpu().numpy(),
+                     out=self.out.cpu().numpy())
+        return r

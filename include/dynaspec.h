@@ -1,0 +1,251 @@
+/*
+ * dynaspec.h -- C-ABI of the MI355X (gfx950) shortlisted draft head.
+ *
+ * The calls follow the DynaSpec pipeline: a router scores vocabulary
+ * clusters from the draft hidden state, the top clusters under a
+ * position-aware budget form the shortlist, the draft logits are a gathered
+ * projection over only those rows of the LM head, the drafter samples from
+ * the shortlist distribution, and the target verifies over the full
+ * vocabulary by rejection sampling.  Sources (pages cited by title and
+ * section):
+ *   [A] "DynaSpec: Context-aware Dynamic Speculative Sampling for
+ *       Large-Vocabulary Language Models", arXiv abstract page, Abstract.
+ *   [S] papers.lunadong.com summary of DynaSpec, sections "Problem
+ *       Definition", "Pipeline Flow", "System Modules", "Novel Architectural
+ *       Elements", "Modeling / Key Hyperparameters".
+ *   Speculative sampling (accept with min(1, p/q), residual max(0, p - q),
+ *   bonus token) is the textbook algorithm of the speculative-decoding works
+ *   that [A] builds on.
+ *
+ * Conventions for every call:
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or retains caller memory, and keeps no
+ *     state between calls apart from a per-process pool of HIP events used
+ *     by ds_draft_chain.
+ *   - Calls only enqueue work on the given stream(s) and return; nothing
+ *     synchronises with the host.
+ *   - Argument errors are detected on the host before anything is enqueued
+ *     and return DS_EINVAL / DS_EDTYPE / DS_ESHAPE.  A failed launch returns
+ *     DS_EHIP.  Data-dependent errors (a shortlist over capacity, a cluster
+ *     id out of range) are raised on the device into a caller-owned int32
+ *     flag with atomicMax, so the caller zeroes it once and checks it after
+ *     its own synchronisation.
+ *   - bf16 tensors are raw bf16 (16-bit) arrays; fp32 is IEEE binary32.
+ *   - Identical inputs give bit-identical outputs: no floating-point
+ *     atomics, fixed reduction orders.
+ *   - Shortlists are ragged (CSR) arrays: sl_off holds ABSOLUTE offsets into
+ *     sl_ids; sl_off[0] is the base at which a call's shortlists start, so
+ *     successive calls (draft positions) can append to one buffer.
+ *   - Per-group float outputs (logits, q) use the same absolute offsets:
+ *     the entry (group g, head row i, shortlist index j) lives at
+ *     m*sl_off[g] + i*len_g + j, with len_g = sl_off[g+1] - sl_off[g].
+ *   - Workspaces ("ws") are caller-owned device buffers of at least the size
+ *     the matching *_workspace_bytes() query returns.  They must be
+ *     zero-filled once before first use (the kernels leave them reusable)
+ *     and must not be shared by calls that may run concurrently.
+ */
+#ifndef DYNASPEC_H
+#define DYNASPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DS_OK = 0,
+    DS_EINVAL = 1,    /* bad argument (null pointer, non-positive size, ...) */
+    DS_EDTYPE = 2,    /* unsupported dtype / activation / budget kind       */
+    DS_ESHAPE = 3,    /* sizes inconsistent or beyond the supported limits  */
+    DS_ECAPACITY = 4, /* (device flag) shortlist longer than the capacity   */
+    DS_EHIP = 5       /* a HIP launch or runtime call failed                */
+} ds_status;
+
+typedef enum { DS_F32 = 0, DS_BF16 = 1 } ds_dtype;
+typedef enum { DS_RELU = 0, DS_SILU = 1 } ds_act;
+typedef enum { DS_BUDGET_CLUSTERS = 0, DS_BUDGET_TOKENS = 1 } ds_budget_kind;
+
+/* Limits checked on the host. */
+#define DS_MAX_CLUSTERS 4096    /* M: clusters are ranked in LDS            */
+#define DS_MAX_GROUPS 65535     /* G (and n for selection/build)            */
+#define DS_MAX_HEAD_ROWS 256    /* m: head rows sharing one shortlist       */
+
+const char *ds_status_string(ds_status s);
+const char *ds_version(void);
+
+/*
+ * Router / meta-classifier [S "System Modules: Router"; "Key
+ * Hyperparameters: 2-layer MLP with ReLU"; "Problem Definition": its input is
+ * the draft hidden state H_{t-1}]:
+ *     z_i = act(sum_k W1[i][k] h[k] + b1[i]),  scores[c] = sum_i W2[c][i] z_i + b2[c]
+ * dt      DS_F32 or DS_BF16: dtype of h, W1, b1, W2, b2.
+ * n       rows; row `row` of h starts at h + row*ldh elements (ldh >= d).
+ * d, r, M input width, hidden width, number of clusters.  d and r must be
+ *         multiples of 8 (16-byte rows for bf16, 32-byte for fp32).
+ * act     DS_RELU or DS_SILU.
+ * W1 [r][d], b1 [r] or NULL, W2 [M][r], b2 [M] or NULL.
+ * scores  [n][M] fp32 output (accumulation in fp32, z kept in fp32).
+ * ws      >= ds_router_workspace_bytes(n, r) bytes (holds z).
+ */
+size_t ds_router_workspace_bytes(int n, int r);
+ds_status ds_router_score(hipStream_t s, ds_dtype dt, int n, int d, int r, int M, ds_act act,
+                          const void *h, int64_t ldh, const void *W1, const void *b1,
+                          const void *W2, const void *b2, float *scores, void *ws,
+                          size_t ws_bytes);
+
+/*
+ * Top-cluster selection under a position-aware budget [A "the union of the
+ * top-selected clusters"; S "Key Novelty" (position-aware budget) and "Key
+ * Hyperparameters" (k_c(t) decays from k_0 to k_1)].  Per row, clusters are
+ * ranked by (score descending, cluster id ascending); -0.0 ties with +0.0.
+ *   DS_BUDGET_CLUSTERS: the first clamp(budget[row], 1, M) clusters.
+ *   DS_BUDGET_TOKENS:   the shortest prefix whose total size reaches
+ *                       max(budget[row], 1) tokens (all M if none does).
+ * scores [n][M] fp32 (NaN is invalid input: the result is then unspecified
+ * but every index stays in range); cluster_size [M] int32 >= 0;
+ * budget [n] int32.
+ * Outputs: sel [n][M] int32 ranked ids (entries past n_sel[row] are -1),
+ * n_sel [n] int32, sl_len [n] int32 (sum of the selected sizes).
+ * Limits: 1 <= M <= DS_MAX_CLUSTERS, 1 <= n <= DS_MAX_GROUPS.
+ */
+ds_status ds_select_clusters(hipStream_t s, int n, int M, const float *scores,
+                             const int32_t *cluster_size, ds_budget_kind kind,
+                             const int32_t *budget, int32_t *sel, int32_t *n_sel,
+                             int32_t *sl_len);
+
+/*
+ * Shortlist = union of the selected clusters' member tokens, in ascending
+ * token id [A "the union of the top-selected clusters defines the drafter's
+ * shortlist"; S "Problem Definition": output V_S].
+ * sel [n][M], n_sel [n] as written by ds_select_clusters; cluster_of [V]
+ * int32 maps every token to its cluster.
+ * sl_off [n+1] int64: sl_off[0] is READ (base offset, e.g. the end of the
+ * previous call's shortlists), sl_off[1..n] are written.
+ * sl_ids [capacity] int32: entries sl_off[0] .. sl_off[n]-1 are written.
+ * Offsets never exceed `capacity`; entries beyond it are dropped and
+ * *err_flag raised to DS_ECAPACITY.  Cluster ids outside [0, M) (in sel or
+ * cluster_of) are skipped and raise DS_EINVAL.  err_flag may be NULL.
+ * ws >= ds_build_workspace_bytes(n, V) bytes, zero-filled before first use.
+ */
+size_t ds_build_workspace_bytes(int n, int V);
+ds_status ds_build_shortlist(hipStream_t s, int n, int M, int V, const int32_t *sel,
+                             const int32_t *n_sel, const int32_t *cluster_of, int64_t capacity,
+                             int64_t *sl_off, int32_t *sl_ids, int32_t *err_flag, void *ws,
+                             size_t ws_bytes);
+
+/*
+ * Gathered LM head [S "System Modules: Gathered LM Head" (projects hidden
+ * states only onto the shortlist rows); "Novel Architectural Elements"
+ * (index-select fused with the GEMM, no gathered copy of W); "Comparison to
+ * Prior Work" (O(|V_S| d) instead of O(|V| d))]:
+ *     logits[g][i][j] = sum_k W[S_g[j]][k] * h[g][i][k]
+ * dt      dtype of W and h (fp32 accumulation, fp32 output).
+ * W       [V][d], one token's row contiguous; d a multiple of 8, and a row
+ *         at most 16 KB (d <= 8192 bf16, <= 4096 fp32).
+ * G, m    groups (shortlists) and head rows per group (1 <= m <= 256).
+ * h       row (g, i) at h + g*ldh_g + i*d elements (ldh_g >= m*d).
+ * sl_off  [G+1] absolute offsets, sl_ids the token ids (ascending per group
+ *         is not required by this call).
+ * max_rows host-side upper bound of sl_off[G] - sl_off[0]; sizes the grid
+ *         (rows past the true total are skipped on the device).
+ * logits  output, entry (g, i, j) at m*sl_off[g] + i*len_g + j.
+ * Token ids outside [0, V) give NaN.
+ */
+ds_status ds_gathered_lm_head(hipStream_t s, ds_dtype dt, int V, int d, const void *W, int G,
+                              int m, const void *h, int64_t ldh_g, const int64_t *sl_off,
+                              const int32_t *sl_ids, int64_t max_rows, float *logits);
+
+/*
+ * Draft proposal from the shortlist distribution [A; S "Pipeline Flow"].
+ * Per row (g, i), q = softmax(logits / temperature) over S_g computed in
+ * fp64, and token = S_g[j*] with j* the first index whose running sum of
+ * exp((l_j - max)/T) exceeds u[row] * (their total) (if rounding leaves none,
+ * the last index with non-zero mass).  temperature == 0 gives the argmax
+ * (ties to the lowest index) with a one-hot q.  Empty rows give token -1.
+ * u [G*m] fp32 in [0, 1); token [G*m] int32; q in the logits layout.
+ */
+ds_status ds_shortlist_sample(hipStream_t s, int G, int m, const int64_t *sl_off,
+                              const int32_t *sl_ids, const float *logits, float temperature,
+                              const float *u, int32_t *token, float *q);
+
+/*
+ * Full-vocabulary target distribution p = softmax(target logits) per row
+ * (fp64 exponent and sum, fp32 output) [A: the target verifies over the full
+ * vocabulary].  logits and p are [rows][V] fp32.
+ */
+ds_status ds_target_softmax(hipStream_t s, int rows, int V, const float *logits, float *p);
+
+/*
+ * Rejection-sampling verification over the full vocabulary, which keeps the
+ * emitted tokens distributed exactly as the target [A "the target model
+ * still verifies over the full vocabulary, preserving exactness"; S
+ * "Pipeline Flow: Rejection Sampling Verification"].  For sequence b:
+ *   for t < T: x = draft[t][b] (shortlist row t*B + b, q in the sampler's
+ *   layout with m = 1, q_t(x) = 0 off the shortlist); accept iff
+ *   (double)u_acc[t][b] * q_t(x) < p_t(x).  At the first rejection, draw from
+ *   max(0, p_t - q_t) over all V (from p_t if that has no mass) with
+ *   u_fin[b] by the inverse CDF and stop; if all T are accepted, draw the
+ *   bonus token from p_T with u_fin[b].
+ * p [B][T+1][V] fp32 target probabilities.  Outputs n_acc [B] in [0, T] and
+ * out [B][T+1] (the first n_acc+1 entries are the emitted tokens, the rest
+ * -1).  Limits: 1 <= T <= 64.
+ */
+ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *draft,
+                           const int64_t *sl_off, const int32_t *sl_ids, const float *q,
+                           const float *p, const float *u_acc, const float *u_fin,
+                           int32_t *n_acc, int32_t *out);
+
+/*
+ * One chain-drafting step over T positions for B sequences, with the router
+ * on its own stream, overlapped with the head [A: routing is overlapped with
+ * draft computation via parallel execution streams; S "Novel Architectural
+ * Elements": router on a separate stream].  For each position t:
+ *   router_stream: router(h[:, t]) -> select(budget[t]) -> build (appending
+ *                  to the shortlist buffer) -> event
+ *   head_stream:   wait(event) -> gathered head(h[:, t+1]) -> sample(u_draft[t])
+ * so the router, selection and build of position t+1 run while the head of
+ * position t streams its rows.  Rows are position-major (row t*B + b), the
+ * layout ds_verify_reject reads.  Every pointer is a device pointer except
+ * max_rows (host, [T]).  On return all work is enqueued and head_stream
+ * waits for everything enqueued on router_stream.
+ */
+typedef struct {
+    int B, T, V, d, r, M;
+    ds_dtype dtype;
+    ds_act act;
+    ds_budget_kind budget_kind;
+    float temperature;
+    const void *W;              /* [V][d]                          */
+    const void *W1, *b1, *W2, *b2;
+    const int32_t *cluster_of;  /* [V]                             */
+    const int32_t *cluster_size;/* [M]                             */
+    const void *h;              /* [B][T+1][d]                     */
+    const int32_t *budget;      /* [T][B]                          */
+    const float *u_draft;       /* [T][B]                          */
+    int64_t capacity;           /* elements of sl_ids              */
+    const int64_t *max_rows;    /* HOST [T]: bound on rows per position */
+    float *scores;              /* [T][B][M]                       */
+    int32_t *sel;               /* [T][B][M]                       */
+    int32_t *n_sel, *sl_len;    /* [T][B]                          */
+    int64_t *sl_off;            /* [T*B+1], sl_off[0] read as base */
+    int32_t *sl_ids;            /* [capacity]                      */
+    float *logits, *q;          /* [capacity]                      */
+    int32_t *token;             /* [T][B]                          */
+    int32_t *err_flag;          /* 1 int32 or NULL                 */
+    void *ws;                   /* ds_draft_chain_workspace_bytes  */
+    size_t ws_bytes;
+} ds_draft_chain_args;
+
+size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r);
+ds_status ds_draft_chain(hipStream_t head_stream, hipStream_t router_stream,
+                         const ds_draft_chain_args *a);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DYNASPEC_H */

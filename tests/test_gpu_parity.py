@@ -1,0 +1,345 @@
+"""GPU parity: every C-ABI call against the CPU oracle on identical inputs.
+
+Bars (written in each test): cluster ids, counts, shortlist offsets and ids,
+sampled and verified tokens bit-exact (tokens only outside the draws that the
+oracle flags as lying within 1e-12 of a CDF boundary); logits within 2e-2
+absolute for bf16 inputs and 1e-5 * max(1, max|ref|) for fp32; probabilities
+within one fp32 ulp.  Sizes span several tiles and ragged tails (V not a
+multiple of the 4096-token build chunk, d not a multiple of 512, M not a
+power of two, empty and single-entry shortlists).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dynamic_vocabulary_draft_amd import synthetic as syn
+from dynamic_vocabulary_draft_amd.pipeline import to_dev
+
+pytestmark = pytest.mark.gpu
+
+BF16_ATOL = 2e-2
+F32_RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def N():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from dynamic_vocabulary_draft_amd import native
+    return native
+
+
+def _logit_bar(got, ref, bf16):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    if bf16:
+        err = np.abs(got - ref).max() if got.size else 0.0
+        assert err <= BF16_ATOL, "max |d| = %g > %g" % (err, BF16_ATOL)
+    else:
+        bar = F32_RTOL * max(1.0, np.abs(ref).max() if ref.size else 1.0)
+        err = np.abs(got - ref).max() if got.size else 0.0
+        assert err <= bar, "max |d| = %g > %g" % (err, bar)
+
+
+def _ulp_bar(got, ref):
+    got, ref = np.asarray(got, np.float32), np.asarray(ref, np.float32)
+    spacing = np.spacing(np.maximum(np.abs(ref), np.float32(1e-38)))
+    bad = np.abs(got.astype(np.float64) - ref.astype(np.float64)) > spacing.astype(np.float64)
+    assert not bad.any(), "%d entries beyond one ulp" % bad.sum()
+
+
+def _store(x, bf16):
+    return syn.f32_to_bf16_bits(x) if bf16 else np.ascontiguousarray(x, np.float32)
+
+
+def _cpu(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+# ----------------------------------------------------------------------------
+# router_score
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("bf16,act,n,d,r,M", [
+    (False, syn.ACT_RELU, 4, 256, 256, 64),
+    (True, syn.ACT_SILU, 7, 264, 136, 100),
+    (True, syn.ACT_SILU, 1, 4096, 1024, 1024),
+    (True, syn.ACT_SILU, 64, 3840, 1024, 2048),
+])
+def test_router_parity(N, oracle_lib, bf16, act, n, d, r, M):
+    g = np.random.default_rng(100 + d)
+    cfg = syn.shrink(syn.CONFIGS[4], dtype=syn.DT_BF16 if bf16 else syn.DT_F32, act=act, d=d, r=r,
+                     M=M)
+    R = syn.make_router(cfg)
+    h = _store(g.standard_normal((n, 2, d)).astype(np.float32), bf16)  # rows at stride 2d
+    ref = oracle_lib.router_score(np.ascontiguousarray(h[:, 0]), R["W1"], R["b1"], R["W2"], R["b2"],
+                                  act)
+    hd = to_dev(h)
+    scores = torch.empty(n, M, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(N.router_workspace_bytes(n, r), dtype=torch.uint8, device="cuda")
+    Rd = {k: to_dev(v) for k, v in R.items()}
+    N.router_score(hd[:, 0], Rd["W1"], Rd["b1"], Rd["W2"], Rd["b2"], act, scores, ws, n=n, ldh=2 * d)
+    _logit_bar(_cpu(scores), ref, bf16)
+
+
+# ----------------------------------------------------------------------------
+# select_clusters: bit-exact on identical scores
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M", [1, 3, 64, 100, 1024, 2048, 4096])
+@pytest.mark.parametrize("kind", [syn.BUDGET_CLUSTERS, syn.BUDGET_TOKENS])
+def test_select_parity(N, oracle_lib, M, kind):
+    g = np.random.default_rng(M * 7 + kind)
+    n = 9
+    s = g.standard_normal((n, M)).astype(np.float32)
+    s[:3] = g.integers(-2, 3, size=(3, M)).astype(np.float32)  # heavy ties
+    s[0][s[0] == 0] = -0.0
+    size = (syn.zipf_cluster_sizes(max(M * 40, M), M, 1.1) if M > 1
+            else np.array([7], np.int32))
+    total = int(size.sum())
+    if kind == syn.BUDGET_CLUSTERS:
+        budget = np.array([0, 1, 2, M, M + 5, -3, max(1, M // 2), 3, 8], np.int32)
+    else:
+        budget = np.array([0, 1, total, total + 9, -4, total // 3, total // 5, 17, 5000],
+                          np.int32)
+    ref = oracle_lib.select_clusters(s, size, kind, budget)
+    sel = torch.empty(n, M, dtype=torch.int32, device="cuda")
+    n_sel = torch.empty(n, dtype=torch.int32, device="cuda")
+    sl_len = torch.empty(n, dtype=torch.int32, device="cuda")
+    N.select_clusters(to_dev(s), to_dev(size), kind, to_dev(budget), sel, n_sel, sl_len)
+    assert np.array_equal(_cpu(n_sel), ref[1])
+    assert np.array_equal(_cpu(sl_len), ref[2])
+    assert np.array_equal(_cpu(sel), ref[0])
+
+
+# ----------------------------------------------------------------------------
+# build_shortlist: bit-exact
+# ----------------------------------------------------------------------------
+def _clusters(V, M, seed):
+    g = np.random.default_rng(seed)
+    size = syn.zipf_cluster_sizes(V, M, 1.1)
+    cluster_of = np.empty(V, np.int32)
+    cluster_of[g.permutation(V)] = np.repeat(np.arange(M, dtype=np.int32), size)
+    return cluster_of, size
+
+
+@pytest.mark.parametrize("V,M,n", [(13, 3, 2), (4096, 64, 3), (20000, 100, 5),
+                                   (128256, 1024, 4), (262144, 2048, 2)])
+def test_build_parity(N, oracle_lib, V, M, n):
+    cluster_of, size = _clusters(V, M, V)
+    g = np.random.default_rng(V + 1)
+    s = g.standard_normal((n, M)).astype(np.float32)
+    budget = g.integers(1, max(2, V // 3), size=n).astype(np.int32)
+    sel, n_sel, sl_len = oracle_lib.select_clusters(s, size, syn.BUDGET_TOKENS, budget)
+    base = 17
+    cap = base + int(sl_len.sum())
+    st, off_ref, ids_ref = oracle_lib.build_shortlist(sel, n_sel, cluster_of, capacity=cap,
+                                                      base=base)
+    assert st == 0
+    sl_off = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+    sl_off[0] = base
+    sl_ids = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(N.build_workspace_bytes(n, V), dtype=torch.uint8, device="cuda")
+    for _ in range(2):  # the workspace is reusable call after call
+        N.build_shortlist(to_dev(sel), to_dev(n_sel), to_dev(cluster_of), cap, sl_off, sl_ids,
+                          flag, ws)
+        assert int(_cpu(flag)[0]) == 0
+        assert np.array_equal(_cpu(sl_off), off_ref)
+        assert np.array_equal(_cpu(sl_ids)[base:], ids_ref[base:])
+        assert (_cpu(sl_ids)[:base] == -7).all()
+
+
+def test_build_capacity_and_invalid_ids(N, oracle_lib):
+    V, M, n = 9000, 40, 3
+    cluster_of, size = _clusters(V, M, 5)
+    g = np.random.default_rng(6)
+    sel, n_sel, sl_len = oracle_lib.select_clusters(g.standard_normal((n, M)).astype(np.float32),
+                                                    size, syn.BUDGET_TOKENS,
+                                                    np.full(n, 3000, np.int32))
+    ws = torch.zeros(N.build_workspace_bytes(n, V), dtype=torch.uint8, device="cuda")
+    cap = int(sl_len.sum()) - 100
+    st, off_ref, ids_ref = oracle_lib.build_shortlist(sel, n_sel, cluster_of, capacity=cap)
+    assert st == oracle.ECAPACITY
+    sl_off = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+    sl_ids = torch.empty(cap, dtype=torch.int32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    N.build_shortlist(to_dev(sel), to_dev(n_sel), to_dev(cluster_of), cap, sl_off, sl_ids, flag, ws)
+    assert int(_cpu(flag)[0]) == oracle.ECAPACITY
+    assert np.array_equal(_cpu(sl_off), off_ref)
+    assert np.array_equal(_cpu(sl_ids), ids_ref)
+    # out-of-range cluster ids in the map and in the selection are skipped and flagged
+    bad_map = cluster_of.copy()
+    bad_map[[5, 700, 8999]] = [-1, M, 10 ** 6]
+    bad_sel = sel.copy()
+    bad_sel[1, 0] = M + 3
+    st, off_ref, ids_ref = oracle_lib.build_shortlist(bad_sel, n_sel, bad_map)
+    assert st == oracle.EINVAL
+    cap2 = n * V
+    sl_ids2 = torch.empty(cap2, dtype=torch.int32, device="cuda")
+    flag.zero_()
+    N.build_shortlist(to_dev(bad_sel), to_dev(n_sel), to_dev(bad_map), cap2, sl_off, sl_ids2, flag,
+                      ws)
+    assert int(_cpu(flag)[0]) == oracle.EINVAL
+    got_off = _cpu(sl_off)
+    assert np.array_equal(got_off, off_ref)
+    assert np.array_equal(_cpu(sl_ids2)[: got_off[-1]], ids_ref[: off_ref[-1]])
+
+
+# ----------------------------------------------------------------------------
+# gathered_lm_head
+# ----------------------------------------------------------------------------
+def _random_shortlists(g, V, lens, base=0):
+    sl_off = np.concatenate([[base], base + np.cumsum(lens)]).astype(np.int64)
+    ids = [np.sort(g.choice(V, L, replace=False)) for L in lens]
+    sl_ids = np.full(base + sum(lens), -1, np.int32)
+    if sum(lens):
+        sl_ids[base:] = np.concatenate(ids)
+    return sl_off, sl_ids
+
+
+@pytest.mark.parametrize("bf16,d", [(False, 256), (True, 264), (True, 3840), (True, 4096),
+                                    (False, 1032)])
+@pytest.mark.parametrize("G,m", [(1, 1), (3, 1), (4, 3), (2, 64)])
+def test_head_parity(N, oracle_lib, bf16, d, G, m):
+    V = 5000
+    g = np.random.default_rng(d * 31 + G * 7 + m)
+    cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=50, dtype=syn.DT_BF16 if bf16 else syn.DT_F32)
+    cluster_of, _ = _clusters(V, 50, 3)
+    W = syn.make_lm_head(cfg, cluster_of)
+    h = _store(g.standard_normal((G, m, d)).astype(np.float32), bf16)
+    lens = [int(x) for x in g.integers(0, 700, size=G)]
+    lens[0] = max(lens[0], 1)
+    if G > 2:
+        lens[1] = 0  # an empty group
+    base = 5
+    sl_off, sl_ids = _random_shortlists(g, V, lens, base)
+    ref = oracle_lib.gathered_lm_head(W, h, sl_off - base, sl_ids[base:])
+    Wd, hd = to_dev(W), to_dev(h)
+    total = int(sl_off[-1] - base)
+    for max_rows in (total, max(1, total // 5)):  # any bound gives the same result
+        logits = torch.full((m * int(sl_off[-1]),), float("nan"), device="cuda")
+        N.gathered_lm_head(Wd, hd, to_dev(sl_off), to_dev(sl_ids), max_rows, logits)
+        got = _cpu(logits)[m * base:]
+        assert not np.isnan(got).any()
+        _logit_bar(got, ref, bf16)
+
+
+def test_head_full_vocabulary_is_dense(N, oracle_lib):
+    """With the whole vocabulary as shortlist the head is the dense LM head."""
+    cfg = syn.CONFIGS[0]
+    cluster_of, _ = syn.make_clusters(cfg)
+    W = syn.make_lm_head(cfg, cluster_of)
+    h = syn.make_hidden(cfg)[0, :3]
+    dense = oracle_lib.dense_lm_head(W, h)
+    logits = torch.empty(3 * cfg.V, device="cuda")
+    N.gathered_lm_head(to_dev(W), to_dev(h[None]), to_dev(np.array([0, cfg.V], np.int64)),
+                       to_dev(np.arange(cfg.V, dtype=np.int32)), cfg.V, logits)
+    _logit_bar(_cpu(logits).reshape(3, cfg.V), dense, False)
+
+
+# ----------------------------------------------------------------------------
+# shortlist_sample
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("lens,m", [([1, 5, 255, 256, 257, 1000], 1), ([27000, 3], 1),
+                                    ([600000], 1), ([300, 1, 40], 4)])
+@pytest.mark.parametrize("tau", [1.0, float(np.float32(0.7)), 0.0])
+def test_sample_parity(N, oracle_lib, lens, m, tau):
+    g = np.random.default_rng(sum(lens) + m)
+    G = len(lens)
+    sl_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    sl_ids = np.concatenate([np.sort(g.choice(10 ** 6, L, replace=False)) for L in lens]).astype(np.int32)
+    logits = (g.standard_normal(m * int(sl_off[-1])) * 3).astype(np.float32)
+    u = syn.make_uniforms(syn.CONFIGS[0], 9, G * m, instance=G)
+    u[0] = 0.0
+    tok_ref, q_ref, tie = oracle_lib.shortlist_sample(sl_off, sl_ids, logits, u, m, tau)
+    token = torch.empty(G * m, dtype=torch.int32, device="cuda")
+    q = torch.empty(logits.shape[0], dtype=torch.float32, device="cuda")
+    N.shortlist_sample(to_dev(sl_off), to_dev(sl_ids), to_dev(logits), tau, to_dev(u), token, q, m=m)
+    got = _cpu(token)
+    assert np.array_equal(got[~tie], tok_ref[~tie])
+    _ulp_bar(_cpu(q), q_ref)
+
+
+def test_sample_many_rows_bit_exact(N, oracle_lib):
+    """20k draws over one 5000-entry shortlist: the tokens match the oracle."""
+    L, R = 5000, 20000
+    g = np.random.default_rng(77)
+    lg = (g.standard_normal(L) * 2).astype(np.float32)
+    sl_off = (np.arange(R + 1) * L).astype(np.int64)
+    ids = np.tile(np.arange(L, dtype=np.int32), R)
+    logits = np.tile(lg, R)
+    u = syn.make_uniforms(syn.CONFIGS[0], 9, R, instance=5)
+    tok_ref, q_ref, tie = oracle_lib.shortlist_sample(sl_off, ids, logits, u)
+    token = torch.empty(R, dtype=torch.int32, device="cuda")
+    q = torch.empty(L * R, dtype=torch.float32, device="cuda")
+    N.shortlist_sample(to_dev(sl_off), to_dev(ids), to_dev(logits), 1.0, to_dev(u), token, q)
+    got = _cpu(token)
+    assert np.array_equal(got[~tie], tok_ref[~tie])
+    assert tie.sum() <= 2
+
+
+# ----------------------------------------------------------------------------
+# target_softmax and verify_reject
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("rows,V", [(3, 1000), (5, 128256), (2, 262144)])
+def test_target_softmax_parity(N, oracle_lib, rows, V):
+    g = np.random.default_rng(V)
+    lg = (g.standard_normal((rows, V)) * 3).astype(np.float32)
+    p = torch.empty(rows, V, device="cuda")
+    N.target_softmax(to_dev(lg), p)
+    _ulp_bar(_cpu(p), oracle_lib.target_softmax(lg))
+
+
+def _verify_case(oracle_lib, V, T, B, mode, seed):
+    """Shortlists from random cluster selections, drafts sampled from q,
+    target probabilities per mode; everything computed on the host."""
+    g = np.random.default_rng(seed)
+    M = max(2, V // 64)
+    cluster_of, size = _clusters(V, M, seed)
+    s = g.standard_normal((T * B, M)).astype(np.float32)
+    sel, n_sel, sl_len = oracle_lib.select_clusters(s, size, syn.BUDGET_TOKENS,
+                                                    np.full(T * B, max(1, V // 4), np.int32))
+    st, sl_off, sl_ids = oracle_lib.build_shortlist(sel, n_sel, cluster_of)
+    n = int(sl_off[-1])
+    sl_ids = sl_ids[:n]
+    lg = (g.standard_normal(n) * 2).astype(np.float32)
+    u_d = syn.make_uniforms(syn.CONFIGS[0], 9, T * B, instance=seed)
+    draft, q, _ = oracle_lib.shortlist_sample(sl_off, sl_ids, lg, u_d)
+    if mode == "correlated":  # target logits = draft logits on the shortlist + N(0, 0.5)
+        tl = np.full((B, T + 1, V), -4.0, np.float32)
+        for t in range(T):
+            for b in range(B):
+                r = t * B + b
+                tl[b, t, sl_ids[sl_off[r]:sl_off[r + 1]]] = lg[sl_off[r]:sl_off[r + 1]]
+        tl += (g.standard_normal(tl.shape) * 0.5).astype(np.float32)
+    else:
+        tl = (g.standard_normal((B, T + 1, V)) * 3).astype(np.float32)
+    p = oracle_lib.target_softmax(tl)
+    u_acc = syn.make_uniforms(syn.CONFIGS[0], 10, (T, B), instance=seed)
+    if mode == "accept_all":
+        u_acc[:] = 0.0
+    elif mode == "reject_all":
+        u_acc[:] = np.float32(1 - 2 ** -24)
+    u_fin = syn.make_uniforms(syn.CONFIGS[0], 11, B, instance=seed)
+    return dict(draft=draft.reshape(T, B), sl_off=sl_off, sl_ids=sl_ids, q=q, p=p, u_acc=u_acc,
+                u_fin=u_fin)
+
+
+@pytest.mark.parametrize("V,T,B", [(8, 3, 64), (5000, 4, 16), (128256, 6, 4), (262144, 5, 3)])
+@pytest.mark.parametrize("mode", ["random", "accept_all", "reject_all", "correlated"])
+def test_verify_parity(N, oracle_lib, V, T, B, mode):
+    c = _verify_case(oracle_lib, V, T, B, mode, seed=V + T + B)
+    n_ref, out_ref, tie = oracle_lib.verify_reject(**c)
+    n_acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, T + 1, dtype=torch.int32, device="cuda")
+    dv = {k: to_dev(v) for k, v in c.items()}
+    N.verify_reject(dv["draft"], dv["sl_off"], dv["sl_ids"], dv["q"], dv["p"], dv["u_acc"],
+                    dv["u_fin"], n_acc, out)
+    assert np.array_equal(_cpu(n_acc), n_ref)  # accept decisions are exact
+    got = _cpu(out)
+    assert np.array_equal(got[~tie], out_ref[~tie])
+    if mode == "accept_all":
+        assert (n_ref == T).all()
+    if mode == "correlated":
+        assert n_ref.mean() > 0.5

@@ -1,0 +1,170 @@
+"""Host-side tests (no GPU): the C-ABI library loads and exports everything
+include/dynaspec.h declares, rejects bad arguments before enqueueing, and the
+host logic (seeded generator, capacity bounds) holds.
+
+Every validation case below is rejected on the host before any HIP call, so
+none of them can launch a kernel.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from dynamic_vocabulary_draft_amd import synthetic as syn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dynaspec.h")
+
+
+@pytest.fixture(scope="module")
+def N():
+    from dynamic_vocabulary_draft_amd import build, native  # noqa: F401
+    return native
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(ds_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol(N):
+    decl = declared_functions()
+    assert len(decl) >= 13
+    lib = C.CDLL(N.LIB_PATH)
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(N.SYMBOLS) == decl
+
+
+def test_status_strings_and_version(N):
+    assert "gfx950" in N.version()
+    for code in range(6):
+        assert N.lib.ds_status_string(code)
+    assert N.lib.ds_status_string(99) == b"unknown status"
+
+
+def test_workspace_queries(N):
+    assert N.router_workspace_bytes(64, 1024) == 64 * 1024 * 4
+    assert N.router_workspace_bytes(0, 4) == 0
+    nch = (262144 + 4095) // 4096
+    assert N.build_workspace_bytes(64, 262144) == 256 + 64 * nch * 8
+    assert N.draft_chain_workspace_bytes(1, 6, 128256, 1024) >= 4096 + 256
+
+
+FAKE = C.c_void_p(4096)  # aligned, never dereferenced: every call below fails validation
+
+
+def test_router_rejects_bad_arguments(N):
+    L = N.lib
+    args = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
+        ("s", None), ("dt", N.BF16), ("n", 4), ("d", 64), ("r", 64), ("M", 8), ("act", N.SILU),
+        ("h", FAKE), ("ldh", 64), ("W1", FAKE), ("b1", None), ("W2", FAKE), ("b2", None),
+        ("scores", FAKE), ("ws", None), ("ws_bytes", 0)]]
+    assert L.ds_router_score(*args(h=None)) == 1
+    assert L.ds_router_score(*args(n=0)) == 1
+    assert L.ds_router_score(*args(dt=7)) == 2
+    assert L.ds_router_score(*args(act=9)) == 2
+    assert L.ds_router_score(*args(d=60, ldh=60)) == 3
+    assert L.ds_router_score(*args(ldh=32)) == 3
+    assert L.ds_router_score(*args(h=C.c_void_p(4100))) == 1  # misaligned
+    assert L.ds_router_score(*args()) == 1  # no workspace
+
+
+def test_select_build_head_sample_verify_reject_bad_arguments(N):
+    L = N.lib
+    assert L.ds_select_clusters(None, 2, 5000, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE) == 3
+    assert L.ds_select_clusters(None, 2, 64, FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE) == 2
+    assert L.ds_select_clusters(None, 0, 64, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE) == 1
+    assert L.ds_select_clusters(None, 2, 64, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE) == 1
+    assert L.ds_build_shortlist(None, 2, 64, 1000, FAKE, FAKE, FAKE, 10, FAKE, FAKE, None, FAKE,
+                                0) == 1  # workspace too small
+    assert L.ds_build_shortlist(None, 2, 99999, 1000, FAKE, FAKE, FAKE, 10, FAKE, FAKE, None,
+                                FAKE, 1 << 20) == 3
+    assert L.ds_build_shortlist(None, 2, 64, 1000, FAKE, FAKE, FAKE, -1, FAKE, FAKE, None, FAKE,
+                                1 << 20) == 1
+    head = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
+        ("s", None), ("dt", N.BF16), ("V", 100), ("d", 64), ("W", FAKE), ("G", 2), ("m", 1),
+        ("h", FAKE), ("ldh_g", 64), ("sl_off", FAKE), ("sl_ids", FAKE), ("max_rows", 10),
+        ("logits", FAKE)]]
+    assert L.ds_gathered_lm_head(*head(W=None)) == 1
+    assert L.ds_gathered_lm_head(*head(dt=5)) == 2
+    assert L.ds_gathered_lm_head(*head(d=62, ldh_g=62)) == 3
+    assert L.ds_gathered_lm_head(*head(m=2)) == 3  # ldh_g < m*d
+    assert L.ds_gathered_lm_head(*head(m=300, ldh_g=300 * 64)) == 3
+    assert L.ds_gathered_lm_head(*head(d=8200, ldh_g=8200)) == 3
+    assert L.ds_gathered_lm_head(*head(dt=N.F32, d=4104, ldh_g=4104)) == 3
+    assert L.ds_gathered_lm_head(*head(max_rows=-1)) == 1
+    assert L.ds_shortlist_sample(None, 2, 1, FAKE, FAKE, FAKE, C.c_float(-1.0), FAKE, FAKE,
+                                 FAKE) == 1
+    assert L.ds_shortlist_sample(None, 2, 1, FAKE, FAKE, FAKE, C.c_float(float("nan")), FAKE,
+                                 FAKE, FAKE) == 1
+    assert L.ds_shortlist_sample(None, 0, 1, FAKE, FAKE, FAKE, C.c_float(1.0), FAKE, FAKE,
+                                 FAKE) == 1
+    assert L.ds_target_softmax(None, 0, 10, FAKE, FAKE) == 1
+    assert L.ds_verify_reject(None, 2, 65, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE) == 3
+    assert L.ds_verify_reject(None, 2, 3, (1 << 20) + 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE) == 3
+    assert L.ds_verify_reject(None, 2, 3, 100, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE) == 1
+    assert L.ds_draft_chain(None, None, None) == 1
+    a = N.ChainArgs(B=0, T=6)
+    assert L.ds_draft_chain(None, None, C.byref(a)) == 1
+
+
+# ----------------------------------------------------------------------------
+# host logic
+# ----------------------------------------------------------------------------
+def test_generator_is_deterministic_and_shaped():
+    a = syn.make_workload(0)
+    b = syn.make_workload(0)
+    for k in ("W", "h", "u_draft", "u_acc", "u_fin", "cluster_of", "target_logits"):
+        assert np.array_equal(getattr(a, k), getattr(b, k))
+    c = syn.make_workload(0, instance=1)
+    assert not np.array_equal(a.h, c.h)
+    assert np.array_equal(a.W, c.W)
+    assert a.h.shape == (1, 5, 256) and a.W.shape == (8192, 256)
+    assert (a.u_draft * 2 ** 24 == np.round(a.u_draft * 2 ** 24)).all()
+    assert ((a.u_draft >= 0) & (a.u_draft < 1)).all()
+
+
+def test_bf16_rounding_matches_torch():
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 7
+    x[:4] = [0.0, -0.0, 1e-40, 3.4e38]
+    ours = syn.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(syn.bf16_bits_to_f32(ours),
+                          torch.from_numpy(ours.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+@pytest.mark.parametrize("index", [1, 3, 4])
+def test_zipf_clusters_partition_vocabulary(index):
+    cfg = syn.CONFIGS[index]
+    cluster_of, size = syn.make_clusters(cfg)
+    assert size.sum() == cfg.V and size.min() >= 1
+    assert np.array_equal(np.bincount(cluster_of, minlength=cfg.M), size)
+    assert (np.diff(size) <= 0).all()  # ranks ordered by size
+
+
+def test_budget_schedules():
+    assert syn.CONFIGS[1].budget == (32768, 29491, 26214, 22938, 19661, 16384)
+    assert syn.CONFIGS[4].budget == (49152, 43008, 36864, 30720, 24576)
+    assert syn.linear_budget(5, 5, 1) == (5,)
+
+
+@pytest.mark.parametrize("index", [0, 1, 4])
+def test_capacity_bounds_cover_every_selection(oracle_lib, index):
+    from dynamic_vocabulary_draft_amd.pipeline import shortlist_bounds
+    cfg = syn.CONFIGS[index]
+    cluster_of, size = syn.make_clusters(cfg)
+    bounds = shortlist_bounds(cfg, size)
+    g = np.random.default_rng(index)
+    for t, b in enumerate(cfg.budget):
+        s = g.standard_normal((50, cfg.M)).astype(np.float32)
+        _, _, L = oracle_lib.select_clusters(s, size, cfg.budget_kind, np.full(50, b, np.int32))
+        assert L.max() * cfg.B <= bounds[t]
