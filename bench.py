@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Throughput of one speculative draft step of the shortlisted draft head.
+
+A step is the whole hot path over one batch: for each of T draft positions
+the router scores the clusters, the position's budget selects clusters, the
+shortlist is built, the gathered LM head projects the hidden state onto it
+and a draft token is sampled (router work of position t+1 on a second stream,
+overlapped with the head of position t); then the target distribution is the
+softmax of the target logits and the drafts are verified by rejection
+sampling.  Default workload: Llama-3-8B-shaped head, V=128256, d=4096, bf16,
+1024 Zipf-sized clusters, batch 1, depth 6, token budget 32768 -> 16384.
+
+Inputs are seeded and synthetic.  Steps rotate over several input instances
+(different hidden states, hence different shortlists), and every (instance,
+position) head launch reads its own identical copy of W in HBM, so no launch
+finds its rows in the 256 MB memory-side cache from an earlier one.
+
+Printed: one JSON line (value = draft tokens/s of the whole step), with
+`roofline` for the gathered head (algorithmic bytes per launch / its mean
+duration, from HIP events recorded around every head launch of the timed
+steps on the head stream) and `cpu_baseline` (the CPU oracle, one core, on a
+bounded sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "head_gemv_traffic.json")
+HEAD_SOURCES = ["dynamic_vocabulary_draft_amd/csrc/head.hip",
+                "dynamic_vocabulary_draft_amd/csrc/common.h"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def head_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in HEAD_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+class HipEvents:
+    """Timing events created through the HIP runtime (torch's Event only sees
+    torch's own streams)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def array(self, n: int):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError("hipEventCreate failed: %d" % rc)
+            arr[i] = e.value
+            self.made.append(e.value)
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(ms.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.made = []
+
+
+def cpu_baseline(wl, seconds: float) -> dict:
+    import oracle
+    from oracle import pipeline as opipe
+    oracle.build(force=False)
+    cfg = wl.cfg
+    n, t0 = 0, time.perf_counter()
+    while True:
+        opipe.run_step(wl)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+        log("oracle step %d done (%.1f s)" % (n, el))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": cfg.B * cfg.T * n / el, "unit": "draft tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d full step(s) of instance 0 (router, selection, shortlist, fp64 "
+                      "gathered head, sampling for all %d positions, target softmax and "
+                      "verification), %.1f s on 1 thread of %d (%s)"
+                      % (n, cfg.T, el, os.cpu_count() or 0, model or platform.machine())}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload index (1: Llama-shaped b1)")
+    ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--no-replicas", action="store_true",
+                    help="all head launches read one copy of W (cache-warm)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from dynamic_vocabulary_draft_amd import synthetic as syn
+    from dynamic_vocabulary_draft_amd.pipeline import DraftStep, to_dev
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = syn.CONFIGS[args.config]
+    e = cfg.elem_bytes
+    t_gen = time.perf_counter()
+    cluster_of, _ = syn.make_clusters(cfg)
+    W_host = syn.make_lm_head(cfg, cluster_of, threads=min(16, os.cpu_count() or 8))
+    log("W generated (%.1f s)" % (time.perf_counter() - t_gen))
+    W = to_dev(W_host)
+    wls = [syn.make_workload(args.config, instance=i, with_W=False) for i in range(args.instances)]
+    for wl in wls:
+        wl.W = W_host
+    steps = [DraftStep(wl, W=W) for wl in wls]
+    npos = 1 if cfg.is_tree else cfg.T
+    if not args.no_replicas and not cfg.is_tree:
+        for i, st in enumerate(steps):
+            reps = [W if (i == 0 and t == 0) else W.clone() for t in range(npos)]
+            st.set_W_positions(reps)
+        log("W replicas: %d x %.2f GB" % (args.instances * npos, W.numel() * e / 1e9))
+    del W_host
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    stream = torch.cuda.current_stream()
+    args.warmup = max(args.warmup, len(steps))  # every instance has run once
+    for k in range(args.warmup):
+        steps[k % len(steps)].step(stream)
+    torch.cuda.synchronize()
+    log("warmup done (%d steps)" % args.warmup)
+
+    # shortlist sizes per (instance, position): deterministic per instance
+    sizes = []
+    for st in steps:
+        off = st.sl_off.cpu().numpy()
+        ids = st.sl_ids.cpu().numpy()
+        per = []
+        for t in range(npos):
+            lo, hi = int(off[t * cfg.B]), int(off[(t + 1) * cfg.B])
+            per.append({"total": hi - lo, "union": int(np.unique(ids[lo:hi]).size)})
+        sizes.append(per)
+        assert int(st.err_flag.item()) == 0
+
+    ev_arrays = [ev.array(2 * npos) for _ in range(args.steps)] if not cfg.is_tree else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        st = steps[k % len(steps)]
+        if ev_arrays is not None:
+            st.set_head_events(ev_arrays[k])
+        st.step(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for st in steps:
+        if ev_arrays is not None:
+            st.set_head_events(None)
+        assert int(st.err_flag.item()) == 0
+    log("timed %d steps in %.3f s" % (args.steps, wall))
+
+    tokens_per_step = cfg.B * (cfg.tree_nodes if cfg.is_tree else cfg.T)
+    value = tokens_per_step * args.steps / wall
+    roof = None
+    head = None
+    if ev_arrays is not None:
+        durs, nbytes, rows = [], [], []
+        for k in range(args.steps):
+            i = k % len(steps)
+            for t in range(npos):
+                durs.append(ev.elapsed_ms(ev_arrays[k][2 * t], ev_arrays[k][2 * t + 1]))
+                sz = sizes[i][t]
+                # every needed W row once, the ids, the hidden rows, the logits
+                nbytes.append(sz["union"] * cfg.d * e + sz["total"] * 4 + cfg.B * cfg.d * e
+                              + sz["total"] * 4)
+                rows.append(sz["total"])
+        mean_ms = float(np.mean(durs))
+        achieved = float(np.sum(nbytes)) / (float(np.sum(durs)) * 1e-3) / 1e9
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                tr = json.load(f)
+            if tr.get("kernel_source_sha256") == head_source_sha() and \
+                    tr.get("workload") == cfg.name:
+                traffic = tr.get("bytes_per_launch")
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+        head = {"kernel": "head_gemv_kernel", "launches": len(durs),
+                "mean_us": round(mean_ms * 1e3, 2), "p10_us": round(float(np.percentile(durs, 10)) * 1e3, 2),
+                "p90_us": round(float(np.percentile(durs, 90)) * 1e3, 2),
+                "mean_rows": round(float(np.mean(rows)), 1),
+                "mean_algorithmic_bytes": round(float(np.mean(nbytes)), 0),
+                "head_only_tokens_per_s": round(cfg.B / (mean_ms * 1e-3), 1),
+                "w_replicas": not args.no_replicas}
+    ev.close()
+
+    out = {
+        "metric": "gathered-LM-head draft tokens/sec + HBM GB/s (% peak), V=128256 d=4096 bf16",
+        "value": round(value, 1), "unit": "draft tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == syn.DT_BF16 else "f32",
+        "data": "synthetic (seeded clustered-Gaussian W, N(0,1) hidden states, N(0,3) target "
+                "logits; %d instances rotated)" % args.instances,
+        "config": {"workload": cfg.name, "V": cfg.V, "d": cfg.d, "clusters": cfg.M,
+                   "batch": cfg.B, "depth": cfg.T, "tree_nodes": cfg.tree_nodes,
+                   "budget": list(cfg.budget), "router": "%d->%d->%d" % (cfg.d, cfg.r, cfg.M),
+                   "step": "router+select+build+gathered head+sample per position, "
+                           "target softmax + verify"},
+        "roofline": roof,
+        "head": head,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        wl0 = syn.make_workload(args.config, instance=0)
+        out["cpu_baseline"] = cpu_baseline(wl0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -271,9 +271,14 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
         return DS_EINVAL;
     if (!(a->temperature >= 0.0f))
         return DS_EINVAL;
-    for (int t = 0; t < T; ++t)
+    for (int t = 0; t < T; ++t) {
         if (a->max_rows[t] < 0)
             return DS_EINVAL;
+        if (a->W_pos && (!a->W_pos[t] || !aligned16(a->W_pos[t])))
+            return DS_EINVAL;
+        if (a->head_events && (!a->head_events[2 * t] || !a->head_events[2 * t + 1]))
+            return DS_EINVAL;
+    }
 
     float *z = reinterpret_cast<float *>(a->ws);
     void *bws = reinterpret_cast<char *>(a->ws) + round_up(ds_router_workspace_bytes(B, a->r), 256);
@@ -301,10 +306,14 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
             err = hipEventRecord(g_events.ev[t], rs);
         if (err == hipSuccess)
             err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
+        if (err == hipSuccess && a->head_events)
+            err = hipEventRecord(a->head_events[2 * t], hs);
         if (err == hipSuccess)
-            err = ds::head_launch(hs, bf16, a->V, a->d, a->W, B, 1,
+            err = ds::head_launch(hs, bf16, a->V, a->d, a->W_pos ? a->W_pos[t] : a->W, B, 1,
                                   hb + (size_t)(t + 1) * a->d * e, ldh, a->sl_off + rb, a->sl_ids,
                                   a->max_rows[t], a->logits);
+        if (err == hipSuccess && a->head_events)
+            err = hipEventRecord(a->head_events[2 * t + 1], hs);
         if (err == hipSuccess)
             err = ds::sample_launch(hs, B, 1, a->sl_off + rb, a->sl_ids, a->logits, a->temperature,
                                     a->u_draft + rb, a->token + rb, a->q);

@@ -39,7 +39,8 @@ class ChainArgs(C.Structure):
                 ("u_draft", _vp), ("capacity", _i64), ("max_rows", _vp),
                 ("scores", _vp), ("sel", _vp), ("n_sel", _vp), ("sl_len", _vp),
                 ("sl_off", _vp), ("sl_ids", _vp), ("logits", _vp), ("q", _vp),
-                ("token", _vp), ("err_flag", _vp), ("ws", _vp), ("ws_bytes", _sz)]
+                ("token", _vp), ("err_flag", _vp), ("ws", _vp), ("ws_bytes", _sz),
+                ("W_pos", _vp), ("head_events", _vp)]
 
 
 _SIGS = {

@@ -11,6 +11,8 @@ PyTorch only allocates memory and provides the streams.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import torch
 
@@ -108,6 +110,22 @@ class DraftStep:
         self.W = W
         if self._args is not None:
             self._args.W = W.data_ptr()
+
+    def set_W_positions(self, Ws: list[torch.Tensor] | None) -> None:
+        """One head matrix per draft position (None: W everywhere)."""
+        if Ws is None:
+            self._W_pos, self._args.W_pos = None, None
+            return
+        assert len(Ws) == self.cfg.T
+        self._W_pos_keep = Ws
+        self._W_pos = (ctypes.c_void_p * self.cfg.T)(*[w.data_ptr() for w in Ws])
+        self._args.W_pos = ctypes.cast(self._W_pos, ctypes.c_void_p)
+
+    def set_head_events(self, events) -> None:
+        """events: ctypes array of 2T hipEvent_t handles (or None)."""
+        self._head_events = events
+        self._args.head_events = (None if events is None
+                                  else ctypes.cast(events, ctypes.c_void_p))
 
     def draft(self, stream=None) -> None:
         stream = stream or torch.cuda.current_stream()

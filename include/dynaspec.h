@@ -210,8 +210,15 @@ ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *dr
  * so the router, selection and build of position t+1 run while the head of
  * position t streams its rows.  Rows are position-major (row t*B + b), the
  * layout ds_verify_reject reads.  Every pointer is a device pointer except
- * max_rows (host, [T]).  On return all work is enqueued and head_stream
- * waits for everything enqueued on router_stream.
+ * max_rows, W_pos and head_events (host arrays).  On return all work is
+ * enqueued and head_stream waits for everything enqueued on router_stream.
+ * Optional fields:
+ *   W_pos        host array [T] of head matrices, one per position (drafters
+ *                with a separate head per position, or copies of one head on
+ *                different memory); NULL means W at every position.
+ *   head_events  host array [2T] of caller-created HIP events; when non-NULL,
+ *                events 2t and 2t+1 are recorded on head_stream immediately
+ *                before and after the head launch of position t (profiling).
  */
 typedef struct {
     int B, T, V, d, r, M;
@@ -238,6 +245,8 @@ typedef struct {
     int32_t *err_flag;          /* 1 int32 or NULL                 */
     void *ws;                   /* ds_draft_chain_workspace_bytes  */
     size_t ws_bytes;
+    const void *const *W_pos;   /* HOST [T] or NULL                */
+    hipEvent_t *head_events;    /* HOST [2T] or NULL               */
 } ds_draft_chain_args;
 
 size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r);
