@@ -130,6 +130,8 @@ def main():
                     help="all head launches read one copy of W (cache-warm)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from the host instead of replaying step graphs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -166,12 +168,13 @@ def main():
     torch.cuda.synchronize()
 
     ev = HipEvents()
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream()  # a capturable (non-default) head stream
     args.warmup = max(args.warmup, len(steps))  # every instance has run once
-    for k in range(args.warmup):
-        steps[k % len(steps)].step(stream)
+    with torch.cuda.stream(stream):
+        for k in range(args.warmup):
+            steps[k % len(steps)].step(stream)
     torch.cuda.synchronize()
-    log("warmup done (%d steps)" % args.warmup)
+    log("eager warmup done (%d steps)" % args.warmup)
 
     # shortlist sizes per (instance, position): deterministic per instance
     sizes = []
@@ -185,32 +188,64 @@ def main():
         sizes.append(per)
         assert int(st.err_flag.item()) == 0
 
-    ev_arrays = [ev.array(2 * npos) for _ in range(args.steps)] if not cfg.is_tree else None
+    timed_events = not cfg.is_tree
+    graphs, mode = [], "eager"
+    if not args.eager:
+        # a few graphs per instance, replayed round-robin
+        n_graphs = max(len(steps), min(args.steps, 16) // len(steps) * len(steps))
+        try:
+            for g in range(n_graphs):
+                graphs.append(steps[g % len(steps)].capture(stream))
+            mode = "hip-graph"
+        except Exception as exc:  # noqa: BLE001 - fall back to eager launches
+            log("graph capture unavailable (%s); timing eager steps" % exc)
+            graphs = []
+    if mode == "hip-graph":
+        for g in graphs:
+            g.launch(stream)
+        torch.cuda.synchronize()
+        log("captured %d step graphs" % len(graphs))
+
+    def eager_steps(n, with_events):
+        sets = [ev.array(2 * npos) if with_events else None for _ in range(n)]
+        for k in range(n):
+            st = steps[k % len(steps)]
+            st.set_head_events(sets[k])
+            st.step(stream)
+        return sets
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        st = steps[k % len(steps)]
-        if ev_arrays is not None:
-            st.set_head_events(ev_arrays[k])
-        st.step(stream)
+    if mode == "hip-graph":
+        for k in range(args.steps):
+            graphs[k % len(graphs)].launch(stream)
+    else:
+        ev_sets = eager_steps(args.steps, timed_events)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    log("timed %d steps in %.3f s (%s)" % (args.steps, wall, mode))
+    if timed_events and mode == "hip-graph":
+        # HIP cannot time events recorded inside graphs: the head launches
+        # are timed on the same steps launched eagerly (same kernels, data)
+        n_ev = min(args.steps, 120)
+        torch.cuda.synchronize()
+        ev_sets = eager_steps(n_ev, True)
+        torch.cuda.synchronize()
+        log("timed %d eager steps for the head roofline" % n_ev)
     for st in steps:
-        if ev_arrays is not None:
-            st.set_head_events(None)
+        st.set_head_events(None)
         assert int(st.err_flag.item()) == 0
-    log("timed %d steps in %.3f s" % (args.steps, wall))
 
     tokens_per_step = cfg.B * (cfg.tree_nodes if cfg.is_tree else cfg.T)
     value = tokens_per_step * args.steps / wall
     roof = None
     head = None
-    if ev_arrays is not None:
+    if timed_events:
         durs, nbytes, rows = [], [], []
-        for k in range(args.steps):
+        for k in range(len(ev_sets)):
             i = k % len(steps)
             for t in range(npos):
-                durs.append(ev.elapsed_ms(ev_arrays[k][2 * t], ev_arrays[k][2 * t + 1]))
+                durs.append(ev.elapsed_ms(ev_sets[k][2 * t], ev_sets[k][2 * t + 1]))
                 sz = sizes[i][t]
                 # every needed W row once, the ids, the hidden rows, the logits
                 nbytes.append(sz["union"] * cfg.d * e + sz["total"] * 4 + cfg.B * cfg.d * e
@@ -227,13 +262,17 @@ def main():
                 traffic = tr.get("bytes_per_launch")
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
-        head = {"kernel": "head_gemv_kernel", "launches": len(durs),
-                "mean_us": round(mean_ms * 1e3, 2), "p10_us": round(float(np.percentile(durs, 10)) * 1e3, 2),
+        head = {"kernel": "head_gemv_kernel", "launches_timed": len(durs),
+                "mean_us": round(mean_ms * 1e3, 2),
+                "p10_us": round(float(np.percentile(durs, 10)) * 1e3, 2),
                 "p90_us": round(float(np.percentile(durs, 90)) * 1e3, 2),
                 "mean_rows": round(float(np.mean(rows)), 1),
                 "mean_algorithmic_bytes": round(float(np.mean(nbytes)), 0),
                 "head_only_tokens_per_s": round(cfg.B / (mean_ms * 1e-3), 1),
-                "w_replicas": not args.no_replicas}
+                "w_replicas": not args.no_replicas,
+                "timed_on": "eager steps (HIP events around each head launch)"}
+    for g in graphs:
+        g.close()
     ev.close()
 
     out = {
@@ -249,7 +288,8 @@ def main():
                    "batch": cfg.B, "depth": cfg.T, "tree_nodes": cfg.tree_nodes,
                    "budget": list(cfg.budget), "router": "%d->%d->%d" % (cfg.d, cfg.r, cfg.M),
                    "step": "router+select+build+gathered head+sample per position, "
-                           "target softmax + verify"},
+                           "target softmax + verify",
+                   "launch": mode},
         "roofline": roof,
         "head": head,
         "cpu_baseline": None,

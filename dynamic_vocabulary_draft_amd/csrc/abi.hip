@@ -1,10 +1,35 @@
 // C-ABI of the shortlisted draft head: host-side argument checks, workspace
 // sizes, dispatch to the kernel families, and the two-stream chain runner.
 // Nothing here allocates device memory.
+#include <atomic>
+#include <new>
 #include <vector>
 
 #include "common.h"
 #include "kernels.h"
+
+namespace ds {
+
+int device_cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 256;
+    if (dev < 64) {
+        int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0)
+            return v;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64)
+        cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+}  // namespace ds
 
 namespace {
 
@@ -48,7 +73,7 @@ ds_status check_router(ds_dtype dt, int n, int d, int r, int M, ds_act act, cons
         return DS_EDTYPE;
     if (act != DS_RELU && act != DS_SILU)
         return DS_EDTYPE;
-    if (d % 8 || r % 8 || ldh < d || ldh % 8)
+    if (d % 8 || r % 8 || ldh < d || ldh % 8 || d > 8192 || r > 8192)
         return DS_ESHAPE;
     if (!aligned16(h) || !aligned16(W1) || !aligned16(W2))
         return DS_EINVAL;
@@ -73,10 +98,10 @@ ds_status check_select(int n, int M, const float *scores, const int32_t *cluster
 }
 
 ds_status check_build(int n, int M, int V, const int32_t *sel, const int32_t *n_sel,
-                      const int32_t *cluster_of, int64_t capacity, int64_t *sl_off,
-                      int32_t *sl_ids, void *ws, size_t ws_bytes)
+                      const int32_t *cluster_of, const int32_t *index, int64_t capacity,
+                      int64_t *sl_off, int32_t *sl_ids, void *ws, size_t ws_bytes)
 {
-    if (!sel || !n_sel || !cluster_of || !sl_off || !sl_ids || !ws)
+    if (!sel || !n_sel || !cluster_of || !index || !sl_off || !sl_ids || !ws)
         return DS_EINVAL;
     if (n <= 0 || M <= 0 || V <= 0 || capacity < 0)
         return DS_EINVAL;
@@ -107,13 +132,15 @@ ds_status check_head(ds_dtype dt, int V, int d, const void *W, int G, int m, con
 }
 
 ds_status check_sample(int G, int m, const int64_t *sl_off, const int32_t *sl_ids,
-                       const float *logits, float temperature, const float *u, int32_t *token,
-                       float *q)
+                       const float *logits, float temperature, const float *u, int64_t max_len,
+                       int32_t *token, float *q)
 {
     if (!sl_off || !sl_ids || !logits || !u || !token || !q)
         return DS_EINVAL;
-    if (G <= 0 || m <= 0 || m > DS_MAX_HEAD_ROWS || G > DS_MAX_GROUPS)
+    if (G <= 0 || m <= 0 || m > DS_MAX_HEAD_ROWS || G > DS_MAX_GROUPS || max_len <= 0)
         return DS_EINVAL;
+    if (max_len > (1 << 20) || (int64_t)G * m > 65535)
+        return DS_ESHAPE;
     if (!(temperature >= 0.0f) || temperature > 3.0e38f)
         return DS_EINVAL;
     return DS_OK;
@@ -127,7 +154,7 @@ ds_status check_verify(int B, int T, int V, const int32_t *draft, const int64_t 
         return DS_EINVAL;
     if (B <= 0 || T <= 0 || V <= 0)
         return DS_EINVAL;
-    if (T > 64 || V > (1 << 20) || B > DS_MAX_GROUPS)
+    if (T > 64 || V > (1 << 20) || B > DS_MAX_GROUPS || (int64_t)B * T > (1ll << 30))
         return DS_ESHAPE;
     return DS_OK;
 }
@@ -181,21 +208,36 @@ ds_status ds_select_clusters(hipStream_t s, int n, int M, const float *scores,
         ds::select_launch(s, n, M, scores, cluster_size, kind, budget, sel, n_sel, sl_len));
 }
 
+size_t ds_cluster_index_bytes(int M, int V)
+{
+    return M > 0 && V > 0 ? ds::index_bytes(M, V) : 0;
+}
+
+ds_status ds_cluster_index(hipStream_t s, int M, int V, const int32_t *cluster_of,
+                           int32_t *index, int32_t *err_flag)
+{
+    if (!cluster_of || !index || M <= 0 || V <= 0)
+        return DS_EINVAL;
+    if (M > DS_MAX_CLUSTERS)
+        return DS_ESHAPE;
+    return hip_status(ds::index_launch(s, M, V, cluster_of, index, err_flag));
+}
+
 size_t ds_build_workspace_bytes(int n, int V)
 {
     return n > 0 && V > 0 ? ds::build_ws_bytes(n, V) : 0;
 }
 
 ds_status ds_build_shortlist(hipStream_t s, int n, int M, int V, const int32_t *sel,
-                             const int32_t *n_sel, const int32_t *cluster_of, int64_t capacity,
-                             int64_t *sl_off, int32_t *sl_ids, int32_t *err_flag, void *ws,
-                             size_t ws_bytes)
+                             const int32_t *n_sel, const int32_t *cluster_of,
+                             const int32_t *index, int64_t capacity, int64_t *sl_off,
+                             int32_t *sl_ids, int32_t *err_flag, void *ws, size_t ws_bytes)
 {
-    ds_status st = check_build(n, M, V, sel, n_sel, cluster_of, capacity, sl_off, sl_ids, ws,
-                               ws_bytes);
+    ds_status st = check_build(n, M, V, sel, n_sel, cluster_of, index, capacity, sl_off, sl_ids,
+                               ws, ws_bytes);
     if (st != DS_OK)
         return st;
-    return hip_status(ds::build_launch(s, n, M, V, sel, n_sel, cluster_of, capacity, sl_off,
+    return hip_status(ds::build_launch(s, n, M, V, sel, n_sel, cluster_of, index, capacity, sl_off,
                                        sl_ids, err_flag, ws));
 }
 
@@ -210,40 +252,67 @@ ds_status ds_gathered_lm_head(hipStream_t s, ds_dtype dt, int V, int d, const vo
                                       max_rows, logits));
 }
 
-ds_status ds_shortlist_sample(hipStream_t s, int G, int m, const int64_t *sl_off,
-                              const int32_t *sl_ids, const float *logits, float temperature,
-                              const float *u, int32_t *token, float *q)
+size_t ds_sample_workspace_bytes(int G, int m, int64_t max_len)
 {
-    ds_status st = check_sample(G, m, sl_off, sl_ids, logits, temperature, u, token, q);
-    if (st != DS_OK)
-        return st;
-    return hip_status(ds::sample_launch(s, G, m, sl_off, sl_ids, logits, temperature, u, token, q));
+    return G > 0 && m > 0 && max_len > 0 ? ds::sample_ws_bytes((int64_t)G * m, max_len) : 0;
 }
 
-ds_status ds_target_softmax(hipStream_t s, int rows, int V, const float *logits, float *p)
+ds_status ds_shortlist_sample(hipStream_t s, int G, int m, const int64_t *sl_off,
+                              const int32_t *sl_ids, const float *logits, float temperature,
+                              const float *u, int64_t max_len, int32_t *token, float *q, void *ws,
+                              size_t ws_bytes)
+{
+    ds_status st = check_sample(G, m, sl_off, sl_ids, logits, temperature, u, max_len, token, q);
+    if (st != DS_OK)
+        return st;
+    if (!ws || ws_bytes < ds_sample_workspace_bytes(G, m, max_len))
+        return DS_EINVAL;
+    return hip_status(ds::sample_launch(s, G, m, sl_off, sl_ids, logits, temperature, u, token, q,
+                                        max_len, ws));
+}
+
+size_t ds_softmax_workspace_bytes(int rows, int V)
+{
+    return rows > 0 && V > 0 ? ds::softmax_ws_bytes(rows, V) : 0;
+}
+
+ds_status ds_target_softmax(hipStream_t s, int rows, int V, const float *logits, float *p,
+                            void *ws, size_t ws_bytes)
 {
     if (!logits || !p || rows <= 0 || V <= 0)
         return DS_EINVAL;
-    return hip_status(ds::softmax_launch(s, rows, V, logits, p));
+    if (V > (1 << 20) || rows > 65535)
+        return DS_ESHAPE;
+    if (!ws || ws_bytes < ds_softmax_workspace_bytes(rows, V))
+        return DS_EINVAL;
+    return hip_status(ds::softmax_launch(s, rows, V, logits, p, ws));
+}
+
+size_t ds_verify_workspace_bytes(int B, int T, int V)
+{
+    return B > 0 && T > 0 && V > 0 ? ds::verify_ws_bytes(B, T, V) : 0;
 }
 
 ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *draft,
                            const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                            const float *p, const float *u_acc, const float *u_fin,
-                           int32_t *n_acc, int32_t *out)
+                           int32_t *n_acc, int32_t *out, void *ws, size_t ws_bytes)
 {
     ds_status st = check_verify(B, T, V, draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out);
     if (st != DS_OK)
         return st;
-    return hip_status(
-        ds::verify_launch(s, B, T, V, draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out));
+    if (!ws || ws_bytes < ds_verify_workspace_bytes(B, T, V))
+        return DS_EINVAL;
+    return hip_status(ds::verify_launch(s, B, T, V, draft, sl_off, sl_ids, q, p, u_acc, u_fin,
+                                        n_acc, out, ws));
 }
 
-size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r)
+size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r, int64_t max_len)
 {
-    if (B <= 0 || T <= 0 || V <= 0 || r <= 0)
+    if (B <= 0 || T <= 0 || V <= 0 || r <= 0 || max_len <= 0)
         return 0;
-    return round_up(ds_router_workspace_bytes(B, r), 256) + ds::build_ws_bytes(B, V);
+    return round_up(ds_router_workspace_bytes(B, r), 256) +
+           round_up(ds::build_ws_bytes(B, V), 256) + ds::sample_ws_bytes(B, max_len);
 }
 
 ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_args *a)
@@ -251,7 +320,8 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
     if (!a)
         return DS_EINVAL;
     const int B = a->B, T = a->T;
-    if (B <= 0 || T <= 0 || !a->max_rows || !a->budget || !a->u_draft || !a->token || !a->q)
+    if (B <= 0 || T <= 0 || !a->max_rows || !a->max_len || !a->budget || !a->u_draft ||
+        !a->token || !a->q)
         return DS_EINVAL;
     const size_t e = a->dtype == DS_BF16 ? 2 : 4;
     const int64_t ldh = (int64_t)(T + 1) * a->d;  // h is [B][T+1][d]
@@ -265,8 +335,15 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
                         a->logits);
     if (st != DS_OK)
         return st;
-    if (!a->cluster_of || !a->sl_off || !a->sl_ids || !a->ws || a->capacity < 0 ||
-        a->ws_bytes < ds_draft_chain_workspace_bytes(B, T, a->V, a->r) ||
+    int64_t len_bound = 0;
+    for (int t = 0; t < T; ++t) {
+        if (a->max_len[t] <= 0 || a->max_len[t] > (1 << 20))
+            return DS_ESHAPE;
+        len_bound = a->max_len[t] > len_bound ? a->max_len[t] : len_bound;
+    }
+    if (!a->cluster_of || !a->cluster_index || !a->sl_off || !a->sl_ids || !a->ws ||
+        a->capacity < 0 ||
+        a->ws_bytes < ds_draft_chain_workspace_bytes(B, T, a->V, a->r, len_bound) ||
         !aligned16(a->cluster_of))
         return DS_EINVAL;
     if (!(a->temperature >= 0.0f))
@@ -282,9 +359,11 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
 
     float *z = reinterpret_cast<float *>(a->ws);
     void *bws = reinterpret_cast<char *>(a->ws) + round_up(ds_router_workspace_bytes(B, a->r), 256);
-    if (g_events.ensure((size_t)T + 1) != hipSuccess)
+    void *sws = reinterpret_cast<char *>(bws) + round_up(ds::build_ws_bytes(B, a->V), 256);
+    // events: [0, T) router done, [T, 2T) head about to start, 2T fork
+    if (g_events.ensure(2 * (size_t)T + 1) != hipSuccess)
         return DS_EHIP;
-    hipEvent_t fork = g_events.ev[T];
+    hipEvent_t fork = g_events.ev[2 * T];
     const bool bf16 = a->dtype == DS_BF16;
     const char *hb = reinterpret_cast<const char *>(a->h);
     hipError_t err = hipEventRecord(fork, hs);
@@ -292,7 +371,10 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
         err = hipStreamWaitEvent(rs, fork, 0);
     for (int t = 0; t < T && err == hipSuccess; ++t) {
         const int64_t rb = (int64_t)t * B;
-        err = ds::router_launch(rs, bf16, B, a->d, a->r, a->M, a->act, hb + (size_t)t * a->d * e,
+        if (t > 0)  // H_{t-1} exists once the head of position t-1 may start
+            err = hipStreamWaitEvent(rs, g_events.ev[T + t - 1], 0);
+        if (err == hipSuccess)
+            err = ds::router_launch(rs, bf16, B, a->d, a->r, a->M, a->act, hb + (size_t)t * a->d * e,
                                 ldh, a->W1, a->b1, a->W2, a->b2, a->scores + rb * a->M, z);
         if (err == hipSuccess)
             err = ds::select_launch(rs, B, a->M, a->scores + rb * a->M, a->cluster_size,
@@ -300,12 +382,14 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
                                     a->n_sel + rb, a->sl_len + rb);
         if (err == hipSuccess)
             err = ds::build_launch(rs, B, a->M, a->V, a->sel + rb * a->M, a->n_sel + rb,
-                                   a->cluster_of, a->capacity, a->sl_off + rb, a->sl_ids,
-                                   a->err_flag, bws);
+                                   a->cluster_of, a->cluster_index, a->capacity, a->sl_off + rb,
+                                   a->sl_ids, a->err_flag, bws);
         if (err == hipSuccess)
             err = hipEventRecord(g_events.ev[t], rs);
         if (err == hipSuccess)
             err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
+        if (err == hipSuccess)
+            err = hipEventRecord(g_events.ev[T + t], hs);
         if (err == hipSuccess && a->head_events)
             err = hipEventRecord(a->head_events[2 * t], hs);
         if (err == hipSuccess)
@@ -316,9 +400,63 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
             err = hipEventRecord(a->head_events[2 * t + 1], hs);
         if (err == hipSuccess)
             err = ds::sample_launch(hs, B, 1, a->sl_off + rb, a->sl_ids, a->logits, a->temperature,
-                                    a->u_draft + rb, a->token + rb, a->q);
+                                    a->u_draft + rb, a->token + rb, a->q, a->max_len[t], sws);
     }
     return hip_status(err);
+}
+
+struct ds_graph_s {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+ds_status ds_capture_begin(hipStream_t s)
+{
+    if (!s)
+        return DS_EINVAL;  // the legacy default stream cannot be captured
+    return hip_status(hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed));
+}
+
+ds_status ds_capture_end(hipStream_t s, ds_graph *out)
+{
+    if (!s || !out)
+        return DS_EINVAL;
+    *out = nullptr;
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(s, &g);
+    if (e != hipSuccess || !g)
+        return DS_EHIP;
+    hipGraphExec_t x = nullptr;
+    e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        return DS_EHIP;
+    }
+    ds_graph h = new (std::nothrow) ds_graph_s{g, x};
+    if (!h) {
+        (void)hipGraphExecDestroy(x);
+        (void)hipGraphDestroy(g);
+        return DS_EHIP;
+    }
+    *out = h;
+    return DS_OK;
+}
+
+ds_status ds_graph_launch(ds_graph g, hipStream_t s)
+{
+    if (!g)
+        return DS_EINVAL;
+    return hip_status(hipGraphLaunch(g->exec, s));
+}
+
+ds_status ds_graph_destroy(ds_graph g)
+{
+    if (!g)
+        return DS_EINVAL;
+    hipError_t e1 = hipGraphExecDestroy(g->exec);
+    hipError_t e2 = hipGraphDestroy(g->graph);
+    delete g;
+    return (e1 == hipSuccess && e2 == hipSuccess) ? DS_OK : DS_EHIP;
 }
 
 }  // extern "C"

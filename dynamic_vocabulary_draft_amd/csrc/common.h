@@ -156,6 +156,10 @@ __device__ __forceinline__ void raise_flag(int32_t *flag, int32_t code)
         atomicMax(flag, code);
 }
 
+// Host-side: compute units of the current device (cached per device id; the
+// first call on a device queries the runtime).
+int device_cu_count();
+
 }  // namespace ds
 
 // Host-side: turn a launch error into a status.

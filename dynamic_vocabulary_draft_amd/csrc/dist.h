@@ -1,0 +1,235 @@
+// Chunked normalisation and inverse-CDF draws over long rows, shared by the
+// shortlist sampler, the target softmax and the verifier.  Not method
+// arithmetic of its own: this is how "normalise non-negative weights, then
+// take the first index whose running sum exceeds u * total" is spread over
+// many workgroups on gfx950 without any cross-workgroup wait.
+//
+// A row is cut into chunks of kChunk = 1024 elements; one 256-thread
+// workgroup owns a chunk, wave w its w-th 256-element sub-chunk, lane l its
+// four consecutive elements 4l..4l+3 (coalesced 16-byte accesses).  Two
+// launches, each with one workgroup per (chunk, row):
+//   1. chunk statistics: the chunk max m_c (and the first index holding
+//      it) and the chunk sum of the weights taken relative to m_c, in a
+//      fixed association (lane sums of four, wave inclusive scan, the four
+//      wave totals in order);
+//   2. every workgroup rebuilds the same row max M, the chunk sums rescaled
+//      to M (s_c * exp(m_c - M)), their prefix sums and the total (one
+//      wave, fixed order), writes its normalised chunk, and the one
+//      workgroup whose chunk holds the threshold walks it with weights
+//      taken relative to M.
+// The running sum at an element is: chunk prefix + earlier waves' totals +
+// earlier lanes' inclusive scan + this lane's partial sum.  If rounding
+// leaves no element past the threshold in that chunk, its last element with
+// non-zero mass is taken; if no chunk reaches the threshold, the last
+// element with non-zero mass of the row.  All sums have fixed association,
+// so results are reproducible bit for bit.
+#pragma once
+
+#include "common.h"
+
+namespace ds {
+
+constexpr int kChunk = 1024;
+constexpr int kChunkThreads = 256;
+
+// chunk statistics kept in a caller workspace: [rows][nchmax] of each
+struct ChunkWs {
+    float *cmax;
+    int *cidx;
+    double *csum;
+    double *csum2;  // second weight family (verify: plain p for the fallback)
+};
+
+__host__ __device__ inline size_t chunk_ws_bytes(int64_t rows, int64_t nchmax)
+{
+    return (size_t)rows * (size_t)nchmax * (8 + 8 + 4 + 4) + 256;
+}
+
+__host__ __device__ inline int64_t chunks_for(int64_t len) { return (len + kChunk - 1) / kChunk; }
+
+__host__ __device__ inline ChunkWs chunk_ws(void *ws, int64_t rows, int64_t nchmax)
+{
+    ChunkWs w;
+    char *p = reinterpret_cast<char *>(ws);
+    const size_t n = (size_t)rows * (size_t)nchmax;
+    w.csum = reinterpret_cast<double *>(p);
+    w.csum2 = reinterpret_cast<double *>(p + n * 8);
+    w.cmax = reinterpret_cast<float *>(p + n * 16);
+    w.cidx = reinterpret_cast<int *>(p + n * 20);
+    return w;
+}
+
+// Block (256 threads) max over a chunk and the first index attaining it.
+// `v[k]` is this lane's element 4l+k of wave w's sub-chunk (-inf if absent).
+__device__ inline void block_chunk_max(const float v[4], int64_t j0_lane, float *s_max, int *s_idx,
+                                       float *out_max, int *out_idx)
+{
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    float m = v[0];
+    int idx = 0;
+#pragma unroll
+    for (int k = 1; k < 4; ++k)
+        if (v[k] > m) {
+            m = v[k];
+            idx = k;
+        }
+    float wm = wave_max(m);
+    uint64_t bal = __ballot(m == wm);
+    int L = __ffsll((unsigned long long)bal) - 1;
+    int first = __shfl((int)(j0_lane + idx), L);
+    if (lane == 0) {
+        s_max[wave] = wm;
+        s_idx[wave] = first;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float bm = s_max[0];
+        int bi = s_idx[0];
+        for (int w = 1; w < (int)(blockDim.x >> 6); ++w)
+            if (s_max[w] > bm) {
+                bm = s_max[w];
+                bi = s_idx[w];
+            }
+        *out_max = bm;
+        *out_idx = bi;
+    }
+}
+
+// Sum of four fp64 weights per lane over the wave: returns the wave total;
+// *incl gets this lane's inclusive prefix (lane order).
+__device__ __forceinline__ double wave_chunk_sum(const double w[4], double *incl)
+{
+    double lv = ((w[0] + w[1]) + w[2]) + w[3];
+    *incl = wave_incl_scan_f64(lv);
+    return __shfl(*incl, kWave - 1);
+}
+
+// Row-wide chunk prefix sums (exclusive) into P[0..nch), the chunk sums into
+// S[0..nch) (both LDS) and the row total, computed by wave 0 in a fixed
+// order; call from all threads (barrier inside).
+__device__ inline double row_prefix(const double *__restrict__ csum, int nch, double *P, double *S,
+                                    double *s_total)
+{
+    if ((threadIdx.x >> 6) == 0) {
+        const int lane = lane_id();
+        double carry = 0.0;
+        for (int b = 0; b < nch; b += kWave) {
+            const int c = b + lane;
+            double v = c < nch ? csum[c] : 0.0;
+            double incl = wave_incl_scan_f64(v);
+            double ex = __shfl_up(incl, 1);
+            if (lane == 0)
+                ex = 0.0;
+            if (c < nch) {
+                P[c] = carry + ex;
+                S[c] = v;
+            }
+            carry += __shfl(incl, kWave - 1);
+        }
+        if (lane == 0)
+            *s_total = carry;
+    }
+    __syncthreads();
+    return *s_total;
+}
+
+// Which chunk owns the draw: the first with prefix + sum > thr; else (no
+// crossing) the last chunk with non-zero mass, flagged as a fallback (-1 if
+// none).  P and S in LDS; evaluated by wave 0 with ballots, 64 chunks per
+// step; the result goes to *s_owner / *s_fb after a barrier.
+__device__ inline void owner_chunk(const double *P, const double *S, int nch, double thr,
+                                   int *s_owner, int *s_fb)
+{
+    if ((threadIdx.x >> 6) == 0) {
+        const int lane = lane_id();
+        int owner = -1, fb = 0;
+        for (int b = 0; b < nch; b += kWave) {
+            const int c = b + lane;
+            const uint64_t bal = __ballot(c < nch && P[c] + S[c] > thr);
+            if (bal) {
+                owner = b + __ffsll((unsigned long long)bal) - 1;
+                break;
+            }
+        }
+        if (owner < 0) {
+            fb = 1;
+            for (int b = ((nch - 1) / kWave) * kWave; b >= 0; b -= kWave) {
+                const int c = b + lane;
+                const uint64_t bal = __ballot(c < nch && S[c] > 0.0);
+                if (bal) {
+                    owner = b + 63 - __clzll((long long)bal);
+                    break;
+                }
+            }
+        }
+        if (lane == 0) {
+            *s_owner = owner;
+            *s_fb = fb;
+        }
+    }
+    __syncthreads();
+}
+
+// Walk of the owning chunk by its workgroup.  w[4] are this lane's weights
+// (elements j0_lane..j0_lane+3), wtot[wave] the four wave totals of the
+// chunk (in LDS), Pc the chunk prefix.  Returns (to every thread) the
+// element index picked: first with non-zero mass whose running sum exceeds
+// thr, else (fallback or rounding) the last element with non-zero mass.
+__device__ inline int64_t chunk_walk(const double w[4], int64_t j0_lane, const double *wtot,
+                                     double incl, double Pc, double thr, bool fallback,
+                                     int64_t *s_pick)
+{
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    unsigned long long *sp = reinterpret_cast<unsigned long long *>(s_pick);
+    if (threadIdx.x == 0)
+        sp[0] = ~0ull, sp[1] = 0ull;  // first pick; last positive index + 1
+    __syncthreads();
+    double run = Pc;
+    for (int k = 0; k < wave; ++k)
+        run += wtot[k];
+    double prev = __shfl_up(incl, 1);
+    if (lane == 0)
+        prev = 0.0;
+    double pk = 0.0;
+    int64_t first = INT64_MAX, last = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        pk += w[k];
+        if (w[k] > 0.0) {
+            last = j0_lane + k;
+            if (first == INT64_MAX && !fallback && run + (prev + pk) > thr)
+                first = j0_lane + k;
+        }
+    }
+    if (first != INT64_MAX)
+        atomicMin(&sp[0], (unsigned long long)first);
+    if (last >= 0)
+        atomicMax(&sp[1], (unsigned long long)(last + 1));
+    __syncthreads();
+    return sp[0] != ~0ull ? (int64_t)sp[0] : (int64_t)sp[1] - 1;
+}
+
+// First index a in [0, len] with S[a] >= x for an ascending int32 array,
+// found by a whole wave in three dependent loads for len <= 64^3 (each
+// round samples 64 evenly spaced entries and keeps one gap).  For an array
+// that is not ascending the result is still within [0, len].
+__device__ inline int64_t wave_lower_bound(const int32_t *__restrict__ S, int64_t len, int32_t x)
+{
+    const int lane = lane_id();
+    int64_t lo = 0, hi = len;
+    while (hi - lo > kWave) {
+        const int64_t step = (hi - lo + kWave - 1) / kWave;
+        const int64_t idx = lo + (int64_t)lane * step;
+        const bool lt = idx < hi && S[idx] < x;
+        const int k = __popcll(__ballot(lt));
+        const int64_t nlo = k > 0 ? lo + (int64_t)(k - 1) * step + 1 : lo;
+        const int64_t nhi = min(hi, lo + (int64_t)k * step);
+        lo = nlo;
+        hi = nhi;
+    }
+    const int64_t idx = lo + lane;
+    const bool lt = idx < hi && S[idx] < x;
+    return lo + __popcll(__ballot(lt));
+}
+
+}  // namespace ds

@@ -10,7 +10,8 @@
 // token's whole W row with 16-byte loads per lane (64 lanes x 16 B = 1 KB
 // contiguous per load instruction, KC instructions per row), all RPW rows
 // issued before any arithmetic so that RPW*d*e bytes per wave are in
-// flight.  The hidden vector of the entry's group is held in registers in
+// flight; the grid is capped at two workgroups per compute unit and strides
+// over the entries.  The hidden vector of the entry's group is held in registers in
 // the same lane layout and reloaded only when the group changes.  Products
 // use v_dot2_f32_bf16 (bf16 pairs, fp32 accumulation); the lane partials are
 // reduced with a fixed DPP order, so the result is reproducible bit for bit.
@@ -141,9 +142,18 @@ hipError_t launch_kc(hipStream_t s, int V, int nch, const void *W, int G, int m,
 {
     constexpr int RPW = (KC >= 8) ? 2 : 4;
     const int64_t waves = (max_rows + RPW - 1) / RPW;
-    const int64_t blocks = (waves + 3) / 4;
+    int64_t blocks = (waves + 3) / 4;
     if (blocks <= 0)
         return hipSuccess;
+    // At most kBlocksPerCU resident workgroups per compute unit: enough
+    // bytes in flight to saturate HBM, while half of each CU's wave slots
+    // stay free so kernels on other streams (the router of the next draft
+    // position) start at once instead of queueing behind thousands of
+    // pending head workgroups.  The grid-stride loop covers the rest.
+    constexpr int kBlocksPerCU = 2;
+    const int64_t cap = (int64_t)kBlocksPerCU * device_cu_count();
+    if (blocks > cap)
+        blocks = cap;
     hipLaunchKernelGGL((head_gemv_kernel<BF16, KC, RPW>), dim3((unsigned)blocks), dim3(256), 0, s,
                        V, nch, reinterpret_cast<const u32x4 *>(W), G, m,
                        reinterpret_cast<const u32x4 *>(h), ldh_g_ch, sl_off, sl_ids, logits);

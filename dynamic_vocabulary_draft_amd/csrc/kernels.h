@@ -15,26 +15,33 @@ hipError_t select_launch(hipStream_t s, int n, int M, const float *scores,
                          const int32_t *cluster_size, int kind, const int32_t *budget,
                          int32_t *sel, int32_t *n_sel, int32_t *sl_len);
 
-// build: chunk counts + last-block scan, then compaction
+// build: per-cluster chunk-prefix index (built once), then compaction
 constexpr int kBuildChunk = 4096;  // tokens per workgroup
+size_t index_bytes(int M, int V);
+hipError_t index_launch(hipStream_t s, int M, int V, const int32_t *cluster_of, int32_t *index,
+                        int32_t *err_flag);
 size_t build_ws_bytes(int n, int V);
 hipError_t build_launch(hipStream_t s, int n, int M, int V, const int32_t *sel,
-                        const int32_t *n_sel, const int32_t *cluster_of, int64_t capacity,
-                        int64_t *sl_off, int32_t *sl_ids, int32_t *err_flag, void *ws);
+                        const int32_t *n_sel, const int32_t *cluster_of, const int32_t *index,
+                        int64_t capacity, int64_t *sl_off, int32_t *sl_ids, int32_t *err_flag,
+                        void *ws);
 
 hipError_t head_launch(hipStream_t s, bool bf16, int V, int d, const void *W, int G, int m,
                        const void *h, int64_t ldh_g, const int64_t *sl_off,
                        const int32_t *sl_ids, int64_t max_rows, float *logits);
 
+size_t sample_ws_bytes(int64_t rows, int64_t max_len);
 hipError_t sample_launch(hipStream_t s, int G, int m, const int64_t *sl_off,
                          const int32_t *sl_ids, const float *logits, float temperature,
-                         const float *u, int32_t *token, float *q);
+                         const float *u, int32_t *token, float *q, int64_t max_len, void *ws);
 
-hipError_t softmax_launch(hipStream_t s, int rows, int V, const float *logits, float *p);
+size_t softmax_ws_bytes(int64_t rows, int64_t V);
+hipError_t softmax_launch(hipStream_t s, int rows, int V, const float *logits, float *p, void *ws);
 
+size_t verify_ws_bytes(int B, int T, int V);
 hipError_t verify_launch(hipStream_t s, int B, int T, int V, const int32_t *draft,
                          const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                          const float *p, const float *u_acc, const float *u_fin, int32_t *n_acc,
-                         int32_t *out);
+                         int32_t *out, void *ws);
 
 }  // namespace ds

@@ -5,11 +5,12 @@
 //
 // Both layers are small-n matrix-vector products against weights that are
 // read once from HBM (8 MB + 2 MB bf16 for the Llama-shaped router), so
-// each is a tiled GEMV: a wave owns NR weight rows and XB input rows, walks
-// the reduction dimension in 16-byte chunks per lane (coalesced 1 KB per
-// wave per load), and reduces its NR*XB partial sums across the wave with a
-// fixed DPP order.  Bias and activation are fused into the epilogue; the
-// hidden activations z stay fp32.
+// each is a GEMV: a wave owns one weight row and up to 8 input rows, holds
+// the whole weight row in registers (16-byte loads per lane, 1 KB per wave
+// per load instruction, all issued at once), and reduces each partial sum
+// across the wave with a fixed DPP order.  Bias and activation are fused
+// into the epilogue; the hidden activations z stay fp32.  Weight rows are
+// limited to 8192 elements (KC <= 16 chunks of 8 per lane).
 #include "common.h"
 #include "kernels.h"
 
@@ -60,84 +61,108 @@ __device__ __forceinline__ float load_scalar(const void *p, int idx, bool bf16)
 }
 
 // Y[row][o] = act(sum_k A[o][k] X[row][k] + bias[o]) for o < R, row < n.
-template <bool A_BF16, bool X_BF16, int NR, int XB>
-__global__ __launch_bounds__(256) void gemv_tile_kernel(int n, int K, int R, const void *__restrict__ A,
+// One wave per weight row o; lane l owns the 8-element chunks l, l+64, ...
+// (KC of them).  Every weight chunk is loaded before any arithmetic, so a
+// wave keeps a whole row (8 KB at d = 4096 bf16) in flight; the XB input
+// rows are then read chunk by chunk (L1/L2-resident, shared by all waves).
+template <bool A_BF16, bool X_BF16, int KC, int XB>
+__global__ __launch_bounds__(256) void gemv_rows_kernel(int n, int K, int R, const void *__restrict__ A,
                                                         const void *__restrict__ bias,
                                                         const void *__restrict__ X, int64_t ldx,
                                                         int act, float *__restrict__ Y, int64_t ldy)
 {
     const int lane = lane_id();
-    const int wave = uniform(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
-    const int o0 = wave * NR;
+    const int o = uniform(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
     const int x0 = uniform(blockIdx.y * XB);
-    if (o0 >= R)
+    if (o >= R)
         return;
-    const int nr = min(NR, R - o0), nx = min(XB, n - x0);
     const int nch = K >> 3;
-    float acc[NR][XB];
+    Chunk8<A_BF16> a[KC];
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
+    for (int k = 0; k < KC; ++k) {
+        const int c = lane + k * kWave;
+        if (c < nch)
+            a[k].load(A, (int64_t)o * K + c * 8);
+    }
+    float acc[XB];
 #pragma unroll
-        for (int x = 0; x < XB; ++x)
-            acc[r][x] = 0.f;
-
-    for (int c = lane; c < nch; c += kWave) {
-        float a[NR][8];
+    for (int x = 0; x < XB; ++x)
+        acc[x] = 0.f;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            Chunk8<A_BF16> ch;
-            if (r < nr) {
-                ch.load(A, (int64_t)(o0 + r) * K + c * 8);
-                ch.unpack(a[r]);
+    for (int k = 0; k < KC; ++k) {
+        const int c = lane + k * kWave;
+        if (c >= nch)
+            break;
+        float av[8];
+        if constexpr (!(A_BF16 && X_BF16))
+            a[k].unpack(av);
+#pragma unroll
+        for (int x = 0; x < XB; ++x) {
+            if (x0 + x >= n)
+                break;
+            Chunk8<X_BF16> xc;
+            xc.load(X, (int64_t)(x0 + x) * ldx + c * 8);
+            if constexpr (A_BF16 && X_BF16) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[x] = dot2_bf16(a[k].v[e], xc.v[e], acc[x]);
             } else {
+                float xv[8];
+                xc.unpack(xv);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    a[r][e] = 0.f;
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < XB; ++x) {
-            if (x < nx) {
-                Chunk8<X_BF16> ch;
-                ch.load(X, (int64_t)(x0 + x) * ldx + c * 8);
-                float xv[8];
-                ch.unpack(xv);
-#pragma unroll
-                for (int r = 0; r < NR; ++r)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[r][x] = fmaf(a[r][e], xv[e], acc[r][x]);
+                    acc[x] = fmaf(av[e], xv[e], acc[x]);
             }
         }
     }
+    const float bv = bias ? load_scalar(bias, o, A_BF16) : 0.f;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-#pragma unroll
-        for (int x = 0; x < XB; ++x) {
-            float s = wave_sum(acc[r][x]);
-            if (r < nr && x < nx && lane == ((r * XB + x) & (kWave - 1))) {
-                if (bias)
-                    s += load_scalar(bias, o0 + r, A_BF16);
-                if (act == DS_RELU + 1)       // layer-1 ReLU
-                    s = fmaxf(s, 0.f);
-                else if (act == DS_SILU + 1)  // layer-1 SiLU
-                    s = s / (1.f + expf(-s));
-                Y[(int64_t)(x0 + x) * ldy + o0 + r] = s;
-            }
+    for (int x = 0; x < XB; ++x) {
+        float s = wave_sum(acc[x]);
+        if (x0 + x < n && lane == 0) {
+            s += bv;
+            if (act == DS_RELU + 1)       // layer-1 ReLU
+                s = fmaxf(s, 0.f);
+            else if (act == DS_SILU + 1)  // layer-1 SiLU
+                s = s / (1.f + expf(-s));
+            Y[(int64_t)(x0 + x) * ldy + o] = s;
         }
     }
+}
+
+template <bool A_BF16, bool X_BF16, int KC>
+hipError_t launch_kc(hipStream_t s, int n, int K, int R, const void *A, const void *bias,
+                     const void *X, int64_t ldx, int act, float *Y, int64_t ldy)
+{
+    dim3 block(256);
+    if (n == 1) {
+        hipLaunchKernelGGL((gemv_rows_kernel<A_BF16, X_BF16, KC, 1>), dim3((R + 3) / 4, 1), block,
+                           0, s, n, K, R, A, bias, X, ldx, act, Y, ldy);
+    } else if (n <= 4) {
+        hipLaunchKernelGGL((gemv_rows_kernel<A_BF16, X_BF16, KC, 4>), dim3((R + 3) / 4, 1), block,
+                           0, s, n, K, R, A, bias, X, ldx, act, Y, ldy);
+    } else {
+        hipLaunchKernelGGL((gemv_rows_kernel<A_BF16, X_BF16, KC, 8>),
+                           dim3((R + 3) / 4, (n + 7) / 8), block, 0, s, n, K, R, A, bias, X, ldx,
+                           act, Y, ldy);
+    }
+    return hipGetLastError();
 }
 
 template <bool A_BF16, bool X_BF16>
 hipError_t launch_gemv(hipStream_t s, int n, int K, int R, const void *A, const void *bias,
                        const void *X, int64_t ldx, int act, float *Y, int64_t ldy)
 {
-    constexpr int NR = 2, XB = 4;
-    const int waves = (R + NR - 1) / NR;
-    dim3 grid((waves + 3) / 4, (n + XB - 1) / XB);
-    hipLaunchKernelGGL((gemv_tile_kernel<A_BF16, X_BF16, NR, XB>), grid, dim3(256), 0, s, n, K, R,
-                       A, bias, X, ldx, act, Y, ldy);
-    return hipGetLastError();
+    const int kc = ((K >> 3) + kWave - 1) / kWave;
+    if (kc <= 1)
+        return launch_kc<A_BF16, X_BF16, 1>(s, n, K, R, A, bias, X, ldx, act, Y, ldy);
+    if (kc <= 2)
+        return launch_kc<A_BF16, X_BF16, 2>(s, n, K, R, A, bias, X, ldx, act, Y, ldy);
+    if (kc <= 4)
+        return launch_kc<A_BF16, X_BF16, 4>(s, n, K, R, A, bias, X, ldx, act, Y, ldy);
+    if (kc <= 8)
+        return launch_kc<A_BF16, X_BF16, 8>(s, n, K, R, A, bias, X, ldx, act, Y, ldy);
+    return launch_kc<A_BF16, X_BF16, 16>(s, n, K, R, A, bias, X, ldx, act, Y, ldy);
 }
 
 }  // namespace

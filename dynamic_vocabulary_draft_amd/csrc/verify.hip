@@ -1,216 +1,239 @@
-// Target side of the speculative step: full-vocabulary target distribution
-// and rejection-sampling verification, which keeps the emitted tokens
-// distributed exactly as the target (DynaSpec abstract: "the target model
-// still verifies over the full vocabulary, preserving exactness"; summary
-// page, "Pipeline Flow: Rejection Sampling Verification"; the accept /
-// residual / bonus rules are textbook speculative sampling).
+// Rejection-sampling verification over the full vocabulary, which keeps the
+// emitted tokens distributed exactly as the target (DynaSpec abstract: "the
+// target model still verifies over the full vocabulary, preserving
+// exactness"; summary page, "Pipeline Flow: Rejection Sampling
+// Verification"; the accept / residual / bonus rules are textbook
+// speculative sampling).
 //
-// softmax: one workgroup per row, three coalesced passes (fp32 max, fp64 sum
-// of exp(l - max) with a fixed reduction order, fp32 write of the ratio).
-//
-// verify: one workgroup per sequence.  Wave 0 evaluates the T accept tests
-// at once (lane t: binary search of the draft token in its ascending
-// shortlist, exact fp64 product u*q against p) and finds the first
-// rejection with a ballot.  The draw then scans all V tokens once through
-// the block inverse CDF: for a rejection the weights are max(0, p - q),
-// where q is scattered chunk by chunk into per-wave LDS from the shortlist
-// (a table of chunk starts, built in one pass over the shortlist, says
-// which entries fall in each 256-token chunk); otherwise the weights are
-// the bonus position's p.
+// Two launches, one workgroup per (1024-token chunk of V, sequence):
+//   sum:    the workgroup's four waves run the T accept tests (the draft
+//           token is found in its ascending shortlist with a three-round
+//           wave search; the exact fp64 test u*q < p) and take the first
+//           rejected position t*; for a rejection the chunk's residual
+//           weights max(0, p - q) (q of the shortlist entries inside the
+//           chunk scattered into LDS) and the plain p weights are summed;
+//           after T acceptances the bonus position's p is summed;
+//   final:  every workgroup rebuilds the same prefixes and total (the
+//           residual, or p when the residual has no mass); the owner of the
+//           threshold u_fin * total walks its chunk and writes the drawn
+//           token; chunk 0 writes the accepted tokens, -1 padding and n_acc.
 #include <float.h>
 
-#include "cdf.h"
 #include "common.h"
+#include "dist.h"
 #include "kernels.h"
 
 namespace ds {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kMaxSub = 4096;  // 256-token chunks of V in the start table
+constexpr int kMaxVChunks = 1024;  // V up to 2^20
 
-struct ProbWeights {
-    const float *p;
-    int64_t V;
-    __device__ void operator()(int64_t j0, double w[4]) const
-    {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            w[k] = j0 + k < V ? (double)p[j0 + k] : 0.0;
-    }
+struct VerifyWs {
+    ChunkWs ch;
+    int32_t *tstar;  // [B]: first rejected position (T if none)
 };
 
-struct ResidualWeights {
-    const float *p;       // target probabilities of the rejected position
-    const int32_t *S;     // its shortlist (ascending token ids)
-    const float *q;       // draft probabilities aligned with S
-    const int *start;     // LDS: first shortlist entry of every 256-token chunk
-    float *qbuf;          // LDS: 256 floats per wave
-    int64_t V;
-    __device__ void operator()(int64_t j0, double w[4]) const
-    {
-        const int lane = lane_id();
-        const int64_t base = j0 - lane * 4;
-        const int sc = (int)(base >> 8);
-        float *buf = qbuf + (threadIdx.x >> 6) * 256;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            buf[lane * 4 + k] = 0.f;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int e = start[sc] + lane; e < start[sc + 1]; e += kWave) {
-            const int64_t off = (int64_t)S[e] - base;
-            if (off >= 0 && off < 256)
-                buf[off] = q[e];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int64_t y = j0 + k;
-            double r = y < V ? (double)p[y] - (double)buf[lane * 4 + k] : 0.0;
-            w[k] = r > 0.0 ? r : 0.0;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-};
-
-__global__ __launch_bounds__(kThreads) void softmax_kernel(int V, const float *__restrict__ logits,
-                                                           float *__restrict__ p)
+__host__ __device__ inline VerifyWs verify_ws(void *ws, int B, int64_t nchV)
 {
-    __shared__ float shf[kThreads / kWave];
-    __shared__ double shd[kThreads / kWave];
-    const int64_t row = blockIdx.x;
-    const float *l = logits + row * V;
-    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    float mx = -FLT_MAX;
-    for (int y = threadIdx.x; y < V; y += blockDim.x)
-        mx = fmaxf(mx, l[y]);
-    mx = wave_max(mx);
-    if (lane_id() == 0)
-        shf[wave] = mx;
-    __syncthreads();
-    mx = shf[0];
-    for (int i = 1; i < nw; ++i)
-        mx = fmaxf(mx, shf[i]);
-    const double dmx = (double)mx;
-    double z = 0.0;
-    for (int y = threadIdx.x; y < V; y += blockDim.x)
-        z += exp((double)l[y] - dmx);
-    z = wave_sum_f64(z);
-    if (lane_id() == 0)
-        shd[wave] = z;
-    __syncthreads();
-    double Z = shd[0];
-    for (int i = 1; i < nw; ++i)
-        Z += shd[i];
-    for (int y = threadIdx.x; y < V; y += blockDim.x)
-        p[row * V + y] = (float)(exp((double)l[y] - dmx) / Z);
+    VerifyWs w;
+    w.ch = chunk_ws(ws, B, nchV);
+    w.tstar = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ws) + chunk_ws_bytes(B, nchV));
+    return w;
 }
 
-__global__ __launch_bounds__(kThreads) void verify_kernel(int B, int T, int V,
-                                                          const int32_t *__restrict__ draft,
-                                                          const int64_t *__restrict__ sl_off,
-                                                          const int32_t *__restrict__ sl_ids,
-                                                          const float *__restrict__ q,
-                                                          const float *__restrict__ p,
-                                                          const float *__restrict__ u_acc,
-                                                          const float *__restrict__ u_fin,
-                                                          int32_t *__restrict__ n_acc,
-                                                          int32_t *__restrict__ out)
+// The T accept tests of sequence b, split over the workgroup's waves; returns
+// (to every thread) the first rejected position, T if all are accepted.
+__device__ int first_rejection(int B, int T, int V, int b, const int32_t *__restrict__ draft,
+                               const int64_t *__restrict__ sl_off,
+                               const int32_t *__restrict__ sl_ids, const float *__restrict__ q,
+                               const float *__restrict__ p, const float *__restrict__ u_acc,
+                               int *s_rej)
 {
-    __shared__ double sh[kCdfShDoubles];
-    __shared__ int start[kMaxSub + 1];
-    __shared__ float qbuf[(kThreads / kWave) * 256];
-    __shared__ int s_int[2];
-    __shared__ int s_tstar;
-    const int b = blockIdx.x, lane = lane_id(), wave = threadIdx.x >> 6;
-
-    if (wave == 0) {
-        bool reject = false;
-        if (lane < T) {
-            const int64_t row = (int64_t)lane * B + b;
-            const int32_t x = draft[row];
-            int64_t lo = sl_off[row], hi = sl_off[row + 1];
-            while (lo < hi) {  // lower_bound of x in the ascending shortlist
-                int64_t mid = (lo + hi) >> 1;
-                if (sl_ids[mid] < x)
-                    lo = mid + 1;
-                else
-                    hi = mid;
-            }
-            const bool found = lo < sl_off[row + 1] && sl_ids[lo] == x;
-            const double qx = found ? (double)q[lo] : 0.0;
-            const double px = (x >= 0 && x < V) ? (double)p[((int64_t)b * (T + 1) + lane) * V + x] : 0.0;
-            reject = !((double)u_acc[row] * qx < px);
-        }
-        uint64_t bal = __ballot(reject);
-        const int tstar = bal ? __ffsll((unsigned long long)bal) - 1 : T;
-        if (lane == 0)
-            s_tstar = tstar;
-        for (int k = lane; k <= T; k += kWave)
-            if (k != tstar)  // entry tstar is written once the draw is known
-                out[(int64_t)b * (T + 1) + k] = k < tstar ? draft[(int64_t)k * B + b] : -1;
-        if (lane == 0)
-            n_acc[b] = tstar;
+    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if (threadIdx.x == 0)
+        *s_rej = T;
+    __syncthreads();
+    for (int t = wave; t < T; t += nw) {
+        const int64_t row = (int64_t)t * B + b;
+        const int32_t x = draft[row];
+        const int64_t lo = sl_off[row], len = sl_off[row + 1] - lo;
+        const int64_t j = wave_lower_bound(sl_ids + lo, len, x);
+        const bool found = j < len && sl_ids[lo + j] == x;
+        const double qx = found ? (double)q[lo + j] : 0.0;
+        const double px = (x >= 0 && x < V) ? (double)p[((int64_t)b * (T + 1) + t) * V + x] : 0.0;
+        if (lane_id() == 0 && !((double)u_acc[row] * qx < px))
+            atomicMin(s_rej, t);
     }
     __syncthreads();
-    const int tstar = s_tstar;
-    const double uf = (double)u_fin[b];
-    const float *pt = p + ((int64_t)b * (T + 1) + tstar) * V;
-    int64_t pick;
-    double total;
-    if (tstar < T) {
-        const int64_t row = (int64_t)tstar * B + b;
-        const int64_t lo = sl_off[row], len = sl_off[row + 1] - lo;
-        const int32_t *S = sl_ids + lo;
-        const int nsub = (V + 255) >> 8;
-        // start[c] = first shortlist entry with token id >= 256*c.  Every
-        // entry is preset to len so the table stays within [0, len] even if
-        // the shortlist is not ascending (invalid input).
-        for (int c = threadIdx.x; c <= nsub; c += blockDim.x)
-            start[c] = (int)len;
-        __syncthreads();
-        for (int64_t e = threadIdx.x; e < len; e += blockDim.x) {
-            const int cy = S[e] >> 8;
-            const int cp = e > 0 ? (S[e - 1] >> 8) : -1;
-            for (int c = cp + 1 > 0 ? cp + 1 : 0; c <= cy && c <= nsub; ++c)
-                start[c] = (int)e;
+    return *s_rej;
+}
+
+// The chunk's q values (shortlist entries with token ids in [base, base+1024))
+// scattered into a dense LDS array; returns after a barrier.
+__device__ void scatter_q(const int32_t *__restrict__ S, const float *__restrict__ qrow,
+                          int64_t len, int64_t base, float *qd, int64_t *s_rng)
+{
+    for (int i = threadIdx.x; i < kChunk; i += blockDim.x)
+        qd[i] = 0.0f;
+    if ((threadIdx.x >> 6) == 0) {
+        const int64_t a = wave_lower_bound(S, len, (int32_t)base);
+        const int64_t e = wave_lower_bound(S, len, (int32_t)min(base + kChunk, (int64_t)INT32_MAX));
+        if (lane_id() == 0) {
+            s_rng[0] = a;
+            s_rng[1] = e;
         }
-        __syncthreads();
-        ResidualWeights rw{pt, S, q + lo, start, qbuf, V};
-        pick = block_inverse_cdf(rw, V, uf, sh, s_int, &total);
-        if (!(total > 0.0)) {
-            ProbWeights pw{pt, V};
-            pick = block_inverse_cdf(pw, V, uf, sh, s_int, &total);
-        }
-    } else {
-        ProbWeights pw{pt, V};
-        pick = block_inverse_cdf(pw, V, uf, sh, s_int, &total);
     }
+    __syncthreads();
+    for (int64_t k = s_rng[0] + threadIdx.x; k < s_rng[1]; k += blockDim.x) {
+        const int64_t o = (int64_t)S[k] - base;
+        if (o >= 0 && o < kChunk)
+            qd[o] = qrow[k];
+    }
+    __syncthreads();
+}
+
+// weights of this lane's four tokens: family 0 = residual (or bonus p),
+// family 1 = plain p of the rejected position
+__device__ __forceinline__ void lane_weights(const float *__restrict__ pt, int64_t y0, int V,
+                                             const float *qd, int64_t local0, bool resid,
+                                             double w0[4], double w1[4])
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t y = y0 + k;
+        const double pv = y < V ? (double)pt[y] : 0.0;
+        w1[k] = pv;
+        if (resid) {
+            const double r = y < V ? pv - (double)qd[local0 + k] : 0.0;
+            w0[k] = r > 0.0 ? r : 0.0;
+        } else {
+            w0[k] = pv;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kChunkThreads) void verify_sum_kernel(
+    int B, int T, int V, const int32_t *__restrict__ draft, const int64_t *__restrict__ sl_off,
+    const int32_t *__restrict__ sl_ids, const float *__restrict__ q, const float *__restrict__ p,
+    const float *__restrict__ u_acc, int64_t nchV, void *ws)
+{
+    __shared__ float qd[kChunk];
+    __shared__ int64_t s_rng[2];
+    __shared__ double s_w0[4], s_w1[4];
+    __shared__ int s_rej;
+    const int b = blockIdx.y;
+    const int64_t c = blockIdx.x;
+    VerifyWs w = verify_ws(ws, B, nchV);
+    const int tstar = first_rejection(B, T, V, b, draft, sl_off, sl_ids, q, p, u_acc, &s_rej);
+    if (c == 0 && threadIdx.x == 0)
+        w.tstar[b] = tstar;
+    const float *pt = p + ((int64_t)b * (T + 1) + tstar) * V;
+    const bool resid = tstar < T;
+    const int64_t base = c * kChunk;
+    if (resid) {
+        const int64_t row = (int64_t)tstar * B + b;
+        const int64_t lo = sl_off[row];
+        scatter_q(sl_ids + lo, q + lo, sl_off[row + 1] - lo, base, qd, s_rng);
+    }
+    const int64_t local0 = (threadIdx.x >> 6) * 256 + lane_id() * 4;
+    double w0[4], w1[4];
+    lane_weights(pt, base + local0, V, qd, local0, resid, w0, w1);
+    double i0, i1;
+    double t0 = wave_chunk_sum(w0, &i0), t1 = wave_chunk_sum(w1, &i1);
+    if (lane_id() == 0) {
+        s_w0[threadIdx.x >> 6] = t0;
+        s_w1[threadIdx.x >> 6] = t1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        w.ch.csum[(int64_t)b * nchV + c] = ((s_w0[0] + s_w0[1]) + s_w0[2]) + s_w0[3];
+        w.ch.csum2[(int64_t)b * nchV + c] = ((s_w1[0] + s_w1[1]) + s_w1[2]) + s_w1[3];
+    }
+}
+
+__global__ __launch_bounds__(kChunkThreads) void verify_final_kernel(
+    int B, int T, int V, const int32_t *__restrict__ draft, const int64_t *__restrict__ sl_off,
+    const int32_t *__restrict__ sl_ids, const float *__restrict__ q, const float *__restrict__ p,
+    const float *__restrict__ u_fin, int64_t nchV, const void *ws, int32_t *__restrict__ n_acc,
+    int32_t *__restrict__ out)
+{
+    __shared__ double P[kMaxVChunks], S[kMaxVChunks];
+    __shared__ float qd[kChunk];
+    __shared__ int64_t s_rng[2];
+    __shared__ double s_wt[4];
+    __shared__ double s_total;
+    __shared__ int s_owner, s_fallback;
+    __shared__ int64_t s_pick[2];
+    const int b = blockIdx.y;
+    const int64_t c = blockIdx.x;
+    VerifyWs w = verify_ws(const_cast<void *>(ws), B, nchV);
+    const int tstar = w.tstar[b];
+    const int nch = (int)nchV;
+    const double *cs0 = w.ch.csum + (int64_t)b * nchV;
+    const double *cs1 = w.ch.csum2 + (int64_t)b * nchV;
+    const bool resid = tstar < T;
+    double Z = row_prefix(cs0, nch, P, S, &s_total);
+    bool use_p = false;
+    if (resid && !(Z > 0.0)) {  // residual without mass: draw from p_t itself
+        use_p = true;
+        __syncthreads();
+        Z = row_prefix(cs1, nch, P, S, &s_total);
+    }
+    const double thr = (double)u_fin[b] * Z;
+    owner_chunk(P, S, nch, thr, &s_owner, &s_fallback);
+    int32_t *ob = out + (int64_t)b * (T + 1);
+    if (c == 0) {
+        for (int k = threadIdx.x; k <= T; k += blockDim.x)
+            if (k != tstar || s_owner < 0)
+                ob[k] = k < tstar ? draft[(int64_t)k * B + b] : -1;
+        if (threadIdx.x == 0)
+            n_acc[b] = tstar;
+    }
+    if (c != s_owner)
+        return;
+    const float *pt = p + ((int64_t)b * (T + 1) + tstar) * V;
+    const int64_t base = c * kChunk;
+    if (resid && !use_p) {
+        const int64_t row = (int64_t)tstar * B + b;
+        const int64_t lo = sl_off[row];
+        scatter_q(sl_ids + lo, q + lo, sl_off[row + 1] - lo, base, qd, s_rng);
+    }
+    const int64_t local0 = (threadIdx.x >> 6) * 256 + lane_id() * 4;
+    double w0[4], w1[4];
+    lane_weights(pt, base + local0, V, qd, local0, resid && !use_p, w0, w1);
+    double incl;
+    double tot = wave_chunk_sum(w0, &incl);
+    if (lane_id() == 0)
+        s_wt[threadIdx.x >> 6] = tot;
+    __syncthreads();
+    const int64_t pick = chunk_walk(w0, base + local0, s_wt, incl, P[c], thr, s_fallback != 0,
+                                    s_pick);
     if (threadIdx.x == 0)
-        out[(int64_t)b * (T + 1) + tstar] = (int32_t)pick;
+        ob[tstar] = (int32_t)pick;
 }
 
 }  // namespace
 
-hipError_t softmax_launch(hipStream_t s, int rows, int V, const float *logits, float *p)
+size_t verify_ws_bytes(int B, int T, int V)
 {
-    hipLaunchKernelGGL(softmax_kernel, dim3(rows), dim3(kThreads), 0, s, V, logits, p);
-    return hipGetLastError();
+    (void)T;
+    return chunk_ws_bytes(B, chunks_for(V)) + (size_t)B * sizeof(int32_t) + 256;
 }
 
 hipError_t verify_launch(hipStream_t s, int B, int T, int V, const int32_t *draft,
                          const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                          const float *p, const float *u_acc, const float *u_fin, int32_t *n_acc,
-                         int32_t *out)
+                         int32_t *out, void *ws)
 {
-    hipLaunchKernelGGL(verify_kernel, dim3(B), dim3(kThreads), 0, s, B, T, V, draft, sl_off,
-                       sl_ids, q, p, u_acc, u_fin, n_acc, out);
+    const int64_t nchV = chunks_for(V);
+    dim3 grid((unsigned)nchV, (unsigned)B);
+    hipLaunchKernelGGL(verify_sum_kernel, grid, dim3(kChunkThreads), 0, s, B, T, V, draft, sl_off,
+                       sl_ids, q, p, u_acc, nchV, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(verify_final_kernel, grid, dim3(kChunkThreads), 0, s, B, T, V, draft,
+                       sl_off, sl_ids, q, p, u_fin, nchV, (const void *)ws, n_acc, out);
     return hipGetLastError();
 }
 

@@ -35,8 +35,9 @@ class ChainArgs(C.Structure):
     _fields_ = [("B", _i), ("T", _i), ("V", _i), ("d", _i), ("r", _i), ("M", _i),
                 ("dtype", _i), ("act", _i), ("budget_kind", _i), ("temperature", _f),
                 ("W", _vp), ("W1", _vp), ("b1", _vp), ("W2", _vp), ("b2", _vp),
-                ("cluster_of", _vp), ("cluster_size", _vp), ("h", _vp), ("budget", _vp),
-                ("u_draft", _vp), ("capacity", _i64), ("max_rows", _vp),
+                ("cluster_of", _vp), ("cluster_index", _vp), ("cluster_size", _vp), ("h", _vp),
+                ("budget", _vp),
+                ("u_draft", _vp), ("capacity", _i64), ("max_rows", _vp), ("max_len", _vp),
                 ("scores", _vp), ("sel", _vp), ("n_sel", _vp), ("sl_len", _vp),
                 ("sl_off", _vp), ("sl_ids", _vp), ("logits", _vp), ("q", _vp),
                 ("token", _vp), ("err_flag", _vp), ("ws", _vp), ("ws_bytes", _sz),
@@ -50,14 +51,25 @@ _SIGS = {
     "ds_router_score": (_i, [_vp, _i, _i, _i, _i, _i, _i, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
                              _vp, _sz]),
     "ds_select_clusters": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp]),
+    "ds_cluster_index_bytes": (_sz, [_i, _i]),
+    "ds_cluster_index": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "ds_build_workspace_bytes": (_sz, [_i, _i]),
-    "ds_build_shortlist": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz]),
+    "ds_build_shortlist": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
+                                _sz]),
     "ds_gathered_lm_head": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i64, _vp, _vp, _i64, _vp]),
-    "ds_shortlist_sample": (_i, [_vp, _i, _i, _vp, _vp, _vp, _f, _vp, _vp, _vp]),
-    "ds_target_softmax": (_i, [_vp, _i, _i, _vp, _vp]),
-    "ds_verify_reject": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "ds_draft_chain_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "ds_sample_workspace_bytes": (_sz, [_i, _i, _i64]),
+    "ds_shortlist_sample": (_i, [_vp, _i, _i, _vp, _vp, _vp, _f, _vp, _i64, _vp, _vp, _vp, _sz]),
+    "ds_softmax_workspace_bytes": (_sz, [_i, _i]),
+    "ds_target_softmax": (_i, [_vp, _i, _i, _vp, _vp, _vp, _sz]),
+    "ds_verify_workspace_bytes": (_sz, [_i, _i, _i]),
+    "ds_verify_reject": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _sz]),
+    "ds_draft_chain_workspace_bytes": (_sz, [_i, _i, _i, _i, _i64]),
     "ds_draft_chain": (_i, [_vp, _vp, C.POINTER(ChainArgs)]),
+    "ds_capture_begin": (_i, [_vp]),
+    "ds_capture_end": (_i, [_vp, C.POINTER(_vp)]),
+    "ds_graph_launch": (_i, [_vp, _vp]),
+    "ds_graph_destroy": (_i, [_vp]),
 }
 
 SYMBOLS = tuple(_SIGS)
@@ -123,8 +135,29 @@ def build_workspace_bytes(n: int, V: int) -> int:
     return int(lib.ds_build_workspace_bytes(n, V))
 
 
-def draft_chain_workspace_bytes(B: int, T: int, V: int, r: int) -> int:
-    return int(lib.ds_draft_chain_workspace_bytes(B, T, V, r))
+def draft_chain_workspace_bytes(B: int, T: int, V: int, r: int, max_len: int) -> int:
+    return int(lib.ds_draft_chain_workspace_bytes(B, T, V, r, int(max_len)))
+
+
+def sample_workspace_bytes(G: int, m: int, max_len: int) -> int:
+    return int(lib.ds_sample_workspace_bytes(G, m, int(max_len)))
+
+
+def softmax_workspace_bytes(rows: int, V: int) -> int:
+    return int(lib.ds_softmax_workspace_bytes(rows, V))
+
+
+def verify_workspace_bytes(B: int, T: int, V: int) -> int:
+    return int(lib.ds_verify_workspace_bytes(B, T, V))
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled device workspace of at least nbytes bytes."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def router_score(h, W1, b1, W2, b2, act, scores, ws, *, n=None, ldh=None, stream=None):
@@ -135,7 +168,7 @@ def router_score(h, W1, b1, W2, b2, act, scores, ws, *, n=None, ldh=None, stream
     M = W2.shape[0]
     _check("ds_router_score", lib.ds_router_score(
         _s(stream), _dt(W1), n, d, r, M, act, _p(h), ldh, _p(W1), _p(b1), _p(W2), _p(b2),
-        _p(scores), _p(ws), ws.numel() * ws.element_size()))
+        _p(scores), _p(ws), _nbytes(ws)))
 
 
 def select_clusters(scores, cluster_size, kind, budget, sel, n_sel, sl_len, *, stream=None):
@@ -145,12 +178,27 @@ def select_clusters(scores, cluster_size, kind, budget, sel, n_sel, sl_len, *, s
         _p(sl_len)))
 
 
-def build_shortlist(sel, n_sel, cluster_of, capacity, sl_off, sl_ids, err_flag, ws, *,
+def cluster_index_bytes(M: int, V: int) -> int:
+    return int(lib.ds_cluster_index_bytes(M, V))
+
+
+def cluster_index(cluster_of, M, index=None, err_flag=None, *, stream=None):
+    """The per-chunk prefix counts of every cluster (int32 [(nchunks+1)][M])."""
+    V = cluster_of.shape[0]
+    if index is None:
+        index = torch.empty(cluster_index_bytes(M, V) // 4, dtype=torch.int32,
+                            device=cluster_of.device)
+    _check("ds_cluster_index", lib.ds_cluster_index(_s(stream), M, V, _p(cluster_of), _p(index),
+                                                    _p(err_flag)))
+    return index
+
+
+def build_shortlist(sel, n_sel, cluster_of, index, capacity, sl_off, sl_ids, err_flag, ws, *,
                     stream=None):
     n, M = sel.shape
     _check("ds_build_shortlist", lib.ds_build_shortlist(
-        _s(stream), n, M, cluster_of.shape[0], _p(sel), _p(n_sel), _p(cluster_of), int(capacity),
-        _p(sl_off), _p(sl_ids), _p(err_flag), _p(ws), ws.numel() * ws.element_size()))
+        _s(stream), n, M, cluster_of.shape[0], _p(sel), _p(n_sel), _p(cluster_of), _p(index),
+        int(capacity), _p(sl_off), _p(sl_ids), _p(err_flag), _p(ws), _nbytes(ws)))
 
 
 def gathered_lm_head(W, h, sl_off, sl_ids, max_rows, logits, *, G=None, m=None, ldh_g=None,
@@ -165,27 +213,63 @@ def gathered_lm_head(W, h, sl_off, sl_ids, max_rows, logits, *, G=None, m=None, 
         int(max_rows), _p(logits)))
 
 
-def shortlist_sample(sl_off, sl_ids, logits, temperature, u, token, q, *, m=1, stream=None):
+def shortlist_sample(sl_off, sl_ids, logits, temperature, u, token, q, ws, *, max_len, m=1,
+                     stream=None):
     G = sl_off.shape[0] - 1
     _check("ds_shortlist_sample", lib.ds_shortlist_sample(
         _s(stream), G, m, _p(sl_off), _p(sl_ids), _p(logits), float(temperature), _p(u),
-        _p(token), _p(q)))
+        int(max_len), _p(token), _p(q), _p(ws), _nbytes(ws)))
 
 
-def target_softmax(logits, p, *, stream=None):
+def target_softmax(logits, p, ws, *, stream=None):
     V = logits.shape[-1]
     _check("ds_target_softmax", lib.ds_target_softmax(
-        _s(stream), logits.numel() // V, V, _p(logits), _p(p)))
+        _s(stream), logits.numel() // V, V, _p(logits), _p(p), _p(ws), _nbytes(ws)))
 
 
-def verify_reject(draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out, *, stream=None):
+def verify_reject(draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out, ws, *, stream=None):
     T, B = draft.shape
     V = p.shape[-1]
     _check("ds_verify_reject", lib.ds_verify_reject(
         _s(stream), B, T, V, _p(draft), _p(sl_off), _p(sl_ids), _p(q), _p(p), _p(u_acc),
-        _p(u_fin), _p(n_acc), _p(out)))
+        _p(u_fin), _p(n_acc), _p(out), _p(ws), _nbytes(ws)))
 
 
 def draft_chain(args: ChainArgs, head_stream=None, router_stream=None):
     _check("ds_draft_chain", lib.ds_draft_chain(_s(head_stream), _s(router_stream),
                                                 C.byref(args)))
+
+
+class Graph:
+    """A captured, instantiated HIP graph (see ds_capture_begin)."""
+
+    def __init__(self, handle: C.c_void_p):
+        self._h = handle
+
+    def launch(self, stream=None) -> None:
+        _check("ds_graph_launch", lib.ds_graph_launch(self._h, _s(stream)))
+
+    def close(self) -> None:
+        if self._h:
+            lib.ds_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def capture(fn, stream) -> Graph:
+    """Run fn() (which enqueues ds_* calls on `stream`) under graph capture
+    and return the instantiated graph.  `stream` must not be the legacy
+    default stream."""
+    _check("ds_capture_begin", lib.ds_capture_begin(_s(stream)))
+    try:
+        fn()
+    finally:
+        h = C.c_void_p()
+        code = lib.ds_capture_end(_s(stream), C.byref(h))
+    _check("ds_capture_end", code)
+    return Graph(h)

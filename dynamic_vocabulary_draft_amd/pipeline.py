@@ -32,8 +32,11 @@ def to_dev(a: np.ndarray | None, device="cuda") -> torch.Tensor | None:
     return out.view(torch.bfloat16) if a.dtype == np.uint16 else out
 
 
-def shortlist_bounds(cfg: syn.Config, cluster_size: np.ndarray) -> np.ndarray:
-    """Host-side upper bound of the shortlist rows of each position-call."""
+def row_bounds(cfg: syn.Config, cluster_size: np.ndarray) -> np.ndarray:
+    """Host-side upper bound of one shortlist's length at each position: the
+    budget plus the largest cluster (token budgets; the prefix stops at the
+    first cluster reaching the budget), or the k largest clusters (cluster
+    budgets)."""
     srt = np.sort(cluster_size)[::-1].astype(np.int64)
     out = []
     for b in cfg.budget:
@@ -42,8 +45,13 @@ def shortlist_bounds(cfg: syn.Config, cluster_size: np.ndarray) -> np.ndarray:
         else:
             k = min(max(int(b), 1), cfg.M)
             per_row = int(srt[:k].sum())
-        out.append(per_row * cfg.B)
+        out.append(per_row)
     return np.asarray(out, dtype=np.int64)
+
+
+def shortlist_bounds(cfg: syn.Config, cluster_size: np.ndarray) -> np.ndarray:
+    """Host-side upper bound of the shortlist rows of each position-call."""
+    return row_bounds(cfg, cluster_size) * cfg.B
 
 
 class DraftStep:
@@ -58,6 +66,9 @@ class DraftStep:
         self.W1, self.b1, self.W2, self.b2 = (dev(R[k]) for k in ("W1", "b1", "W2", "b2"))
         self.cluster_of = dev(wl.cluster_of)
         self.cluster_size = dev(wl.cluster_size)
+        self.err_flag = torch.zeros(1, dtype=torch.int32, device=device)
+        # per-clustering preprocessing: chunk-prefix counts of every cluster
+        self.cluster_index = N.cluster_index(self.cluster_of, cfg.M, err_flag=self.err_flag)
         self.h = dev(wl.h)
         self.budget = dev(wl.budget)
         self.u_draft = dev(wl.u_draft)
@@ -65,7 +76,8 @@ class DraftStep:
         self.u_fin = dev(wl.u_fin)
         self.target_logits = dev(wl.target_logits)
         B, T, M, V = cfg.B, cfg.T, cfg.M, cfg.V
-        self.max_rows = shortlist_bounds(cfg, wl.cluster_size)
+        self.max_len = row_bounds(cfg, wl.cluster_size)
+        self.max_rows = self.max_len * cfg.B
         self.capacity = int(self.max_rows.sum())
         i32 = dict(dtype=torch.int32, device=device)
         f32 = dict(dtype=torch.float32, device=device)
@@ -79,14 +91,17 @@ class DraftStep:
         self.logits = torch.empty(max(self.capacity * m, 1), **f32)
         self.q = torch.empty(max(self.capacity * m, 1), **f32)
         self.token = torch.empty((B, m) if cfg.is_tree else (T, B), **i32)
-        self.err_flag = torch.zeros(1, **i32)
-        nbytes = N.draft_chain_workspace_bytes(B, T, V, cfg.r)
-        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        nbytes = N.draft_chain_workspace_bytes(B, T, V, cfg.r, int(self.max_len.max()))
+        if cfg.is_tree:
+            nbytes = max(nbytes, N.sample_workspace_bytes(B, m, int(self.max_len.max())))
+        self.ws = N.workspace(nbytes, device)
         self.router_stream = torch.cuda.Stream(device=device)
         if self.target_logits is not None:
             self.p = torch.empty(B, T + 1, V, **f32)
             self.n_acc = torch.empty(B, **i32)
             self.out = torch.empty(B, T + 1, **i32)
+            self.softmax_ws = N.workspace(N.softmax_workspace_bytes(B * (T + 1), V), device)
+            self.verify_ws = N.workspace(N.verify_workspace_bytes(B, T, V), device)
         self._args = self._chain_args() if not cfg.is_tree else None
 
     # ------------------------------------------------------------------ chains
@@ -98,9 +113,11 @@ class DraftStep:
             dtype=N.BF16 if cfg.dtype == syn.DT_BF16 else N.F32, act=cfg.act,
             budget_kind=cfg.budget_kind, temperature=self.temperature,
             W=p(self.W), W1=p(self.W1), b1=p(self.b1), W2=p(self.W2), b2=p(self.b2),
-            cluster_of=p(self.cluster_of), cluster_size=p(self.cluster_size), h=p(self.h),
+            cluster_of=p(self.cluster_of), cluster_index=p(self.cluster_index),
+            cluster_size=p(self.cluster_size), h=p(self.h),
             budget=p(self.budget), u_draft=p(self.u_draft), capacity=self.capacity,
-            max_rows=self.max_rows.ctypes.data, scores=p(self.scores), sel=p(self.sel),
+            max_rows=self.max_rows.ctypes.data, max_len=self.max_len.ctypes.data,
+            scores=p(self.scores), sel=p(self.sel),
             n_sel=p(self.n_sel), sl_len=p(self.sl_len), sl_off=p(self.sl_off),
             sl_ids=p(self.sl_ids), logits=p(self.logits), q=p(self.q), token=p(self.token),
             err_flag=p(self.err_flag), ws=p(self.ws), ws_bytes=self.ws.numel())
@@ -134,33 +151,38 @@ class DraftStep:
         N.draft_chain(self._args, stream, self.router_stream)
 
     def verify(self, stream=None) -> None:
-        N.target_softmax(self.target_logits, self.p, stream=stream)
+        N.target_softmax(self.target_logits, self.p, self.softmax_ws, stream=stream)
         N.verify_reject(self.token, self.sl_off, self.sl_ids, self.q, self.p, self.u_acc,
-                        self.u_fin, self.n_acc, self.out, stream=stream)
+                        self.u_fin, self.n_acc, self.out, self.verify_ws, stream=stream)
 
     def step(self, stream=None) -> None:
         self.draft(stream)
         if self.target_logits is not None:
             self.verify(stream)
 
+    def capture(self, stream) -> "N.Graph":
+        """One whole step (draft + verification) as a HIP graph on `stream`
+        (a non-default stream); replay it with graph.launch(stream)."""
+        return N.capture(lambda: self.step(stream), stream)
+
     # ------------------------------------------------------------------- trees
     def _draft_tree(self, stream) -> None:
         cfg = self.cfg
-        B, M, m = cfg.B, cfg.M, cfg.tree_nodes
-        z = self.ws  # router z and build workspace share the chain workspace
+        B, m, d = cfg.B, cfg.tree_nodes, cfg.d
         zbytes = (N.router_workspace_bytes(B, cfg.r) + 255) // 256 * 256
+        bbytes = (N.build_workspace_bytes(B, cfg.V) + 255) // 256 * 256
         N.router_score(self.h, self.W1, self.b1, self.W2, self.b2, cfg.act, self.scores[0],
-                       z[:zbytes], n=B, ldh=(1 + cfg.tree_nodes) * cfg.d, stream=stream)
+                       self.ws[:zbytes], n=B, ldh=(1 + m) * d, stream=stream)
         N.select_clusters(self.scores[0], self.cluster_size, cfg.budget_kind, self.budget[0],
                           self.sel[0], self.n_sel[0], self.sl_len[0], stream=stream)
-        N.build_shortlist(self.sel[0], self.n_sel[0], self.cluster_of, self.capacity,
-                          self.sl_off, self.sl_ids, self.err_flag, z[zbytes:], stream=stream)
-        d = cfg.d
+        N.build_shortlist(self.sel[0], self.n_sel[0], self.cluster_of, self.cluster_index,
+                          self.capacity, self.sl_off, self.sl_ids, self.err_flag,
+                          self.ws[zbytes:zbytes + bbytes], stream=stream)
         N.gathered_lm_head(self.W, self.h[:, 1:], self.sl_off, self.sl_ids, self.max_rows[0],
                            self.logits, G=B, m=m, ldh_g=(1 + m) * d, stream=stream)
         N.shortlist_sample(self.sl_off, self.sl_ids, self.logits, self.temperature,
-                           self.u_draft, self.token, self.q, m=m, stream=stream)
-        del d
+                           self.u_draft, self.token, self.q, self.ws,
+                           max_len=int(self.max_len[0]), m=m, stream=stream)
 
     # ----------------------------------------------------------------- results
     def host(self) -> dict:

@@ -20,8 +20,8 @@
  * Conventions for every call:
  *   - Every array pointer is a DEVICE pointer owned by the caller.  The
  *     library never allocates, frees or retains caller memory, and keeps no
- *     state between calls apart from a per-process pool of HIP events used
- *     by ds_draft_chain.
+ *     state between calls apart from a per-thread pool of HIP events used
+ *     by ds_draft_chain and a per-device cache of the compute-unit count.
  *   - Calls only enqueue work on the given stream(s) and return; nothing
  *     synchronises with the host.
  *   - Argument errors are detected on the host before anything is enqueued
@@ -118,24 +118,40 @@ ds_status ds_select_clusters(hipStream_t s, int n, int M, const float *scores,
                              int32_t *sl_len);
 
 /*
+ * Cluster index, built once per clustering (it depends only on cluster_of):
+ * the vocabulary is cut into chunks of 4096 token ids, and
+ * index[k][c] (k = 0..nchunks, nchunks = ceil(V/4096)) is the number of
+ * members of cluster c among token ids below 4096*k, so index[nchunks][c]
+ * is the size of cluster c.  int32 [(nchunks+1)][M], caller-owned, of
+ * ds_cluster_index_bytes(M, V) bytes.  Entries of cluster_of outside
+ * [0, M) are not counted and raise DS_EINVAL in *err_flag (may be NULL).
+ * The shortlist build uses it to place every chunk's tokens directly.
+ */
+size_t ds_cluster_index_bytes(int M, int V);
+ds_status ds_cluster_index(hipStream_t s, int M, int V, const int32_t *cluster_of,
+                           int32_t *index, int32_t *err_flag);
+
+/*
  * Shortlist = union of the selected clusters' member tokens, in ascending
  * token id [A "the union of the top-selected clusters defines the drafter's
  * shortlist"; S "Problem Definition": output V_S].
  * sel [n][M], n_sel [n] as written by ds_select_clusters; cluster_of [V]
- * int32 maps every token to its cluster.
+ * int32 maps every token to its cluster; index is its cluster index
+ * (ds_cluster_index of the same cluster_of).
  * sl_off [n+1] int64: sl_off[0] is READ (base offset, e.g. the end of the
  * previous call's shortlists), sl_off[1..n] are written.
  * sl_ids [capacity] int32: entries sl_off[0] .. sl_off[n]-1 are written.
  * Offsets never exceed `capacity`; entries beyond it are dropped and
- * *err_flag raised to DS_ECAPACITY.  Cluster ids outside [0, M) (in sel or
- * cluster_of) are skipped and raise DS_EINVAL.  err_flag may be NULL.
- * ws >= ds_build_workspace_bytes(n, V) bytes, zero-filled before first use.
+ * *err_flag raised to DS_ECAPACITY.  Cluster ids in sel outside [0, M) are
+ * skipped and raise DS_EINVAL (cluster_of entries outside [0, M) are skipped;
+ * ds_cluster_index reports them).  err_flag may be NULL.
+ * ws >= ds_build_workspace_bytes(n, V) bytes.
  */
 size_t ds_build_workspace_bytes(int n, int V);
 ds_status ds_build_shortlist(hipStream_t s, int n, int M, int V, const int32_t *sel,
-                             const int32_t *n_sel, const int32_t *cluster_of, int64_t capacity,
-                             int64_t *sl_off, int32_t *sl_ids, int32_t *err_flag, void *ws,
-                             size_t ws_bytes);
+                             const int32_t *n_sel, const int32_t *cluster_of,
+                             const int32_t *index, int64_t capacity, int64_t *sl_off,
+                             int32_t *sl_ids, int32_t *err_flag, void *ws, size_t ws_bytes);
 
 /*
  * Gathered LM head [S "System Modules: Gathered LM Head" (projects hidden
@@ -167,37 +183,48 @@ ds_status ds_gathered_lm_head(hipStream_t s, ds_dtype dt, int V, int d, const vo
  * the last index with non-zero mass).  temperature == 0 gives the argmax
  * (ties to the lowest index) with a one-hot q.  Empty rows give token -1.
  * u [G*m] fp32 in [0, 1); token [G*m] int32; q in the logits layout.
+ * max_len  host-side bound on every group's shortlist length (sizes the
+ *          grid; 1 <= max_len <= 2^20).  Longer rows give unspecified
+ *          results (memory accesses stay in bounds).
+ * ws       >= ds_sample_workspace_bytes(G, m, max_len) bytes.
  */
+size_t ds_sample_workspace_bytes(int G, int m, int64_t max_len);
 ds_status ds_shortlist_sample(hipStream_t s, int G, int m, const int64_t *sl_off,
                               const int32_t *sl_ids, const float *logits, float temperature,
-                              const float *u, int32_t *token, float *q);
+                              const float *u, int64_t max_len, int32_t *token, float *q, void *ws,
+                              size_t ws_bytes);
 
 /*
  * Full-vocabulary target distribution p = softmax(target logits) per row
  * (fp64 exponent and sum, fp32 output) [A: the target verifies over the full
- * vocabulary].  logits and p are [rows][V] fp32.
+ * vocabulary].  logits and p are [rows][V] fp32, V <= 2^20.
+ * ws >= ds_softmax_workspace_bytes(rows, V) bytes.
  */
-ds_status ds_target_softmax(hipStream_t s, int rows, int V, const float *logits, float *p);
+size_t ds_softmax_workspace_bytes(int rows, int V);
+ds_status ds_target_softmax(hipStream_t s, int rows, int V, const float *logits, float *p,
+                            void *ws, size_t ws_bytes);
 
 /*
  * Rejection-sampling verification over the full vocabulary, which keeps the
  * emitted tokens distributed exactly as the target [A "the target model
  * still verifies over the full vocabulary, preserving exactness"; S
  * "Pipeline Flow: Rejection Sampling Verification"].  For sequence b:
- *   for t < T: x = draft[t][b] (shortlist row t*B + b, q in the sampler's
- *   layout with m = 1, q_t(x) = 0 off the shortlist); accept iff
- *   (double)u_acc[t][b] * q_t(x) < p_t(x).  At the first rejection, draw from
- *   max(0, p_t - q_t) over all V (from p_t if that has no mass) with
- *   u_fin[b] by the inverse CDF and stop; if all T are accepted, draw the
- *   bonus token from p_T with u_fin[b].
+ *   for t < T: x = draft[t][b] (shortlist row t*B + b, ascending token ids,
+ *   q in the sampler's layout with m = 1, q_t(x) = 0 off the shortlist);
+ *   accept iff (double)u_acc[t][b] * q_t(x) < p_t(x).  At the first
+ *   rejection, draw from max(0, p_t - q_t) over all V (from p_t if that has
+ *   no mass) with u_fin[b] by the inverse CDF and stop; if all T are
+ *   accepted, draw the bonus token from p_T with u_fin[b].
  * p [B][T+1][V] fp32 target probabilities.  Outputs n_acc [B] in [0, T] and
  * out [B][T+1] (the first n_acc+1 entries are the emitted tokens, the rest
- * -1).  Limits: 1 <= T <= 64.
+ * -1).  Limits: 1 <= T <= 64, V <= 2^20.
+ * ws >= ds_verify_workspace_bytes(B, T, V) bytes.
  */
+size_t ds_verify_workspace_bytes(int B, int T, int V);
 ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *draft,
                            const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                            const float *p, const float *u_acc, const float *u_fin,
-                           int32_t *n_acc, int32_t *out);
+                           int32_t *n_acc, int32_t *out, void *ws, size_t ws_bytes);
 
 /*
  * One chain-drafting step over T positions for B sequences, with the router
@@ -207,10 +234,13 @@ ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *dr
  *   router_stream: router(h[:, t]) -> select(budget[t]) -> build (appending
  *                  to the shortlist buffer) -> event
  *   head_stream:   wait(event) -> gathered head(h[:, t+1]) -> sample(u_draft[t])
- * so the router, selection and build of position t+1 run while the head of
- * position t streams its rows.  Rows are position-major (row t*B + b), the
+ * The router of position t needs H_{t-1}, which a drafter produces just
+ * before the head of position t-1; so for t >= 1 router_stream waits for an
+ * event recorded on head_stream immediately before head(t-1), and the
+ * router, selection and build of position t run while the head and sampler
+ * of position t-1 work.  Rows are position-major (row t*B + b), the
  * layout ds_verify_reject reads.  Every pointer is a device pointer except
- * max_rows, W_pos and head_events (host arrays).  On return all work is
+ * max_rows, max_len, W_pos and head_events (host arrays).  On return all work is
  * enqueued and head_stream waits for everything enqueued on router_stream.
  * Optional fields:
  *   W_pos        host array [T] of head matrices, one per position (drafters
@@ -229,12 +259,14 @@ typedef struct {
     const void *W;              /* [V][d]                          */
     const void *W1, *b1, *W2, *b2;
     const int32_t *cluster_of;  /* [V]                             */
+    const int32_t *cluster_index; /* ds_cluster_index of cluster_of */
     const int32_t *cluster_size;/* [M]                             */
     const void *h;              /* [B][T+1][d]                     */
     const int32_t *budget;      /* [T][B]                          */
     const float *u_draft;       /* [T][B]                          */
     int64_t capacity;           /* elements of sl_ids              */
     const int64_t *max_rows;    /* HOST [T]: bound on rows per position */
+    const int64_t *max_len;     /* HOST [T]: bound on one row's length  */
     float *scores;              /* [T][B][M]                       */
     int32_t *sel;               /* [T][B][M]                       */
     int32_t *n_sel, *sl_len;    /* [T][B]                          */
@@ -249,9 +281,26 @@ typedef struct {
     hipEvent_t *head_events;    /* HOST [2T] or NULL               */
 } ds_draft_chain_args;
 
-size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r);
+size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r, int64_t max_len);
 ds_status ds_draft_chain(hipStream_t head_stream, hipStream_t router_stream,
                          const ds_draft_chain_args *a);
+
+/*
+ * HIP graph capture of any sequence of the calls above, so a whole draft
+ * step (about ten launches per position) is replayed with one host call.
+ * ds_capture_begin starts capturing `s` (relaxed mode); every ds_* call made
+ * on `s` (and the router stream that ds_draft_chain forks from it) until
+ * ds_capture_end is recorded instead of executed; ds_capture_end
+ * instantiates the graph.  Replays use the pointers captured: the buffers
+ * must stay allocated and every call must be valid to repeat (the library's
+ * calls are: nothing is accumulated across replays).  The kernels record no
+ * memset nodes.  ds_graph_destroy releases the graph (host-side objects).
+ */
+typedef struct ds_graph_s *ds_graph;
+ds_status ds_capture_begin(hipStream_t s);
+ds_status ds_capture_end(hipStream_t s, ds_graph *out);
+ds_status ds_graph_launch(ds_graph g, hipStream_t s);
+ds_status ds_graph_destroy(ds_graph g);
 
 #ifdef __cplusplus
 }

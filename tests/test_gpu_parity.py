@@ -123,8 +123,21 @@ def _clusters(V, M, seed):
     return cluster_of, size
 
 
-@pytest.mark.parametrize("V,M,n", [(13, 3, 2), (4096, 64, 3), (20000, 100, 5),
-                                   (128256, 1024, 4), (262144, 2048, 2)])
+@pytest.mark.parametrize("V,M", [(13, 3), (4096, 64), (20000, 100), (262144, 2048)])
+def test_cluster_index_is_chunk_prefix_counts(N, V, M):
+    cluster_of, size = _clusters(V, M, V + 3)
+    idx = N.cluster_index(to_dev(cluster_of), M)
+    nch = (V + 4095) // 4096
+    got = _cpu(idx).reshape(nch + 1, M)
+    hist = np.stack([np.bincount(cluster_of[k * 4096:(k + 1) * 4096], minlength=M)
+                     for k in range(nch)])
+    ref = np.concatenate([np.zeros((1, M), np.int64), np.cumsum(hist, axis=0)])
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[-1], size)
+
+
+@pytest.mark.parametrize("V,M,n", [(13, 3, 2), (4096, 64, 3), (20000, 100, 5), (20000, 100, 1),
+                                   (128256, 1024, 4), (128256, 1024, 1), (262144, 2048, 2)])
 def test_build_parity(N, oracle_lib, V, M, n):
     cluster_of, size = _clusters(V, M, V)
     g = np.random.default_rng(V + 1)
@@ -141,17 +154,19 @@ def test_build_parity(N, oracle_lib, V, M, n):
     sl_ids = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws = torch.zeros(N.build_workspace_bytes(n, V), dtype=torch.uint8, device="cuda")
+    cdev = to_dev(cluster_of)
+    index = N.cluster_index(cdev, M, err_flag=flag)
     for _ in range(2):  # the workspace is reusable call after call
-        N.build_shortlist(to_dev(sel), to_dev(n_sel), to_dev(cluster_of), cap, sl_off, sl_ids,
-                          flag, ws)
+        N.build_shortlist(to_dev(sel), to_dev(n_sel), cdev, index, cap, sl_off, sl_ids, flag, ws)
         assert int(_cpu(flag)[0]) == 0
         assert np.array_equal(_cpu(sl_off), off_ref)
         assert np.array_equal(_cpu(sl_ids)[base:], ids_ref[base:])
         assert (_cpu(sl_ids)[:base] == -7).all()
 
 
-def test_build_capacity_and_invalid_ids(N, oracle_lib):
-    V, M, n = 9000, 40, 3
+@pytest.mark.parametrize("n", [1, 3])
+def test_build_capacity_and_invalid_ids(N, oracle_lib, n):
+    V, M = 9000, 40
     cluster_of, size = _clusters(V, M, 5)
     g = np.random.default_rng(6)
     sel, n_sel, sl_len = oracle_lib.select_clusters(g.standard_normal((n, M)).astype(np.float32),
@@ -164,21 +179,29 @@ def test_build_capacity_and_invalid_ids(N, oracle_lib):
     sl_off = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
     sl_ids = torch.empty(cap, dtype=torch.int32, device="cuda")
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
-    N.build_shortlist(to_dev(sel), to_dev(n_sel), to_dev(cluster_of), cap, sl_off, sl_ids, flag, ws)
+    cdev = to_dev(cluster_of)
+    index = N.cluster_index(cdev, M, err_flag=flag)
+    assert int(_cpu(flag)[0]) == 0
+    N.build_shortlist(to_dev(sel), to_dev(n_sel), cdev, index, cap, sl_off, sl_ids, flag, ws)
     assert int(_cpu(flag)[0]) == oracle.ECAPACITY
     assert np.array_equal(_cpu(sl_off), off_ref)
     assert np.array_equal(_cpu(sl_ids), ids_ref)
-    # out-of-range cluster ids in the map and in the selection are skipped and flagged
+    # out-of-range cluster ids: in the map (reported by the index) and in the
+    # selection (reported by the build) are skipped like the oracle does
     bad_map = cluster_of.copy()
     bad_map[[5, 700, 8999]] = [-1, M, 10 ** 6]
     bad_sel = sel.copy()
-    bad_sel[1, 0] = M + 3
+    bad_sel[0, 0] = M + 3
     st, off_ref, ids_ref = oracle_lib.build_shortlist(bad_sel, n_sel, bad_map)
     assert st == oracle.EINVAL
     cap2 = n * V
     sl_ids2 = torch.empty(cap2, dtype=torch.int32, device="cuda")
     flag.zero_()
-    N.build_shortlist(to_dev(bad_sel), to_dev(n_sel), to_dev(bad_map), cap2, sl_off, sl_ids2, flag,
+    bdev = to_dev(bad_map)
+    index2 = N.cluster_index(bdev, M, err_flag=flag)
+    assert int(_cpu(flag)[0]) == oracle.EINVAL
+    flag.zero_()
+    N.build_shortlist(to_dev(bad_sel), to_dev(n_sel), bdev, index2, cap2, sl_off, sl_ids2, flag,
                       ws)
     assert int(_cpu(flag)[0]) == oracle.EINVAL
     got_off = _cpu(sl_off)
@@ -255,7 +278,9 @@ def test_sample_parity(N, oracle_lib, lens, m, tau):
     tok_ref, q_ref, tie = oracle_lib.shortlist_sample(sl_off, sl_ids, logits, u, m, tau)
     token = torch.empty(G * m, dtype=torch.int32, device="cuda")
     q = torch.empty(logits.shape[0], dtype=torch.float32, device="cuda")
-    N.shortlist_sample(to_dev(sl_off), to_dev(sl_ids), to_dev(logits), tau, to_dev(u), token, q, m=m)
+    ws = N.workspace(N.sample_workspace_bytes(G, m, max(lens)))
+    N.shortlist_sample(to_dev(sl_off), to_dev(sl_ids), to_dev(logits), tau, to_dev(u), token, q, ws,
+                       max_len=max(lens), m=m)
     got = _cpu(token)
     assert np.array_equal(got[~tie], tok_ref[~tie])
     _ulp_bar(_cpu(q), q_ref)
@@ -273,7 +298,9 @@ def test_sample_many_rows_bit_exact(N, oracle_lib):
     tok_ref, q_ref, tie = oracle_lib.shortlist_sample(sl_off, ids, logits, u)
     token = torch.empty(R, dtype=torch.int32, device="cuda")
     q = torch.empty(L * R, dtype=torch.float32, device="cuda")
-    N.shortlist_sample(to_dev(sl_off), to_dev(ids), to_dev(logits), 1.0, to_dev(u), token, q)
+    ws = N.workspace(N.sample_workspace_bytes(R, 1, L))
+    N.shortlist_sample(to_dev(sl_off), to_dev(ids), to_dev(logits), 1.0, to_dev(u), token, q, ws,
+                       max_len=L)
     got = _cpu(token)
     assert np.array_equal(got[~tie], tok_ref[~tie])
     assert tie.sum() <= 2
@@ -287,7 +314,7 @@ def test_target_softmax_parity(N, oracle_lib, rows, V):
     g = np.random.default_rng(V)
     lg = (g.standard_normal((rows, V)) * 3).astype(np.float32)
     p = torch.empty(rows, V, device="cuda")
-    N.target_softmax(to_dev(lg), p)
+    N.target_softmax(to_dev(lg), p, N.workspace(N.softmax_workspace_bytes(rows, V)))
     _ulp_bar(_cpu(p), oracle_lib.target_softmax(lg))
 
 
@@ -335,7 +362,7 @@ def test_verify_parity(N, oracle_lib, V, T, B, mode):
     out = torch.empty(B, T + 1, dtype=torch.int32, device="cuda")
     dv = {k: to_dev(v) for k, v in c.items()}
     N.verify_reject(dv["draft"], dv["sl_off"], dv["sl_ids"], dv["q"], dv["p"], dv["u_acc"],
-                    dv["u_fin"], n_acc, out)
+                    dv["u_fin"], n_acc, out, N.workspace(N.verify_workspace_bytes(B, T, V)))
     assert np.array_equal(_cpu(n_acc), n_ref)  # accept decisions are exact
     got = _cpu(out)
     assert np.array_equal(got[~tie], out_ref[~tie])

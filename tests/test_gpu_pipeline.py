@@ -158,3 +158,35 @@ def test_step_full_size(oracle_lib, index):
     step.step()
     r = step.host()
     check_stagewise(wl, r, head_samples=256 if index != 2 else 64, seed=index)
+
+
+@pytest.mark.parametrize("name", ["tiny-fp32", "small-bf16-b3", "small-tree"])
+def test_graph_replay_matches_eager(oracle_lib, name):
+    """A captured step replayed three times, with eager work and
+    synchronisation between replays, reproduces the eager step bit for bit."""
+    cfg = small_configs()[name]
+    wl = syn.make_workload(cfg.index, cfg=cfg)
+    step = DraftStep(wl)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step.step(stream)
+    eager = step.host()
+    check_stagewise(wl, eager)
+    graph = step.capture(stream)
+    keys = [k for k in eager if k != "err_flag"]
+    for rep in range(3):
+        with torch.cuda.stream(stream):  # eager work between replays
+            for t in (step.logits, step.q):
+                t.fill_(float("nan"))
+            step.sl_ids.fill_(-5)
+            step.token.fill_(-9)
+            step.sl_off[1:].fill_(-1)
+            if step.target_logits is not None:
+                step.out.fill_(-3)
+                step.p.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.launch(stream)
+        got = step.host()
+        for k in keys:
+            assert np.array_equal(got[k], eager[k], equal_nan=True), (rep, k)
+    graph.close()

@@ -51,8 +51,14 @@ def test_workspace_queries(N):
     assert N.router_workspace_bytes(64, 1024) == 64 * 1024 * 4
     assert N.router_workspace_bytes(0, 4) == 0
     nch = (262144 + 4095) // 4096
-    assert N.build_workspace_bytes(64, 262144) == 256 + 64 * nch * 8
-    assert N.draft_chain_workspace_bytes(1, 6, 128256, 1024) >= 4096 + 256
+    assert N.build_workspace_bytes(64, 262144) == 256 + 64 * 8
+    assert N.cluster_index_bytes(2048, 262144) == (nch + 1) * 2048 * 4
+    assert N.sample_workspace_bytes(1, 1, 1024) == 24 + 256
+    assert N.sample_workspace_bytes(3, 4, 1025) == 12 * 2 * 24 + 256
+    assert N.softmax_workspace_bytes(7, 128256) == 7 * 126 * 24 + 256
+    assert N.verify_workspace_bytes(2, 6, 128256) >= 2 * 126 * 24 + 2 * 4
+    assert N.draft_chain_workspace_bytes(1, 6, 128256, 1024, 55734) >= 4096 + 256
+    assert N.sample_workspace_bytes(0, 1, 10) == 0
 
 
 FAKE = C.c_void_p(4096)  # aligned, never dereferenced: every call below fails validation
@@ -80,12 +86,17 @@ def test_select_build_head_sample_verify_reject_bad_arguments(N):
     assert L.ds_select_clusters(None, 2, 64, FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE) == 2
     assert L.ds_select_clusters(None, 0, 64, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE) == 1
     assert L.ds_select_clusters(None, 2, 64, None, FAKE, 1, FAKE, FAKE, FAKE, FAKE) == 1
-    assert L.ds_build_shortlist(None, 2, 64, 1000, FAKE, FAKE, FAKE, 10, FAKE, FAKE, None, FAKE,
-                                0) == 1  # workspace too small
-    assert L.ds_build_shortlist(None, 2, 99999, 1000, FAKE, FAKE, FAKE, 10, FAKE, FAKE, None,
-                                FAKE, 1 << 20) == 3
-    assert L.ds_build_shortlist(None, 2, 64, 1000, FAKE, FAKE, FAKE, -1, FAKE, FAKE, None, FAKE,
-                                1 << 20) == 1
+    bld = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
+        ("s", None), ("n", 2), ("M", 64), ("V", 1000), ("sel", FAKE), ("n_sel", FAKE),
+        ("cluster_of", FAKE), ("index", FAKE), ("cap", 10), ("sl_off", FAKE), ("sl_ids", FAKE),
+        ("flag", None), ("ws", FAKE), ("ws_bytes", 1 << 20)]]
+    assert L.ds_build_shortlist(*bld(ws_bytes=0)) == 1  # workspace too small
+    assert L.ds_build_shortlist(*bld(M=99999)) == 3
+    assert L.ds_build_shortlist(*bld(cap=-1)) == 1
+    assert L.ds_build_shortlist(*bld(index=None)) == 1
+    assert L.ds_cluster_index(None, 64, 1000, None, FAKE, None) == 1
+    assert L.ds_cluster_index(None, 5000, 1000, FAKE, FAKE, None) == 3
+    assert L.ds_cluster_index(None, 0, 1000, FAKE, FAKE, None) == 1
     head = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
         ("s", None), ("dt", N.BF16), ("V", 100), ("d", 64), ("W", FAKE), ("G", 2), ("m", 1),
         ("h", FAKE), ("ldh_g", 64), ("sl_off", FAKE), ("sl_ids", FAKE), ("max_rows", 10),
@@ -98,22 +109,34 @@ def test_select_build_head_sample_verify_reject_bad_arguments(N):
     assert L.ds_gathered_lm_head(*head(d=8200, ldh_g=8200)) == 3
     assert L.ds_gathered_lm_head(*head(dt=N.F32, d=4104, ldh_g=4104)) == 3
     assert L.ds_gathered_lm_head(*head(max_rows=-1)) == 1
-    assert L.ds_shortlist_sample(None, 2, 1, FAKE, FAKE, FAKE, C.c_float(-1.0), FAKE, FAKE,
-                                 FAKE) == 1
-    assert L.ds_shortlist_sample(None, 2, 1, FAKE, FAKE, FAKE, C.c_float(float("nan")), FAKE,
-                                 FAKE, FAKE) == 1
-    assert L.ds_shortlist_sample(None, 0, 1, FAKE, FAKE, FAKE, C.c_float(1.0), FAKE, FAKE,
-                                 FAKE) == 1
-    assert L.ds_target_softmax(None, 0, 10, FAKE, FAKE) == 1
-    assert L.ds_verify_reject(None, 2, 65, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              FAKE) == 3
-    assert L.ds_verify_reject(None, 2, 3, (1 << 20) + 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              FAKE, FAKE) == 3
-    assert L.ds_verify_reject(None, 2, 3, 100, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              FAKE) == 1
+    smp = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
+        ("s", None), ("G", 2), ("m", 1), ("sl_off", FAKE), ("sl_ids", FAKE), ("logits", FAKE),
+        ("tau", C.c_float(1.0)), ("u", FAKE), ("max_len", 100), ("token", FAKE), ("q", FAKE),
+        ("ws", FAKE), ("ws_bytes", 0)]]
+    assert L.ds_shortlist_sample(*smp(tau=C.c_float(-1.0))) == 1
+    assert L.ds_shortlist_sample(*smp(tau=C.c_float(float("nan")))) == 1
+    assert L.ds_shortlist_sample(*smp(G=0)) == 1
+    assert L.ds_shortlist_sample(*smp(max_len=0)) == 1
+    assert L.ds_shortlist_sample(*smp(max_len=(1 << 20) + 1)) == 3
+    assert L.ds_shortlist_sample(*smp()) == 1  # workspace too small
+    assert L.ds_target_softmax(None, 0, 10, FAKE, FAKE, FAKE, 1 << 20) == 1
+    assert L.ds_target_softmax(None, 2, (1 << 20) + 4, FAKE, FAKE, FAKE, 1 << 30) == 3
+    assert L.ds_target_softmax(None, 2, 1000, FAKE, FAKE, FAKE, 8) == 1
+    ver = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
+        ("s", None), ("B", 2), ("T", 3), ("V", 100), ("draft", FAKE), ("sl_off", FAKE),
+        ("sl_ids", FAKE), ("q", FAKE), ("p", FAKE), ("u_acc", FAKE), ("u_fin", FAKE),
+        ("n_acc", FAKE), ("out", FAKE), ("ws", FAKE), ("ws_bytes", 0)]]
+    assert L.ds_verify_reject(*ver(T=65)) == 3
+    assert L.ds_verify_reject(*ver(V=(1 << 20) + 1)) == 3
+    assert L.ds_verify_reject(*ver(draft=None)) == 1
+    assert L.ds_verify_reject(*ver()) == 1  # workspace too small
     assert L.ds_draft_chain(None, None, None) == 1
     a = N.ChainArgs(B=0, T=6)
     assert L.ds_draft_chain(None, None, C.byref(a)) == 1
+    assert L.ds_capture_begin(None) == 1
+    assert L.ds_capture_end(None, None) == 1
+    assert L.ds_graph_launch(None, None) == 1
+    assert L.ds_graph_destroy(None) == 1
 
 
 # ----------------------------------------------------------------------------
