@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "head_gemv_traffic.json")
 HEAD_SOURCES = ["dynamic_vocabulary_draft_amd/csrc/head.hip",
+                "dynamic_vocabulary_draft_amd/csrc/head_mfma.hip",
                 "dynamic_vocabulary_draft_amd/csrc/common.h"]
 
 
@@ -188,7 +189,7 @@ def main():
         sizes.append(per)
         assert int(st.err_flag.item()) == 0
 
-    timed_events = not cfg.is_tree
+    timed_events = True
     graphs, mode = [], "eager"
     if not args.eager:
         # a few graphs per instance, replayed round-robin
@@ -237,6 +238,7 @@ def main():
         assert int(st.err_flag.item()) == 0
 
     tokens_per_step = cfg.B * (cfg.tree_nodes if cfg.is_tree else cfg.T)
+    hrows = cfg.tree_nodes if cfg.is_tree else 1  # head rows per shortlist
     value = tokens_per_step * args.steps / wall
     roof = None
     head = None
@@ -248,8 +250,8 @@ def main():
                 durs.append(ev.elapsed_ms(ev_sets[k][2 * t], ev_sets[k][2 * t + 1]))
                 sz = sizes[i][t]
                 # every needed W row once, the ids, the hidden rows, the logits
-                nbytes.append(sz["union"] * cfg.d * e + sz["total"] * 4 + cfg.B * cfg.d * e
-                              + sz["total"] * 4)
+                nbytes.append(sz["union"] * cfg.d * e + sz["total"] * 4
+                              + cfg.B * hrows * cfg.d * e + sz["total"] * hrows * 4)
                 rows.append(sz["total"])
         mean_ms = float(np.mean(durs))
         achieved = float(np.sum(nbytes)) / (float(np.sum(durs)) * 1e-3) / 1e9
@@ -262,13 +264,17 @@ def main():
                 traffic = tr.get("bytes_per_launch")
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
-        head = {"kernel": "head_gemv_kernel", "launches_timed": len(durs),
+        mfma = cfg.dtype == syn.DT_BF16 and ((hrows == 1 and cfg.B >= 8) or hrows >= 8)
+        kname = ("head_gemv_kernel" if not mfma else
+                 "union_start_kernel + head_union_kernel" if hrows == 1 else
+                 "head_gathered_kernel")
+        head = {"kernel": kname, "launches_timed": len(durs),
                 "mean_us": round(mean_ms * 1e3, 2),
                 "p10_us": round(float(np.percentile(durs, 10)) * 1e3, 2),
                 "p90_us": round(float(np.percentile(durs, 90)) * 1e3, 2),
                 "mean_rows": round(float(np.mean(rows)), 1),
                 "mean_algorithmic_bytes": round(float(np.mean(nbytes)), 0),
-                "head_only_tokens_per_s": round(cfg.B / (mean_ms * 1e-3), 1),
+                "head_only_tokens_per_s": round(cfg.B * hrows / (mean_ms * 1e-3), 1),
                 "w_replicas": not args.no_replicas,
                 "timed_on": "eager steps (HIP events around each head launch)"}
     for g in graphs:

@@ -241,15 +241,24 @@ ds_status ds_build_shortlist(hipStream_t s, int n, int M, int V, const int32_t *
                                        sl_ids, err_flag, ws));
 }
 
+size_t ds_head_workspace_bytes(int G, int m, int V)
+{
+    return G > 0 && m > 0 && V > 0 ? ds::head_ws_bytes(G, m, V) : 0;
+}
+
 ds_status ds_gathered_lm_head(hipStream_t s, ds_dtype dt, int V, int d, const void *W, int G,
                               int m, const void *h, int64_t ldh_g, const int64_t *sl_off,
-                              const int32_t *sl_ids, int64_t max_rows, float *logits)
+                              const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
+                              size_t ws_bytes)
 {
     ds_status st = check_head(dt, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows, logits);
     if (st != DS_OK)
         return st;
+    const size_t need = ds_head_workspace_bytes(G, m, V);
+    if (need && (!ws || ws_bytes < need))
+        return DS_EINVAL;
     return hip_status(ds::head_launch(s, dt == DS_BF16, V, d, W, G, m, h, ldh_g, sl_off, sl_ids,
-                                      max_rows, logits));
+                                      max_rows, logits, ws));
 }
 
 size_t ds_sample_workspace_bytes(int G, int m, int64_t max_len)
@@ -312,7 +321,8 @@ size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r, int64_t max_le
     if (B <= 0 || T <= 0 || V <= 0 || r <= 0 || max_len <= 0)
         return 0;
     return round_up(ds_router_workspace_bytes(B, r), 256) +
-           round_up(ds::build_ws_bytes(B, V), 256) + ds::sample_ws_bytes(B, max_len);
+           round_up(ds::build_ws_bytes(B, V), 256) + round_up(ds::sample_ws_bytes(B, max_len), 256) +
+           ds::head_ws_bytes(B, 1, V);
 }
 
 ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_args *a)
@@ -360,6 +370,7 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
     float *z = reinterpret_cast<float *>(a->ws);
     void *bws = reinterpret_cast<char *>(a->ws) + round_up(ds_router_workspace_bytes(B, a->r), 256);
     void *sws = reinterpret_cast<char *>(bws) + round_up(ds::build_ws_bytes(B, a->V), 256);
+    void *hws = reinterpret_cast<char *>(sws) + round_up(ds::sample_ws_bytes(B, len_bound), 256);
     // events: [0, T) router done, [T, 2T) head about to start, 2T fork
     if (g_events.ensure(2 * (size_t)T + 1) != hipSuccess)
         return DS_EHIP;
@@ -395,7 +406,7 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
         if (err == hipSuccess)
             err = ds::head_launch(hs, bf16, a->V, a->d, a->W_pos ? a->W_pos[t] : a->W, B, 1,
                                   hb + (size_t)(t + 1) * a->d * e, ldh, a->sl_off + rb, a->sl_ids,
-                                  a->max_rows[t], a->logits);
+                                  a->max_rows[t], a->logits, hws);
         if (err == hipSuccess && a->head_events)
             err = hipEventRecord(a->head_events[2 * t + 1], hs);
         if (err == hipSuccess)

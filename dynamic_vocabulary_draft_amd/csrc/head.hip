@@ -184,8 +184,10 @@ hipError_t launch_dtype(hipStream_t s, int V, int d, const void *W, int G, int m
 
 hipError_t head_launch(hipStream_t s, bool bf16, int V, int d, const void *W, int G, int m,
                        const void *h, int64_t ldh_g, const int64_t *sl_off,
-                       const int32_t *sl_ids, int64_t max_rows, float *logits)
+                       const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws)
 {
+    if (head_mfma_applies(bf16, V, d, G, m))
+        return head_mfma_launch(s, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows, logits, ws);
     return bf16 ? launch_dtype<true>(s, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows, logits)
                 : launch_dtype<false>(s, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows, logits);
 }

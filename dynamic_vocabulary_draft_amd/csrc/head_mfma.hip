@@ -1,0 +1,446 @@
+// Gathered LM head, matrix-core regimes (DynaSpec summary page, "System
+// Modules: Gathered LM Head" and "Novel Architectural Elements": the
+// projection restricted to the shortlist rows, fused with the index
+// selection; "Comparison to Prior Work": O(|V_S| d)).
+//
+// Both kernels use v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32
+// accumulation).  A wave owns 32 rows of W; per 64-element slice of the
+// hidden dimension it reads the rows' 128-byte lines whole and passes them
+// through a small per-wave LDS buffer into MFMA order, where lane l holds
+// 64 contiguous bytes of row l%32 (lanes l and l+32 the two halves) for four
+// MFMA steps; the same permutation of the reduction index is applied to the
+// B operand, so the products are exact and only the summation order differs
+// from a plain dot product.  The B operand (hidden vectors) is staged in LDS
+// per phase of several slices and shared by the workgroup's four waves.
+//
+// union (batched drafting: many shortlists, one head row each): the union
+//   of B shortlists covers nearly all of V already at B = 32, so instead of
+//   streaming every group's rows (B times the bytes) the kernel walks W in
+//   128-token tiles in token-id order, reads each row once, multiplies it
+//   with all G hidden vectors (columns of the MFMA), and writes only the
+//   (row, group) pairs on that group's shortlist.  A pre-pass over the
+//   shortlists records, per group and 32-token tile, where the tile's
+//   entries start in the group's shortlist (shortlists are ascending).
+// gathered (tree drafting: m head rows share one shortlist): a gathered
+//   GEMM per group, rows = shortlist entries (gathered W rows), columns =
+//   the m head rows; workgroups of different groups with the same tile
+//   index are launched next to each other, so rows shared by several
+//   shortlists are read while still in the memory-side cache.
+#include "common.h"
+#include "kernels.h"
+
+namespace ds {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kKs = 64;         // hidden-dimension slice per MFMA group
+constexpr int kTileRows = 128;  // W rows per workgroup (4 waves x 32)
+
+__device__ __forceinline__ f32x16 mfma(const u32x4 &a, const u32x4 &b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// W rows are read with raw buffer loads: one 32-bit byte offset per lane, the
+// 16-byte piece offsets as instruction immediates, and the hardware range
+// check (offset >= num_records reads zero) instead of clamping -- so every
+// load is unconditional and the compiler waits only for the slice it uses.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, CDNA encoding
+constexpr int kNonTemporal = 2;         // streamed once: do not keep in cache
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+// W is read in whole 128-byte lines: per 64-wide slice a wave's 32 rows are
+// four loads of 8 rows x 128 B (lane l: row l/8 + 8i, bytes 16*(l%8) of the
+// slice).  Loads that give each lane its own MFMA row instead (two lanes per
+// row, 32 B of a line per load) stream at well under half the bandwidth.
+// `voff[i]` = byte offset of this lane's row for load i plus 16*(l%8).
+__device__ __forceinline__ void load_a(rsrc_t w, const uint32_t voff[4], int k0, u32x4 a[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        a[i] = __builtin_amdgcn_raw_buffer_load_b128(w, voff[i] + 2u * (uint32_t)k0, 0,
+                                                     kNonTemporal);
+}
+
+// Per-wave LDS slice of A: 32 rows x 64 bf16; the 16-byte piece p of row r
+// sits in slot p ^ (r & 7), so the row-wise writes and the MFMA-order reads
+// (eight rows, one piece each) both touch distinct banks.
+constexpr int kASlice = 32 * kKs;  // bf16 elements per wave
+
+// B operand (hidden vectors) for one phase of KP hidden elements, staged in
+// LDS as [NB*32][KP + 8] bf16 (rows past nrows and elements past d are zero).
+// Each of the 256 threads moves kStage 16-byte pieces: all loads of a phase
+// are issued one slice group before the phase starts, into registers.
+template <int NB>
+constexpr int phase_len() { return 512 / NB; }
+template <int NB>
+constexpr int lds_row() { return phase_len<NB>() + 8; }
+constexpr int kStage = 32 * 512 / 8 / 256;  // pieces per thread per phase
+
+template <int NB, class Src>
+__device__ __forceinline__ void load_phase(u32x4 v[kStage], int k0, int d, int nrows, Src src)
+{
+    constexpr int KP = phase_len<NB>();
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+        const int p = threadIdx.x + 256 * i;
+        const int r = min(p / (KP / 8), nrows - 1), k = min(k0 + (p % (KP / 8)) * 8, d - 8);
+        v[i] = *reinterpret_cast<const u32x4 *>(src(r) + k);
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void store_phase(uint16_t *lds, const u32x4 v[kStage], int k0, int d,
+                                            int nrows)
+{
+    constexpr int KP = phase_len<NB>(), LR = lds_row<NB>();
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+        const int p = threadIdx.x + 256 * i;
+        const int r = p / (KP / 8), kk = (p % (KP / 8)) * 8;
+        const bool ok = r < nrows && k0 + kk < d;
+        *reinterpret_cast<u32x4 *>(lds + r * LR + kk) = ok ? v[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// MFMA over one 64-wide slice (hidden offset kabs, column koff of the staged
+// phase): the slice's loads go through the wave's LDS slice into MFMA order
+// (lane l: row l%32, pieces 4*(l/32) .. +3); a slice reaching past d zeroes
+// this lane's pieces at k >= d.  One wave's LDS operations execute in order,
+// so the wave's slice buffer needs no barrier.
+template <int NB>
+__device__ __forceinline__ void slice_mma(const u32x4 ld[4], uint16_t *aw, const uint16_t *lds,
+                                          int koff, int kabs, int d, f32x16 acc[NB])
+{
+    constexpr int LR = lds_row<NB>();
+    const int lane = lane_id();
+    const int wr = lane >> 3, wp = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4 *>(aw + (wr + 8 * i) * kKs + ((wp ^ wr) << 3)) = ld[i];
+    const int rr = lane & 31, hh = lane >> 5;
+    u32x4 a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        a[s] = *reinterpret_cast<const u32x4 *>(aw + rr * kKs + (((4 * hh + s) ^ (rr & 7)) << 3));
+    if (kabs + kKs > d) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            if (kabs + 32 * hh + 8 * s >= d)
+                a[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+    const int kb = koff + 32 * hh;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const uint16_t *brow = lds + (nb * 32 + rr) * LR + kb;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const u32x4 b = *reinterpret_cast<const u32x4 *>(brow + 8 * s);
+            acc[nb] = mfma(a[s], b, acc[nb]);
+        }
+    }
+}
+
+// acc[nb] = (this wave's 32 W rows) x (NB*32 staged B rows)^T over all d.
+// W streams through a register ring of four 64-wide slices (16 KB per wave
+// in flight); a phase (phase_len<NB>() hidden elements of B) is staged in
+// LDS between two barriers, its loads issued one slice group earlier so the
+// switch waits for them and not for the W ring.
+template <int NB, class Src>
+__device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], int d,
+                                             uint16_t *lds, uint16_t *aw, int nrows, Src src,
+                                             f32x16 acc[NB])
+{
+    constexpr int KP = phase_len<NB>(), NS = KP / kKs, GP = NS / 4;  // groups of 4 slices
+    const int nsl = (d + kKs - 1) / kKs, nph = (d + KP - 1) / KP;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = f32x16{};
+    u32x4 hv[kStage];
+    load_phase<NB>(hv, 0, d, nrows, src);
+    __builtin_amdgcn_sched_barrier(0);  // B loads first, as in the loop
+    u32x4 r0[4], r1[4], r2[4], r3[4];
+    load_a(w, voff, 0 * kKs, r0);
+    load_a(w, voff, 1 * kKs, r1);
+    load_a(w, voff, 2 * kKs, r2);
+    load_a(w, voff, 3 * kKs, r3);
+    for (int ph = 0; ph < nph; ++ph) {
+        __syncthreads();  // every wave is done with the previous phase
+        store_phase<NB>(lds, hv, ph * KP, d, nrows);
+        __syncthreads();
+#pragma unroll
+        for (int gi = 0; gi < GP; ++gi) {
+            const int ks = ph * NS + 4 * gi;  // first slice of this group
+            if (ks >= nsl)
+                break;  // only in the last phase
+            if (gi == GP - 1) {
+                load_phase<NB>(hv, (ph + 1) * KP, d, nrows, src);
+                // keep these loads ahead of the ring reloads below: the switch
+                // then waits for them alone (loads complete in issue order)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            slice_mma<NB>(r0, aw, lds, (4 * gi + 0) * kKs, (ks + 0) * kKs, d, acc);
+            load_a(w, voff, (ks + 4) * kKs, r0);
+            slice_mma<NB>(r1, aw, lds, (4 * gi + 1) * kKs, (ks + 1) * kKs, d, acc);
+            load_a(w, voff, (ks + 5) * kKs, r1);
+            slice_mma<NB>(r2, aw, lds, (4 * gi + 2) * kKs, (ks + 2) * kKs, d, acc);
+            load_a(w, voff, (ks + 6) * kKs, r2);
+            slice_mma<NB>(r3, aw, lds, (4 * gi + 3) * kKs, (ks + 3) * kKs, d, acc);
+            load_a(w, voff, (ks + 7) * kKs, r3);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ union
+// start[g][t] = first index j of group g's shortlist with S_g[j] >= 32*t,
+// t = 0..nt (nt = ceil(V/32)); written only for non-empty groups.  Entries
+// with ids outside [0, V) get their NaN logit here.
+__global__ __launch_bounds__(256) void union_start_kernel(int G, int nt, int V,
+                                                          const int64_t *__restrict__ sl_off,
+                                                          const int32_t *__restrict__ sl_ids,
+                                                          int32_t *__restrict__ start,
+                                                          float *__restrict__ logits)
+{
+    const int64_t beg = sl_off[0], end = sl_off[G];
+    for (int64_t J = beg + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; J < end;
+         J += (int64_t)gridDim.x * blockDim.x) {
+        int lo = 0, hi = G;  // group: last g with sl_off[g] <= J
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sl_off[mid] <= J)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        const int g = lo;
+        const int64_t j = J - sl_off[g], len = sl_off[g + 1] - sl_off[g];
+        auto tile = [nt](int32_t y) { return y < 0 ? -1 : min((int64_t)(y >> 5), (int64_t)nt); };
+        const int32_t yJ = sl_ids[J];
+        if (yJ < 0 || yJ >= V)
+            logits[J] = __builtin_nanf("");
+        const int64_t tc = tile(yJ);
+        const int64_t tp = j > 0 ? tile(sl_ids[J - 1]) : -1;
+        int32_t *row = start + (int64_t)g * (nt + 1);
+        for (int64_t t = tp + 1; t <= tc; ++t)
+            row[t] = (int32_t)j;
+        if (j == len - 1)
+            for (int64_t t = (tc < 0 ? 0 : tc + 1); t <= nt; ++t)
+                row[t] = (int32_t)len;
+    }
+}
+
+template <int NB>
+__global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uint16_t *__restrict__ W,
+                                                         int G, int g0, const uint16_t *__restrict__ h,
+                                                         int64_t ldh_g, const int64_t *__restrict__ sl_off,
+                                                         const int32_t *__restrict__ sl_ids,
+                                                         const int32_t *__restrict__ start, int nt,
+                                                         float *__restrict__ logits)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NB * 32 * lds_row<NB>()];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[4 * kASlice];
+    __shared__ int s_any;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int ng = min(NB * 32, G - g0);  // groups of this column pass
+    const int64_t y0 = (int64_t)blockIdx.x * kTileRows;
+    const int t32 = (int)(y0 >> 5) + wave;  // this wave's 32-token tile
+
+    // skip tiles no shortlist touches
+    if (threadIdx.x == 0)
+        s_any = 0;
+    __syncthreads();
+    for (int q = threadIdx.x; q < ng * 4; q += blockDim.x) {
+        const int g = g0 + q / 4, t = (int)(y0 >> 5) + q % 4;
+        if (t < nt && sl_off[g + 1] > sl_off[g]) {
+            const int32_t *st = start + (int64_t)g * (nt + 1);
+            if (st[t + 1] > st[t])
+                s_any = 1;
+        }
+    }
+    __syncthreads();
+    if (!s_any)
+        return;
+
+    // the block's W rows y0 .. y0+127 (rows past V read zero; never written)
+    const int64_t rows = min((int64_t)kTileRows, (int64_t)V - y0);
+    const rsrc_t w = make_rsrc(W + y0 * d, (uint32_t)(rows * d * 2));
+    uint32_t voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        voff[i] = (uint32_t)((32 * wave + (lane >> 3) + 8 * i) * d * 2 + 16 * (lane & 7));
+    f32x16 acc[NB];
+    auto hsrc = [&](int r) { return h + (int64_t)(g0 + r) * ldh_g; };
+    rows_times_b<NB>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc, acc);
+
+    // epilogue: (row, group) pairs on the group's shortlist
+    const int64_t tbase = (int64_t)t32 * 32;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int gl = nb * 32 + (lane & 31);
+        if (gl >= ng || t32 >= nt)
+            continue;
+        const int g = g0 + gl;
+        const int64_t off = sl_off[g], len = sl_off[g + 1] - off;
+        if (len <= 0)
+            continue;
+        const int32_t *st = start + (int64_t)g * (nt + 1);
+        int64_t a0 = st[t32], a1 = st[t32 + 1];
+        a0 = a0 < 0 ? 0 : (a0 > len ? len : a0);
+        a1 = a1 < a0 ? a0 : (a1 > len ? len : a1);
+        if (a1 - a0 > 32)
+            a1 = a0 + 32;
+        uint32_t mask = 0;
+        for (int64_t e = a0; e < a1; ++e) {
+            const int32_t id = sl_ids[off + e];
+            const int64_t o = (int64_t)id - tbase;
+            if (o >= 0 && o < 32 && id < V)  // ids outside [0, V): NaN from the pre-pass
+                mask |= 1u << o;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int mrow = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if ((mask >> mrow) & 1u) {
+                const int64_t pos = a0 + __popc(mask & ((1u << mrow) - 1u));
+                if (pos < len)
+                    logits[off + pos] = acc[nb][r];
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------- gathered
+template <int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void head_gathered_kernel(int V, int d, const uint16_t *__restrict__ W,
+                                                            int G, int m, int n0,
+                                                            const uint16_t *__restrict__ h,
+                                                            int64_t ldh_g,
+                                                            const int64_t *__restrict__ sl_off,
+                                                            const int32_t *__restrict__ sl_ids,
+                                                            int tiles_stride,
+                                                            float *__restrict__ logits)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NB * 32 * lds_row<NB>()];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[4 * kASlice];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int g = blockIdx.x % G;  // neighbouring workgroups: same tile, other groups
+    const int64_t off = sl_off[g], len = sl_off[g + 1] - off;
+    const int mm = min(m - n0, NB * 32);  // head rows n0 .. n0+mm-1 in this pass
+    const uint16_t *hg = h + (int64_t)g * ldh_g + (int64_t)n0 * d;
+    auto hsrc = [&](int r) { return hg + (int64_t)r * d; };
+    const rsrc_t w = make_rsrc(W, (uint32_t)((int64_t)V * d * 2));  // V*d*2 < 4 GiB
+    for (int64_t tile = blockIdx.x / G; tile * kTileRows < len; tile += tiles_stride) {
+        const int64_t e = tile * kTileRows + 32 * wave + (lane & 31);
+        const bool evalid = e < len;
+        int32_t id = evalid ? sl_ids[off + e] : 0;
+        const bool valid = evalid && id >= 0 && id < V;  // else row 0, result not used
+        const int yrow = valid ? id : 0;
+        uint32_t voff[4];  // load i of lane l reads the row of the wave's entry l/8 + 8i
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            voff[i] = (uint32_t)__shfl(yrow, (lane >> 3) + 8 * i) * (uint32_t)d * 2u +
+                      16u * (lane & 7);
+        f32x16 acc[NB];
+        rows_times_b<NB>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc);
+        // epilogue: column = head row (node), row = shortlist entry; the
+        // entry of accumulator row i was loaded by lanes i and i + 32
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int nl = nb * 32 + (lane & 31);
+            float *out = logits + (int64_t)m * off + (int64_t)(n0 + nl) * len;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int64_t ent = tile * kTileRows + 32 * wave + i;
+                const bool ok = __shfl(valid ? 1 : 0, i) != 0;
+                if (nl < mm && ent < len)
+                    out[ent] = ok ? acc[nb][r] : __builtin_nanf("");
+            }
+        }
+    }
+}
+
+}  // namespace
+
+size_t head_ws_bytes(int G, int m, int V)
+{
+    if (G < kUnionMinGroups || m != 1)
+        return 0;
+    const int64_t nt = ((int64_t)V + 31) / 32;
+    return (size_t)G * (size_t)(nt + 1) * sizeof(int32_t) + 256;
+}
+
+bool head_mfma_applies(bool bf16, int V, int d, int G, int m)
+{
+    if (!bf16)
+        return false;
+    if (m == 1)
+        return G >= kUnionMinGroups;
+    // gathered rows are addressed by 32-bit byte offsets into the whole of W
+    return m >= kGatheredMinRows && (int64_t)V * d * 2 + 4096 <= (int64_t)UINT32_MAX;
+}
+
+hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, int m,
+                            const void *h, int64_t ldh_g, const int64_t *sl_off,
+                            const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws)
+{
+    const uint16_t *Wb = reinterpret_cast<const uint16_t *>(W);
+    const uint16_t *hb = reinterpret_cast<const uint16_t *>(h);
+    hipError_t e;
+    if (m == 1) {
+        const int nt = (V + 31) / 32;
+        int32_t *start = reinterpret_cast<int32_t *>(ws);
+        int64_t blocks = (max_rows + 255) / 256;
+        const int64_t cap = 4LL * device_cu_count();
+        if (blocks > cap)
+            blocks = cap;
+        if (blocks < 1)
+            blocks = 1;
+        hipLaunchKernelGGL(union_start_kernel, dim3((unsigned)blocks), dim3(256), 0, s, G, nt, V,
+                           sl_off, sl_ids, start, logits);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+        const unsigned tiles = (unsigned)((V + kTileRows - 1) / kTileRows);
+        for (int g0 = 0; g0 < G; g0 += 64) {  // column passes of up to 64 groups
+            if (G - g0 > 32)
+                hipLaunchKernelGGL(head_union_kernel<2>, dim3(tiles), dim3(256), 0, s, V, d, Wb, G, g0,
+                                   hb, ldh_g, sl_off, sl_ids, start, nt, logits);
+            else
+                hipLaunchKernelGGL(head_union_kernel<1>, dim3(tiles), dim3(256), 0, s, V, d, Wb, G, g0,
+                                   hb, ldh_g, sl_off, sl_ids, start, nt, logits);
+            if ((e = hipGetLastError()) != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
+    // gathered: persistent-style grid, groups interleaved
+    int64_t per_group = (max_rows + kTileRows - 1) / kTileRows;
+    const int64_t want = (2LL * device_cu_count() + G - 1) / G;
+    if (per_group > want)
+        per_group = want;
+    if (per_group < 1)
+        per_group = 1;
+    const unsigned blocks = (unsigned)(per_group * G);
+    const int ts = (int)per_group;
+    for (int n0 = 0; n0 < m; n0 += 64) {  // passes of up to 64 head rows
+        if (m - n0 > 32)
+            hipLaunchKernelGGL(head_gathered_kernel<2>, dim3(blocks), dim3(256), 0, s, V, d, Wb, G, m,
+                               n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
+        else
+            hipLaunchKernelGGL(head_gathered_kernel<1>, dim3(blocks), dim3(256), 0, s, V, d, Wb, G, m,
+                               n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace ds

@@ -26,9 +26,19 @@ hipError_t build_launch(hipStream_t s, int n, int M, int V, const int32_t *sel,
                         int64_t capacity, int64_t *sl_off, int32_t *sl_ids, int32_t *err_flag,
                         void *ws);
 
+// gathered head: GEMV kernel (few head rows, few groups or fp32), or the
+// matrix-core kernels (bf16 with >= kUnionMinGroups single-row groups, or
+// >= kGatheredMinRows head rows per group)
+constexpr int kUnionMinGroups = 8;
+constexpr int kGatheredMinRows = 8;
+size_t head_ws_bytes(int G, int m, int V);
+bool head_mfma_applies(bool bf16, int V, int d, int G, int m);
+hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, int m,
+                            const void *h, int64_t ldh_g, const int64_t *sl_off,
+                            const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws);
 hipError_t head_launch(hipStream_t s, bool bf16, int V, int d, const void *W, int G, int m,
                        const void *h, int64_t ldh_g, const int64_t *sl_off,
-                       const int32_t *sl_ids, int64_t max_rows, float *logits);
+                       const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws);
 
 size_t sample_ws_bytes(int64_t rows, int64_t max_len);
 hipError_t sample_launch(hipStream_t s, int G, int m, const int64_t *sl_off,

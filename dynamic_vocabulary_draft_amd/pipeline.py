@@ -95,6 +95,7 @@ class DraftStep:
         if cfg.is_tree:
             nbytes = max(nbytes, N.sample_workspace_bytes(B, m, int(self.max_len.max())))
         self.ws = N.workspace(nbytes, device)
+        self.head_ws = N.workspace(N.head_workspace_bytes(B, m, V), device)
         self.router_stream = torch.cuda.Stream(device=device)
         if self.target_logits is not None:
             self.p = torch.empty(B, T + 1, V, **f32)
@@ -130,6 +131,10 @@ class DraftStep:
 
     def set_W_positions(self, Ws: list[torch.Tensor] | None) -> None:
         """One head matrix per draft position (None: W everywhere)."""
+        if self._args is None:
+            if Ws is not None:
+                raise ValueError("per-position head matrices apply to chain drafting only")
+            return
         if Ws is None:
             self._W_pos, self._args.W_pos = None, None
             return
@@ -139,10 +144,12 @@ class DraftStep:
         self._args.W_pos = ctypes.cast(self._W_pos, ctypes.c_void_p)
 
     def set_head_events(self, events) -> None:
-        """events: ctypes array of 2T hipEvent_t handles (or None)."""
+        """events: ctypes array of hipEvent_t handles recorded around every
+        head launch, two per position (2T for chains, 2 for trees), or None."""
         self._head_events = events
-        self._args.head_events = (None if events is None
-                                  else ctypes.cast(events, ctypes.c_void_p))
+        if self._args is not None:
+            self._args.head_events = (None if events is None
+                                      else ctypes.cast(events, ctypes.c_void_p))
 
     def draft(self, stream=None) -> None:
         stream = stream or torch.cuda.current_stream()
@@ -178,8 +185,14 @@ class DraftStep:
         N.build_shortlist(self.sel[0], self.n_sel[0], self.cluster_of, self.cluster_index,
                           self.capacity, self.sl_off, self.sl_ids, self.err_flag,
                           self.ws[zbytes:zbytes + bbytes], stream=stream)
+        ev = getattr(self, "_head_events", None)
+        if ev is not None:
+            N.event_record(ev[0], stream)
         N.gathered_lm_head(self.W, self.h[:, 1:], self.sl_off, self.sl_ids, self.max_rows[0],
-                           self.logits, G=B, m=m, ldh_g=(1 + m) * d, stream=stream)
+                           self.logits, self.head_ws, G=B, m=m, ldh_g=(1 + m) * d,
+                           stream=stream)
+        if ev is not None:
+            N.event_record(ev[1], stream)
         N.shortlist_sample(self.sl_off, self.sl_ids, self.logits, self.temperature,
                            self.u_draft, self.token, self.q, self.ws,
                            max_len=int(self.max_len[0]), m=m, stream=stream)

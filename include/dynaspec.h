@@ -164,16 +164,24 @@ ds_status ds_build_shortlist(hipStream_t s, int n, int M, int V, const int32_t *
  *         at most 16 KB (d <= 8192 bf16, <= 4096 fp32).
  * G, m    groups (shortlists) and head rows per group (1 <= m <= 256).
  * h       row (g, i) at h + g*ldh_g + i*d elements (ldh_g >= m*d).
- * sl_off  [G+1] absolute offsets, sl_ids the token ids (ascending per group
- *         is not required by this call).
+ * sl_off  [G+1] absolute offsets, sl_ids the token ids.
  * max_rows host-side upper bound of sl_off[G] - sl_off[0]; sizes the grid
  *         (rows past the true total are skipped on the device).
  * logits  output, entry (g, i, j) at m*sl_off[g] + i*len_g + j.
- * Token ids outside [0, V) give NaN.
+ * ws      >= ds_head_workspace_bytes(G, m, V) bytes (may be NULL when that
+ *         is 0).
+ * Token ids outside [0, V) give NaN.  Kernel choice: bf16 heads with
+ * G >= 8 single-row groups (batched drafting) walk W once in token order on
+ * the matrix cores and write only shortlisted (row, group) pairs -- this
+ * path requires every shortlist to be ascending; bf16 heads with m >= 8
+ * (tree drafting) run a gathered matrix-core GEMM per group; everything
+ * else streams the shortlisted rows as a GEMV.
  */
+size_t ds_head_workspace_bytes(int G, int m, int V);
 ds_status ds_gathered_lm_head(hipStream_t s, ds_dtype dt, int V, int d, const void *W, int G,
                               int m, const void *h, int64_t ldh_g, const int64_t *sl_off,
-                              const int32_t *sl_ids, int64_t max_rows, float *logits);
+                              const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
+                              size_t ws_bytes);
 
 /*
  * Draft proposal from the shortlist distribution [A; S "Pipeline Flow"].

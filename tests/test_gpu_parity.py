@@ -223,8 +223,12 @@ def _random_shortlists(g, V, lens, base=0):
 
 @pytest.mark.parametrize("bf16,d", [(False, 256), (True, 264), (True, 3840), (True, 4096),
                                     (False, 1032)])
-@pytest.mark.parametrize("G,m", [(1, 1), (3, 1), (4, 3), (2, 64)])
+@pytest.mark.parametrize("G,m", [(1, 1), (3, 1), (4, 3), (2, 64), (16, 1), (64, 1), (70, 1),
+                                 (3, 8), (2, 100)])
 def test_head_parity(N, oracle_lib, bf16, d, G, m):
+    """GEMV path (fp32, or few single-row groups), union matrix-core path
+    (bf16, >= 8 single-row groups; 70 groups take two column passes) and
+    gathered matrix-core path (bf16, >= 8 head rows; 100 rows take two)."""
     V = 5000
     g = np.random.default_rng(d * 31 + G * 7 + m)
     cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=50, dtype=syn.DT_BF16 if bf16 else syn.DT_F32)
@@ -246,6 +250,43 @@ def test_head_parity(N, oracle_lib, bf16, d, G, m):
         got = _cpu(logits)[m * base:]
         assert not np.isnan(got).any()
         _logit_bar(got, ref, bf16)
+
+
+@pytest.mark.parametrize("G,m", [(3, 1), (16, 1), (3, 8)])
+def test_head_invalid_ids_are_nan(N, oracle_lib, G, m):
+    """Ids outside [0, V) give NaN on every kernel path (GEMV, union, gathered);
+    the valid entries of the same ascending shortlists are unaffected.  The
+    ids >= V include ones inside the last 32-token tile."""
+    V, d, bf16 = 5000, 264, True
+    g = np.random.default_rng(900 + G * 10 + m)
+    cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=50, dtype=syn.DT_BF16)
+    cluster_of, _ = _clusters(V, 50, 3)
+    W = syn.make_lm_head(cfg, cluster_of)
+    h = _store(g.standard_normal((G, m, d)).astype(np.float32), bf16)
+    lens = [int(x) for x in g.integers(50, 400, size=G)]
+    sl_off, sl_ids = _random_shortlists(g, V, lens)
+    bad = np.zeros(sl_ids.shape[0], bool)
+    for k in range(G):
+        a, b = int(sl_off[k]), int(sl_off[k + 1])
+        if k % 2 == 0:
+            sl_ids[a:a + 2] = [-7, -1]
+            bad[a:a + 2] = True
+        sl_ids[b - 3:b] = [V, V + 3, 2 ** 31 - 1]
+        bad[b - 3:b] = True
+        sl_ids[a:b] = np.sort(sl_ids[a:b])
+    ref = oracle_lib.gathered_lm_head(W, h, sl_off, np.where(bad, 0, sl_ids).astype(np.int32))
+    logits = torch.zeros(m * int(sl_off[-1]), device="cuda")
+    N.gathered_lm_head(to_dev(W), to_dev(h), to_dev(sl_off), to_dev(sl_ids), int(sl_off[-1]),
+                       logits)
+    got = _cpu(logits)
+    bad_m = np.zeros(got.shape[0], bool)
+    for k in range(G):
+        a, b = int(sl_off[k]), int(sl_off[k + 1])
+        for i in range(m):
+            bad_m[m * a + i * (b - a): m * a + (i + 1) * (b - a)] = bad[a:b]
+    assert np.isnan(got[bad_m]).all()
+    assert not np.isnan(got[~bad_m]).any()
+    _logit_bar(got[~bad_m], ref[~bad_m], bf16)
 
 
 def test_head_full_vocabulary_is_dense(N, oracle_lib):

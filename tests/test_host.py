@@ -100,7 +100,7 @@ def test_select_build_head_sample_verify_reject_bad_arguments(N):
     head = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
         ("s", None), ("dt", N.BF16), ("V", 100), ("d", 64), ("W", FAKE), ("G", 2), ("m", 1),
         ("h", FAKE), ("ldh_g", 64), ("sl_off", FAKE), ("sl_ids", FAKE), ("max_rows", 10),
-        ("logits", FAKE)]]
+        ("logits", FAKE), ("ws", None), ("ws_bytes", 0)]]
     assert L.ds_gathered_lm_head(*head(W=None)) == 1
     assert L.ds_gathered_lm_head(*head(dt=5)) == 2
     assert L.ds_gathered_lm_head(*head(d=62, ldh_g=62)) == 3
@@ -109,6 +109,8 @@ def test_select_build_head_sample_verify_reject_bad_arguments(N):
     assert L.ds_gathered_lm_head(*head(d=8200, ldh_g=8200)) == 3
     assert L.ds_gathered_lm_head(*head(dt=N.F32, d=4104, ldh_g=4104)) == 3
     assert L.ds_gathered_lm_head(*head(max_rows=-1)) == 1
+    assert L.ds_gathered_lm_head(*head(G=16)) == 1  # union path needs its workspace
+    assert N.head_workspace_bytes(16, 1, 100) > 0 and N.head_workspace_bytes(4, 1, 100) == 0
     smp = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
         ("s", None), ("G", 2), ("m", 1), ("sl_off", FAKE), ("sl_ids", FAKE), ("logits", FAKE),
         ("tau", C.c_float(1.0)), ("u", FAKE), ("max_len", 100), ("token", FAKE), ("q", FAKE),
