@@ -20,7 +20,8 @@
 //   with all G hidden vectors (columns of the MFMA), and writes only the
 //   (row, group) pairs on that group's shortlist.  A pre-pass over the
 //   shortlists records, per group and 32-token tile, where the tile's
-//   entries start in the group's shortlist (shortlists are ascending).
+//   entries start in the group's shortlist (shortlists are ascending) and
+//   which of the tile's 32 tokens they are.
 // gathered (tree drafting: m head rows share one shortlist): a gathered
 //   GEMM per group, rows = shortlist entries (gathered W rows), columns =
 //   the m head rows; workgroups of different groups with the same tile
@@ -201,40 +202,88 @@ __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], i
 }
 
 // ------------------------------------------------------------------ union
-// start[g][t] = first index j of group g's shortlist with S_g[j] >= 32*t,
-// t = 0..nt (nt = ceil(V/32)); written only for non-empty groups.  Entries
-// with ids outside [0, V) get their NaN logit here.
-__global__ __launch_bounds__(256) void union_start_kernel(int G, int nt, int V,
+// Tile index of the shortlists, per group g and 32-token tile t (t = 0..nt,
+// nt = ceil(V/32)): start = first index j of S_g with S_g[j] >= 32*t, mask =
+// the set of offsets y - 32*t of the tile's ids y < V on S_g.  Shortlists are
+// ascending, so a tile's entries are contiguous and the first of them builds
+// the tile's mask from at most 32 following entries.  Written only for
+// non-empty groups.  Entries with ids outside [0, V) get their NaN logit here.
+struct TileIx {
+    int32_t start;
+    uint32_t mask;
+};
+
+__global__ __launch_bounds__(256) void union_index_kernel(int G, int nt, int V,
                                                           const int64_t *__restrict__ sl_off,
                                                           const int32_t *__restrict__ sl_ids,
-                                                          int32_t *__restrict__ start,
+                                                          TileIx *__restrict__ tix,
                                                           float *__restrict__ logits)
 {
+    const int lane = lane_id();
     const int64_t beg = sl_off[0], end = sl_off[G];
-    for (int64_t J = beg + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; J < end;
-         J += (int64_t)gridDim.x * blockDim.x) {
-        int lo = 0, hi = G;  // group: last g with sl_off[g] <= J
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (sl_off[mid] <= J)
-                lo = mid;
-            else
-                hi = mid;
-        }
-        const int g = lo;
-        const int64_t j = J - sl_off[g], len = sl_off[g + 1] - sl_off[g];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    // the loop runs the same number of times in every lane of a wave (the
+    // mask below combines lanes), so lanes past the end carry an empty key
+    for (int64_t J0 = beg + (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~(kWave - 1));
+         J0 < end; J0 += stride) {
+        const int64_t J = J0 + lane;
+        const bool in = J < end;
+        int g = 0;
+        int64_t gbeg = 0, j = 0, len = 0, tc = -1, tp = -1;
+        int32_t yJ = -1;
         auto tile = [nt](int32_t y) { return y < 0 ? -1 : min((int64_t)(y >> 5), (int64_t)nt); };
-        const int32_t yJ = sl_ids[J];
-        if (yJ < 0 || yJ >= V)
-            logits[J] = __builtin_nanf("");
-        const int64_t tc = tile(yJ);
-        const int64_t tp = j > 0 ? tile(sl_ids[J - 1]) : -1;
-        int32_t *row = start + (int64_t)g * (nt + 1);
-        for (int64_t t = tp + 1; t <= tc; ++t)
-            row[t] = (int32_t)j;
+        if (in) {
+            int lo = 0, hi = G;  // group: last g with sl_off[g] <= J
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (sl_off[mid] <= J)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            g = lo;
+            gbeg = sl_off[g];
+            j = J - gbeg;
+            len = sl_off[g + 1] - gbeg;
+            yJ = sl_ids[J];
+            if (yJ < 0 || yJ >= V)
+                logits[J] = __builtin_nanf("");
+            tc = tile(yJ);
+            tp = j > 0 ? tile(sl_ids[J - 1]) : -1;
+        }
+        // mask of tile tc: OR over the following lanes with the same (group,
+        // tile) key -- a contiguous run of lanes, as the shortlist ascends
+        const int64_t key = in && tc >= 0 ? (int64_t)g * (nt + 1) + tc : -1 - lane;
+        uint32_t m = (in && yJ >= 0 && yJ < V) ? 1u << (yJ & 31) : 0u;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t mo = __shfl_down(m, o);
+            const int64_t ko = __shfl_down(key, o);
+            if (lane + o < kWave && ko == key)
+                m |= mo;
+        }
+        const int64_t last_key = __shfl(key, kWave - 1);  // all lanes, before any branch
+        if (!in)
+            continue;
+        TileIx *row = tix + (int64_t)g * (nt + 1);
+        for (int64_t t = tp + 1; t < tc; ++t)  // tiles without entries
+            row[t] = TileIx{(int32_t)j, 0u};
+        if (tc > tp) {  // first entry of tile tc
+            // the run may continue past this wave: those entries are read here
+            int64_t e = j + (kWave - lane);
+            if (last_key == key)
+                for (; e < len && e < j + 32; ++e) {
+                    const int32_t y = sl_ids[gbeg + e];
+                    if (tile(y) != tc)
+                        break;
+                    if (y < V)
+                        m |= 1u << (y & 31);
+                }
+            row[tc] = TileIx{(int32_t)j, m};
+        }
         if (j == len - 1)
             for (int64_t t = (tc < 0 ? 0 : tc + 1); t <= nt; ++t)
-                row[t] = (int32_t)len;
+                row[t] = TileIx{(int32_t)len, 0u};
     }
 }
 
@@ -242,8 +291,7 @@ template <int NB>
 __global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uint16_t *__restrict__ W,
                                                          int G, int g0, const uint16_t *__restrict__ h,
                                                          int64_t ldh_g, const int64_t *__restrict__ sl_off,
-                                                         const int32_t *__restrict__ sl_ids,
-                                                         const int32_t *__restrict__ start, int nt,
+                                                         const TileIx *__restrict__ tix, int nt,
                                                          float *__restrict__ logits)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[NB * 32 * lds_row<NB>()];
@@ -260,15 +308,42 @@ __global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uin
     __syncthreads();
     for (int q = threadIdx.x; q < ng * 4; q += blockDim.x) {
         const int g = g0 + q / 4, t = (int)(y0 >> 5) + q % 4;
-        if (t < nt && sl_off[g + 1] > sl_off[g]) {
-            const int32_t *st = start + (int64_t)g * (nt + 1);
-            if (st[t + 1] > st[t])
-                s_any = 1;
-        }
+        if (t < nt && sl_off[g + 1] > sl_off[g] && tix[(int64_t)g * (nt + 1) + t].mask != 0u)
+            s_any = 1;
     }
     __syncthreads();
     if (!s_any)
         return;
+
+    // where this lane's groups put the tile's logits, fetched before the
+    // K loop (lane l, column block nb: group g0 + 32*nb + l%32); wave 0
+    // records where each group's run for the block's four tiles begins
+    __shared__ int64_t s_dst[NB * 32];
+    __shared__ int32_t s_s0[NB * 32], s_cnt[NB * 32];
+    int64_t o_off[NB];
+    TileIx o_ix[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int gl = nb * 32 + (lane & 31);
+        o_off[nb] = 0;
+        o_ix[nb] = TileIx{0, 0u};
+        if (gl < ng && t32 < nt) {
+            const int g = g0 + gl;
+            const int64_t off = sl_off[g], len = sl_off[g + 1] - off;
+            if (len > 0) {
+                o_off[nb] = off;
+                o_ix[nb] = tix[(int64_t)g * (nt + 1) + t32];
+                const int64_t a0 = o_ix[nb].start;  // entries a0 .. a0+popc(mask)-1 < len
+                if (a0 < 0 || a0 + __popc(o_ix[nb].mask) > len)
+                    o_ix[nb].mask = 0u;
+            }
+        }
+        if (wave == 0 && lane < 32) {
+            s_dst[gl] = o_off[nb] + o_ix[nb].start;
+            s_s0[gl] = o_ix[nb].start;
+            s_cnt[gl] = 0;
+        }
+    }
 
     // the block's W rows y0 .. y0+127 (rows past V read zero; never written)
     const int64_t rows = min((int64_t)kTileRows, (int64_t)V - y0);
@@ -281,39 +356,34 @@ __global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uin
     auto hsrc = [&](int r) { return h + (int64_t)(g0 + r) * ldh_g; };
     rows_times_b<NB>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc, acc);
 
-    // epilogue: (row, group) pairs on the group's shortlist
-    const int64_t tbase = (int64_t)t32 * 32;
+    // epilogue: the (row, group) pairs on the group's shortlist.  A group's
+    // entries for the block's four tiles are one contiguous run of its
+    // logits; the values are gathered per group in LDS (the phase buffer,
+    // free after the K loop) and each run is written with coalesced stores.
+    float *res = reinterpret_cast<float *>(lds);  // [NB*32][kTileRows]
+    static_assert(sizeof(lds) >= NB * 32 * kTileRows * sizeof(float), "LDS run buffer");
+    __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int gl = nb * 32 + (lane & 31);
-        if (gl >= ng || t32 >= nt)
-            continue;
-        const int g = g0 + gl;
-        const int64_t off = sl_off[g], len = sl_off[g + 1] - off;
-        if (len <= 0)
-            continue;
-        const int32_t *st = start + (int64_t)g * (nt + 1);
-        int64_t a0 = st[t32], a1 = st[t32 + 1];
-        a0 = a0 < 0 ? 0 : (a0 > len ? len : a0);
-        a1 = a1 < a0 ? a0 : (a1 > len ? len : a1);
-        if (a1 - a0 > 32)
-            a1 = a0 + 32;
-        uint32_t mask = 0;
-        for (int64_t e = a0; e < a1; ++e) {
-            const int32_t id = sl_ids[off + e];
-            const int64_t o = (int64_t)id - tbase;
-            if (o >= 0 && o < 32 && id < V)  // ids outside [0, V): NaN from the pre-pass
-                mask |= 1u << o;
-        }
+        uint32_t mask = o_ix[nb].mask;
+        const int base = o_ix[nb].start - s_s0[gl];  // entries of earlier tiles of the block
+        if (base < 0 || base + __popc(mask) > kTileRows)
+            mask = 0u;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int mrow = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if ((mask >> mrow) & 1u) {
-                const int64_t pos = a0 + __popc(mask & ((1u << mrow) - 1u));
-                if (pos < len)
-                    logits[off + pos] = acc[nb][r];
-            }
+            if ((mask >> mrow) & 1u)
+                res[gl * kTileRows + base + __popc(mask & ((1u << mrow) - 1u))] = acc[nb][r];
         }
+        if (mask != 0u && lane < 32)
+            atomicMax(&s_cnt[gl], base + __popc(mask));
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < ng * kTileRows; q += blockDim.x) {
+        const int gl = q / kTileRows, k = q % kTileRows;
+        if (k < s_cnt[gl])
+            logits[s_dst[gl] + k] = res[q];
     }
 }
 
@@ -375,7 +445,7 @@ size_t head_ws_bytes(int G, int m, int V)
     if (G < kUnionMinGroups || m != 1)
         return 0;
     const int64_t nt = ((int64_t)V + 31) / 32;
-    return (size_t)G * (size_t)(nt + 1) * sizeof(int32_t) + 256;
+    return (size_t)G * (size_t)(nt + 1) * sizeof(TileIx) + 256;
 }
 
 bool head_mfma_applies(bool bf16, int V, int d, int G, int m)
@@ -397,25 +467,26 @@ hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, i
     hipError_t e;
     if (m == 1) {
         const int nt = (V + 31) / 32;
-        int32_t *start = reinterpret_cast<int32_t *>(ws);
+        TileIx *tix = reinterpret_cast<TileIx *>(ws);
+        // one entry per thread: each does a dependent search, so the
+        // latency is hidden by having every entry in flight at once
         int64_t blocks = (max_rows + 255) / 256;
-        const int64_t cap = 4LL * device_cu_count();
-        if (blocks > cap)
-            blocks = cap;
+        if (blocks > 65535)
+            blocks = 65535;
         if (blocks < 1)
             blocks = 1;
-        hipLaunchKernelGGL(union_start_kernel, dim3((unsigned)blocks), dim3(256), 0, s, G, nt, V,
-                           sl_off, sl_ids, start, logits);
+        hipLaunchKernelGGL(union_index_kernel, dim3((unsigned)blocks), dim3(256), 0, s, G, nt, V,
+                           sl_off, sl_ids, tix, logits);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
         const unsigned tiles = (unsigned)((V + kTileRows - 1) / kTileRows);
         for (int g0 = 0; g0 < G; g0 += 64) {  // column passes of up to 64 groups
             if (G - g0 > 32)
                 hipLaunchKernelGGL(head_union_kernel<2>, dim3(tiles), dim3(256), 0, s, V, d, Wb, G, g0,
-                                   hb, ldh_g, sl_off, sl_ids, start, nt, logits);
+                                   hb, ldh_g, sl_off, tix, nt, logits);
             else
                 hipLaunchKernelGGL(head_union_kernel<1>, dim3(tiles), dim3(256), 0, s, V, d, Wb, G, g0,
-                                   hb, ldh_g, sl_off, sl_ids, start, nt, logits);
+                                   hb, ldh_g, sl_off, tix, nt, logits);
             if ((e = hipGetLastError()) != hipSuccess)
                 return e;
         }

@@ -252,6 +252,33 @@ def test_head_parity(N, oracle_lib, bf16, d, G, m):
         _logit_bar(got, ref, bf16)
 
 
+@pytest.mark.parametrize("drop", [0, 37])
+def test_head_union_dense_shortlists(N, oracle_lib, drop):
+    """Batched path with shortlists covering (nearly) all of V: every 32-token
+    tile is full or nearly so, and runs of one tile's entries cross the
+    boundaries between the waves that index them."""
+    V, d, G = 4999, 264, 9
+    g = np.random.default_rng(4242 + drop)
+    cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=50, dtype=syn.DT_BF16)
+    cluster_of, _ = _clusters(V, 50, 3)
+    W = syn.make_lm_head(cfg, cluster_of)
+    h = _store(g.standard_normal((G, 1, d)).astype(np.float32), True)
+    ids = []
+    for k in range(G):
+        keep = np.ones(V, bool)
+        if drop:
+            keep[g.choice(V, drop * (k + 1), replace=False)] = False
+        ids.append(np.nonzero(keep)[0].astype(np.int32))
+    sl_off = np.concatenate([[0], np.cumsum([len(x) for x in ids])]).astype(np.int64)
+    sl_ids = np.concatenate(ids)
+    ref = oracle_lib.gathered_lm_head(W, h, sl_off, sl_ids)
+    logits = torch.full((int(sl_off[-1]),), float("nan"), device="cuda")
+    N.gathered_lm_head(to_dev(W), to_dev(h), to_dev(sl_off), to_dev(sl_ids), int(sl_off[-1]), logits)
+    got = _cpu(logits)
+    assert not np.isnan(got).any()
+    _logit_bar(got, ref, True)
+
+
 @pytest.mark.parametrize("G,m", [(3, 1), (16, 1), (3, 8)])
 def test_head_invalid_ids_are_nan(N, oracle_lib, G, m):
     """Ids outside [0, V) give NaN on every kernel path (GEMV, union, gathered);
