@@ -4,14 +4,16 @@
 // sampling), and the full-vocabulary target softmax (same normalisation on
 // dense rows).
 //
-// Both run as the two chunked launches of dist.h, one 256-thread workgroup
-// per 1024-element chunk of a row, so a 29K-entry shortlist is spread over
-// 29 workgroups instead of one:
+// Both run as the two chunked launches of dist.h over 1024-element chunks,
+// one 256-thread workgroup per chunk when the launch is small (a 29K-entry
+// shortlist is spread over 29 workgroups instead of one), several
+// consecutive chunks per workgroup when it is large:
 //   stats: chunk max m_c (fp32, exact), its first index, and the chunk sum
 //          of exp((l - m_c) / T) in a fixed association;
 //   final: row max M from the chunk maxima, chunk sums rescaled to M, their
 //          prefixes and the row total rebuilt identically by every
-//          workgroup; q (or p) = exp((l - M) / T) / total written as fp32;
+//          workgroup; q (or p) = exp((l - M) / T) * (1 / total) written as
+//          fp32 (within one fp32 ulp of the quotient);
 //          the workgroup owning the threshold u * total walks its chunk.
 // Temperature 0 is the argmax (ties to the lowest index) with one-hot q.
 #include <float.h>
@@ -50,13 +52,25 @@ struct Dense {
     }
 };
 
+// this lane's four consecutive elements (-FLT_MAX past the row end); one
+// 16-byte load when the row base is 16-byte aligned (j0 is a multiple of 4)
 __device__ __forceinline__ void load4(const float *__restrict__ l, int64_t j0, int64_t len,
                                       float v[4])
 {
+    const bool vec = (reinterpret_cast<uintptr_t>(l) & 15) == 0;
+    if (vec && j0 + 3 < len) {
+        const float4 q = *reinterpret_cast<const float4 *>(l + j0);
+        v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         v[k] = j0 + k < len ? l[j0 + k] : -FLT_MAX;
 }
+
+// (x) / T; T = 1 (the usual case, and always for the target) skips the
+// fp64 division, which leaves the value unchanged
+__device__ __forceinline__ double over_tau(double x, double tau) { return tau == 1.0 ? x : x / tau; }
 
 // row max from the chunk maxima (order-independent), into every thread
 __device__ float row_max(const float *__restrict__ cmax, int nch, float *sh)
@@ -74,8 +88,9 @@ __device__ float row_max(const float *__restrict__ cmax, int nch, float *sh)
     return r;
 }
 
-// chunk max m_c, first index of it, and the chunk sum of exp((l - m_c)/T)
-template <class L>
+// chunk max m_c, first index of it, and the chunk sum of exp((l - m_c)/T);
+// a workgroup handles R consecutive chunks of a row, all loads issued first
+template <class L, int R>
 __global__ __launch_bounds__(kChunkThreads) void norm_stats_kernel(L layout,
                                                                    const float *__restrict__ in,
                                                                    double tau, int64_t nchmax,
@@ -84,32 +99,43 @@ __global__ __launch_bounds__(kChunkThreads) void norm_stats_kernel(L layout,
     __shared__ float s_max[4];
     __shared__ int s_idx[4];
     __shared__ double s_wt[4];
-    const int64_t row = blockIdx.y, c = blockIdx.x;
+    const int64_t row = blockIdx.y, c0 = (int64_t)blockIdx.x * R;
     int64_t off, len, ids_off;
     layout.locate(row, &off, &len, &ids_off);
-    if (c * kChunk >= len)
+    if (c0 * kChunk >= len)
         return;
     ChunkWs w = chunk_ws(ws, rows, nchmax);
-    const int64_t j0 = c * kChunk + (threadIdx.x >> 6) * 256 + lane_id() * 4;
-    float v[4];
-    load4(in + off, j0, len, v);
-    block_chunk_max(v, j0, s_max, s_idx, &w.cmax[row * nchmax + c], &w.cidx[row * nchmax + c]);
-    if (tau == 0.0)
-        return;
-    float mc = s_max[0];  // block_chunk_max ends after a barrier
-    for (int i = 1; i < 4; ++i)
-        mc = fmaxf(mc, s_max[i]);
-    double wt[4];
+    const int64_t jl = (threadIdx.x >> 6) * 256 + lane_id() * 4;  // lane's offset in a chunk
+    float v[R][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        wt[k] = j0 + k < len ? exp(((double)v[k] - (double)mc) / tau) : 0.0;
-    double incl;
-    double tot = wave_chunk_sum(wt, &incl);
-    if (lane_id() == 0)
-        s_wt[threadIdx.x >> 6] = tot;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        w.csum[row * nchmax + c] = ((s_wt[0] + s_wt[1]) + s_wt[2]) + s_wt[3];
+    for (int r = 0; r < R; ++r)
+        load4(in + off, (c0 + r) * kChunk + jl, len, v[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t c = c0 + r;
+        if (c * kChunk >= len || c >= nchmax)
+            break;
+        const int64_t j0 = c * kChunk + jl;
+        __syncthreads();  // the previous chunk's use of the shared scratch is over
+        block_chunk_max(v[r], j0, s_max, s_idx, &w.cmax[row * nchmax + c],
+                        &w.cidx[row * nchmax + c]);
+        if (tau == 0.0)
+            continue;
+        float mc = s_max[0];  // block_chunk_max ends after a barrier
+        for (int i = 1; i < 4; ++i)
+            mc = fmaxf(mc, s_max[i]);
+        double wt[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            wt[k] = j0 + k < len ? exp(over_tau((double)v[r][k] - (double)mc, tau)) : 0.0;
+        double incl;
+        double tot = wave_chunk_sum(wt, &incl);
+        if (lane_id() == 0)
+            s_wt[threadIdx.x >> 6] = tot;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            w.csum[row * nchmax + c] = ((s_wt[0] + s_wt[1]) + s_wt[2]) + s_wt[3];
+    }
 }
 
 // chunk sums rescaled to the row max: csum_c * exp((m_c - M)/T), into LDS
@@ -117,12 +143,14 @@ __device__ void rescaled_sums(const float *__restrict__ cmax, const double *__re
                               int nch, double mx, double tau, double *S)
 {
     for (int c = threadIdx.x; c < nch; c += blockDim.x)
-        S[c] = csum[c] * exp(((double)cmax[c] - mx) / tau);
+        S[c] = csum[c] * exp(over_tau((double)cmax[c] - mx, tau));
     __syncthreads();
 }
 
 // PICK: draw a token with u (sampler); otherwise only normalise (softmax).
-template <class L, bool PICK>
+// A workgroup handles R consecutive chunks of a row: the row statistics are
+// rebuilt once for all of them, after the chunks' loads have been issued.
+template <class L, bool PICK, int R>
 __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
     L layout, const float *__restrict__ in, double tau, int64_t nchmax, const void *ws,
     int64_t rows, const int32_t *__restrict__ sl_ids, const float *__restrict__ u,
@@ -134,19 +162,23 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
     __shared__ float s_f[4];
     __shared__ int s_owner, s_fallback;
     __shared__ int64_t s_pick[2];
-    const int64_t row = blockIdx.y, c = blockIdx.x;
+    const int64_t row = blockIdx.y, c0 = (int64_t)blockIdx.x * R;
     int64_t off, len, ids_off;
     layout.locate(row, &off, &len, &ids_off);
-    if (PICK && c == 0 && len <= 0 && threadIdx.x == 0)
+    if (PICK && c0 == 0 && len <= 0 && threadIdx.x == 0)
         token[row] = -1;
-    if (c * kChunk >= len)
+    if (c0 * kChunk >= len)
         return;
     ChunkWs w = chunk_ws(const_cast<void *>(ws), rows, nchmax);
     const int nch = (int)min(chunks_for(len), nchmax);  // rows beyond max_len: in bounds
+    const int64_t jl = (threadIdx.x >> 6) * 256 + lane_id() * 4;
+    float v[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        load4(in + off, (c0 + r) * kChunk + jl, (c0 + r) < nch ? len : 0, v[r]);
     const float *cmax = w.cmax + row * nchmax;
     const double *csum = w.csum + row * nchmax;
     const float mxf = row_max(cmax, nch, s_f);
-    const int64_t j0 = c * kChunk + (threadIdx.x >> 6) * 256 + lane_id() * 4;
 
     if (tau == 0.0) {  // argmax: the first chunk holding the max has its index
         if ((threadIdx.x >> 6) == 0) {
@@ -166,10 +198,16 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
         __syncthreads();
         const int64_t jstar = s_fallback;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (j0 + k < len)
-                out[off + j0 + k] = j0 + k == jstar ? 1.0f : 0.0f;
-        if (PICK && c == s_owner && threadIdx.x == 0)
+        for (int r = 0; r < R; ++r) {
+            const int64_t j0 = (c0 + r) * kChunk + jl;
+            if (c0 + r >= nch)
+                break;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (j0 + k < len)
+                    out[off + j0 + k] = j0 + k == jstar ? 1.0f : 0.0f;
+        }
+        if (PICK && s_owner >= c0 && s_owner < c0 + R && threadIdx.x == 0)
             token[row] = sl_ids[ids_off + jstar];
         return;
     }
@@ -177,20 +215,34 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
     const double mx = (double)mxf;
     rescaled_sums(cmax, csum, nch, mx, tau, S2);
     const double Z = row_prefix(S2, nch, P, S, &s_total);
-    double wt[4];
+    const double rZ = 1.0 / Z;  // q = w * (1/Z): within one fp32 ulp of w / Z
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        wt[k] = j0 + k < len ? exp(((double)in[off + j0 + k] - mx) / tau) : 0.0;
+    for (int r = 0; r < R; ++r) {
+        const int64_t j0 = (c0 + r) * kChunk + jl;
+        if (c0 + r >= nch)
+            break;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-        if (j0 + k < len)
-            out[off + j0 + k] = (float)(wt[k] / Z);
+        for (int k = 0; k < 4; ++k)
+            if (j0 + k < len)
+                out[off + j0 + k] = (float)(exp(over_tau((double)v[r][k] - mx, tau)) * rZ);
+    }
     if (!PICK)
         return;
     const double thr = (double)u[row] * Z;
     owner_chunk(P, S, nch, thr, &s_owner, &s_fallback);
-    if (c != s_owner)
+    const int64_t c = s_owner;
+    if (c < c0 || c >= c0 + R)
         return;
+    // the owner chunk's weights again (same operations, same values)
+    const int64_t j0 = c * kChunk + jl;
+    double wt[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (c0 + r == c) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                wt[k] = j0 + k < len ? exp(over_tau((double)v[r][k] - mx, tau)) : 0.0;
+        }
     double incl;
     double tot = wave_chunk_sum(wt, &incl);
     if (lane_id() == 0)
@@ -201,21 +253,35 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
         token[row] = sl_ids[ids_off + (pick < 0 ? 0 : pick)];
 }
 
+template <class L, bool PICK, int R>
+hipError_t launch_norm_r(hipStream_t s, L layout, int64_t rows, int64_t nchmax, const float *in,
+                         double tau, void *ws, const int32_t *sl_ids, const float *u,
+                         int32_t *token, float *out)
+{
+    dim3 grid((unsigned)((nchmax + R - 1) / R), (unsigned)rows);
+    hipLaunchKernelGGL((norm_stats_kernel<L, R>), grid, dim3(kChunkThreads), 0, s, layout, in, tau,
+                       nchmax, ws, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((norm_final_kernel<L, PICK, R>), grid, dim3(kChunkThreads), 0, s, layout,
+                       in, tau, nchmax, (const void *)ws, rows, sl_ids, u, token, out);
+    return hipGetLastError();
+}
+
+// Chunks per workgroup: one by default (a short shortlist still spreads
+// over many workgroups); four for long rows in large launches, where every
+// workgroup would otherwise rebuild the statistics of hundreds of chunks.
 template <class L, bool PICK>
 hipError_t launch_norm(hipStream_t s, L layout, int64_t rows, int64_t max_len, const float *in,
                        double tau, void *ws, const int32_t *sl_ids, const float *u,
                        int32_t *token, float *out)
 {
     const int64_t nchmax = chunks_for(max_len > 0 ? max_len : 1);
-    dim3 grid((unsigned)nchmax, (unsigned)rows);
-    hipLaunchKernelGGL((norm_stats_kernel<L>), grid, dim3(kChunkThreads), 0, s, layout, in, tau,
-                       nchmax, ws, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((norm_final_kernel<L, PICK>), grid, dim3(kChunkThreads), 0, s, layout, in,
-                       tau, nchmax, (const void *)ws, rows, sl_ids, u, token, out);
-    return hipGetLastError();
+    if (nchmax >= 64 && rows * nchmax / 4 >= 2048)
+        return launch_norm_r<L, PICK, 4>(s, layout, rows, nchmax, in, tau, ws, sl_ids, u, token,
+                                         out);
+    return launch_norm_r<L, PICK, 1>(s, layout, rows, nchmax, in, tau, ws, sl_ids, u, token, out);
 }
 
 }  // namespace

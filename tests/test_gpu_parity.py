@@ -374,11 +374,39 @@ def test_sample_many_rows_bit_exact(N, oracle_lib):
     assert tie.sum() <= 2
 
 
+@pytest.mark.parametrize("rows,maxlen", [(800, 12000), (150, 70000)])
+@pytest.mark.parametrize("tau", [1.0, float(np.float32(0.7)), 0.0])
+def test_sample_multi_chunk_workgroups(N, oracle_lib, rows, maxlen, tau):
+    """Ragged rows in large launches: 800 short rows (one chunk per
+    workgroup), 150 rows up to 70000 entries (four chunks per workgroup),
+    shorter rows ending inside a workgroup."""
+    g = np.random.default_rng(rows + int(tau * 10))
+    lens = g.integers(1, maxlen, size=rows)
+    lens[:3] = [1, 1024, maxlen]
+    sl_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    sl_ids = np.concatenate([np.sort(g.choice(10 ** 6, L, replace=False)) for L in lens])
+    sl_ids = sl_ids.astype(np.int32)
+    logits = (g.standard_normal(int(sl_off[-1])) * 3).astype(np.float32)
+    u = syn.make_uniforms(syn.CONFIGS[0], 9, rows, instance=rows)
+    tok_ref, q_ref, tie = oracle_lib.shortlist_sample(sl_off, sl_ids, logits, u, 1, tau)
+    token = torch.empty(rows, dtype=torch.int32, device="cuda")
+    q = torch.empty(logits.shape[0], dtype=torch.float32, device="cuda")
+    ws = N.workspace(N.sample_workspace_bytes(rows, 1, int(lens.max())))
+    N.shortlist_sample(to_dev(sl_off), to_dev(sl_ids), to_dev(logits), tau, to_dev(u), token, q,
+                       ws, max_len=int(lens.max()))
+    got = _cpu(token)
+    assert np.array_equal(got[~tie], tok_ref[~tie])
+    _ulp_bar(_cpu(q), q_ref)
+
+
 # ----------------------------------------------------------------------------
 # target_softmax and verify_reject
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("rows,V", [(3, 1000), (5, 128256), (2, 262144)])
+@pytest.mark.parametrize("rows,V", [(3, 1000), (5, 128256), (2, 262144), (40, 128256),
+                                    (70, 128256)])
 def test_target_softmax_parity(N, oracle_lib, rows, V):
+    """Single-chunk and multi-chunk workgroups (40 and 70 rows of 126 chunks
+    take 4 and 8 chunks per workgroup, the last one partial)."""
     g = np.random.default_rng(V)
     lg = (g.standard_normal((rows, V)) * 3).astype(np.float32)
     p = torch.empty(rows, V, device="cuda")
