@@ -17,9 +17,21 @@ finds its rows in the 256 MB memory-side cache from an earlier one.
 
 Printed: one JSON line (value = draft tokens/s of the whole step), with
 `roofline` for the gathered head (algorithmic bytes per launch / its mean
-duration, from HIP events recorded around every head launch of the timed
-steps on the head stream) and `cpu_baseline` (the CPU oracle, one core, on a
-bounded sample of the same workload).
+duration; the duration comes from HIP events stamped at the head kernels'
+own start and end, on eager replays of the timed steps, since events cannot
+be timed inside graphs) and `cpu_baseline` (the CPU oracle, one core, on a
+bounded sample of the same workload).  `roofline.traffic` is the head's
+measured HBM bytes per launch when profiles/head_gemv_traffic.json was made
+from the current head sources for this workload (see --pmc-probe).
+
+HBM traffic of the head (two profiler passes, then one parse):
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -- python3 bench.py --pmc-probe
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -- python3 bench.py --pmc-probe
+    python3 bench.py --traffic-from OUT/fetch OUT/write
+(all three with the same --probe-file)
+The probe runs eager steps of the workload, then a 1 GiB device-to-device
+copy; each counter of the head is scaled by known bytes / the counter of
+that copy.
 """
 from __future__ import annotations
 
@@ -120,6 +132,104 @@ def cpu_baseline(wl, seconds: float) -> dict:
                       % (n, cfg.T, el, os.cpu_count() or 0, model or platform.machine())}
 
 
+COPY_BYTES = 1 << 30
+
+
+def head_kernel_name(cfg) -> str:
+    from dynamic_vocabulary_draft_amd import synthetic as syn
+    hrows = cfg.tree_nodes if cfg.is_tree else 1
+    bf16 = cfg.dtype == syn.DT_BF16
+    if bf16 and hrows == 1 and cfg.B >= 8:
+        return "head_union_kernel"
+    if bf16 and hrows >= 8:
+        return "head_gathered_kernel"
+    return "head_gemv_kernel"
+
+
+def pmc_probe(args, cfg, steps, sizes, npos, stream, torch, np):
+    """Eager steps over every (instance, position), then a plain copy of
+    COPY_BYTES; writes the algorithmic bytes of each head launch, in launch
+    order, to --probe-file."""
+    e = cfg.elem_bytes
+    hrows = cfg.tree_nodes if cfg.is_tree else 1
+    n_steps = 2 * len(steps)
+    launch_bytes = []
+    with torch.cuda.stream(stream):
+        for k in range(n_steps):
+            i = k % len(steps)
+            steps[i].step(stream)
+            for t in range(npos):
+                sz = sizes[i][t]
+                launch_bytes.append(sz["union"] * cfg.d * e + sz["total"] * 4
+                                    + cfg.B * hrows * cfg.d * e + sz["total"] * hrows * 4)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    with open(args.probe_file, "w") as f:
+        json.dump({"workload": cfg.name, "head_kernel": head_kernel_name(cfg),
+                   "launch_bytes": launch_bytes, "copy_bytes": COPY_BYTES,
+                   "kernel_source_sha256": head_source_sha()}, f)
+    log("pmc probe: %d head launches, copy of %d bytes" % (len(launch_bytes), COPY_BYTES))
+
+
+def _counter_rows(d, counter):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc csv output."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((int(r.get("Dispatch_Id", 0)), r["Kernel_Name"],
+                                 float(r["Counter_Value"])))
+    rows.sort()
+    return [(k, v) for _, k, v in rows]
+
+
+def traffic_from(args):
+    with open(args.probe_file) as f:
+        probe = json.load(f)
+    out = {"workload": probe["workload"], "kernel_source_sha256": probe["kernel_source_sha256"]}
+    per = {}
+    for name, d in (("FETCH_SIZE", args.traffic_from[0]), ("WRITE_SIZE", args.traffic_from[1])):
+        rows = _counter_rows(d, name)
+        copy = [v for k, v in rows if "copy" in k.lower()]
+        head = [v for k, v in rows if probe["head_kernel"] in k]
+        if not copy or not head:
+            raise SystemExit("%s: copy or head dispatches missing" % name)
+        copy_kib = copy[-1]  # the probe's copy is its last dispatch
+        scale = probe["copy_bytes"] / (copy_kib * 1024.0)
+        per[name] = {"head_kib_mean": sum(head) / len(head), "launches": len(head),
+                     "copy_kib": copy_kib, "scale": scale,
+                     "bytes_per_launch": sum(head) / len(head) * 1024.0 * scale}
+    alg = sum(probe["launch_bytes"]) / len(probe["launch_bytes"])
+    out.update({
+        "head_kernel": probe["head_kernel"],
+        "fetch_bytes_per_launch": round(per["FETCH_SIZE"]["bytes_per_launch"]),
+        "write_bytes_per_launch": round(per["WRITE_SIZE"]["bytes_per_launch"]),
+        "bytes_per_launch": round(per["FETCH_SIZE"]["bytes_per_launch"]
+                                  + per["WRITE_SIZE"]["bytes_per_launch"]),
+        "algorithmic_bytes_per_launch": round(alg),
+        "fetch_scale": per["FETCH_SIZE"]["scale"], "write_scale": per["WRITE_SIZE"]["scale"],
+        "launches": per["FETCH_SIZE"]["launches"],
+        "copy_bytes": probe["copy_bytes"],
+        "copy_fetch_kib": per["FETCH_SIZE"]["copy_kib"],
+        "copy_write_kib": per["WRITE_SIZE"]["copy_kib"],
+    })
+    out["traffic_over_algorithmic"] = round(out["bytes_per_launch"] / alg, 4)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,10 +241,19 @@ def main():
                     help="all head launches read one copy of W (cache-warm)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run eager steps and a 1 GiB copy under a counter profiler, then exit")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc outputs of --pmc-probe into "
+                         "profiles/head_gemv_traffic.json and exit")
+    ap.add_argument("--probe-file", default=os.path.join(ROOT, "pmc_probe.json"),
+                    help="where --pmc-probe writes (and --traffic-from reads) the launch list")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying step graphs")
     args = ap.parse_args()
 
+    if args.traffic_from:
+        return traffic_from(args)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -189,6 +308,8 @@ def main():
         sizes.append(per)
         assert int(st.err_flag.item()) == 0
 
+    if args.pmc_probe:
+        return pmc_probe(args, cfg, steps, sizes, npos, stream, torch, np)
     timed_events = True
     graphs, mode = [], "eager"
     if not args.eager:
@@ -276,7 +397,8 @@ def main():
                 "mean_algorithmic_bytes": round(float(np.mean(nbytes)), 0),
                 "head_only_tokens_per_s": round(cfg.B * hrows / (mean_ms * 1e-3), 1),
                 "w_replicas": not args.no_replicas,
-                "timed_on": "eager steps (HIP events around each head launch)"}
+                "timed_on": "eager steps (HIP events stamped at each head's own kernel start "
+                             "and end)"}
     for g in graphs:
         g.close()
     ev.close()

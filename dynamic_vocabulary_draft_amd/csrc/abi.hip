@@ -261,6 +261,21 @@ ds_status ds_gathered_lm_head(hipStream_t s, ds_dtype dt, int V, int d, const vo
                                       max_rows, logits, ws));
 }
 
+ds_status ds_gathered_lm_head_timed(hipStream_t s, ds_dtype dt, int V, int d, const void *W, int G,
+                                    int m, const void *h, int64_t ldh_g, const int64_t *sl_off,
+                                    const int32_t *sl_ids, int64_t max_rows, float *logits,
+                                    void *ws, size_t ws_bytes, hipEvent_t start, hipEvent_t stop)
+{
+    ds_status st = check_head(dt, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows, logits);
+    if (st != DS_OK)
+        return st;
+    const size_t need = ds_head_workspace_bytes(G, m, V);
+    if (need && (!ws || ws_bytes < need))
+        return DS_EINVAL;
+    return hip_status(ds::head_launch(s, dt == DS_BF16, V, d, W, G, m, h, ldh_g, sl_off, sl_ids,
+                                      max_rows, logits, ws, start, stop));
+}
+
 size_t ds_sample_workspace_bytes(int G, int m, int64_t max_len)
 {
     return G > 0 && m > 0 && max_len > 0 ? ds::sample_ws_bytes((int64_t)G * m, max_len) : 0;
@@ -401,14 +416,12 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
             err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
         if (err == hipSuccess)
             err = hipEventRecord(g_events.ev[T + t], hs);
-        if (err == hipSuccess && a->head_events)
-            err = hipEventRecord(a->head_events[2 * t], hs);
         if (err == hipSuccess)
             err = ds::head_launch(hs, bf16, a->V, a->d, a->W_pos ? a->W_pos[t] : a->W, B, 1,
                                   hb + (size_t)(t + 1) * a->d * e, ldh, a->sl_off + rb, a->sl_ids,
-                                  a->max_rows[t], a->logits, hws);
-        if (err == hipSuccess && a->head_events)
-            err = hipEventRecord(a->head_events[2 * t + 1], hs);
+                                  a->max_rows[t], a->logits, hws,
+                                  a->head_events ? a->head_events[2 * t] : nullptr,
+                                  a->head_events ? a->head_events[2 * t + 1] : nullptr);
         if (err == hipSuccess)
             err = ds::sample_launch(hs, B, 1, a->sl_off + rb, a->sl_ids, a->logits, a->temperature,
                                     a->u_draft + rb, a->token + rb, a->q, a->max_len[t], sws);

@@ -4,6 +4,7 @@
 // run to run), and launch-error plumbing.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -159,6 +160,20 @@ __device__ __forceinline__ void raise_flag(int32_t *flag, int32_t code)
 // Host-side: compute units of the current device (cached per device id; the
 // first call on a device queries the runtime).
 int device_cu_count();
+
+// Host-side: launch `kernel`; non-null t0 / t1 are timing events stamped at
+// the kernel's own start / end (the dispatch's begin and end timestamps,
+// not the host-enqueue order), for measuring a kernel inside a sequence.
+template <typename K, typename... Args>
+inline hipError_t launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t t0,
+                               hipEvent_t t1, Args... args)
+{
+    if (t0 || t1)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t0, t1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+    return hipGetLastError();
+}
 
 }  // namespace ds
 

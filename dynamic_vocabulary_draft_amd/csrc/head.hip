@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void head_gemv_kernel(int V, int nch, const u3
 template <bool BF16, int KC>
 hipError_t launch_kc(hipStream_t s, int V, int nch, const void *W, int G, int m, const void *h,
                      int64_t ldh_g_ch, const int64_t *sl_off, const int32_t *sl_ids,
-                     int64_t max_rows, float *logits)
+                     int64_t max_rows, float *logits, hipEvent_t t0, hipEvent_t t1)
 {
     constexpr int RPW = (KC >= 8) ? 2 : 4;
     const int64_t waves = (max_rows + RPW - 1) / RPW;
@@ -154,42 +154,45 @@ hipError_t launch_kc(hipStream_t s, int V, int nch, const void *W, int G, int m,
     const int64_t cap = (int64_t)kBlocksPerCU * device_cu_count();
     if (blocks > cap)
         blocks = cap;
-    hipLaunchKernelGGL((head_gemv_kernel<BF16, KC, RPW>), dim3((unsigned)blocks), dim3(256), 0, s,
-                       V, nch, reinterpret_cast<const u32x4 *>(W), G, m,
-                       reinterpret_cast<const u32x4 *>(h), ldh_g_ch, sl_off, sl_ids, logits);
-    return hipGetLastError();
+    return launch_timed(head_gemv_kernel<BF16, KC, RPW>, dim3((unsigned)blocks), dim3(256), s, t0,
+                        t1, V, nch, reinterpret_cast<const u32x4 *>(W), G, m,
+                        reinterpret_cast<const u32x4 *>(h), ldh_g_ch, sl_off, sl_ids, logits);
 }
 
 template <bool BF16>
 hipError_t launch_dtype(hipStream_t s, int V, int d, const void *W, int G, int m, const void *h,
                         int64_t ldh_g, const int64_t *sl_off, const int32_t *sl_ids,
-                        int64_t max_rows, float *logits)
+                        int64_t max_rows, float *logits, hipEvent_t t0, hipEvent_t t1)
 {
     const int e = BF16 ? 2 : 4;
     const int nch = d * e / 16;                 // 16-byte chunks per row
     const int64_t ldh_g_ch = ldh_g * e / 16;    // group stride in chunks
     const int kc = (nch + kWave - 1) / kWave;
     if (kc <= 1)
-        return launch_kc<BF16, 1>(s, V, nch, W, G, m, h, ldh_g_ch, sl_off, sl_ids, max_rows, logits);
+        return launch_kc<BF16, 1>(s, V, nch, W, G, m, h, ldh_g_ch, sl_off, sl_ids, max_rows, logits, t0, t1);
     if (kc <= 2)
-        return launch_kc<BF16, 2>(s, V, nch, W, G, m, h, ldh_g_ch, sl_off, sl_ids, max_rows, logits);
+        return launch_kc<BF16, 2>(s, V, nch, W, G, m, h, ldh_g_ch, sl_off, sl_ids, max_rows, logits, t0, t1);
     if (kc <= 4)
-        return launch_kc<BF16, 4>(s, V, nch, W, G, m, h, ldh_g_ch, sl_off, sl_ids, max_rows, logits);
+        return launch_kc<BF16, 4>(s, V, nch, W, G, m, h, ldh_g_ch, sl_off, sl_ids, max_rows, logits, t0, t1);
     if (kc <= 8)
-        return launch_kc<BF16, 8>(s, V, nch, W, G, m, h, ldh_g_ch, sl_off, sl_ids, max_rows, logits);
-    return launch_kc<BF16, 16>(s, V, nch, W, G, m, h, ldh_g_ch, sl_off, sl_ids, max_rows, logits);
+        return launch_kc<BF16, 8>(s, V, nch, W, G, m, h, ldh_g_ch, sl_off, sl_ids, max_rows, logits, t0, t1);
+    return launch_kc<BF16, 16>(s, V, nch, W, G, m, h, ldh_g_ch, sl_off, sl_ids, max_rows, logits, t0, t1);
 }
 
 }  // namespace
 
 hipError_t head_launch(hipStream_t s, bool bf16, int V, int d, const void *W, int G, int m,
                        const void *h, int64_t ldh_g, const int64_t *sl_off,
-                       const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws)
+                       const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
+                       hipEvent_t t0, hipEvent_t t1)
 {
     if (head_mfma_applies(bf16, V, d, G, m))
-        return head_mfma_launch(s, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows, logits, ws);
-    return bf16 ? launch_dtype<true>(s, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows, logits)
-                : launch_dtype<false>(s, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows, logits);
+        return head_mfma_launch(s, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows, logits, ws,
+                                t0, t1);
+    return bf16 ? launch_dtype<true>(s, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows, logits,
+                                     t0, t1)
+                : launch_dtype<false>(s, V, d, W, G, m, h, ldh_g, sl_off, sl_ids, max_rows,
+                                      logits, t0, t1);
 }
 
 }  // namespace ds

@@ -460,7 +460,8 @@ bool head_mfma_applies(bool bf16, int V, int d, int G, int m)
 
 hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, int m,
                             const void *h, int64_t ldh_g, const int64_t *sl_off,
-                            const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws)
+                            const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
+                            hipEvent_t t0, hipEvent_t t1)
 {
     const uint16_t *Wb = reinterpret_cast<const uint16_t *>(W);
     const uint16_t *hb = reinterpret_cast<const uint16_t *>(h);
@@ -475,19 +476,19 @@ hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, i
             blocks = 65535;
         if (blocks < 1)
             blocks = 1;
-        hipLaunchKernelGGL(union_index_kernel, dim3((unsigned)blocks), dim3(256), 0, s, G, nt, V,
-                           sl_off, sl_ids, tix, logits);
-        if ((e = hipGetLastError()) != hipSuccess)
+        if ((e = launch_timed(union_index_kernel, dim3((unsigned)blocks), dim3(256), s, t0, nullptr,
+                              G, nt, V, sl_off, sl_ids, tix, logits)) != hipSuccess)
             return e;
         const unsigned tiles = (unsigned)((V + kTileRows - 1) / kTileRows);
         for (int g0 = 0; g0 < G; g0 += 64) {  // column passes of up to 64 groups
+            hipEvent_t stop = g0 + 64 >= G ? t1 : nullptr;
             if (G - g0 > 32)
-                hipLaunchKernelGGL(head_union_kernel<2>, dim3(tiles), dim3(256), 0, s, V, d, Wb, G, g0,
-                                   hb, ldh_g, sl_off, tix, nt, logits);
+                e = launch_timed(head_union_kernel<2>, dim3(tiles), dim3(256), s, nullptr, stop, V, d,
+                                 Wb, G, g0, hb, ldh_g, sl_off, (const TileIx *)tix, nt, logits);
             else
-                hipLaunchKernelGGL(head_union_kernel<1>, dim3(tiles), dim3(256), 0, s, V, d, Wb, G, g0,
-                                   hb, ldh_g, sl_off, tix, nt, logits);
-            if ((e = hipGetLastError()) != hipSuccess)
+                e = launch_timed(head_union_kernel<1>, dim3(tiles), dim3(256), s, nullptr, stop, V, d,
+                                 Wb, G, g0, hb, ldh_g, sl_off, (const TileIx *)tix, nt, logits);
+            if (e != hipSuccess)
                 return e;
         }
         return hipSuccess;
@@ -502,13 +503,14 @@ hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, i
     const unsigned blocks = (unsigned)(per_group * G);
     const int ts = (int)per_group;
     for (int n0 = 0; n0 < m; n0 += 64) {  // passes of up to 64 head rows
+        hipEvent_t start = n0 == 0 ? t0 : nullptr, stop = n0 + 64 >= m ? t1 : nullptr;
         if (m - n0 > 32)
-            hipLaunchKernelGGL(head_gathered_kernel<2>, dim3(blocks), dim3(256), 0, s, V, d, Wb, G, m,
-                               n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
+            e = launch_timed(head_gathered_kernel<2>, dim3(blocks), dim3(256), s, start, stop, V, d,
+                             Wb, G, m, n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
         else
-            hipLaunchKernelGGL(head_gathered_kernel<1>, dim3(blocks), dim3(256), 0, s, V, d, Wb, G, m,
-                               n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
-        if ((e = hipGetLastError()) != hipSuccess)
+            e = launch_timed(head_gathered_kernel<1>, dim3(blocks), dim3(256), s, start, stop, V, d,
+                             Wb, G, m, n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
+        if (e != hipSuccess)
             return e;
     }
     return hipSuccess;

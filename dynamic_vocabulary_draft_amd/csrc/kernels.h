@@ -33,12 +33,16 @@ constexpr int kUnionMinGroups = 8;
 constexpr int kGatheredMinRows = 8;
 size_t head_ws_bytes(int G, int m, int V);
 bool head_mfma_applies(bool bf16, int V, int d, int G, int m);
+// t0 / t1 (may be null): timing events stamped at the start of the first
+// and the end of the last kernel of the head
 hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, int m,
                             const void *h, int64_t ldh_g, const int64_t *sl_off,
-                            const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws);
+                            const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
+                            hipEvent_t t0, hipEvent_t t1);
 hipError_t head_launch(hipStream_t s, bool bf16, int V, int d, const void *W, int G, int m,
                        const void *h, int64_t ldh_g, const int64_t *sl_off,
-                       const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws);
+                       const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
+                       hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 size_t sample_ws_bytes(int64_t rows, int64_t max_len);
 hipError_t sample_launch(hipStream_t s, int G, int m, const int64_t *sl_off,

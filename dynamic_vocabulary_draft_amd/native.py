@@ -59,6 +59,8 @@ _SIGS = {
     "ds_head_workspace_bytes": (_sz, [_i, _i, _i]),
     "ds_gathered_lm_head": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i64, _vp, _vp, _i64, _vp, _vp,
                                  _sz]),
+    "ds_gathered_lm_head_timed": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i64, _vp, _vp, _i64, _vp,
+                                       _vp, _sz, _vp, _vp]),
     "ds_sample_workspace_bytes": (_sz, [_i, _i, _i64]),
     "ds_shortlist_sample": (_i, [_vp, _i, _i, _vp, _vp, _vp, _f, _vp, _i64, _vp, _vp, _vp, _sz]),
     "ds_softmax_workspace_bytes": (_sz, [_i, _i]),
@@ -208,18 +210,24 @@ def head_workspace_bytes(G: int, m: int, V: int) -> int:
 
 
 def gathered_lm_head(W, h, sl_off, sl_ids, max_rows, logits, ws=None, *, G=None, m=None,
-                     ldh_g=None, stream=None):
+                     ldh_g=None, stream=None, events=None):
     """h is [G][m][d] (or pass G, m, ldh_g for a strided view).  ws: at least
-    head_workspace_bytes(G, m, V) bytes (allocated here when None)."""
+    head_workspace_bytes(G, m, V) bytes (allocated here when None).  events:
+    optional (start, stop) raw hipEvent_t handles stamped at the head
+    kernels' own start and end (ds_gathered_lm_head_timed)."""
     V, d = W.shape
     if G is None:
         G, m = h.shape[0], h.shape[1]
         ldh_g = _ld(h)
     if ws is None:
         ws = workspace(head_workspace_bytes(G, m, V), W.device)
-    _check("ds_gathered_lm_head", lib.ds_gathered_lm_head(
-        _s(stream), _dt(W), V, d, _p(W), G, m, _p(h), ldh_g, _p(sl_off), _p(sl_ids),
-        int(max_rows), _p(logits), _p(ws), _nbytes(ws)))
+    args = (_s(stream), _dt(W), V, d, _p(W), G, m, _p(h), ldh_g, _p(sl_off), _p(sl_ids),
+            int(max_rows), _p(logits), _p(ws), _nbytes(ws))
+    if events is None:
+        _check("ds_gathered_lm_head", lib.ds_gathered_lm_head(*args))
+    else:
+        _check("ds_gathered_lm_head_timed", lib.ds_gathered_lm_head_timed(
+            *args, C.c_void_p(events[0]), C.c_void_p(events[1])))
 
 
 def shortlist_sample(sl_off, sl_ids, logits, temperature, u, token, q, ws, *, max_len, m=1,
@@ -268,23 +276,6 @@ class Graph:
             self.close()
         except Exception:
             pass
-
-
-_hip_rt = None
-
-
-def event_record(event: int, stream=None) -> None:
-    """hipEventRecord(event, stream) for a raw hipEvent_t handle (timing
-    events around launches made through this binding)."""
-    global _hip_rt
-    if _hip_rt is None:
-        rt = C.CDLL("libamdhip64.so")
-        rt.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
-        rt.hipEventRecord.restype = C.c_int
-        _hip_rt = rt
-    code = _hip_rt.hipEventRecord(C.c_void_p(event), _s(stream))
-    if code != 0:
-        raise RuntimeError("hipEventRecord failed: %d" % code)
 
 
 def capture(fn, stream) -> Graph:

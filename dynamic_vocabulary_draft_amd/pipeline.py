@@ -186,13 +186,9 @@ class DraftStep:
                           self.capacity, self.sl_off, self.sl_ids, self.err_flag,
                           self.ws[zbytes:zbytes + bbytes], stream=stream)
         ev = getattr(self, "_head_events", None)
-        if ev is not None:
-            N.event_record(ev[0], stream)
         N.gathered_lm_head(self.W, self.h[:, 1:], self.sl_off, self.sl_ids, self.max_rows[0],
                            self.logits, self.head_ws, G=B, m=m, ldh_g=(1 + m) * d,
-                           stream=stream)
-        if ev is not None:
-            N.event_record(ev[1], stream)
+                           stream=stream, events=None if ev is None else (ev[0], ev[1]))
         N.shortlist_sample(self.sl_off, self.sl_ids, self.logits, self.temperature,
                            self.u_draft, self.token, self.q, self.ws,
                            max_len=int(self.max_len[0]), m=m, stream=stream)

@@ -182,6 +182,16 @@ ds_status ds_gathered_lm_head(hipStream_t s, ds_dtype dt, int V, int d, const vo
                               int m, const void *h, int64_t ldh_g, const int64_t *sl_off,
                               const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
                               size_t ws_bytes);
+/*
+ * Same as ds_gathered_lm_head; start / stop (caller-created HIP events with
+ * timing enabled, either may be NULL) are stamped at the start of the first
+ * and the end of the last kernel the head launches, for measuring the head's
+ * own execution time inside a longer sequence.
+ */
+ds_status ds_gathered_lm_head_timed(hipStream_t s, ds_dtype dt, int V, int d, const void *W, int G,
+                                    int m, const void *h, int64_t ldh_g, const int64_t *sl_off,
+                                    const int32_t *sl_ids, int64_t max_rows, float *logits,
+                                    void *ws, size_t ws_bytes, hipEvent_t start, hipEvent_t stop);
 
 /*
  * Draft proposal from the shortlist distribution [A; S "Pipeline Flow"].
@@ -254,9 +264,11 @@ ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *dr
  *   W_pos        host array [T] of head matrices, one per position (drafters
  *                with a separate head per position, or copies of one head on
  *                different memory); NULL means W at every position.
- *   head_events  host array [2T] of caller-created HIP events; when non-NULL,
- *                events 2t and 2t+1 are recorded on head_stream immediately
- *                before and after the head launch of position t (profiling).
+ *   head_events  host array [2T] of caller-created HIP events (created with
+ *                timing enabled); when non-NULL, events 2t and 2t+1 are
+ *                stamped at the start of the first and the end of the last
+ *                head kernel of position t (the kernels' own begin and end,
+ *                so hipEventElapsedTime gives the head's execution time).
  */
 typedef struct {
     int B, T, V, d, r, M;
