@@ -102,14 +102,17 @@ class HipEvents:
         self.made = []
 
 
-def cpu_baseline(wl, seconds: float) -> dict:
+def cpu_baseline(wl, seconds: float, static_ids=None) -> dict:
     import oracle
     from oracle import pipeline as opipe
     oracle.build(force=False)
     cfg = wl.cfg
     n, t0 = 0, time.perf_counter()
     while True:
-        opipe.run_step(wl)
+        if static_ids is None:
+            opipe.run_step(wl)
+        else:
+            opipe.run_static_step(wl, static_ids)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -126,10 +129,12 @@ def cpu_baseline(wl, seconds: float) -> dict:
         pass
     return {"value": cfg.B * cfg.T * n / el, "unit": "draft tokens/s", "cores": 1,
             "kind": "oracle",
-            "sample": "%d full step(s) of instance 0 (router, selection, shortlist, fp64 "
-                      "gathered head, sampling for all %d positions, target softmax and "
-                      "verification), %.1f s on 1 thread of %d (%s)"
-                      % (n, cfg.T, el, os.cpu_count() or 0, model or platform.machine())}
+            "sample": "%d full step(s) of instance 0 (%s for all %d positions, target "
+                      "softmax and verification), %.1f s on 1 thread of %d (%s)"
+                      % (n, "router, selection, shortlist, fp64 gathered head, sampling"
+                         if static_ids is None else
+                         "fp64 head over the static shortlist, sampling",
+                         cfg.T, el, os.cpu_count() or 0, model or platform.machine())}
 
 
 COPY_BYTES = 1 << 30
@@ -248,6 +253,11 @@ def main():
                          "profiles/head_gemv_traffic.json and exit")
     ap.add_argument("--probe-file", default=os.path.join(ROOT, "pmc_probe.json"),
                     help="where --pmc-probe writes (and --traffic-from reads) the launch list")
+    ap.add_argument("--static", choices=["gathered", "packed"],
+                    help="time the static baseline instead: one fixed frequency-ranked "
+                         "shortlist at every position, gathered from W or from a packed slab")
+    ap.add_argument("--static-size", type=int, default=32768,
+                    help="tokens on the static list (the pages' static baselines keep ~32K)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying step graphs")
     args = ap.parse_args()
@@ -263,7 +273,7 @@ def main():
     import torch
 
     from dynamic_vocabulary_draft_amd import synthetic as syn
-    from dynamic_vocabulary_draft_amd.pipeline import DraftStep, to_dev
+    from dynamic_vocabulary_draft_amd.pipeline import DraftStep, StaticStep, to_dev
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -277,13 +287,22 @@ def main():
     wls = [syn.make_workload(args.config, instance=i, with_W=False) for i in range(args.instances)]
     for wl in wls:
         wl.W = W_host
-    steps = [DraftStep(wl, W=W) for wl in wls]
+    static_ids = None
+    if args.static:
+        if cfg.is_tree:
+            raise SystemExit("--static drafts chains; pick a chain workload")
+        static_ids = syn.static_shortlist(cfg, args.static_size)
+        steps = [StaticStep(wl, static_ids, W=W, packed=args.static == "packed") for wl in wls]
+    else:
+        steps = [DraftStep(wl, W=W) for wl in wls]
     npos = 1 if cfg.is_tree else cfg.T
     if not args.no_replicas and not cfg.is_tree:
         for i, st in enumerate(steps):
-            reps = [W if (i == 0 and t == 0) else W.clone() for t in range(npos)]
+            base = st.head_matrix() if args.static else W
+            reps = [base if t == 0 else base.clone() for t in range(npos)]
             st.set_W_positions(reps)
-        log("W replicas: %d x %.2f GB" % (args.instances * npos, W.numel() * e / 1e9))
+        log("head-matrix replicas: %d x %.2f GB" % (args.instances * npos,
+                                                    reps[0].numel() * e / 1e9))
     del W_host
     torch.cuda.synchronize()
 
@@ -304,7 +323,7 @@ def main():
         per = []
         for t in range(npos):
             lo, hi = int(off[t * cfg.B]), int(off[(t + 1) * cfg.B])
-            per.append({"total": hi - lo, "union": int(np.unique(ids[lo:hi]).size)})
+            per.append({"total": hi - lo, "union": int(np.unique(ids[lo:hi]).size)})  # rows read
         sizes.append(per)
         assert int(st.err_flag.item()) == 0
 
@@ -412,11 +431,16 @@ def main():
         "dtype": "bf16" if cfg.dtype == syn.DT_BF16 else "f32",
         "data": "synthetic (seeded clustered-Gaussian W, N(0,1) hidden states, N(0,3) target "
                 "logits; %d instances rotated)" % args.instances,
-        "config": {"workload": cfg.name, "V": cfg.V, "d": cfg.d, "clusters": cfg.M,
+        "config": {"workload": cfg.name if static_ids is None else
+                   "%s, static %s |S|=%d" % (cfg.name, args.static, static_ids.shape[0]),
+                   "V": cfg.V, "d": cfg.d, "clusters": cfg.M,
                    "batch": cfg.B, "depth": cfg.T, "tree_nodes": cfg.tree_nodes,
                    "budget": list(cfg.budget), "router": "%d->%d->%d" % (cfg.d, cfg.r, cfg.M),
-                   "step": "router+select+build+gathered head+sample per position, "
-                           "target softmax + verify",
+                   "step": ("router+select+build+gathered head+sample per position, "
+                            "target softmax + verify") if static_ids is None else
+                           ("static baseline: %s head over one fixed %d-token frequency-ranked "
+                            "shortlist + sample per position, target softmax + verify"
+                            % (args.static, static_ids.shape[0])),
                    "launch": mode},
         "roofline": roof,
         "head": head,
@@ -424,7 +448,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         wl0 = syn.make_workload(args.config, instance=0)
-        out["cpu_baseline"] = cpu_baseline(wl0, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl0, args.cpu_seconds, static_ids)
     print(json.dumps(out), flush=True)
 
 

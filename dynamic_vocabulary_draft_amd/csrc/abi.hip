@@ -276,6 +276,22 @@ ds_status ds_gathered_lm_head_timed(hipStream_t s, ds_dtype dt, int V, int d, co
                                       max_rows, logits, ws, start, stop));
 }
 
+ds_status ds_pack_rows(hipStream_t s, ds_dtype dt, int V, int d, const void *W, int64_t n,
+                       const int32_t *ids, void *out)
+{
+    if (n < 0 || V <= 0 || d <= 0)
+        return DS_EINVAL;
+    if (dt != DS_F32 && dt != DS_BF16)
+        return DS_EDTYPE;
+    if (d % 8)
+        return DS_ESHAPE;
+    if (n == 0)
+        return DS_OK;
+    if (!W || !ids || !out || !aligned16(W) || !aligned16(out))
+        return DS_EINVAL;
+    return hip_status(ds::pack_launch(s, dt == DS_BF16, V, d, W, n, ids, out));
+}
+
 size_t ds_sample_workspace_bytes(int G, int m, int64_t max_len)
 {
     return G > 0 && m > 0 && max_len > 0 ? ds::sample_ws_bytes((int64_t)G * m, max_len) : 0;
@@ -386,7 +402,8 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
     void *bws = reinterpret_cast<char *>(a->ws) + round_up(ds_router_workspace_bytes(B, a->r), 256);
     void *sws = reinterpret_cast<char *>(bws) + round_up(ds::build_ws_bytes(B, a->V), 256);
     void *hws = reinterpret_cast<char *>(sws) + round_up(ds::sample_ws_bytes(B, len_bound), 256);
-    // events: [0, T) router done, [T, 2T) head about to start, 2T fork
+    // events: [0, T) build of position t done, [T, 2T) h[t+1] ready (token
+    // t-1 sampled), 2T fork
     if (g_events.ensure(2 * (size_t)T + 1) != hipSuccess)
         return DS_EHIP;
     hipEvent_t fork = g_events.ev[2 * T];
@@ -397,7 +414,7 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
         err = hipStreamWaitEvent(rs, fork, 0);
     for (int t = 0; t < T && err == hipSuccess; ++t) {
         const int64_t rb = (int64_t)t * B;
-        if (t > 0)  // H_{t-1} exists once the head of position t-1 may start
+        if (t > 0)  // h[t] (H_{t-1}) exists once token t-2 is sampled
             err = hipStreamWaitEvent(rs, g_events.ev[T + t - 1], 0);
         if (err == hipSuccess)
             err = ds::router_launch(rs, bf16, B, a->d, a->r, a->M, a->act, hb + (size_t)t * a->d * e,
@@ -412,10 +429,14 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
                                    a->sl_ids, a->err_flag, bws);
         if (err == hipSuccess)
             err = hipEventRecord(g_events.ev[t], rs);
-        if (err == hipSuccess)
-            err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
+        // h[t+1] (read by head t and by router t+1) is ready once token t-1
+        // is sampled: the record follows sample t-1 directly, before the
+        // head stream waits for build t, so router t+1 may run alongside
+        // head t
         if (err == hipSuccess)
             err = hipEventRecord(g_events.ev[T + t], hs);
+        if (err == hipSuccess)
+            err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
         if (err == hipSuccess)
             err = ds::head_launch(hs, bf16, a->V, a->d, a->W_pos ? a->W_pos[t] : a->W, B, 1,
                                   hb + (size_t)(t + 1) * a->d * e, ldh, a->sl_off + rb, a->sl_ids,

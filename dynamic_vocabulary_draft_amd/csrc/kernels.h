@@ -44,6 +44,10 @@ hipError_t head_launch(hipStream_t s, bool bf16, int V, int d, const void *W, in
                        const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
                        hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
+// static shortlist slab: out[i] = W[ids[i]] (NaN row for ids outside [0, V))
+hipError_t pack_launch(hipStream_t s, bool bf16, int V, int d, const void *W, int64_t n,
+                       const int32_t *ids, void *out);
+
 size_t sample_ws_bytes(int64_t rows, int64_t max_len);
 hipError_t sample_launch(hipStream_t s, int G, int m, const int64_t *sl_off,
                          const int32_t *sl_ids, const float *logits, float temperature,

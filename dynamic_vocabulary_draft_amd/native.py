@@ -61,6 +61,7 @@ _SIGS = {
                                  _sz]),
     "ds_gathered_lm_head_timed": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i64, _vp, _vp, _i64, _vp,
                                        _vp, _sz, _vp, _vp]),
+    "ds_pack_rows": (_i, [_vp, _i, _i, _i, _vp, _i64, _vp, _vp]),
     "ds_sample_workspace_bytes": (_sz, [_i, _i, _i64]),
     "ds_shortlist_sample": (_i, [_vp, _i, _i, _vp, _vp, _vp, _f, _vp, _i64, _vp, _vp, _vp, _sz]),
     "ds_softmax_workspace_bytes": (_sz, [_i, _i]),
@@ -228,6 +229,13 @@ def gathered_lm_head(W, h, sl_off, sl_ids, max_rows, logits, ws=None, *, G=None,
     else:
         _check("ds_gathered_lm_head_timed", lib.ds_gathered_lm_head_timed(
             *args, C.c_void_p(events[0]), C.c_void_p(events[1])))
+
+
+def pack_rows(W, ids, out, *, stream=None):
+    """out[i] = W[ids[i]] (NaN rows for ids outside [0, V))."""
+    V, d = W.shape
+    _check("ds_pack_rows", lib.ds_pack_rows(_s(stream), _dt(W), V, d, _p(W), ids.numel(),
+                                            _p(ids), _p(out)))
 
 
 def shortlist_sample(sl_off, sl_ids, logits, temperature, u, token, q, ws, *, max_len, m=1,

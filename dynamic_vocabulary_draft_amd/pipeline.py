@@ -207,3 +207,107 @@ class DraftStep:
             r.update(p=self.p.cpu().numpy(), n_acc=self.n_acc.cpu().numpy(),
                      out=self.out.cpu().numpy())
         return r
+
+
+class StaticStep:
+    """The static baseline the pages compare against (DynaSpec abstract, on
+    FR-Spec / VocabTrim: drafting from a fixed, frequency-ranked shortlist):
+    every position drafts from the same list, with no router, selection or
+    build, then the same verification.  ``packed``: the list's rows are
+    copied once into a contiguous slab (ds_pack_rows) and the head runs over
+    the slab (ids 0..L-1) instead of gathering from W; the sampler still
+    reports real token ids."""
+
+    def __init__(self, wl: syn.Workload, static_ids: np.ndarray, device="cuda",
+                 W: torch.Tensor | None = None, packed: bool = False,
+                 temperature: float = 1.0):
+        cfg = self.cfg = wl.cfg
+        assert not cfg.is_tree, "the static step drafts chains"
+        self.device = device
+        self.temperature = float(temperature)
+        self.packed = packed
+        dev = lambda a: to_dev(a, device)  # noqa: E731
+        B, T, V, d = cfg.B, cfg.T, cfg.V, cfg.d
+        L = self.L = int(static_ids.shape[0])
+        self.W = W if W is not None else dev(wl.W)
+        self.h = dev(wl.h)
+        self.u_draft = dev(wl.u_draft)
+        self.u_acc = dev(wl.u_acc)
+        self.u_fin = dev(wl.u_fin)
+        self.target_logits = dev(wl.target_logits)
+        self.static_ids = dev(static_ids)
+        self.sl_off = dev((np.arange(T * B + 1) * L).astype(np.int64))
+        self.sl_ids = dev(np.tile(static_ids, T * B).astype(np.int32))
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        if packed:
+            self.slab = torch.empty(L, d, dtype=self.W.dtype, device=device)
+            N.pack_rows(self.W, self.static_ids, self.slab)
+            self.head_ids = dev(np.tile(np.arange(L, dtype=np.int32), T * B))
+        self.logits = torch.empty(max(T * B * L, 1), **f32)
+        self.q = torch.empty(max(T * B * L, 1), **f32)
+        self.token = torch.empty(T, B, **i32)
+        self.err_flag = torch.zeros(1, **i32)
+        self.head_ws = N.workspace(N.head_workspace_bytes(B, 1, L if packed else V), device)
+        self.sample_ws = N.workspace(N.sample_workspace_bytes(B, 1, max(L, 1)), device)
+        if self.target_logits is not None:
+            self.p = torch.empty(B, T + 1, V, **f32)
+            self.n_acc = torch.empty(B, **i32)
+            self.out = torch.empty(B, T + 1, **i32)
+            self.softmax_ws = N.workspace(N.softmax_workspace_bytes(B * (T + 1), V), device)
+            self.verify_ws = N.workspace(N.verify_workspace_bytes(B, T, V), device)
+        self._W_pos = None
+        self._head_events = None
+
+    def head_matrix(self) -> torch.Tensor:
+        """What the head reads: the packed slab, or W."""
+        return self.slab if self.packed else self.W
+
+    def set_W_positions(self, Ws: list[torch.Tensor] | None) -> None:
+        """One head matrix per draft position (identical copies of the slab,
+        or of W), or None."""
+        assert Ws is None or len(Ws) == self.cfg.T
+        self._W_pos = Ws
+
+    def set_head_events(self, events) -> None:
+        self._head_events = events
+
+    def draft(self, stream=None) -> None:
+        cfg = self.cfg
+        B, T, d = cfg.B, cfg.T, cfg.d
+        ids = self.head_ids if self.packed else self.sl_ids
+        for t in range(T):
+            rb = t * B
+            Wt = self._W_pos[t] if self._W_pos is not None else self.head_matrix()
+            ev = self._head_events
+            N.gathered_lm_head(Wt, self.h[:, t + 1], self.sl_off[rb:rb + B + 1], ids, B * self.L,
+                               self.logits, self.head_ws, G=B, m=1, ldh_g=(T + 1) * d,
+                               stream=stream,
+                               events=None if ev is None else (ev[2 * t], ev[2 * t + 1]))
+            N.shortlist_sample(self.sl_off[rb:rb + B + 1], self.sl_ids, self.logits,
+                               self.temperature, self.u_draft[t], self.token[t], self.q,
+                               self.sample_ws, max_len=self.L, stream=stream)
+
+    def verify(self, stream=None) -> None:
+        N.target_softmax(self.target_logits, self.p, self.softmax_ws, stream=stream)
+        N.verify_reject(self.token, self.sl_off, self.sl_ids, self.q, self.p, self.u_acc,
+                        self.u_fin, self.n_acc, self.out, self.verify_ws, stream=stream)
+
+    def step(self, stream=None) -> None:
+        self.draft(stream)
+        if self.target_logits is not None:
+            self.verify(stream)
+
+    def capture(self, stream) -> "N.Graph":
+        return N.capture(lambda: self.step(stream), stream)
+
+    def host(self) -> dict:
+        torch.cuda.synchronize(self.device)
+        r = {k: getattr(self, k).cpu().numpy() for k in ("sl_off", "token", "err_flag")}
+        r["sl_ids"] = self.sl_ids.cpu().numpy()
+        r["logits"] = self.logits.cpu().numpy()
+        r["q"] = self.q.cpu().numpy()
+        if self.target_logits is not None:
+            r.update(p=self.p.cpu().numpy(), n_acc=self.n_acc.cpu().numpy(),
+                     out=self.out.cpu().numpy())
+        return r

@@ -9,7 +9,8 @@ rounded to nearest-even and stored as their raw 16-bit patterns (uint16).
 Streams: 0 centroids, 1 noise (one sub-stream per block of ``ROW_BLOCK`` rows),
 2 token permutation, 3-6 router W1/b1/W2/b2, 7 hidden states (sub-stream =
 instance), 8 target logits, 9 draft uniforms, 10 accept uniforms, 11 final
-uniforms (9-11 also take the instance).
+uniforms (9-11 also take the instance), 12 token frequency ranking (the
+order a fixed, frequency-ranked shortlist takes tokens in).
 
 The workload shapes stand in for the pages' Llama-3-8B, Qwen3-8B and
 Gemma-3-12B drafting set-ups (DynaSpec summary page, "Evaluation Setup" and
@@ -187,6 +188,20 @@ def make_hidden(cfg: Config, instance: int = 0) -> np.ndarray:
     rows = (1 + cfg.tree_nodes) if cfg.is_tree else (cfg.T + 1)
     h = rng(cfg.index, 7, instance).standard_normal((cfg.B, rows, cfg.d), dtype=np.float32)
     return _store(h, cfg.dtype)
+
+
+def frequency_rank(cfg: Config) -> np.ndarray:
+    """Token ids from most to least frequent.  There is no corpus here, so a
+    seeded permutation of [0, V) stands in for the ranking a static
+    baseline would count (its head and sampling costs depend only on the
+    list's size and scatter, not on which tokens it holds)."""
+    return rng(cfg.index, 12).permutation(cfg.V).astype(np.int32)
+
+
+def static_shortlist(cfg: Config, size: int) -> np.ndarray:
+    """The ``size`` most frequent tokens in ascending id: the fixed list of
+    a frequency-ranked static baseline."""
+    return np.sort(frequency_rank(cfg)[: min(int(size), cfg.V)]).astype(np.int32)
 
 
 def make_uniforms(cfg: Config, stream: int, shape, instance: int = 0) -> np.ndarray:

@@ -194,6 +194,19 @@ ds_status ds_gathered_lm_head_timed(hipStream_t s, ds_dtype dt, int V, int d, co
                                     void *ws, size_t ws_bytes, hipEvent_t start, hipEvent_t stop);
 
 /*
+ * Static-shortlist slab [A on FR-Spec / VocabTrim: a fixed, frequency-ranked
+ * shortlist; S "Comparison to Prior Work", "Evaluation Highlights" (a static
+ * list of about 32K tokens)]: out[i][k] = W[ids[i]][k] for i < n, a plain
+ * copy, so that a fixed list's head can run over contiguous rows (pass the
+ * slab as W with ids 0..n-1) instead of gathering.
+ * W [V][d] (dt), ids [n] int32, out [n][d] (dt), both 16-byte aligned;
+ * d a multiple of 8.  A row whose id lies outside [0, V) is filled with quiet
+ * NaN.  n = 0 enqueues nothing.
+ */
+ds_status ds_pack_rows(hipStream_t s, ds_dtype dt, int V, int d, const void *W, int64_t n,
+                       const int32_t *ids, void *out);
+
+/*
  * Draft proposal from the shortlist distribution [A; S "Pipeline Flow"].
  * Per row (g, i), q = softmax(logits / temperature) over S_g computed in
  * fp64, and token = S_g[j*] with j* the first index whose running sum of
@@ -252,11 +265,12 @@ ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *dr
  *   router_stream: router(h[:, t]) -> select(budget[t]) -> build (appending
  *                  to the shortlist buffer) -> event
  *   head_stream:   wait(event) -> gathered head(h[:, t+1]) -> sample(u_draft[t])
- * The router of position t needs H_{t-1}, which a drafter produces just
- * before the head of position t-1; so for t >= 1 router_stream waits for an
- * event recorded on head_stream immediately before head(t-1), and the
- * router, selection and build of position t run while the head and sampler
- * of position t-1 work.  Rows are position-major (row t*B + b), the
+ * The router of position t needs H_{t-1} = h[:, t], which a drafter
+ * produces from the token sampled at position t-2; so for t >= 1
+ * router_stream waits for an event recorded on head_stream right after the
+ * sampler of position t-2 (at the start for t = 1), and the router,
+ * selection and build of position t run while the head and sampler of
+ * position t-1 work.  Rows are position-major (row t*B + b), the
  * layout ds_verify_reject reads.  Every pointer is a device pointer except
  * max_rows, max_len, W_pos and head_events (host arrays).  On return all work is
  * enqueued and head_stream waits for everything enqueued on router_stream.

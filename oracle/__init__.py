@@ -121,6 +121,19 @@ def gathered_lm_head(W, h, sl_off, sl_ids):
     return out
 
 
+def pack_rows(W, ids):
+    """out[i] = W[ids[i]] as a new [n][d] array of W's dtype (NaN rows for
+    ids outside [0, V))."""
+    lib = _load()
+    W = _c(W)
+    V, d = W.shape
+    ids = _c(ids, np.int32)
+    out = np.empty((ids.shape[0], d), W.dtype)
+    lib.oracle_pack_rows(C.c_int(_dtype_code(W)), C.c_int(V), C.c_int(d), _p(W),
+                         C.c_int64(ids.shape[0]), _p(ids), _p(out))
+    return out
+
+
 def dense_lm_head(W, h):
     """logits[n][V] for h[n][d] over every row of W."""
     lib = _load()

@@ -250,6 +250,32 @@ void oracle_gathered_lm_head(int dtype, int V, int d, const void *W, int G,
 }
 
 /*
+ * Static-shortlist slab [A, on FR-Spec / VocabTrim: drafting restricted to a
+ * fixed, frequency-ranked shortlist; S "Comparison to Prior Work"]: the rows
+ * of a fixed list copied into one contiguous array, out[i] = W[ids[i]].  A
+ * row whose id lies outside [0, V) is filled with quiet NaN (the bit pattern
+ * 0x7FC0 per bf16 element, NAN per fp32 element).
+ */
+void oracle_pack_rows(int dtype, int V, int d, const void *W, int64_t n,
+                      const int32_t *ids, void *out)
+{
+    const size_t e = dtype == 1 ? 2 : 4;
+    for (int64_t i = 0; i < n; ++i) {
+        char *dst = (char *)out + (size_t)i * d * e;
+        const int32_t y = ids[i];
+        if (y >= 0 && y < V) {
+            memcpy(dst, (const char *)W + (size_t)y * d * e, (size_t)d * e);
+        } else if (dtype == 1) {
+            for (int k = 0; k < d; ++k)
+                ((uint16_t *)dst)[k] = 0x7FC0;
+        } else {
+            for (int k = 0; k < d; ++k)
+                ((float *)dst)[k] = NAN;
+        }
+    }
+}
+
+/*
  * Dense (full-vocabulary) head, the O(|V| d) projection the method replaces
  * [A; S "Core Problem"]: logits[row][y] = sum_k W[y][k] h_row[k].
  * Same summation as the gathered head, so the two agree bit for bit.

@@ -73,3 +73,37 @@ def run_step(wl, temperature: float = 1.0, p: np.ndarray | None = None) -> dict:
         n_acc, out, vtie = oracle.verify_reject(draft, sl_off, sl_ids, q, p, wl.u_acc, wl.u_fin)
         res.update(p=p, n_acc=n_acc, out=out, verify_tie=vtie)
     return res
+
+
+def run_static_step(wl, static_ids: np.ndarray, temperature: float = 1.0,
+                    p: np.ndarray | None = None) -> dict:
+    """The static baseline's step: every position drafts from the same fixed
+    shortlist (no router, selection or build), then the same verification.
+    Source: DynaSpec abstract, on fixed frequency-ranked shortlists
+    (FR-Spec, VocabTrim)."""
+    cfg = wl.cfg
+    B, T = cfg.B, cfg.T
+    L = int(static_ids.shape[0])
+    local_off = (np.arange(B + 1) * L).astype(np.int64)
+    ids_t = np.tile(static_ids, B)
+    lg_parts, q_parts, toks, ties = [], [], [], []
+    for t in range(T):
+        lg = oracle.gathered_lm_head(wl.W, np.ascontiguousarray(wl.h[:, t + 1][:, None, :]),
+                                     local_off, ids_t)
+        tok, q, tie = oracle.shortlist_sample(local_off, ids_t, lg, wl.u_draft[t], 1, temperature)
+        lg_parts.append(lg)
+        q_parts.append(q)
+        toks.append(tok)
+        ties.append(tie)
+    sl_off = (np.arange(T * B + 1) * L).astype(np.int64)
+    sl_ids = np.tile(static_ids, T * B)
+    q = np.concatenate(q_parts)
+    draft = np.stack(toks)
+    res = dict(sl_off=sl_off, sl_ids=sl_ids, logits=np.concatenate(lg_parts), q=q, token=draft,
+               tie=np.stack(ties))
+    if wl.target_logits is not None:
+        if p is None:
+            p = oracle.target_softmax(wl.target_logits)
+        n_acc, out, vtie = oracle.verify_reject(draft, sl_off, sl_ids, q, p, wl.u_acc, wl.u_fin)
+        res.update(p=p, n_acc=n_acc, out=out, verify_tie=vtie)
+    return res

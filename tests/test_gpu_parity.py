@@ -330,6 +330,49 @@ def test_head_full_vocabulary_is_dense(N, oracle_lib):
 
 
 # ----------------------------------------------------------------------------
+# static-shortlist slab
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("bf16,d", [(True, 264), (False, 1032), (True, 4096)])
+def test_pack_rows_bit_exact(N, oracle_lib, bf16, d):
+    V, n = 3000, 2500
+    g = np.random.default_rng(d)
+    W = g.standard_normal((V, d)).astype(np.float32)
+    W = syn.f32_to_bf16_bits(W) if bf16 else W
+    ids = g.integers(0, V, size=n).astype(np.int32)
+    ids[[0, 7, n - 1]] = [-1, V, 2 ** 31 - 1]
+    ref = oracle_lib.pack_rows(W, ids)
+    Wd = to_dev(W)
+    out = torch.empty((n, d), dtype=Wd.dtype, device="cuda")
+    N.pack_rows(Wd, to_dev(ids), out)
+    got = _cpu(out.view(torch.int16) if bf16 else out.view(torch.int32))
+    want = ref.view(np.int16) if bf16 else ref.view(np.int32)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("G", [1, 16])
+def test_packed_head_equals_gathered_head_gpu(N, oracle_lib, G):
+    """Head over a packed slab (ids 0..L-1) == gathered head over the list,
+    bit for bit, on the GEMV (1 group) and union (16 groups) paths."""
+    cfg = syn.shrink(syn.CONFIGS[1], V=6000, d=264, M=40)
+    cluster_of, _ = _clusters(6000, 40, 5)
+    W = syn.make_lm_head(cfg, cluster_of)
+    ids = syn.static_shortlist(cfg, 1500)
+    L = ids.shape[0]
+    h = _store(np.random.default_rng(G).standard_normal((G, 1, 264)).astype(np.float32), True)
+    off = (np.arange(G + 1) * L).astype(np.int64)
+    Wd = to_dev(W)
+    slab = torch.empty((L, 264), dtype=Wd.dtype, device="cuda")
+    N.pack_rows(Wd, to_dev(ids), slab)
+    a = torch.empty(G * L, device="cuda")
+    b = torch.empty(G * L, device="cuda")
+    N.gathered_lm_head(Wd, to_dev(h), to_dev(off), to_dev(np.tile(ids, G)), G * L, a)
+    N.gathered_lm_head(slab, to_dev(h), to_dev(off), to_dev(np.tile(np.arange(L, dtype=np.int32), G)),
+                       G * L, b)
+    assert torch.equal(a, b)
+    _logit_bar(_cpu(a), oracle_lib.gathered_lm_head(W, h, off, np.tile(ids, G)), True)
+
+
+# ----------------------------------------------------------------------------
 # shortlist_sample
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("lens,m", [([1, 5, 255, 256, 257, 1000], 1), ([27000, 3], 1),

@@ -502,3 +502,50 @@ def test_oracle_step_matches_golden_c0(oracle_lib):
         want = json.load(f)
     got = json.loads(json.dumps(make_golden.c0_summary()))
     assert got == want
+
+
+# ----------------------------------------------------------------------------
+# static-shortlist baseline: the packed slab and the frequency-ranked list
+# ----------------------------------------------------------------------------
+def test_pack_rows_is_row_gather(oracle_lib):
+    """The C copy against numpy fancy indexing (an independent gather), bf16
+    and fp32, with NaN rows for ids outside [0, V)."""
+    g = np.random.default_rng(3)
+    W32 = g.standard_normal((50, 24)).astype(np.float32)
+    Wb = syn.f32_to_bf16_bits(W32)
+    ids = np.array([3, 49, 0, 3, -1, 50, 17], np.int32)
+    ok = (ids >= 0) & (ids < 50)
+    for W in (W32, Wb):
+        out = oracle_lib.pack_rows(W, ids)
+        assert out.dtype == W.dtype and out.shape == (7, 24)
+        assert np.array_equal(out[ok], W[ids[ok]])
+        if W.dtype == np.uint16:
+            assert (out[~ok] == 0x7FC0).all()
+        else:
+            assert np.isnan(out[~ok]).all()
+
+
+def test_packed_head_equals_gathered_head(oracle_lib):
+    """The head over a packed slab with ids 0..L-1 is the gathered head over
+    the list, bit for bit (same rows, same summation)."""
+    cfg = syn.shrink(syn.CONFIGS[1], V=3000, d=64, M=20)
+    cluster_of, _ = syn.make_clusters(cfg)
+    W = syn.make_lm_head(cfg, cluster_of)
+    ids = syn.static_shortlist(cfg, 700)
+    h = syn.f32_to_bf16_bits(np.random.default_rng(1).standard_normal((2, 1, 64)).astype(np.float32))
+    off = np.array([0, 700, 1400], np.int64)
+    both = np.concatenate([ids, ids])
+    ref = oracle_lib.gathered_lm_head(W, h, off, both)
+    slab = oracle_lib.pack_rows(W, ids)
+    got = oracle_lib.gathered_lm_head(slab, h, off, np.tile(np.arange(700, dtype=np.int32), 2))
+    assert np.array_equal(got, ref)
+
+
+def test_static_shortlist_is_top_of_ranking():
+    cfg = syn.CONFIGS[1]
+    rank = syn.frequency_rank(cfg)
+    assert np.array_equal(np.sort(rank), np.arange(cfg.V))
+    s = syn.static_shortlist(cfg, 32768)
+    assert s.shape == (32768,) and (np.diff(s) > 0).all()
+    assert set(s.tolist()) == set(rank[:32768].tolist())
+    assert np.array_equal(syn.static_shortlist(cfg, 10 ** 9), np.arange(cfg.V))
