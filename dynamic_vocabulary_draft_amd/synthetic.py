@@ -10,7 +10,8 @@ Streams: 0 centroids, 1 noise (one sub-stream per block of ``ROW_BLOCK`` rows),
 2 token permutation, 3-6 router W1/b1/W2/b2, 7 hidden states (sub-stream =
 instance), 8 target logits, 9 draft uniforms, 10 accept uniforms, 11 final
 uniforms (9-11 also take the instance), 12 token frequency ranking (the
-order a fixed, frequency-ranked shortlist takes tokens in).
+order a fixed, frequency-ranked shortlist takes tokens in), 13 initial
+k-means labels.
 
 The workload shapes stand in for the pages' Llama-3-8B, Qwen3-8B and
 Gemma-3-12B drafting set-ups (DynaSpec summary page, "Evaluation Setup" and
@@ -202,6 +203,17 @@ def static_shortlist(cfg: Config, size: int) -> np.ndarray:
     """The ``size`` most frequent tokens in ascending id: the fixed list of
     a frequency-ranked static baseline."""
     return np.sort(frequency_rank(cfg)[: min(int(size), cfg.V)]).astype(np.int32)
+
+
+def kmeans_init_assign(cfg: Config, cluster_of: np.ndarray, noise: float) -> np.ndarray:
+    """Initial labels for the clustering: the planted cluster of each row,
+    with a fraction ``noise`` of rows given a seeded uniformly random label
+    instead (noise = 1 is a random partition)."""
+    g = rng(cfg.index, 13)
+    lab = np.asarray(cluster_of, np.int32).copy()
+    flip = g.random(cfg.V) < noise
+    lab[flip] = g.integers(0, cfg.M, size=int(flip.sum()), dtype=np.int32)
+    return lab
 
 
 def make_uniforms(cfg: Config, stream: int, shape, instance: int = 0) -> np.ndarray:

@@ -189,3 +189,46 @@ def verify_reject(draft, sl_off, sl_ids, q, p, u_acc, u_fin):
                              _p(sl_ids), _p(q), _p(p), _p(u_acc), _p(u_fin), _p(n_acc),
                              _p(out), _p(tie))
     return n_acc, out, tie.astype(bool)
+
+
+# ---------------------------------------------------------------------------
+# spherical k-means over the LM-head rows (bf16 W)
+# ---------------------------------------------------------------------------
+def kmeans_inv_norms(W) -> np.ndarray:
+    lib = _load()
+    W = _c(W, np.uint16)
+    V, d = W.shape
+    out = np.empty(V, np.float32)
+    lib.oracle_kmeans_inv_norms(C.c_int(V), C.c_int(d), _p(W), _p(out))
+    return out
+
+
+def kmeans_assign(W, Cb):
+    """(assign [V] int32, score [V] fp32, tie [V] bool) for bf16 W [V][d]
+    and bf16 centroids Cb [M][d]."""
+    lib = _load()
+    W, Cb = _c(W, np.uint16), _c(Cb, np.uint16)
+    V, d = W.shape
+    M = Cb.shape[0]
+    assign = np.empty(V, np.int32)
+    score = np.empty(V, np.float32)
+    tie = np.empty(V, np.uint8)
+    lib.oracle_kmeans_assign(C.c_int(V), C.c_int(d), _p(W), C.c_int(M), _p(Cb), _p(assign),
+                             _p(score), _p(tie))
+    return assign, score, tie.astype(bool)
+
+
+def kmeans_update(W, inv_norm, assign, C_prev):
+    """(C_out [M][d] fp32, size [M] int32, norm [M] fp64)."""
+    lib = _load()
+    W = _c(W, np.uint16)
+    V, d = W.shape
+    C_prev = _c(C_prev, np.float32)
+    M = C_prev.shape[0]
+    inv_norm, assign = _c(inv_norm, np.float32), _c(assign, np.int32)
+    C_out = np.empty((M, d), np.float32)
+    size = np.empty(M, np.int32)
+    norm = np.empty(M, np.float64)
+    lib.oracle_kmeans_update(C.c_int(V), C.c_int(d), _p(W), _p(inv_norm), C.c_int(M), _p(assign),
+                             _p(C_prev), _p(C_out), _p(size), _p(norm))
+    return C_out, size, norm

@@ -477,3 +477,104 @@ void oracle_verify_reject(int B, int T, int V, const int32_t *draft,
     free(w);
     free(qd);
 }
+
+
+/*
+ * ---------------------------------------------------------------------------
+ * Spherical k-means over the rows of the LM head [S "Key Novelty" (clusters
+ * from the semantic similarity of LM-head weights), "Modeling / Key
+ * Hyperparameters" (clustering algorithm: spherical k-means), "Key Terms"
+ * (spherical k-means groups by cosine similarity, i.e. direction)].  The
+ * algorithm is the published one (Dhillon and Modha, concept
+ * decompositions): with unit rows x_y = w_y / |w_y| and unit centroids,
+ * assign every row to the centroid of largest cosine, then replace every
+ * centroid by the normalised sum of its rows.  W is bf16.
+ * ---------------------------------------------------------------------------
+ */
+
+/* inv_norm[y] = 1 / |w_y| (fp64, rounded once); 0 for an all-zero row. */
+void oracle_kmeans_inv_norms(int V, int d, const uint16_t *W, float *inv_norm)
+{
+    for (int y = 0; y < V; ++y) {
+        double ss = 0.0;
+        for (int k = 0; k < d; ++k) {
+            double v = bf16_to_double(W[(int64_t)y * d + k]);
+            ss += v * v;
+        }
+        inv_norm[y] = ss > 0.0 ? (float)(1.0 / sqrt(ss)) : 0.0f;
+    }
+}
+
+/*
+ * Assignment: assign[y] = argmax_c w_y . C[c] over bf16 centroids C [M][d]
+ * (the row norm does not change the argmax), ties to the lower c; score[y]
+ * the winning dot product (fp64, rounded to fp32).  tie[y] = 1 where the
+ * runner-up is within tol of the winner, tol = d * 2^-22 * sum_k |w_yk C_ck|
+ * of the winner: inside that band an fp32 accumulation in another order may
+ * legitimately pick the runner-up.
+ */
+void oracle_kmeans_assign(int V, int d, const uint16_t *W, int M, const uint16_t *C,
+                          int32_t *assign, float *score, uint8_t *tie)
+{
+    for (int y = 0; y < V; ++y) {
+        const uint16_t *w = W + (int64_t)y * d;
+        double best = -INFINITY, second = -INFINITY, mag = 0.0;
+        int bc = 0;
+        for (int c = 0; c < M; ++c) {
+            const uint16_t *cv = C + (int64_t)c * d;
+            double acc = 0.0, a = 0.0;
+            for (int k = 0; k < d; ++k) {
+                double p = bf16_to_double(w[k]) * bf16_to_double(cv[k]);
+                acc += p;
+                a += fabs(p);
+            }
+            if (acc > best) {
+                second = best;
+                best = acc;
+                bc = c;
+                mag = a;
+            } else if (acc > second) {
+                second = acc;
+            }
+        }
+        assign[y] = bc;
+        score[y] = (float)best;
+        tie[y] = (uint8_t)(M > 1 && best - second <= (double)d * ldexp(1.0, -22) * mag);
+    }
+}
+
+/*
+ * Update: s_c = sum over rows y with assign[y] = c, in ascending y, of
+ * w_y * inv_norm[y] (fp64); C_out[c] = s_c / |s_c| rounded to fp32; a
+ * cluster without rows (or with s_c = 0) keeps C_prev[c].  size[c] = its row
+ * count; norm[c] = |s_c|, whose sum over c is the spherical k-means
+ * objective sum_y x_y . C_out[assign[y]] reached by this update.
+ */
+void oracle_kmeans_update(int V, int d, const uint16_t *W, const float *inv_norm, int M,
+                          const int32_t *assign, const float *C_prev, float *C_out,
+                          int32_t *size, double *norm)
+{
+    double *acc = (double *)calloc((size_t)M * d, sizeof(double));
+    for (int c = 0; c < M; ++c)
+        size[c] = 0;
+    for (int y = 0; y < V; ++y) {
+        int c = assign[y];
+        if (c < 0 || c >= M)
+            continue;
+        size[c] += 1;
+        for (int k = 0; k < d; ++k)
+            acc[(int64_t)c * d + k] += bf16_to_double(W[(int64_t)y * d + k]) * (double)inv_norm[y];
+    }
+    for (int c = 0; c < M; ++c) {
+        double ss = 0.0;
+        for (int k = 0; k < d; ++k)
+            ss += acc[(int64_t)c * d + k] * acc[(int64_t)c * d + k];
+        double nrm = sqrt(ss);
+        norm[c] = size[c] > 0 ? nrm : 0.0;
+        for (int k = 0; k < d; ++k)
+            C_out[(int64_t)c * d + k] = (size[c] > 0 && nrm > 0.0)
+                                            ? (float)(acc[(int64_t)c * d + k] / nrm)
+                                            : C_prev[(int64_t)c * d + k];
+    }
+    free(acc);
+}

@@ -549,3 +549,92 @@ def test_static_shortlist_is_top_of_ranking():
     assert s.shape == (32768,) and (np.diff(s) > 0).all()
     assert set(s.tolist()) == set(rank[:32768].tolist())
     assert np.array_equal(syn.static_shortlist(cfg, 10 ** 9), np.arange(cfg.V))
+
+
+# ----------------------------------------------------------------------------
+# spherical k-means over the LM-head rows
+# ----------------------------------------------------------------------------
+def _km_case(V=3000, d=64, M=20, seed=0):
+    cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=M)
+    cluster_of, size = syn.make_clusters(cfg)
+    W = syn.make_lm_head(cfg, cluster_of)
+    return cfg, cluster_of, size, W
+
+
+def _ulp32(got, ref):
+    got, ref = np.asarray(got, np.float32), np.asarray(ref, np.float32)
+    sp = np.spacing(np.maximum(np.abs(ref), np.float32(1e-38))).astype(np.float64)
+    return (np.abs(got.astype(np.float64) - ref.astype(np.float64)) <= sp).all()
+
+
+def test_kmeans_inv_norms_vs_numpy(oracle_lib):
+    cfg, _, _, W = _km_case()
+    Wf = syn.bf16_bits_to_f32(W).astype(np.float64)
+    ref = (1.0 / np.linalg.norm(Wf, axis=1)).astype(np.float32)
+    assert _ulp32(oracle_lib.kmeans_inv_norms(W), ref)
+    Wz = W.copy()
+    Wz[5] = 0
+    assert oracle_lib.kmeans_inv_norms(Wz)[5] == 0.0
+
+
+def test_kmeans_assign_vs_brute_force(oracle_lib):
+    cfg, cluster_of, _, W = _km_case(seed=1)
+    g = np.random.default_rng(2)
+    Cb = syn.f32_to_bf16_bits(g.standard_normal((cfg.M, cfg.d)).astype(np.float32))
+    a, sc, tie = oracle_lib.kmeans_assign(W, Cb)
+    S = syn.bf16_bits_to_f32(W).astype(np.float64) @ syn.bf16_bits_to_f32(Cb).astype(np.float64).T
+    ref = S.argmax(1)  # first maximum: the lower cluster id on ties
+    assert np.array_equal(a[~tie], ref[~tie])
+    assert tie.mean() < 0.01
+    assert np.allclose(sc, S.max(1), rtol=1e-6, atol=1e-6)
+    # exact ties (two identical centroids) go to the lower id
+    Cb2 = np.concatenate([Cb[:3], Cb[1:2]])
+    a2, _, _ = oracle_lib.kmeans_assign(W, Cb2)
+    assert not (a2 == 3).any()
+
+
+def test_kmeans_update_vs_numpy_and_closed_forms(oracle_lib):
+    cfg, cluster_of, _, W = _km_case(seed=2)
+    inv = oracle_lib.kmeans_inv_norms(W)
+    lab = syn.kmeans_init_assign(cfg, cluster_of, 0.3)
+    lab[lab == 7] = 8  # cluster 7 empty: keeps its previous centroid
+    lab[11] = 19
+    lab[lab == 19] = 18
+    lab[11] = 19  # cluster 19 has exactly one row
+    Cp = np.random.default_rng(5).standard_normal((cfg.M, cfg.d)).astype(np.float32)
+    Cn, size, nrm = oracle_lib.kmeans_update(W, inv, lab, Cp)
+    Wf = syn.bf16_bits_to_f32(W).astype(np.float64) * inv.astype(np.float64)[:, None]
+    for c in range(cfg.M):
+        mem = lab == c
+        assert size[c] == mem.sum()
+        if not mem.any():
+            assert np.array_equal(Cn[c], Cp[c])
+            assert nrm[c] == 0.0
+            continue
+        s_c = Wf[mem].sum(0)
+        assert abs(nrm[c] - np.linalg.norm(s_c)) <= 1e-12 * np.linalg.norm(s_c)
+        assert _ulp32(Cn[c], (s_c / np.linalg.norm(s_c)).astype(np.float32))
+    w11 = syn.bf16_bits_to_f32(W[11]).astype(np.float64)
+    assert _ulp32(Cn[19], (w11 / np.linalg.norm(w11)).astype(np.float32))
+
+
+def test_kmeans_objective_monotone_and_planted_recovery(oracle_lib):
+    """Spherical k-means never decreases its objective (up to the bf16
+    rounding of the centroids the assignment reads), and from a 30%-noisy
+    start one update + one assignment recovers the planted partition of the
+    clustered synthetic head."""
+    cfg, cluster_of, _, W = _km_case(seed=3)
+    inv = oracle_lib.kmeans_inv_norms(W)
+    lab = syn.kmeans_init_assign(cfg, cluster_of, 0.3)
+    assert (lab != cluster_of).mean() > 0.2
+    Cp = np.zeros((cfg.M, cfg.d), np.float32)
+    objs = []
+    for it in range(4):
+        Cn, size, nrm = oracle_lib.kmeans_update(W, inv, lab, Cp)
+        objs.append(float(nrm.sum()))
+        lab, _, _ = oracle_lib.kmeans_assign(W, syn.f32_to_bf16_bits(Cn))
+        if it == 0:
+            assert np.array_equal(lab, cluster_of)
+        Cp = Cn
+    assert all(b >= a * (1 - 1e-6) for a, b in zip(objs, objs[1:]))
+    assert objs[-1] > objs[0]
