@@ -235,6 +235,106 @@ def traffic_from(args):
     print(json.dumps(out))
 
 
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def kmeans_bench(args):
+    """Spherical k-means over the LM head's rows at the workload's shape:
+    inverse norms once, then timed iterations of update (centroids from the
+    labels) + assignment (labels from the centroids, on the matrix cores)."""
+    import numpy as np
+    import torch
+
+    from dynamic_vocabulary_draft_amd import native as N
+    from dynamic_vocabulary_draft_amd import synthetic as syn
+    from dynamic_vocabulary_draft_amd.pipeline import to_dev
+
+    torch.cuda.set_device(0)
+    cfg = syn.CONFIGS[args.config]
+    if cfg.dtype != syn.DT_BF16:
+        raise SystemExit("--kmeans needs a bf16 head")
+    V, d, M = cfg.V, cfg.d, cfg.M
+    cluster_of, _ = syn.make_clusters(cfg)
+    W_host = syn.make_lm_head(cfg, cluster_of, threads=min(16, os.cpu_count() or 8))
+    W = to_dev(W_host)
+    lab0 = syn.kmeans_init_assign(cfg, cluster_of, 0.5)
+    lab = to_dev(lab0)
+    inv = torch.empty(V, device="cuda")
+    C32 = torch.zeros(M, d, device="cuda")
+    C32b = torch.empty(M, d, device="cuda")
+    Cb = torch.empty(M, d, dtype=torch.bfloat16, device="cuda")
+    size = torch.empty(M, dtype=torch.int32, device="cuda")
+    norm = torch.empty(M, dtype=torch.float64, device="cuda")
+    score = torch.empty(V, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    uws = N.workspace(N.kmeans_update_workspace_bytes(V, d, M))
+    aws = N.workspace(N.lib.ds_kmeans_assign_workspace_bytes(V))
+    ev = HipEvents()
+    N.kmeans_inv_norms(W, inv)
+    bufs = [C32, C32b]
+
+    def iteration(k, events=None):
+        prev, out = bufs[k % 2], bufs[(k + 1) % 2]
+        N.kmeans_update(W, inv, lab, prev, out, Cb, size, norm, uws, err_flag=flag)
+        N.kmeans_assign(W, Cb, lab, score, aws, events=events)
+
+    iteration(0)
+    torch.cuda.synchronize()
+    objs = [float(norm.sum().item())]
+    n_it = args.kmeans_iters
+    evs = ev.array(2 * n_it)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(n_it):
+        iteration(k + 1, (evs[2 * k], evs[2 * k + 1]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    objs.append(float(norm.sum().item()))
+    assert int(flag.item()) == 0
+    durs = [ev.elapsed_ms(evs[2 * k], evs[2 * k + 1]) for k in range(n_it)]
+    flops = 2.0 * V * M * d
+    t_assign = float(np.mean(durs)) * 1e-3
+    achieved = flops / t_assign / 1e12
+    out = {
+        "metric": "spherical k-means iterations/s over the LM-head rows (update + assignment), "
+                  "V=%d d=%d M=%d bf16" % (V, d, M),
+        "value": round(n_it / wall, 3), "unit": "iterations/s", "n_gpus": 1,
+        "steps": n_it, "warmup": 1, "ms_per_step": round(wall * 1e3 / n_it, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic clustered-Gaussian LM head, labels started from the planted "
+                "clusters with half of them random",
+        "config": {"workload": "spherical k-means over the %s head" % cfg.name, "V": V, "d": d,
+                   "clusters": M},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "assign": {"kernel": "kmeans_assign_kernel", "mean_us": round(t_assign * 1e6, 1),
+                   "flops": flops, "timed_on": "HIP events stamped at the kernel's own start "
+                                               "and end"},
+        "update_plus_assign_ms": round(wall * 1e3 / n_it, 3),
+        "objective": {"after_first_update": objs[0], "after_last_update": objs[1]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        rows = 256
+        t1 = time.perf_counter()
+        oracle.kmeans_assign(W_host[:rows], Cb.cpu().view(torch.int16).numpy().view(np.uint16))
+        t_rows = time.perf_counter() - t1
+        t1 = time.perf_counter()
+        inv_h = oracle.kmeans_inv_norms(W_host)
+        oracle.kmeans_update(W_host, inv_h, lab0, np.zeros((M, d), np.float32))
+        t_upd = time.perf_counter() - t1
+        t_it = t_rows * V / rows + t_upd
+        out["cpu_baseline"] = {
+            "value": round(1.0 / t_it, 6), "unit": "iterations/s", "cores": 1, "kind": "oracle",
+            "sample": "assignment of %d of %d rows (%.1f s, extrapolated linearly to all rows) "
+                      "+ inverse norms and one full update (%.1f s), 1 thread"
+                      % (rows, V, t_rows, t_upd)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,12 +358,20 @@ def main():
                          "shortlist at every position, gathered from W or from a packed slab")
     ap.add_argument("--static-size", type=int, default=32768,
                     help="tokens on the static list (the pages' static baselines keep ~32K)")
+    ap.add_argument("--kmeans", action="store_true",
+                    help="time spherical k-means iterations over the workload's LM head instead")
+    ap.add_argument("--kmeans-iters", type=int, default=5)
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying step graphs")
     args = ap.parse_args()
 
     if args.traffic_from:
         return traffic_from(args)
+    if args.kmeans:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        return kmeans_bench(args)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

@@ -292,6 +292,54 @@ ds_status ds_pack_rows(hipStream_t s, ds_dtype dt, int V, int d, const void *W, 
     return hip_status(ds::pack_launch(s, dt == DS_BF16, V, d, W, n, ids, out));
 }
 
+ds_status ds_kmeans_inv_norms(hipStream_t s, int V, int d, const void *W, float *inv_norm)
+{
+    if (!W || !inv_norm || V <= 0 || d <= 0)
+        return DS_EINVAL;
+    if (d % 8 || d > 8192)
+        return DS_ESHAPE;
+    if (!aligned16(W))
+        return DS_EINVAL;
+    return hip_status(ds::kmeans_inv_norm_launch(s, V, d, W, inv_norm));
+}
+
+size_t ds_kmeans_assign_workspace_bytes(int V) { return V > 0 ? ds::kmeans_assign_ws_bytes(V) : 0; }
+
+ds_status ds_kmeans_assign(hipStream_t s, int V, int d, const void *W, int M, const void *C,
+                           int32_t *assign, float *score, void *ws, size_t ws_bytes,
+                           hipEvent_t start, hipEvent_t stop)
+{
+    if (!W || !C || !assign || !score || V <= 0 || d <= 0 || M <= 0)
+        return DS_EINVAL;
+    if (d % 64 || d > 8192 || M > DS_MAX_CLUSTERS)
+        return DS_ESHAPE;
+    if (!aligned16(W) || !aligned16(C) || !ws || ws_bytes < ds_kmeans_assign_workspace_bytes(V))
+        return DS_EINVAL;
+    return hip_status(ds::kmeans_assign_launch(s, V, d, W, M, C, assign, score, ws, start, stop));
+}
+
+size_t ds_kmeans_update_workspace_bytes(int V, int d, int M)
+{
+    return V > 0 && d > 0 && M > 0 ? ds::kmeans_update_ws_bytes(V, d, M) : 0;
+}
+
+ds_status ds_kmeans_update(hipStream_t s, int V, int d, const void *W, const float *inv_norm, int M,
+                           const int32_t *assign, const float *C_prev, float *C_out,
+                           void *C_out_bf16, int32_t *size, double *norm, int32_t *err_flag,
+                           void *ws, size_t ws_bytes)
+{
+    if (!W || !inv_norm || !assign || !C_prev || !C_out || !C_out_bf16 || !size || !norm)
+        return DS_EINVAL;
+    if (V <= 0 || d <= 0 || M <= 0)
+        return DS_EINVAL;
+    if (d % 8 || d > 8192 || M > DS_MAX_CLUSTERS)
+        return DS_ESHAPE;
+    if (!aligned16(W) || !ws || ws_bytes < ds_kmeans_update_workspace_bytes(V, d, M))
+        return DS_EINVAL;
+    return hip_status(ds::kmeans_update_launch(s, V, d, W, inv_norm, M, assign, C_prev, C_out,
+                                               C_out_bf16, size, norm, err_flag, ws));
+}
+
 size_t ds_sample_workspace_bytes(int G, int m, int64_t max_len)
 {
     return G > 0 && m > 0 && max_len > 0 ? ds::sample_ws_bytes((int64_t)G * m, max_len) : 0;

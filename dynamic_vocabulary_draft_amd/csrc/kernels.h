@@ -44,6 +44,18 @@ hipError_t head_launch(hipStream_t s, bool bf16, int V, int d, const void *W, in
                        const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
                        hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
+// spherical k-means over W's rows (bf16)
+hipError_t kmeans_inv_norm_launch(hipStream_t s, int V, int d, const void *W, float *inv_norm);
+size_t kmeans_assign_ws_bytes(int V);
+hipError_t kmeans_assign_launch(hipStream_t s, int V, int d, const void *W, int M, const void *C,
+                                int32_t *assign, float *score, void *ws, hipEvent_t t0,
+                                hipEvent_t t1);
+size_t kmeans_update_ws_bytes(int V, int d, int M);
+hipError_t kmeans_update_launch(hipStream_t s, int V, int d, const void *W, const float *inv_norm,
+                                int M, const int32_t *assign, const float *C_prev, float *C_out,
+                                void *C_out_bf16, int32_t *size, double *norm, int32_t *err_flag,
+                                void *ws);
+
 // static shortlist slab: out[i] = W[ids[i]] (NaN row for ids outside [0, V))
 hipError_t pack_launch(hipStream_t s, bool bf16, int V, int d, const void *W, int64_t n,
                        const int32_t *ids, void *out);

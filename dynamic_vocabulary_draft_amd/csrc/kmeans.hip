@@ -1,0 +1,596 @@
+// Spherical k-means over the rows of the LM head: the offline step that
+// makes the vocabulary clusters the router selects from (DynaSpec summary
+// page, "Key Novelty": clusters from the semantic similarity of LM-head
+// weights; "Modeling / Key Hyperparameters": spherical k-means; "Key
+// Terms": clusters by cosine similarity).  The algorithm is the published
+// one (Dhillon and Modha, concept decompositions): unit rows x_y = w_y/|w_y|
+// are assigned to the unit centroid of largest cosine, then every centroid
+// becomes the normalised sum of its rows.  W is bf16.
+//
+// inverse norms: one wave per row, fp64 sums (once per W).
+// assign:  the V x M x d contraction on v_mfma_f32_32x32x16_bf16 with the
+//          argmax fused: a workgroup owns 128 rows x 128 centroids, each
+//          wave a 64 x 64 block (2 x 2 MFMA tiles); per 64-wide slice of d
+//          both tiles arrive as whole 128-byte lines (8 rows per load) into
+//          a double-buffered, XOR-swizzled LDS tile (one barrier per slice).
+//          Workgroups that share a row tile are laid out on one XCD (blocks
+//          are dealt round-robin over the 8 XCDs), so the tile is read from
+//          HBM once and then from that XCD's L2.  The epilogue reduces each
+//          row over its 128 columns (ties to the lower centroid) and keeps
+//          the row's best with a 64-bit atomicMax of (order-preserving score
+//          bits, ~centroid id): the maximum does not depend on the order the
+//          workgroups finish in, so the result is deterministic.  The row
+//          norm does not change the argmax, so the rows are not normalised.
+// update:  members grouped by cluster in ascending row id without atomics
+//          (per-chunk cluster counts, then a stable scatter: each 4096-row
+//          chunk sorts its (cluster, row) keys in LDS); fp64 sums of
+//          w_y * inv_norm[y] over member ranges of at most kUpdRange rows
+//          (clusters are Zipf-sized, so ranges balance the work), then one
+//          workgroup per cluster adds its ranges in order and normalises.
+#include "common.h"
+#include "kernels.h"
+
+namespace ds {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, CDNA encoding
+
+constexpr int kTileR = 128;  // W rows per workgroup
+constexpr int kTileC = 128;  // centroids per workgroup
+constexpr int kSlice = 64;   // hidden elements per LDS stage (128 B per row)
+constexpr int kScatterChunk = 4096;
+constexpr int kUpdRange = 1024;  // member rows per partial sum
+constexpr int kUpdGroup = 2048;  // hidden elements covered by one pass of 256 threads x 8
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+__device__ __forceinline__ f32x16 mfma(const u32x4 &a, const u32x4 &b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp32 -> order-preserving uint32 (larger float, larger integer; -0 and +0
+// are one value, as in a floating-point comparison)
+__device__ __forceinline__ uint32_t f32_key(float v)
+{
+    const uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_f32(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return 0x7FC0;  // NaN
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// --------------------------------------------------------------- inverse norms
+__global__ __launch_bounds__(256) void inv_norm_kernel(int V, int nch, const u32x4 *__restrict__ W,
+                                                       float *__restrict__ inv_norm)
+{
+    const int lane = lane_id();
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+    for (int64_t y = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); y < V; y += nw) {
+        const u32x4 *row = W + y * nch;
+        double ss = 0.0;
+        for (int c = lane; c < nch; c += kWave) {
+            const u32x4 v = __builtin_nontemporal_load(row + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double lo = bf16_lo(v[e]), hi = bf16_hi(v[e]);
+                ss += lo * lo;
+                ss += hi * hi;
+            }
+        }
+        ss = wave_sum_f64(ss);
+        if (lane == 0)
+            inv_norm[y] = ss > 0.0 ? (float)(1.0 / sqrt(ss)) : 0.0f;
+    }
+}
+
+// --------------------------------------------------------------------- assign
+__global__ void fill_u64_kernel(uint64_t *p, int64_t n, uint64_t v)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// this thread's four 16-byte pieces of a 128-row tile's slice: piece q =
+// tid + 256 i is row q/8 (tid/8 + 32 i), piece q%8 of the row's 128 bytes
+__device__ __forceinline__ void tile_load(rsrc_t r, int d, int k0, u32x4 v[4])
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (uint32_t)((tid >> 3) + 32 * i) * (uint32_t)d * 2u +
+                             2u * (uint32_t)k0 + 16u * (uint32_t)(tid & 7);
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    }
+}
+// LDS tile: [row][64 bf16], piece p of row r in slot p ^ (r & 7)
+__device__ __forceinline__ void tile_store(uint16_t *t, const u32x4 v[4])
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = (tid >> 3) + 32 * i, p = tid & 7;
+        *reinterpret_cast<u32x4 *>(t + row * kSlice + ((p ^ (row & 7)) << 3)) = v[i];
+    }
+}
+// MFMA operand: row `row` of a tile, pieces 4*(lane/32) + s (k permuted the
+// same way for both operands, so the products pair up exactly)
+__device__ __forceinline__ u32x4 frag(const uint16_t *t, int row, int s)
+{
+    const int p = 4 * (lane_id() >> 5) + s;
+    return *reinterpret_cast<const u32x4 *>(t + row * kSlice + ((p ^ (row & 7)) << 3));
+}
+
+__global__ __launch_bounds__(256) void kmeans_assign_kernel(int V, int d, const uint16_t *__restrict__ W,
+                                                            int M, const uint16_t *__restrict__ C,
+                                                            int RT, int CT,
+                                                            unsigned long long *__restrict__ best)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(kTileR + kTileC) * kSlice];
+    const int b = blockIdx.x;
+    const int rt = (b / (8 * CT)) * 8 + (b % 8), ct = (b / 8) % CT;  // a row tile stays on one XCD
+    if (rt >= RT)
+        return;
+    const int lane = lane_id(), wave = threadIdx.x >> 6, wr = wave >> 1, wc = wave & 1;
+    const int64_t y0 = (int64_t)rt * kTileR;
+    const int c0 = ct * kTileC;
+    const int rows = (int)min((int64_t)kTileR, (int64_t)V - y0), cols = min(kTileC, M - c0);
+    const rsrc_t ra = make_rsrc(W + y0 * d, (uint32_t)rows * (uint32_t)d * 2u);
+    const rsrc_t rb = make_rsrc(C + (int64_t)c0 * d, (uint32_t)cols * (uint32_t)d * 2u);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = f32x16{};
+    const int nsl = d / kSlice;
+    u32x4 va[4], vb[4];
+    tile_load(ra, d, 0, va);
+    tile_load(rb, d, 0, vb);
+    tile_store(lds[0], va);
+    tile_store(lds[0] + kTileR * kSlice, vb);
+    __syncthreads();
+    for (int s = 0; s < nsl; ++s) {
+        if (s + 1 < nsl) {  // next slice in flight during this one's MFMAs
+            tile_load(ra, d, (s + 1) * kSlice, va);
+            tile_load(rb, d, (s + 1) * kSlice, vb);
+        }
+        const uint16_t *ta = lds[s & 1], *tb = lds[s & 1] + kTileR * kSlice;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            u32x4 a[2], bb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = frag(ta, wr * 64 + i * 32 + (lane & 31), st);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bb[j] = frag(tb, wc * 64 + j * 32 + (lane & 31), st);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = mfma(a[i], bb[j], acc[i][j]);
+        }
+        if (s + 1 < nsl) {
+            tile_store(lds[(s + 1) & 1], va);
+            tile_store(lds[(s + 1) & 1] + kTileR * kSlice, vb);
+        }
+        __syncthreads();
+    }
+    // epilogue: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 of
+    // the 32 x 32 tile, column l%32
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            int col0 = wc * 64 + (lane & 31), col1 = col0 + 32;
+            float v0 = col0 < cols ? acc[i][0][r] : -INFINITY;
+            float v1 = col1 < cols ? acc[i][1][r] : -INFINITY;
+            float v = v0;
+            int c = col0;
+            if (v1 > v0) {
+                v = v1;
+                c = col1;
+            }
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) {  // within each 32-lane half
+                const float ov = __shfl_xor(v, o);
+                const int oc = __shfl_xor(c, o);
+                if (ov > v || (ov == v && oc < c)) {
+                    v = ov;
+                    c = oc;
+                }
+            }
+            const int row = wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if ((lane & 31) == 0 && row < rows && v > -INFINITY) {
+                const uint64_t key = ((uint64_t)f32_key(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)(c0 + c));
+                atomicMax(&best[y0 + row], (unsigned long long)key);
+            }
+        }
+    }
+}
+
+__global__ void assign_finalize_kernel(int V, const unsigned long long *__restrict__ best,
+                                       int32_t *__restrict__ assign, float *__restrict__ score)
+{
+    for (int64_t y = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; y < V;
+         y += (int64_t)gridDim.x * blockDim.x) {
+        const uint64_t k = best[y];
+        assign[y] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+        score[y] = key_f32((uint32_t)(k >> 32));
+    }
+}
+
+// --------------------------------------------------------------------- update
+// offsets: off[c] = first member slot of cluster c, item_off[c] = first
+// partial-sum item of c (ceil(size/kUpdRange) items each); one workgroup
+__global__ __launch_bounds__(1024) void update_offsets_kernel(int M, int nchunks,
+                                                              const int32_t *__restrict__ index,
+                                                              int32_t *__restrict__ off,
+                                                              int32_t *__restrict__ item_off,
+                                                              int32_t *__restrict__ size)
+{
+    __shared__ int64_t sh[kWave + 1];
+    const int32_t *sizes = index + (int64_t)nchunks * M;
+    int64_t carry_m = 0, carry_i = 0;
+    for (int c0 = 0; c0 < M; c0 += 1024) {
+        const int c = c0 + (int)threadIdx.x;
+        const int64_t n = c < M ? sizes[c] : 0;
+        const int64_t it = (n + kUpdRange - 1) / kUpdRange;
+        int64_t tot_m, tot_i;
+        const int64_t em = block_excl_scan_i64(n, sh, &tot_m);
+        const int64_t ei = block_excl_scan_i64(it, sh, &tot_i);
+        if (c < M) {
+            off[c] = (int32_t)(carry_m + em);
+            item_off[c] = (int32_t)(carry_i + ei);
+            size[c] = (int32_t)n;
+        }
+        carry_m += tot_m;
+        carry_i += tot_i;
+    }
+    if (threadIdx.x == 0) {
+        off[M] = (int32_t)carry_m;
+        item_off[M] = (int32_t)carry_i;
+    }
+}
+
+// stable scatter of one 4096-row chunk: sort its (cluster, row) keys, then
+// a row's slot is its cluster's start + the cluster's members in earlier
+// chunks + its rank among the chunk's members of that cluster
+__global__ __launch_bounds__(256) void update_scatter_kernel(int V, int M,
+                                                             const int32_t *__restrict__ assign,
+                                                             const int32_t *__restrict__ index,
+                                                             const int32_t *__restrict__ off,
+                                                             int32_t *__restrict__ members)
+{
+    __shared__ uint64_t key[kScatterChunk];
+    __shared__ int s_wmax[4];
+    const int chunk = blockIdx.x;
+    const int64_t y0 = (int64_t)chunk * kScatterChunk;
+    for (int i = threadIdx.x; i < kScatterChunk; i += blockDim.x) {
+        const int64_t y = y0 + i;
+        const int c = y < V ? assign[y] : -1;
+        key[i] = (c >= 0 && c < M) ? (((uint64_t)(uint32_t)c << 32) | (uint32_t)y) : ~0ull;
+    }
+    __syncthreads();
+    for (int k = 2; k <= kScatterChunk; k <<= 1) {  // bitonic sort, ascending
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int t = threadIdx.x; t < kScatterChunk / 2; t += blockDim.x) {
+                const int i = 2 * t - (t & (j - 1));
+                const bool up = (i & k) == 0;
+                const uint64_t a = key[i], bk = key[i + j];
+                if ((a > bk) == up) {
+                    key[i] = bk;
+                    key[i + j] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // segment starts: thread t owns sorted slots 16t .. 16t+15
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int i0 = threadIdx.x * 16;
+    int start[16];
+    int run = -1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int i = i0 + e;
+        const bool first = i == 0 || (key[i] >> 32) != (key[i - 1] >> 32);
+        if (first)
+            run = i;
+        start[e] = run;
+    }
+    // carry the last start from earlier threads (inclusive max scan)
+    int m = run;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(m, o);
+        if (lane >= o)
+            m = max(m, t);
+    }
+    if (lane == kWave - 1)
+        s_wmax[wave] = m;
+    __syncthreads();
+    int carry = __shfl_up(m, 1);
+    if (lane == 0)
+        carry = -1;
+    for (int w = 0; w < wave; ++w)
+        carry = max(carry, s_wmax[w]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int i = i0 + e;
+        const uint64_t kv = key[i];
+        if (kv == ~0ull)
+            continue;
+        const int c = (int)(kv >> 32);
+        const int st = start[e] >= 0 ? start[e] : carry;
+        members[off[c] + index[(int64_t)chunk * M + c] + (i - st)] = (int32_t)(uint32_t)kv;
+    }
+}
+
+// fp64 sum of w_y * inv_norm[y] over one member range (ascending y); thread
+// t owns hidden elements 8t .. 8t+7 of every 2048-element group
+template <int G>
+__global__ __launch_bounds__(256) void update_partial_kernel(int d, const uint16_t *__restrict__ W,
+                                                             const float *__restrict__ inv_norm,
+                                                             int M, const int32_t *__restrict__ off,
+                                                             const int32_t *__restrict__ item_off,
+                                                             const int32_t *__restrict__ members,
+                                                             double *__restrict__ partial)
+{
+    const int b = blockIdx.x;
+    if (b >= item_off[M])
+        return;
+    int lo = 0, hi = M;  // cluster: last c with item_off[c] <= b
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (item_off[mid] <= b)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const int c = lo;
+    const int64_t j0 = (int64_t)off[c] + (int64_t)(b - item_off[c]) * kUpdRange;
+    const int64_t j1 = min(j0 + kUpdRange, (int64_t)off[c + 1]);
+    double acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[g][e] = 0.0;
+    const int kt = threadIdx.x * 8;
+    for (int64_t j = j0; j < j1; j += 4) {
+        u32x4 v[4][G];
+        double s[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // four member rows in flight
+            const bool in = j + q < j1;
+            const int32_t y = in ? members[j + q] : 0;
+            s[q] = in ? (double)inv_norm[y] : 0.0;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int k = g * kUpdGroup + kt;
+                v[q][g] = (in && k < d)
+                              ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(W + (int64_t)y * d + k))
+                              : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[g][2 * e] += (double)bf16_lo(v[q][g][e]) * s[q];
+                    acc[g][2 * e + 1] += (double)bf16_hi(v[q][g][e]) * s[q];
+                }
+    }
+    double *out = partial + (int64_t)b * d;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int k = g * kUpdGroup + kt;
+        if (k < d)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                out[k + e] = acc[g][e];
+    }
+}
+
+// one workgroup per cluster: its ranges added in order, normalised
+template <int G>
+__global__ __launch_bounds__(256) void update_finalize_kernel(int d, int M,
+                                                              const int32_t *__restrict__ item_off,
+                                                              const int32_t *__restrict__ size,
+                                                              const double *__restrict__ partial,
+                                                              const float *__restrict__ C_prev,
+                                                              float *__restrict__ C_out,
+                                                              uint16_t *__restrict__ C_out_bf16,
+                                                              double *__restrict__ norm)
+{
+    __shared__ double s_w[4];
+    const int c = blockIdx.x;
+    const int kt = threadIdx.x * 8;
+    double sv[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            sv[g][e] = 0.0;
+    for (int it = item_off[c]; it < item_off[c + 1]; ++it) {
+        const double *p = partial + (int64_t)it * d;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int k = g * kUpdGroup + kt;
+            if (k < d)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    sv[g][e] += p[k + e];
+        }
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            ss += sv[g][e] * sv[g][e];
+    ss = wave_sum_f64(ss);
+    if (lane_id() == 0)
+        s_w[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    ss = ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
+    const double nrm = sqrt(ss);
+    const bool keep = size[c] <= 0 || !(nrm > 0.0);
+    if (threadIdx.x == 0)
+        norm[c] = size[c] > 0 ? nrm : 0.0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int k = g * kUpdGroup + kt;
+        if (k < d)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t at = (int64_t)c * d + k + e;
+                const float v = keep ? C_prev[at] : (float)(sv[g][e] / nrm);
+                C_out[at] = v;
+                C_out_bf16[at] = f32_to_bf16_rne(v);
+            }
+    }
+}
+
+struct UpdWs {
+    int32_t *index, *off, *item_off, *members;
+    double *partial;
+};
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+UpdWs upd_ws(void *ws, int V, int d, int M)
+{
+    const int64_t nch = ((int64_t)V + kScatterChunk - 1) / kScatterChunk;
+    char *p = reinterpret_cast<char *>(ws);
+    UpdWs w;
+    w.index = reinterpret_cast<int32_t *>(p);
+    p += align256((size_t)(nch + 1) * M * 4);
+    w.off = reinterpret_cast<int32_t *>(p);
+    p += align256((size_t)(M + 1) * 4);
+    w.item_off = reinterpret_cast<int32_t *>(p);
+    p += align256((size_t)(M + 1) * 4);
+    w.members = reinterpret_cast<int32_t *>(p);
+    p += align256((size_t)V * 4);
+    w.partial = reinterpret_cast<double *>(p);
+    return w;
+}
+
+int64_t max_items(int V, int M) { return (int64_t)M + ((int64_t)V + kUpdRange - 1) / kUpdRange; }
+
+template <int G>
+hipError_t launch_update_g(hipStream_t s, int V, int d, const uint16_t *W, const float *inv_norm,
+                           int M, const UpdWs &w, const float *C_prev, float *C_out,
+                           uint16_t *C_out_bf16, int32_t *size, double *norm)
+{
+    hipLaunchKernelGGL((update_partial_kernel<G>), dim3((unsigned)max_items(V, M)), dim3(256), 0, s,
+                       d, W, inv_norm, M, w.off, w.item_off, w.members, w.partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((update_finalize_kernel<G>), dim3((unsigned)M), dim3(256), 0, s, d, M,
+                       w.item_off, size, w.partial, C_prev, C_out, C_out_bf16, norm);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t kmeans_inv_norm_launch(hipStream_t s, int V, int d, const void *W, float *inv_norm)
+{
+    int64_t blocks = ((int64_t)V + 3) / 4;
+    const int64_t cap = 8LL * device_cu_count();
+    if (blocks > cap)
+        blocks = cap;
+    hipLaunchKernelGGL(inv_norm_kernel, dim3((unsigned)blocks), dim3(256), 0, s, V, d / 8,
+                       reinterpret_cast<const u32x4 *>(W), inv_norm);
+    return hipGetLastError();
+}
+
+size_t kmeans_assign_ws_bytes(int V) { return (size_t)V * 8 + 256; }
+
+hipError_t kmeans_assign_launch(hipStream_t s, int V, int d, const void *W, int M, const void *C,
+                                int32_t *assign, float *score, void *ws, hipEvent_t t0,
+                                hipEvent_t t1)
+{
+    unsigned long long *best = reinterpret_cast<unsigned long long *>(ws);
+    const unsigned fb = (unsigned)min(((int64_t)V + 255) / 256, (int64_t)4096);
+    hipLaunchKernelGGL(fill_u64_kernel, dim3(fb), dim3(256), 0, s, reinterpret_cast<uint64_t *>(best),
+                       (int64_t)V, (uint64_t)0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int RT = (V + kTileR - 1) / kTileR, CT = (M + kTileC - 1) / kTileC;
+    const int RTp = (RT + 7) / 8 * 8;  // row tiles padded to whole XCD rounds
+    e = launch_timed(kmeans_assign_kernel, dim3((unsigned)((int64_t)RTp * CT)), dim3(256), s, t0, t1,
+                     V, d, reinterpret_cast<const uint16_t *>(W), M,
+                     reinterpret_cast<const uint16_t *>(C), RT, CT, best);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(assign_finalize_kernel, dim3(fb), dim3(256), 0, s, V,
+                       (const unsigned long long *)best, assign, score);
+    return hipGetLastError();
+}
+
+size_t kmeans_update_ws_bytes(int V, int d, int M)
+{
+    const int64_t nch = ((int64_t)V + kScatterChunk - 1) / kScatterChunk;
+    return align256((size_t)(nch + 1) * M * 4) + 2 * align256((size_t)(M + 1) * 4) +
+           align256((size_t)V * 4) + (size_t)max_items(V, M) * d * 8 + 256;
+}
+
+hipError_t kmeans_update_launch(hipStream_t s, int V, int d, const void *W, const float *inv_norm,
+                                int M, const int32_t *assign, const float *C_prev, float *C_out,
+                                void *C_out_bf16, int32_t *size, double *norm, int32_t *err_flag,
+                                void *ws)
+{
+    UpdWs w = upd_ws(ws, V, d, M);
+    const int nch = (V + kScatterChunk - 1) / kScatterChunk;
+    hipError_t e = index_launch(s, M, V, assign, w.index, err_flag);  // per-chunk cluster counts
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(update_offsets_kernel, dim3(1), dim3(1024), 0, s, M, nch,
+                       (const int32_t *)w.index, w.off, w.item_off, size);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(update_scatter_kernel, dim3((unsigned)nch), dim3(256), 0, s, V, M, assign,
+                       (const int32_t *)w.index, (const int32_t *)w.off, w.members);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    const uint16_t *Wb = reinterpret_cast<const uint16_t *>(W);
+    uint16_t *Cb = reinterpret_cast<uint16_t *>(C_out_bf16);
+    const int G = (d + kUpdGroup - 1) / kUpdGroup;
+    switch (G) {
+    case 1:
+        return launch_update_g<1>(s, V, d, Wb, inv_norm, M, w, C_prev, C_out, Cb, size, norm);
+    case 2:
+        return launch_update_g<2>(s, V, d, Wb, inv_norm, M, w, C_prev, C_out, Cb, size, norm);
+    case 3:
+        return launch_update_g<3>(s, V, d, Wb, inv_norm, M, w, C_prev, C_out, Cb, size, norm);
+    default:
+        return launch_update_g<4>(s, V, d, Wb, inv_norm, M, w, C_prev, C_out, Cb, size, norm);
+    }
+}
+
+}  // namespace ds

@@ -62,6 +62,12 @@ _SIGS = {
     "ds_gathered_lm_head_timed": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _i64, _vp, _vp, _i64, _vp,
                                        _vp, _sz, _vp, _vp]),
     "ds_pack_rows": (_i, [_vp, _i, _i, _i, _vp, _i64, _vp, _vp]),
+    "ds_kmeans_inv_norms": (_i, [_vp, _i, _i, _vp, _vp]),
+    "ds_kmeans_assign_workspace_bytes": (_sz, [_i]),
+    "ds_kmeans_assign": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "ds_kmeans_update_workspace_bytes": (_sz, [_i, _i, _i]),
+    "ds_kmeans_update": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                              _sz]),
     "ds_sample_workspace_bytes": (_sz, [_i, _i, _i64]),
     "ds_shortlist_sample": (_i, [_vp, _i, _i, _vp, _vp, _vp, _f, _vp, _i64, _vp, _vp, _vp, _sz]),
     "ds_softmax_workspace_bytes": (_sz, [_i, _i]),
@@ -236,6 +242,38 @@ def pack_rows(W, ids, out, *, stream=None):
     V, d = W.shape
     _check("ds_pack_rows", lib.ds_pack_rows(_s(stream), _dt(W), V, d, _p(W), ids.numel(),
                                             _p(ids), _p(out)))
+
+
+def kmeans_inv_norms(W, inv_norm, *, stream=None):
+    V, d = W.shape
+    _check("ds_kmeans_inv_norms", lib.ds_kmeans_inv_norms(_s(stream), V, d, _p(W), _p(inv_norm)))
+
+
+def kmeans_assign(W, Cb, assign, score, ws=None, *, stream=None, events=None):
+    """W [V][d] bf16, Cb [M][d] bf16 centroids -> assign [V] int32, score [V]
+    fp32.  events: optional (start, stop) raw hipEvent_t handles."""
+    V, d = W.shape
+    M = Cb.shape[0]
+    if ws is None:
+        ws = workspace(lib.ds_kmeans_assign_workspace_bytes(V), W.device)
+    ev = (None, None) if events is None else (C.c_void_p(events[0]), C.c_void_p(events[1]))
+    _check("ds_kmeans_assign", lib.ds_kmeans_assign(
+        _s(stream), V, d, _p(W), M, _p(Cb), _p(assign), _p(score), _p(ws), _nbytes(ws), *ev))
+
+
+def kmeans_update_workspace_bytes(V: int, d: int, M: int) -> int:
+    return lib.ds_kmeans_update_workspace_bytes(V, d, M)
+
+
+def kmeans_update(W, inv_norm, assign, C_prev, C_out, C_out_bf16, size, norm, ws=None, *,
+                  err_flag=None, stream=None):
+    V, d = W.shape
+    M = C_prev.shape[0]
+    if ws is None:
+        ws = workspace(kmeans_update_workspace_bytes(V, d, M), W.device)
+    _check("ds_kmeans_update", lib.ds_kmeans_update(
+        _s(stream), V, d, _p(W), _p(inv_norm), M, _p(assign), _p(C_prev), _p(C_out),
+        _p(C_out_bf16), _p(size), _p(norm), _p(err_flag), _p(ws), _nbytes(ws)))
 
 
 def shortlist_sample(sl_off, sl_ids, logits, temperature, u, token, q, ws, *, max_len, m=1,

@@ -207,6 +207,51 @@ ds_status ds_pack_rows(hipStream_t s, ds_dtype dt, int V, int d, const void *W, 
                        const int32_t *ids, void *out);
 
 /*
+ * Spherical k-means over the rows of the LM head, the offline clustering the
+ * router selects from [S "Key Novelty": clusters from the semantic
+ * similarity of LM-head weights; "Modeling / Key Hyperparameters":
+ * spherical k-means; "Key Terms": clusters by cosine similarity].  The
+ * algorithm is the published one (Dhillon and Modha, concept
+ * decompositions): assign each unit row x_y = w_y / |w_y| to the unit
+ * centroid of largest cosine, then replace each centroid by the normalised
+ * sum of its rows.  W is [V][d] bf16, 16-byte aligned.  All three calls are
+ * deterministic (no floating-point atomics).
+ *
+ * ds_kmeans_inv_norms: inv_norm[y] = 1 / |w_y| (fp64 sums, fp32 result; 0 for
+ * an all-zero row).  d a multiple of 8, at most 8192.
+ */
+ds_status ds_kmeans_inv_norms(hipStream_t s, int V, int d, const void *W, float *inv_norm);
+/*
+ * ds_kmeans_assign: assign[y] = argmax_c w_y . C[c] (the row norm does not
+ * change the argmax) over bf16 unit centroids C [M][d], ties to the lower
+ * c; score[y] = that dot product (bf16 products, fp32 accumulation on the
+ * matrix cores).  d a multiple of 64, at most 8192; M <= DS_MAX_CLUSTERS.
+ * ws >= ds_kmeans_assign_workspace_bytes(V) bytes.  start / stop (may be
+ * NULL): timing events stamped at the contraction kernel's own start and end.
+ */
+size_t ds_kmeans_assign_workspace_bytes(int V);
+ds_status ds_kmeans_assign(hipStream_t s, int V, int d, const void *W, int M, const void *C,
+                           int32_t *assign, float *score, void *ws, size_t ws_bytes,
+                           hipEvent_t start, hipEvent_t stop);
+/*
+ * ds_kmeans_update: for every cluster c, s_c = sum over rows y with
+ * assign[y] = c, in ascending y, of w_y * inv_norm[y] (fp64); C_out[c] =
+ * s_c / |s_c| as fp32 and C_out_bf16[c] its bf16 rounding (nearest-even),
+ * the centroids the next ds_kmeans_assign reads.  A cluster without rows
+ * keeps C_prev[c].  size[c] = its row count; norm[c] = |s_c| (0 when
+ * empty), whose sum is the objective sum_y x_y . C_out[assign[y]].  Labels
+ * outside [0, M) are skipped and raise DS_EINVAL in *err_flag (may be
+ * NULL).  d a multiple of 8, at most 8192; M <= DS_MAX_CLUSTERS.
+ * C_prev, C_out [M][d] fp32; C_out_bf16 [M][d] bf16; norm [M] fp64.
+ * ws >= ds_kmeans_update_workspace_bytes(V, d, M) bytes.
+ */
+size_t ds_kmeans_update_workspace_bytes(int V, int d, int M);
+ds_status ds_kmeans_update(hipStream_t s, int V, int d, const void *W, const float *inv_norm, int M,
+                           const int32_t *assign, const float *C_prev, float *C_out,
+                           void *C_out_bf16, int32_t *size, double *norm, int32_t *err_flag,
+                           void *ws, size_t ws_bytes);
+
+/*
  * Draft proposal from the shortlist distribution [A; S "Pipeline Flow"].
  * Per row (g, i), q = softmax(logits / temperature) over S_g computed in
  * fp64, and token = S_g[j*] with j* the first index whose running sum of

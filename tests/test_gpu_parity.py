@@ -509,3 +509,124 @@ def test_verify_parity(N, oracle_lib, V, T, B, mode):
         assert (n_ref == T).all()
     if mode == "correlated":
         assert n_ref.mean() > 0.5
+
+
+# ----------------------------------------------------------------------------
+# spherical k-means over the LM-head rows
+# ----------------------------------------------------------------------------
+def _km_head(V, d, M, seed):
+    cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=M)
+    cluster_of, _ = syn.make_clusters(cfg)
+    return cfg, cluster_of, syn.make_lm_head(cfg, cluster_of)
+
+
+def _bf16_rne(x32):
+    return syn.f32_to_bf16_bits(np.asarray(x32, np.float32))
+
+
+@pytest.mark.parametrize("V,d", [(3001, 64), (5000, 3840)])
+def test_kmeans_inv_norms(N, oracle_lib, V, d):
+    cfg, _, W = _km_head(V, d, 16, 0)
+    W[3] = 0
+    out = torch.empty(V, device="cuda")
+    N.kmeans_inv_norms(to_dev(W), out)
+    _ulp_bar(_cpu(out), oracle_lib.kmeans_inv_norms(W))
+
+
+@pytest.mark.parametrize("V,d,M", [(3001, 64, 200), (4000, 256, 128), (2500, 3840, 37),
+                                   (1000, 128, 1)])
+def test_kmeans_assign(N, oracle_lib, V, d, M):
+    """Ragged row and centroid tiles, one and many 64-wide slices; rows are
+    compared outside the band where fp32 accumulation order may decide."""
+    cfg, _, W = _km_head(V, d, max(M, 2), 1)
+    g = np.random.default_rng(V + M)
+    Cf = g.standard_normal((M, d)).astype(np.float32)
+    Cf /= np.linalg.norm(Cf, axis=1, keepdims=True)
+    Cb = _bf16_rne(Cf)
+    if M > 4:
+        Cb[M - 1] = Cb[2]  # an exact duplicate: the lower id must win
+    ref, sref, tie = oracle_lib.kmeans_assign(W, Cb)
+    a = torch.empty(V, dtype=torch.int32, device="cuda")
+    sc = torch.empty(V, device="cuda")
+    N.kmeans_assign(to_dev(W), to_dev(Cb), a, sc)
+    got = _cpu(a)
+    assert np.array_equal(got[~tie], ref[~tie])
+    assert ((got >= 0) & (got < M)).all()
+    if M > 4:
+        assert not (got == M - 1).any()
+    bound = d * 2.0 ** -22 * np.abs(sref).max() + 1e-6
+    assert np.abs(_cpu(sc)[~tie] - sref[~tie]).max() <= bound * 50
+
+
+def _km_update_gpu(N, W, inv, lab, Cp, M, err=None):
+    V, d = W.shape
+    out = torch.empty(M, d, device="cuda")
+    outb = torch.empty(M, d, dtype=torch.bfloat16, device="cuda")
+    size = torch.empty(M, dtype=torch.int32, device="cuda")
+    norm = torch.empty(M, dtype=torch.float64, device="cuda")
+    N.kmeans_update(to_dev(W), inv, to_dev(lab), to_dev(Cp), out, outb, size, norm, err_flag=err)
+    return _cpu(out), _cpu(outb.view(torch.int16)).view(np.uint16), _cpu(size), _cpu(norm)
+
+
+@pytest.mark.parametrize("V,d,M", [(3001, 64, 20), (9000, 264, 300), (20000, 2056, 64)])
+def test_kmeans_update(N, oracle_lib, V, d, M):
+    """Clusters from empty to larger than one member range (1024 rows),
+    several scatter chunks, d with a partial 2048-element group."""
+    cfg, cluster_of, W = _km_head(V, d, M, 2)
+    inv_h = oracle_lib.kmeans_inv_norms(W)
+    lab = syn.kmeans_init_assign(cfg, cluster_of, 0.3)
+    lab[lab == 5] = 6  # cluster 5 empty
+    if V > 10000:
+        lab[: V // 2] = 1  # one cluster of 10000 rows: ten member ranges
+    Cp = np.random.default_rng(7).standard_normal((M, d)).astype(np.float32)
+    inv = to_dev(inv_h)
+    out, outb, size, norm = _km_update_gpu(N, W, inv, lab, Cp, M)
+    ref, rsize, rnorm = oracle_lib.kmeans_update(W, inv_h, lab, Cp)
+    assert np.array_equal(size, rsize)
+    _ulp_bar(out, ref)
+    assert np.array_equal(out[5], Cp[5])
+    assert np.array_equal(outb, _bf16_rne(out))
+    assert np.allclose(norm, rnorm, rtol=1e-12, atol=0)
+
+
+def test_kmeans_update_invalid_labels(N, oracle_lib):
+    cfg, cluster_of, W = _km_head(3000, 64, 20, 3)
+    inv_h = oracle_lib.kmeans_inv_norms(W)
+    lab = cluster_of.astype(np.int32).copy()
+    lab[[4, 99]] = [-1, 20]
+    Cp = np.zeros((20, 64), np.float32)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, _, size, _ = _km_update_gpu(N, W, to_dev(inv_h), lab, Cp, 20, err=flag)
+    assert int(_cpu(flag)[0]) == oracle.EINVAL
+    ref, rsize, _ = oracle_lib.kmeans_update(W, inv_h, lab, Cp)
+    assert np.array_equal(size, rsize)
+    _ulp_bar(out, ref)
+
+
+def test_kmeans_iterations_recover_planted(N, oracle_lib):
+    """Several GPU iterations checked stage by stage against the oracle on the
+    GPU's own inputs; from a 30%-noisy start they recover the planted
+    partition and the objective does not decrease."""
+    V, d, M = 6000, 256, 40
+    cfg, cluster_of, W = _km_head(V, d, M, 4)
+    Wd = to_dev(W)
+    inv = torch.empty(V, device="cuda")
+    N.kmeans_inv_norms(Wd, inv)
+    inv_h = _cpu(inv)
+    lab = syn.kmeans_init_assign(cfg, cluster_of, 0.3)
+    Cp = np.zeros((M, d), np.float32)
+    objs = []
+    a = torch.empty(V, dtype=torch.int32, device="cuda")
+    sc = torch.empty(V, device="cuda")
+    for it in range(3):
+        out, outb, size, norm = _km_update_gpu(N, W, inv, lab, Cp, M)
+        ref, _, _ = oracle_lib.kmeans_update(W, inv_h, lab, Cp)
+        _ulp_bar(out, ref)
+        objs.append(float(norm.sum()))
+        N.kmeans_assign(Wd, to_dev(outb), a, sc)
+        lab = _cpu(a)
+        rl, _, tie = oracle_lib.kmeans_assign(W, outb)
+        assert np.array_equal(lab[~tie], rl[~tie])
+        Cp = out
+    assert np.array_equal(lab, cluster_of)
+    assert all(b >= a_ * (1 - 1e-6) for a_, b in zip(objs, objs[1:]))
