@@ -42,7 +42,8 @@ constexpr int kTileR = 128;  // W rows per workgroup
 constexpr int kTileC = 128;  // centroids per workgroup
 constexpr int kSlice = 64;   // hidden elements per LDS stage (128 B per row)
 constexpr int kScatterChunk = 4096;
-constexpr int kUpdRange = 1024;  // member rows per partial sum
+constexpr int kUpdRange = 128;   // member rows per partial sum
+constexpr int kUpdBatch = 8;     // member rows in flight per workgroup
 constexpr int kUpdGroup = 2048;  // hidden elements covered by one pass of 256 threads x 8
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -377,30 +378,41 @@ __global__ __launch_bounds__(256) void update_partial_kernel(int d, const uint16
         for (int e = 0; e < 8; ++e)
             acc[g][e] = 0.0;
     const int kt = threadIdx.x * 8;
-    for (int64_t j = j0; j < j1; j += 4) {
-        u32x4 v[4][G];
-        double s[4];
+    // ids and scales of the next batch are fetched while this batch's rows load
+    int32_t yn[kUpdBatch];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {  // four member rows in flight
-            const bool in = j + q < j1;
-            const int32_t y = in ? members[j + q] : 0;
-            s[q] = in ? (double)inv_norm[y] : 0.0;
+    for (int q = 0; q < kUpdBatch; ++q)
+        yn[q] = j0 + q < j1 ? members[j0 + q] : -1;
+    for (int64_t j = j0; j < j1; j += kUpdBatch) {
+        int32_t y[kUpdBatch];
+#pragma unroll
+        for (int q = 0; q < kUpdBatch; ++q)
+            y[q] = yn[q];
+        u32x4 v[kUpdBatch][G];
+        double sc[kUpdBatch];
+#pragma unroll
+        for (int q = 0; q < kUpdBatch; ++q) {
+            const bool in = y[q] >= 0;
+            sc[q] = in ? (double)inv_norm[y[q]] : 0.0;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const int k = g * kUpdGroup + kt;
                 v[q][g] = (in && k < d)
-                              ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(W + (int64_t)y * d + k))
+                              ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(W + (int64_t)y[q] * d + k))
                               : u32x4{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < kUpdBatch; ++q)
+            yn[q] = j + kUpdBatch + q < j1 ? members[j + kUpdBatch + q] : -1;
+#pragma unroll
+        for (int q = 0; q < kUpdBatch; ++q)  // members in ascending order
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    acc[g][2 * e] += (double)bf16_lo(v[q][g][e]) * s[q];
-                    acc[g][2 * e + 1] += (double)bf16_hi(v[q][g][e]) * s[q];
+                    acc[g][2 * e] += (double)bf16_lo(v[q][g][e]) * sc[q];
+                    acc[g][2 * e + 1] += (double)bf16_hi(v[q][g][e]) * sc[q];
                 }
     }
     double *out = partial + (int64_t)b * d;

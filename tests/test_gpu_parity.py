@@ -570,7 +570,7 @@ def _km_update_gpu(N, W, inv, lab, Cp, M, err=None):
 
 @pytest.mark.parametrize("V,d,M", [(3001, 64, 20), (9000, 264, 300), (20000, 2056, 64)])
 def test_kmeans_update(N, oracle_lib, V, d, M):
-    """Clusters from empty to larger than one member range (1024 rows),
+    """Clusters from empty to many member ranges (128 rows each),
     several scatter chunks, d with a partial 2048-element group."""
     cfg, cluster_of, W = _km_head(V, d, M, 2)
     inv_h = oracle_lib.kmeans_inv_norms(W)
