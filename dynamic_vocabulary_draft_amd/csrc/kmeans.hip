@@ -9,8 +9,10 @@
 //
 // inverse norms: one wave per row, fp64 sums (once per W).
 // assign:  the V x M x d contraction on v_mfma_f32_32x32x16_bf16 with the
-//          argmax fused: a workgroup owns 128 rows x 128 centroids, each
-//          wave a 64 x 64 block (2 x 2 MFMA tiles); per 64-wide slice of d
+//          argmax fused: a workgroup (8 waves) owns 256 rows x 128
+//          centroids, each wave a 64 x 64 block (2 x 2 MFMA tiles; the tall
+//          tile halves how often the centroids, which do not fit one XCD's
+//          L2, are streamed again); per 64-wide slice of d
 //          both tiles arrive as whole 128-byte lines (8 rows per load) into
 //          a double-buffered, XOR-swizzled LDS tile (one barrier per slice).
 //          Workgroups that share a row tile are laid out on one XCD (blocks
@@ -38,8 +40,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, CDNA encoding
 
-constexpr int kTileR = 128;  // W rows per workgroup
-constexpr int kTileC = 128;  // centroids per workgroup
+constexpr int kTileR = 256;  // W rows per workgroup (4 waves high)
+constexpr int kTileC = 128;  // centroids per workgroup (2 waves wide)
+constexpr int kAsgThreads = 512;
 constexpr int kSlice = 64;   // hidden elements per LDS stage (128 B per row)
 constexpr int kScatterChunk = 4096;
 constexpr int kUpdRange = 128;   // member rows per partial sum
@@ -110,25 +113,36 @@ __global__ void fill_u64_kernel(uint64_t *p, int64_t n, uint64_t v)
         p[i] = v;
 }
 
-// this thread's four 16-byte pieces of a 128-row tile's slice: piece q =
-// tid + 256 i is row q/8 (tid/8 + 32 i), piece q%8 of the row's 128 bytes
-__device__ __forceinline__ void tile_load(rsrc_t r, int d, int k0, u32x4 v[4])
+// this thread's 16-byte pieces of an R-row tile's slice: piece q = tid +
+// kAsgThreads i is row q/8, piece q%8 of the row's 128 bytes.  The per-lane
+// part of the offset (row, piece) is fixed, vo[i]; the slice offset is
+// wave-uniform and goes in the scalar offset (the range check uses vo[i]:
+// rows past the tile read zero).
+template <int R>
+__device__ __forceinline__ void tile_offsets(int d, uint32_t vo[R * 8 / kAsgThreads])
 {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (uint32_t)((tid >> 3) + 32 * i) * (uint32_t)d * 2u +
-                             2u * (uint32_t)k0 + 16u * (uint32_t)(tid & 7);
-        v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    }
+    for (int i = 0; i < R * 8 / kAsgThreads; ++i)
+        vo[i] = (uint32_t)((tid >> 3) + (kAsgThreads / 8) * i) * (uint32_t)d * 2u +
+                16u * (uint32_t)(tid & 7);
+}
+template <int R>
+__device__ __forceinline__ void tile_load(rsrc_t r, const uint32_t vo[R * 8 / kAsgThreads], int k0,
+                                          u32x4 v[R * 8 / kAsgThreads])
+{
+#pragma unroll
+    for (int i = 0; i < R * 8 / kAsgThreads; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, vo[i], 2 * k0, 0);
 }
 // LDS tile: [row][64 bf16], piece p of row r in slot p ^ (r & 7)
-__device__ __forceinline__ void tile_store(uint16_t *t, const u32x4 v[4])
+template <int R>
+__device__ __forceinline__ void tile_store(uint16_t *t, const u32x4 v[R * 8 / kAsgThreads])
 {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 3) + 32 * i, p = tid & 7;
+    for (int i = 0; i < R * 8 / kAsgThreads; ++i) {
+        const int row = (tid >> 3) + (kAsgThreads / 8) * i, p = tid & 7;
         *reinterpret_cast<u32x4 *>(t + row * kSlice + ((p ^ (row & 7)) << 3)) = v[i];
     }
 }
@@ -140,7 +154,7 @@ __device__ __forceinline__ u32x4 frag(const uint16_t *t, int row, int s)
     return *reinterpret_cast<const u32x4 *>(t + row * kSlice + ((p ^ (row & 7)) << 3));
 }
 
-__global__ __launch_bounds__(256) void kmeans_assign_kernel(int V, int d, const uint16_t *__restrict__ W,
+__global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d, const uint16_t *__restrict__ W,
                                                             int M, const uint16_t *__restrict__ C,
                                                             int RT, int CT,
                                                             unsigned long long *__restrict__ best)
@@ -150,7 +164,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(int V, int d, const 
     const int rt = (b / (8 * CT)) * 8 + (b % 8), ct = (b / 8) % CT;  // a row tile stays on one XCD
     if (rt >= RT)
         return;
-    const int lane = lane_id(), wave = threadIdx.x >> 6, wr = wave >> 1, wc = wave & 1;
+    const int lane = lane_id(), wave = threadIdx.x >> 6, wr = wave >> 1, wc = wave & 1;  // 4 x 2 waves
     const int64_t y0 = (int64_t)rt * kTileR;
     const int c0 = ct * kTileC;
     const int rows = (int)min((int64_t)kTileR, (int64_t)V - y0), cols = min(kTileC, M - c0);
@@ -163,39 +177,59 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(int V, int d, const 
         for (int j = 0; j < 2; ++j)
             acc[i][j] = f32x16{};
     const int nsl = d / kSlice;
-    u32x4 va[4], vb[4];
-    tile_load(ra, d, 0, va);
-    tile_load(rb, d, 0, vb);
-    tile_store(lds[0], va);
-    tile_store(lds[0] + kTileR * kSlice, vb);
-    __syncthreads();
-    for (int s = 0; s < nsl; ++s) {
-        if (s + 1 < nsl) {  // next slice in flight during this one's MFMAs
-            tile_load(ra, d, (s + 1) * kSlice, va);
-            tile_load(rb, d, (s + 1) * kSlice, vb);
-        }
-        const uint16_t *ta = lds[s & 1], *tb = lds[s & 1] + kTileR * kSlice;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            u32x4 a[2], bb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                a[i] = frag(ta, wr * 64 + i * 32 + (lane & 31), st);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bb[j] = frag(tb, wc * 64 + j * 32 + (lane & 31), st);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = mfma(a[i], bb[j], acc[i][j]);
-        }
-        if (s + 1 < nsl) {
-            tile_store(lds[(s + 1) & 1], va);
-            tile_store(lds[(s + 1) & 1] + kTileR * kSlice, vb);
-        }
-        __syncthreads();
+    constexpr int NA = kTileR * 8 / kAsgThreads, NB = kTileC * 8 / kAsgThreads;
+    // register ring of two slices (a loaded memory round trip is longer
+    // than one slice of MFMA work): while slice t is multiplied, slice t+1
+    // moves to LDS and slice t+3 is requested.  Loads past the last slice
+    // re-read it (clamped), so every load is unconditional and the compiler
+    // waits only for the slice it stores.
+    u32x4 a0[NA], b0[NB], a1[NA], b1[NB];
+    uint32_t voa[NA], vob[NB];
+    tile_offsets<kTileR>(d, voa);
+    tile_offsets<kTileC>(d, vob);
+#define KM_LOAD(T, VA, VB)                                      \
+    {                                                           \
+        const int k0_ = min((T), nsl - 1) * kSlice;             \
+        tile_load<kTileR>(ra, voa, k0_, VA);                    \
+        tile_load<kTileC>(rb, vob, k0_, VB);                    \
     }
+    // one step: multiply slice T, move slice T+1 (held in VA/VB) to LDS,
+    // request slice T+3 into VA/VB
+#define KM_STEP(T, VA, VB)                                                          \
+    {                                                                               \
+        const uint16_t *ta_ = lds[(T) & 1], *tb_ = lds[(T) & 1] + kTileR * kSlice;  \
+        _Pragma("unroll") for (int st = 0; st < 4; ++st)                            \
+        {                                                                           \
+            u32x4 fa_[2], fb_[2];                                                   \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i)                           \
+                fa_[i] = frag(ta_, wr * 64 + i * 32 + (lane & 31), st);             \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j)                           \
+                fb_[j] = frag(tb_, wc * 64 + j * 32 + (lane & 31), st);             \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i)                           \
+                _Pragma("unroll") for (int j = 0; j < 2; ++j)                       \
+                    acc[i][j] = mfma(fa_[i], fb_[j], acc[i][j]);                    \
+        }                                                                           \
+        if ((T) + 1 < nsl) {                                                        \
+            tile_store<kTileR>(lds[((T) + 1) & 1], VA);                             \
+            tile_store<kTileC>(lds[((T) + 1) & 1] + kTileR * kSlice, VB);           \
+        }                                                                           \
+        KM_LOAD((T) + 3, VA, VB)                                                    \
+        __syncthreads();                                                            \
+    }
+    KM_LOAD(0, a0, b0)
+    KM_LOAD(1, a1, b1)
+    tile_store<kTileR>(lds[0], a0);
+    tile_store<kTileC>(lds[0] + kTileR * kSlice, b0);
+    KM_LOAD(2, a0, b0)
+    __syncthreads();
+    for (int t = 0; t < nsl; t += 2) {
+        KM_STEP(t, a1, b1)
+        if (t + 1 >= nsl)
+            break;
+        KM_STEP(t + 1, a0, b0)
+    }
+#undef KM_STEP
+#undef KM_LOAD
     // epilogue: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 of
     // the 32 x 32 tile, column l%32
 #pragma unroll
@@ -555,7 +589,7 @@ hipError_t kmeans_assign_launch(hipStream_t s, int V, int d, const void *W, int 
         return e;
     const int RT = (V + kTileR - 1) / kTileR, CT = (M + kTileC - 1) / kTileC;
     const int RTp = (RT + 7) / 8 * 8;  // row tiles padded to whole XCD rounds
-    e = launch_timed(kmeans_assign_kernel, dim3((unsigned)((int64_t)RTp * CT)), dim3(256), s, t0, t1,
+    e = launch_timed(kmeans_assign_kernel, dim3((unsigned)((int64_t)RTp * CT)), dim3(kAsgThreads), s, t0, t1,
                      V, d, reinterpret_cast<const uint16_t *>(W), M,
                      reinterpret_cast<const uint16_t *>(C), RT, CT, best);
     if (e != hipSuccess)
