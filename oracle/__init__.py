@@ -232,3 +232,24 @@ def kmeans_update(W, inv_norm, assign, C_prev):
     lib.oracle_kmeans_update(C.c_int(V), C.c_int(d), _p(W), _p(inv_norm), C.c_int(M), _p(assign),
                              _p(C_prev), _p(C_out), _p(size), _p(norm))
     return C_out, size, norm
+
+
+def verify_tree(parent, token, sl_off, sl_ids, q, p, u_acc, u_fin):
+    """Tree verification (multi-step speculative sampling).  parent, token,
+    u_acc [B][m]; p [B][m][V]; q in the sampler layout.  Returns (n_acc [B],
+    out [B][m], path [B][m], tie [B] bool)."""
+    lib = _load()
+    parent, token = _c(parent, np.int32), _c(token, np.int32)
+    B, m = parent.shape
+    p = _c(p, np.float32)
+    V = p.shape[-1]
+    sl_off, sl_ids, q = _c(sl_off, np.int64), _c(sl_ids, np.int32), _c(q, np.float32)
+    u_acc, u_fin = _c(u_acc, np.float32), _c(u_fin, np.float32)
+    n_acc = np.empty(B, np.int32)
+    out = np.empty((B, m), np.int32)
+    path = np.empty((B, m), np.int32)
+    tie = np.empty(B, np.uint8)
+    lib.oracle_verify_tree(C.c_int(B), C.c_int(m), C.c_int(V), _p(parent), _p(token), _p(sl_off),
+                           _p(sl_ids), _p(q), _p(p), _p(u_acc), _p(u_fin), _p(n_acc), _p(out),
+                           _p(path), _p(tie))
+    return n_acc, out, path, tie.astype(bool)

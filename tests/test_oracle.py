@@ -638,3 +638,86 @@ def test_kmeans_objective_monotone_and_planted_recovery(oracle_lib):
         Cp = Cn
     assert all(b >= a * (1 - 1e-6) for a, b in zip(objs, objs[1:]))
     assert objs[-1] > objs[0]
+
+
+# ----------------------------------------------------------------------------
+# tree verification (multi-step speculative sampling): exact enumeration
+# ----------------------------------------------------------------------------
+class _TreeCase:
+    """Root (node 0) with k leaf children (nodes 1..k) sharing shortlist S."""
+
+    def __init__(self, oracle_lib, V, nS, k, seed):
+        g = np.random.default_rng(seed)
+        self.o, self.V, self.k, self.m = oracle_lib, V, k, k + 1
+        self.S = np.sort(g.choice(V, nS, replace=False)).astype(np.int32)
+        q = g.dirichlet(np.full(nS, 0.7), size=self.m).astype(np.float32)  # q for every node
+        p = g.dirichlet(np.full(V, 0.8), size=self.m) + 1e-3
+        self.p = (p / p.sum(1, keepdims=True)).astype(np.float32)[None]  # [1][m][V]
+        self.q0 = q[0]
+        self.qcat = q.reshape(-1)  # layout m * sl_off[b] + u * len + j
+        self.sl_off = np.array([0, nS], np.int64)
+        self.parent = np.array([[-1] + [0] * k], np.int32)
+
+    def run(self, toks, u_acc, u_fin):
+        token = np.array([[-1] + list(toks)], np.int32)
+        ua = np.array([[0.0] + list(u_acc)], np.float32)
+        n, out, path, _ = self.o.verify_tree(self.parent, token, self.sl_off, self.S, self.qcat,
+                                             self.p, ua, np.array([u_fin], np.float32))
+        return int(n[0]), out[0], path[0]
+
+
+@pytest.mark.parametrize("V,nS,k,seed", [(5, 3, 2, 0), (6, 4, 3, 1), (4, 4, 2, 2), (6, 2, 3, 3)])
+def test_verify_tree_reproduces_target_distribution(oracle_lib, V, nS, k, seed):
+    import itertools
+    c = _TreeCase(oracle_lib, V, nS, k, seed)
+    p0 = c.p[0, 0].astype(np.float64)
+    qd = np.zeros(V)
+    qd[c.S] = c.q0
+    hi = 1.0 - 2.0 ** -24
+    emitted = np.zeros(V)
+    for combo in itertools.product(range(nS), repeat=k):
+        toks = [int(c.S[j]) for j in combo]
+        w = float(np.prod([c.q0[j] for j in combo], dtype=np.float64))
+        reach = 1.0
+        for i in range(k):  # child i tried after children 0..i-1 were rejected
+            def acc(kk, i=i):
+                ua = [hi] * i + [kk * 2.0 ** -24] + [0.0] * (k - i - 1)
+                n, out, path = c.run(toks, ua, 0.5)
+                return n >= 1 and path[0] == i + 1
+            a = _bisect(acc) / TWO24
+            if i == 0:  # against the target itself: min(1, p/q)
+                assert abs(a - min(1.0, p0[toks[0]] / qd[toks[0]])) <= 2.0 ** -23 + 1e-12
+            emitted[toks[i]] += w * reach * a
+            reach *= 1.0 - a
+            if reach <= 0.0:
+                break
+        if reach > 0.0:  # every child rejected: the final draw from the residual
+            prev = 0
+            for y in range(V):
+                cnt = _bisect(lambda kk: c.run(toks, [hi] * k, kk * 2.0 ** -24)[1][0] <= y)
+                emitted[y] += w * reach * (cnt - prev) / TWO24
+                prev = cnt
+    np.testing.assert_allclose(emitted, p0 / p0.sum(), atol=4e-6 * k)
+
+
+def test_verify_tree_bonus_and_childless_root(oracle_lib):
+    c = _TreeCase(oracle_lib, 6, 3, 2, 7)
+    # child 1 accepted (u = 0): the next token is the bonus from p of node 1
+    toks = [int(c.S[0]), int(c.S[1])]
+    prev, dist = 0, np.zeros(6)
+    for y in range(6):
+        cnt = _bisect(lambda kk: c.run(toks, [0.0, 0.0], kk * 2.0 ** -24)[1][1] <= y)
+        dist[y] = (cnt - prev) / TWO24
+        prev = cnt
+    n, out, path = c.run(toks, [0.0, 0.0], 0.3)
+    assert n == 1 and path[0] == 1 and out[0] == toks[0]
+    p1 = c.p[0, 1].astype(np.float64)
+    np.testing.assert_allclose(dist, p1 / p1.sum(), atol=2e-6)
+    # a root without children draws straight from p_root
+    parent = np.array([[-1, -1, -1]], np.int32)  # nodes 1, 2 detached (no parent in [0, i))
+    parent[0, 1:] = 5  # not a child of anything visited
+    n, out, path, tie = oracle_lib.verify_tree(parent, np.array([[-1, 0, 1]], np.int32), c.sl_off,
+                                               c.S, c.qcat, c.p, np.zeros((1, 3), np.float32),
+                                               np.array([0.0], np.float32))
+    assert n[0] == 0 and (path[0] == -1).all()
+    assert out[0, 0] == int(np.flatnonzero(c.p[0, 0] > 0)[0])
