@@ -667,7 +667,7 @@ void oracle_verify_tree(int B, int m, int V, const int32_t *parent, const int32_
             }
             int dt = 0;
             const int64_t pick = inverse_cdf(r, V, (double)u_fin[b], &dt, NULL);
-            if (rejected && dt)
+            if (dt)
                 t = 1;
             ob[n] = (int32_t)pick;
             break;
