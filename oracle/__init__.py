@@ -235,18 +235,21 @@ def kmeans_update(W, inv_norm, assign, C_prev):
 
 
 def verify_tree(parent, token, sl_off, sl_ids, q, p, u_acc, u_fin):
-    """Tree verification (multi-step speculative sampling).  parent, token,
-    u_acc [B][m]; p [B][m][V]; q in the sampler layout.  Returns (n_acc [B],
-    out [B][m], path [B][m], tie [B] bool)."""
+    """Tree verification (multi-step speculative sampling).  Nodes 0..m per
+    sequence, node 0 the root; parent, token, u_acc [B][m] describe drafted
+    nodes 1..m (index i-1 for node i); q in the sampler layout, row i-1 the
+    proposal of node i; p [B][m+1][V].  Returns (n_acc [B], out [B][m+1],
+    path [B][m], tie [B] bool)."""
     lib = _load()
     parent, token = _c(parent, np.int32), _c(token, np.int32)
     B, m = parent.shape
     p = _c(p, np.float32)
     V = p.shape[-1]
+    assert p.shape == (B, m + 1, V)
     sl_off, sl_ids, q = _c(sl_off, np.int64), _c(sl_ids, np.int32), _c(q, np.float32)
     u_acc, u_fin = _c(u_acc, np.float32), _c(u_fin, np.float32)
     n_acc = np.empty(B, np.int32)
-    out = np.empty((B, m), np.int32)
+    out = np.empty((B, m + 1), np.int32)
     path = np.empty((B, m), np.int32)
     tie = np.empty(B, np.uint8)
     lib.oracle_verify_tree(C.c_int(B), C.c_int(m), C.c_int(V), _p(parent), _p(token), _p(sl_off),

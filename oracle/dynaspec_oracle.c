@@ -587,25 +587,29 @@ void oracle_kmeans_update(int V, int d, const uint16_t *W, const float *inv_norm
  * not define how a tree is verified.  This is the multi-step speculative
  * sampling of SpecInfer ("SpecInfer: Accelerating Generative Large Language
  * Model Serving with Tree-based Speculative Inference and Verification", a
- * reference of the DySpec page): starting at the root, the children of the
- * current node u (their tokens drawn from the drafter's q_u) are tried in
- * index order against a running residual r, which starts as the target p_u:
- * child c is accepted iff u_acc[c] * q_u(x_c) < r(x_c) (probability
- * min(1, r/q)); after a rejection r <- max(0, r - q_u) / sum (over all V;
- * back to p_u should that have no mass).  An accepted child becomes the
- * current node; when no child is accepted (or the node has none) one token is
- * drawn from r with u_fin by the inverse CDF and the sequence stops.  The
- * emitted tokens are distributed as the target.
+ * reference of the DySpec page), in its general form where every child
+ * carries the proposal it was drawn from: starting at the root, the children
+ * of the current node u are tried in index order against a running residual
+ * r, which starts as the target p_u.  Child c (token x_c drawn from q_c) is
+ * accepted iff u_acc[c] * q_c(x_c) < r(x_c) (probability min(1, r/q_c));
+ * after a rejection r <- max(0, r - q_c) / sum (over all V; back to p_u
+ * should that have no mass).  An accepted child becomes the current node;
+ * when no child is accepted (or the node has none) one token is drawn from r
+ * with u_fin by the inverse CDF and the sequence stops.  The emitted tokens
+ * are distributed as the target.  A tree that is a path is the chain
+ * verifier above.
  *
- * Per sequence b: m nodes, node 0 the root (its token is not drafted),
- * parent[b][i] in [0, i) for i >= 1; token[b][i] the drafted token of node i;
- * the nodes share shortlist b (sl_off[b] .. sl_off[b+1]); q for node u at
- * m*sl_off[b] + u*len_b + j (the sampler's layout); p [B][m][V].
- * Outputs: n_acc[b] accepted nodes, path[b][0..n_acc) their indices,
- * out[b][0..n_acc] the emitted tokens (accepted tokens, then the final
- * draw), the rest -1.  tie[b] = 1 where a decision after a rejection, or the
- * final draw, lies within 1e-12 (relative) of its threshold: there the
- * order of the residual's sums may decide.
+ * Per sequence b: nodes 0..m, node 0 the root (the last emitted token, not
+ * drafted), nodes 1..m drafted.  Drafted node i is described at index i-1 of
+ * the [B][m] arrays: parent (in [0, i); any other value detaches the node),
+ * token, u_acc, and its proposal q_i = row i-1 of group b in the sampler's
+ * layout (q[m*sl_off[b] + (i-1)*len_b + j] over shortlist b).  p [B][m+1][V]
+ * holds the target at every node (row 0: the root).  Outputs: n_acc[b]
+ * accepted nodes, path[b][0..n_acc) their numbers (1..m), out[b][0..n_acc]
+ * the emitted tokens (accepted tokens, then the final draw), the rest -1.
+ * tie[b] = 1 where a decision after a rejection, or the final draw, lies
+ * within 1e-12 (relative) of its threshold: there the order of the
+ * residual's sums may decide.
  * ---------------------------------------------------------------------------
  */
 void oracle_verify_tree(int B, int m, int V, const int32_t *parent, const int32_t *token,
@@ -618,30 +622,33 @@ void oracle_verify_tree(int B, int m, int V, const int32_t *parent, const int32_
     for (int b = 0; b < B; ++b) {
         const int32_t *par = parent + (int64_t)b * m, *tok = token + (int64_t)b * m;
         const int64_t off = sl_off[b], len = sl_off[b + 1] - sl_off[b];
-        int32_t *ob = out + (int64_t)b * m, *pb = path + (int64_t)b * m;
+        int32_t *ob = out + (int64_t)b * (m + 1), *pb = path + (int64_t)b * m;
+        for (int i = 0; i <= m; ++i)
+            ob[i] = -1;
         for (int i = 0; i < m; ++i)
-            ob[i] = pb[i] = -1;
+            pb[i] = -1;
         int t = 0;
         int u = 0, n = 0;
         for (;;) {
-            const float *pu = p + ((int64_t)b * m + u) * V;
-            for (int64_t y = 0; y < V; ++y) {
-                qd[y] = 0.0;
+            const float *pu = p + ((int64_t)b * (m + 1) + u) * V;
+            for (int64_t y = 0; y < V; ++y)
                 r[y] = (double)pu[y];
-            }
-            const float *qu = q + (int64_t)m * off + (int64_t)u * len;
-            for (int64_t j = 0; j < len; ++j) {
-                int32_t y = sl_ids[off + j];
-                if (y >= 0 && y < V)
-                    qd[y] = (double)qu[j];
-            }
             int accepted = -1, rejected = 0;
-            for (int c = u + 1; c < m; ++c) {
-                if (par[c] != u)
+            for (int c = u + 1; c <= m; ++c) {
+                if (par[c - 1] != u)
                     continue;
-                const int32_t x = tok[c];
+                /* the child's proposal as a dense vector over V */
+                const float *qc = q + (int64_t)m * off + (int64_t)(c - 1) * len;
+                for (int64_t y = 0; y < V; ++y)
+                    qd[y] = 0.0;
+                for (int64_t j = 0; j < len; ++j) {
+                    int32_t y = sl_ids[off + j];
+                    if (y >= 0 && y < V)
+                        qd[y] = (double)qc[j];
+                }
+                const int32_t x = tok[c - 1];
                 const int ok = x >= 0 && x < V;
-                const double lhs = (double)u_acc[(int64_t)b * m + c] * (ok ? qd[x] : 0.0);
+                const double lhs = (double)u_acc[(int64_t)b * m + c - 1] * (ok ? qd[x] : 0.0);
                 const double rx = ok ? r[x] : 0.0;
                 if (rejected && fabs(lhs - rx) <= TIE_REL * (lhs + rx))
                     t = 1;
@@ -659,7 +666,7 @@ void oracle_verify_tree(int B, int m, int V, const int32_t *parent, const int32_
                     r[y] = Z > 0.0 ? r[y] / Z : (double)pu[y];
             }
             if (accepted >= 0) {
-                ob[n] = tok[accepted];
+                ob[n] = tok[accepted - 1];
                 pb[n] = accepted;
                 ++n;
                 u = accepted;

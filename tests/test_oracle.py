@@ -644,40 +644,50 @@ def test_kmeans_objective_monotone_and_planted_recovery(oracle_lib):
 # tree verification (multi-step speculative sampling): exact enumeration
 # ----------------------------------------------------------------------------
 class _TreeCase:
-    """Root (node 0) with k leaf children (nodes 1..k) sharing shortlist S."""
+    """Root (node 0) with k leaf children (nodes 1..k) sharing shortlist S;
+    child i's token is drawn from its own proposal q_i (all equal when
+    same_q: one drafter sampling with replacement)."""
 
-    def __init__(self, oracle_lib, V, nS, k, seed):
+    def __init__(self, oracle_lib, V, nS, k, seed, same_q=False):
         g = np.random.default_rng(seed)
-        self.o, self.V, self.k, self.m = oracle_lib, V, k, k + 1
+        self.o, self.V, self.k, self.m = oracle_lib, V, k, k
         self.S = np.sort(g.choice(V, nS, replace=False)).astype(np.int32)
-        q = g.dirichlet(np.full(nS, 0.7), size=self.m).astype(np.float32)  # q for every node
-        p = g.dirichlet(np.full(V, 0.8), size=self.m) + 1e-3
-        self.p = (p / p.sum(1, keepdims=True)).astype(np.float32)[None]  # [1][m][V]
-        self.q0 = q[0]
-        self.qcat = q.reshape(-1)  # layout m * sl_off[b] + u * len + j
+        q = g.dirichlet(np.full(nS, 0.7), size=k).astype(np.float32)  # proposal of nodes 1..k
+        if same_q:
+            q[:] = q[0]
+        p = g.dirichlet(np.full(V, 0.8), size=k + 1) + 1e-3
+        self.p = (p / p.sum(1, keepdims=True)).astype(np.float32)[None]  # [1][k+1][V]
+        self.qs = q
+        self.qcat = q.reshape(-1)  # layout m * sl_off[b] + (i-1) * len + j
         self.sl_off = np.array([0, nS], np.int64)
-        self.parent = np.array([[-1] + [0] * k], np.int32)
+        self.parent = np.zeros((1, k), np.int32)
 
     def run(self, toks, u_acc, u_fin):
-        token = np.array([[-1] + list(toks)], np.int32)
-        ua = np.array([[0.0] + list(u_acc)], np.float32)
+        token = np.array([list(toks)], np.int32)
+        ua = np.array([list(u_acc)], np.float32)
         n, out, path, _ = self.o.verify_tree(self.parent, token, self.sl_off, self.S, self.qcat,
                                              self.p, ua, np.array([u_fin], np.float32))
         return int(n[0]), out[0], path[0]
 
 
-@pytest.mark.parametrize("V,nS,k,seed", [(5, 3, 2, 0), (6, 4, 3, 1), (4, 4, 2, 2), (6, 2, 3, 3)])
-def test_verify_tree_reproduces_target_distribution(oracle_lib, V, nS, k, seed):
+@pytest.mark.parametrize("V,nS,k,seed,same_q", [(5, 3, 2, 0, False), (6, 4, 3, 1, False),
+                                                (4, 4, 2, 2, True), (6, 2, 3, 3, False),
+                                                (5, 3, 3, 4, True)])
+def test_verify_tree_reproduces_target_distribution(oracle_lib, V, nS, k, seed, same_q):
+    """Exact enumeration: over every combination of child tokens (child i
+    drawn from q_i) and the whole 2^-24 grid of uniforms (by bisection),
+    the first emitted token is distributed as p_root, and the first child is
+    accepted with probability min(1, p/q_1)."""
     import itertools
-    c = _TreeCase(oracle_lib, V, nS, k, seed)
+    c = _TreeCase(oracle_lib, V, nS, k, seed, same_q)
     p0 = c.p[0, 0].astype(np.float64)
-    qd = np.zeros(V)
-    qd[c.S] = c.q0
+    q1 = np.zeros(V)
+    q1[c.S] = c.qs[0]
     hi = 1.0 - 2.0 ** -24
     emitted = np.zeros(V)
     for combo in itertools.product(range(nS), repeat=k):
         toks = [int(c.S[j]) for j in combo]
-        w = float(np.prod([c.q0[j] for j in combo], dtype=np.float64))
+        w = float(np.prod([c.qs[i][j] for i, j in enumerate(combo)], dtype=np.float64))
         reach = 1.0
         for i in range(k):  # child i tried after children 0..i-1 were rejected
             def acc(kk, i=i):
@@ -686,7 +696,7 @@ def test_verify_tree_reproduces_target_distribution(oracle_lib, V, nS, k, seed):
                 return n >= 1 and path[0] == i + 1
             a = _bisect(acc) / TWO24
             if i == 0:  # against the target itself: min(1, p/q)
-                assert abs(a - min(1.0, p0[toks[0]] / qd[toks[0]])) <= 2.0 ** -23 + 1e-12
+                assert abs(a - min(1.0, p0[toks[0]] / q1[toks[0]])) <= 2.0 ** -23 + 1e-12
             emitted[toks[i]] += w * reach * a
             reach *= 1.0 - a
             if reach <= 0.0:
@@ -710,14 +720,48 @@ def test_verify_tree_bonus_and_childless_root(oracle_lib):
         dist[y] = (cnt - prev) / TWO24
         prev = cnt
     n, out, path = c.run(toks, [0.0, 0.0], 0.3)
-    assert n == 1 and path[0] == 1 and out[0] == toks[0]
+    assert n == 1 and path[0] == 1 and out[0] == toks[0] and path[1] == -1 and out[2] == -1
     p1 = c.p[0, 1].astype(np.float64)
     np.testing.assert_allclose(dist, p1 / p1.sum(), atol=2e-6)
     # a root without children draws straight from p_root
-    parent = np.array([[-1, -1, -1]], np.int32)  # nodes 1, 2 detached (no parent in [0, i))
-    parent[0, 1:] = 5  # not a child of anything visited
-    n, out, path, tie = oracle_lib.verify_tree(parent, np.array([[-1, 0, 1]], np.int32), c.sl_off,
-                                               c.S, c.qcat, c.p, np.zeros((1, 3), np.float32),
+    parent = np.array([[5, 5]], np.int32)  # no node has a parent in [0, i): all detached
+    n, out, path, tie = oracle_lib.verify_tree(parent, np.array([[0, 1]], np.int32), c.sl_off,
+                                               c.S, c.qcat, c.p, np.zeros((1, 2), np.float32),
                                                np.array([0.0], np.float32))
-    assert n[0] == 0 and (path[0] == -1).all()
+    assert n[0] == 0 and (path[0] == -1).all() and (out[0, 1:] == -1).all()
     assert out[0, 0] == int(np.flatnonzero(c.p[0, 0] > 0)[0])
+
+
+def test_verify_tree_path_is_the_chain_verifier(oracle_lib):
+    """A tree whose nodes form one path (parent of node i is i-1) is a
+    drafted chain: outputs equal the chain verifier's (pinned above by its
+    own enumeration) on the same proposals, targets and uniforms, wherever
+    neither flags a near-threshold decision."""
+    g = np.random.default_rng(11)
+    B, T, V, nS = 6, 4, 40, 12
+    S = [np.sort(g.choice(V, nS, replace=False)).astype(np.int32) for _ in range(B)]
+    q = g.dirichlet(np.full(nS, 0.5), size=(B, T)).astype(np.float32)
+    p = g.dirichlet(np.full(V, 0.5), size=(B, T + 1)).astype(np.float32)
+    for b in range(B):  # make the drafts likely to be accepted part of the time
+        p[b, :T, S[b]] += 0.5 * q[b].T
+    p /= p.sum(-1, keepdims=True)
+    draft = np.array([[S[b][g.integers(nS)] for b in range(B)] for _ in range(T)], np.int32)
+    u_acc = g.random((T, B), dtype=np.float32)
+    u_fin = g.random(B, dtype=np.float32)
+    # chain layout: row t*B + b owns S[b] and q[b][t]
+    c_off = np.arange(T * B + 1, dtype=np.int64) * nS
+    c_ids = np.concatenate([S[r % B] for r in range(T * B)])
+    c_q = np.concatenate([q[r % B, r // B] for r in range(T * B)])
+    n_c, out_c, tie_c = oracle_lib.verify_reject(draft, c_off, c_ids, c_q, p, u_acc, u_fin)
+    # tree layout: sequence b owns S[b]; node i's proposal is row i-1
+    parent = np.tile(np.arange(T, dtype=np.int32), (B, 1))
+    t_off = np.arange(B + 1, dtype=np.int64) * nS
+    n_t, out_t, path_t, tie_t = oracle_lib.verify_tree(
+        parent, draft.T.copy(), t_off, np.concatenate(S), q.reshape(-1), p, u_acc.T.copy(),
+        u_fin)
+    ok = ~(tie_c | tie_t)
+    assert ok.sum() >= B - 1 and 0 < n_c.sum() < B * T
+    np.testing.assert_array_equal(n_t[ok], n_c[ok])
+    np.testing.assert_array_equal(out_t[ok], out_c[ok])
+    for b in np.flatnonzero(ok):
+        np.testing.assert_array_equal(path_t[b, :n_t[b]], np.arange(1, n_t[b] + 1))
