@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdynaspec.so")
 SOURCES = ["abi.hip", "router.hip", "select.hip", "shortlist.hip", "head.hip", "head_mfma.hip",
-           "pack.hip", "sample.hip", "verify.hip", "kmeans.hip"]
+           "pack.hip", "sample.hip", "verify.hip", "verify_tree.hip",
+           "kmeans.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",

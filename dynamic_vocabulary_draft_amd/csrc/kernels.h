@@ -74,4 +74,12 @@ hipError_t verify_launch(hipStream_t s, int B, int T, int V, const int32_t *draf
                          const float *p, const float *u_acc, const float *u_fin, int32_t *n_acc,
                          int32_t *out, void *ws);
 
+size_t verify_tree_ws_bytes(int B, int m, int V, int64_t max_len);
+hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
+                              const int32_t *token, const int64_t *sl_off, const int32_t *sl_ids,
+                              const float *q, const float *p, const float *u_acc,
+                              const float *u_fin, int64_t max_len, int32_t *n_acc, int32_t *out,
+                              int32_t *path, void *ws, hipEvent_t t0 = nullptr,
+                              hipEvent_t t1 = nullptr);
+
 }  // namespace ds

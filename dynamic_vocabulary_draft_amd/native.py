@@ -75,6 +75,9 @@ _SIGS = {
     "ds_verify_workspace_bytes": (_sz, [_i, _i, _i]),
     "ds_verify_reject": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               _sz]),
+    "ds_verify_tree_workspace_bytes": (_sz, [_i, _i, _i, _i64]),
+    "ds_verify_tree": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
+                            _vp, _vp, _vp, _sz]),
     "ds_draft_chain_workspace_bytes": (_sz, [_i, _i, _i, _i, _i64]),
     "ds_draft_chain": (_i, [_vp, _vp, C.POINTER(ChainArgs)]),
     "ds_capture_begin": (_i, [_vp]),
@@ -296,6 +299,22 @@ def verify_reject(draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out, ws, *, 
     _check("ds_verify_reject", lib.ds_verify_reject(
         _s(stream), B, T, V, _p(draft), _p(sl_off), _p(sl_ids), _p(q), _p(p), _p(u_acc),
         _p(u_fin), _p(n_acc), _p(out), _p(ws), _nbytes(ws)))
+
+
+def verify_tree_workspace_bytes(B: int, m: int, V: int, max_len: int) -> int:
+    return int(lib.ds_verify_tree_workspace_bytes(B, m, V, max_len))
+
+
+def verify_tree(parent, token, sl_off, sl_ids, q, p, u_acc, u_fin, max_len, n_acc, out, path,
+                ws, *, stream=None):
+    """parent, token, u_acc [B][m] (drafted nodes 1..m); p [B][m+1][V];
+    outputs n_acc [B], out [B][m+1], path [B][m]."""
+    B, m = parent.shape
+    V = p.shape[-1]
+    _check("ds_verify_tree", lib.ds_verify_tree(
+        _s(stream), B, m, V, _p(parent), _p(token), _p(sl_off), _p(sl_ids), _p(q), _p(p),
+        _p(u_acc), _p(u_fin), int(max_len), _p(n_acc), _p(out), _p(path), _p(ws),
+        _nbytes(ws)))
 
 
 def draft_chain(args: ChainArgs, head_stream=None, router_stream=None):

@@ -73,6 +73,7 @@ typedef enum { DS_BUDGET_CLUSTERS = 0, DS_BUDGET_TOKENS = 1 } ds_budget_kind;
 #define DS_MAX_CLUSTERS 4096    /* M: clusters are ranked in LDS            */
 #define DS_MAX_GROUPS 65535     /* G (and n for selection/build)            */
 #define DS_MAX_HEAD_ROWS 256    /* m: head rows sharing one shortlist       */
+#define DS_MAX_TREE_NODES 1024  /* m: drafted nodes of one verified tree    */
 
 const char *ds_status_string(ds_status s);
 const char *ds_version(void);
@@ -301,6 +302,50 @@ ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *dr
                            const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                            const float *p, const float *u_acc, const float *u_fin,
                            int32_t *n_acc, int32_t *out, void *ws, size_t ws_bytes);
+
+/*
+ * Tree verification by multi-step speculative sampling, which keeps the
+ * emitted tokens distributed exactly as the target (SpecInfer, "Accelerating
+ * Generative Large Language Model Serving with Tree-based Speculative
+ * Inference and Verification", a reference of the DySpec page; the pages
+ * draft trees [tree-shaped workload] and verify over the full vocabulary
+ * [A], so the tree is verified by the published tree form of the
+ * rejection rule).  Per sequence b the tree has nodes 0..m: node 0 the root
+ * (the last emitted token), nodes 1..m drafted, drafted node i described at
+ * index i-1 of the [B][m] arrays:
+ *   parent  its parent in [0, i) (any other value detaches the node);
+ *   token   its token, drawn from its own proposal q_i;
+ *   u_acc   its acceptance uniform in [0, 1);
+ *   q_i     row i-1 of group b in the sampler's layout:
+ *           q[m*sl_off[b] + (i-1)*len_b + j] over shortlist b
+ *           (sl_ids[sl_off[b] .. sl_off[b+1]), ascending distinct ids;
+ *           the sampler's output with G = B and m rows per group).
+ * p [B][m+1][V] fp32 target probabilities at every node (row 0: the root).
+ * From u = 0, the children c of u (parent == u) are tried in increasing
+ * order against a residual r that starts as p_u: accept iff
+ * u_acc * q_c(x_c) < r(x_c); after a rejection r <- max(0, r - q_c) / sum
+ * over all V (back to p_u if that has no mass).  An accepted child becomes
+ * u; when no child is accepted, one token is drawn from r with u_fin[b] by
+ * the inverse CDF and the sequence stops.  The first test at a node is
+ * exact (fp32 values compared in fp64); later tests and the draw use fp64
+ * sums whose order differs from a sequential sum by rounding only.
+ * Outputs: n_acc [B] accepted nodes (-1: the sequence's shortlist is longer
+ * than max_len or has a negative length, its other outputs -1);
+ * path [B][m] the accepted node numbers, then -1; out [B][m+1] the accepted
+ * tokens, the final draw, then -1.
+ * max_len  host-side bound on every sequence's shortlist length.
+ * Limits: 1 <= m <= DS_MAX_TREE_NODES, V <= 2^20, B <= DS_MAX_GROUPS,
+ * max_len <= 2^24.  Unsorted or repeated shortlist ids give unspecified
+ * results (memory accesses stay in bounds).  Two kernels on stream s.
+ * ws >= ds_verify_tree_workspace_bytes(B, m, V, max_len) bytes; no
+ * initialisation needed.
+ */
+size_t ds_verify_tree_workspace_bytes(int B, int m, int V, int64_t max_len);
+ds_status ds_verify_tree(hipStream_t s, int B, int m, int V, const int32_t *parent,
+                         const int32_t *token, const int64_t *sl_off, const int32_t *sl_ids,
+                         const float *q, const float *p, const float *u_acc, const float *u_fin,
+                         int64_t max_len, int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
+                         size_t ws_bytes);
 
 /*
  * One chain-drafting step over T positions for B sequences, with the router

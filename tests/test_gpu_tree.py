@@ -1,0 +1,204 @@
+"""GPU parity of tree verification (ds_verify_tree) against the oracle.
+
+Bars: accepted node paths, emitted tokens and counts bit-exact for every
+sequence the oracle does not flag (a decision after a rejection, or the
+final draw, within 1e-12 of its threshold); flagged sequences must still
+emit a valid walk (each accepted node a child of the previous one, its token
+the node's token).  Sizes span ragged 1024-token chunks (V not a multiple of
+1024), empty and single-entry shortlists, chains, stars, random and binary
+trees, and the Qwen3-8B-shaped tree (V = 151936, 64 nodes, 24K shortlist).
+"""
+import numpy as np
+import pytest
+import torch
+
+from dynamic_vocabulary_draft_amd.pipeline import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def N():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from dynamic_vocabulary_draft_amd import native
+    return native
+
+
+def _parents(topo, B, m, g):
+    i = np.arange(1, m + 1)
+    if topo == "chain":
+        par = i - 1
+    elif topo == "star":
+        par = np.zeros(m, np.int64)
+    elif topo == "binary":
+        par = (i - 1) // 2
+    else:
+        return np.stack([[g.integers(0, k) for k in i] for _ in range(B)]).astype(np.int32)
+    return np.tile(par.astype(np.int32), (B, 1))
+
+
+def _softmax64(x):
+    x = np.asarray(x, np.float64)
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def _tree_case(V, m, B, seed, lens, topo="random", mode="random"):
+    """Shortlists of the given lengths, each node's proposal a softmax over
+    its sequence's shortlist, its token drawn from that proposal, targets
+    per mode (independent N(0, 3) softmax, or mixed with the children's
+    proposals, or mostly the first child's, so that walks go deep)."""
+    g = np.random.default_rng(seed)
+    S = [np.sort(g.choice(V, L, replace=False)).astype(np.int32) for L in lens]
+    sl_off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    parent = _parents(topo, B, m, g)
+    q = np.zeros(int(sl_off[-1]) * m, np.float32)
+    qd = np.zeros((B, m, V))
+    token = np.empty((B, m), np.int32)
+    for b in range(B):
+        L = lens[b]
+        for i in range(m):
+            if L == 0:
+                token[b, i] = g.integers(0, V)  # nothing proposed on the shortlist
+                continue
+            qi = _softmax64(g.standard_normal(L) * 2).astype(np.float32)
+            base = m * sl_off[b] + i * L
+            q[base:base + L] = qi
+            qd[b, i, S[b]] = qi
+            token[b, i] = S[b][min(np.searchsorted(np.cumsum(qi, dtype=np.float64), g.random(),
+                                                   side="right"), L - 1)]
+    p = np.empty((B, m + 1, V), np.float32)
+    for b in range(B):
+        for u in range(m + 1):
+            t = _softmax64(g.standard_normal(V) * 3)
+            kids = np.flatnonzero(parent[b] == u)
+            if mode == "correlated" and kids.size:
+                t = 0.3 * t + 0.7 * qd[b, kids].mean(0)
+            elif mode == "first" and kids.size:  # the first child is accepted most of the time
+                t = 0.1 * t + 0.9 * qd[b, kids[0]]
+            p[b, u] = t.astype(np.float32)
+    u_acc = g.random((B, m), dtype=np.float32)
+    u_fin = g.random(B, dtype=np.float32)
+    return dict(parent=parent, token=token, sl_off=sl_off, sl_ids=np.concatenate(S + [[]]).astype(
+        np.int32), q=q, p=p, u_acc=u_acc, u_fin=u_fin)
+
+
+def _run(N, c, max_len=None):
+    B, m = c["parent"].shape
+    V = c["p"].shape[-1]
+    lens = np.diff(c["sl_off"])
+    max_len = int(max(1, lens.max())) if max_len is None else max_len
+    dv = {k: to_dev(np.asarray(v)) for k, v in c.items()}
+    if dv["sl_ids"].numel() == 0:
+        dv["sl_ids"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if dv["q"].numel() == 0:
+        dv["q"] = torch.zeros(1, dtype=torch.float32, device="cuda")
+    n_acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((B, m + 1), -7, dtype=torch.int32, device="cuda")
+    path = torch.full((B, m), -7, dtype=torch.int32, device="cuda")
+    ws = N.workspace(N.verify_tree_workspace_bytes(B, m, V, max_len))
+    ws.fill_(0x5A)  # no initialisation is needed
+    N.verify_tree(dv["parent"], dv["token"], dv["sl_off"], dv["sl_ids"], dv["q"], dv["p"],
+                  dv["u_acc"], dv["u_fin"], max_len, n_acc, out, path, ws)
+    torch.cuda.synchronize()
+    return n_acc.cpu().numpy(), out.cpu().numpy(), path.cpu().numpy()
+
+
+def _check(oracle_lib, c, got, min_clean=1):
+    n, out, path = got
+    n_ref, out_ref, path_ref, tie = oracle_lib.verify_tree(**c)
+    ok = ~tie
+    assert ok.sum() >= min_clean, "too many flagged sequences: %d" % tie.sum()
+    np.testing.assert_array_equal(n[ok], n_ref[ok])
+    np.testing.assert_array_equal(out[ok], out_ref[ok])
+    np.testing.assert_array_equal(path[ok], path_ref[ok])
+    # every sequence: a valid walk from the root, -1 padding
+    B, m = path.shape
+    for b in range(B):
+        k = int(n[b])
+        assert 0 <= k <= m
+        prev = 0
+        for j in range(k):
+            node = int(path[b, j])
+            assert 1 <= node <= m and c["parent"][b, node - 1] == prev
+            assert out[b, j] == c["token"][b, node - 1]
+            prev = node
+        assert (path[b, k:] == -1).all() and (out[b, k + 1:] == -1).all()
+        assert 0 <= out[b, k] < c["p"].shape[-1]
+    return n_ref
+
+
+@pytest.mark.parametrize("topo", ["random", "binary", "chain", "star"])
+@pytest.mark.parametrize("mode", ["random", "correlated"])
+def test_verify_tree_parity(N, oracle_lib, topo, mode):
+    V, m, B = 5000, 24, 6
+    lens = [700, 1, 0, 2500, 4999, 1200]  # empty, single-entry and near-full shortlists
+    seed = 10 * ["random", "binary", "chain", "star"].index(topo) + (mode == "correlated")
+    c = _tree_case(V, m, B, seed=seed, lens=lens, topo=topo, mode=mode)
+    n_ref = _check(oracle_lib, c, _run(N, c), min_clean=B - 1)
+    if mode == "correlated" and topo != "star":
+        assert n_ref.max() >= 2  # walks go past the first level
+
+
+@pytest.mark.parametrize("u", [0.0, 1.0 - 2.0 ** -24])
+def test_verify_tree_accept_and_reject_all(N, oracle_lib, u):
+    V, m, B = 3001, 15, 4
+    c = _tree_case(V, m, B, seed=5, lens=[900, 3000, 17, 450], topo="binary")
+    c["u_acc"][:] = np.float32(u)
+    n_ref = _check(oracle_lib, c, _run(N, c), min_clean=B - 1)
+    if u == 0.0:  # the first child of every node is taken down to a leaf (1, 3, 7, 15)
+        assert (n_ref == 4).all()
+    else:
+        assert (n_ref == 0).all()
+
+
+def test_verify_tree_invalid_and_off_shortlist_tokens(N, oracle_lib):
+    V, m, B = 2100, 10, 3
+    c = _tree_case(V, m, B, seed=8, lens=[300, 1000, 64], topo="random", mode="correlated")
+    c["token"][0, ::3] = -5
+    c["token"][1, 1::2] = V + 3
+    S1 = c["sl_ids"][300:1300]
+    off = np.setdiff1d(np.arange(V), S1)
+    c["token"][1, ::2] = off[:5]  # valid tokens with no proposal mass: accepted where p > 0
+    c["parent"][2, 4:] = 99  # detached nodes
+    _check(oracle_lib, c, _run(N, c), min_clean=B)
+
+
+def test_verify_tree_zero_mass_residual_falls_back_to_target(N, oracle_lib):
+    """Proposal >= target everywhere (the target is the proposal with the
+    drafted token's mass removed): the residual after the rejection has no
+    mass and the next tests and the draw use p_u itself."""
+    V, m, B = 700, 3, 2
+    c = _tree_case(V, m, B, seed=3, lens=[V, V], topo="star")
+    for b in range(B):
+        q0 = c["q"][m * V * b: m * V * b + V]
+        c["q"][m * V * b + V: m * V * b + 3 * V] = np.tile(q0, 2)  # all three share q_1
+        c["token"][b, :] = c["token"][b, 0]
+        for u in range(m + 1):
+            c["p"][b, u] = q0
+        c["p"][b, 0, c["token"][b, 0]] = 0.0
+    n_ref = _check(oracle_lib, c, _run(N, c), min_clean=B)
+    assert (n_ref == 0).all()
+
+
+def test_verify_tree_long_shortlist_is_reported(N, oracle_lib):
+    V, m, B = 1500, 6, 3
+    c = _tree_case(V, m, B, seed=4, lens=[100, 400, 50], topo="binary")
+    n, out, path = _run(N, c, max_len=200)
+    assert n[1] == -1 and (out[1] == -1).all() and (path[1] == -1).all()
+    n_ref, out_ref, path_ref, tie = oracle_lib.verify_tree(**c)
+    for b in (0, 2):
+        if not tie[b]:
+            assert n[b] == n_ref[b] and (out[b] == out_ref[b]).all()
+
+
+def test_verify_tree_qwen3_shape(N, oracle_lib):
+    """64 nodes as a binary tree over V = 151936 with one 24K shortlist per
+    sequence (the tree-drafting shape); targets that accept deep, mixed and
+    independent."""
+    V, m = 151936, 64
+    for mode, seed in (("first", 21), ("correlated", 23), ("random", 22)):
+        c = _tree_case(V, m, 3, seed=seed, lens=[24576, 24000, 25000], topo="binary", mode=mode)
+        n_ref = _check(oracle_lib, c, _run(N, c), min_clean=2)
+        if mode == "first":
+            assert n_ref.max() >= 3
