@@ -127,14 +127,16 @@ def cpu_baseline(wl, seconds: float, static_ids=None) -> dict:
                     break
     except OSError:
         pass
-    return {"value": cfg.B * cfg.T * n / el, "unit": "draft tokens/s", "cores": 1,
+    per_step = cfg.B * (cfg.tree_nodes if cfg.is_tree else cfg.T)
+    what = ("router, selection, shortlist, fp64 gathered head over all %d tree nodes, sampling, "
+            "target softmax and tree verification" % cfg.tree_nodes if cfg.is_tree else
+            "%s for all %d positions, target softmax and verification"
+            % ("router, selection, shortlist, fp64 gathered head, sampling"
+               if static_ids is None else "fp64 head over the static shortlist, sampling", cfg.T))
+    return {"value": per_step * n / el, "unit": "draft tokens/s", "cores": 1,
             "kind": "oracle",
-            "sample": "%d full step(s) of instance 0 (%s for all %d positions, target "
-                      "softmax and verification), %.1f s on 1 thread of %d (%s)"
-                      % (n, "router, selection, shortlist, fp64 gathered head, sampling"
-                         if static_ids is None else
-                         "fp64 head over the static shortlist, sampling",
-                         cfg.T, el, os.cpu_count() or 0, model or platform.machine())}
+            "sample": "%d full step(s) of instance 0 (%s), %.1f s on 1 thread of %d (%s)"
+                      % (n, what, el, os.cpu_count() or 0, model or platform.machine())}
 
 
 COPY_BYTES = 1 << 30
@@ -544,7 +546,12 @@ def main():
                    "V": cfg.V, "d": cfg.d, "clusters": cfg.M,
                    "batch": cfg.B, "depth": cfg.T, "tree_nodes": cfg.tree_nodes,
                    "budget": list(cfg.budget), "router": "%d->%d->%d" % (cfg.d, cfg.r, cfg.M),
-                   "step": ("router+select+build+gathered head+sample per position, "
+                   "step": ("router+select+build for the %d roots, gathered head over the "
+                            "%d nodes of each tree + sample per node, target softmax over "
+                            "the %d nodes + tree verify" % (cfg.B, cfg.tree_nodes,
+                                                            cfg.tree_nodes + 1))
+                           if cfg.is_tree else
+                           ("router+select+build+gathered head+sample per position, "
                             "target softmax + verify") if static_ids is None else
                            ("static baseline: %s head over one fixed %d-token frequency-ranked "
                             "shortlist + sample per position, target softmax + verify"

@@ -9,26 +9,34 @@
 // accepted child becomes the current node; otherwise one token is drawn
 // from r and the sequence stops.
 //
-// The walk is sequential per sequence, so one 1024-thread workgroup owns a
-// sequence.  The residual is kept unnormalised: r = R / P with R = p_u off
-// the shortlist (a proposal has no mass there, so those entries only
-// rescale) and R_S in a workspace on the shortlist, P the current
-// normaliser.  A rejection updates R_S <- max(0, R_S - P q_c) and P <-
-// (off-shortlist mass of p_u) + sum R_S, so the long V-wide row is read
-// once per node that sees a rejection (for its off-shortlist mass, per
-// 1024-token chunk) and never rescaled.  The first test at a node compares
-// fp32 values exactly in fp64 (u * q < p); every later test and the final
-// draw differ from a sequential fp64 evaluation by rounding order only.
+// The walk is sequential per sequence, so one 512-thread workgroup owns a
+// sequence, and every phase is a flat stream that keeps many loads in
+// flight from that one compute unit.  The residual is kept unnormalised:
+// r = R / P with R = p_u off the shortlist (a proposal has no mass there, so
+// those entries only rescale) and R_S in a workspace on the shortlist, P the
+// current normaliser.  A rejection updates R_S <- max(0, R_S - P q_c) and
+// P <- (off-shortlist mass of p_u) + sum R_S, so the long V-wide row is read
+// once per node that sees a rejection or ends the walk, never rescaled.
+// The first test at a node compares fp32 values exactly in fp64
+// (u * q < p); every later test and the final draw differ from a sequential
+// fp64 evaluation by rounding order only.
 //
 // Two launches:
 //   bits: one workgroup per (32768 tokens, sequence) writes the shortlist's
-//         membership bitmap (bit y set iff token y is in the shortlist), so
-//         the position of a token in the ascending shortlist is the chunk's
-//         first shortlist index plus a popcount;
-//   walk: one workgroup per sequence: chunk ranges of the shortlist, every
-//         drafted node's shortlist position, u * q and target value at its
-//         parent (in LDS, all tests at a node's first child need nothing
-//         else), then the walk and the final inverse-CDF draw over V.
+//         membership bitmap (bit y set iff token y is listed) and, per
+//         32-token word, the number of listed tokens before it, so the
+//         position of a listed token in the ascending shortlist is
+//         rank[word] + a popcount;
+//   walk: one workgroup per sequence: every drafted node's shortlist
+//         position, u * q and target value at its parent go to LDS (a
+//         node's first test then needs no memory access), then the walk.
+//         The vocabulary is cut into eight slices, one per wave: at a
+//         node's first rejection one pass over p_u totals each slice's mass
+//         off and on the shortlist; each rejection streams R_S, q_c (and,
+//         the first time, p_u at the listed ids); the final draw adds R_S
+//         over each slice's listed range, picks the slice holding the
+//         threshold, scans one segment of that slice per thread and walks
+//         the one segment that holds it.
 #include <limits.h>
 
 #include "common.h"
@@ -38,168 +46,204 @@
 namespace ds {
 namespace {
 
-constexpr int kTreeThreads = 1024;
+constexpr int kTreeThreads = 512;
 constexpr int kTreeWaves = kTreeThreads / kWave;
 constexpr int kTreeMaxNodes = DS_MAX_TREE_NODES;
-constexpr int kTreeMaxChunks = (1 << 20) / kChunk;  // V <= 2^20
-constexpr int kBitsTokens = 32768;                  // tokens per bitmap workgroup
-constexpr int kWordsPerChunk = kChunk / 32;
+constexpr int kBitsTokens = 32768;  // tokens per bitmap workgroup
+constexpr int kBitsThreads = 256;
 
-__host__ __device__ inline int tree_chunks(int V) { return (V + kChunk - 1) / kChunk; }
+// bitmap words per sequence: whole bitmap workgroups
+__host__ __device__ inline int64_t tree_words(int V)
+{
+    return ((int64_t)V + kBitsTokens - 1) / kBitsTokens * (kBitsTokens / 32);
+}
 
 __host__ __device__ inline size_t tree_R_bytes(int B, int64_t max_len)
 {
     return ((size_t)B * (size_t)max_len * 8 + 255) / 256 * 256;
 }
 
-__global__ __launch_bounds__(256) void tree_bits_kernel(int V, int64_t max_len,
-                                                         const int64_t *__restrict__ sl_off,
-                                                         const int32_t *__restrict__ sl_ids,
-                                                         uint32_t *__restrict__ bits)
+__host__ __device__ inline size_t tree_bits_bytes(int B, int V)
+{
+    return ((size_t)B * (size_t)tree_words(V) * 4 + 255) / 256 * 256;
+}
+
+__global__ __launch_bounds__(kBitsThreads) void tree_bits_kernel(
+    int V, int64_t max_len, const int64_t *__restrict__ sl_off, const int32_t *__restrict__ sl_ids,
+    uint32_t *__restrict__ bits, uint32_t *__restrict__ rank)
 {
     __shared__ uint32_t sw[kBitsTokens / 32];
     __shared__ int64_t s_rng[2];
-    const int b = blockIdx.y;
-    const int64_t nwords = (int64_t)tree_chunks(V) * kWordsPerChunk;
+    __shared__ int64_t s_scan[kWave + 1];
+    const int b = blockIdx.y, tid = threadIdx.x;
+    const int64_t nw = tree_words(V);
     const int64_t t0 = (int64_t)blockIdx.x * kBitsTokens;  // < V by the grid
     const int64_t t1 = min(t0 + kBitsTokens, (int64_t)V);
     const int64_t off = sl_off[b];
     int64_t len = sl_off[b + 1] - off;
     if (len < 0 || len > max_len)
         len = 0;  // the walk reports such a sequence
-    for (int i = threadIdx.x; i < kBitsTokens / 32; i += blockDim.x)
+    const int32_t *S = sl_ids + off;
+    for (int i = tid; i < kBitsTokens / 32; i += kBitsThreads)
         sw[i] = 0u;
-    if (threadIdx.x < kWave) {
-        const int64_t a = wave_lower_bound(sl_ids + off, len, (int32_t)t0);
-        const int64_t e = wave_lower_bound(sl_ids + off, len, (int32_t)t1);
-        if (lane_id() == 0) {
-            s_rng[0] = a;
-            s_rng[1] = e;
-        }
+    if (tid < 2 * kWave) {  // wave 0: first entry >= t0, wave 1: first entry >= t1
+        const int64_t r = wave_lower_bound(S, len, (int32_t)(tid < kWave ? t0 : t1));
+        if (lane_id() == 0)
+            s_rng[tid >> 6] = r;
     }
     __syncthreads();
-    for (int64_t j = s_rng[0] + threadIdx.x; j < s_rng[1]; j += blockDim.x) {
-        const int32_t y = sl_ids[off + j];
-        if (y >= t0 && y < t1)
-            atomicOr(&sw[(y - t0) >> 5], 1u << (y & 31));
-    }
-    __syncthreads();
-    uint32_t *ob = bits + (int64_t)b * nwords + t0 / 32;
-    for (int i = threadIdx.x; i < kBitsTokens / 32 && t0 / 32 + i < nwords; i += blockDim.x)
-        ob[i] = sw[i];
-}
-
-__device__ __forceinline__ int wave_sum_int(int v)
-{
+    const int64_t a = s_rng[0], e = s_rng[1];
+    constexpr int U = 8;
+    for (int64_t j0 = a + tid; j0 < e; j0 += (int64_t)kBitsThreads * U) {
+        int32_t y[U];
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1)
-        v += __shfl_xor(v, o);
-    return v;
+        for (int k = 0; k < U; ++k) {
+            const int64_t j = j0 + (int64_t)k * kBitsThreads;
+            y[k] = j < e ? S[j] : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (y[k] >= t0 && y[k] < t1)
+                atomicOr(&sw[(y[k] - t0) >> 5], 1u << (y[k] & 31));
+    }
+    __syncthreads();
+    // thread t owns words 4t .. 4t+3 of the block
+    uint32_t w[4];
+    int64_t cnt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        w[k] = sw[4 * tid + k];
+        cnt += __popc(w[k]);
+    }
+    int64_t tot;
+    int64_t run = a + block_excl_scan_i64(cnt, s_scan, &tot);
+    uint32_t *ob = bits + (int64_t)b * nw, *orank = rank + (int64_t)b * nw;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t gw = t0 / 32 + 4 * tid + k;
+        if (gw < nw) {
+            ob[gw] = w[k];
+            orank[gw] = (uint32_t)run;
+        }
+        run += __popc(w[k]);
+    }
 }
 
-// Block sum with a fixed association (lane 0's wave sum, then the wave sums
-// in order); every thread gets the same value.
-__device__ double block_sum_f64(double v, double *sh)
+// Every thread gets the block sum of one double per thread, in a fixed
+// association (lane 0's wave butterfly, then the wave sums in order).
+__device__ __forceinline__ double block_sum_f64(double v, double *sh)
 {
     const double w = wave_sum_f64(v);
     if (lane_id() == 0)
         sh[threadIdx.x >> 6] = w;
     __syncthreads();
     double t = 0.0;
+#pragma unroll
     for (int k = 0; k < kTreeWaves; ++k)
         t += sh[k];
     __syncthreads();
     return t;
 }
 
-// Position of token x in the ascending shortlist (-1 if absent), from the
-// chunk's first shortlist index cb and the bitmap words of x's chunk; called
-// by a whole wave.
-__device__ __forceinline__ int shortlist_pos(const uint32_t *__restrict__ bits_b, const int *cb,
-                                             int V, int32_t x)
+// four consecutive target values from y0 (y0 % 4 == 0); zero at or beyond
+// lim (<= V).  The loads are unconditional (clamped addresses), so no
+// branch separates them from the loads issued around them.
+__device__ __forceinline__ void load4(const float *__restrict__ pu, int64_t y0, int64_t lim, int V,
+                                      bool vec, float v[4])
 {
-    if (x < 0 || x >= V)
-        return -1;
-    const int lane = lane_id();
-    const int ch = x >> 10, o = x & (kChunk - 1), wi = o >> 5;
-    const uint32_t mw = lane < kWordsPerChunk ? bits_b[(int64_t)ch * kWordsPerChunk + lane] : 0u;
-    const uint32_t below = lane < wi ? mw : (lane == wi ? mw & ((1u << (o & 31)) - 1u) : 0u);
-    const int cnt = wave_sum_int(__popc(below));
-    const uint32_t word = __shfl(mw, wi);
-    return ((word >> (o & 31)) & 1u) ? cb[ch] + cnt : -1;
+    if (vec) {  // V % 4 == 0 and pu 16-byte aligned: one dwordx4 load
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 t = reinterpret_cast<const f32x4 *>(pu)[min(y0, (int64_t)V - 4) >> 2];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = y0 + e < lim ? t[e] : 0.f;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float t = pu[min(y0 + e, (int64_t)V - 1)];
+            v[e] = y0 + e < lim ? t : 0.0f;
+        }
+    }
 }
 
-// Target mass of row pu off the shortlist, per 1024-token chunk into s_off;
-// returns the row's total (chunk order).  Wave w takes chunks w, w+16, ...,
-// two at a time; lane l its tokens 64k + l of the chunk (coalesced loads).
-__device__ double off_sums(const float *__restrict__ pu, const uint32_t *__restrict__ bits_b,
-                           int V, int nch, double *s_off, double *sh)
+// The vocabulary is split into kTreeWaves slices of SC tokens (SC a multiple
+// of 32), slice w = [w SC, (w+1) SC) clipped to V.
+struct Slices {
+    int64_t SC;
+    __device__ int64_t lo(int w, int V) const { return min((int64_t)w * SC, (int64_t)V); }
+    __device__ int64_t hi(int w, int V) const { return min((int64_t)(w + 1) * SC, (int64_t)V); }
+};
+
+// Listed tokens below token a (a a multiple of 32, or V).
+__device__ __forceinline__ int rank_at(const uint32_t *__restrict__ rank_b, int64_t a, int V,
+                                       int rank_end)
+{
+    return a >= V ? rank_end : (int)rank_b[a >> 5];
+}
+
+// One pass over row pu: wave w streams its slice (lane l the tokens
+// lo + 4(l + 64 i) .. +3, eight float4 loads in flight per lane) and totals
+// into s_wsum[w] the target mass off the shortlist (OFF) or all of it.
+// Branch-free fp64 accumulation: on one compute unit the conversions and
+// adds cost as much as the loads.
+template <bool OFF>
+__device__ __forceinline__ void slice_pass(const float *__restrict__ pu,
+                                           const uint32_t *__restrict__ bits_b, int V, Slices sl,
+                                           bool vec, double *s_wsum)
 {
     const int lane = lane_id(), wave = threadIdx.x >> 6;
-    for (int c0 = wave; c0 < nch; c0 += 2 * kTreeWaves) {
-        float pv[2][16];
-        uint32_t mw[2];
+    const int64_t a = sl.lo(wave, V), e = sl.hi(wave, V);
+    constexpr int U = 8;
+    double acc = 0.0;
+    for (int64_t y00 = a + 4 * lane; y00 < e; y00 += 4 * kWave * U) {
+        float v[U][4];
+        uint32_t wd[U];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int c = c0 + h * kTreeWaves;
-            const int64_t base = (int64_t)c * kChunk;
-            mw[h] = (c < nch && lane < kWordsPerChunk) ? bits_b[(int64_t)c * kWordsPerChunk + lane]
-                                                       : 0u;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int64_t y = base + k * kWave + lane;
-                pv[h][k] = (c < nch && y < V) ? pu[y] : 0.0f;
-            }
+        for (int k = 0; k < U; ++k) {
+            const int64_t y0 = y00 + 4 * kWave * k;
+            load4(pu, y0, e, V, vec, v[k]);
+            if (OFF)
+                wd[k] = bits_b[min(y0, (int64_t)V - 1) >> 5];
         }
+        const int sh0 = (lane & 7) << 2;  // y0 & 31 (slices start at multiples of 32)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            double acc = 0.0;
+        for (int k = 0; k < U; ++k)
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t w = __shfl(mw[h], 2 * k + (lane >> 5));
-                if (!((w >> (lane & 31)) & 1u))
-                    acc += (double)pv[h][k];
+            for (int c = 0; c < 4; ++c) {
+                const double x = (double)v[k][c];
+                acc += (OFF && ((wd[k] >> (sh0 + c)) & 1u)) ? 0.0 : x;
             }
-            acc = wave_sum_f64(acc);
-            const int c = c0 + h * kTreeWaves;
-            if (lane == 0 && c < nch)
-                s_off[c] = acc;
-        }
     }
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-        double carry = 0.0;
-        for (int c0 = 0; c0 < nch; c0 += kWave)
-            carry += wave_sum_f64(c0 + lane < nch ? s_off[c0 + lane] : 0.0);
-        if (lane == 0)
-            sh[kWave] = carry;
-    }
-    __syncthreads();
-    const double t = sh[kWave];
-    __syncthreads();
-    return t;
+    acc = wave_sum_f64(acc);
+    if (lane == 0)
+        s_wsum[wave] = acc;
 }
 
-// R <- max(0, R - P q_c) on the shortlist (R read as p_u at the shortlist
-// ids when fresh); returns sum R.
-__device__ double residual_update(const float *__restrict__ pu, const int32_t *__restrict__ S,
-                                  const float *__restrict__ qc, int len, int V, bool fresh,
-                                  double P, double *__restrict__ R, double *sh)
+// R <- max(0, R - P q_c) over the shortlist (R read as p_u at the listed
+// ids when fresh; ids outside [0, V) carry no mass); returns sum R.
+__device__ __forceinline__ double residual_update(const float *__restrict__ pu,
+                                                  const int32_t *__restrict__ S,
+                                                  const float *__restrict__ qc, int len, int V,
+                                                  bool fresh, double P, double *__restrict__ R,
+                                                  double *sh)
 {
-    constexpr int U = 4;
+    constexpr int U = 16;
     double acc = 0.0;
     for (int j0 = threadIdx.x; j0 < len; j0 += kTreeThreads * U) {
         double r[U];
         float qv[U];
+        // unconditional loads at clamped indices (j0 < len), masked after
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int j = j0 + k * kTreeThreads;
-            qv[k] = j < len ? qc[j] : 0.0f;
+            const int j = min(j0 + k * kTreeThreads, len - 1);
+            qv[k] = qc[j];
             if (fresh) {
-                const int32_t y = j < len ? S[j] : -1;
-                r[k] = (y >= 0 && y < V) ? (double)pu[y] : 0.0;
+                const int32_t y = S[j];
+                const bool ok = y >= 0 && y < V;
+                const float t = pu[ok ? y : 0];
+                r[k] = ok ? (double)t : 0.0;
             } else {
-                r[k] = j < len ? R[j] : 0.0;
+                r[k] = R[j];
             }
         }
 #pragma unroll
@@ -216,27 +260,54 @@ __device__ double residual_update(const float *__restrict__ pu, const int32_t *_
     return block_sum_f64(acc, sh);
 }
 
+// Weights of the four tokens y0 .. y0+3 (zero at or beyond lim) in the
+// final draw: the target off the shortlist, R on it (p_u everywhere when
+// fresh).
+__device__ __forceinline__ void draw_weights(const float *__restrict__ pu,
+                                             const uint32_t *__restrict__ bits_b,
+                                             const uint32_t *__restrict__ rank_b,
+                                             const double *__restrict__ R, int len, int64_t y0,
+                                             int64_t lim, int V, bool vec, bool fresh, double w[4])
+{
+    float v[4];
+    load4(pu, y0, lim, V, vec, v);
+    if (fresh) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            w[c] = (double)v[c];
+        return;
+    }
+    const int64_t wi = min(y0, (int64_t)V - 1) >> 5;
+    const uint32_t wd = bits_b[wi];
+    const int rk = (int)rank_b[wi];
+    const int sh0 = (int)(y0 & 31);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int bit = sh0 + c;
+        const bool in = y0 + c < lim && ((wd >> bit) & 1u);
+        w[c] = in ? R[max(0, min(len - 1, rk + (int)__popc(wd & ((1u << bit) - 1u))))]
+                   : (double)v[c];
+    }
+}
+
 __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
-    int m, int V, int64_t max_len, const int32_t *__restrict__ parent,
+    int m, int V, int64_t max_len, bool vec, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ token, const int64_t *__restrict__ sl_off,
     const int32_t *__restrict__ sl_ids, const float *__restrict__ q, const float *__restrict__ p,
     const float *__restrict__ u_acc, const float *__restrict__ u_fin,
-    const uint32_t *__restrict__ bits, double *__restrict__ Rws, int32_t *__restrict__ n_acc,
-    int32_t *__restrict__ out, int32_t *__restrict__ path)
+    const uint32_t *__restrict__ bits, const uint32_t *__restrict__ rank,
+    double *__restrict__ Rws, int32_t *__restrict__ n_acc, int32_t *__restrict__ out,
+    int32_t *__restrict__ path)
 {
     __shared__ int s_par[kTreeMaxNodes], s_pos[kTreeMaxNodes], s_tok[kTreeMaxNodes];
     __shared__ double s_lhs[kTreeMaxNodes], s_px[kTreeMaxNodes];
-    __shared__ int s_cb[kTreeMaxChunks + 2];
-    __shared__ double s_off[kTreeMaxChunks], s_tot[kTreeMaxChunks], s_pre[kTreeMaxChunks];
+    __shared__ double s_woff[kTreeWaves], s_wt[kTreeWaves], s_w2[kTreeWaves];
     __shared__ double sh[kWave + 1];
-    __shared__ uint32_t s_mw[kWordsPerChunk];
-    __shared__ int s_mpre[kWordsPerChunk];
     __shared__ int s_int[4];
 
     const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int nch = tree_chunks(V);
-    const int64_t nwords = (int64_t)nch * kWordsPerChunk;
-    const uint32_t *bits_b = bits + (int64_t)b * nwords;
+    const int64_t nw = tree_words(V);
+    const uint32_t *bits_b = bits + (int64_t)b * nw, *rank_b = rank + (int64_t)b * nw;
     double *R = Rws + (int64_t)b * max_len;
     const int64_t off = sl_off[b];
     const int64_t len64 = sl_off[b + 1] - off;
@@ -253,53 +324,32 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
     }
     const int len = (int)len64;
     const int32_t *S = sl_ids + off;
+    // listed ids in [0, V)
+    const int rank_end = min(len, (int)rank_b[nw - 1] + (int)__popc(bits_b[nw - 1]));
+    const Slices sl{((int64_t)V + 32 * kTreeWaves - 1) / (32 * kTreeWaves) * 32};
 
-    // shortlist range of every chunk: s_cb[c] = #{ids < 1024 c}, c = 0..nch
-    for (int i = tid; i < nch + 2; i += kTreeThreads)
-        s_cb[i] = 0;
-    __syncthreads();
-    for (int j = tid; j < len; j += kTreeThreads) {
-        const int32_t y = S[j];
-        const int k = y < 0 ? 0 : (y >= nch * kChunk ? nch + 1 : (y >> 10) + 1);
-        atomicAdd(&s_cb[k], 1);
-    }
-    __syncthreads();
-    if (wave == 0) {
-        int carry = 0;
-        for (int c0 = 0; c0 <= nch; c0 += kWave) {
-            const int c = c0 + lane;
-            int v = c <= nch ? s_cb[c] : 0;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int t = __shfl_up(v, o);
-                if (lane >= o)
-                    v += t;
-            }
-            if (c <= nch)
-                s_cb[c] = carry + v;
-            carry += __shfl(v, kWave - 1);
-        }
-    }
-    __syncthreads();
-
-    // per drafted node i (index i-1): parent, token, shortlist position,
-    // u * q_i(x) (exact in fp64) and the target at its parent p_par(x)
-    for (int i = wave + 1; i <= m; i += kTreeWaves) {
+    // drafted node i (index i-1): parent, token, shortlist position,
+    // u * q_i(x) (exact in fp64) and the target at its parent
+    for (int i = tid + 1; i <= m; i += kTreeThreads) {
         const int64_t e = (int64_t)b * m + i - 1;
         const int32_t x = token[e];
         const int par = parent[e];
-        const int pos = shortlist_pos(bits_b, s_cb, V, x);
-        if (lane == 0) {
-            const float *qi = q + (int64_t)m * off + (int64_t)(i - 1) * len;
-            const double qx = pos >= 0 ? (double)qi[pos] : 0.0;
-            const bool valid = x >= 0 && x < V;
-            const bool linked = par >= 0 && par < i;
-            s_par[i - 1] = linked ? par : -1;
-            s_tok[i - 1] = x;
-            s_pos[i - 1] = pos;
-            s_lhs[i - 1] = (double)u_acc[e] * qx;
-            s_px[i - 1] = (valid && linked) ? (double)p[((int64_t)b * (m + 1) + par) * V + x] : 0.0;
+        const float ua = u_acc[e];
+        const bool valid = x >= 0 && x < V;
+        const bool linked = par >= 0 && par < i;
+        int pos = -1;
+        if (valid) {
+            const uint32_t w = bits_b[x >> 5];
+            if ((w >> (x & 31)) & 1u)
+                pos = min(len - 1, (int)rank_b[x >> 5] + (int)__popc(w & ((1u << (x & 31)) - 1u)));
         }
+        const double qx =
+            pos >= 0 ? (double)q[(int64_t)m * off + (int64_t)(i - 1) * len + pos] : 0.0;
+        s_par[i - 1] = linked ? par : -1;
+        s_tok[i - 1] = x;
+        s_pos[i - 1] = pos;
+        s_lhs[i - 1] = (double)ua * qx;
+        s_px[i - 1] = (valid && linked) ? (double)p[((int64_t)b * (m + 1) + par) * V + x] : 0.0;
     }
     __syncthreads();
 
@@ -320,8 +370,13 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
                 acc = c;
                 break;
             }
-            if (!have_off) {  // (its barriers also order this test's reads of R)
-                Poff = off_sums(pu, bits_b, V, nch, s_off, sh);
+            if (!have_off) {
+                slice_pass<true>(pu, bits_b, V, sl, vec, s_woff);
+                __syncthreads();  // (also orders this test's reads of R)
+                Poff = 0.0;
+#pragma unroll
+                for (int w = 0; w < kTreeWaves; ++w)
+                    Poff += s_woff[w];
                 have_off = true;
             } else {
                 __syncthreads();  // every thread has read R for this test
@@ -347,75 +402,144 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
             continue;
         }
 
-        // final draw from r over all V (inverse CDF, chunk by chunk)
-        if (!have_off)
-            Poff = off_sums(pu, bits_b, V, nch, s_off, sh);
-        for (int c = wave; c < nch; c += kTreeWaves) {
-            const int lo = s_cb[c], hi = s_cb[c + 1];
+        // final draw from r over all V (inverse CDF): slice totals, the
+        // owning slice, the owning thread's segment of it, its token
+        if (fresh) {  // r is p_u: slice totals of the row
+            slice_pass<false>(pu, bits_b, V, sl, vec, s_wt);
+        } else {  // wave w adds R over the listed ids of its slice
+            const int j0 = rank_at(rank_b, sl.lo(wave, V), V, rank_end);
+            const int j1 = rank_at(rank_b, sl.hi(wave, V), V, rank_end);
             double a = 0.0;
-            for (int j = lo + lane; j < hi; j += kWave) {
-                if (fresh) {
-                    const int32_t y = S[j];
-                    a += (y >= 0 && y < V) ? (double)pu[y] : 0.0;
-                } else {
-                    a += R[j];
-                }
+            constexpr int U = 16;
+            for (int jj = j0 + lane; jj < j1; jj += kWave * U) {
+                double r[U];
+#pragma unroll
+                for (int k = 0; k < U; ++k)
+                    r[k] = R[min(jj + k * kWave, j1 - 1)];
+#pragma unroll
+                for (int k = 0; k < U; ++k)
+                    if (jj + k * kWave < j1)
+                        a += r[k];
             }
             a = wave_sum_f64(a);
             if (lane == 0)
-                s_tot[c] = s_off[c] + a;
+                s_wt[wave] = s_woff[wave] + a;
         }
         __syncthreads();
-        const double total = row_prefix(s_tot, nch, s_pre, s_tot, &sh[kWave]);
-        const double thr = (double)u_fin[b] * total;
-        owner_chunk(s_pre, s_tot, nch, thr, &s_int[0], &s_int[1]);
-        const int owner = s_int[0];
-        const bool fb = s_int[1] != 0;
+        // slice prefix (fixed order), threshold, owner (first slice whose
+        // prefix passes the threshold; else the last slice with mass)
+        double pre[kTreeWaves + 1];
+        pre[0] = 0.0;
+#pragma unroll
+        for (int w = 0; w < kTreeWaves; ++w)
+            pre[w + 1] = pre[w] + s_wt[w];
+        const double thr = (double)u_fin[b] * pre[kTreeWaves];
+        int owner = -1;
+        bool fb = false;
+#pragma unroll
+        for (int w = kTreeWaves - 1; w >= 0; --w)
+            if (pre[w + 1] > thr)
+                owner = w;
+        if (owner < 0) {
+            fb = true;
+#pragma unroll
+            for (int w = 0; w < kTreeWaves; ++w)
+                if (s_wt[w] > 0.0)
+                    owner = w;
+        }
         int32_t pick = -1;
         if (owner >= 0) {
-            if (wave == 0) {
-                const uint32_t mw =
-                    lane < kWordsPerChunk ? bits_b[(int64_t)owner * kWordsPerChunk + lane] : 0u;
-                int v = __popc(mw), incl = v;
+            // The owning slice in rows of 256 tokens (lane l: tokens 4l ..
+            // 4l+3 of a row); wave w takes RW consecutive rows.  Pass 1: the
+            // wave totals; pass 2: the wave holding the threshold scans its
+            // rows in order.
+            const int64_t a = sl.lo(owner, V), e = sl.hi(owner, V);
+            const int nrows = (int)((e - a + 4 * kWave - 1) / (4 * kWave));
+            const int RW = (nrows + kTreeWaves - 1) / kTreeWaves;
+            const int r0 = min(nrows, wave * RW), r1 = min(nrows, r0 + RW);
+            constexpr int G = 8;  // rows in flight per wave
+            double mine = 0.0;
+            for (int g = r0; g < r1; g += G) {
+                double w[G][4];
 #pragma unroll
-                for (int o = 1; o < kWave; o <<= 1) {
-                    const int t = __shfl_up(incl, o);
-                    if (lane >= o)
-                        incl += t;
+                for (int k = 0; k < G; ++k) {
+                    const int64_t y0 = a + (int64_t)(g + k) * 4 * kWave + 4 * lane;
+                    draw_weights(pu, bits_b, rank_b, R, len, y0, g + k < r1 ? e : 0, V, vec,
+                                 fresh, w[k]);
                 }
-                if (lane < kWordsPerChunk) {
-                    s_mw[lane] = mw;
-                    s_mpre[lane] = incl - v;
-                }
+#pragma unroll
+                for (int k = 0; k < G; ++k)
+                    mine += ((w[k][0] + w[k][1]) + w[k][2]) + w[k][3];
+            }
+            mine = wave_sum_f64(mine);
+            if (lane == 0)
+                s_w2[wave] = mine;
+            __syncthreads();
+            double run = pre[owner];
+            int ow = -1;
+            for (int w = 0; w < kTreeWaves; ++w) {  // first wave past the threshold
+                if (ow < 0 && !fb && run + s_w2[w] > thr)
+                    ow = w;
+                if (ow < 0)
+                    run += s_w2[w];
             }
             if (tid == 0) {
-                s_int[2] = INT_MAX;  // first index past the threshold
-                s_int[3] = -1;       // last index with mass
+                s_int[0] = -1;  // the pick
+                s_int[1] = -1;  // last token with mass in the slice
             }
             __syncthreads();
-            const int o = tid;
-            const int64_t y = (int64_t)owner * kChunk + o;
-            double w = 0.0;
-            if (y < V) {
-                const uint32_t word = s_mw[o >> 5];
-                if (!fresh && ((word >> (o & 31)) & 1u))
-                    w = R[s_cb[owner] + s_mpre[o >> 5] + __popc(word & ((1u << (o & 31)) - 1u))];
-                else
-                    w = (double)pu[y];
-            }
-            double tot;
-            const double ex = block_excl_scan_f64(w, sh, &tot);
-            if (w > 0.0) {
-                if (!fb && s_pre[owner] + (ex + w) > thr)
-                    atomicMin(&s_int[2], o);
-                atomicMax(&s_int[3], o);
+            if (ow < 0) {  // rounding or fallback: the last token with mass
+                int64_t last = -1;
+                for (int g = r0; g < r1; g += G) {
+                    double w[G][4];
+#pragma unroll
+                    for (int k = 0; k < G; ++k) {
+                        const int64_t y0 = a + (int64_t)(g + k) * 4 * kWave + 4 * lane;
+                        draw_weights(pu, bits_b, rank_b, R, len, y0, g + k < r1 ? e : 0, V, vec,
+                                     fresh, w[k]);
+                    }
+#pragma unroll
+                    for (int k = 0; k < G; ++k)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            if (w[k][c] > 0.0)
+                                last = a + (int64_t)(g + k) * 4 * kWave + 4 * lane + c;
+                }
+                if (last >= 0)
+                    atomicMax(&s_int[1], (int)last);
+            } else if (wave == ow) {
+                const int rw0 = min(nrows, ow * RW), rw1 = min(nrows, rw0 + RW);
+                int64_t last = -1;
+                for (int r = rw0; r < rw1; ++r) {
+                    const int64_t y0 = a + (int64_t)r * 4 * kWave + 4 * lane;
+                    double w[4];
+                    draw_weights(pu, bits_b, rank_b, R, len, y0, e, V, vec, fresh, w);
+                    const double lsum = ((w[0] + w[1]) + w[2]) + w[3];
+                    const double incl = wave_incl_scan_f64(lsum);
+                    double part = run + (incl - lsum);
+                    int found = -1;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        part += w[c];
+                        if (w[c] > 0.0) {
+                            last = y0 + c;
+                            if (found < 0 && part > thr)
+                                found = c;
+                        }
+                    }
+                    const uint64_t hit = __ballot(found >= 0);
+                    if (hit) {  // wave-uniform
+                        if (lane == __ffsll((unsigned long long)hit) - 1)
+                            s_int[0] = (int)(y0 + found);
+                        break;
+                    }
+                    run += __shfl(incl, kWave - 1);
+                }
+                if (last >= 0)
+                    atomicMax(&s_int[1], (int)last);
             }
             __syncthreads();
-            const int first = s_int[2], last = s_int[3];
-            if (first != INT_MAX)
-                pick = owner * kChunk + first;
-            else if (last >= 0)
-                pick = owner * kChunk + last;
+            pick = s_int[0] >= 0 ? s_int[0] : s_int[1];
         }
         if (tid == 0)
             ob[n] = pick;
@@ -430,7 +554,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
 size_t verify_tree_ws_bytes(int B, int m, int V, int64_t max_len)
 {
     (void)m;
-    return tree_R_bytes(B, max_len) + (size_t)B * tree_chunks(V) * kWordsPerChunk * 4 + 256;
+    return tree_R_bytes(B, max_len) + 2 * tree_bits_bytes(B, V) + 256;
 }
 
 hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
@@ -439,18 +563,21 @@ hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t 
                               const float *u_fin, int64_t max_len, int32_t *n_acc, int32_t *out,
                               int32_t *path, void *ws, hipEvent_t t0, hipEvent_t t1)
 {
-    double *R = reinterpret_cast<double *>(ws);
-    uint32_t *bits = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) +
-                                                  tree_R_bytes(B, max_len));
-    const int nch = tree_chunks(V);
-    const int bx = (nch * kChunk + kBitsTokens - 1) / kBitsTokens;
-    hipError_t e = launch_timed(tree_bits_kernel, dim3((unsigned)bx, (unsigned)B), dim3(256), s,
-                                t0, nullptr, V, max_len, sl_off, sl_ids, bits);
+    char *base = reinterpret_cast<char *>(ws);
+    double *R = reinterpret_cast<double *>(base);
+    uint32_t *bits = reinterpret_cast<uint32_t *>(base + tree_R_bytes(B, max_len));
+    uint32_t *rank = reinterpret_cast<uint32_t *>(base + tree_R_bytes(B, max_len) +
+                                                  tree_bits_bytes(B, V));
+    const int bx = (V + kBitsTokens - 1) / kBitsTokens;
+    const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+    hipError_t e = launch_timed(tree_bits_kernel, dim3((unsigned)bx, (unsigned)B),
+                                dim3(kBitsThreads), s, t0, nullptr, V, max_len, sl_off, sl_ids,
+                                bits, rank);
     if (e != hipSuccess)
         return e;
-    return launch_timed(verify_tree_kernel, dim3((unsigned)B), dim3(kTreeThreads), s, nullptr,
-                        t1, m, V, max_len, parent, token, sl_off, sl_ids, q, p, u_acc, u_fin,
-                        (const uint32_t *)bits, R, n_acc, out, path);
+    return launch_timed(verify_tree_kernel, dim3((unsigned)B), dim3(kTreeThreads), s, nullptr, t1,
+                        m, V, max_len, vec, parent, token, sl_off, sl_ids, q, p, u_acc, u_fin,
+                        (const uint32_t *)bits, (const uint32_t *)rank, R, n_acc, out, path);
 }
 
 }  // namespace ds

@@ -6,7 +6,8 @@
       then ds_target_softmax and ds_verify_reject on the head stream;
   trees (B sequences x m nodes sharing one shortlist): router, select and
       build for the B roots, then one gathered head with m rows per group and
-      one sample per node.
+      one sample per node, then ds_target_softmax over the m+1 nodes and
+      ds_verify_tree.
 PyTorch only allocates memory and provides the streams.
 """
 from __future__ import annotations
@@ -98,11 +99,18 @@ class DraftStep:
         self.head_ws = N.workspace(N.head_workspace_bytes(B, m, V), device)
         self.router_stream = torch.cuda.Stream(device=device)
         if self.target_logits is not None:
-            self.p = torch.empty(B, T + 1, V, **f32)
+            rows = syn.target_rows(cfg)
+            self.p = torch.empty(B, rows, V, **f32)
             self.n_acc = torch.empty(B, **i32)
-            self.out = torch.empty(B, T + 1, **i32)
-            self.softmax_ws = N.workspace(N.softmax_workspace_bytes(B * (T + 1), V), device)
-            self.verify_ws = N.workspace(N.verify_workspace_bytes(B, T, V), device)
+            self.out = torch.empty(B, rows, **i32)
+            self.softmax_ws = N.workspace(N.softmax_workspace_bytes(B * rows, V), device)
+            if cfg.is_tree:
+                self.parent = dev(wl.parent)
+                self.path = torch.empty(B, m, **i32)
+                self.verify_ws = N.workspace(
+                    N.verify_tree_workspace_bytes(B, m, V, int(self.max_len[0])), device)
+            else:
+                self.verify_ws = N.workspace(N.verify_workspace_bytes(B, T, V), device)
         self._args = self._chain_args() if not cfg.is_tree else None
 
     # ------------------------------------------------------------------ chains
@@ -159,6 +167,11 @@ class DraftStep:
 
     def verify(self, stream=None) -> None:
         N.target_softmax(self.target_logits, self.p, self.softmax_ws, stream=stream)
+        if self.cfg.is_tree:
+            N.verify_tree(self.parent, self.token, self.sl_off, self.sl_ids, self.q, self.p,
+                          self.u_acc, self.u_fin, int(self.max_len[0]), self.n_acc, self.out,
+                          self.path, self.verify_ws, stream=stream)
+            return
         N.verify_reject(self.token, self.sl_off, self.sl_ids, self.q, self.p, self.u_acc,
                         self.u_fin, self.n_acc, self.out, self.verify_ws, stream=stream)
 
@@ -206,6 +219,8 @@ class DraftStep:
         if self.target_logits is not None:
             r.update(p=self.p.cpu().numpy(), n_acc=self.n_acc.cpu().numpy(),
                      out=self.out.cpu().numpy())
+            if self.cfg.is_tree:
+                r["path"] = self.path.cpu().numpy()
         return r
 
 

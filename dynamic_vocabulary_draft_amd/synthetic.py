@@ -221,13 +221,29 @@ def make_uniforms(cfg: Config, stream: int, shape, instance: int = 0) -> np.ndar
     return (k.astype(np.float64) * 2.0 ** -U_BITS).astype(np.float32)
 
 
+def target_rows(cfg: Config) -> int:
+    """Target distributions per sequence: one per drafted position plus the
+    bonus position (chains), one per tree node including the root (trees)."""
+    return cfg.tree_nodes + 1 if cfg.is_tree else cfg.T + 1
+
+
 def make_target_logits(cfg: Config, instance: int = 0) -> np.ndarray:
-    """Full-vocabulary target logits N(0, 3) of shape [B][T+1][V] (fp32)."""
+    """Full-vocabulary target logits N(0, 3) of shape [B][rows][V] (fp32)."""
     g = rng(cfg.index, 8, instance)
-    out = np.empty((cfg.B, cfg.T + 1, cfg.V), dtype=np.float32)
+    rows = target_rows(cfg)
+    out = np.empty((cfg.B, rows, cfg.V), dtype=np.float32)
     for b in range(cfg.B):
-        out[b] = g.standard_normal((cfg.T + 1, cfg.V), dtype=np.float32) * np.float32(cfg.target_std)
+        out[b] = g.standard_normal((rows, cfg.V), dtype=np.float32) * np.float32(cfg.target_std)
     return out
+
+
+def tree_parent(cfg: Config) -> np.ndarray:
+    """Tree shape [B][m]: entry i-1 is the parent of drafted node i.  The
+    tree workload fixes 64 nodes per tree but no shape; a complete binary
+    tree in heap order (parent of node i is (i-1) // 2, depth 6 for 64
+    nodes) is taken, the same for every sequence.  No random draw."""
+    i = np.arange(1, cfg.tree_nodes + 1, dtype=np.int64)
+    return np.tile(((i - 1) // 2).astype(np.int32), (cfg.B, 1))
 
 
 def budget_rows(cfg: Config) -> np.ndarray:
@@ -245,9 +261,10 @@ class Workload:
     h: np.ndarray
     budget: np.ndarray  # [T][B]
     u_draft: np.ndarray  # chains [T][B]; trees [B][nodes]
-    u_acc: np.ndarray  # [T][B]
+    u_acc: np.ndarray  # chains [T][B]; trees [B][nodes]
     u_fin: np.ndarray  # [B]
-    target_logits: np.ndarray | None  # [B][T+1][V]
+    target_logits: np.ndarray | None  # [B][target_rows][V]
+    parent: np.ndarray | None = None  # trees: [B][nodes]
 
 
 def make_workload(index: int, instance: int = 0, with_W: bool = True,
@@ -262,10 +279,10 @@ def make_workload(index: int, instance: int = 0, with_W: bool = True,
         router=make_router(cfg), h=make_hidden(cfg, instance),
         budget=budget_rows(cfg),
         u_draft=make_uniforms(cfg, 9, udraft_shape, instance),
-        u_acc=make_uniforms(cfg, 10, (cfg.T, cfg.B), instance),
+        u_acc=make_uniforms(cfg, 10, udraft_shape, instance),
         u_fin=make_uniforms(cfg, 11, (cfg.B,), instance),
-        target_logits=(make_target_logits(cfg, instance)
-                       if with_target and not cfg.is_tree else None),
+        target_logits=make_target_logits(cfg, instance) if with_target else None,
+        parent=tree_parent(cfg) if cfg.is_tree else None,
     )
 
 

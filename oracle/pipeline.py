@@ -8,7 +8,9 @@ positions), the head projects h[:, t+1] (H_t) onto it and a token is sampled
 with u_draft[t].  Then the target distribution is the softmax of the target
 logits and the drafts are verified.  Trees (tree_nodes > 1): one router row
 per sequence (h[:, 0]), one shortlist per sequence shared by its nodes
-h[:, 1:], one sample per node, no verification.
+h[:, 1:], one sample per node (node i's token from its own row), then the
+tree is verified by multi-step speculative sampling against the target at
+every node.
 
 Sources: DynaSpec summary page, "Pipeline Flow" (router, drafter,
 synchronisation and gathered projection, rejection-sampling verification) and
@@ -37,6 +39,13 @@ def run_step(wl, temperature: float = 1.0, p: np.ndarray | None = None) -> dict:
         res.update(scores=[sc], sel=[sel], n_sel=[n_sel], sl_len=[sl_len], status=[st],
                    sl_off=sl_off, sl_ids=sl_ids[:sl_off[-1]], logits=logits, token=tok, q=q,
                    tie=tie)
+        if wl.target_logits is not None:
+            if p is None:
+                p = oracle.target_softmax(wl.target_logits)
+            n_acc, out, path, vtie = oracle.verify_tree(wl.parent, tok.reshape(B, m), sl_off,
+                                                        sl_ids[:sl_off[-1]], q, p, wl.u_acc,
+                                                        wl.u_fin)
+            res.update(p=p, n_acc=n_acc, out=out, path=path, verify_tie=vtie)
         return res
     offs = [np.zeros(1, np.int64)]
     ids, logit_parts, q_parts, toks, ties = [], [], [], [], []

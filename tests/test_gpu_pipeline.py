@@ -100,6 +100,14 @@ def check_stagewise(wl, r, head_samples=None, seed=0):
         _ulp(r["q"][m * lo:m * hi], q)
     if "p" in r:
         _ulp(r["p"], oracle.target_softmax(wl.target_logits))
+        if cfg.is_tree:
+            n_acc, out, path, tie = oracle.verify_tree(wl.parent, r["token"], r["sl_off"],
+                                                       r["sl_ids"], r["q"], r["p"], wl.u_acc,
+                                                       wl.u_fin)
+            assert np.array_equal(r["n_acc"][~tie], n_acc[~tie])
+            assert np.array_equal(r["path"][~tie], path[~tie])
+            assert np.array_equal(r["out"][~tie], out[~tie])
+            return
         n_acc, out, tie = oracle.verify_reject(r["token"], r["sl_off"], r["sl_ids"], r["q"], r["p"],
                                                wl.u_acc, wl.u_fin)
         assert np.array_equal(r["n_acc"], n_acc)
@@ -127,6 +135,10 @@ def check_from_scratch(wl, r):
     if cfg.is_tree:
         tok_ok = ~ref["tie"].reshape(B, -1) & ok_rows[0][:, None]
         assert np.array_equal(r["token"][tok_ok], ref["token"].reshape(B, -1)[tok_ok])
+        if "n_acc" in ref:
+            seq_ok = tok_ok.all(1) & ~ref["verify_tie"]
+            for k in ("n_acc", "out", "path"):
+                assert np.array_equal(r[k][seq_ok], ref[k][seq_ok]), k
         return
     good = ok_rows & ~ref["tie"]
     assert np.array_equal(r["token"][good], ref["token"][good])
@@ -184,6 +196,9 @@ def test_graph_replay_matches_eager(oracle_lib, name):
             if step.target_logits is not None:
                 step.out.fill_(-3)
                 step.p.fill_(-1.0)
+                if step.cfg.is_tree:
+                    step.path.fill_(-4)
+                    step.n_acc.fill_(-6)
         torch.cuda.synchronize()
         graph.launch(stream)
         got = step.host()
