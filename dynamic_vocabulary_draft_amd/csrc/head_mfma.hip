@@ -51,7 +51,14 @@ __device__ __forceinline__ f32x16 mfma(const u32x4 &a, const u32x4 &b, f32x16 c)
 // load is unconditional and the compiler waits only for the slice it uses.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, CDNA encoding
-constexpr int kNonTemporal = 2;         // streamed once: do not keep in cache
+// Cache policy of the W loads (the aux field of the buffer load).  The union
+// kernel reads every row once: nontemporal (2) keeps W from displacing the
+// hidden vectors.  The gathered kernel's trees share many rows, and groups
+// with the same tile index run side by side, so its rows stay cacheable
+// (0): measured 15% faster on the 8 x 64 tree than nontemporal, while the
+// union kernel is 10% slower without the hint.
+constexpr int kNonTemporal = 2;
+constexpr int kCached = 0;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -64,12 +71,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 // slice).  Loads that give each lane its own MFMA row instead (two lanes per
 // row, 32 B of a line per load) stream at well under half the bandwidth.
 // `voff[i]` = byte offset of this lane's row for load i plus 16*(l%8).
+template <int AUX>
 __device__ __forceinline__ void load_a(rsrc_t w, const uint32_t voff[4], int k0, u32x4 a[4])
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         a[i] = __builtin_amdgcn_raw_buffer_load_b128(w, voff[i] + 2u * (uint32_t)k0, 0,
-                                                     kNonTemporal);
+                                                     AUX);
 }
 
 // Per-wave LDS slice of A: 32 rows x 64 bf16; the 16-byte piece p of row r
@@ -156,7 +164,7 @@ __device__ __forceinline__ void slice_mma(const u32x4 ld[4], uint16_t *aw, const
 // in flight); a phase (phase_len<NB>() hidden elements of B) is staged in
 // LDS between two barriers, its loads issued one slice group earlier so the
 // switch waits for them and not for the W ring.
-template <int NB, class Src>
+template <int NB, int AUX, class Src>
 __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], int d,
                                              uint16_t *lds, uint16_t *aw, int nrows, Src src,
                                              f32x16 acc[NB])
@@ -170,10 +178,10 @@ __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], i
     load_phase<NB>(hv, 0, d, nrows, src);
     __builtin_amdgcn_sched_barrier(0);  // B loads first, as in the loop
     u32x4 r0[4], r1[4], r2[4], r3[4];
-    load_a(w, voff, 0 * kKs, r0);
-    load_a(w, voff, 1 * kKs, r1);
-    load_a(w, voff, 2 * kKs, r2);
-    load_a(w, voff, 3 * kKs, r3);
+    load_a<AUX>(w, voff, 0 * kKs, r0);
+    load_a<AUX>(w, voff, 1 * kKs, r1);
+    load_a<AUX>(w, voff, 2 * kKs, r2);
+    load_a<AUX>(w, voff, 3 * kKs, r3);
     for (int ph = 0; ph < nph; ++ph) {
         __syncthreads();  // every wave is done with the previous phase
         store_phase<NB>(lds, hv, ph * KP, d, nrows);
@@ -190,13 +198,13 @@ __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], i
                 __builtin_amdgcn_sched_barrier(0);
             }
             slice_mma<NB>(r0, aw, lds, (4 * gi + 0) * kKs, (ks + 0) * kKs, d, acc);
-            load_a(w, voff, (ks + 4) * kKs, r0);
+            load_a<AUX>(w, voff, (ks + 4) * kKs, r0);
             slice_mma<NB>(r1, aw, lds, (4 * gi + 1) * kKs, (ks + 1) * kKs, d, acc);
-            load_a(w, voff, (ks + 5) * kKs, r1);
+            load_a<AUX>(w, voff, (ks + 5) * kKs, r1);
             slice_mma<NB>(r2, aw, lds, (4 * gi + 2) * kKs, (ks + 2) * kKs, d, acc);
-            load_a(w, voff, (ks + 6) * kKs, r2);
+            load_a<AUX>(w, voff, (ks + 6) * kKs, r2);
             slice_mma<NB>(r3, aw, lds, (4 * gi + 3) * kKs, (ks + 3) * kKs, d, acc);
-            load_a(w, voff, (ks + 7) * kKs, r3);
+            load_a<AUX>(w, voff, (ks + 7) * kKs, r3);
         }
     }
 }
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uin
         voff[i] = (uint32_t)((32 * wave + (lane >> 3) + 8 * i) * d * 2 + 16 * (lane & 7));
     f32x16 acc[NB];
     auto hsrc = [&](int r) { return h + (int64_t)(g0 + r) * ldh_g; };
-    rows_times_b<NB>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc, acc);
+    rows_times_b<NB, kNonTemporal>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc, acc);
 
     // epilogue: the (row, group) pairs on the group's shortlist.  A group's
     // entries for the block's four tiles are one contiguous run of its
@@ -419,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void h
             voff[i] = (uint32_t)__shfl(yrow, (lane >> 3) + 8 * i) * (uint32_t)d * 2u +
                       16u * (lane & 7);
         f32x16 acc[NB];
-        rows_times_b<NB>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc);
+        rows_times_b<NB, kCached>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc);
         // epilogue: column = head row (node), row = shortlist entry; the
         // entry of accumulator row i was loaded by lanes i and i + 32
 #pragma unroll
