@@ -256,3 +256,34 @@ def verify_tree(parent, token, sl_off, sl_ids, q, p, u_acc, u_fin):
                            _p(sl_ids), _p(q), _p(p), _p(u_acc), _p(u_fin), _p(n_acc), _p(out),
                            _p(path), _p(tie))
     return n_acc, out, path, tie.astype(bool)
+
+
+def topl_labels(logits, cluster_of, M: int, L: int):
+    """labels[n][M] uint8: cluster c is positive iff it holds one of the
+    top-L tokens of the row (logit desc, id asc)."""
+    lib = _load()
+    logits = _c(logits, np.float32)
+    n, V = logits.shape
+    cluster_of = _c(cluster_of, np.int32)
+    out = np.empty((n, M), np.uint8)
+    lib.oracle_topl_labels(C.c_int(n), C.c_int(V), C.c_int(M), C.c_int(L), _p(logits),
+                           C.c_int64(V), _p(cluster_of), _p(out))
+    return out
+
+
+def router_train_step(h, labels, W1, b1, W2, b2, act: int, lr: float):
+    """One SGD step; returns (loss, grads dict (float64), new params dict
+    (float32)).  h[n][d] fp32 or bf16 bits; params fp32."""
+    lib = _load()
+    h = _c(h)
+    n, d = h.shape
+    W1, b1, W2, b2 = (np.array(x, dtype=np.float32, copy=True) for x in (W1, b1, W2, b2))
+    r, M = W1.shape[0], W2.shape[0]
+    labels = _c(labels, np.uint8)
+    g = {"W1": np.empty((r, d)), "b1": np.empty(r), "W2": np.empty((M, r)), "b2": np.empty(M)}
+    loss = C.c_double()
+    lib.oracle_router_train_step(C.c_int(_dtype_code(h)), C.c_int(n), C.c_int(d), C.c_int(r),
+                                 C.c_int(M), C.c_int(act), _p(h), C.c_int64(d), _p(labels),
+                                 C.c_float(lr), _p(W1), _p(b1), _p(W2), _p(b2), _p(g["W1"]),
+                                 _p(g["b1"]), _p(g["W2"]), _p(g["b2"]), C.byref(loss))
+    return loss.value, g, {"W1": W1, "b1": b1, "W2": W2, "b2": b2}

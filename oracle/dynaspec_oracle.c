@@ -685,3 +685,159 @@ void oracle_verify_tree(int B, int m, int V, const int32_t *parent, const int32_
     free(r);
     free(qd);
 }
+
+/*
+ * ---------------------------------------------------------------------------
+ * Router training [S "Modeling": supervised multi-label classification; the
+ * objective is binary cross entropy over clusters, a cluster's label being
+ * positive when it holds a token from the top-L of the full drafter; the
+ * trainable part of the router is its 2-layer MLP].
+ * ---------------------------------------------------------------------------
+ */
+
+/* order used for the top-L: logit descending, then token id ascending */
+static const float *g_topl_row;
+static int topl_cmp(const void *a, const void *b)
+{
+    int ia = *(const int *)a, ib = *(const int *)b;
+    float sa = g_topl_row[ia], sb = g_topl_row[ib];
+    if (sa > sb)
+        return -1;
+    if (sa < sb)
+        return 1;
+    return ia < ib ? -1 : (ia > ib ? 1 : 0);
+}
+
+/*
+ * Labels from the full drafter's logits: row i of logits (V values, row
+ * stride ldl) orders the tokens by (logit desc, id asc); the first
+ * min(L, V) of them are the top-L; labels[i][c] = 1 iff one of them lies in
+ * cluster c (cluster_of[y] in [0, M); others are ignored), else 0.
+ */
+void oracle_topl_labels(int n, int V, int M, int L, const float *logits, int64_t ldl,
+                        const int32_t *cluster_of, uint8_t *labels)
+{
+    int *idx = (int *)malloc(sizeof(int) * (size_t)V);
+    for (int i = 0; i < n; ++i) {
+        for (int y = 0; y < V; ++y)
+            idx[y] = y;
+        g_topl_row = logits + (int64_t)i * ldl;
+        qsort(idx, (size_t)V, sizeof(int), topl_cmp);
+        uint8_t *lab = labels + (int64_t)i * M;
+        memset(lab, 0, (size_t)M);
+        for (int k = 0; k < L && k < V; ++k) {
+            int32_t c = cluster_of[idx[k]];
+            if (c >= 0 && c < M)
+                lab[c] = 1;
+        }
+    }
+    free(idx);
+}
+
+static double sigmoid(double x)
+{
+    if (x >= 0.0)
+        return 1.0 / (1.0 + exp(-x));
+    double e = exp(x);
+    return e / (1.0 + e);
+}
+
+/* log(1 + e^x) without overflow */
+static double softplus(double x) { return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x))); }
+
+static double activation_grad(int act, double a)
+{
+    if (act == 0)
+        return a > 0.0 ? 1.0 : 0.0;          /* ReLU (0 at the kink) */
+    double s = sigmoid(a);                   /* SiLU: d/da a s(a) */
+    return s * (1.0 + a * (1.0 - s));
+}
+
+/*
+ * One plain SGD step of the router on a batch of n rows h[i] (row stride
+ * ldh; fp32 or bf16 bits by dtype_h), labels y[i][c] in {0, 1}:
+ *   a = W1 h + b1, z = act(a), s = W2 z + b2         (the router's forward)
+ *   loss = 1/(n M) sum_{i,c} [softplus(s_ic) - y_ic s_ic]
+ *        (= mean of -y log sigmoid(s) - (1 - y) log(1 - sigmoid(s)))
+ *   g_s = (sigmoid(s) - y) / (n M)
+ *   dW2 = g_s^T z, db2 = sum_i g_s, g_z = g_s W2, g_a = g_z * act'(a),
+ *   dW1 = g_a^T h, db1 = sum_i g_a
+ *   param <- param - lr * grad   (fp32 parameters, updated in place)
+ * Gradients and the loss are returned in double; W1[r][d], W2[M][r].
+ */
+void oracle_router_train_step(int dtype_h, int n, int d, int r, int M, int act, const void *h,
+                              int64_t ldh, const uint8_t *labels, float lr, float *W1,
+                              float *b1, float *W2, float *b2, double *dW1, double *db1,
+                              double *dW2, double *db2, double *loss)
+{
+    double *a = (double *)malloc(sizeof(double) * (size_t)n * r);
+    double *z = (double *)malloc(sizeof(double) * (size_t)n * r);
+    double *gs = (double *)malloc(sizeof(double) * (size_t)n * M);
+    double *ga = (double *)malloc(sizeof(double) * (size_t)n * r);
+    const double inv = 1.0 / ((double)n * (double)M);
+    double L = 0.0;
+    for (int i = 0; i < n; ++i) {
+        for (int j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k)
+                acc += (double)W1[(int64_t)j * d + k] * load_elem(dtype_h, h, (int64_t)i * ldh + k);
+            acc += (double)b1[j];
+            a[(int64_t)i * r + j] = acc;
+            z[(int64_t)i * r + j] = activation(act, acc);
+        }
+        for (int c = 0; c < M; ++c) {
+            double s = 0.0;
+            for (int j = 0; j < r; ++j)
+                s += (double)W2[(int64_t)c * r + j] * z[(int64_t)i * r + j];
+            s += (double)b2[c];
+            const double y = labels[(int64_t)i * M + c] ? 1.0 : 0.0;
+            L += softplus(s) - y * s;
+            gs[(int64_t)i * M + c] = (sigmoid(s) - y) * inv;
+        }
+    }
+    *loss = L * inv;
+    for (int c = 0; c < M; ++c) {
+        double bsum = 0.0;
+        for (int i = 0; i < n; ++i)
+            bsum += gs[(int64_t)i * M + c];
+        db2[c] = bsum;
+        for (int j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < n; ++i)
+                acc += gs[(int64_t)i * M + c] * z[(int64_t)i * r + j];
+            dW2[(int64_t)c * r + j] = acc;
+        }
+    }
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int c = 0; c < M; ++c)
+                acc += gs[(int64_t)i * M + c] * (double)W2[(int64_t)c * r + j];
+            ga[(int64_t)i * r + j] = acc * activation_grad(act, a[(int64_t)i * r + j]);
+        }
+    for (int j = 0; j < r; ++j) {
+        double bsum = 0.0;
+        for (int i = 0; i < n; ++i)
+            bsum += ga[(int64_t)i * r + j];
+        db1[j] = bsum;
+        for (int k = 0; k < d; ++k) {
+            double acc = 0.0;
+            for (int i = 0; i < n; ++i)
+                acc += ga[(int64_t)i * r + j] * load_elem(dtype_h, h, (int64_t)i * ldh + k);
+            dW1[(int64_t)j * d + k] = acc;
+        }
+    }
+    /* the step, after every gradient is formed from the old parameters */
+    for (int64_t e = 0; e < (int64_t)r * d; ++e)
+        W1[e] = (float)((double)W1[e] - (double)lr * dW1[e]);
+    for (int j = 0; j < r; ++j)
+        b1[j] = (float)((double)b1[j] - (double)lr * db1[j]);
+    for (int64_t e = 0; e < (int64_t)M * r; ++e)
+        W2[e] = (float)((double)W2[e] - (double)lr * dW2[e]);
+    for (int c = 0; c < M; ++c)
+        b2[c] = (float)((double)b2[c] - (double)lr * db2[c]);
+    free(a);
+    free(z);
+    free(gs);
+    free(ga);
+}

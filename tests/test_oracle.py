@@ -765,3 +765,89 @@ def test_verify_tree_path_is_the_chain_verifier(oracle_lib):
     np.testing.assert_array_equal(out_t[ok], out_c[ok])
     for b in np.flatnonzero(ok):
         np.testing.assert_array_equal(path_t[b, :n_t[b]], np.arange(1, n_t[b] + 1))
+
+
+# ----------------------------------------------------------- router training
+def test_topl_labels_brute_force(oracle_lib):
+    """Top-L by (logit desc, id asc), brute force in Python, on tie-heavy
+    rows; ids without a cluster are skipped; L >= V and L = 0 edge cases."""
+    g = np.random.default_rng(5)
+    n, V, M, L = 6, 300, 17, 12
+    lg = g.integers(-5, 6, size=(n, V)).astype(np.float32)  # heavy ties
+    lg[0] = g.standard_normal(V).astype(np.float32)
+    cluster_of = g.integers(0, M, size=V).astype(np.int32)
+    cluster_of[np.argsort(-lg[1], kind="stable")[0]] = -1  # row 1's best token has no cluster
+    for LL in (L, 0, V + 5):
+        got = oracle_lib.topl_labels(lg, cluster_of, M, LL)
+        for i in range(n):
+            top = sorted(range(V), key=lambda y: (-float(lg[i, y]), y))[:LL]
+            ref = np.zeros(M, np.uint8)
+            for y in top:
+                if 0 <= cluster_of[y] < M:
+                    ref[cluster_of[y]] = 1
+            assert np.array_equal(got[i], ref), (LL, i)
+
+
+def _router_case(seed, n=3, d=5, r=4, M=6, act=syn.ACT_SILU):
+    g = np.random.default_rng(seed)
+    h = g.standard_normal((n, d)).astype(np.float32)
+    W1 = (g.standard_normal((r, d)) * 0.7).astype(np.float32)
+    b1 = (g.standard_normal(r) * 0.3).astype(np.float32)
+    if act == syn.ACT_RELU:  # keep every pre-activation away from the kink
+        a = h.astype(np.float64) @ W1.T.astype(np.float64) + b1
+        b1 = (b1 + np.where(np.abs(a) < 0.05, 0.1, 0.0).max(0)).astype(np.float32)
+    W2 = (g.standard_normal((M, r)) * 0.7).astype(np.float32)
+    b2 = (g.standard_normal(M) * 0.3).astype(np.float32)
+    y = (g.random((n, M)) < 0.4).astype(np.uint8)
+    return h, y, W1, b1, W2, b2
+
+
+@pytest.mark.parametrize("act", [syn.ACT_RELU, syn.ACT_SILU])
+def test_router_train_loss_is_log_loss(oracle_lib, act):
+    """The step's loss is the mean binary cross entropy of sigmoid(router
+    scores) against the labels, as sklearn computes it."""
+    from scipy.special import expit
+    from sklearn.metrics import log_loss
+    h, y, W1, b1, W2, b2 = _router_case(1, n=7, d=9, r=8, M=11, act=act)
+    loss, _, _ = oracle_lib.router_train_step(h, y, W1, b1, W2, b2, act, 0.0)
+    s = oracle_lib.router_score(h, W1, b1, W2, b2, act).astype(np.float64)
+    ref = log_loss(y.ravel(), expit(s.ravel()), labels=[0, 1])
+    assert abs(loss - ref) <= 1e-6 * ref
+
+
+@pytest.mark.parametrize("act", [syn.ACT_RELU, syn.ACT_SILU])
+def test_router_train_gradients_match_finite_differences(oracle_lib, act):
+    """Every gradient entry against a central difference of the loss."""
+    h, y, W1, b1, W2, b2 = _router_case(2, act=act)
+    _, grad, _ = oracle_lib.router_train_step(h, y, W1, b1, W2, b2, act, 0.0)
+    params = {"W1": W1, "b1": b1, "W2": W2, "b2": b2}
+    for name, P in params.items():
+        flat = P.reshape(-1)
+        for e in range(flat.size):
+            hi, lo = flat.copy(), flat.copy()
+            hi[e] = np.float32(flat[e] + np.float32(2e-3))
+            lo[e] = np.float32(flat[e] - np.float32(2e-3))
+            Lh = oracle_lib.router_train_step(h, y, **{**params, name: hi.reshape(P.shape)},
+                                              act=act, lr=0.0)[0]
+            Ll = oracle_lib.router_train_step(h, y, **{**params, name: lo.reshape(P.shape)},
+                                              act=act, lr=0.0)[0]
+            fd = (Lh - Ll) / (float(hi[e]) - float(lo[e]))
+            an = grad[name].reshape(-1)[e]
+            assert abs(fd - an) <= 2e-5 + 1e-3 * abs(an), (name, e, fd, an)
+
+
+def test_router_train_step_update_and_zero_head(oracle_lib):
+    """SGD moves every parameter by -lr * grad (rounded to fp32); with the
+    second layer at zero the loss is log 2, db2 = mean(0.5 - y) per column
+    and no gradient reaches the first layer."""
+    h, y, W1, b1, W2, b2 = _router_case(3, n=5, d=6, r=4, M=3)
+    lr = 0.37
+    loss, grad, new = oracle_lib.router_train_step(h, y, W1, b1, W2, b2, syn.ACT_SILU, lr)
+    for name, P in (("W1", W1), ("b1", b1), ("W2", W2), ("b2", b2)):
+        ref = (P.astype(np.float64) - float(np.float32(lr)) * grad[name]).astype(np.float32)
+        assert np.array_equal(new[name], ref), name
+    W2z, b2z = np.zeros_like(W2), np.zeros_like(b2)
+    loss, grad, _ = oracle_lib.router_train_step(h, y, W1, b1, W2z, b2z, syn.ACT_SILU, 0.0)
+    assert abs(loss - np.log(2.0)) < 1e-15
+    np.testing.assert_allclose(grad["b2"], (0.5 - y).sum(0) / y.size, rtol=0, atol=1e-16)
+    assert not grad["W1"].any() and not grad["b1"].any()
