@@ -21,7 +21,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdynaspec.so")
 SOURCES = ["abi.hip", "router.hip", "select.hip", "shortlist.hip", "head.hip", "head_mfma.hip",
            "pack.hip", "sample.hip", "verify.hip", "verify_tree.hip",
-           "kmeans.hip"]
+           "kmeans.hip", "router_train.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",

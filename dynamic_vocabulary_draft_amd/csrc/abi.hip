@@ -421,6 +421,44 @@ ds_status ds_verify_tree(hipStream_t s, int B, int m, int V, const int32_t *pare
                                              u_acc, u_fin, max_len, n_acc, out, path, ws));
 }
 
+ds_status ds_router_labels(hipStream_t s, int n, int V, int M, int L, const float *logits,
+                           int64_t ldl, const int32_t *cluster_of, uint8_t *labels)
+{
+    if (!logits || !cluster_of || !labels || n <= 0 || V <= 0 || M <= 0 || L < 0 || ldl < V)
+        return DS_EINVAL;
+    if (M > DS_MAX_CLUSTERS || n > (1 << 30))
+        return DS_ESHAPE;
+    return hip_status(ds::topl_labels_launch(s, n, V, M, L, logits, ldl, cluster_of, labels));
+}
+
+size_t ds_router_train_workspace_bytes(int n, int r, int M)
+{
+    if (n <= 0 || r <= 0 || M <= 0)
+        return 0;
+    return ds::router_train_ws_bytes(n, r, M);
+}
+
+ds_status ds_router_train_step(hipStream_t s, const ds_router_train_args *a)
+{
+    if (!a || !a->h || !a->labels || !a->W1 || !a->b1 || !a->W2 || !a->b2 || !a->dW1 ||
+        !a->db1 || !a->dW2 || !a->db2 || !a->loss || !a->ws)
+        return DS_EINVAL;
+    if (a->n <= 0 || a->d <= 0 || a->r <= 0 || a->M <= 0 || a->ldh < a->d)
+        return DS_EINVAL;
+    if (a->act != DS_RELU && a->act != DS_SILU)
+        return DS_EDTYPE;
+    if (a->h_dtype != DS_F32 && a->h_dtype != DS_BF16)
+        return DS_EDTYPE;
+    if ((int64_t)a->n * a->d > (1ll << 31) || (int64_t)a->r * a->d > (1ll << 31) ||
+        (int64_t)a->n * a->M > (1ll << 31))
+        return DS_ESHAPE;
+    if (a->ws_bytes < ds_router_train_workspace_bytes(a->n, a->r, a->M))
+        return DS_EINVAL;
+    return hip_status(ds::router_train_launch(
+        s, a->n, a->d, a->r, a->M, a->act, a->h_dtype == DS_BF16, a->h, a->ldh, a->labels, a->lr,
+        a->W1, a->b1, a->W2, a->b2, a->dW1, a->db1, a->dW2, a->db2, a->loss, a->ws));
+}
+
 size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r, int64_t max_len)
 {
     if (B <= 0 || T <= 0 || V <= 0 || r <= 0 || max_len <= 0)

@@ -74,6 +74,14 @@ hipError_t verify_launch(hipStream_t s, int B, int T, int V, const int32_t *draf
                          const float *p, const float *u_acc, const float *u_fin, int32_t *n_acc,
                          int32_t *out, void *ws);
 
+hipError_t topl_labels_launch(hipStream_t s, int n, int V, int M, int L, const float *logits,
+                              int64_t ldl, const int32_t *cluster_of, uint8_t *labels);
+size_t router_train_ws_bytes(int n, int r, int M);
+hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int act, bool h_bf16,
+                               const void *h, int64_t ldh, const uint8_t *labels, float lr,
+                               float *W1, float *b1, float *W2, float *b2, float *dW1,
+                               float *db1, float *dW2, float *db2, double *loss, void *ws);
+
 size_t verify_tree_ws_bytes(int B, int m, int V, int64_t max_len);
 hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
                               const int32_t *token, const int64_t *sl_off, const int32_t *sl_ids,

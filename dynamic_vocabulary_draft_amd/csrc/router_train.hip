@@ -1,0 +1,435 @@
+// Router training (DynaSpec summary page, "Modeling": the router is trained
+// by supervised multi-label classification, binary cross entropy over the
+// clusters, a cluster's label being positive when it holds a token from the
+// top-L of the full drafter; the trainable part is the 2-layer MLP).
+//
+// Labels: one workgroup per training row selects the row's top-L tokens of
+// the full drafter's logits (logit descending, token id ascending) with a
+// four-pass radix select on order-preserving 32-bit keys (per-wave LDS
+// histograms of one byte per pass), then marks the clusters of the selected
+// tokens.  Ties at the L-th key are resolved by id with a block scan, which
+// only runs when the tie is split.
+//
+// Training step (fp32 parameters, fp32 arithmetic): a 64 x 64-tile GEMM
+// kernel (256 threads, 4 x 4 outputs per thread, 16-deep k slices staged in
+// LDS, every output summed in ascending k order) with a fused epilogue per
+// product:
+//   a = h W1^T + b1, z = act(a)        (epilogue keeps a and z)
+//   s = z W2^T + b2                    (then g_s = (sigmoid(s) - y)/(n M) and
+//                                       the loss, summed in fp64 in a fixed order)
+//   g_a = (g_s W2) * act'(a)           (before W2 moves)
+//   dW2 = g_s^T z, W2 -= lr dW2;  dW1 = g_a^T h, W1 -= lr dW1
+//   db2, db1: column sums of g_s and g_a, then the bias steps.
+// These products are small (inner sizes n, r or d up to a few thousand) and
+// run on the vector ALUs; the dense logits that feed the labels come from
+// the gathered head with the whole vocabulary as the shortlist.
+#include <limits.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace ds {
+namespace {
+
+// ------------------------------------------------------------------ labels
+constexpr int kLabThreads = 1024;
+constexpr int kLabWaves = kLabThreads / kWave;
+
+// larger float -> larger key; -0 and +0 are one value, as in a float compare
+__device__ __forceinline__ uint32_t order_key(float x)
+{
+    const uint32_t u = __float_as_uint(x == 0.0f ? 0.0f : x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(kLabThreads) void topl_labels_kernel(int V, int M, int L,
+                                                                 const float *__restrict__ logits,
+                                                                 int64_t ldl,
+                                                                 const int32_t *__restrict__ cluster_of,
+                                                                 uint8_t *__restrict__ labels)
+{
+    __shared__ uint32_t hist[kLabWaves][256];
+    __shared__ uint32_t s_tot[256];
+    __shared__ uint8_t s_lab[DS_MAX_CLUSTERS];
+    __shared__ uint32_t s_sel[4];  // prefix, need (rank within the equal keys), equal count
+    __shared__ int s_wsum[kLabWaves];
+    const int row = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const float *lg = logits + (int64_t)row * ldl;
+    for (int c = tid; c < M; c += kLabThreads)
+        s_lab[c] = 0;
+    const int Lc = min(L, V);
+    if (Lc > 0) {
+        // radix select of the Lc-th largest key, one byte per pass
+        uint32_t prefix = 0, mask = 0, need = (uint32_t)Lc;
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            for (int i = tid; i < kLabWaves * 256; i += kLabThreads)
+                (&hist[0][0])[i] = 0u;
+            __syncthreads();
+            constexpr int U = 8;
+            for (int y0 = tid; y0 < V; y0 += kLabThreads * U) {
+                uint32_t k[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    k[u] = order_key(lg[min(y0 + u * kLabThreads, V - 1)]);
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (y0 + u * kLabThreads < V && (k[u] & mask) == prefix)
+                        atomicAdd(&hist[wave][(k[u] >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid < 256) {
+                uint32_t t = 0;
+#pragma unroll
+                for (int w = 0; w < kLabWaves; ++w)
+                    t += hist[w][tid];
+                s_tot[tid] = t;
+            }
+            __syncthreads();
+            if (tid == 0) {  // the digit holding the need-th largest key
+                uint32_t cum = 0;
+                int digit = 0;
+                for (int b = 255; b >= 0; --b) {
+                    if (cum + s_tot[b] >= need) {
+                        digit = b;
+                        break;
+                    }
+                    cum += s_tot[b];
+                }
+                s_sel[0] = prefix | ((uint32_t)digit << shift);
+                s_sel[1] = need - cum;
+                s_sel[2] = s_tot[digit];
+            }
+            __syncthreads();
+            prefix = s_sel[0];
+            need = s_sel[1];
+            mask |= 0xFFu << shift;
+        }
+        const uint32_t K = prefix, n_eq = s_sel[2];
+        // every key above K is taken; of the n_eq keys equal to K the first
+        // `need` by token id
+        if (need >= n_eq) {
+            for (int y = tid; y < V; y += kLabThreads)
+                if (order_key(lg[y]) >= K) {
+                    const int32_t c = cluster_of[y];
+                    if (c >= 0 && c < M)
+                        s_lab[c] = 1;
+                }
+        } else {
+            int carry = 0;  // equal keys at ids below this chunk
+            for (int y0 = 0; y0 < V; y0 += kLabThreads) {
+                const int y = y0 + tid;
+                const uint32_t k = y < V ? order_key(lg[y]) : 0u;
+                const bool eq = y < V && k == K;
+                const uint64_t bal = __ballot(eq);
+                const int below = __popcll(bal & ((1ull << lane) - 1ull));
+                if (lane == 0)
+                    s_wsum[wave] = __popcll(bal);
+                __syncthreads();
+                int before = carry;
+                for (int w = 0; w < wave; ++w)
+                    before += s_wsum[w];
+                int tot = 0;
+                for (int w = 0; w < kLabWaves; ++w)
+                    tot += s_wsum[w];
+                if (y < V && (k > K || (eq && (uint32_t)(before + below) < need))) {
+                    const int32_t c = cluster_of[y];
+                    if (c >= 0 && c < M)
+                        s_lab[c] = 1;
+                }
+                carry += tot;
+                __syncthreads();
+            }
+        }
+    }
+    __syncthreads();
+    uint8_t *out = labels + (int64_t)row * M;
+    for (int c = tid; c < M; c += kLabThreads)
+        out[c] = s_lab[c];
+}
+
+// -------------------------------------------------------------- fp32 GEMM
+constexpr int kGT = 64;   // output tile edge
+constexpr int kGK = 16;   // k slice
+
+// element of an fp32 array, or of bf16 bits widened exactly
+__device__ __forceinline__ float ld_f(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_f(const uint16_t *p, int64_t i) { return bf16_lo((uint32_t)p[i]); }
+
+// C[m][n] = sum_k A(m, k) B(k, n) with A(m, k) = A[m*sam + k*sak] and
+// B(k, n) = B[k*sbk + n*sbn]; the epilogue consumes each C entry.
+template <class TA, class TB, class Epi>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(int Mr, int Nc, int K, const TA *__restrict__ A,
+                                                       int64_t sam, int64_t sak,
+                                                       const TB *__restrict__ B, int64_t sbk,
+                                                       int64_t sbn, Epi epi)
+{
+    __shared__ float As[kGK][kGT + 4];
+    __shared__ float Bs[kGK][kGT + 4];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int m0 = blockIdx.y * kGT, n0 = blockIdx.x * kGT;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += kGK) {
+        // 64 x 16 of A and 16 x 64 of B, four elements of each per thread
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = tid + 256 * u;
+            const int am = e >> 4, ak = e & 15;        // A: m-major pieces
+            const int bk = e >> 6, bn = e & 63;        // B: n-major pieces
+            const int gm = m0 + am, gk = k0 + ak;
+            As[ak][am] = (gm < Mr && gk < K) ? ld_f(A, gm * sam + gk * sak) : 0.0f;
+            const int gk2 = k0 + bk, gn = n0 + bn;
+            Bs[bk][bn] = (gk2 < K && gn < Nc) ? ld_f(B, gk2 * sbk + gn * sbn) : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kGK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = As[kk][ty * 4 + i];
+                b[i] = Bs[kk][tx * 4 + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+            if (m < Mr && n < Nc)
+                epi(m, n, acc[i][j]);
+        }
+}
+
+__device__ __forceinline__ float sigmoidf_(float x)
+{
+    if (x >= 0.0f)
+        return 1.0f / (1.0f + expf(-x));
+    const float e = expf(x);
+    return e / (1.0f + e);
+}
+
+__device__ __forceinline__ float act_f(int act, float x)
+{
+    return act == DS_RELU ? fmaxf(x, 0.0f) : x * sigmoidf_(x);
+}
+
+__device__ __forceinline__ float act_grad_f(int act, float x)
+{
+    if (act == DS_RELU)
+        return x > 0.0f ? 1.0f : 0.0f;
+    const float s = sigmoidf_(x);
+    return s * (1.0f + x * (1.0f - s));
+}
+
+struct EpiFwd1 {  // a = acc + b1, z = act(a)
+    const float *b1;
+    float *a, *z;
+    int r, act;
+    __device__ void operator()(int i, int j, float v) const
+    {
+        v += b1[j];
+        a[(int64_t)i * r + j] = v;
+        z[(int64_t)i * r + j] = act_f(act, v);
+    }
+};
+
+struct EpiFwd2 {  // s = acc + b2
+    const float *b2;
+    float *s;
+    int M;
+    __device__ void operator()(int i, int c, float v) const { s[(int64_t)i * M + c] = v + b2[c]; }
+};
+
+struct EpiGa {  // g_a = acc * act'(a)
+    const float *a;
+    float *ga;
+    int r, act;
+    __device__ void operator()(int i, int j, float v) const
+    {
+        ga[(int64_t)i * r + j] = v * act_grad_f(act, a[(int64_t)i * r + j]);
+    }
+};
+
+struct EpiStep {  // grad = acc, param -= lr * grad
+    float *grad, *param;
+    float lr;
+    int ld;
+    __device__ void operator()(int m, int n, float v) const
+    {
+        const int64_t e = (int64_t)m * ld + n;
+        grad[e] = v;
+        param[e] -= lr * v;
+    }
+};
+
+// g_s = (sigmoid(s) - y) / (n M) in place; per-block fp64 loss partials of
+// softplus(s) - y s (fixed association: thread, then wave, then block order)
+constexpr int kBceThreads = 256;
+__global__ __launch_bounds__(kBceThreads) void bce_kernel(int64_t total, float inv,
+                                                           const uint8_t *__restrict__ y,
+                                                           float *__restrict__ s,
+                                                           double *__restrict__ part)
+{
+    __shared__ double sw[kBceThreads / kWave];
+    double acc = 0.0;
+    const int64_t stride = (int64_t)gridDim.x * kBceThreads;
+    for (int64_t e = (int64_t)blockIdx.x * kBceThreads + threadIdx.x; e < total; e += stride) {
+        const float v = s[e];
+        const double yv = y[e] ? 1.0 : 0.0;
+        const double dv = (double)v;
+        acc += (dv > 0.0 ? dv : 0.0) + log1p(exp(-fabs(dv))) - yv * dv;
+        s[e] = (sigmoidf_(v) - (float)yv) * inv;
+    }
+    acc = wave_sum_f64(acc);
+    if (lane_id() == 0)
+        sw[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        for (int w = 0; w < kBceThreads / kWave; ++w)
+            t += sw[w];
+        part[blockIdx.x] = t;
+    }
+}
+
+__global__ void loss_final_kernel(int nparts, double inv, const double *__restrict__ part,
+                                  double *__restrict__ loss)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        double t = 0.0;
+        for (int i = 0; i < nparts; ++i)
+            t += part[i];
+        *loss = t * inv;
+    }
+}
+
+// column sums of X [rows][cols] (ascending rows), written as the gradient;
+// the bias steps by -lr times it
+__global__ __launch_bounds__(256) void colsum_step_kernel(int rows, int cols,
+                                                          const float *__restrict__ X,
+                                                          float *__restrict__ grad,
+                                                          float *__restrict__ bias, float lr)
+{
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= cols)
+        return;
+    float t = 0.0f;
+    for (int i = 0; i < rows; ++i)
+        t += X[(int64_t)i * cols + c];
+    grad[c] = t;
+    bias[c] -= lr * t;
+}
+
+constexpr int kBceBlocks = 256;
+
+struct TrainWs {
+    float *a, *z, *s, *ga;
+    double *part;
+};
+
+inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+TrainWs train_ws(void *ws, int n, int r, int M)
+{
+    char *p = reinterpret_cast<char *>(ws);
+    TrainWs w;
+    const size_t nr = al256((size_t)n * r * 4), nm = al256((size_t)n * M * 4);
+    w.a = reinterpret_cast<float *>(p);
+    w.z = reinterpret_cast<float *>(p + nr);
+    w.ga = reinterpret_cast<float *>(p + 2 * nr);
+    w.s = reinterpret_cast<float *>(p + 3 * nr);
+    w.part = reinterpret_cast<double *>(p + 3 * nr + nm);
+    return w;
+}
+
+template <class TA, class TB, class Epi>
+hipError_t gemm(hipStream_t s, int Mr, int Nc, int K, const TA *A, int64_t sam, int64_t sak,
+                const TB *B, int64_t sbk, int64_t sbn, Epi epi)
+{
+    dim3 grid((unsigned)((Nc + kGT - 1) / kGT), (unsigned)((Mr + kGT - 1) / kGT));
+    hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, Epi>), grid, dim3(256), 0, s, Mr, Nc, K, A, sam,
+                       sak, B, sbk, sbn, epi);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t topl_labels_launch(hipStream_t s, int n, int V, int M, int L, const float *logits,
+                              int64_t ldl, const int32_t *cluster_of, uint8_t *labels)
+{
+    hipLaunchKernelGGL(topl_labels_kernel, dim3((unsigned)n), dim3(kLabThreads), 0, s, V, M, L,
+                       logits, ldl, cluster_of, labels);
+    return hipGetLastError();
+}
+
+size_t router_train_ws_bytes(int n, int r, int M)
+{
+    return 3 * al256((size_t)n * r * 4) + al256((size_t)n * M * 4) +
+           al256((size_t)kBceBlocks * 8) + 256;
+}
+
+hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int act, bool h_bf16,
+                               const void *h, int64_t ldh, const uint8_t *labels, float lr,
+                               float *W1, float *b1, float *W2, float *b2, float *dW1,
+                               float *db1, float *dW2, float *db2, double *loss, void *ws)
+{
+    TrainWs w = train_ws(ws, n, r, M);
+    hipError_t e;
+    // a = h W1^T + b1, z = act(a): A = h [n][d], B(k, j) = W1[j][k]
+    if (h_bf16)
+        e = gemm(s, n, r, d, reinterpret_cast<const uint16_t *>(h), ldh, (int64_t)1, W1,
+                 (int64_t)1, (int64_t)d, EpiFwd1{b1, w.a, w.z, r, act});
+    else
+        e = gemm(s, n, r, d, reinterpret_cast<const float *>(h), ldh, (int64_t)1, W1,
+                 (int64_t)1, (int64_t)d, EpiFwd1{b1, w.a, w.z, r, act});
+    if (e != hipSuccess)
+        return e;
+    // s = z W2^T + b2
+    if ((e = gemm(s, n, M, r, (const float *)w.z, (int64_t)r, (int64_t)1, W2, (int64_t)1,
+                  (int64_t)r, EpiFwd2{b2, w.s, M})) != hipSuccess)
+        return e;
+    const int64_t total = (int64_t)n * M;
+    const double inv = 1.0 / ((double)n * (double)M);
+    hipLaunchKernelGGL(bce_kernel, dim3(kBceBlocks), dim3(kBceThreads), 0, s, total, (float)inv,
+                       labels, w.s, w.part);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(64), 0, s, kBceBlocks, inv,
+                       (const double *)w.part, loss);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    // g_a = (g_s W2) * act'(a), with W2 before its step
+    if ((e = gemm(s, n, r, M, (const float *)w.s, (int64_t)M, (int64_t)1, W2, (int64_t)r,
+                  (int64_t)1, EpiGa{w.a, w.ga, r, act})) != hipSuccess)
+        return e;
+    // dW2[c][j] = sum_i g_s[i][c] z[i][j]
+    if ((e = gemm(s, M, r, n, (const float *)w.s, (int64_t)1, (int64_t)M, w.z, (int64_t)r,
+                  (int64_t)1, EpiStep{dW2, W2, lr, r})) != hipSuccess)
+        return e;
+    // dW1[j][k] = sum_i g_a[i][j] h[i][k]
+    if (h_bf16)
+        e = gemm(s, r, d, n, (const float *)w.ga, (int64_t)1, (int64_t)r,
+                 reinterpret_cast<const uint16_t *>(h), ldh, (int64_t)1, EpiStep{dW1, W1, lr, d});
+    else
+        e = gemm(s, r, d, n, (const float *)w.ga, (int64_t)1, (int64_t)r,
+                 reinterpret_cast<const float *>(h), ldh, (int64_t)1, EpiStep{dW1, W1, lr, d});
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(colsum_step_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, n,
+                       M, (const float *)w.s, db2, b2, lr);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(colsum_step_kernel, dim3((unsigned)((r + 255) / 256)), dim3(256), 0, s, n,
+                       r, (const float *)w.ga, db1, b1, lr);
+    return hipGetLastError();
+}
+
+}  // namespace ds

@@ -30,6 +30,15 @@ class DynaspecError(RuntimeError):
         self.code = code
 
 
+class RouterTrainArgs(C.Structure):
+    """Mirror of ds_router_train_args."""
+    _fields_ = [("n", _i), ("d", _i), ("r", _i), ("M", _i), ("act", _i), ("h_dtype", _i),
+                ("h", _vp), ("ldh", _i64), ("labels", _vp), ("lr", _f),
+                ("W1", _vp), ("b1", _vp), ("W2", _vp), ("b2", _vp),
+                ("dW1", _vp), ("db1", _vp), ("dW2", _vp), ("db2", _vp),
+                ("loss", _vp), ("ws", _vp), ("ws_bytes", _sz)]
+
+
 class ChainArgs(C.Structure):
     """Mirror of ds_draft_chain_args."""
     _fields_ = [("B", _i), ("T", _i), ("V", _i), ("d", _i), ("r", _i), ("M", _i),
@@ -78,6 +87,9 @@ _SIGS = {
     "ds_verify_tree_workspace_bytes": (_sz, [_i, _i, _i, _i64]),
     "ds_verify_tree": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
                             _vp, _vp, _vp, _sz]),
+    "ds_router_labels": (_i, [_vp, _i, _i, _i, _i, _vp, _i64, _vp, _vp]),
+    "ds_router_train_workspace_bytes": (_sz, [_i, _i, _i]),
+    "ds_router_train_step": (_i, [_vp, C.POINTER(RouterTrainArgs)]),
     "ds_draft_chain_workspace_bytes": (_sz, [_i, _i, _i, _i, _i64]),
     "ds_draft_chain": (_i, [_vp, _vp, C.POINTER(ChainArgs)]),
     "ds_capture_begin": (_i, [_vp]),
@@ -315,6 +327,31 @@ def verify_tree(parent, token, sl_off, sl_ids, q, p, u_acc, u_fin, max_len, n_ac
         _s(stream), B, m, V, _p(parent), _p(token), _p(sl_off), _p(sl_ids), _p(q), _p(p),
         _p(u_acc), _p(u_fin), int(max_len), _p(n_acc), _p(out), _p(path), _p(ws),
         _nbytes(ws)))
+
+
+def router_labels(logits, cluster_of, M: int, L: int, labels, *, stream=None):
+    """labels [n][M] uint8 from the full drafter's logits [n][V] (fp32)."""
+    n, V = logits.shape
+    _check("ds_router_labels", lib.ds_router_labels(_s(stream), n, V, M, L, _p(logits),
+                                                    _ld(logits), _p(cluster_of), _p(labels)))
+
+
+def router_train_workspace_bytes(n: int, r: int, M: int) -> int:
+    return int(lib.ds_router_train_workspace_bytes(n, r, M))
+
+
+def router_train_step(h, labels, W1, b1, W2, b2, grads, loss, act: int, lr: float, ws, *,
+                      stream=None):
+    """One SGD step; W1, b1, W2, b2 (fp32) are updated in place; grads is a
+    dict of fp32 tensors W1, b1, W2, b2; loss a 1-element float64 tensor."""
+    n, d = h.shape
+    r, M = W1.shape[0], W2.shape[0]
+    a = RouterTrainArgs(n=n, d=d, r=r, M=M, act=act, h_dtype=_dt(h), h=_p(h), ldh=_ld(h),
+                        labels=_p(labels), lr=float(lr), W1=_p(W1), b1=_p(b1), W2=_p(W2),
+                        b2=_p(b2), dW1=_p(grads["W1"]), db1=_p(grads["b1"]),
+                        dW2=_p(grads["W2"]), db2=_p(grads["b2"]), loss=_p(loss), ws=_p(ws),
+                        ws_bytes=_nbytes(ws))
+    _check("ds_router_train_step", lib.ds_router_train_step(_s(stream), C.byref(a)))
 
 
 def draft_chain(args: ChainArgs, head_stream=None, router_stream=None):

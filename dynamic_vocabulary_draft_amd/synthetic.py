@@ -11,7 +11,7 @@ Streams: 0 centroids, 1 noise (one sub-stream per block of ``ROW_BLOCK`` rows),
 instance), 8 target logits, 9 draft uniforms, 10 accept uniforms, 11 final
 uniforms (9-11 also take the instance), 12 token frequency ranking (the
 order a fixed, frequency-ranked shortlist takes tokens in), 13 initial
-k-means labels.
+k-means labels, 14 router-training hidden states (sub-stream = instance).
 
 The workload shapes stand in for the pages' Llama-3-8B, Qwen3-8B and
 Gemma-3-12B drafting set-ups (DynaSpec summary page, "Evaluation Setup" and
@@ -189,6 +189,14 @@ def make_hidden(cfg: Config, instance: int = 0) -> np.ndarray:
     rows = (1 + cfg.tree_nodes) if cfg.is_tree else (cfg.T + 1)
     h = rng(cfg.index, 7, instance).standard_normal((cfg.B, rows, cfg.d), dtype=np.float32)
     return _store(h, cfg.dtype)
+
+
+def make_train_hidden(cfg: Config, n: int, instance: int = 0) -> np.ndarray:
+    """n router-training inputs h ~ N(0, 1), [n][d] in the config's dtype
+    (drafter hidden states; the pages train on the drafter's states of
+    ShareGPT/UltraChat prompts, which are not available)."""
+    g = rng(cfg.index, 14, instance)
+    return _store(g.standard_normal((n, cfg.d), dtype=np.float32), cfg.dtype)
 
 
 def frequency_rank(cfg: Config) -> np.ndarray:

@@ -348,6 +348,53 @@ ds_status ds_verify_tree(hipStream_t s, int B, int m, int V, const int32_t *pare
                          size_t ws_bytes);
 
 /*
+ * Router training labels [S "Modeling": binary cross entropy over clusters,
+ * a cluster's label positive when it holds a token in the top-L of the full
+ * drafter].  Row i of logits (V fp32 values of the full drafter -- the dense
+ * head over all V, e.g. ds_gathered_lm_head with the shortlist 0..V-1 --
+ * row stride ldl) orders its tokens by (logit desc, id asc); the first
+ * min(L, V) are its top-L; labels[i][c] = 1 iff one of them lies in cluster
+ * c, else 0 (ids whose cluster is outside [0, M) mark nothing).  NaN logits
+ * are invalid input.  labels [n][M] uint8.  One workgroup per row, no
+ * workspace.  Limits: 1 <= M <= DS_MAX_CLUSTERS, L >= 0, V >= 1.
+ */
+ds_status ds_router_labels(hipStream_t s, int n, int V, int M, int L, const float *logits,
+                           int64_t ldl, const int32_t *cluster_of, uint8_t *labels);
+
+/*
+ * One plain SGD step of the router on a batch [S "Modeling": supervised
+ * multi-label classification, binary cross entropy over clusters; the
+ * router is the 2-layer MLP of ds_router_score]:
+ *   a = W1 h + b1, z = act(a), s = W2 z + b2
+ *   loss = 1/(n M) sum_{i,c} [log(1 + e^s_ic) - y_ic s_ic]
+ *   g_s = (sigmoid(s) - y)/(n M); dW2 = g_s^T z, db2 = sum_i g_s;
+ *   g_a = (g_s W2) * act'(a) (ReLU' = 0 at 0); dW1 = g_a^T h, db1 = sum_i g_a
+ *   every parameter p <- p - lr * dp (all gradients from the old values).
+ * Fields: h [n][d] (row stride ldh) in h_dtype (fp32 or bf16 bits); labels
+ * [n][M] uint8 (0 or 1); W1 [r][d], b1 [r], W2 [M][r], b2 [M] fp32, updated
+ * in place; dW1, db1, dW2, db2 fp32 gradient outputs of the same shapes;
+ * loss one double; every pointer device memory.  Arithmetic fp32 (products
+ * summed in ascending index order), the loss summed in fp64; results are
+ * reproducible bit for bit.  ws >= ds_router_train_workspace_bytes(n, r, M).
+ */
+typedef struct {
+    int n, d, r, M;
+    ds_act act;
+    ds_dtype h_dtype;
+    const void *h;
+    int64_t ldh;
+    const uint8_t *labels;
+    float lr;
+    float *W1, *b1, *W2, *b2;
+    float *dW1, *db1, *dW2, *db2;
+    double *loss;
+    void *ws;
+    size_t ws_bytes;
+} ds_router_train_args;
+size_t ds_router_train_workspace_bytes(int n, int r, int M);
+ds_status ds_router_train_step(hipStream_t s, const ds_router_train_args *a);
+
+/*
  * One chain-drafting step over T positions for B sequences, with the router
  * on its own stream, overlapped with the head [A: routing is overlapped with
  * draft computation via parallel execution streams; S "Novel Architectural
