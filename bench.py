@@ -337,6 +337,132 @@ def kmeans_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def router_train_bench(args):
+    """Router training at the workload's shape: per step, the full drafter's
+    logits for n training rows (the gathered head over the whole vocabulary),
+    their top-L cluster labels, and one SGD step of the router; input batches
+    rotate over four instances."""
+    import numpy as np
+    import torch
+
+    from dynamic_vocabulary_draft_amd import native as N
+    from dynamic_vocabulary_draft_amd import synthetic as syn
+    from dynamic_vocabulary_draft_amd.pipeline import to_dev
+
+    torch.cuda.set_device(0)
+    cfg = syn.CONFIGS[args.config]
+    if cfg.dtype != syn.DT_BF16:
+        raise SystemExit("--router-train needs a bf16 head")
+    V, d, r, M = cfg.V, cfg.d, cfg.r, cfg.M
+    n, L = args.train_rows, args.train_top
+    cluster_of, _ = syn.make_clusters(cfg)
+    W_host = syn.make_lm_head(cfg, cluster_of, threads=min(16, os.cpu_count() or 8))
+    W = to_dev(W_host)
+    R = syn.make_router(cfg)
+    f32 = {k: syn.bf16_bits_to_f32(v) for k, v in R.items()}  # fp32 master weights
+    P = {k: to_dev(v) for k, v in f32.items()}
+    G = {k: torch.empty_like(v) for k, v in P.items()}
+    hs = [to_dev(syn.make_train_hidden(cfg, n, instance=i)) for i in range(4)]
+    co = to_dev(cluster_of)
+    sl_off = torch.tensor([0, V], dtype=torch.int64, device="cuda")
+    sl_ids = torch.arange(V, dtype=torch.int32, device="cuda")
+    logits = torch.empty(n * V, device="cuda")
+    labels = torch.empty(n, M, dtype=torch.uint8, device="cuda")
+    loss = torch.empty(1, dtype=torch.float64, device="cuda")
+    hws = N.workspace(N.head_workspace_bytes(1, n, V))
+    tws = N.workspace(N.router_train_workspace_bytes(n, r, M))
+    ev = HipEvents()
+    lr = 0.05
+
+    def step(k, events=None):
+        h = hs[k % len(hs)]
+        N.gathered_lm_head(W, h[None], sl_off, sl_ids, V, logits, hws, events=events)
+        N.router_labels(logits.view(n, V), co, M, L, labels)
+        N.router_train_step(h, labels, P["W1"], P["b1"], P["W2"], P["b2"], G, loss, cfg.act, lr,
+                            tws)
+
+    for k in range(max(args.warmup, 4)):
+        step(k)
+    torch.cuda.synchronize()
+    losses = [float(loss.item())]
+    steps = args.steps
+    evs = ev.array(2 * steps)
+    t_lab = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        h = hs[k % len(hs)]
+        N.gathered_lm_head(W, h[None], sl_off, sl_ids, V, logits, hws,
+                           events=(evs[2 * k], evs[2 * k + 1]))
+        t_lab[3 * k].record()
+        N.router_labels(logits.view(n, V), co, M, L, labels)
+        t_lab[3 * k + 1].record()
+        N.router_train_step(h, labels, P["W1"], P["b1"], P["W2"], P["b2"], G, loss, cfg.act, lr,
+                            tws)
+        t_lab[3 * k + 2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    losses.append(float(loss.item()))
+    head_us = float(np.mean([ev.elapsed_ms(evs[2 * k], evs[2 * k + 1]) for k in range(steps)])) * 1e3
+    lab_us = float(np.mean([t_lab[3 * k].elapsed_time(t_lab[3 * k + 1])
+                            for k in range(steps)])) * 1e3
+    trn_us = float(np.mean([t_lab[3 * k + 1].elapsed_time(t_lab[3 * k + 2])
+                            for k in range(steps)])) * 1e3
+    e = cfg.elem_bytes
+    head_bytes = V * d * e + n * d * e + n * V * 4  # W once, the hidden rows, the logits
+    head_flops = 2.0 * n * V * d
+    achieved = head_bytes / (head_us * 1e-6) / 1e9
+    train_flops = 2.0 * n * (2 * r * d + 3 * M * r)
+    out = {
+        "metric": "router training rows/s (full-drafter logits, top-%d cluster labels, one SGD "
+                  "step of the %d->%d->%d router), V=%d d=%d bf16 head" % (L, d, r, M, V, d),
+        "value": round(n * steps / wall, 1), "unit": "training rows/s", "n_gpus": 1,
+        "steps": steps, "warmup": max(args.warmup, 4), "ms_per_step": round(wall * 1e3 / steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: clustered-Gaussian head, N(0,1) training hidden states (4 batches "
+                "rotated), router initialised as the drafting router",
+        "config": {"workload": "router training on the %s head, %d rows per step" % (cfg.name, n),
+                   "V": V, "d": d, "router": "%d->%d->%d" % (d, r, M), "rows": n, "top_L": L,
+                   "lr": lr},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "dense_head": {"kernel": head_kernel_name(syn.shrink(cfg, B=1, tree_nodes=n)),
+                       "mean_us": round(head_us, 1), "algorithmic_bytes": head_bytes,
+                       "tflops": round(head_flops / (head_us * 1e-6) / 1e12, 1),
+                       "mfma_frac": round(head_flops / (head_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                                          4),
+                       "passes_over_W": (n + 63) // 64},
+        "labels_us": round(lab_us, 1),
+        "train_step": {"mean_us": round(trn_us, 1), "flops": train_flops,
+                       "tflops_fp32": round(train_flops / (trn_us * 1e-6) / 1e12, 2)},
+        "loss": {"before": losses[0], "after": losses[1]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        rows = 2
+        hh = syn.make_train_hidden(cfg, rows)
+        t1 = time.perf_counter()
+        lg = oracle.dense_lm_head(W_host, hh)
+        lab = oracle.topl_labels(lg, cluster_of, M, L)
+        t_lab_rows = time.perf_counter() - t1
+        nt = 8
+        ht = syn.bf16_bits_to_f32(syn.make_train_hidden(cfg, nt))
+        yt = np.zeros((nt, M), np.uint8)
+        yt[:rows] = lab
+        t1 = time.perf_counter()
+        oracle.router_train_step(ht, yt, f32["W1"], f32["b1"], f32["W2"], f32["b2"], cfg.act, lr)
+        t_step = time.perf_counter() - t1
+        per_row = t_lab_rows / rows + t_step / nt
+        out["cpu_baseline"] = {
+            "value": round(1.0 / per_row, 4), "unit": "training rows/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "dense logits + labels of %d rows (%.1f s) and one step on %d rows "
+                      "(%.1f s), 1 thread; per-row costs added" % (rows, t_lab_rows, nt, t_step)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +489,10 @@ def main():
     ap.add_argument("--kmeans", action="store_true",
                     help="time spherical k-means iterations over the workload's LM head instead")
     ap.add_argument("--kmeans-iters", type=int, default=5)
+    ap.add_argument("--router-train", action="store_true",
+                    help="time router training steps (labels from the dense head + SGD)")
+    ap.add_argument("--train-rows", type=int, default=256)
+    ap.add_argument("--train-top", type=int, default=64)
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying step graphs")
     args = ap.parse_args()
@@ -374,6 +504,11 @@ def main():
             print("bench.py measures one GPU only", file=sys.stderr)
             sys.exit(2)
         return kmeans_bench(args)
+    if args.router_train:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        return router_train_bench(args)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

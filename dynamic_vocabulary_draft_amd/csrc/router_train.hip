@@ -12,8 +12,9 @@
 //
 // Training step (fp32 parameters, fp32 arithmetic): a 64 x 64-tile GEMM
 // kernel (256 threads, 4 x 4 outputs per thread, 16-deep k slices staged in
-// LDS, every output summed in ascending k order) with a fused epilogue per
-// product:
+// LDS, every output summed in ascending k order; the first layer, whose
+// output is small and whose k = d is long, splits k in eight and adds the
+// splits in order) with a fused epilogue per product:
 //   a = h W1^T + b1, z = act(a)        (epilogue keeps a and z)
 //   s = z W2^T + b2                    (then g_s = (sigmoid(s) - y)/(n M) and
 //                                       the loss, summed in fp64 in a fixed order)
@@ -158,18 +159,23 @@ __device__ __forceinline__ float ld_f(const uint16_t *p, int64_t i) { return bf1
 
 // C[m][n] = sum_k A(m, k) B(k, n) with A(m, k) = A[m*sam + k*sak] and
 // B(k, n) = B[k*sbk + n*sbn]; the epilogue consumes each C entry.
+// Split K: blockIdx.z takes k in [z*kchunk, min((z+1)*kchunk, K)) and, with
+// more than one split, writes its partial tile to part[z][Mr][Nc] instead of
+// calling the epilogue (a second kernel adds the splits in z order).
 template <class TA, class TB, class Epi>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(int Mr, int Nc, int K, const TA *__restrict__ A,
                                                        int64_t sam, int64_t sak,
                                                        const TB *__restrict__ B, int64_t sbk,
-                                                       int64_t sbn, Epi epi)
+                                                       int64_t sbn, Epi epi, int kchunk,
+                                                       float *__restrict__ part)
 {
     __shared__ float As[kGK][kGT + 4];
     __shared__ float Bs[kGK][kGT + 4];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int m0 = blockIdx.y * kGT, n0 = blockIdx.x * kGT;
+    const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
     float acc[4][4] = {};
-    for (int k0 = 0; k0 < K; k0 += kGK) {
+    for (int k0 = kb; k0 < ke; k0 += kGK) {
         // 64 x 16 of A and 16 x 64 of B, four elements of each per thread
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -177,9 +183,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int Mr, int Nc, int K, co
             const int am = e >> 4, ak = e & 15;        // A: m-major pieces
             const int bk = e >> 6, bn = e & 63;        // B: n-major pieces
             const int gm = m0 + am, gk = k0 + ak;
-            As[ak][am] = (gm < Mr && gk < K) ? ld_f(A, gm * sam + gk * sak) : 0.0f;
+            As[ak][am] = (gm < Mr && gk < ke) ? ld_f(A, gm * sam + gk * sak) : 0.0f;
             const int gk2 = k0 + bk, gn = n0 + bn;
-            Bs[bk][bn] = (gk2 < K && gn < Nc) ? ld_f(B, gk2 * sbk + gn * sbn) : 0.0f;
+            Bs[bk][bn] = (gk2 < ke && gn < Nc) ? ld_f(B, gk2 * sbk + gn * sbn) : 0.0f;
         }
         __syncthreads();
 #pragma unroll
@@ -203,9 +209,27 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int Mr, int Nc, int K, co
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
-            if (m < Mr && n < Nc)
-                epi(m, n, acc[i][j]);
+            if (m < Mr && n < Nc) {
+                if (gridDim.z > 1)
+                    part[((int64_t)blockIdx.z * Mr + m) * Nc + n] = acc[i][j];
+                else
+                    epi(m, n, acc[i][j]);
+            }
         }
+}
+
+// the split-K partials added in split order, then the epilogue
+template <class Epi>
+__global__ __launch_bounds__(256) void splitk_sum_kernel(int Mr, int Nc, int splits,
+                                                         const float *__restrict__ part, Epi epi)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)Mr * Nc)
+        return;
+    float t = part[e];
+    for (int z = 1; z < splits; ++z)
+        t += part[(int64_t)z * Mr * Nc + e];
+    epi((int)(e / Nc), (int)(e % Nc), t);
 }
 
 __device__ __forceinline__ float sigmoidf_(float x)
@@ -311,27 +335,40 @@ __global__ void loss_final_kernel(int nparts, double inv, const double *__restri
     }
 }
 
-// column sums of X [rows][cols] (ascending rows), written as the gradient;
-// the bias steps by -lr times it
-__global__ __launch_bounds__(256) void colsum_step_kernel(int rows, int cols,
-                                                          const float *__restrict__ X,
-                                                          float *__restrict__ grad,
-                                                          float *__restrict__ bias, float lr)
+// column sums of X [rows][cols], written as the gradient; the bias steps
+// by -lr times it.  A workgroup owns 64 columns; thread (q, c) sums the rows
+// q, q + 16, q + 32, ... of column c, and the 16 partials are added in q
+// order (a fixed association).
+constexpr int kColQ = 16;
+__global__ __launch_bounds__(64 * kColQ) void colsum_step_kernel(int rows, int cols,
+                                                                 const float *__restrict__ X,
+                                                                 float *__restrict__ grad,
+                                                                 float *__restrict__ bias, float lr)
 {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= cols)
-        return;
+    __shared__ float part[kColQ][64];
+    const int cl = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + cl;
     float t = 0.0f;
-    for (int i = 0; i < rows; ++i)
-        t += X[(int64_t)i * cols + c];
-    grad[c] = t;
-    bias[c] -= lr * t;
+    if (c < cols)
+        for (int i = q; i < rows; i += kColQ)
+            t += X[(int64_t)i * cols + c];
+    part[q][cl] = t;
+    __syncthreads();
+    if (q == 0 && c < cols) {
+        float s = part[0][cl];
+        for (int k = 1; k < kColQ; ++k)
+            s += part[k][cl];
+        grad[c] = s;
+        bias[c] -= lr * s;
+    }
 }
 
 constexpr int kBceBlocks = 256;
 
+constexpr int kSplitK = 8;  // first-layer forward: K = d is long, the output small
+
 struct TrainWs {
-    float *a, *z, *s, *ga;
+    float *a, *z, *s, *ga, *kpart;
     double *part;
 };
 
@@ -347,16 +384,27 @@ TrainWs train_ws(void *ws, int n, int r, int M)
     w.ga = reinterpret_cast<float *>(p + 2 * nr);
     w.s = reinterpret_cast<float *>(p + 3 * nr);
     w.part = reinterpret_cast<double *>(p + 3 * nr + nm);
+    w.kpart = reinterpret_cast<float *>(p + 3 * nr + nm + al256((size_t)kBceBlocks * 8));
     return w;
 }
 
+// splits > 1 needs part >= splits * Mr * Nc floats
 template <class TA, class TB, class Epi>
 hipError_t gemm(hipStream_t s, int Mr, int Nc, int K, const TA *A, int64_t sam, int64_t sak,
-                const TB *B, int64_t sbk, int64_t sbn, Epi epi)
+                const TB *B, int64_t sbk, int64_t sbn, Epi epi, int splits = 1,
+                float *part = nullptr)
 {
-    dim3 grid((unsigned)((Nc + kGT - 1) / kGT), (unsigned)((Mr + kGT - 1) / kGT));
+    const int kchunk = ((K + splits - 1) / splits + kGK - 1) / kGK * kGK;
+    splits = (K + kchunk - 1) / kchunk;
+    dim3 grid((unsigned)((Nc + kGT - 1) / kGT), (unsigned)((Mr + kGT - 1) / kGT), (unsigned)splits);
     hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, Epi>), grid, dim3(256), 0, s, Mr, Nc, K, A, sam,
-                       sak, B, sbk, sbn, epi);
+                       sak, B, sbk, sbn, epi, kchunk, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1)
+        return e;
+    const int64_t total = (int64_t)Mr * Nc;
+    hipLaunchKernelGGL((splitk_sum_kernel<Epi>), dim3((unsigned)((total + 255) / 256)), dim3(256),
+                       0, s, Mr, Nc, splits, (const float *)part, epi);
     return hipGetLastError();
 }
 
@@ -373,7 +421,7 @@ hipError_t topl_labels_launch(hipStream_t s, int n, int V, int M, int L, const f
 size_t router_train_ws_bytes(int n, int r, int M)
 {
     return 3 * al256((size_t)n * r * 4) + al256((size_t)n * M * 4) +
-           al256((size_t)kBceBlocks * 8) + 256;
+           al256((size_t)kBceBlocks * 8) + al256((size_t)kSplitK * n * r * 4) + 256;
 }
 
 hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int act, bool h_bf16,
@@ -386,10 +434,10 @@ hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int ac
     // a = h W1^T + b1, z = act(a): A = h [n][d], B(k, j) = W1[j][k]
     if (h_bf16)
         e = gemm(s, n, r, d, reinterpret_cast<const uint16_t *>(h), ldh, (int64_t)1, W1,
-                 (int64_t)1, (int64_t)d, EpiFwd1{b1, w.a, w.z, r, act});
+                 (int64_t)1, (int64_t)d, EpiFwd1{b1, w.a, w.z, r, act}, kSplitK, w.kpart);
     else
         e = gemm(s, n, r, d, reinterpret_cast<const float *>(h), ldh, (int64_t)1, W1,
-                 (int64_t)1, (int64_t)d, EpiFwd1{b1, w.a, w.z, r, act});
+                 (int64_t)1, (int64_t)d, EpiFwd1{b1, w.a, w.z, r, act}, kSplitK, w.kpart);
     if (e != hipSuccess)
         return e;
     // s = z W2^T + b2
@@ -423,12 +471,12 @@ hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int ac
                  reinterpret_cast<const float *>(h), ldh, (int64_t)1, EpiStep{dW1, W1, lr, d});
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(colsum_step_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, n,
-                       M, (const float *)w.s, db2, b2, lr);
+    hipLaunchKernelGGL(colsum_step_kernel, dim3((unsigned)((M + 63) / 64)), dim3(64 * kColQ), 0, s,
+                       n, M, (const float *)w.s, db2, b2, lr);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(colsum_step_kernel, dim3((unsigned)((r + 255) / 256)), dim3(256), 0, s, n,
-                       r, (const float *)w.ga, db1, b1, lr);
+    hipLaunchKernelGGL(colsum_step_kernel, dim3((unsigned)((r + 63) / 64)), dim3(64 * kColQ), 0, s,
+                       n, r, (const float *)w.ga, db1, b1, lr);
     return hipGetLastError();
 }
 
