@@ -339,8 +339,8 @@ def kmeans_bench(args):
 
 def router_train_bench(args):
     """Router training at the workload's shape: per step, the full drafter's
-    logits for n training rows (the gathered head over the whole vocabulary),
-    their top-L cluster labels, and one SGD step of the router; input batches
+    logits for n training rows (the dense head on the matrix cores), their
+    top-L cluster labels, and one SGD step of the router; input batches
     rotate over four instances."""
     import numpy as np
     import torch
@@ -364,20 +364,17 @@ def router_train_bench(args):
     G = {k: torch.empty_like(v) for k, v in P.items()}
     hs = [to_dev(syn.make_train_hidden(cfg, n, instance=i)) for i in range(4)]
     co = to_dev(cluster_of)
-    sl_off = torch.tensor([0, V], dtype=torch.int64, device="cuda")
-    sl_ids = torch.arange(V, dtype=torch.int32, device="cuda")
-    logits = torch.empty(n * V, device="cuda")
+    logits = torch.empty(n, V, device="cuda")
     labels = torch.empty(n, M, dtype=torch.uint8, device="cuda")
     loss = torch.empty(1, dtype=torch.float64, device="cuda")
-    hws = N.workspace(N.head_workspace_bytes(1, n, V))
     tws = N.workspace(N.router_train_workspace_bytes(n, r, M))
     ev = HipEvents()
     lr = 0.05
 
     def step(k, events=None):
         h = hs[k % len(hs)]
-        N.gathered_lm_head(W, h[None], sl_off, sl_ids, V, logits, hws, events=events)
-        N.router_labels(logits.view(n, V), co, M, L, labels)
+        N.dense_lm_head(W, h, logits, events=events)
+        N.router_labels(logits, co, M, L, labels)
         N.router_train_step(h, labels, P["W1"], P["b1"], P["W2"], P["b2"], G, loss, cfg.act, lr,
                             tws)
 
@@ -392,10 +389,9 @@ def router_train_bench(args):
     t0 = time.perf_counter()
     for k in range(steps):
         h = hs[k % len(hs)]
-        N.gathered_lm_head(W, h[None], sl_off, sl_ids, V, logits, hws,
-                           events=(evs[2 * k], evs[2 * k + 1]))
+        N.dense_lm_head(W, h, logits, events=(evs[2 * k], evs[2 * k + 1]))
         t_lab[3 * k].record()
-        N.router_labels(logits.view(n, V), co, M, L, labels)
+        N.router_labels(logits, co, M, L, labels)
         t_lab[3 * k + 1].record()
         N.router_train_step(h, labels, P["W1"], P["b1"], P["W2"], P["b2"], G, loss, cfg.act, lr,
                             tws)
@@ -426,12 +422,14 @@ def router_train_bench(args):
                    "lr": lr},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
-        "dense_head": {"kernel": head_kernel_name(syn.shrink(cfg, B=1, tree_nodes=n)),
+        "dense_head": {"kernel": "kmeans_assign_kernel<true> (dense head: W x h^T on the "
+                                 "matrix cores, store epilogue)",
                        "mean_us": round(head_us, 1), "algorithmic_bytes": head_bytes,
+                       "algorithmic_flops": head_flops,
+                       "flop_per_byte": round(head_flops / head_bytes, 1),
                        "tflops": round(head_flops / (head_us * 1e-6) / 1e12, 1),
                        "mfma_frac": round(head_flops / (head_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-                                          4),
-                       "passes_over_W": (n + 63) // 64},
+                                          4)},
         "labels_us": round(lab_us, 1),
         "train_step": {"mean_us": round(trn_us, 1), "flops": train_flops,
                        "tflops_fp32": round(train_flops / (trn_us * 1e-6) / 1e12, 2)},

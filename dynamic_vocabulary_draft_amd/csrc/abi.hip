@@ -421,6 +421,18 @@ ds_status ds_verify_tree(hipStream_t s, int B, int m, int V, const int32_t *pare
                                              u_acc, u_fin, max_len, n_acc, out, path, ws));
 }
 
+ds_status ds_dense_lm_head(hipStream_t s, int V, int d, const void *W, int n, const void *h,
+                           float *logits, int64_t ldl, hipEvent_t *events)
+{
+    if (!W || !h || !logits || V <= 0 || d <= 0 || n <= 0 || ldl < V)
+        return DS_EINVAL;
+    if (d % 64 != 0 || d > 8192 || V > (1 << 30) || n > (1 << 20))
+        return DS_ESHAPE;
+    return hip_status(ds::dense_head_launch(s, V, d, W, n, h, logits, ldl,
+                                            events ? events[0] : nullptr,
+                                            events ? events[1] : nullptr));
+}
+
 ds_status ds_router_labels(hipStream_t s, int n, int V, int M, int L, const float *logits,
                            int64_t ldl, const int32_t *cluster_of, uint8_t *labels)
 {

@@ -74,6 +74,9 @@ hipError_t verify_launch(hipStream_t s, int B, int T, int V, const int32_t *draf
                          const float *p, const float *u_acc, const float *u_fin, int32_t *n_acc,
                          int32_t *out, void *ws);
 
+hipError_t dense_head_launch(hipStream_t s, int V, int d, const void *W, int n, const void *h,
+                             float *logits, int64_t ldl, hipEvent_t t0 = nullptr,
+                             hipEvent_t t1 = nullptr);
 hipError_t topl_labels_launch(hipStream_t s, int n, int V, int M, int L, const float *logits,
                               int64_t ldl, const int32_t *cluster_of, uint8_t *labels);
 size_t router_train_ws_bytes(int n, int r, int M);

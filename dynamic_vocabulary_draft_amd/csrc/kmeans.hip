@@ -23,6 +23,9 @@
 //          bits, ~centroid id): the maximum does not depend on the order the
 //          workgroups finish in, so the result is deterministic.  The row
 //          norm does not change the argmax, so the rows are not normalised.
+// dense head: the same contraction with the hidden vectors of the full
+//          drafter as the columns and a plain store epilogue (every logit,
+//          [n][V]); used for the router's training labels.
 // update:  members grouped by cluster in ascending row id without atomics
 //          (per-chunk cluster counts, then a stable scatter: each 4096-row
 //          chunk sorts its (cluster, row) keys in LDS); fp64 sums of
@@ -154,10 +157,15 @@ __device__ __forceinline__ u32x4 frag(const uint16_t *t, int row, int s)
     return *reinterpret_cast<const u32x4 *>(t + row * kSlice + ((p ^ (row & 7)) << 3));
 }
 
+// STORE = false: the assignment (argmax epilogue into best); STORE = true:
+// the plain product, out[c][y] = W[y] . C[c] (row stride ldo), which is the
+// dense LM head when C holds hidden vectors.
+template <bool STORE>
 __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d, const uint16_t *__restrict__ W,
                                                             int M, const uint16_t *__restrict__ C,
                                                             int RT, int CT,
-                                                            unsigned long long *__restrict__ best)
+                                                            unsigned long long *__restrict__ best,
+                                                            float *__restrict__ out, int64_t ldo)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][(kTileR + kTileC) * kSlice];
     const int b = blockIdx.x;
@@ -232,6 +240,23 @@ __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d
 #undef KM_LOAD
     // epilogue: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 of
     // the 32 x 32 tile, column l%32
+    if constexpr (STORE) {
+        // lanes l and l + 32 cover 32 consecutive rows of one column over
+        // their 16 registers, so each column's 128-byte run fills in L2
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int col = wc * 64 + j * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (col < cols && row < rows)
+                        out[(int64_t)(c0 + col) * ldo + y0 + row] = acc[i][j][r];
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -589,9 +614,10 @@ hipError_t kmeans_assign_launch(hipStream_t s, int V, int d, const void *W, int 
         return e;
     const int RT = (V + kTileR - 1) / kTileR, CT = (M + kTileC - 1) / kTileC;
     const int RTp = (RT + 7) / 8 * 8;  // row tiles padded to whole XCD rounds
-    e = launch_timed(kmeans_assign_kernel, dim3((unsigned)((int64_t)RTp * CT)), dim3(kAsgThreads), s, t0, t1,
+    e = launch_timed(kmeans_assign_kernel<false>, dim3((unsigned)((int64_t)RTp * CT)), dim3(kAsgThreads), s, t0, t1,
                      V, d, reinterpret_cast<const uint16_t *>(W), M,
-                     reinterpret_cast<const uint16_t *>(C), RT, CT, best);
+                     reinterpret_cast<const uint16_t *>(C), RT, CT, best, (float *)nullptr,
+                     (int64_t)0);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(assign_finalize_kernel, dim3(fb), dim3(256), 0, s, V,
@@ -637,6 +663,21 @@ hipError_t kmeans_update_launch(hipStream_t s, int V, int d, const void *W, cons
     default:
         return launch_update_g<4>(s, V, d, Wb, inv_norm, M, w, C_prev, C_out, Cb, size, norm);
     }
+}
+
+}  // namespace ds
+
+namespace ds {
+
+hipError_t dense_head_launch(hipStream_t s, int V, int d, const void *W, int n, const void *h,
+                             float *logits, int64_t ldl, hipEvent_t t0, hipEvent_t t1)
+{
+    const int RT = (V + kTileR - 1) / kTileR, CT = (n + kTileC - 1) / kTileC;
+    const int RTp = (RT + 7) / 8 * 8;
+    return launch_timed(kmeans_assign_kernel<true>, dim3((unsigned)((int64_t)RTp * CT)),
+                        dim3(kAsgThreads), s, t0, t1, V, d, reinterpret_cast<const uint16_t *>(W),
+                        n, reinterpret_cast<const uint16_t *>(h), RT, CT,
+                        (unsigned long long *)nullptr, logits, ldl);
 }
 
 }  // namespace ds

@@ -87,6 +87,7 @@ _SIGS = {
     "ds_verify_tree_workspace_bytes": (_sz, [_i, _i, _i, _i64]),
     "ds_verify_tree": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
                             _vp, _vp, _vp, _sz]),
+    "ds_dense_lm_head": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp, _i64, _vp]),
     "ds_router_labels": (_i, [_vp, _i, _i, _i, _i, _vp, _i64, _vp, _vp]),
     "ds_router_train_workspace_bytes": (_sz, [_i, _i, _i]),
     "ds_router_train_step": (_i, [_vp, C.POINTER(RouterTrainArgs)]),
@@ -327,6 +328,18 @@ def verify_tree(parent, token, sl_off, sl_ids, q, p, u_acc, u_fin, max_len, n_ac
         _s(stream), B, m, V, _p(parent), _p(token), _p(sl_off), _p(sl_ids), _p(q), _p(p),
         _p(u_acc), _p(u_fin), int(max_len), _p(n_acc), _p(out), _p(path), _p(ws),
         _nbytes(ws)))
+
+
+def dense_lm_head(W, h, logits, *, stream=None, events=None):
+    """logits [n][V] (fp32, any row stride >= V) = h W^T over every token;
+    W [V][d], h [n][d] bf16 with contiguous rows.  events: optional (start,
+    stop) raw hipEvent_t handles stamped at the kernel's own start and end."""
+    V, d = W.shape
+    n = h.shape[0]
+    assert h.stride(-1) == 1 and (n == 1 or h.stride(0) == d), "h rows must be contiguous"
+    ev = None if events is None else (C.c_void_p * 2)(*events)
+    _check("ds_dense_lm_head", lib.ds_dense_lm_head(_s(stream), V, d, _p(W), n, _p(h),
+                                                    _p(logits), _ld(logits), ev))
 
 
 def router_labels(logits, cluster_of, M: int, L: int, labels, *, stream=None):

@@ -348,6 +348,20 @@ ds_status ds_verify_tree(hipStream_t s, int B, int m, int V, const int32_t *pare
                          size_t ws_bytes);
 
 /*
+ * Dense LM head of the full drafter over every token, the O(|V| d)
+ * projection the shortlist avoids [S "Comparison to Prior Work": EAGLE's
+ * O(|V| d) head; "Modeling": the full drafter whose top-L gives the
+ * router's training labels]:  logits[i][y] = sum_k W[y][k] h[i][k].
+ * bf16 only (fp32 accumulation on the matrix cores); W [V][d], h [n][d]
+ * contiguous rows; logits [n][V] fp32 with row stride ldl >= V.  d a
+ * multiple of 64, at most 8192.  events (optional, host array of 2
+ * caller-created HIP events with timing) are stamped at the kernel's own
+ * start and end.
+ */
+ds_status ds_dense_lm_head(hipStream_t s, int V, int d, const void *W, int n, const void *h,
+                           float *logits, int64_t ldl, hipEvent_t *events);
+
+/*
  * Router training labels [S "Modeling": binary cross entropy over clusters,
  * a cluster's label positive when it holds a token in the top-L of the full
  * drafter].  Row i of logits (V fp32 values of the full drafter -- the dense

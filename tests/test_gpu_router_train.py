@@ -55,7 +55,8 @@ def test_router_labels_bit_exact(N, oracle_lib, n, V, M, L):
 
 def test_router_labels_from_dense_head(N, oracle_lib):
     """Labels of the Llama-shaped head: the full drafter's logits come from
-    the gathered head with the whole vocabulary as the shortlist."""
+    the dense head (and agree with the gathered head over the whole
+    vocabulary within the bf16 bar)."""
     cfg = syn.CONFIGS[1]
     wl = syn.make_workload(1, with_target=False)
     n, V, M, L = 16, cfg.V, cfg.M, 64
@@ -65,8 +66,11 @@ def test_router_labels_from_dense_head(N, oracle_lib):
     sl_ids = torch.arange(V, dtype=torch.int32, device="cuda")
     logits = torch.empty(n * V, dtype=torch.float32, device="cuda")
     N.gathered_lm_head(W, h[None], sl_off, sl_ids, V, logits)
+    dense = torch.empty(n, V, dtype=torch.float32, device="cuda")
+    N.dense_lm_head(W, h, dense)
     torch.cuda.synchronize()
-    lg = logits.view(n, V).cpu().numpy()
+    assert float((dense - logits.view(n, V)).abs().max()) <= 2e-2
+    lg = dense.cpu().numpy()
     got = _labels_gpu(N, lg, wl.cluster_of, M, L)
     assert np.array_equal(got, oracle_lib.topl_labels(lg, wl.cluster_of, M, L))
     assert got.sum(1).min() >= 1 and got.sum(1).max() <= L
@@ -123,3 +127,19 @@ def test_router_train_step(N, oracle_lib, shape, act, h_bf16):
     assert loss2 == loss
     for k in g:
         assert np.array_equal(g2[k], g[k]) and np.array_equal(p2[k], p[k])
+
+
+@pytest.mark.parametrize("V,d,n", [(5000, 256, 37), (20011, 1024, 300), (1000, 64, 1)])
+def test_dense_lm_head_parity(N, oracle_lib, V, d, n):
+    """The dense head over all V against the oracle (bf16 bar 2e-2), on
+    ragged row and column tiles."""
+    g = np.random.default_rng(V + n)
+    W = syn.f32_to_bf16_bits((g.standard_normal((V, d)) * 0.05).astype(np.float32))
+    h = syn.f32_to_bf16_bits(g.standard_normal((n, d)).astype(np.float32))
+    out = torch.full((n, V + 3), float("nan"), device="cuda")  # a padded row stride
+    N.dense_lm_head(to_dev(W), to_dev(h), out[:, :V])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = oracle_lib.dense_lm_head(W, h)
+    assert np.abs(got[:, :V].astype(np.float64) - ref).max() <= 2e-2
+    assert np.isnan(got[:, V:]).all()  # nothing written past V
