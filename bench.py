@@ -49,9 +49,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "head_gemv_traffic.json")
+# the GEMV head's translation unit: the traffic counters hold while it is unchanged
 HEAD_SOURCES = ["dynamic_vocabulary_draft_amd/csrc/head.hip",
-                "dynamic_vocabulary_draft_amd/csrc/head_mfma.hip",
-                "dynamic_vocabulary_draft_amd/csrc/common.h"]
+                "dynamic_vocabulary_draft_amd/csrc/common.h",
+                "dynamic_vocabulary_draft_amd/csrc/kernels.h"]
 
 
 def log(*a):

@@ -91,6 +91,7 @@ constexpr int kASlice = 32 * kKs;  // bf16 elements per wave
 // are issued one slice group before the phase starts, into registers.
 template <int NB>
 constexpr int phase_len() { return 512 / NB; }
+constexpr int kPhaseRot = 7;  // phase rotation per tile (coprime to 8, 15 and 16 phases)
 template <int NB>
 constexpr int lds_row() { return phase_len<NB>() + 8; }
 constexpr int kStage = 32 * 512 / 8 / 256;  // pieces per thread per phase
@@ -164,25 +165,36 @@ __device__ __forceinline__ void slice_mma(const u32x4 ld[4], uint16_t *aw, const
 // in flight); a phase (phase_len<NB>() hidden elements of B) is staged in
 // LDS between two barriers, its loads issued one slice group earlier so the
 // switch waits for them and not for the W ring.
+// The phases are visited from phase rot % nph on, wrapping around (when d
+// fills every phase): rows read at the same moment by different workgroups
+// then sit at different column offsets, which spreads consecutive rows (8 KB
+// apart) over the memory channels -- without it, consecutive rows read 128
+// bytes at a time stream at 4.8 TB/s instead of 5.7.  Only the order of the
+// hidden-dimension sums changes, the same for every call.  The union head
+// rotates by tile; the gathered head's rows are scattered over the table
+// already and start at phase 0.
 template <int NB, int AUX, class Src>
 __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], int d,
                                              uint16_t *lds, uint16_t *aw, int nrows, Src src,
-                                             f32x16 acc[NB])
+                                             f32x16 acc[NB], int rot)
 {
     constexpr int KP = phase_len<NB>(), NS = KP / kKs, GP = NS / 4;  // groups of 4 slices
     const int nsl = (d + kKs - 1) / kKs, nph = (d + KP - 1) / KP;
+    const int ph0 = nsl == nph * NS ? rot % nph : 0;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
         acc[nb] = f32x16{};
     u32x4 hv[kStage];
-    load_phase<NB>(hv, 0, d, nrows, src);
+    load_phase<NB>(hv, ph0 * KP, d, nrows, src);
     __builtin_amdgcn_sched_barrier(0);  // B loads first, as in the loop
     u32x4 r0[4], r1[4], r2[4], r3[4];
-    load_a<AUX>(w, voff, 0 * kKs, r0);
-    load_a<AUX>(w, voff, 1 * kKs, r1);
-    load_a<AUX>(w, voff, 2 * kKs, r2);
-    load_a<AUX>(w, voff, 3 * kKs, r3);
-    for (int ph = 0; ph < nph; ++ph) {
+    load_a<AUX>(w, voff, (ph0 * NS + 0) * kKs, r0);
+    load_a<AUX>(w, voff, (ph0 * NS + 1) * kKs, r1);
+    load_a<AUX>(w, voff, (ph0 * NS + 2) * kKs, r2);
+    load_a<AUX>(w, voff, (ph0 * NS + 3) * kKs, r3);
+    for (int j = 0; j < nph; ++j) {
+        const int ph = j + ph0 < nph ? j + ph0 : j + ph0 - nph;
+        const int phn = j + 1 + ph0 < nph ? j + 1 + ph0 : j + 1 + ph0 - nph;  // next phase
         __syncthreads();  // every wave is done with the previous phase
         store_phase<NB>(lds, hv, ph * KP, d, nrows);
         __syncthreads();
@@ -191,20 +203,23 @@ __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], i
             const int ks = ph * NS + 4 * gi;  // first slice of this group
             if (ks >= nsl)
                 break;  // only in the last phase
+            // first slice of the next group: the next in this phase, else the
+            // next phase's first (past the end: a slice whose data goes unused)
+            const int kn = (gi < GP - 1 || j + 1 == nph) ? ks + 4 : phn * NS;
             if (gi == GP - 1) {
-                load_phase<NB>(hv, (ph + 1) * KP, d, nrows, src);
+                load_phase<NB>(hv, phn * KP, d, nrows, src);
                 // keep these loads ahead of the ring reloads below: the switch
                 // then waits for them alone (loads complete in issue order)
                 __builtin_amdgcn_sched_barrier(0);
             }
             slice_mma<NB>(r0, aw, lds, (4 * gi + 0) * kKs, (ks + 0) * kKs, d, acc);
-            load_a<AUX>(w, voff, (ks + 4) * kKs, r0);
+            load_a<AUX>(w, voff, (kn + 0) * kKs, r0);
             slice_mma<NB>(r1, aw, lds, (4 * gi + 1) * kKs, (ks + 1) * kKs, d, acc);
-            load_a<AUX>(w, voff, (ks + 5) * kKs, r1);
+            load_a<AUX>(w, voff, (kn + 1) * kKs, r1);
             slice_mma<NB>(r2, aw, lds, (4 * gi + 2) * kKs, (ks + 2) * kKs, d, acc);
-            load_a<AUX>(w, voff, (ks + 6) * kKs, r2);
+            load_a<AUX>(w, voff, (kn + 2) * kKs, r2);
             slice_mma<NB>(r3, aw, lds, (4 * gi + 3) * kKs, (ks + 3) * kKs, d, acc);
-            load_a<AUX>(w, voff, (ks + 7) * kKs, r3);
+            load_a<AUX>(w, voff, (kn + 3) * kKs, r3);
         }
     }
 }
@@ -362,7 +377,8 @@ __global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uin
         voff[i] = (uint32_t)((32 * wave + (lane >> 3) + 8 * i) * d * 2 + 16 * (lane & 7));
     f32x16 acc[NB];
     auto hsrc = [&](int r) { return h + (int64_t)(g0 + r) * ldh_g; };
-    rows_times_b<NB, kNonTemporal>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc, acc);
+    rows_times_b<NB, kNonTemporal>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc, acc,
+                                   (int)(blockIdx.x * kPhaseRot));
 
     // epilogue: the (row, group) pairs on the group's shortlist.  A group's
     // entries for the block's four tiles are one contiguous run of its
@@ -427,7 +443,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void h
             voff[i] = (uint32_t)__shfl(yrow, (lane >> 3) + 8 * i) * (uint32_t)d * 2u +
                       16u * (lane & 7);
         f32x16 acc[NB];
-        rows_times_b<NB, kCached>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc);
+        rows_times_b<NB, kCached>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc, 0);
         // epilogue: column = head row (node), row = shortlist entry; the
         // entry of accumulator row i was loaded by lanes i and i + 32
 #pragma unroll
