@@ -4,9 +4,9 @@
 // sampling), and the full-vocabulary target softmax (same normalisation on
 // dense rows).
 //
-// Both run as the two chunked launches of dist.h over 1024-element chunks,
-// one 256-thread workgroup per chunk when the launch is small (a 29K-entry
-// shortlist is spread over 29 workgroups instead of one), several
+// The sampler runs as the two chunked launches of dist.h over 1024-element
+// chunks, one 256-thread workgroup per chunk when the launch is small (a
+// 29K-entry shortlist is spread over 29 workgroups instead of one), several
 // consecutive chunks per workgroup when it is large:
 //   stats: chunk max m_c (fp32, exact), its first index, and the chunk sum
 //          of exp((l - m_c) / T) in a fixed association;
@@ -16,6 +16,10 @@
 //          fp32 (within one fp32 ulp of the quotient);
 //          the workgroup owning the threshold u * total walks its chunk.
 // Temperature 0 is the argmax (ties to the lowest index) with one-hot q.
+// The target softmax draws nothing, so it needs no prefix sums: two launches
+// over 4096-element segments, the first writing each segment's max and sum
+// of exp(l - max), the second rebuilding the row max and total in every
+// wave and writing p.
 #include <float.h>
 
 #include "common.h"
@@ -41,17 +45,6 @@ struct Ragged {
     }
 };
 
-// Row r of a dense [rows][V] array.
-struct Dense {
-    int64_t V;
-    __device__ void locate(int64_t row, int64_t *in_off, int64_t *len, int64_t *ids_off) const
-    {
-        *len = V;
-        *in_off = row * V;
-        *ids_off = 0;
-    }
-};
-
 // this lane's four consecutive elements (-FLT_MAX past the row end); one
 // 16-byte load when the row base is 16-byte aligned (j0 is a multiple of 4)
 __device__ __forceinline__ void load4(const float *__restrict__ l, int64_t j0, int64_t len,
@@ -71,6 +64,40 @@ __device__ __forceinline__ void load4(const float *__restrict__ l, int64_t j0, i
 // (x) / T; T = 1 (the usual case, and always for the target) skips the
 // fp64 division, which leaves the value unchanged
 __device__ __forceinline__ double over_tau(double x, double tau) { return tau == 1.0 ? x : x / tau; }
+
+// exp(x) in fp64 by Tang's table-driven method (ACM TOMS 15(2), 1989):
+// x = (64n + j) ln2/64 + r with |r| <= ln2/128 (ln2/64 split in two parts,
+// so r is exact to ~1e-19), exp(x) = 2^n * 2^(j/64) * e^r, and e^r - 1 from
+// its Taylor series through r^5 (the next term is below 4e-17).  About 16
+// instructions against some 75 for the library routine; relative error at
+// most 2 fp64 ulp for x > -708 (below that the result is subnormal and its
+// absolute error under one subnormal ulp).  x below -1000 gives 0, NaN stays
+// NaN.  tab[j] = 2^(j/64), filled by fill_exp2_table.
+__device__ __forceinline__ double exp_tab(double x, const double *tab)
+{
+    constexpr double kInvL = 0x1.71547652b82fep+6;   // 64 / ln 2
+    constexpr double kL1 = 0x1.62e42fefa39efp-7;     // ln 2 / 64, leading part
+    constexpr double kL2 = 0x1.abc9e3b39803fp-62;    // ln 2 / 64 - kL1
+    x = x < -1000.0 ? -1000.0 : (x > 1000.0 ? 1000.0 : x);
+    const double kf = rint(x * kInvL);
+    double r = fma(-kf, kL1, x);
+    r = fma(-kf, kL2, r);
+    const int k = (int)kf;
+    const double t = tab[k & 63];
+    double q = fma(r, 1.0 / 120, 1.0 / 24);
+    q = fma(q, r, 1.0 / 6);
+    q = fma(q, r, 0.5);
+    const double pm1 = fma(q, r * r, r);  // e^r - 1
+    return ldexp(fma(t, pm1, t), k >> 6);
+}
+
+// tab[j] = 2^(j/64) in LDS, by the first wave; visible after the caller's
+// next barrier
+__device__ __forceinline__ void fill_exp2_table(double *tab)
+{
+    if (threadIdx.x < 64)
+        tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+}
 
 // row max from the chunk maxima (order-independent), into every thread
 __device__ float row_max(const float *__restrict__ cmax, int nch, float *sh)
@@ -99,6 +126,7 @@ __global__ __launch_bounds__(kChunkThreads) void norm_stats_kernel(L layout,
     __shared__ float s_max[4];
     __shared__ int s_idx[4];
     __shared__ double s_wt[4];
+    __shared__ double s_exp2[64];
     const int64_t row = blockIdx.y, c0 = (int64_t)blockIdx.x * R;
     int64_t off, len, ids_off;
     layout.locate(row, &off, &len, &ids_off);
@@ -110,6 +138,7 @@ __global__ __launch_bounds__(kChunkThreads) void norm_stats_kernel(L layout,
 #pragma unroll
     for (int r = 0; r < R; ++r)
         load4(in + off, (c0 + r) * kChunk + jl, len, v[r]);
+    fill_exp2_table(s_exp2);  // ordered before its use by the barrier in the loop
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int64_t c = c0 + r;
@@ -127,7 +156,8 @@ __global__ __launch_bounds__(kChunkThreads) void norm_stats_kernel(L layout,
         double wt[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            wt[k] = j0 + k < len ? exp(over_tau((double)v[r][k] - (double)mc, tau)) : 0.0;
+            wt[k] = j0 + k < len ? exp_tab(over_tau((double)v[r][k] - (double)mc, tau), s_exp2)
+                                 : 0.0;
         double incl;
         double tot = wave_chunk_sum(wt, &incl);
         if (lane_id() == 0)
@@ -140,10 +170,10 @@ __global__ __launch_bounds__(kChunkThreads) void norm_stats_kernel(L layout,
 
 // chunk sums rescaled to the row max: csum_c * exp((m_c - M)/T), into LDS
 __device__ void rescaled_sums(const float *__restrict__ cmax, const double *__restrict__ csum,
-                              int nch, double mx, double tau, double *S)
+                              int nch, double mx, double tau, const double *tab, double *S)
 {
     for (int c = threadIdx.x; c < nch; c += blockDim.x)
-        S[c] = csum[c] * exp(over_tau((double)cmax[c] - mx, tau));
+        S[c] = csum[c] * exp_tab(over_tau((double)cmax[c] - mx, tau), tab);
     __syncthreads();
 }
 
@@ -162,6 +192,7 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
     __shared__ float s_f[4];
     __shared__ int s_owner, s_fallback;
     __shared__ int64_t s_pick[2];
+    __shared__ double s_exp2[64];
     const int64_t row = blockIdx.y, c0 = (int64_t)blockIdx.x * R;
     int64_t off, len, ids_off;
     layout.locate(row, &off, &len, &ids_off);
@@ -178,6 +209,7 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
         load4(in + off, (c0 + r) * kChunk + jl, (c0 + r) < nch ? len : 0, v[r]);
     const float *cmax = w.cmax + row * nchmax;
     const double *csum = w.csum + row * nchmax;
+    fill_exp2_table(s_exp2);  // ordered before its use by the barrier in row_max
     const float mxf = row_max(cmax, nch, s_f);
 
     if (tau == 0.0) {  // argmax: the first chunk holding the max has its index
@@ -213,7 +245,7 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
     }
 
     const double mx = (double)mxf;
-    rescaled_sums(cmax, csum, nch, mx, tau, S2);
+    rescaled_sums(cmax, csum, nch, mx, tau, s_exp2, S2);
     const double Z = row_prefix(S2, nch, P, S, &s_total);
     const double rZ = 1.0 / Z;  // q = w * (1/Z): within one fp32 ulp of w / Z
 #pragma unroll
@@ -224,7 +256,8 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (j0 + k < len)
-                out[off + j0 + k] = (float)(exp(over_tau((double)v[r][k] - mx, tau)) * rZ);
+                out[off + j0 + k] =
+                    (float)(exp_tab(over_tau((double)v[r][k] - mx, tau), s_exp2) * rZ);
     }
     if (!PICK)
         return;
@@ -241,7 +274,7 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
         if (c0 + r == c) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                wt[k] = j0 + k < len ? exp(over_tau((double)v[r][k] - mx, tau)) : 0.0;
+                wt[k] = j0 + k < len ? exp_tab(over_tau((double)v[r][k] - mx, tau), s_exp2) : 0.0;
         }
     double incl;
     double tot = wave_chunk_sum(wt, &incl);
@@ -284,6 +317,111 @@ hipError_t launch_norm(hipStream_t s, L layout, int64_t rows, int64_t max_len, c
     return launch_norm_r<L, PICK, 1>(s, layout, rows, nchmax, in, tau, ws, sl_ids, u, token, out);
 }
 
+// ------------------------------------------------------------ target softmax
+// Segment of kSeg elements per 256-thread workgroup; lane l of wave w holds
+// elements 1024 i + 256 w + 4 l + k (i, k < 4) of it (16-byte accesses).
+constexpr int kSeg = 4 * kChunk;
+constexpr int kSegPer = kSeg / kChunkThreads;  // elements per thread
+
+__device__ __forceinline__ void load_seg(const float *__restrict__ lr, int64_t j0, int64_t V,
+                                         float v[4][4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        load4(lr, j0 + i * kChunk, V, v[i]);
+}
+
+// Segment max (fp32, exact) and the sum of exp(l - max) over the segment in
+// fp64, in a fixed association (each lane's 16 terms in order, the wave
+// butterfly, the four wave sums in order).  -inf logits weigh 0.
+__global__ __launch_bounds__(kChunkThreads) void softmax_stats_kernel(int64_t V,
+                                                                      const float *__restrict__ in,
+                                                                      double *__restrict__ ssum,
+                                                                      float *__restrict__ smax)
+{
+    __shared__ float s_m[4];
+    __shared__ double s_s[4];
+    __shared__ double s_exp2[64];
+    const int64_t row = blockIdx.y, nseg = gridDim.x;
+    const int64_t j0 = (int64_t)blockIdx.x * kSeg + (threadIdx.x >> 6) * 256 + lane_id() * 4;
+    float v[4][4];
+    load_seg(in + row * V, j0, V, v);
+    fill_exp2_table(s_exp2);
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            m = fmaxf(m, v[i][k]);  // -FLT_MAX past V
+    m = wave_max(m);
+    if (lane_id() == 0)
+        s_m[threadIdx.x >> 6] = m;
+    __syncthreads();  // also orders the table
+    const float mseg = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float x = v[i][k];
+            if (j0 + i * kChunk + k < V && x != -INFINITY)
+                acc += exp_tab((double)x - (double)mseg, s_exp2);
+        }
+    acc = wave_sum_f64(acc);
+    if (lane_id() == 0)
+        s_s[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        ssum[row * nseg + blockIdx.x] = ((s_s[0] + s_s[1]) + s_s[2]) + s_s[3];
+        smax[row * nseg + blockIdx.x] = mseg;
+    }
+}
+
+// p = exp(l - M) * (1 / Z), M the row max, Z = sum over segments of
+// ssum_s * exp(smax_s - M); every wave rebuilds M and Z in the same order,
+// so all workgroups of a row use the same values.
+__global__ __launch_bounds__(kChunkThreads) void softmax_final_kernel(
+    int64_t V, const float *__restrict__ in, const double *__restrict__ ssum,
+    const float *__restrict__ smax, float *__restrict__ p)
+{
+    __shared__ double s_exp2[64];
+    const int64_t row = blockIdx.y, nseg = gridDim.x;
+    const int64_t j0 = (int64_t)blockIdx.x * kSeg + (threadIdx.x >> 6) * 256 + lane_id() * 4;
+    float v[4][4];
+    load_seg(in + row * V, j0, V, v);
+    fill_exp2_table(s_exp2);
+    const float *sm = smax + row * nseg;
+    const double *ss = ssum + row * nseg;
+    float M = -INFINITY;
+    for (int64_t c = lane_id(); c < nseg; c += kWave)
+        M = fmaxf(M, sm[c]);
+    M = wave_max(M);
+    __syncthreads();  // the table
+    double z = 0.0;
+    for (int64_t c = lane_id(); c < nseg; c += kWave)
+        z += ss[c] * exp_tab((double)sm[c] - (double)M, s_exp2);
+    z = wave_sum_f64(z);
+    const double rZ = 1.0 / z;  // p = w * (1/Z): within one fp32 ulp of w / Z
+    float *pr = p + row * V;
+    const bool vec = (reinterpret_cast<uintptr_t>(pr) & 15) == 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t j = j0 + i * kChunk;
+        float o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            o[k] = (float)(exp_tab((double)v[i][k] - (double)M, s_exp2) * rZ);
+        if (vec && j + 3 < V) {
+            *reinterpret_cast<float4 *>(pr + j) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (j + k < V)
+                    pr[j + k] = o[k];
+        }
+    }
+}
+
 }  // namespace
 
 size_t sample_ws_bytes(int64_t rows, int64_t max_len)
@@ -300,13 +438,28 @@ hipError_t sample_launch(hipStream_t s, int G, int m, const int64_t *sl_off,
                                      (double)temperature, ws, sl_ids, u, token, q);
 }
 
-size_t softmax_ws_bytes(int64_t rows, int64_t V) { return chunk_ws_bytes(rows, chunks_for(V)); }
+static int64_t segments_for(int64_t V) { return (V + kSeg - 1) / kSeg; }
+
+// [rows][nseg] segment sums (fp64), then [rows][nseg] segment maxima (fp32)
+size_t softmax_ws_bytes(int64_t rows, int64_t V)
+{
+    return (size_t)rows * (size_t)segments_for(V) * 12 + 256;
+}
 
 hipError_t softmax_launch(hipStream_t s, int rows, int V, const float *logits, float *p, void *ws)
 {
-    Dense layout{V};
-    return launch_norm<Dense, false>(s, layout, rows, V, logits, 1.0, ws, nullptr, nullptr,
-                                     nullptr, p);
+    const int64_t nseg = segments_for(V);
+    double *ssum = reinterpret_cast<double *>(ws);
+    float *smax = reinterpret_cast<float *>(ssum + (size_t)rows * nseg);
+    const dim3 grid((unsigned)nseg, (unsigned)rows);
+    hipLaunchKernelGGL(softmax_stats_kernel, grid, dim3(kChunkThreads), 0, s, (int64_t)V, logits,
+                       ssum, smax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(softmax_final_kernel, grid, dim3(kChunkThreads), 0, s, (int64_t)V, logits,
+                       (const double *)ssum, (const float *)smax, p);
+    return hipGetLastError();
 }
 
 }  // namespace ds

@@ -86,7 +86,7 @@ def test_router_parity(N, oracle_lib, bf16, act, n, d, r, M):
 # ----------------------------------------------------------------------------
 # select_clusters: bit-exact on identical scores
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("M", [1, 3, 64, 100, 1024, 2048, 4096])
+@pytest.mark.parametrize("M", [1, 3, 64, 100, 200, 300, 1024, 2048, 4096])
 @pytest.mark.parametrize("kind", [syn.BUDGET_CLUSTERS, syn.BUDGET_TOKENS])
 def test_select_parity(N, oracle_lib, M, kind):
     g = np.random.default_rng(M * 7 + kind)
@@ -446,15 +446,37 @@ def test_sample_multi_chunk_workgroups(N, oracle_lib, rows, maxlen, tau):
 # target_softmax and verify_reject
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("rows,V", [(3, 1000), (5, 128256), (2, 262144), (40, 128256),
-                                    (70, 128256)])
+                                    (70, 128256), (9, 151936)])
 def test_target_softmax_parity(N, oracle_lib, rows, V):
-    """Single-chunk and multi-chunk workgroups (40 and 70 rows of 126 chunks
-    take 4 and 8 chunks per workgroup, the last one partial)."""
+    """One segment (V = 1000) and many, the last one partial."""
     g = np.random.default_rng(V)
     lg = (g.standard_normal((rows, V)) * 3).astype(np.float32)
     p = torch.empty(rows, V, device="cuda")
     N.target_softmax(to_dev(lg), p, N.workspace(N.softmax_workspace_bytes(rows, V)))
     _ulp_bar(_cpu(p), oracle_lib.target_softmax(lg))
+
+
+def test_target_softmax_extreme_logits(N, oracle_lib):
+    """-inf logits (two whole 4096-element segments, every third entry), a
+    spread that takes exp through its whole range to underflow and to
+    subnormal p, a single huge logit, a constant row, a large negative
+    offset; V = 10001 leaves rows unaligned for 16-byte accesses."""
+    rows, V = 7, 10001
+    g = np.random.default_rng(11)
+    lg = (g.standard_normal((rows, V)) * 40).astype(np.float32)
+    lg[0, :8192] = -np.inf
+    lg[1, ::3] = -np.inf
+    lg[2] = g.permutation(np.linspace(0.0, -1100.0, V)).astype(np.float32)  # every exponent
+    lg[3, 5000] = 3.0e38
+    lg[4] = 7.0
+    lg[5] = (g.standard_normal(V) * 3 - 1.0e4).astype(np.float32)
+    ref = oracle_lib.target_softmax(lg)
+    assert (ref[2] == 0).sum() > V // 2 and ((ref[2] > 0) & (ref[2] < 1.2e-38)).sum() > 50
+    p = torch.full((rows, V), float("nan"), device="cuda")
+    N.target_softmax(to_dev(lg), p, N.workspace(N.softmax_workspace_bytes(rows, V)))
+    got = _cpu(p)
+    _ulp_bar(got, ref)
+    assert (got[0, :8192] == 0).all() and (got[1, ::3] == 0).all() and got[3, 5000] == 1.0
 
 
 def _verify_case(oracle_lib, V, T, B, mode, seed):

@@ -55,7 +55,7 @@ def test_workspace_queries(N):
     assert N.cluster_index_bytes(2048, 262144) == (nch + 1) * 2048 * 4
     assert N.sample_workspace_bytes(1, 1, 1024) == 24 + 256
     assert N.sample_workspace_bytes(3, 4, 1025) == 12 * 2 * 24 + 256
-    assert N.softmax_workspace_bytes(7, 128256) == 7 * 126 * 24 + 256
+    assert N.softmax_workspace_bytes(7, 128256) == 7 * 32 * 12 + 256  # 4096-entry segments
     assert N.verify_workspace_bytes(2, 6, 128256) >= 2 * 126 * 24 + 2 * 4
     assert N.draft_chain_workspace_bytes(1, 6, 128256, 1024, 55734) >= 4096 + 256
     assert N.sample_workspace_bytes(0, 1, 10) == 0
