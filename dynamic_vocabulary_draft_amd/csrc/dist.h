@@ -201,10 +201,20 @@ __device__ inline int64_t chunk_walk(const double w[4], int64_t j0_lane, const d
                 first = j0_lane + k;
         }
     }
-    if (first != INT64_MAX)
-        atomicMin(&sp[0], (unsigned long long)first);
-    if (last >= 0)
-        atomicMax(&sp[1], (unsigned long long)(last + 1));
+    // elements ascend with the lane: the wave's first pick is the lowest
+    // lane's, its last positive index the highest lane's; one LDS atomic per
+    // wave (same-address atomics from every lane serialise)
+    const uint64_t bf = __ballot(first != INT64_MAX), bl = __ballot(last >= 0);
+    if (bf) {
+        const int64_t f = __shfl(first, __ffsll((unsigned long long)bf) - 1);
+        if (lane == 0)
+            atomicMin(&sp[0], (unsigned long long)f);
+    }
+    if (bl) {
+        const int64_t l = __shfl(last, 63 - __clzll((long long)bl));
+        if (lane == 0)
+            atomicMax(&sp[1], (unsigned long long)(l + 1));
+    }
     __syncthreads();
     return sp[0] != ~0ull ? (int64_t)sp[0] : (int64_t)sp[1] - 1;
 }
