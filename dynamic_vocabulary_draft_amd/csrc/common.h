@@ -62,32 +62,63 @@ __device__ __forceinline__ float wave_sum(float v)
     return ((r0 + r1) + r2) + r3;
 }
 
+// A double moved across lanes by DPP (both halves with the same control);
+// lanes whose source is outside the row, or whose row is not in ROWS, get 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xF,
+                                                             false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL,
+                                                             ROWS, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum over the 64 lanes in a fixed association (as wave_sum), every lane
+// receiving the same value.
 __device__ __forceinline__ double wave_sum_f64(double v)
 {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1)
-        v += __shfl_xor(v, o);
-    return v;
+    v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f64<0x141>(v);  // row_half_mirror
+    v += dpp_f64<0x140>(v);  // row_mirror
+    return ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
 }
 
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1)
-        v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-// Inclusive scan over the wave in lane order (Hillis-Steele, fixed order).
+// Inclusive scan over the wave in lane order, fixed association: within each
+// row of 16 lanes by shifts of 1, 2, 4, 8 (Hillis-Steele), then the row
+// totals carried across rows (row 0's into row 1, row 2's into row 3, then
+// rows 0-1's into rows 2 and 3).
 __device__ __forceinline__ double wave_incl_scan_f64(double v)
 {
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        double t = __shfl_up(v, o);
-        if (lane >= o)
-            v += t;
-    }
+    v += dpp_f64<0x111>(v);       // row_shr:1
+    v += dpp_f64<0x112>(v);       // row_shr:2
+    v += dpp_f64<0x114>(v);       // row_shr:4
+    v += dpp_f64<0x118>(v);       // row_shr:8
+    v += dpp_f64<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_f64<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
