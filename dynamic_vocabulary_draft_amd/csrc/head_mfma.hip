@@ -236,14 +236,35 @@ struct TileIx {
     uint32_t mask;
 };
 
+// OR over the 64 lanes (DPP within rows, then the four row results)
+__device__ __forceinline__ uint32_t wave_or(uint32_t v)
+{
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);
+    return (uint32_t)(__builtin_amdgcn_readlane((int)v, 0) | __builtin_amdgcn_readlane((int)v, 16) |
+                      __builtin_amdgcn_readlane((int)v, 32) | __builtin_amdgcn_readlane((int)v, 48));
+}
+
+constexpr int kIxLdsGroups = 4095;  // group offsets staged in LDS up to this G
+
 __global__ __launch_bounds__(256) void union_index_kernel(int G, int nt, int V,
                                                           const int64_t *__restrict__ sl_off,
                                                           const int32_t *__restrict__ sl_ids,
                                                           TileIx *__restrict__ tix,
                                                           float *__restrict__ logits)
 {
+    __shared__ int64_t s_off[kIxLdsGroups + 1];
     const int lane = lane_id();
-    const int64_t beg = sl_off[0], end = sl_off[G];
+    const bool lds_off = G <= kIxLdsGroups;
+    if (lds_off) {
+        for (int i = threadIdx.x; i <= G; i += blockDim.x)
+            s_off[i] = sl_off[i];
+        __syncthreads();
+    }
+    const int64_t *off = lds_off ? s_off : sl_off;
+    const int64_t beg = off[0], end = off[G];
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     // the loop runs the same number of times in every lane of a wave (the
     // mask below combines lanes), so lanes past the end carry an empty key
@@ -259,15 +280,15 @@ __global__ __launch_bounds__(256) void union_index_kernel(int G, int nt, int V,
             int lo = 0, hi = G;  // group: last g with sl_off[g] <= J
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
-                if (sl_off[mid] <= J)
+                if (off[mid] <= J)
                     lo = mid;
                 else
                     hi = mid;
             }
             g = lo;
-            gbeg = sl_off[g];
+            gbeg = off[g];
             j = J - gbeg;
-            len = sl_off[g + 1] - gbeg;
+            len = off[g + 1] - gbeg;
             yJ = sl_ids[J];
             if (yJ < 0 || yJ >= V)
                 logits[J] = __builtin_nanf("");
@@ -286,22 +307,30 @@ __global__ __launch_bounds__(256) void union_index_kernel(int G, int nt, int V,
                 m |= mo;
         }
         const int64_t last_key = __shfl(key, kWave - 1);  // all lanes, before any branch
+        // The run of the last lane's key may continue past this wave (at
+        // most 31 more entries of one tile): lanes 0..31 take the next 32
+        // entries; the leading ones in the same group and tile add their
+        // bits, one OR over the wave.
+        uint32_t mx = 0u;
+        if (last_key >= 0) {  // wave-uniform
+            const int64_t gl = last_key / (nt + 1), tl = last_key % (nt + 1);
+            const int64_t gend = off[gl + 1];
+            const int64_t JX = J0 + kWave + lane;
+            const bool ld = lane < 32 && JX < gend;
+            const int32_t yx = ld ? sl_ids[JX] : -1;
+            const bool same = ld && tile(yx) == tl;
+            const uint64_t bc = __ballot(same);
+            const int run = __ffsll((unsigned long long)~bc) - 1;  // leading lanes in the run
+            mx = wave_or(lane < run && yx < V ? 1u << (yx & 31) : 0u);
+        }
         if (!in)
             continue;
         TileIx *row = tix + (int64_t)g * (nt + 1);
         for (int64_t t = tp + 1; t < tc; ++t)  // tiles without entries
             row[t] = TileIx{(int32_t)j, 0u};
         if (tc > tp) {  // first entry of tile tc
-            // the run may continue past this wave: those entries are read here
-            int64_t e = j + (kWave - lane);
             if (last_key == key)
-                for (; e < len && e < j + 32; ++e) {
-                    const int32_t y = sl_ids[gbeg + e];
-                    if (tile(y) != tc)
-                        break;
-                    if (y < V)
-                        m |= 1u << (y & 31);
-                }
+                m |= mx;
             row[tc] = TileIx{(int32_t)j, m};
         }
         if (j == len - 1)
