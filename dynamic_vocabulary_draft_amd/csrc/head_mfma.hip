@@ -36,8 +36,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kKs = 64;         // hidden-dimension slice per MFMA group
-constexpr int kTileRows = 128;  // W rows per workgroup (4 waves x 32)
+constexpr int kKs = 64;  // hidden-dimension slice per MFMA group
+// W rows per workgroup: WV waves x 32.  The staged hidden vectors are shared
+// by all of a workgroup's rows, so taller tiles move fewer hidden-vector
+// bytes from L2 per W row.
+template <int WV>
+constexpr int tile_rows() { return 32 * WV; }
 
 __device__ __forceinline__ f32x16 mfma(const u32x4 &a, const u32x4 &b, f32x16 c)
 {
@@ -81,41 +85,47 @@ __device__ __forceinline__ void load_a(rsrc_t w, const uint32_t voff[4], int k0,
 }
 
 // Per-wave LDS slice of A: 32 rows x 64 bf16; the 16-byte piece p of row r
-// sits in slot p ^ (r & 7), so the row-wise writes and the MFMA-order reads
-// (eight rows, one piece each) both touch distinct banks.
+// sits in slot p ^ akey(r), so the row-wise writes and the MFMA-order reads
+// (one piece of each of 8 consecutive rows per 128 bytes of banks, 16 rows
+// per 256) both touch distinct banks: akey takes 8 distinct values on any 8
+// aligned rows and on the even and the odd rows of any 16 aligned rows (with
+// r & 7 alone, rows r and r + 8 share banks when 16 lanes are served at once).
 constexpr int kASlice = 32 * kKs;  // bf16 elements per wave
+__device__ __forceinline__ int akey(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // B operand (hidden vectors) for one phase of KP hidden elements, staged in
 // LDS as [NB*32][KP + 8] bf16 (rows past nrows and elements past d are zero).
-// Each of the 256 threads moves kStage 16-byte pieces: all loads of a phase
-// are issued one slice group before the phase starts, into registers.
+// Each of the NT threads moves stage_n<NT>() 16-byte pieces: all loads of a
+// phase are issued one slice group before the phase starts, into registers.
 template <int NB>
 constexpr int phase_len() { return 512 / NB; }
 constexpr int kPhaseRot = 7;  // phase rotation per tile (coprime to 8, 15 and 16 phases)
 template <int NB>
 constexpr int lds_row() { return phase_len<NB>() + 8; }
-constexpr int kStage = 32 * 512 / 8 / 256;  // pieces per thread per phase
+template <int NT>
+constexpr int stage_n() { return 32 * 512 / 8 / NT; }  // pieces per thread per phase
 
-template <int NB, class Src>
-__device__ __forceinline__ void load_phase(u32x4 v[kStage], int k0, int d, int nrows, Src src)
+template <int NB, int NT, class Src>
+__device__ __forceinline__ void load_phase(u32x4 v[stage_n<NT>()], int k0, int d, int nrows,
+                                           Src src)
 {
     constexpr int KP = phase_len<NB>();
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-        const int p = threadIdx.x + 256 * i;
+    for (int i = 0; i < stage_n<NT>(); ++i) {
+        const int p = threadIdx.x + NT * i;
         const int r = min(p / (KP / 8), nrows - 1), k = min(k0 + (p % (KP / 8)) * 8, d - 8);
         v[i] = *reinterpret_cast<const u32x4 *>(src(r) + k);
     }
 }
 
-template <int NB>
-__device__ __forceinline__ void store_phase(uint16_t *lds, const u32x4 v[kStage], int k0, int d,
-                                            int nrows)
+template <int NB, int NT>
+__device__ __forceinline__ void store_phase(uint16_t *lds, const u32x4 v[stage_n<NT>()], int k0,
+                                            int d, int nrows)
 {
     constexpr int KP = phase_len<NB>(), LR = lds_row<NB>();
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-        const int p = threadIdx.x + 256 * i;
+    for (int i = 0; i < stage_n<NT>(); ++i) {
+        const int p = threadIdx.x + NT * i;
         const int r = p / (KP / 8), kk = (p % (KP / 8)) * 8;
         const bool ok = r < nrows && k0 + kk < d;
         *reinterpret_cast<u32x4 *>(lds + r * LR + kk) = ok ? v[i] : u32x4{0u, 0u, 0u, 0u};
@@ -136,12 +146,12 @@ __device__ __forceinline__ void slice_mma(const u32x4 ld[4], uint16_t *aw, const
     const int wr = lane >> 3, wp = lane & 7;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4 *>(aw + (wr + 8 * i) * kKs + ((wp ^ wr) << 3)) = ld[i];
+        *reinterpret_cast<u32x4 *>(aw + (wr + 8 * i) * kKs + ((wp ^ akey(wr + 8 * i)) << 3)) = ld[i];
     const int rr = lane & 31, hh = lane >> 5;
     u32x4 a[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        a[s] = *reinterpret_cast<const u32x4 *>(aw + rr * kKs + (((4 * hh + s) ^ (rr & 7)) << 3));
+        a[s] = *reinterpret_cast<const u32x4 *>(aw + rr * kKs + (((4 * hh + s) ^ akey(rr)) << 3));
     if (kabs + kKs > d) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -173,7 +183,7 @@ __device__ __forceinline__ void slice_mma(const u32x4 ld[4], uint16_t *aw, const
 // hidden-dimension sums changes, the same for every call.  The union head
 // rotates by tile; the gathered head's rows are scattered over the table
 // already and start at phase 0.
-template <int NB, int AUX, class Src>
+template <int NB, int NT, int AUX, class Src>
 __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], int d,
                                              uint16_t *lds, uint16_t *aw, int nrows, Src src,
                                              f32x16 acc[NB], int rot)
@@ -184,8 +194,8 @@ __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], i
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
         acc[nb] = f32x16{};
-    u32x4 hv[kStage];
-    load_phase<NB>(hv, ph0 * KP, d, nrows, src);
+    u32x4 hv[stage_n<NT>()];
+    load_phase<NB, NT>(hv, ph0 * KP, d, nrows, src);
     __builtin_amdgcn_sched_barrier(0);  // B loads first, as in the loop
     u32x4 r0[4], r1[4], r2[4], r3[4];
     load_a<AUX>(w, voff, (ph0 * NS + 0) * kKs, r0);
@@ -196,7 +206,7 @@ __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], i
         const int ph = j + ph0 < nph ? j + ph0 : j + ph0 - nph;
         const int phn = j + 1 + ph0 < nph ? j + 1 + ph0 : j + 1 + ph0 - nph;  // next phase
         __syncthreads();  // every wave is done with the previous phase
-        store_phase<NB>(lds, hv, ph * KP, d, nrows);
+        store_phase<NB, NT>(lds, hv, ph * KP, d, nrows);
         __syncthreads();
 #pragma unroll
         for (int gi = 0; gi < GP; ++gi) {
@@ -207,7 +217,7 @@ __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], i
             // next phase's first (past the end: a slice whose data goes unused)
             const int kn = (gi < GP - 1 || j + 1 == nph) ? ks + 4 : phn * NS;
             if (gi == GP - 1) {
-                load_phase<NB>(hv, phn * KP, d, nrows, src);
+                load_phase<NB, NT>(hv, phn * KP, d, nrows, src);
                 // keep these loads ahead of the ring reloads below: the switch
                 // then waits for them alone (loads complete in issue order)
                 __builtin_amdgcn_sched_barrier(0);
@@ -222,6 +232,14 @@ __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], i
             load_a<AUX>(w, voff, (kn + 3) * kKs, r3);
         }
     }
+}
+
+// LDS of the matrix-core heads: the B phase buffer, then the waves' A slices;
+// after the K loop the union epilogue reuses the front as its run buffer
+template <int NB, int WV>
+constexpr int lds_bytes()
+{
+    return NB * 32 * lds_row<NB>() * 2 + WV * kASlice * 2;
 }
 
 // ------------------------------------------------------------------ union
@@ -339,15 +357,16 @@ __global__ __launch_bounds__(256) void union_index_kernel(int G, int nt, int V,
     }
 }
 
-template <int NB>
-__global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uint16_t *__restrict__ W,
+template <int NB, int WV>
+__global__ __launch_bounds__(64 * WV) void head_union_kernel(int V, int d, const uint16_t *__restrict__ W,
                                                          int G, int g0, const uint16_t *__restrict__ h,
                                                          int64_t ldh_g, const int64_t *__restrict__ sl_off,
                                                          const TileIx *__restrict__ tix, int nt,
                                                          float *__restrict__ logits)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[NB * 32 * lds_row<NB>()];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_a[4 * kASlice];
+    constexpr int kTileRows = tile_rows<WV>();
+    __shared__ __attribute__((aligned(16))) uint16_t lds_all[lds_bytes<NB, WV>() / 2];
+    uint16_t *lds = lds_all, *lds_a = lds_all + NB * 32 * lds_row<NB>();
     __shared__ int s_any;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int ng = min(NB * 32, G - g0);  // groups of this column pass
@@ -358,8 +377,8 @@ __global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uin
     if (threadIdx.x == 0)
         s_any = 0;
     __syncthreads();
-    for (int q = threadIdx.x; q < ng * 4; q += blockDim.x) {
-        const int g = g0 + q / 4, t = (int)(y0 >> 5) + q % 4;
+    for (int q = threadIdx.x; q < ng * WV; q += blockDim.x) {
+        const int g = g0 + q / WV, t = (int)(y0 >> 5) + q % WV;
         if (t < nt && sl_off[g + 1] > sl_off[g] && tix[(int64_t)g * (nt + 1) + t].mask != 0u)
             s_any = 1;
     }
@@ -369,7 +388,7 @@ __global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uin
 
     // where this lane's groups put the tile's logits, fetched before the
     // K loop (lane l, column block nb: group g0 + 32*nb + l%32); wave 0
-    // records where each group's run for the block's four tiles begins
+    // records where each group's run for the block's WV tiles begins
     __shared__ int64_t s_dst[NB * 32];
     __shared__ int32_t s_s0[NB * 32], s_cnt[NB * 32];
     int64_t o_off[NB];
@@ -397,7 +416,7 @@ __global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uin
         }
     }
 
-    // the block's W rows y0 .. y0+127 (rows past V read zero; never written)
+    // the block's W rows y0 .. y0+kTileRows-1 (rows past V read zero; never written)
     const int64_t rows = min((int64_t)kTileRows, (int64_t)V - y0);
     const rsrc_t w = make_rsrc(W + y0 * d, (uint32_t)(rows * d * 2));
     uint32_t voff[4];
@@ -406,15 +425,16 @@ __global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uin
         voff[i] = (uint32_t)((32 * wave + (lane >> 3) + 8 * i) * d * 2 + 16 * (lane & 7));
     f32x16 acc[NB];
     auto hsrc = [&](int r) { return h + (int64_t)(g0 + r) * ldh_g; };
-    rows_times_b<NB, kNonTemporal>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc, acc,
-                                   (int)(blockIdx.x * kPhaseRot));
+    rows_times_b<NB, 64 * WV, kNonTemporal>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc,
+                                            acc, (int)(blockIdx.x * kPhaseRot));
 
     // epilogue: the (row, group) pairs on the group's shortlist.  A group's
-    // entries for the block's four tiles are one contiguous run of its
-    // logits; the values are gathered per group in LDS (the phase buffer,
+    // entries for the block's WV tiles are one contiguous run of its logits;
+    // the values are gathered per group in LDS (the phase and A buffers,
     // free after the K loop) and each run is written with coalesced stores.
-    float *res = reinterpret_cast<float *>(lds);  // [NB*32][kTileRows]
-    static_assert(sizeof(lds) >= NB * 32 * kTileRows * sizeof(float), "LDS run buffer");
+    float *res = reinterpret_cast<float *>(lds_all);  // [NB*32][kTileRows]
+    static_assert(lds_bytes<NB, WV>() >= NB * 32 * kTileRows * (int)sizeof(float),
+                  "LDS run buffer");
     __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -441,8 +461,8 @@ __global__ __launch_bounds__(256) void head_union_kernel(int V, int d, const uin
 }
 
 // --------------------------------------------------------------- gathered
-template <int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void head_gathered_kernel(int V, int d, const uint16_t *__restrict__ W,
+template <int NB, int WV>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) void head_gathered_kernel(int V, int d, const uint16_t *__restrict__ W,
                                                             int G, int m, int n0,
                                                             const uint16_t *__restrict__ h,
                                                             int64_t ldh_g,
@@ -451,8 +471,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void h
                                                             int tiles_stride,
                                                             float *__restrict__ logits)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[NB * 32 * lds_row<NB>()];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_a[4 * kASlice];
+    constexpr int kTileRows = tile_rows<WV>();
+    __shared__ __attribute__((aligned(16))) uint16_t lds_all[lds_bytes<NB, WV>() / 2];
+    uint16_t *lds = lds_all, *lds_a = lds_all + NB * 32 * lds_row<NB>();
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int g = blockIdx.x % G;  // neighbouring workgroups: same tile, other groups
     const int64_t off = sl_off[g], len = sl_off[g + 1] - off;
@@ -472,7 +493,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void h
             voff[i] = (uint32_t)__shfl(yrow, (lane >> 3) + 8 * i) * (uint32_t)d * 2u +
                       16u * (lane & 7);
         f32x16 acc[NB];
-        rows_times_b<NB, kCached>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc, 0);
+        rows_times_b<NB, 64 * WV, kCached>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc,
+                                           0);
         // epilogue: column = head row (node), row = shortlist entry; the
         // entry of accumulator row i was loaded by lanes i and i + 32
 #pragma unroll
@@ -511,6 +533,66 @@ bool head_mfma_applies(bool bf16, int V, int d, int G, int m)
     return m >= kGatheredMinRows && (int64_t)V * d * 2 + 4096 <= (int64_t)UINT32_MAX;
 }
 
+namespace {
+
+// Column passes of up to 64 groups.  Passes over 33..64 groups run 256-row
+// tiles (8 waves; measured 444 vs 471 us at 64 groups on the Gemma shape),
+// passes over up to 32 groups 128-row tiles, two workgroups per compute unit
+// (208 vs 274 us at 32 groups on the Llama shape).
+hipError_t union_passes(hipStream_t s, int V, int d, const uint16_t *Wb, int G, const uint16_t *hb,
+                        int64_t ldh_g, const int64_t *sl_off, const TileIx *tix, int nt,
+                        float *logits, hipEvent_t t1)
+{
+    for (int g0 = 0; g0 < G; g0 += 64) {
+        hipEvent_t stop = g0 + 64 >= G ? t1 : nullptr;
+        hipError_t e;
+        if (G - g0 > 32)
+            e = launch_timed(head_union_kernel<2, 8>, dim3((V + tile_rows<8>() - 1) / tile_rows<8>()),
+                             dim3(512), s, nullptr, stop, V, d, Wb, G, g0, hb, ldh_g, sl_off, tix,
+                             nt, logits);
+        else
+            e = launch_timed(head_union_kernel<1, 4>, dim3((V + tile_rows<4>() - 1) / tile_rows<4>()),
+                             dim3(256), s, nullptr, stop, V, d, Wb, G, g0, hb, ldh_g, sl_off, tix,
+                             nt, logits);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+// gathered: persistent-style grid (one 8-wave or two 4-wave workgroups per
+// compute unit), groups interleaved
+template <int WV>
+hipError_t gathered_passes(hipStream_t s, int V, int d, const uint16_t *Wb, int G, int m,
+                           const uint16_t *hb, int64_t ldh_g, const int64_t *sl_off,
+                           const int32_t *sl_ids, int64_t max_rows, float *logits, hipEvent_t t0,
+                           hipEvent_t t1)
+{
+    int64_t per_group = (max_rows + tile_rows<WV>() - 1) / tile_rows<WV>();
+    const int64_t want = ((8 / WV) * (int64_t)device_cu_count() + G - 1) / G;
+    if (per_group > want)
+        per_group = want;
+    if (per_group < 1)
+        per_group = 1;
+    const unsigned blocks = (unsigned)(per_group * G);
+    const int ts = (int)per_group;
+    for (int n0 = 0; n0 < m; n0 += 64) {  // passes of up to 64 head rows
+        hipEvent_t start = n0 == 0 ? t0 : nullptr, stop = n0 + 64 >= m ? t1 : nullptr;
+        hipError_t e;
+        if (m - n0 > 32)
+            e = launch_timed(head_gathered_kernel<2, WV>, dim3(blocks), dim3(64 * WV), s, start,
+                             stop, V, d, Wb, G, m, n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
+        else
+            e = launch_timed(head_gathered_kernel<1, WV>, dim3(blocks), dim3(64 * WV), s, start,
+                             stop, V, d, Wb, G, m, n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
 hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, int m,
                             const void *h, int64_t ldh_g, const int64_t *sl_off,
                             const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
@@ -518,7 +600,6 @@ hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, i
 {
     const uint16_t *Wb = reinterpret_cast<const uint16_t *>(W);
     const uint16_t *hb = reinterpret_cast<const uint16_t *>(h);
-    hipError_t e;
     if (m == 1) {
         const int nt = (V + 31) / 32;
         TileIx *tix = reinterpret_cast<TileIx *>(ws);
@@ -529,44 +610,14 @@ hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, i
             blocks = 65535;
         if (blocks < 1)
             blocks = 1;
-        if ((e = launch_timed(union_index_kernel, dim3((unsigned)blocks), dim3(256), s, t0, nullptr,
-                              G, nt, V, sl_off, sl_ids, tix, logits)) != hipSuccess)
-            return e;
-        const unsigned tiles = (unsigned)((V + kTileRows - 1) / kTileRows);
-        for (int g0 = 0; g0 < G; g0 += 64) {  // column passes of up to 64 groups
-            hipEvent_t stop = g0 + 64 >= G ? t1 : nullptr;
-            if (G - g0 > 32)
-                e = launch_timed(head_union_kernel<2>, dim3(tiles), dim3(256), s, nullptr, stop, V, d,
-                                 Wb, G, g0, hb, ldh_g, sl_off, (const TileIx *)tix, nt, logits);
-            else
-                e = launch_timed(head_union_kernel<1>, dim3(tiles), dim3(256), s, nullptr, stop, V, d,
-                                 Wb, G, g0, hb, ldh_g, sl_off, (const TileIx *)tix, nt, logits);
-            if (e != hipSuccess)
-                return e;
-        }
-        return hipSuccess;
-    }
-    // gathered: persistent-style grid, groups interleaved
-    int64_t per_group = (max_rows + kTileRows - 1) / kTileRows;
-    const int64_t want = (2LL * device_cu_count() + G - 1) / G;
-    if (per_group > want)
-        per_group = want;
-    if (per_group < 1)
-        per_group = 1;
-    const unsigned blocks = (unsigned)(per_group * G);
-    const int ts = (int)per_group;
-    for (int n0 = 0; n0 < m; n0 += 64) {  // passes of up to 64 head rows
-        hipEvent_t start = n0 == 0 ? t0 : nullptr, stop = n0 + 64 >= m ? t1 : nullptr;
-        if (m - n0 > 32)
-            e = launch_timed(head_gathered_kernel<2>, dim3(blocks), dim3(256), s, start, stop, V, d,
-                             Wb, G, m, n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
-        else
-            e = launch_timed(head_gathered_kernel<1>, dim3(blocks), dim3(256), s, start, stop, V, d,
-                             Wb, G, m, n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
+        hipError_t e = launch_timed(union_index_kernel, dim3((unsigned)blocks), dim3(256), s, t0,
+                                    nullptr, G, nt, V, sl_off, sl_ids, tix, logits);
         if (e != hipSuccess)
             return e;
+        return union_passes(s, V, d, Wb, G, hb, ldh_g, sl_off, tix, nt, logits, t1);
     }
-    return hipSuccess;
+    return gathered_passes<8>(s, V, d, Wb, G, m, hb, ldh_g, sl_off, sl_ids, max_rows, logits, t0,
+                              t1);
 }
 
 }  // namespace ds
