@@ -475,9 +475,12 @@ size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r, int64_t max_le
 {
     if (B <= 0 || T <= 0 || V <= 0 || r <= 0 || max_len <= 0)
         return 0;
+    // batched heads: two tile indices (positions alternate; the build of
+    // position t+1 writes one while head t reads the other)
+    const size_t tix = B >= ds::kUnionMinGroups ? 2 * round_up(ds::tile_index_bytes(B, V), 256) : 0;
     return round_up(ds_router_workspace_bytes(B, r), 256) +
            round_up(ds::build_ws_bytes(B, V), 256) + round_up(ds::sample_ws_bytes(B, max_len), 256) +
-           ds::head_ws_bytes(B, 1, V);
+           tix;
 }
 
 ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_args *a)
@@ -525,7 +528,12 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
     float *z = reinterpret_cast<float *>(a->ws);
     void *bws = reinterpret_cast<char *>(a->ws) + round_up(ds_router_workspace_bytes(B, a->r), 256);
     void *sws = reinterpret_cast<char *>(bws) + round_up(ds::build_ws_bytes(B, a->V), 256);
-    void *hws = reinterpret_cast<char *>(sws) + round_up(ds::sample_ws_bytes(B, len_bound), 256);
+    char *tws = reinterpret_cast<char *>(sws) + round_up(ds::sample_ws_bytes(B, len_bound), 256);
+    // batched bf16 heads run on the matrix cores over the tile index that the
+    // build writes alongside each shortlist (slot t % 2); build t+2 reuses a
+    // slot only after sample t, hence after head t
+    const bool prebuilt = ds::head_mfma_applies(a->dtype == DS_BF16, a->V, a->d, B, 1);
+    const size_t tslot = round_up(ds::tile_index_bytes(B, a->V), 256);
     // events: [0, T) build of position t done, [T, 2T) h[t+1] ready (token
     // t-1 sampled), 2T fork
     if (g_events.ensure(2 * (size_t)T + 1) != hipSuccess)
@@ -550,7 +558,9 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
         if (err == hipSuccess)
             err = ds::build_launch(rs, B, a->M, a->V, a->sel + rb * a->M, a->n_sel + rb,
                                    a->cluster_of, a->cluster_index, a->capacity, a->sl_off + rb,
-                                   a->sl_ids, a->err_flag, bws);
+                                   a->sl_ids, a->err_flag, bws,
+                                   prebuilt ? reinterpret_cast<ds::TileIx *>(tws + (t & 1) * tslot)
+                                            : nullptr);
         if (err == hipSuccess)
             err = hipEventRecord(g_events.ev[t], rs);
         // h[t+1] (read by head t and by router t+1) is ready once token t-1
@@ -561,12 +571,17 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
             err = hipEventRecord(g_events.ev[T + t], hs);
         if (err == hipSuccess)
             err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
-        if (err == hipSuccess)
-            err = ds::head_launch(hs, bf16, a->V, a->d, a->W_pos ? a->W_pos[t] : a->W, B, 1,
-                                  hb + (size_t)(t + 1) * a->d * e, ldh, a->sl_off + rb, a->sl_ids,
-                                  a->max_rows[t], a->logits, hws,
-                                  a->head_events ? a->head_events[2 * t] : nullptr,
-                                  a->head_events ? a->head_events[2 * t + 1] : nullptr);
+        hipEvent_t h0 = a->head_events ? a->head_events[2 * t] : nullptr;
+        hipEvent_t h1 = a->head_events ? a->head_events[2 * t + 1] : nullptr;
+        const void *Wt = a->W_pos ? a->W_pos[t] : a->W;
+        if (err == hipSuccess && prebuilt)
+            err = ds::head_union_prebuilt_launch(
+                hs, a->V, a->d, Wt, B, hb + (size_t)(t + 1) * a->d * e, ldh, a->sl_off + rb,
+                reinterpret_cast<const ds::TileIx *>(tws + (t & 1) * tslot), a->logits, h0, h1);
+        else if (err == hipSuccess)
+            err = ds::head_launch(hs, bf16, a->V, a->d, Wt, B, 1, hb + (size_t)(t + 1) * a->d * e,
+                                  ldh, a->sl_off + rb, a->sl_ids, a->max_rows[t], a->logits,
+                                  nullptr, h0, h1);
         if (err == hipSuccess)
             err = ds::sample_launch(hs, B, 1, a->sl_off + rb, a->sl_ids, a->logits, a->temperature,
                                     a->u_draft + rb, a->token + rb, a->q, a->max_len[t], sws);

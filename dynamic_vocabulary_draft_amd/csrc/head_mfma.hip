@@ -243,16 +243,11 @@ constexpr int lds_bytes()
 }
 
 // ------------------------------------------------------------------ union
-// Tile index of the shortlists, per group g and 32-token tile t (t = 0..nt,
-// nt = ceil(V/32)): start = first index j of S_g with S_g[j] >= 32*t, mask =
-// the set of offsets y - 32*t of the tile's ids y < V on S_g.  Shortlists are
-// ascending, so a tile's entries are contiguous and the first of them builds
-// the tile's mask from at most 32 following entries.  Written only for
-// non-empty groups.  Entries with ids outside [0, V) get their NaN logit here.
-struct TileIx {
-    int32_t start;
-    uint32_t mask;
-};
+// Tile index (TileIx) of the shortlists, built here from the shortlists
+// themselves: shortlists are ascending, so a tile's entries are contiguous
+// and the first of them builds the tile's mask from at most 32 following
+// entries.  Written only for non-empty groups.  Entries with ids outside
+// [0, V) get their NaN logit here.
 
 // OR over the 64 lanes (DPP within rows, then the four row results)
 __device__ __forceinline__ uint32_t wave_or(uint32_t v)
@@ -515,12 +510,17 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 }  // namespace
 
+size_t tile_index_bytes(int G, int V)
+{
+    const int64_t nt = ((int64_t)V + 31) / 32;
+    return (size_t)G * (size_t)(nt + 1) * sizeof(TileIx);
+}
+
 size_t head_ws_bytes(int G, int m, int V)
 {
     if (G < kUnionMinGroups || m != 1)
         return 0;
-    const int64_t nt = ((int64_t)V + 31) / 32;
-    return (size_t)G * (size_t)(nt + 1) * sizeof(TileIx) + 256;
+    return tile_index_bytes(G, V) + 256;
 }
 
 bool head_mfma_applies(bool bf16, int V, int d, int G, int m)
@@ -541,18 +541,18 @@ namespace {
 // (208 vs 274 us at 32 groups on the Llama shape).
 hipError_t union_passes(hipStream_t s, int V, int d, const uint16_t *Wb, int G, const uint16_t *hb,
                         int64_t ldh_g, const int64_t *sl_off, const TileIx *tix, int nt,
-                        float *logits, hipEvent_t t1)
+                        float *logits, hipEvent_t t0, hipEvent_t t1)
 {
     for (int g0 = 0; g0 < G; g0 += 64) {
-        hipEvent_t stop = g0 + 64 >= G ? t1 : nullptr;
+        hipEvent_t start = g0 == 0 ? t0 : nullptr, stop = g0 + 64 >= G ? t1 : nullptr;
         hipError_t e;
         if (G - g0 > 32)
             e = launch_timed(head_union_kernel<2, 8>, dim3((V + tile_rows<8>() - 1) / tile_rows<8>()),
-                             dim3(512), s, nullptr, stop, V, d, Wb, G, g0, hb, ldh_g, sl_off, tix,
+                             dim3(512), s, start, stop, V, d, Wb, G, g0, hb, ldh_g, sl_off, tix,
                              nt, logits);
         else
             e = launch_timed(head_union_kernel<1, 4>, dim3((V + tile_rows<4>() - 1) / tile_rows<4>()),
-                             dim3(256), s, nullptr, stop, V, d, Wb, G, g0, hb, ldh_g, sl_off, tix,
+                             dim3(256), s, start, stop, V, d, Wb, G, g0, hb, ldh_g, sl_off, tix,
                              nt, logits);
         if (e != hipSuccess)
             return e;
@@ -614,10 +614,20 @@ hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, i
                                     nullptr, G, nt, V, sl_off, sl_ids, tix, logits);
         if (e != hipSuccess)
             return e;
-        return union_passes(s, V, d, Wb, G, hb, ldh_g, sl_off, tix, nt, logits, t1);
+        return union_passes(s, V, d, Wb, G, hb, ldh_g, sl_off, tix, nt, logits, nullptr, t1);
     }
     return gathered_passes<8>(s, V, d, Wb, G, m, hb, ldh_g, sl_off, sl_ids, max_rows, logits, t0,
                               t1);
+}
+
+hipError_t head_union_prebuilt_launch(hipStream_t s, int V, int d, const void *W, int G,
+                                      const void *h, int64_t ldh_g, const int64_t *sl_off,
+                                      const TileIx *tix, float *logits, hipEvent_t t0,
+                                      hipEvent_t t1)
+{
+    return union_passes(s, V, d, reinterpret_cast<const uint16_t *>(W), G,
+                        reinterpret_cast<const uint16_t *>(h), ldh_g, sl_off, tix, (V + 31) / 32,
+                        logits, t0, t1);
 }
 
 }  // namespace ds

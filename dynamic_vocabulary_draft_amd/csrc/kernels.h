@@ -21,10 +21,22 @@ size_t index_bytes(int M, int V);
 hipError_t index_launch(hipStream_t s, int M, int V, const int32_t *cluster_of, int32_t *index,
                         int32_t *err_flag);
 size_t build_ws_bytes(int n, int V);
+
+// Tile index of a set of ascending shortlists, per row g and 32-token tile t
+// (t = 0..nt, nt = ceil(V/32), row stride nt + 1): start = the first
+// position j of S_g with S_g[j] >= 32*t, mask = the offsets y - 32*t of the
+// tile's ids y < V on S_g.  The batched matrix-core head reads it.
+struct TileIx {
+    int32_t start;
+    uint32_t mask;
+};
+
+// tix (may be null): the build also writes the tile index of the rows it
+// builds for tiles 0..nt-1 (the head reads no other)
 hipError_t build_launch(hipStream_t s, int n, int M, int V, const int32_t *sel,
                         const int32_t *n_sel, const int32_t *cluster_of, const int32_t *index,
                         int64_t capacity, int64_t *sl_off, int32_t *sl_ids, int32_t *err_flag,
-                        void *ws);
+                        void *ws, TileIx *tix = nullptr);
 
 // gathered head: GEMV kernel (few head rows, few groups or fp32), or the
 // matrix-core kernels (bf16 with >= kUnionMinGroups single-row groups, or
@@ -39,6 +51,13 @@ hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, i
                             const void *h, int64_t ldh_g, const int64_t *sl_off,
                             const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,
                             hipEvent_t t0, hipEvent_t t1);
+// batched matrix-core head (head_mfma_applies with m = 1) over shortlists
+// whose tile index tix the build already wrote: no index pass
+size_t tile_index_bytes(int G, int V);
+hipError_t head_union_prebuilt_launch(hipStream_t s, int V, int d, const void *W, int G,
+                                      const void *h, int64_t ldh_g, const int64_t *sl_off,
+                                      const TileIx *tix, float *logits, hipEvent_t t0,
+                                      hipEvent_t t1);
 hipError_t head_launch(hipStream_t s, bool bf16, int V, int d, const void *W, int G, int m,
                        const void *h, int64_t ldh_g, const int64_t *sl_off,
                        const int32_t *sl_ids, int64_t max_rows, float *logits, void *ws,

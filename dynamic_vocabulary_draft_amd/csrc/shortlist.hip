@@ -17,7 +17,10 @@
 //          of cluster_of, and writes them at row base + chunk offset + a
 //          block-wide exclusive scan of per-thread counts -- ascending token
 //          id without any sort.  For n = 1 the row base is sl_off[0] and
-//          chunk 0 writes sl_off[1].
+//          chunk 0 writes sl_off[1].  Optionally it also writes the row's
+//          tile index for the batched head: per 32-token tile (two threads'
+//          16 tokens) the tile's first shortlist position and membership
+//          mask, which the compaction has in hand.
 // All integer, hence bit-exact; no workgroup waits on another.
 #include "common.h"
 #include "kernels.h"
@@ -195,7 +198,8 @@ __global__ __launch_bounds__(kThreads) void build_compact_kernel(
     int n, int M, int V, int nchunks, const int32_t *__restrict__ sel,
     const int32_t *__restrict__ n_sel, const int32_t *__restrict__ cluster_of,
     const int32_t *__restrict__ index, int64_t capacity, int64_t *sl_off,
-    int32_t *__restrict__ sl_ids, int32_t *err_flag, const int64_t *__restrict__ row_base)
+    int32_t *__restrict__ sl_ids, int32_t *err_flag, const int64_t *__restrict__ row_base,
+    TileIx *__restrict__ tix)
 {
     __shared__ uint32_t bm[kMaxBitmapWords];
     __shared__ int64_t sh[kWave + 1];
@@ -222,7 +226,16 @@ __global__ __launch_bounds__(kThreads) void build_compact_kernel(
     const int64_t y0 = (int64_t)chunk * kBuildChunk + threadIdx.x * kPerThread;
     uint32_t mask = y0 < V ? token_mask(bm, M, V, cluster_of, y0) : 0u;
     int64_t tot;
-    int64_t pos = block_excl_scan_i64(__popc(mask), sh, &tot) + base + chunk_off;
+    const int64_t rel = block_excl_scan_i64(__popc(mask), sh, &tot) + chunk_off;
+    int64_t pos = rel + base;
+    static_assert(kPerThread == 16, "two threads per 32-token tile");
+    if (tix) {  // block-uniform
+        const uint32_t hi = (uint32_t)__shfl_down((int)mask, 1);  // the odd neighbour's 16 tokens
+        const int nt = (V + 31) / 32;
+        const int64_t t = y0 >> 5;
+        if ((threadIdx.x & 1) == 0 && t < nt)
+            tix[(int64_t)row * (nt + 1) + t] = TileIx{(int32_t)rel, mask | (hi << 16)};
+    }
     while (mask) {
         int e = __ffs(mask) - 1;
         mask &= mask - 1;
@@ -263,7 +276,7 @@ size_t build_ws_bytes(int n, int V)
 hipError_t build_launch(hipStream_t s, int n, int M, int V, const int32_t *sel,
                         const int32_t *n_sel, const int32_t *cluster_of, const int32_t *index,
                         int64_t capacity, int64_t *sl_off, int32_t *sl_ids, int32_t *err_flag,
-                        void *ws)
+                        void *ws, TileIx *tix)
 {
     const int nchunks = (V + kBuildChunk - 1) / kBuildChunk;
     int64_t *row_base = reinterpret_cast<int64_t *>(reinterpret_cast<char *>(ws) + 256);
@@ -276,7 +289,7 @@ hipError_t build_launch(hipStream_t s, int n, int M, int V, const int32_t *sel,
     }
     hipLaunchKernelGGL(build_compact_kernel, dim3(nchunks, n), dim3(kThreads), 0, s, n, M, V,
                        nchunks, sel, n_sel, cluster_of, index, capacity, sl_off, sl_ids, err_flag,
-                       (const int64_t *)row_base);
+                       (const int64_t *)row_base, tix);
     return hipGetLastError();
 }
 

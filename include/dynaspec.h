@@ -422,7 +422,11 @@ ds_status ds_router_train_step(hipStream_t s, const ds_router_train_args *a);
  * sampler of position t-2 (at the start for t = 1), and the router,
  * selection and build of position t run while the head and sampler of
  * position t-1 work.  Rows are position-major (row t*B + b), the
- * layout ds_verify_reject reads.  Every pointer is a device pointer except
+ * layout ds_verify_reject reads.  With B >= 8 bf16 sequences the build also
+ * writes each shortlist's 32-token tile index (first position and
+ * membership mask per tile, two slots of the workspace used alternately),
+ * so the head walks W once on the matrix cores without an index pass of
+ * its own; the logits are those of ds_gathered_lm_head.  Every pointer is a device pointer except
  * max_rows, max_len, W_pos and head_events (host arrays).  On return all work is
  * enqueued and head_stream waits for everything enqueued on router_stream.
  * Optional fields:

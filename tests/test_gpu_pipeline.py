@@ -32,6 +32,10 @@ def small_configs():
                                           budget=syn.linear_budget(2000, 1000, 3)),
         "small-tree": syn.shrink(syn.CONFIGS[3], V=12000, d=520, M=80, r=64, B=3,
                                  budget=(3000,), tree_nodes=5),
+        # batched head on the matrix cores over the build's tile index: a
+        # ragged last 32-token tile and a partial last build chunk
+        "small-bf16-b12": syn.shrink(c1, V=9001, d=264, M=60, r=64, B=12, T=3,
+                                     budget=syn.linear_budget(3000, 1500, 3)),
     }
 
 
@@ -172,7 +176,7 @@ def test_step_full_size(oracle_lib, index):
     check_stagewise(wl, r, head_samples=256 if index != 2 else 64, seed=index)
 
 
-@pytest.mark.parametrize("name", ["tiny-fp32", "small-bf16-b3", "small-tree"])
+@pytest.mark.parametrize("name", ["tiny-fp32", "small-bf16-b3", "small-tree", "small-bf16-b12"])
 def test_graph_replay_matches_eager(oracle_lib, name):
     """A captured step replayed three times, with eager work and
     synchronisation between replays, reproduces the eager step bit for bit."""
