@@ -180,7 +180,7 @@ const char *ds_version(void) { return "dynaspec-mi355x 0.1 gfx950"; }
 
 size_t ds_router_workspace_bytes(int n, int r)
 {
-    return n > 0 && r > 0 ? (size_t)n * (size_t)r * sizeof(float) : 0;
+    return n > 0 && r > 0 ? ds::router_ws_bytes(n, r) : 0;
 }
 
 ds_status ds_router_score(hipStream_t s, ds_dtype dt, int n, int d, int r, int M, ds_act act,

@@ -508,6 +508,99 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
 }
 
+// ------------------------------------------------------- router, layer 1
+// The router's first layer for a batch of n >= 8 bf16 inputs is a dense
+// n x r x d contraction (32 x 1024 x 4096 at the Llama shape: 8 MB of
+// weights, 268 MFLOP): split over k into windows of kRouterWin elements so
+// that about a hundred workgroups stream the weights at once.  A workgroup
+// takes 128 weight rows (4 waves x 32) of one window and up to 64 inputs
+// (columns): every W load of the window is issued at once, the inputs'
+// window is staged in LDS, and the slices go through the waves' LDS slices
+// into MFMA order as in the heads.  part[w][c][i] holds window w's sum for
+// input c0 + c of the current column pass and weight row i;
+// router_l1_finish adds the windows in order.  Passes run in stream order
+// and reuse part.
+constexpr int kRouterWin = 256;  // k-window (4 slices)
+constexpr int kRouterCols = 64;  // inputs per column pass
+constexpr int kRouterMaxWin = 8192 / kRouterWin;  // d <= 8192
+
+template <int NB>
+__global__ __launch_bounds__(256) void router_l1_kernel(int n, int d, int r,
+                                                        const uint16_t *__restrict__ W1,
+                                                        const uint16_t *__restrict__ h,
+                                                        int64_t ldh, int c0,
+                                                        float *__restrict__ part)
+{
+    static_assert(phase_len<NB>() >= kRouterWin, "the window is one staged phase");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NB * 32 * lds_row<NB>()];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[4 * kASlice];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int row0 = blockIdx.x * 128, win = blockIdx.y;
+    const int k0 = win * kRouterWin, klen = min(kRouterWin, d - k0);
+    const int rows = min(128, r - row0), ncols = min(kRouterCols, n - c0);
+    const int nsl = (klen + kKs - 1) / kKs;
+    // rows past the tile read zero (the range ends with the last row's window)
+    const rsrc_t w = make_rsrc(W1 + (int64_t)row0 * d + k0,
+                               (uint32_t)((rows - 1) * d * 2 + klen * 2));
+    uint32_t voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        voff[i] = (uint32_t)((32 * wave + (lane >> 3) + 8 * i) * d * 2 + 16 * (lane & 7));
+    u32x4 ld[4][4];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+        if (sl < nsl)
+            load_a<kNonTemporal>(w, voff, sl * kKs, ld[sl]);
+    const uint16_t *hb = h + (int64_t)c0 * ldh + k0;
+    auto hsrc = [&](int c) { return hb + (int64_t)c * ldh; };
+    u32x4 hv[stage_n<256>()];
+    load_phase<NB, 256>(hv, 0, klen, ncols, hsrc);
+    store_phase<NB, 256>(lds, hv, 0, klen, ncols);
+    __syncthreads();
+    f32x16 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = f32x16{};
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+        if (sl < nsl)
+            slice_mma<NB>(ld[sl], lds_a + wave * kASlice, lds, sl * kKs, sl * kKs, klen, acc);
+    // register q of lane l: weight row 8*(q/4) + 4*(l/32) + q%4 of the wave's
+    // 32, input (l%32) + 32*nb
+    float *pw = part + (int64_t)win * kRouterCols * r;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int c = nb * 32 + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = 32 * wave + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+            if (c < ncols && i < rows)
+                pw[(int64_t)c * r + row0 + i] = acc[nb][q];
+        }
+    }
+}
+
+// z[c0 + c][i] = act(sum over windows w in order of part[w][c][i] + b1[i])
+__global__ __launch_bounds__(256) void router_l1_finish(int r, int nwin, int c0, int ncols,
+                                                        const float *__restrict__ part,
+                                                        const uint16_t *__restrict__ b1, int act,
+                                                        float *__restrict__ z)
+{
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= (int64_t)ncols * r)
+        return;
+    float s = 0.f;
+    for (int w = 0; w < nwin; ++w)
+        s += part[(int64_t)w * kRouterCols * r + q];
+    if (b1)
+        s += __uint_as_float((uint32_t)b1[q % r] << 16);
+    if (act == DS_RELU)
+        s = fmaxf(s, 0.f);
+    else if (act == DS_SILU)
+        s = s / (1.f + expf(-s));
+    z[(int64_t)c0 * r + q] = s;
+}
+
 }  // namespace
 
 size_t tile_index_bytes(int G, int V)
@@ -618,6 +711,39 @@ hipError_t head_mfma_launch(hipStream_t s, int V, int d, const void *W, int G, i
     }
     return gathered_passes<8>(s, V, d, Wb, G, m, hb, ldh_g, sl_off, sl_ids, max_rows, logits, t0,
                               t1);
+}
+
+size_t router_l1_ws_bytes(int r)
+{
+    return (size_t)kRouterMaxWin * kRouterCols * (size_t)r * sizeof(float);
+}
+
+hipError_t router_l1_mfma_launch(hipStream_t s, int n, int d, int r, int act, const void *h,
+                                 int64_t ldh, const void *W1, const void *b1, float *z, float *part)
+{
+    const int nwin = (d + kRouterWin - 1) / kRouterWin;
+    const dim3 grid((unsigned)((r + 127) / 128), (unsigned)nwin);
+    const uint16_t *Wb = reinterpret_cast<const uint16_t *>(W1);
+    const uint16_t *hb = reinterpret_cast<const uint16_t *>(h);
+    for (int c0 = 0; c0 < n; c0 += kRouterCols) {
+        const int nc = n - c0 < kRouterCols ? n - c0 : kRouterCols;
+        if (nc > 32)
+            hipLaunchKernelGGL(router_l1_kernel<2>, grid, dim3(256), 0, s, n, d, r, Wb, hb, ldh, c0,
+                               part);
+        else
+            hipLaunchKernelGGL(router_l1_kernel<1>, grid, dim3(256), 0, s, n, d, r, Wb, hb, ldh, c0,
+                               part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        const int64_t cnt = (int64_t)nc * r;
+        hipLaunchKernelGGL(router_l1_finish, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s,
+                           r, nwin, c0, nc, (const float *)part,
+                           reinterpret_cast<const uint16_t *>(b1), act, z);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t head_union_prebuilt_launch(hipStream_t s, int V, int d, const void *W, int G,

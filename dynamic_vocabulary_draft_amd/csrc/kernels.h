@@ -7,9 +7,18 @@
 
 namespace ds {
 
+// workspace z: n*r floats, then (n >= kRouterMfmaMin, for bf16 routers) the
+// first layer's window partial sums, router_l1_ws_bytes(r) bytes
+constexpr int kRouterMfmaMin = 8;
+size_t router_ws_bytes(int n, int r);
 hipError_t router_launch(hipStream_t s, bool bf16, int n, int d, int r, int M, int act,
                          const void *h, int64_t ldh, const void *W1, const void *b1,
                          const void *W2, const void *b2, float *scores, float *z);
+// first layer on the matrix cores (bf16, d <= 8192): z = act(W1 h + b1) via
+// k-window partial sums in part (router_l1_ws_bytes(r) bytes)
+size_t router_l1_ws_bytes(int r);
+hipError_t router_l1_mfma_launch(hipStream_t s, int n, int d, int r, int act, const void *h,
+                                 int64_t ldh, const void *W1, const void *b1, float *z, float *part);
 
 hipError_t select_launch(hipStream_t s, int n, int M, const float *scores,
                          const int32_t *cluster_size, int kind, const int32_t *budget,

@@ -3,14 +3,17 @@
 // Modules: Router" and "Key Hyperparameters": 2-layer MLP; "Problem
 // Definition": input H_{t-1}).
 //
-// Both layers are small-n matrix-vector products against weights that are
-// read once from HBM (8 MB + 2 MB bf16 for the Llama-shaped router), so
-// each is a GEMV: a wave owns one weight row and up to 8 input rows, holds
+// For a few inputs both layers are matrix-vector products against weights
+// that are read once from HBM (8 MB + 2 MB bf16 for the Llama-shaped
+// router), so each is a GEMV: a wave owns one weight row and up to 8 input
+// rows, holds
 // the whole weight row in registers (16-byte loads per lane, 1 KB per wave
 // per load instruction, all issued at once), and reduces each partial sum
 // across the wave with a fixed DPP order.  Bias and activation are fused
 // into the epilogue; the hidden activations z stay fp32.  Weight rows are
-// limited to 8192 elements (KC <= 16 chunks of 8 per lane).
+// limited to 8192 elements (KC <= 16 chunks of 8 per lane).  A batch of
+// 8 or more bf16 inputs runs the first layer on the matrix cores instead
+// (head_mfma.hip), with the same fp32 accumulation of exact bf16 products.
 #include "common.h"
 #include "kernels.h"
 
@@ -167,14 +170,29 @@ hipError_t launch_gemv(hipStream_t s, int n, int K, int R, const void *A, const 
 
 }  // namespace
 
+size_t router_ws_bytes(int n, int r)
+{
+    const size_t zb = ((size_t)n * (size_t)r * sizeof(float) + 255) / 256 * 256;
+    return zb + (n >= kRouterMfmaMin ? router_l1_ws_bytes(r) : 0);
+}
+
 hipError_t router_launch(hipStream_t s, bool bf16, int n, int d, int r, int M, int act,
                          const void *h, int64_t ldh, const void *W1, const void *b1,
                          const void *W2, const void *b2, float *scores, float *z)
 {
     hipError_t e;
-    // layer 1: z = act(W1 h + b1), act encoded as act + 1 (0 = identity)
-    e = bf16 ? launch_gemv<true, true>(s, n, d, r, W1, b1, h, ldh, act + 1, z, r)
-             : launch_gemv<false, false>(s, n, d, r, W1, b1, h, ldh, act + 1, z, r);
+    // layer 1: z = act(W1 h + b1).  A batch of bf16 inputs is a dense
+    // contraction: matrix cores, split over k (the GEMV below re-reads each
+    // weight row once per 8 inputs); else the GEMV with act encoded as
+    // act + 1 (0 = identity)
+    if (bf16 && n >= kRouterMfmaMin) {
+        float *part = reinterpret_cast<float *>(
+            reinterpret_cast<char *>(z) + ((size_t)n * (size_t)r * sizeof(float) + 255) / 256 * 256);
+        e = router_l1_mfma_launch(s, n, d, r, act, h, ldh, W1, b1, z, part);
+    } else {
+        e = bf16 ? launch_gemv<true, true>(s, n, d, r, W1, b1, h, ldh, act + 1, z, r)
+                 : launch_gemv<false, false>(s, n, d, r, W1, b1, h, ldh, act + 1, z, r);
+    }
     if (e != hipSuccess)
         return e;
     // layer 2: scores = W2 z + b2 (z is fp32)

@@ -90,7 +90,10 @@ const char *ds_version(void);
  * act     DS_RELU or DS_SILU.
  * W1 [r][d], b1 [r] or NULL, W2 [M][r], b2 [M] or NULL.
  * scores  [n][M] fp32 output (accumulation in fp32, z kept in fp32).
- * ws      >= ds_router_workspace_bytes(n, r) bytes (holds z).
+ * ws      >= ds_router_workspace_bytes(n, r) bytes (holds z; for n >= 8 it
+ *         also holds the first layer's partial sums over 256-element windows
+ *         of d: a batch of bf16 inputs runs that layer on the matrix cores,
+ *         still bf16 products accumulated in fp32).
  */
 size_t ds_router_workspace_bytes(int n, int r);
 ds_status ds_router_score(hipStream_t s, ds_dtype dt, int n, int d, int r, int M, ds_act act,

@@ -66,6 +66,12 @@ def _cpu(t):
     (True, syn.ACT_SILU, 7, 264, 136, 100),
     (True, syn.ACT_SILU, 1, 4096, 1024, 1024),
     (True, syn.ACT_SILU, 64, 3840, 1024, 2048),
+    # batches of >= 8 bf16 inputs: first layer on the matrix cores, split over
+    # 256-element windows of d (a partial last window, a ragged last row tile,
+    # two column passes)
+    (True, syn.ACT_SILU, 8, 264, 136, 100),
+    (True, syn.ACT_SILU, 32, 4096, 1024, 1024),
+    (True, syn.ACT_RELU, 70, 520, 200, 64),
 ])
 def test_router_parity(N, oracle_lib, bf16, act, n, d, r, M):
     g = np.random.default_rng(100 + d)

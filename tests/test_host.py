@@ -48,7 +48,9 @@ def test_status_strings_and_version(N):
 
 
 def test_workspace_queries(N):
-    assert N.router_workspace_bytes(64, 1024) == 64 * 1024 * 4
+    assert N.router_workspace_bytes(4, 1024) == 4 * 1024 * 4
+    # 8 or more inputs: plus the first layer's partial sums, 32 windows x 64 inputs
+    assert N.router_workspace_bytes(64, 1024) == 64 * 1024 * 4 + 32 * 64 * 1024 * 4
     assert N.router_workspace_bytes(0, 4) == 0
     nch = (262144 + 4095) // 4096
     assert N.build_workspace_bytes(64, 262144) == 256 + 64 * 8
