@@ -544,47 +544,94 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
     hipError_t err = hipEventRecord(fork, hs);
     if (err == hipSuccess)
         err = hipStreamWaitEvent(rs, fork, 0);
-    for (int t = 0; t < T && err == hipSuccess; ++t) {
+    auto router_at = [&](hipStream_t st, int t) {  // router layers of position t (reads h[:, t])
         const int64_t rb = (int64_t)t * B;
-        if (t > 0)  // h[t] (H_{t-1}) exists once token t-2 is sampled
-            err = hipStreamWaitEvent(rs, g_events.ev[T + t - 1], 0);
-        if (err == hipSuccess)
-            err = ds::router_launch(rs, bf16, B, a->d, a->r, a->M, a->act, hb + (size_t)t * a->d * e,
-                                ldh, a->W1, a->b1, a->W2, a->b2, a->scores + rb * a->M, z);
-        if (err == hipSuccess)
-            err = ds::select_launch(rs, B, a->M, a->scores + rb * a->M, a->cluster_size,
-                                    a->budget_kind, a->budget + rb, a->sel + rb * a->M,
-                                    a->n_sel + rb, a->sl_len + rb);
-        if (err == hipSuccess)
-            err = ds::build_launch(rs, B, a->M, a->V, a->sel + rb * a->M, a->n_sel + rb,
-                                   a->cluster_of, a->cluster_index, a->capacity, a->sl_off + rb,
-                                   a->sl_ids, a->err_flag, bws,
-                                   prebuilt ? reinterpret_cast<ds::TileIx *>(tws + (t & 1) * tslot)
-                                            : nullptr);
-        if (err == hipSuccess)
-            err = hipEventRecord(g_events.ev[t], rs);
-        // h[t+1] (read by head t and by router t+1) is ready once token t-1
-        // is sampled: the record follows sample t-1 directly, before the
-        // head stream waits for build t, so router t+1 may run alongside
-        // head t
-        if (err == hipSuccess)
-            err = hipEventRecord(g_events.ev[T + t], hs);
-        if (err == hipSuccess)
-            err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
+        return ds::router_launch(st, bf16, B, a->d, a->r, a->M, a->act, hb + (size_t)t * a->d * e,
+                                 ldh, a->W1, a->b1, a->W2, a->b2, a->scores + rb * a->M, z);
+    };
+    auto select_build_at = [&](hipStream_t st, int t) {
+        const int64_t rb = (int64_t)t * B;
+        hipError_t r = ds::select_launch(st, B, a->M, a->scores + rb * a->M, a->cluster_size,
+                                         a->budget_kind, a->budget + rb, a->sel + rb * a->M,
+                                         a->n_sel + rb, a->sl_len + rb);
+        if (r == hipSuccess)
+            r = ds::build_launch(st, B, a->M, a->V, a->sel + rb * a->M, a->n_sel + rb,
+                                 a->cluster_of, a->cluster_index, a->capacity, a->sl_off + rb,
+                                 a->sl_ids, a->err_flag, bws,
+                                 prebuilt ? reinterpret_cast<ds::TileIx *>(tws + (t & 1) * tslot)
+                                          : nullptr);
+        return r;
+    };
+    auto head_sample_at = [&](int t) {
+        const int64_t rb = (int64_t)t * B;
         hipEvent_t h0 = a->head_events ? a->head_events[2 * t] : nullptr;
         hipEvent_t h1 = a->head_events ? a->head_events[2 * t + 1] : nullptr;
         const void *Wt = a->W_pos ? a->W_pos[t] : a->W;
-        if (err == hipSuccess && prebuilt)
-            err = ds::head_union_prebuilt_launch(
+        hipError_t r;
+        if (prebuilt)
+            r = ds::head_union_prebuilt_launch(
                 hs, a->V, a->d, Wt, B, hb + (size_t)(t + 1) * a->d * e, ldh, a->sl_off + rb,
                 reinterpret_cast<const ds::TileIx *>(tws + (t & 1) * tslot), a->logits, h0, h1);
-        else if (err == hipSuccess)
-            err = ds::head_launch(hs, bf16, a->V, a->d, Wt, B, 1, hb + (size_t)(t + 1) * a->d * e,
-                                  ldh, a->sl_off + rb, a->sl_ids, a->max_rows[t], a->logits,
-                                  nullptr, h0, h1);
+        else
+            r = ds::head_launch(hs, bf16, a->V, a->d, Wt, B, 1, hb + (size_t)(t + 1) * a->d * e,
+                                ldh, a->sl_off + rb, a->sl_ids, a->max_rows[t], a->logits, nullptr,
+                                h0, h1);
+        if (r == hipSuccess)
+            r = ds::sample_launch(hs, B, 1, a->sl_off + rb, a->sl_ids, a->logits, a->temperature,
+                                  a->u_draft + rb, a->token + rb, a->q, a->max_len[t], sws);
+        return r;
+    };
+    if (!prebuilt) {
+        // events: [0, T) build of position t done, [T, 2T) h[t+1] ready
+        // (token t-1 sampled), 2T fork
+        for (int t = 0; t < T && err == hipSuccess; ++t) {
+            if (t > 0)  // h[t] (H_{t-1}) exists once token t-2 is sampled
+                err = hipStreamWaitEvent(rs, g_events.ev[T + t - 1], 0);
+            if (err == hipSuccess)
+                err = router_at(rs, t);
+            if (err == hipSuccess)
+                err = select_build_at(rs, t);
+            if (err == hipSuccess)
+                err = hipEventRecord(g_events.ev[t], rs);
+            // h[t+1] (read by head t and by router t+1) is ready once token
+            // t-1 is sampled: the record follows sample t-1 directly, before
+            // the head stream waits for build t, so router t+1 may run
+            // alongside head t
+            if (err == hipSuccess)
+                err = hipEventRecord(g_events.ev[T + t], hs);
+            if (err == hipSuccess)
+                err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
+            if (err == hipSuccess)
+                err = head_sample_at(t);
+        }
+        return hip_status(err);
+    }
+    // Batched matrix-core heads fill every compute unit, so router kernels
+    // beside them wait for the head's workgroups to retire (measured, 32
+    // sequences: the first router layer took 90-100 us beside the head, 8.5
+    // us alone).  The router layers of position t+1 therefore run on the
+    // head stream just before head t (h[:, t+1] exists then: token t-1 is
+    // sampled), and only selection and build of t+1 run beside head t.
+    // events: [0, T) build of position t done, [T, 2T) router of t done.
+    if (err == hipSuccess)
+        err = router_at(hs, 0);
+    if (err == hipSuccess)
+        err = hipEventRecord(g_events.ev[T], hs);
+    for (int t = 0; t < T && err == hipSuccess; ++t) {
+        err = hipStreamWaitEvent(rs, g_events.ev[T + t], 0);
         if (err == hipSuccess)
-            err = ds::sample_launch(hs, B, 1, a->sl_off + rb, a->sl_ids, a->logits, a->temperature,
-                                    a->u_draft + rb, a->token + rb, a->q, a->max_len[t], sws);
+            err = select_build_at(rs, t);
+        if (err == hipSuccess)
+            err = hipEventRecord(g_events.ev[t], rs);
+        if (err == hipSuccess && t + 1 < T) {
+            err = router_at(hs, t + 1);
+            if (err == hipSuccess)
+                err = hipEventRecord(g_events.ev[T + t + 1], hs);
+        }
+        if (err == hipSuccess)
+            err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
+        if (err == hipSuccess)
+            err = head_sample_at(t);
     }
     return hip_status(err);
 }

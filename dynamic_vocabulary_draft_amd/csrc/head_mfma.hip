@@ -352,12 +352,13 @@ __global__ __launch_bounds__(256) void union_index_kernel(int G, int nt, int V,
     }
 }
 
+// one 32*WV-row tile of W (tile index `tile`) against the column pass
 template <int NB, int WV>
-__global__ __launch_bounds__(64 * WV) void head_union_kernel(int V, int d, const uint16_t *__restrict__ W,
-                                                         int G, int g0, const uint16_t *__restrict__ h,
-                                                         int64_t ldh_g, const int64_t *__restrict__ sl_off,
-                                                         const TileIx *__restrict__ tix, int nt,
-                                                         float *__restrict__ logits)
+__device__ __forceinline__ void union_tile(int V, int d, const uint16_t *__restrict__ W, int G,
+                                           int g0, const uint16_t *__restrict__ h, int64_t ldh_g,
+                                           const int64_t *__restrict__ sl_off,
+                                           const TileIx *__restrict__ tix, int nt,
+                                           float *__restrict__ logits, int tile)
 {
     constexpr int kTileRows = tile_rows<WV>();
     __shared__ __attribute__((aligned(16))) uint16_t lds_all[lds_bytes<NB, WV>() / 2];
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(64 * WV) void head_union_kernel(int V, int d, const
     __shared__ int s_any;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int ng = min(NB * 32, G - g0);  // groups of this column pass
-    const int64_t y0 = (int64_t)blockIdx.x * kTileRows;
+    const int64_t y0 = (int64_t)tile * kTileRows;
     const int t32 = (int)(y0 >> 5) + wave;  // this wave's 32-token tile
 
     // skip tiles no shortlist touches
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(64 * WV) void head_union_kernel(int V, int d, const
     f32x16 acc[NB];
     auto hsrc = [&](int r) { return h + (int64_t)(g0 + r) * ldh_g; };
     rows_times_b<NB, 64 * WV, kNonTemporal>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc,
-                                            acc, (int)(blockIdx.x * kPhaseRot));
+                                            acc, tile * kPhaseRot);
 
     // epilogue: the (row, group) pairs on the group's shortlist.  A group's
     // entries for the block's WV tiles are one contiguous run of its logits;
@@ -452,6 +453,19 @@ __global__ __launch_bounds__(64 * WV) void head_union_kernel(int V, int d, const
         const int gl = q / kTileRows, k = q % kTileRows;
         if (k < s_cnt[gl])
             logits[s_dst[gl] + k] = res[q];
+    }
+}
+
+template <int NB, int WV>
+__global__ __launch_bounds__(64 * WV) void head_union_kernel(int V, int d, const uint16_t *__restrict__ W,
+                                                         int G, int g0, const uint16_t *__restrict__ h,
+                                                         int64_t ldh_g, const int64_t *__restrict__ sl_off,
+                                                         const TileIx *__restrict__ tix, int nt,
+                                                         float *__restrict__ logits, int ntiles)
+{
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        union_tile<NB, WV>(V, d, W, G, g0, h, ldh_g, sl_off, tix, nt, logits, tile);
+        __syncthreads();  // the tile's epilogue is done with the shared buffers
     }
 }
 
@@ -628,6 +642,19 @@ bool head_mfma_applies(bool bf16, int V, int d, int G, int m)
 
 namespace {
 
+// Persistent grid over ntiles tiles with at most `slots` workgroups resident:
+// every workgroup takes the same number of tiles (give or take one), so no
+// partial round of workgroups trails the launch (32 groups, Llama shape:
+// 1002 tiles on 501 workgroups, 186.5 us against 204.7 us with one
+// workgroup per tile).
+inline int balanced_grid(int ntiles, int slots)
+{
+    if (slots < 1)
+        slots = 1;
+    const int per = (ntiles + slots - 1) / slots;
+    return (ntiles + per - 1) / per;
+}
+
 // Column passes of up to 64 groups.  Passes over 33..64 groups run 256-row
 // tiles (8 waves; measured 444 vs 471 us at 64 groups on the Gemma shape),
 // passes over up to 32 groups 128-row tiles, two workgroups per compute unit
@@ -636,17 +663,21 @@ hipError_t union_passes(hipStream_t s, int V, int d, const uint16_t *Wb, int G, 
                         int64_t ldh_g, const int64_t *sl_off, const TileIx *tix, int nt,
                         float *logits, hipEvent_t t0, hipEvent_t t1)
 {
+    const int cus = device_cu_count();
     for (int g0 = 0; g0 < G; g0 += 64) {
         hipEvent_t start = g0 == 0 ? t0 : nullptr, stop = g0 + 64 >= G ? t1 : nullptr;
         hipError_t e;
-        if (G - g0 > 32)
-            e = launch_timed(head_union_kernel<2, 8>, dim3((V + tile_rows<8>() - 1) / tile_rows<8>()),
-                             dim3(512), s, start, stop, V, d, Wb, G, g0, hb, ldh_g, sl_off, tix,
-                             nt, logits);
-        else
-            e = launch_timed(head_union_kernel<1, 4>, dim3((V + tile_rows<4>() - 1) / tile_rows<4>()),
-                             dim3(256), s, start, stop, V, d, Wb, G, g0, hb, ldh_g, sl_off, tix,
-                             nt, logits);
+        if (G - g0 > 32) {
+            const int nti = (V + tile_rows<8>() - 1) / tile_rows<8>();
+            e = launch_timed(head_union_kernel<2, 8>, dim3(balanced_grid(nti, cus)), dim3(512), s,
+                             start, stop, V, d, Wb, G, g0, hb, ldh_g, sl_off, tix, nt, logits,
+                             nti);
+        } else {
+            const int nti = (V + tile_rows<4>() - 1) / tile_rows<4>();
+            e = launch_timed(head_union_kernel<1, 4>, dim3(balanced_grid(nti, 2 * cus)), dim3(256),
+                             s, start, stop, V, d, Wb, G, g0, hb, ldh_g, sl_off, tix, nt, logits,
+                             nti);
+        }
         if (e != hipSuccess)
             return e;
     }

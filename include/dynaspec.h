@@ -429,7 +429,11 @@ ds_status ds_router_train_step(hipStream_t s, const ds_router_train_args *a);
  * writes each shortlist's 32-token tile index (first position and
  * membership mask per tile, two slots of the workspace used alternately),
  * so the head walks W once on the matrix cores without an index pass of
- * its own; the logits are those of ds_gathered_lm_head.  Every pointer is a device pointer except
+ * its own; the logits are those of ds_gathered_lm_head.  That head keeps
+ * every compute unit busy, so kernels beside it wait for its workgroups to
+ * retire: in this mode the two router layers of position t+1 run on
+ * head_stream just before head t (h[:, t+1] exists then), and only the
+ * selection and build of position t+1 run on router_stream beside head t.  Every pointer is a device pointer except
  * max_rows, max_len, W_pos and head_events (host arrays).  On return all work is
  * enqueued and head_stream waits for everything enqueued on router_stream.
  * Optional fields:
