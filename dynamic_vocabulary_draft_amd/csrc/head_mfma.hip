@@ -16,7 +16,8 @@
 // union (batched drafting: many shortlists, one head row each): the union
 //   of B shortlists covers nearly all of V already at B = 32, so instead of
 //   streaming every group's rows (B times the bytes) the kernel walks W in
-//   128-token tiles in token-id order, reads each row once, multiplies it
+//   128- or 256-token tiles in token-id order (a persistent grid, the same
+//   number of tiles per workgroup), reads each row once, multiplies it
 //   with all G hidden vectors (columns of the MFMA), and writes only the
 //   (row, group) pairs on that group's shortlist.  A pre-pass over the
 //   shortlists records, per group and 32-token tile, where the tile's
