@@ -285,6 +285,29 @@ def test_head_union_dense_shortlists(N, oracle_lib, drop):
     _logit_bar(got, ref, True)
 
 
+@pytest.mark.parametrize("G", [9, 40])
+def test_head_union_persistent_grid(N, oracle_lib, G):
+    """Batched head over more tiles than resident workgroups: each workgroup
+    of the persistent grid strides over about two tiles (128-row tiles for
+    up to 32 groups, 256-row tiles above), with a ragged last tile; every
+    logit is checked."""
+    V, d = 70001, 264
+    g = np.random.default_rng(7000 + G)
+    cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=50, dtype=syn.DT_BF16)
+    cluster_of, _ = _clusters(V, 50, 3)
+    W = syn.make_lm_head(cfg, cluster_of)
+    h = _store(g.standard_normal((G, 1, d)).astype(np.float32), True)
+    lens = [int(x) for x in g.integers(V // 5, V // 2, size=G)]
+    sl_off, sl_ids = _random_shortlists(g, V, lens)
+    ref = oracle_lib.gathered_lm_head(W, h, sl_off, sl_ids)
+    logits = torch.full((int(sl_off[-1]),), float("nan"), device="cuda")
+    N.gathered_lm_head(to_dev(W), to_dev(h), to_dev(sl_off), to_dev(sl_ids), int(sl_off[-1]),
+                       logits)
+    got = _cpu(logits)
+    assert not np.isnan(got).any()
+    _logit_bar(got, ref, True)
+
+
 @pytest.mark.parametrize("G,m", [(3, 1), (16, 1), (3, 8)])
 def test_head_invalid_ids_are_nan(N, oracle_lib, G, m):
     """Ids outside [0, V) give NaN on every kernel path (GEMV, union, gathered);
