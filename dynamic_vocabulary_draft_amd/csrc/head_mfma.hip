@@ -471,6 +471,69 @@ __global__ __launch_bounds__(64 * WV) void head_union_kernel(int V, int d, const
 }
 
 // --------------------------------------------------------------- gathered
+// one 32*WV-entry tile of group g's shortlist against head rows n0..n0+mm-1
+template <int NB, int WV>
+__device__ __forceinline__ void gathered_tile(rsrc_t w, int V, int d, int m, int n0, int mm,
+                                              const uint16_t *__restrict__ h, int64_t ldh_g,
+                                              const int64_t *__restrict__ sl_off,
+                                              const int32_t *__restrict__ sl_ids,
+                                              float *__restrict__ logits, uint16_t *lds,
+                                              uint16_t *lds_a, int g, int64_t tile)
+{
+    constexpr int kTileRows = tile_rows<WV>();
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t off = sl_off[g], len = sl_off[g + 1] - off;
+    const uint16_t *hg = h + (int64_t)g * ldh_g + (int64_t)n0 * d;
+    auto hsrc = [&](int r) { return hg + (int64_t)r * d; };
+    const int64_t e = tile * kTileRows + 32 * wave + (lane & 31);
+    const bool evalid = e < len;
+    int32_t id = evalid ? sl_ids[off + e] : 0;
+    const bool valid = evalid && id >= 0 && id < V;  // else row 0, result not used
+    const int yrow = valid ? id : 0;
+    uint32_t voff[4];  // load i of lane l reads the row of the wave's entry l/8 + 8i
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        voff[i] = (uint32_t)__shfl(yrow, (lane >> 3) + 8 * i) * (uint32_t)d * 2u +
+                  16u * (lane & 7);
+    f32x16 acc[NB];
+    rows_times_b<NB, 64 * WV, kCached>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc, 0);
+    // epilogue: column = head row (node), row = shortlist entry; the entry
+    // of accumulator row i was loaded by lanes i and i + 32
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int nl = nb * 32 + (lane & 31);
+        float *out = logits + (int64_t)m * off + (int64_t)(n0 + nl) * len;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const int64_t ent = tile * kTileRows + 32 * wave + i;
+            const bool ok = __shfl(valid ? 1 : 0, i) != 0;
+            if (nl < mm && ent < len)
+                out[ent] = ok ? acc[nb][r] : __builtin_nanf("");
+        }
+    }
+}
+
+// The tiles of all groups form one list that the persistent grid strides
+// over.  Shortlists of one launch differ in length (a token budget
+// overshoots by up to one cluster: 24.6K to 51K entries on the Qwen-shaped
+// 8-tree workload), so a fixed number of workgroups per group would leave
+// the longest group's workgroups running alone.
+//   up to kTreeMixGroups groups: tile-index-major (tile t of every group
+//     that has one, in group order, then tile t+1): the groups walk their
+//     shortlists side by side, and while all G = 8 have tiles, group g stays
+//     on XCD g (its hidden rows in that L2).  Every workgroup rebuilds in
+//     LDS the tile counts and C(t) = the number of tiles before index t.
+//   up to kTreeLdsGroups groups: group-major (tile t of group g is entry
+//     tpre[g] + t, tpre = exclusive prefix of the tile counts, in LDS).
+//   above: each group keeps tiles_stride workgroups of its own.
+// Measured on the 8-tree workload (mean over four input instances): a fixed
+// share of workgroups per group 436 us, group-major 424 us, tile-index-major
+// 373 us.
+constexpr int kTreeMixGroups = 64;
+constexpr int kTreeMixTiles = 4096;  // tile indices covered by C in LDS
+constexpr int kTreeLdsGroups = 4096;
+
 template <int NB, int WV>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) void head_gathered_kernel(int V, int d, const uint16_t *__restrict__ W,
                                                             int G, int m, int n0,
@@ -482,45 +545,118 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
                                                             float *__restrict__ logits)
 {
     constexpr int kTileRows = tile_rows<WV>();
+    constexpr int NT = 64 * WV;
     __shared__ __attribute__((aligned(16))) uint16_t lds_all[lds_bytes<NB, WV>() / 2];
+    __shared__ int32_t s_tpre[kTreeLdsGroups + 1 > kTreeMixTiles + 1 + kTreeMixGroups
+                                  ? kTreeLdsGroups + 1
+                                  : kTreeMixTiles + 1 + kTreeMixGroups];
+    __shared__ int64_t s_scan[kWave + 1];
     uint16_t *lds = lds_all, *lds_a = lds_all + NB * 32 * lds_row<NB>();
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    const int g = blockIdx.x % G;  // neighbouring workgroups: same tile, other groups
-    const int64_t off = sl_off[g], len = sl_off[g + 1] - off;
     const int mm = min(m - n0, NB * 32);  // head rows n0 .. n0+mm-1 in this pass
-    const uint16_t *hg = h + (int64_t)g * ldh_g + (int64_t)n0 * d;
-    auto hsrc = [&](int r) { return hg + (int64_t)r * d; };
     const rsrc_t w = make_rsrc(W, (uint32_t)((int64_t)V * d * 2));  // V*d*2 < 4 GiB
-    for (int64_t tile = blockIdx.x / G; tile * kTileRows < len; tile += tiles_stride) {
-        const int64_t e = tile * kTileRows + 32 * wave + (lane & 31);
-        const bool evalid = e < len;
-        int32_t id = evalid ? sl_ids[off + e] : 0;
-        const bool valid = evalid && id >= 0 && id < V;  // else row 0, result not used
-        const int yrow = valid ? id : 0;
-        uint32_t voff[4];  // load i of lane l reads the row of the wave's entry l/8 + 8i
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            voff[i] = (uint32_t)__shfl(yrow, (lane >> 3) + 8 * i) * (uint32_t)d * 2u +
-                      16u * (lane & 7);
-        f32x16 acc[NB];
-        rows_times_b<NB, 64 * WV, kCached>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc,
-                                           0);
-        // epilogue: column = head row (node), row = shortlist entry; the
-        // entry of accumulator row i was loaded by lanes i and i + 32
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const int nl = nb * 32 + (lane & 31);
-            float *out = logits + (int64_t)m * off + (int64_t)(n0 + nl) * len;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int64_t ent = tile * kTileRows + 32 * wave + i;
-                const bool ok = __shfl(valid ? 1 : 0, i) != 0;
-                if (nl < mm && ent < len)
-                    out[ent] = ok ? acc[nb][r] : __builtin_nanf("");
-            }
+    if (G <= kTreeMixGroups) {  // block-uniform; s_tpre holds C(t), then the tile counts
+        int32_t *s_cnt = s_tpre + kTreeMixTiles + 1;
+        __shared__ int s_tmax;
+        if (threadIdx.x == 0)
+            s_tmax = 0;
+        __syncthreads();
+        for (int g = threadIdx.x; g < G; g += NT) {
+            const int64_t len = sl_off[g + 1] - sl_off[g];
+            const int64_t c = len > 0 ? (len + kTileRows - 1) / kTileRows : 0;
+            s_cnt[g] = (int32_t)min(c, (int64_t)kTreeMixTiles);
+            atomicMax(&s_tmax, s_cnt[g]);
         }
+        __syncthreads();
+        const int tmax = s_tmax;  // tiles of the longest group (capped: see below)
+        constexpr int PER = (kTreeMixTiles + NT) / NT;  // tile indices per thread
+        int64_t sum = 0;
+        int32_t act[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int t = threadIdx.x * PER + i;
+            int a = 0;
+            if (t < tmax)
+                for (int g = 0; g < G; ++g)
+                    a += s_cnt[g] > t;
+            act[i] = a;
+            sum += a;
+        }
+        int64_t total;
+        int64_t run = block_excl_scan_i64(sum, s_scan, &total);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int t = threadIdx.x * PER + i;
+            if (t <= tmax)
+                s_tpre[t] = (int32_t)run;
+            run += act[i];
+        }
+        __syncthreads();
+        for (int64_t gt = blockIdx.x; gt < total; gt += gridDim.x) {
+            int lo = 0, hi = tmax;  // tile index: last t with C(t) <= gt
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_tpre[mid] <= gt)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            int r = (int)(gt - s_tpre[lo]), g = 0;  // the r-th group with a tile lo
+            for (;; ++g)
+                if (s_cnt[g] > lo && r-- == 0)
+                    break;
+            gathered_tile<NB, WV>(w, V, d, m, n0, mm, h, ldh_g, sl_off, sl_ids, logits, lds, lds_a,
+                                  g, lo);
+        }
+        // groups longer than kTreeMixTiles tiles: the rest of their tiles,
+        // one group at a time (only for shortlists of over a million entries)
+        for (int g = 0; g < G; ++g) {
+            const int64_t len = sl_off[g + 1] - sl_off[g];
+            for (int64_t tile = kTreeMixTiles + blockIdx.x; tile * kTileRows < len;
+                 tile += gridDim.x)
+                gathered_tile<NB, WV>(w, V, d, m, n0, mm, h, ldh_g, sl_off, sl_ids, logits, lds,
+                                      lds_a, g, tile);
+        }
+        return;
     }
+    if (G <= kTreeLdsGroups) {  // block-uniform
+        constexpr int PER = (kTreeLdsGroups + NT) / NT;  // groups per thread (G + 1 slots)
+        int64_t cnt[PER], sum = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int g = threadIdx.x * PER + i;
+            const int64_t len = g < G ? sl_off[g + 1] - sl_off[g] : 0;
+            cnt[i] = len > 0 ? (len + kTileRows - 1) / kTileRows : 0;
+            sum += cnt[i];
+        }
+        int64_t total;
+        int64_t run = block_excl_scan_i64(sum, s_scan, &total);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int g = threadIdx.x * PER + i;
+            if (g <= G)
+                s_tpre[g] = (int32_t)run;
+            run += cnt[i];
+        }
+        __syncthreads();
+        for (int64_t gt = blockIdx.x; gt < total; gt += gridDim.x) {
+            int lo = 0, hi = G;  // group: last g with s_tpre[g] <= gt
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_tpre[mid] <= gt)
+                    lo = mid;
+                else
+                    hi = mid;
+            }
+            gathered_tile<NB, WV>(w, V, d, m, n0, mm, h, ldh_g, sl_off, sl_ids, logits, lds, lds_a,
+                                  lo, gt - s_tpre[lo]);
+        }
+        return;
+    }
+    const int g = blockIdx.x % G;  // neighbouring workgroups: same tile, other groups
+    const int64_t len = sl_off[g + 1] - sl_off[g];
+    for (int64_t tile = blockIdx.x / G; tile * kTileRows < len; tile += tiles_stride)
+        gathered_tile<NB, WV>(w, V, d, m, n0, mm, h, ldh_g, sl_off, sl_ids, logits, lds, lds_a, g,
+                              tile);
 }
 
 // ------------------------------------------------------- router, layer 1
@@ -685,30 +821,39 @@ hipError_t union_passes(hipStream_t s, int V, int d, const uint16_t *Wb, int G, 
     return hipSuccess;
 }
 
-// gathered: persistent-style grid (one 8-wave or two 4-wave workgroups per
-// compute unit), groups interleaved
+// gathered: persistent grid (one 8-wave or two 4-wave workgroups per compute
+// unit) over the tiles of all groups
 template <int WV>
 hipError_t gathered_passes(hipStream_t s, int V, int d, const uint16_t *Wb, int G, int m,
                            const uint16_t *hb, int64_t ldh_g, const int64_t *sl_off,
                            const int32_t *sl_ids, int64_t max_rows, float *logits, hipEvent_t t0,
                            hipEvent_t t1)
 {
+    const int64_t slots = (8 / WV) * (int64_t)device_cu_count();
     int64_t per_group = (max_rows + tile_rows<WV>() - 1) / tile_rows<WV>();
-    const int64_t want = ((8 / WV) * (int64_t)device_cu_count() + G - 1) / G;
-    if (per_group > want)
-        per_group = want;
-    if (per_group < 1)
-        per_group = 1;
-    const unsigned blocks = (unsigned)(per_group * G);
+    int64_t blocks;
+    if (G <= kTreeLdsGroups) {  // one list of all groups' tiles: at most this many
+        blocks = per_group + G;
+        if (blocks > slots)
+            blocks = slots;
+        per_group = 1;  // unused
+    } else {
+        const int64_t want = (slots + G - 1) / G;
+        if (per_group > want)
+            per_group = want;
+        if (per_group < 1)
+            per_group = 1;
+        blocks = per_group * G;
+    }
     const int ts = (int)per_group;
     for (int n0 = 0; n0 < m; n0 += 64) {  // passes of up to 64 head rows
         hipEvent_t start = n0 == 0 ? t0 : nullptr, stop = n0 + 64 >= m ? t1 : nullptr;
         hipError_t e;
         if (m - n0 > 32)
-            e = launch_timed(head_gathered_kernel<2, WV>, dim3(blocks), dim3(64 * WV), s, start,
+            e = launch_timed(head_gathered_kernel<2, WV>, dim3((unsigned)blocks), dim3(64 * WV), s, start,
                              stop, V, d, Wb, G, m, n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
         else
-            e = launch_timed(head_gathered_kernel<1, WV>, dim3(blocks), dim3(64 * WV), s, start,
+            e = launch_timed(head_gathered_kernel<1, WV>, dim3((unsigned)blocks), dim3(64 * WV), s, start,
                              stop, V, d, Wb, G, m, n0, hb, ldh_g, sl_off, sl_ids, ts, logits);
         if (e != hipSuccess)
             return e;

@@ -308,6 +308,30 @@ def test_head_union_persistent_grid(N, oracle_lib, G):
     _logit_bar(got, ref, True)
 
 
+@pytest.mark.parametrize("G", [4096, 4100])
+def test_head_tree_many_groups(N, oracle_lib, G):
+    """Tree head (8 head rows per group) with thousands of short shortlists,
+    some empty: up to 4096 groups the workgroups share one list of every
+    group's tiles (prefix built in LDS), above it each group keeps its own
+    workgroups."""
+    V, d, m = 5000, 264, 8
+    g = np.random.default_rng(4000 + G)
+    cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=50, dtype=syn.DT_BF16)
+    cluster_of, _ = _clusters(V, 50, 3)
+    W = syn.make_lm_head(cfg, cluster_of)
+    h = _store(g.standard_normal((G, m, d)).astype(np.float32), True)
+    lens = [int(x) for x in g.integers(0, 5, size=G)]
+    lens[-1] = 300  # one group spanning two 256-entry tiles
+    sl_off, sl_ids = _random_shortlists(g, V, lens)
+    ref = oracle_lib.gathered_lm_head(W, h, sl_off, sl_ids)
+    logits = torch.full((m * int(sl_off[-1]),), float("nan"), device="cuda")
+    N.gathered_lm_head(to_dev(W), to_dev(h), to_dev(sl_off), to_dev(sl_ids), int(sl_off[-1]),
+                       logits)
+    got = _cpu(logits)
+    assert not np.isnan(got).any()
+    _logit_bar(got, ref, True)
+
+
 @pytest.mark.parametrize("G,m", [(3, 1), (16, 1), (3, 8)])
 def test_head_invalid_ids_are_nan(N, oracle_lib, G, m):
     """Ids outside [0, V) give NaN on every kernel path (GEMV, union, gathered);
