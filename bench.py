@@ -650,7 +650,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
         mfma = cfg.dtype == syn.DT_BF16 and ((hrows == 1 and cfg.B >= 8) or hrows >= 8)
         kname = ("head_gemv_kernel" if not mfma else
-                 "union_index_kernel + head_union_kernel" if hrows == 1 else
+                 "head_union_kernel (tile index written by the build)" if hrows == 1 else
                  "head_gathered_kernel")
         head = {"kernel": kname, "launches_timed": len(durs),
                 "mean_us": round(mean_ms * 1e3, 2),
