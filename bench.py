@@ -232,7 +232,7 @@ def traffic_from(args):
         "copy_write_kib": per["WRITE_SIZE"]["copy_kib"],
     })
     out["traffic_over_algorithmic"] = round(out["bytes_per_launch"] / alg, 4)
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(args.traffic_out or TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
@@ -478,6 +478,9 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc outputs of --pmc-probe into "
                          "profiles/head_gemv_traffic.json and exit")
+    ap.add_argument("--traffic-out", default=None,
+                    help="where --traffic-from writes (default: the file the default bench "
+                         "line reads its traffic from; give another path for other workloads)")
     ap.add_argument("--probe-file", default=os.path.join(ROOT, "pmc_probe.json"),
                     help="where --pmc-probe writes (and --traffic-from reads) the launch list")
     ap.add_argument("--static", choices=["gathered", "packed"],
