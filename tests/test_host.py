@@ -60,6 +60,11 @@ def test_workspace_queries(N):
     assert N.softmax_workspace_bytes(7, 128256) == 7 * 32 * 12 + 256  # 4096-entry segments
     assert N.verify_workspace_bytes(2, 6, 128256) >= 2 * 126 * 24 + 2 * 4
     assert N.draft_chain_workspace_bytes(1, 6, 128256, 1024, 55734) >= 4096 + 256
+    # batched chains: two 32-token tile-index slots (8 bytes per tile and row)
+    tiles = (128256 + 31) // 32 + 1
+    assert (N.draft_chain_workspace_bytes(32, 6, 128256, 1024, 55734)
+            >= N.router_workspace_bytes(32, 1024) + 2 * 32 * tiles * 8)
+    assert N.head_workspace_bytes(8, 64, 151936) == 0  # tree head: no workspace
     assert N.sample_workspace_bytes(0, 1, 10) == 0
 
 
@@ -80,6 +85,10 @@ def test_router_rejects_bad_arguments(N):
     assert L.ds_router_score(*args(ldh=32)) == 3
     assert L.ds_router_score(*args(h=C.c_void_p(4100))) == 1  # misaligned
     assert L.ds_router_score(*args()) == 1  # no workspace
+    # 8 or more inputs also need the first layer's partial sums: a workspace
+    # that holds only z is rejected before anything is enqueued
+    assert L.ds_router_score(*args(n=8, ws=FAKE, ws_bytes=8 * 64 * 4)) == 1
+    assert L.ds_router_score(*args(n=8, d=8200, ldh=8200, ws=FAKE, ws_bytes=1 << 30)) == 3
 
 
 def test_select_build_head_sample_verify_reject_bad_arguments(N):
