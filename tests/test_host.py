@@ -204,3 +204,41 @@ def test_capacity_bounds_cover_every_selection(oracle_lib, index):
         s = g.standard_normal((50, cfg.M)).astype(np.float32)
         _, _, L = oracle_lib.select_clusters(s, size, cfg.budget_kind, np.full(50, b, np.int32))
         assert L.max() * cfg.B <= bounds[t]
+
+
+def test_traffic_from_scales_counters(tmp_path):
+    """bench.py --traffic-from: per-dispatch FETCH_SIZE / WRITE_SIZE of the
+    head kernel, scaled by what the same counter reads for the probe's plain
+    copy of known size, averaged per launch and set against the algorithmic
+    bytes the probe recorded."""
+    import json
+    import subprocess
+    import sys
+    copy = 1 << 30
+
+    def csv(d, counter, head_kib, copy_kib):
+        d.mkdir()
+        rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        for i, v in enumerate(head_kib):
+            rows.append('%d,"void ds::head_gemv_kernel<true, 8, 2>(int)",%s,%r' % (i + 1, counter, v))
+        rows.append('%d,"__amd_rocclr_copyBuffer",%s,%r' % (len(head_kib) + 1, counter, copy_kib))
+        (d / "p_counter_collection.csv").write_text("\n".join(rows) + "\n")
+
+    csv(tmp_path / "fetch", "FETCH_SIZE", [1000.0, 1200.0], copy / 2 / 1024)  # reads half
+    csv(tmp_path / "write", "WRITE_SIZE", [10.0, 20.0], copy / 1024)
+    probe = tmp_path / "probe.json"
+    probe.write_text(json.dumps({"workload": "w", "head_kernel": "head_gemv_kernel",
+                                 "launch_bytes": [2.0e6, 2.4e6], "copy_bytes": copy,
+                                 "kernel_source_sha256": "x"}))
+    out = tmp_path / "traffic.json"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--traffic-from",
+                        str(tmp_path / "fetch"), str(tmp_path / "write"), "--probe-file",
+                        str(probe), "--traffic-out", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    t = json.loads(out.read_text())
+    assert t["fetch_bytes_per_launch"] == 1100 * 1024 * 2
+    assert t["write_bytes_per_launch"] == 15 * 1024
+    assert t["bytes_per_launch"] == 1100 * 1024 * 2 + 15 * 1024
+    assert t["algorithmic_bytes_per_launch"] == 2200000
+    assert t["traffic_over_algorithmic"] == round((1100 * 1024 * 2 + 15 * 1024) / 2.2e6, 4)
+    assert t["launches"] == 2 and t["workload"] == "w"
