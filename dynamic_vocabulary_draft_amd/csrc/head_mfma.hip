@@ -11,7 +11,7 @@
 // MFMA steps; the same permutation of the reduction index is applied to the
 // B operand, so the products are exact and only the summation order differs
 // from a plain dot product.  The B operand (hidden vectors) is staged in LDS
-// per phase of several slices and shared by the workgroup's four waves.
+// per phase of several slices and shared by the workgroup's waves (4 or 8).
 //
 // union (batched drafting: many shortlists, one head row each): the union
 //   of B shortlists covers nearly all of V already at B = 32, so instead of
@@ -19,15 +19,16 @@
 //   128- or 256-token tiles in token-id order (a persistent grid, the same
 //   number of tiles per workgroup), reads each row once, multiplies it
 //   with all G hidden vectors (columns of the MFMA), and writes only the
-//   (row, group) pairs on that group's shortlist.  A pre-pass over the
-//   shortlists records, per group and 32-token tile, where the tile's
-//   entries start in the group's shortlist (shortlists are ascending) and
-//   which of the tile's 32 tokens they are.
+//   (row, group) pairs on that group's shortlist.  It reads, per group and
+//   32-token tile, where the tile's entries start in the group's shortlist
+//   (shortlists are ascending) and which of the tile's 32 tokens they are:
+//   inside the draft chain the build writes this index, a standalone call
+//   builds it in a pre-pass over the shortlists.
 // gathered (tree drafting: m head rows share one shortlist): a gathered
 //   GEMM per group, rows = shortlist entries (gathered W rows), columns =
-//   the m head rows; workgroups of different groups with the same tile
-//   index are launched next to each other, so rows shared by several
-//   shortlists are read while still in the memory-side cache.
+//   the m head rows; a persistent grid strides over one list of every
+//   group's tiles, ordered by tile index, so groups of unequal length share
+//   the compute units and walk their shortlists side by side.
 #include "common.h"
 #include "kernels.h"
 
