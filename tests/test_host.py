@@ -242,3 +242,14 @@ def test_traffic_from_scales_counters(tmp_path):
     assert t["algorithmic_bytes_per_launch"] == 2200000
     assert t["traffic_over_algorithmic"] == round((1100 * 1024 * 2 + 15 * 1024) / 2.2e6, 4)
     assert t["launches"] == 2 and t["workload"] == "w"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more it says so and exits
+    non-zero before touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
