@@ -36,6 +36,9 @@ def small_configs():
         # ragged last 32-token tile and a partial last build chunk
         "small-bf16-b12": syn.shrink(c1, V=9001, d=264, M=60, r=64, B=12, T=3,
                                      budget=syn.linear_budget(3000, 1500, 3)),
+        # nine fp32 sequences: GEMV router with 8+ inputs, multi-row build,
+        # GEMV head over many groups, two-pass sampler and verification
+        "tiny-fp32-b9": syn.shrink(syn.CONFIGS[0], B=9),
     }
 
 
@@ -176,7 +179,8 @@ def test_step_full_size(oracle_lib, index):
     check_stagewise(wl, r, head_samples=256 if index != 2 else 64, seed=index)
 
 
-@pytest.mark.parametrize("name", ["tiny-fp32", "small-bf16-b3", "small-tree", "small-bf16-b12"])
+@pytest.mark.parametrize("name", ["tiny-fp32", "small-bf16-b3", "small-tree", "small-bf16-b12",
+                                  "tiny-fp32-b9"])
 def test_graph_replay_matches_eager(oracle_lib, name):
     """A captured step replayed three times, with eager work and
     synchronisation between replays, reproduces the eager step bit for bit."""
