@@ -55,7 +55,7 @@ def _ulp(got, ref):
     assert (np.abs(got.astype(np.float64) - ref.astype(np.float64)) <= sp).all()
 
 
-def check_stagewise(wl, r, head_samples=None, seed=0):
+def check_stagewise(wl, r, head_samples=None, seed=0, tau=1.0):
     """Stage-by-stage parity on the GPU's own intermediate outputs."""
     cfg = wl.cfg
     bf16 = cfg.dtype == syn.DT_BF16
@@ -101,7 +101,8 @@ def check_stagewise(wl, r, head_samples=None, seed=0):
                 _bar(got.reshape(-1), ref, bf16)
         # sampling on the GPU's logits
         u = wl.u_draft.reshape(-1) if cfg.is_tree else wl.u_draft[t]
-        tok, q, tie = oracle.shortlist_sample(loc_off, loc_ids, r["logits"][m * lo:m * hi], u, m)
+        tok, q, tie = oracle.shortlist_sample(loc_off, loc_ids, r["logits"][m * lo:m * hi], u, m,
+                                              tau)
         got_tok = r["token"].reshape(-1) if cfg.is_tree else r["token"][t]
         assert np.array_equal(got_tok[~tie], tok[~tie])
         _ulp(r["q"][m * lo:m * hi], q)
@@ -121,10 +122,10 @@ def check_stagewise(wl, r, head_samples=None, seed=0):
         assert np.array_equal(r["out"][~tie], out[~tie])
 
 
-def check_from_scratch(wl, r):
+def check_from_scratch(wl, r, tau=1.0):
     """The oracle's own step vs the GPU's, outside tie zones."""
     cfg = wl.cfg
-    ref = opipe.run_step(wl)
+    ref = opipe.run_step(wl, temperature=tau)
     B = cfg.B
     npos = 1 if cfg.is_tree else cfg.T
     router_err = max(float(np.abs(r["scores"][t] - ref["scores"][t]).max()) for t in range(npos))
@@ -166,6 +167,20 @@ def test_step_small(oracle_lib, name):
         r = step.host()
         check_stagewise(wl, r)
         check_from_scratch(wl, r)
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.7])
+@pytest.mark.parametrize("name", ["small-bf16-b1-d3840", "small-bf16-b12"])
+def test_step_temperature(oracle_lib, name, tau):
+    """The draft chain at another temperature and at 0 (the argmax, one-hot
+    q), stage by stage and against the oracle's own step."""
+    cfg = small_configs()[name]
+    wl = syn.make_workload(cfg.index, cfg=cfg)
+    step = DraftStep(wl, temperature=float(np.float32(tau)))
+    step.step()
+    r = step.host()
+    check_stagewise(wl, r, tau=float(np.float32(tau)))
+    check_from_scratch(wl, r, tau=float(np.float32(tau)))
 
 
 @pytest.mark.parametrize("index", [1, 2, 3, 4])
