@@ -170,7 +170,7 @@ def test_step_small(oracle_lib, name):
 
 
 @pytest.mark.parametrize("tau", [0.0, 0.7])
-@pytest.mark.parametrize("name", ["small-bf16-b1-d3840", "small-bf16-b12"])
+@pytest.mark.parametrize("name", ["small-bf16-b1-d3840", "small-bf16-b12", "small-tree"])
 def test_step_temperature(oracle_lib, name, tau):
     """The draft chain at another temperature and at 0 (the argmax, one-hot
     q), stage by stage and against the oracle's own step."""
