@@ -4,17 +4,22 @@
 // top-L of the full drafter; the trainable part is the 2-layer MLP).
 //
 // Labels: one workgroup per training row selects the row's top-L tokens of
-// the full drafter's logits (logit descending, token id ascending) with a
-// four-pass radix select on order-preserving 32-bit keys (per-wave LDS
-// histograms of one byte per pass), then marks the clusters of the selected
-// tokens.  Ties at the L-th key are resolved by id with a block scan, which
-// only runs when the tie is split.
+// the full drafter's logits (logit descending, token id ascending) on
+// order-preserving 32-bit keys, then marks the clusters of the selected
+// tokens.  Two reads of the row: the first bounds the L-th largest key from
+// below by the L-th largest of the threads' maxima, the second gathers the
+// few keys at or above that bound into LDS, where each is ranked exactly.
+// Where the bound admits more than the LDS holds (heavy ties) or L exceeds
+// the thread count, a four-pass radix select (per-wave LDS histograms of one
+// byte per pass) finds the L-th key instead; ties at it are resolved by id
+// with a block scan, which only runs when the tie is split.
 //
 // Training step (fp32 parameters, fp32 arithmetic): a 64 x 64-tile GEMM
 // kernel (256 threads, 4 x 4 outputs per thread, 16-deep k slices staged in
-// LDS, every output summed in ascending k order; the first layer, whose
-// output is small and whose k = d is long, splits k in eight and adds the
-// splits in order) with a fused epilogue per product:
+// LDS, every output summed in ascending k order; the two forward products
+// and the gradient through act', whose outputs are small (n rows) and whose
+// k is long, split k in eight and add the splits in order) with a fused
+// epilogue per product:
 //   a = h W1^T + b1, z = act(a)        (epilogue keeps a and z)
 //   s = z W2^T + b2                    (then g_s = (sigmoid(s) - y)/(n M) and
 //                                       the loss, summed in fp64 in a fixed order)
@@ -35,6 +40,8 @@ namespace {
 // ------------------------------------------------------------------ labels
 constexpr int kLabThreads = 1024;
 constexpr int kLabWaves = kLabThreads / kWave;
+constexpr int kLabCap = 2048;  // candidates ranked in LDS (>= kLabThreads)
+constexpr int kLabU = 16;      // loads in flight per thread
 
 // larger float -> larger key; -0 and +0 are one value, as in a float compare
 __device__ __forceinline__ uint32_t order_key(float x)
@@ -54,13 +61,88 @@ __global__ __launch_bounds__(kLabThreads) void topl_labels_kernel(int V, int M, 
     __shared__ uint8_t s_lab[DS_MAX_CLUSTERS];
     __shared__ uint32_t s_sel[4];  // prefix, need (rank within the equal keys), equal count
     __shared__ int s_wsum[kLabWaves];
+    __shared__ uint64_t s_cand[kLabCap];
+    __shared__ uint32_t s_cnt, s_t0;
     const int row = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const float *lg = logits + (int64_t)row * ldl;
     for (int c = tid; c < M; c += kLabThreads)
         s_lab[c] = 0;
     const int Lc = min(L, V);
-    if (Lc > 0) {
-        // radix select of the Lc-th largest key, one byte per pass
+    bool fast = false;
+    if (Lc > 0 && Lc <= kLabThreads) {
+        // Pass 1: each thread's largest key over its elements.  The Lc-th
+        // largest of these maxima, T0, belongs to Lc distinct elements, so the
+        // Lc-th largest key of the row is >= T0 and every element that can be
+        // selected (ties at the cut included) has a key >= T0.
+        uint32_t mx = 0;
+        for (int y0 = tid; y0 - lane < V; y0 += kLabThreads * kLabU) {
+            uint32_t k[kLabU];
+#pragma unroll
+            for (int u = 0; u < kLabU; ++u)
+                k[u] = order_key(lg[min(y0 + u * kLabThreads, V - 1)]);
+#pragma unroll
+            for (int u = 0; u < kLabU; ++u)
+                if (y0 + u * kLabThreads < V)
+                    mx = max(mx, k[u]);
+        }
+        s_cand[tid] = ((uint64_t)mx << 32) | (uint32_t)~(uint32_t)tid;  // distinct: ties by thread
+        if (tid == 0)
+            s_cnt = 0u;
+        __syncthreads();
+        {
+            const uint64_t mine = s_cand[tid];
+            int rank = 0;
+            for (int j = 0; j < kLabThreads; ++j)
+                rank += s_cand[j] > mine ? 1 : 0;
+            if (rank == Lc - 1)
+                s_t0 = mx;
+        }
+        __syncthreads();
+        const uint32_t T0 = s_t0;
+        // Pass 2: the candidates (key >= T0) into LDS as (key, ~id): a larger
+        // value ranks first, which is logit descending, then id ascending.
+        for (int y0 = tid; y0 - lane < V; y0 += kLabThreads * kLabU) {
+            uint32_t k[kLabU];
+#pragma unroll
+            for (int u = 0; u < kLabU; ++u)
+                k[u] = order_key(lg[min(y0 + u * kLabThreads, V - 1)]);
+#pragma unroll
+            for (int u = 0; u < kLabU; ++u) {
+                const int y = y0 + u * kLabThreads;
+                const bool c = y < V && k[u] >= T0;
+                const uint64_t bal = __ballot(c);
+                if (bal != 0ull) {  // uniform over the wave
+                    uint32_t base = 0u;
+                    if (lane == 0)
+                        base = atomicAdd(&s_cnt, (uint32_t)__popcll(bal));
+                    base = (uint32_t)__shfl((int)base, 0);
+                    const uint32_t pos = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+                    if (c && pos < (uint32_t)kLabCap)
+                        s_cand[pos] = ((uint64_t)k[u] << 32) | (uint32_t)~(uint32_t)y;
+                }
+            }
+        }
+        __syncthreads();
+        const uint32_t C = s_cnt;
+        if (C <= (uint32_t)kLabCap) {
+            // a candidate is selected iff fewer than Lc candidates rank above it
+            fast = true;
+            for (uint32_t i = tid; i < C; i += kLabThreads) {
+                const uint64_t v = s_cand[i];
+                int rank = 0;
+                for (uint32_t j = 0; j < C; ++j)
+                    rank += s_cand[j] > v ? 1 : 0;
+                if (rank < Lc) {
+                    const int32_t c = cluster_of[(int)~(uint32_t)v];
+                    if (c >= 0 && c < M)
+                        s_lab[c] = 1;
+                }
+            }
+        }
+    }
+    if (Lc > 0 && !fast) {
+        // more than kLabCap candidates (heavy ties) or Lc above the thread
+        // count: radix select of the Lc-th largest key, one byte per pass
         uint32_t prefix = 0, mask = 0, need = (uint32_t)Lc;
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
@@ -365,7 +447,10 @@ __global__ __launch_bounds__(64 * kColQ) void colsum_step_kernel(int rows, int c
 
 constexpr int kBceBlocks = 256;
 
-constexpr int kSplitK = 8;  // first-layer forward: K = d is long, the output small
+// the three forward/backward products with a long K and a small output
+// (first layer: K = d; second layer and the gradient through act': K = r or
+// M) split K eight ways
+constexpr int kSplitK = 8;
 
 struct TrainWs {
     float *a, *z, *s, *ga, *kpart;
@@ -421,7 +506,7 @@ hipError_t topl_labels_launch(hipStream_t s, int n, int V, int M, int L, const f
 size_t router_train_ws_bytes(int n, int r, int M)
 {
     return 3 * al256((size_t)n * r * 4) + al256((size_t)n * M * 4) +
-           al256((size_t)kBceBlocks * 8) + al256((size_t)kSplitK * n * r * 4) + 256;
+           al256((size_t)kBceBlocks * 8) + al256((size_t)kSplitK * n * (r > M ? r : M) * 4) + 256;
 }
 
 hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int act, bool h_bf16,
@@ -442,7 +527,7 @@ hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int ac
         return e;
     // s = z W2^T + b2
     if ((e = gemm(s, n, M, r, (const float *)w.z, (int64_t)r, (int64_t)1, W2, (int64_t)1,
-                  (int64_t)r, EpiFwd2{b2, w.s, M})) != hipSuccess)
+                  (int64_t)r, EpiFwd2{b2, w.s, M}, kSplitK, w.kpart)) != hipSuccess)
         return e;
     const int64_t total = (int64_t)n * M;
     const double inv = 1.0 / ((double)n * (double)M);
@@ -456,7 +541,7 @@ hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int ac
         return e;
     // g_a = (g_s W2) * act'(a), with W2 before its step
     if ((e = gemm(s, n, r, M, (const float *)w.s, (int64_t)M, (int64_t)1, W2, (int64_t)r,
-                  (int64_t)1, EpiGa{w.a, w.ga, r, act})) != hipSuccess)
+                  (int64_t)1, EpiGa{w.a, w.ga, r, act}, kSplitK, w.kpart)) != hipSuccess)
         return e;
     // dW2[c][j] = sum_i g_s[i][c] z[i][j]
     if ((e = gemm(s, M, r, n, (const float *)w.s, (int64_t)1, (int64_t)M, w.z, (int64_t)r,

@@ -390,8 +390,10 @@ ds_status ds_router_labels(hipStream_t s, int n, int V, int M, int L, const floa
  * Fields: h [n][d] (row stride ldh) in h_dtype (fp32 or bf16 bits); labels
  * [n][M] uint8 (0 or 1); W1 [r][d], b1 [r], W2 [M][r], b2 [M] fp32, updated
  * in place; dW1, db1, dW2, db2 fp32 gradient outputs of the same shapes;
- * loss one double; every pointer device memory.  Arithmetic fp32 (products
- * summed in ascending index order), the loss summed in fp64; results are
+ * loss one double; every pointer device memory.  Arithmetic fp32 (each dot
+ * product summed in ascending index order, the three forward/backward
+ * products over r, M or d in up to eight ascending k chunks whose sums are
+ * then added in chunk order), the loss summed in fp64; results are
  * reproducible bit for bit.  ws >= ds_router_train_workspace_bytes(n, r, M).
  */
 typedef struct {

@@ -38,8 +38,14 @@ def _labels_gpu(N, logits, cluster_of, M, L):
 
 
 @pytest.mark.parametrize("n,V,M,L", [(5, 5000, 100, 64), (3, 1000, 17, 1), (4, 777, 33, 780),
-                                     (2, 300, 7, 0), (6, 70000, 1024, 200)])
+                                     (2, 300, 7, 0), (6, 70000, 1024, 200),
+                                     (4, 3000, 50, 1024), (3, 5000, 64, 1500),
+                                     (4, 128256, 1024, 64)])
 def test_router_labels_bit_exact(N, oracle_lib, n, V, M, L):
+    """Row 0 ties at the cut (a few thousand candidates at or above the
+    bound: the LDS ranking below 2048 of them, the radix select above); row
+    2 is all zeros of both signs (every key equal); L = 1024 is the largest
+    L ranked in LDS, L = 1500 takes the radix select."""
     g = np.random.default_rng(V + L)
     lg = (g.standard_normal((n, V)) * 2).astype(np.float32)
     lg[0] = g.integers(0, 3, size=V).astype(np.float32)  # ties split at the L-th key
