@@ -16,10 +16,10 @@
 //
 // Training step (fp32 parameters, fp32 arithmetic): a 64 x 64-tile GEMM
 // kernel (256 threads, 4 x 4 outputs per thread, 16-deep k slices staged in
-// LDS, every output summed in ascending k order; the two forward products
-// and the gradient through act', whose outputs are small (n rows) and whose
-// k is long, split k in eight and add the splits in order) with a fused
-// epilogue per product:
+// LDS, every output summed in ascending k order; the products with a long k
+// and a small output -- the two forward ones, the gradient through act' and
+// dW2 -- split k in up to sixteen chunks and add the chunks in order) with a
+// fused epilogue per product:
 //   a = h W1^T + b1, z = act(a)        (epilogue keeps a and z)
 //   s = z W2^T + b2                    (then g_s = (sigmoid(s) - y)/(n M) and
 //                                       the loss, summed in fp64 in a fixed order)
@@ -377,7 +377,8 @@ struct EpiStep {  // grad = acc, param -= lr * grad
 };
 
 // g_s = (sigmoid(s) - y) / (n M) in place; per-block fp64 loss partials of
-// softplus(s) - y s (fixed association: thread, then wave, then block order)
+// softplus(s) - y s (a fixed association: each thread's terms in order, then
+// a wave sum, then the block's waves in order)
 constexpr int kBceThreads = 256;
 __global__ __launch_bounds__(kBceThreads) void bce_kernel(int64_t total, float inv,
                                                            const uint8_t *__restrict__ y,
@@ -406,14 +407,22 @@ __global__ __launch_bounds__(kBceThreads) void bce_kernel(int64_t total, float i
     }
 }
 
-__global__ void loss_final_kernel(int nparts, double inv, const double *__restrict__ part,
-                                  double *__restrict__ loss)
+// the kBceBlocks partials: one per thread, a wave sum each, the wave sums
+// added in wave order
+__global__ __launch_bounds__(kBceThreads) void loss_final_kernel(double inv,
+                                                                 const double *__restrict__ part,
+                                                                 double *__restrict__ loss)
 {
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
-        double t = 0.0;
-        for (int i = 0; i < nparts; ++i)
-            t += part[i];
-        *loss = t * inv;
+    __shared__ double sw[kBceThreads / kWave];
+    const double t = wave_sum_f64(part[threadIdx.x]);
+    if (lane_id() == 0)
+        sw[threadIdx.x >> 6] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double u = 0.0;
+        for (int w = 0; w < kBceThreads / kWave; ++w)
+            u += sw[w];
+        *loss = u * inv;
     }
 }
 
@@ -447,10 +456,11 @@ __global__ __launch_bounds__(64 * kColQ) void colsum_step_kernel(int rows, int c
 
 constexpr int kBceBlocks = 256;
 
-// the three forward/backward products with a long K and a small output
-// (first layer: K = d; second layer and the gradient through act': K = r or
-// M) split K eight ways
+// split-K ways of the products with a long K and a small output (second
+// layer and the gradient through act': K = r or M)
 constexpr int kSplitK = 8;
+constexpr int kSplitL1 = 16;  // first layer: K = d
+constexpr int kSplitW2 = 4;   // dW2: K = n, a 1024 x 1024 output at the Llama shape
 
 struct TrainWs {
     float *a, *z, *s, *ga, *kpart;
@@ -458,6 +468,14 @@ struct TrainWs {
 };
 
 inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// floats of split-K partials: the largest of the split products
+inline size_t kpart_floats(int n, int r, int M)
+{
+    const size_t a = (size_t)kSplitL1 * n * r, b = (size_t)kSplitK * n * (r > M ? r : M),
+                 c = (size_t)kSplitW2 * M * r;
+    return a > b ? (a > c ? a : c) : (b > c ? b : c);
+}
 
 TrainWs train_ws(void *ws, int n, int r, int M)
 {
@@ -506,7 +524,7 @@ hipError_t topl_labels_launch(hipStream_t s, int n, int V, int M, int L, const f
 size_t router_train_ws_bytes(int n, int r, int M)
 {
     return 3 * al256((size_t)n * r * 4) + al256((size_t)n * M * 4) +
-           al256((size_t)kBceBlocks * 8) + al256((size_t)kSplitK * n * (r > M ? r : M) * 4) + 256;
+           al256((size_t)kBceBlocks * 8) + al256(kpart_floats(n, r, M) * 4) + 256;
 }
 
 hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int act, bool h_bf16,
@@ -519,10 +537,10 @@ hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int ac
     // a = h W1^T + b1, z = act(a): A = h [n][d], B(k, j) = W1[j][k]
     if (h_bf16)
         e = gemm(s, n, r, d, reinterpret_cast<const uint16_t *>(h), ldh, (int64_t)1, W1,
-                 (int64_t)1, (int64_t)d, EpiFwd1{b1, w.a, w.z, r, act}, kSplitK, w.kpart);
+                 (int64_t)1, (int64_t)d, EpiFwd1{b1, w.a, w.z, r, act}, kSplitL1, w.kpart);
     else
         e = gemm(s, n, r, d, reinterpret_cast<const float *>(h), ldh, (int64_t)1, W1,
-                 (int64_t)1, (int64_t)d, EpiFwd1{b1, w.a, w.z, r, act}, kSplitK, w.kpart);
+                 (int64_t)1, (int64_t)d, EpiFwd1{b1, w.a, w.z, r, act}, kSplitL1, w.kpart);
     if (e != hipSuccess)
         return e;
     // s = z W2^T + b2
@@ -535,7 +553,8 @@ hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int ac
                        labels, w.s, w.part);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(64), 0, s, kBceBlocks, inv,
+    static_assert(kBceBlocks == kBceThreads, "one loss partial per thread");
+    hipLaunchKernelGGL(loss_final_kernel, dim3(1), dim3(kBceThreads), 0, s, inv,
                        (const double *)w.part, loss);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
@@ -545,7 +564,7 @@ hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int ac
         return e;
     // dW2[c][j] = sum_i g_s[i][c] z[i][j]
     if ((e = gemm(s, M, r, n, (const float *)w.s, (int64_t)1, (int64_t)M, w.z, (int64_t)r,
-                  (int64_t)1, EpiStep{dW2, W2, lr, r})) != hipSuccess)
+                  (int64_t)1, EpiStep{dW2, W2, lr, r}, kSplitW2, w.kpart)) != hipSuccess)
         return e;
     // dW1[j][k] = sum_i g_a[i][j] h[i][k]
     if (h_bf16)

@@ -391,9 +391,9 @@ ds_status ds_router_labels(hipStream_t s, int n, int V, int M, int L, const floa
  * [n][M] uint8 (0 or 1); W1 [r][d], b1 [r], W2 [M][r], b2 [M] fp32, updated
  * in place; dW1, db1, dW2, db2 fp32 gradient outputs of the same shapes;
  * loss one double; every pointer device memory.  Arithmetic fp32 (each dot
- * product summed in ascending index order, the three forward/backward
- * products over r, M or d in up to eight ascending k chunks whose sums are
- * then added in chunk order), the loss summed in fp64; results are
+ * product summed in ascending index order; the two forward products, the
+ * gradient through act' and dW2 in up to sixteen ascending k chunks whose
+ * sums are then added in chunk order), the loss summed in fp64; results are
  * reproducible bit for bit.  ws >= ds_router_train_workspace_bytes(n, r, M).
  */
 typedef struct {
