@@ -332,6 +332,28 @@ def test_head_tree_many_groups(N, oracle_lib, G):
     _logit_bar(got, ref, True)
 
 
+@pytest.mark.parametrize("G,m,lo,hi", [(8, 64, 10000, 30000), (20, 8, 55000, 60000)])
+def test_head_tree_tile_orders(N, oracle_lib, G, m, lo, hi):
+    """Tree head over long ragged shortlists on the persistent tile list:
+    eight groups of 40 to 120 tiles with 64 head rows each, and twenty
+    groups of 8 head rows with over 4096 tiles in all (more tiles than
+    workgroups many times over)."""
+    V, d = 60000, 264
+    g = np.random.default_rng(G * 1000 + m)
+    cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=50, dtype=syn.DT_BF16)
+    cluster_of, _ = _clusters(V, 50, 3)
+    W = syn.make_lm_head(cfg, cluster_of)
+    h = _store(g.standard_normal((G, m, d)).astype(np.float32), True)
+    lens = [int(x) for x in g.integers(lo, hi, size=G)]
+    sl_off, sl_ids = _random_shortlists(g, V, lens)
+    ref = oracle_lib.gathered_lm_head(W, h, sl_off, sl_ids)
+    logits = torch.full((m * int(sl_off[-1]),), float("nan"), device="cuda")
+    N.gathered_lm_head(to_dev(W), to_dev(h), to_dev(sl_off), to_dev(sl_ids), max(lens), logits)
+    got = _cpu(logits)
+    assert not np.isnan(got).any()
+    _logit_bar(got, ref, True)
+
+
 @pytest.mark.parametrize("G,m", [(3, 1), (16, 1), (3, 8)])
 def test_head_invalid_ids_are_nan(N, oracle_lib, G, m):
     """Ids outside [0, V) give NaN on every kernel path (GEMV, union, gathered);
