@@ -41,7 +41,7 @@ namespace {
 constexpr int kLabThreads = 1024;
 constexpr int kLabWaves = kLabThreads / kWave;
 constexpr int kLabCap = 2048;  // candidates ranked in LDS (>= kLabThreads)
-constexpr int kLabU = 16;      // loads in flight per thread
+constexpr int kLabU = 16;      // elements loaded per thread and round (all in flight)
 
 // larger float -> larger key; -0 and +0 are one value, as in a float compare
 __device__ __forceinline__ uint32_t order_key(float x)
@@ -50,6 +50,51 @@ __device__ __forceinline__ uint32_t order_key(float x)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Calls f(y, key(y), valid) for the row's elements y, kLabU per thread and
+// round, with every lane of a wave calling in step (f may use wave votes).
+// VEC (row start 16-byte aligned): 16-byte loads of four elements, then the
+// last V % 4 elements one per thread.
+template <bool VEC, class F>
+__device__ __forceinline__ void for_row_keys(const float *__restrict__ lg, int V, int tid,
+                                             int lane, F f)
+{
+    if constexpr (VEC) {
+        constexpr int U4 = kLabU / 4;
+        const int nv = V >> 2;  // whole 4-element pieces
+        const float4 *l4 = reinterpret_cast<const float4 *>(lg);
+        for (int c0 = tid; c0 - lane < nv; c0 += kLabThreads * U4) {  // wave-uniform bound
+            float4 v[U4];
+#pragma unroll
+            for (int u = 0; u < U4; ++u)
+                v[u] = l4[min(c0 + u * kLabThreads, nv - 1)];  // nv >= 1 inside the loop
+#pragma unroll
+            for (int u = 0; u < U4; ++u) {
+                const int c = c0 + u * kLabThreads;
+                const bool ok = c < nv;
+                f(4 * c + 0, order_key(v[u].x), ok);
+                f(4 * c + 1, order_key(v[u].y), ok);
+                f(4 * c + 2, order_key(v[u].z), ok);
+                f(4 * c + 3, order_key(v[u].w), ok);
+            }
+        }
+        const int y = 4 * nv + tid;  // the tail, fewer than four
+        const bool ok = y < V;
+        const uint32_t kt = order_key(lg[ok ? y : 0]);  // V >= 1
+        f(y, ok ? kt : 0u, ok);
+    } else {
+        for (int y0 = tid; y0 - lane < V; y0 += kLabThreads * kLabU) {  // wave-uniform bound
+            uint32_t k[kLabU];
+#pragma unroll
+            for (int u = 0; u < kLabU; ++u)
+                k[u] = order_key(lg[min(y0 + u * kLabThreads, V - 1)]);
+#pragma unroll
+            for (int u = 0; u < kLabU; ++u)
+                f(y0 + u * kLabThreads, k[u], y0 + u * kLabThreads < V);
+        }
+    }
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kLabThreads) void topl_labels_kernel(int V, int M, int L,
                                                                  const float *__restrict__ logits,
                                                                  int64_t ldl,
@@ -75,16 +120,10 @@ __global__ __launch_bounds__(kLabThreads) void topl_labels_kernel(int V, int M, 
         // Lc-th largest key of the row is >= T0 and every element that can be
         // selected (ties at the cut included) has a key >= T0.
         uint32_t mx = 0;
-        for (int y0 = tid; y0 - lane < V; y0 += kLabThreads * kLabU) {
-            uint32_t k[kLabU];
-#pragma unroll
-            for (int u = 0; u < kLabU; ++u)
-                k[u] = order_key(lg[min(y0 + u * kLabThreads, V - 1)]);
-#pragma unroll
-            for (int u = 0; u < kLabU; ++u)
-                if (y0 + u * kLabThreads < V)
-                    mx = max(mx, k[u]);
-        }
+        for_row_keys<VEC>(lg, V, tid, lane, [&](int, uint32_t k, bool ok) {
+            if (ok)
+                mx = max(mx, k);
+        });
         s_cand[tid] = ((uint64_t)mx << 32) | (uint32_t)~(uint32_t)tid;  // distinct: ties by thread
         if (tid == 0)
             s_cnt = 0u;
@@ -92,7 +131,8 @@ __global__ __launch_bounds__(kLabThreads) void topl_labels_kernel(int V, int M, 
         {
             const uint64_t mine = s_cand[tid];
             int rank = 0;
-            for (int j = 0; j < kLabThreads; ++j)
+#pragma unroll 16
+            for (int j = 0; j < kLabThreads; ++j)  // broadcast reads, many in flight
                 rank += s_cand[j] > mine ? 1 : 0;
             if (rank == Lc - 1)
                 s_t0 = mx;
@@ -101,27 +141,19 @@ __global__ __launch_bounds__(kLabThreads) void topl_labels_kernel(int V, int M, 
         const uint32_t T0 = s_t0;
         // Pass 2: the candidates (key >= T0) into LDS as (key, ~id): a larger
         // value ranks first, which is logit descending, then id ascending.
-        for (int y0 = tid; y0 - lane < V; y0 += kLabThreads * kLabU) {
-            uint32_t k[kLabU];
-#pragma unroll
-            for (int u = 0; u < kLabU; ++u)
-                k[u] = order_key(lg[min(y0 + u * kLabThreads, V - 1)]);
-#pragma unroll
-            for (int u = 0; u < kLabU; ++u) {
-                const int y = y0 + u * kLabThreads;
-                const bool c = y < V && k[u] >= T0;
-                const uint64_t bal = __ballot(c);
-                if (bal != 0ull) {  // uniform over the wave
-                    uint32_t base = 0u;
-                    if (lane == 0)
-                        base = atomicAdd(&s_cnt, (uint32_t)__popcll(bal));
-                    base = (uint32_t)__shfl((int)base, 0);
-                    const uint32_t pos = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-                    if (c && pos < (uint32_t)kLabCap)
-                        s_cand[pos] = ((uint64_t)k[u] << 32) | (uint32_t)~(uint32_t)y;
-                }
+        for_row_keys<VEC>(lg, V, tid, lane, [&](int y, uint32_t k, bool ok) {
+            const bool c = ok && k >= T0;
+            const uint64_t bal = __ballot(c);
+            if (bal != 0ull) {  // uniform over the wave
+                uint32_t base = 0u;
+                if (lane == 0)
+                    base = atomicAdd(&s_cnt, (uint32_t)__popcll(bal));
+                base = (uint32_t)__shfl((int)base, 0);
+                const uint32_t pos = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+                if (c && pos < (uint32_t)kLabCap)
+                    s_cand[pos] = ((uint64_t)k << 32) | (uint32_t)~(uint32_t)y;
             }
-        }
+        });
         __syncthreads();
         const uint32_t C = s_cnt;
         if (C <= (uint32_t)kLabCap) {
@@ -130,6 +162,7 @@ __global__ __launch_bounds__(kLabThreads) void topl_labels_kernel(int V, int M, 
             for (uint32_t i = tid; i < C; i += kLabThreads) {
                 const uint64_t v = s_cand[i];
                 int rank = 0;
+#pragma unroll 8
                 for (uint32_t j = 0; j < C; ++j)
                     rank += s_cand[j] > v ? 1 : 0;
                 if (rank < Lc) {
@@ -516,7 +549,10 @@ hipError_t gemm(hipStream_t s, int Mr, int Nc, int K, const TA *A, int64_t sam, 
 hipError_t topl_labels_launch(hipStream_t s, int n, int V, int M, int L, const float *logits,
                               int64_t ldl, const int32_t *cluster_of, uint8_t *labels)
 {
-    hipLaunchKernelGGL(topl_labels_kernel, dim3((unsigned)n), dim3(kLabThreads), 0, s, V, M, L,
+    // 16-byte loads where every row starts on a 16-byte boundary
+    const bool vec = (reinterpret_cast<uintptr_t>(logits) & 15) == 0 && ldl % 4 == 0;
+    hipLaunchKernelGGL(vec ? topl_labels_kernel<true> : topl_labels_kernel<false>,
+                       dim3((unsigned)n), dim3(kLabThreads), 0, s, V, M, L,
                        logits, ldl, cluster_of, labels);
     return hipGetLastError();
 }

@@ -59,6 +59,25 @@ def test_router_labels_bit_exact(N, oracle_lib, n, V, M, L):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("V,pad,shift", [(1003, 1, 0), (4099, 5, 0), (4099, 1, 1), (4, 0, 0)])
+def test_router_labels_row_stride(N, oracle_lib, V, pad, shift):
+    """Rows inside a wider buffer (row stride V + pad): 16-byte loads with a
+    tail of V % 4 elements when every row starts 16-byte aligned, element
+    loads when the view starts one element in (shift)."""
+    n, M, L = 3, 40, 64
+    g = np.random.default_rng(V + pad + shift)
+    lg = (g.standard_normal((n, V)) * 2).astype(np.float32)
+    lg[1, -3:] = 50.0  # the largest keys sit in the tail
+    cluster_of = g.integers(0, M, size=V).astype(np.int32)
+    buf = torch.full((n, shift + V + pad), float("nan"), dtype=torch.float32, device="cuda")
+    view = buf[:, shift:shift + V]
+    view.copy_(to_dev(lg))
+    out = torch.full((n, M), 7, dtype=torch.uint8, device="cuda")
+    N.router_labels(view, to_dev(cluster_of), M, L, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle_lib.topl_labels(lg, cluster_of, M, L))
+
+
 def test_router_labels_from_dense_head(N, oracle_lib):
     """Labels of the Llama-shaped head: the full drafter's logits come from
     the dense head (and agree with the gathered head over the whole
