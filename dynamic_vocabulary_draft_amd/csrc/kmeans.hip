@@ -9,12 +9,17 @@
 //
 // inverse norms: one wave per row, fp64 sums (once per W).
 // assign:  the V x M x d contraction on v_mfma_f32_32x32x16_bf16 with the
-//          argmax fused: a workgroup (8 waves) owns 256 rows x 128
-//          centroids, each wave a 64 x 64 block (2 x 2 MFMA tiles; the tall
-//          tile halves how often the centroids, which do not fit one XCD's
-//          L2, are streamed again); per 64-wide slice of d
-//          both tiles arrive as whole 128-byte lines (8 rows per load) into
-//          a double-buffered, XOR-swizzled LDS tile (one barrier per slice).
+//          argmax fused: a workgroup (8 waves, 4 high x 2 wide) owns 256
+//          rows x 256 centroids, each wave a 64 x 128 block (2 x 4 MFMA
+//          tiles: per slice, (256 + 256) rows pass through L2 for 256 x 256
+//          outputs, a third fewer bytes per product than 256 x 128, and the
+//          centroids, which do not fit one XCD's L2, are streamed V/256
+//          times); per 64-wide slice of d both tiles arrive as whole
+//          128-byte lines (8 rows per load) into a double-buffered,
+//          XOR-swizzled LDS tile (128 KB, one barrier per slice).  One slice
+//          is in flight in registers while the previous one is multiplied
+//          (a ring of two slices does not fit the 256 registers of a wave at
+//          two waves per SIMD).
 //          Workgroups that share a row tile are laid out on one XCD (blocks
 //          are dealt round-robin over the 8 XCDs), so the tile is read from
 //          HBM once and then from that XCD's L2.  The epilogue reduces each
@@ -44,7 +49,7 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer, CDNA encoding
 
 constexpr int kTileR = 256;  // W rows per workgroup (4 waves high)
-constexpr int kTileC = 128;  // centroids per workgroup (2 waves wide)
+constexpr int kTileC = 256;  // centroids per workgroup (2 waves wide, 128 each)
 constexpr int kAsgThreads = 512;
 constexpr int kSlice = 64;   // hidden elements per LDS stage (128 B per row)
 constexpr int kScatterChunk = 4096;
@@ -160,81 +165,93 @@ __device__ __forceinline__ u32x4 frag(const uint16_t *t, int row, int s)
 // STORE = false: the assignment (argmax epilogue into best); STORE = true:
 // the plain product, out[c][y] = W[y] . C[c] (row stride ldo), which is the
 // dense LM head when C holds hidden vectors.
-template <bool STORE>
+template <bool STORE, int TC>
 __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d, const uint16_t *__restrict__ W,
                                                             int M, const uint16_t *__restrict__ C,
                                                             int RT, int CT,
                                                             unsigned long long *__restrict__ best,
                                                             float *__restrict__ out, int64_t ldo)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(kTileR + kTileC) * kSlice];
+    constexpr int WCOLS = TC / 2, JT = WCOLS / 32;  // columns per wave, its 32-wide tiles
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(kTileR + TC) * kSlice];
     const int b = blockIdx.x;
     const int rt = (b / (8 * CT)) * 8 + (b % 8), ct = (b / 8) % CT;  // a row tile stays on one XCD
     if (rt >= RT)
         return;
     const int lane = lane_id(), wave = threadIdx.x >> 6, wr = wave >> 1, wc = wave & 1;  // 4 x 2 waves
     const int64_t y0 = (int64_t)rt * kTileR;
-    const int c0 = ct * kTileC;
-    const int rows = (int)min((int64_t)kTileR, (int64_t)V - y0), cols = min(kTileC, M - c0);
+    const int c0 = ct * TC;
+    const int rows = (int)min((int64_t)kTileR, (int64_t)V - y0), cols = min(TC, M - c0);
     const rsrc_t ra = make_rsrc(W + y0 * d, (uint32_t)rows * (uint32_t)d * 2u);
     const rsrc_t rb = make_rsrc(C + (int64_t)c0 * d, (uint32_t)cols * (uint32_t)d * 2u);
-    f32x16 acc[2][2];
+    f32x16 acc[2][JT];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < JT; ++j)
             acc[i][j] = f32x16{};
     const int nsl = d / kSlice;
-    constexpr int NA = kTileR * 8 / kAsgThreads, NB = kTileC * 8 / kAsgThreads;
-    // register ring of two slices (a loaded memory round trip is longer
-    // than one slice of MFMA work): while slice t is multiplied, slice t+1
-    // moves to LDS and slice t+3 is requested.  Loads past the last slice
-    // re-read it (clamped), so every load is unconditional and the compiler
-    // waits only for the slice it stores.
+    constexpr int NA = kTileR * 8 / kAsgThreads, NB = TC * 8 / kAsgThreads;
+    // register ring (128-column tiles: two slices, since a memory round
+    // trip is longer than one slice of their MFMA work; 256-column tiles:
+    // one): while slice t is multiplied, slice t+1 moves to LDS and slice
+    // t+3 (t+2) is requested.  Loads past the last slice re-read it
+    // (clamped), so every load is unconditional and the compiler waits only
+    // for the slice it stores.
     u32x4 a0[NA], b0[NB], a1[NA], b1[NB];
     uint32_t voa[NA], vob[NB];
     tile_offsets<kTileR>(d, voa);
-    tile_offsets<kTileC>(d, vob);
+    tile_offsets<TC>(d, vob);
 #define KM_LOAD(T, VA, VB)                                      \
     {                                                           \
         const int k0_ = min((T), nsl - 1) * kSlice;             \
         tile_load<kTileR>(ra, voa, k0_, VA);                    \
-        tile_load<kTileC>(rb, vob, k0_, VB);                    \
+        tile_load<TC>(rb, vob, k0_, VB);                        \
     }
     // one step: multiply slice T, move slice T+1 (held in VA/VB) to LDS,
     // request slice T+3 into VA/VB
-#define KM_STEP(T, VA, VB)                                                          \
+#define KM_STEP(T, VA, VB, DIST)                                                    \
     {                                                                               \
         const uint16_t *ta_ = lds[(T) & 1], *tb_ = lds[(T) & 1] + kTileR * kSlice;  \
         _Pragma("unroll") for (int st = 0; st < 4; ++st)                            \
         {                                                                           \
-            u32x4 fa_[2], fb_[2];                                                   \
+            u32x4 fa_[2], fb_[JT];                                                  \
             _Pragma("unroll") for (int i = 0; i < 2; ++i)                           \
                 fa_[i] = frag(ta_, wr * 64 + i * 32 + (lane & 31), st);             \
-            _Pragma("unroll") for (int j = 0; j < 2; ++j)                           \
-                fb_[j] = frag(tb_, wc * 64 + j * 32 + (lane & 31), st);             \
+            _Pragma("unroll") for (int j = 0; j < JT; ++j)                          \
+                fb_[j] = frag(tb_, wc * WCOLS + j * 32 + (lane & 31), st);          \
             _Pragma("unroll") for (int i = 0; i < 2; ++i)                           \
-                _Pragma("unroll") for (int j = 0; j < 2; ++j)                       \
+                _Pragma("unroll") for (int j = 0; j < JT; ++j)                      \
                     acc[i][j] = mfma(fa_[i], fb_[j], acc[i][j]);                    \
         }                                                                           \
         if ((T) + 1 < nsl) {                                                        \
             tile_store<kTileR>(lds[((T) + 1) & 1], VA);                             \
-            tile_store<kTileC>(lds[((T) + 1) & 1] + kTileR * kSlice, VB);           \
+            tile_store<TC>(lds[((T) + 1) & 1] + kTileR * kSlice, VB);               \
         }                                                                           \
-        KM_LOAD((T) + 3, VA, VB)                                                    \
+        KM_LOAD((T) + (DIST), VA, VB)                                               \
         __syncthreads();                                                            \
     }
-    KM_LOAD(0, a0, b0)
-    KM_LOAD(1, a1, b1)
-    tile_store<kTileR>(lds[0], a0);
-    tile_store<kTileC>(lds[0] + kTileR * kSlice, b0);
-    KM_LOAD(2, a0, b0)
-    __syncthreads();
-    for (int t = 0; t < nsl; t += 2) {
-        KM_STEP(t, a1, b1)
-        if (t + 1 >= nsl)
-            break;
-        KM_STEP(t + 1, a0, b0)
+    if constexpr (TC <= 128) {
+        KM_LOAD(0, a0, b0)
+        KM_LOAD(1, a1, b1)
+        tile_store<kTileR>(lds[0], a0);
+        tile_store<TC>(lds[0] + kTileR * kSlice, b0);
+        KM_LOAD(2, a0, b0)
+        __syncthreads();
+        for (int t = 0; t < nsl; t += 2) {
+            KM_STEP(t, a1, b1, 3)
+            if (t + 1 >= nsl)
+                break;
+            KM_STEP(t + 1, a0, b0, 3)
+        }
+    } else {  // a ring of one slice: twice the products per slice hide the load
+        KM_LOAD(0, a0, b0)
+        tile_store<kTileR>(lds[0], a0);
+        tile_store<TC>(lds[0] + kTileR * kSlice, b0);
+        KM_LOAD(1, a0, b0)
+        __syncthreads();
+        for (int t = 0; t < nsl; ++t)
+            KM_STEP(t, a0, b0, 2)
     }
 #undef KM_STEP
 #undef KM_LOAD
@@ -246,8 +263,8 @@ __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int col = wc * 64 + j * 32 + (lane & 31);
+            for (int j = 0; j < JT; ++j) {
+                const int col = wc * WCOLS + j * 32 + (lane & 31);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -261,14 +278,17 @@ __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            int col0 = wc * 64 + (lane & 31), col1 = col0 + 32;
-            float v0 = col0 < cols ? acc[i][0][r] : -INFINITY;
-            float v1 = col1 < cols ? acc[i][1][r] : -INFINITY;
-            float v = v0;
-            int c = col0;
-            if (v1 > v0) {
-                v = v1;
-                c = col1;
+            // the lane's columns ascend with j: a strict > keeps the lower
+            int c = wc * WCOLS + (lane & 31);
+            float v = c < cols ? acc[i][0][r] : -INFINITY;
+#pragma unroll
+            for (int j = 1; j < JT; ++j) {
+                const int cj = wc * WCOLS + j * 32 + (lane & 31);
+                const float vj = cj < cols ? acc[i][j][r] : -INFINITY;
+                if (vj > v) {
+                    v = vj;
+                    c = cj;
+                }
             }
 #pragma unroll
             for (int o = 16; o > 0; o >>= 1) {  // within each 32-lane half
@@ -614,7 +634,7 @@ hipError_t kmeans_assign_launch(hipStream_t s, int V, int d, const void *W, int 
         return e;
     const int RT = (V + kTileR - 1) / kTileR, CT = (M + kTileC - 1) / kTileC;
     const int RTp = (RT + 7) / 8 * 8;  // row tiles padded to whole XCD rounds
-    e = launch_timed(kmeans_assign_kernel<false>, dim3((unsigned)((int64_t)RTp * CT)), dim3(kAsgThreads), s, t0, t1,
+    e = launch_timed(kmeans_assign_kernel<false, kTileC>, dim3((unsigned)((int64_t)RTp * CT)), dim3(kAsgThreads), s, t0, t1,
                      V, d, reinterpret_cast<const uint16_t *>(W), M,
                      reinterpret_cast<const uint16_t *>(C), RT, CT, best, (float *)nullptr,
                      (int64_t)0);
@@ -674,7 +694,7 @@ hipError_t dense_head_launch(hipStream_t s, int V, int d, const void *W, int n, 
 {
     const int RT = (V + kTileR - 1) / kTileR, CT = (n + kTileC - 1) / kTileC;
     const int RTp = (RT + 7) / 8 * 8;
-    return launch_timed(kmeans_assign_kernel<true>, dim3((unsigned)((int64_t)RTp * CT)),
+    return launch_timed(kmeans_assign_kernel<true, kTileC>, dim3((unsigned)((int64_t)RTp * CT)),
                         dim3(kAsgThreads), s, t0, t1, V, d, reinterpret_cast<const uint16_t *>(W),
                         n, reinterpret_cast<const uint16_t *>(h), RT, CT,
                         (unsigned long long *)nullptr, logits, ldl);
