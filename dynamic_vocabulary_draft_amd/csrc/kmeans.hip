@@ -192,13 +192,13 @@ __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d
             acc[i][j] = f32x16{};
     const int nsl = d / kSlice;
     constexpr int NA = kTileR * 8 / kAsgThreads, NB = TC * 8 / kAsgThreads;
-    // register ring (128-column tiles: two slices, since a memory round
-    // trip is longer than one slice of their MFMA work; 256-column tiles:
-    // one): while slice t is multiplied, slice t+1 moves to LDS and slice
-    // t+3 (t+2) is requested.  Loads past the last slice re-read it
-    // (clamped), so every load is unconditional and the compiler waits only
-    // for the slice it stores.
-    u32x4 a0[NA], b0[NB], a1[NA], b1[NB];
+    // register ring of one slice (a 256-column slice holds enough MFMA work
+    // to cover a memory round trip; 128-column tiles needed two slices in
+    // flight): while slice t is multiplied, slice t+1 moves to LDS and slice
+    // t+2 is requested.  Loads past the last slice re-read it (clamped), so
+    // every load is unconditional and the compiler waits only for the slice
+    // it stores.
+    u32x4 a0[NA], b0[NB];
     uint32_t voa[NA], vob[NB];
     tile_offsets<kTileR>(d, voa);
     tile_offsets<TC>(d, vob);
@@ -209,8 +209,8 @@ __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d
         tile_load<TC>(rb, vob, k0_, VB);                        \
     }
     // one step: multiply slice T, move slice T+1 (held in VA/VB) to LDS,
-    // request slice T+3 into VA/VB
-#define KM_STEP(T, VA, VB, DIST)                                                    \
+    // request slice T+2 into VA/VB
+#define KM_STEP(T, VA, VB)                                                          \
     {                                                                               \
         const uint16_t *ta_ = lds[(T) & 1], *tb_ = lds[(T) & 1] + kTileR * kSlice;  \
         _Pragma("unroll") for (int st = 0; st < 4; ++st)                            \
@@ -228,31 +228,16 @@ __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d
             tile_store<kTileR>(lds[((T) + 1) & 1], VA);                             \
             tile_store<TC>(lds[((T) + 1) & 1] + kTileR * kSlice, VB);               \
         }                                                                           \
-        KM_LOAD((T) + (DIST), VA, VB)                                               \
+        KM_LOAD((T) + 2, VA, VB)                                                    \
         __syncthreads();                                                            \
     }
-    if constexpr (TC <= 128) {
-        KM_LOAD(0, a0, b0)
-        KM_LOAD(1, a1, b1)
-        tile_store<kTileR>(lds[0], a0);
-        tile_store<TC>(lds[0] + kTileR * kSlice, b0);
-        KM_LOAD(2, a0, b0)
-        __syncthreads();
-        for (int t = 0; t < nsl; t += 2) {
-            KM_STEP(t, a1, b1, 3)
-            if (t + 1 >= nsl)
-                break;
-            KM_STEP(t + 1, a0, b0, 3)
-        }
-    } else {  // a ring of one slice: twice the products per slice hide the load
-        KM_LOAD(0, a0, b0)
-        tile_store<kTileR>(lds[0], a0);
-        tile_store<TC>(lds[0] + kTileR * kSlice, b0);
-        KM_LOAD(1, a0, b0)
-        __syncthreads();
-        for (int t = 0; t < nsl; ++t)
-            KM_STEP(t, a0, b0, 2)
-    }
+    KM_LOAD(0, a0, b0)
+    tile_store<kTileR>(lds[0], a0);
+    tile_store<TC>(lds[0] + kTileR * kSlice, b0);
+    KM_LOAD(1, a0, b0)
+    __syncthreads();
+    for (int t = 0; t < nsl; ++t)
+        KM_STEP(t, a0, b0)
 #undef KM_STEP
 #undef KM_LOAD
     // epilogue: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 of
