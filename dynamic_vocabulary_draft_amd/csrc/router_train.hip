@@ -40,7 +40,8 @@ namespace {
 // ------------------------------------------------------------------ labels
 constexpr int kLabThreads = 1024;
 constexpr int kLabWaves = kLabThreads / kWave;
-constexpr int kLabCap = 2048;  // candidates ranked in LDS (>= kLabThreads)
+constexpr int kLabCap = 2048;  // candidates ranked in LDS
+static_assert(kLabCap >= kLabThreads, "the threads' maxima share the candidate buffer");
 constexpr int kLabU = 16;      // elements loaded per thread and round (all in flight)
 
 // larger float -> larger key; -0 and +0 are one value, as in a float compare
