@@ -1,5 +1,5 @@
 // Top-cluster selection under a position-aware budget (DynaSpec abstract:
-// the union of the top-selected clusters is the shortlist; summary page,
+// the shortlist is the union of the best-scoring clusters; summary page,
 // "Key Novelty" and "Key Hyperparameters": a budget k_c(t) that decays with
 // the draft position).
 //

@@ -1,7 +1,7 @@
 // Shortlist construction: the union of the selected clusters' members, in
-// ascending token id (DynaSpec abstract: "the union of the top-selected
-// clusters defines the drafter's shortlist"; summary page, "Problem
-// Definition": the output is the shortlisted subset V_S).
+// ascending token id (DynaSpec abstract: the shortlist is the union of the
+// selected clusters; summary page, "Problem Definition": the output is the
+// shortlisted subset V_S).
 //
 // The vocabulary is cut into chunks of kBuildChunk = 4096 tokens.  A
 // cluster index, built once per clustering from cluster_of, holds for every

@@ -1,9 +1,8 @@
 // Rejection-sampling verification over the full vocabulary, which keeps the
-// emitted tokens distributed exactly as the target (DynaSpec abstract: "the
-// target model still verifies over the full vocabulary, preserving
-// exactness"; summary page, "Pipeline Flow: Rejection Sampling
-// Verification"; the accept / residual / bonus rules are textbook
-// speculative sampling).
+// emitted tokens distributed exactly as the target (DynaSpec abstract: the
+// target checks every draft against its whole vocabulary, so the output is
+// exact; summary page, "Pipeline Flow: Rejection Sampling Verification"; the
+// accept / residual / bonus rules are textbook speculative sampling).
 //
 // Two launches, one workgroup per (1024-token chunk of V, sequence):
 //   sum:    the workgroup's four waves run the T accept tests (the draft

@@ -102,8 +102,8 @@ ds_status ds_router_score(hipStream_t s, ds_dtype dt, int n, int d, int r, int M
                           size_t ws_bytes);
 
 /*
- * Top-cluster selection under a position-aware budget [A "the union of the
- * top-selected clusters"; S "Key Novelty" (position-aware budget) and "Key
+ * Top-cluster selection under a position-aware budget [A: the shortlist is
+ * the union of the best-scoring clusters; S "Key Novelty" (position-aware budget) and "Key
  * Hyperparameters" (k_c(t) decays from k_0 to k_1)].  Per row, clusters are
  * ranked by (score descending, cluster id ascending); -0.0 ties with +0.0.
  *   DS_BUDGET_CLUSTERS: the first clamp(budget[row], 1, M) clusters.
@@ -137,8 +137,8 @@ ds_status ds_cluster_index(hipStream_t s, int M, int V, const int32_t *cluster_o
 
 /*
  * Shortlist = union of the selected clusters' member tokens, in ascending
- * token id [A "the union of the top-selected clusters defines the drafter's
- * shortlist"; S "Problem Definition": output V_S].
+ * token id [A: the shortlist is the union of the selected clusters;
+ * S "Problem Definition": output V_S].
  * sel [n][M], n_sel [n] as written by ds_select_clusters; cluster_of [V]
  * int32 maps every token to its cluster; index is its cluster index
  * (ds_cluster_index of the same cluster_of).
@@ -286,8 +286,8 @@ ds_status ds_target_softmax(hipStream_t s, int rows, int V, const float *logits,
 
 /*
  * Rejection-sampling verification over the full vocabulary, which keeps the
- * emitted tokens distributed exactly as the target [A "the target model
- * still verifies over the full vocabulary, preserving exactness"; S
+ * emitted tokens distributed exactly as the target [A: the target checks the
+ * drafts against its whole vocabulary, so the output is exact; S
  * "Pipeline Flow: Rejection Sampling Verification"].  For sequence b:
  *   for t < T: x = draft[t][b] (shortlist row t*B + b, ascending token ids,
  *   q in the sampler's layout with m = 1, q_t(x) = 0 off the shortlist);
@@ -415,8 +415,8 @@ ds_status ds_router_train_step(hipStream_t s, const ds_router_train_args *a);
 
 /*
  * One chain-drafting step over T positions for B sequences, with the router
- * on its own stream, overlapped with the head [A: routing is overlapped with
- * draft computation via parallel execution streams; S "Novel Architectural
+ * on its own stream, overlapped with the head [A: the router runs beside the
+ * drafter on concurrent streams to hide its cost; S "Novel Architectural
  * Elements": router on a separate stream].  For each position t:
  *   router_stream: router(h[:, t]) -> select(budget[t]) -> build (appending
  *                  to the shortlist buffer) -> event

@@ -118,8 +118,8 @@ static int rank_cmp(const void *a, const void *b)
 }
 
 /*
- * Top-cluster selection under a position-aware budget [A "the union of the
- * top-selected clusters"; S "Key Novelty": position-aware budget, larger
+ * Top-cluster selection under a position-aware budget [A: the shortlist is
+ * the union of the best-scoring clusters; S "Key Novelty": position-aware budget, larger
  * shortlists for early tokens; "Key Hyperparameters": k_c(t) decays from k_0
  * to k_1].  Clusters are ranked by (score desc, id asc).
  *   kind 0 (cluster budget): the first k = clamp(budget, 1, M) clusters.
@@ -165,9 +165,9 @@ void oracle_select_clusters(int n, int M, const float *scores,
 }
 
 /*
- * Shortlist = union of the selected clusters' members [A "the union of the
- * top-selected clusters defines the drafter's shortlist"; S "Problem
- * Definition": output V_S].  Listed in ascending token id.
+ * Shortlist = union of the selected clusters' members [A: the shortlist is
+ * the union of the selected clusters; S "Problem Definition": output V_S].
+ * Listed in ascending token id.
  * sl_off[0] is read (base offset); sl_off[1..n] are written; offsets never
  * exceed `capacity` (entries past it are dropped and OR_ECAPACITY returned).
  * Cluster ids outside [0, M) are skipped and OR_EINVAL returned.
@@ -407,9 +407,9 @@ void oracle_target_softmax(int rows, int V, const float *logits, float *p)
 
 /*
  * Rejection-sampling verification over the full vocabulary, which keeps the
- * output distributed exactly as the target [A "the target model still
- * verifies over the full vocabulary, preserving exactness"; S "Pipeline
- * Flow: Rejection Sampling Verification"; textbook speculative sampling].
+ * output distributed exactly as the target [A: the target checks the drafts
+ * against its whole vocabulary, so the output is exact; S "Pipeline Flow:
+ * Rejection Sampling Verification"; textbook speculative sampling].
  * For sequence b and positions t = 0..T-1 (draft[t][b], row t*B + b of the
  * shortlist arrays, q in the sampler's layout with m = 1):
  *   accept x iff u_acc * q_t(x) < p_t(x)   (q_t(x) = 0 off the shortlist);
