@@ -67,58 +67,30 @@ def head_source_sha() -> str:
     return h.hexdigest()
 
 
-class HipEvents:
-    """Timing events created through the HIP runtime (torch's Event only sees
-    torch's own streams)."""
-
-    def __init__(self):
-        self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                 ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.made = []
-
-    def array(self, n: int):
-        arr = (ctypes.c_void_p * n)()
-        for i in range(n):
-            e = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(e))
-            if rc != 0:
-                raise RuntimeError("hipEventCreate failed: %d" % rc)
-            arr[i] = e.value
-            self.made.append(e.value)
-        return arr
-
-    def elapsed_ms(self, a, b) -> float:
-        ms = ctypes.c_float()
-        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
-        if rc != 0:
-            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
-        return float(ms.value)
-
-    def close(self):
-        for e in self.made:
-            self.hip.hipEventDestroy(ctypes.c_void_p(e))
-        self.made = []
-
-
 def cpu_baseline(wl, seconds: float, static_ids=None) -> dict:
     import oracle
     from oracle import pipeline as opipe
     oracle.build(force=False)
     cfg = wl.cfg
-    n, t0 = 0, time.perf_counter()
-    while True:
-        if static_ids is None:
-            opipe.run_step(wl)
-        else:
-            opipe.run_static_step(wl, static_ids)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-        log("oracle step %d done (%.1f s)" % (n, el))
+    # one core: this thread is pinned to the lowest core it may run on (in
+    # this process, no re-exec), and the affinity is restored afterwards
+    old_aff = os.sched_getaffinity(0)
+    core = min(old_aff)
+    os.sched_setaffinity(0, {core})
+    try:
+        n, t0 = 0, time.perf_counter()
+        while True:
+            if static_ids is None:
+                opipe.run_step(wl)
+            else:
+                opipe.run_static_step(wl, static_ids)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+            log("oracle step %d done (%.1f s)" % (n, el))
+    finally:
+        os.sched_setaffinity(0, old_aff)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -136,8 +108,9 @@ def cpu_baseline(wl, seconds: float, static_ids=None) -> dict:
                if static_ids is None else "fp64 head over the static shortlist, sampling", cfg.T))
     return {"value": per_step * n / el, "unit": "draft tokens/s", "cores": 1,
             "kind": "oracle",
-            "sample": "%d full step(s) of instance 0 (%s), %.1f s on 1 thread of %d (%s)"
-                      % (n, what, el, os.cpu_count() or 0, model or platform.machine())}
+            "sample": "%d full step(s) of instance 0 (%s), %.1f s on 1 thread pinned to core "
+                      "%d of %d (%s)" % (n, what, el, core, os.cpu_count() or 0,
+                                         model or platform.machine())}
 
 
 COPY_BYTES = 1 << 30
@@ -272,7 +245,7 @@ def kmeans_bench(args):
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     uws = N.workspace(N.kmeans_update_workspace_bytes(V, d, M))
     aws = N.workspace(N.lib.ds_kmeans_assign_workspace_bytes(V))
-    ev = HipEvents()
+    ev = N.HipEvents()
     N.kmeans_inv_norms(W, inv)
     bufs = [C32, C32b]
 
@@ -369,7 +342,7 @@ def router_train_bench(args):
     labels = torch.empty(n, M, dtype=torch.uint8, device="cuda")
     loss = torch.empty(1, dtype=torch.float64, device="cuda")
     tws = N.workspace(N.router_train_workspace_bytes(n, r, M))
-    ev = HipEvents()
+    ev = N.HipEvents()
     lr = 0.05
 
     def step(k, events=None):
@@ -497,6 +470,9 @@ def main():
     ap.add_argument("--train-top", type=int, default=64)
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from the host instead of replaying step graphs")
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help="skip the other full-size workloads after the default one")
+    ap.add_argument("--extra-steps", type=int, default=20)
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -516,51 +492,104 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-
-    from dynamic_vocabulary_draft_amd import synthetic as syn
-    from dynamic_vocabulary_draft_amd.pipeline import DraftStep, StaticStep, to_dev
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    cfg = syn.CONFIGS[args.config]
+    r = run_draft(args.config, n_steps=args.steps, warmup=args.warmup,
+                  instances=args.instances, replicas=not args.no_replicas, eager=args.eager,
+                  static=args.static, static_size=args.static_size,
+                  pmc_probe_file=args.probe_file if args.pmc_probe else None)
+    if r is None:  # --pmc-probe
+        return
+    cfg, static_ids = r["cfg"], r["static_ids"]
+    from dynamic_vocabulary_draft_amd import synthetic as syn
+    out = {
+        "metric": "gathered-LM-head draft tokens/sec + HBM GB/s (% peak), V=128256 d=4096 bf16",
+        "value": r["value"], "unit": "draft tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": r["warmup"],
+        "ms_per_step": r["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == syn.DT_BF16 else "f32",
+        "data": "synthetic (seeded clustered-Gaussian W, N(0,1) hidden states, N(0,3) target "
+                "logits; %d instances rotated)" % args.instances,
+        "config": r["config"],
+        "step_ms": r["step_ms"],
+        "roofline": r["roofline"],
+        "head": r["head"],
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        wl0 = syn.make_workload(args.config, instance=0)
+        out["cpu_baseline"] = cpu_baseline(wl0, args.cpu_seconds, static_ids)
+        del wl0
+    if args.extra and args.config == 1 and not args.static:
+        # the other full-size workloads, head and step figures (fewer steps;
+        # no W replicas: every head launch there streams >= 1 GB, four times
+        # the 256 MB memory-side cache)
+        extra = {}
+        for k in (2, 3, 4):
+            torch.cuda.empty_cache()
+            x = run_draft(k, n_steps=args.extra_steps, warmup=4, instances=2, replicas=False,
+                          eager=args.eager)
+            extra[x["cfg"].name] = {
+                "draft_tokens_per_s": x["value"], "ms_per_step": x["ms_per_step"],
+                "step_ms": x["step_ms"], "steps": args.extra_steps, "instances": 2,
+                "step": x["config"]["step"], "roofline": x["roofline"], "head": x["head"]}
+        out["extra"] = extra
+    print(json.dumps(out), flush=True)
+
+
+def run_draft(index, *, n_steps, warmup, instances, replicas, eager, static=None,
+              static_size=32768, pmc_probe_file=None, n_ev_max=120):
+    """Time n_steps whole draft steps (plus verification) of workload
+    `index` and the head kernels inside them; returns the figures (or None
+    after a --pmc-probe run)."""
+    import numpy as np
+    import torch
+
+    from dynamic_vocabulary_draft_amd import native as N
+    from dynamic_vocabulary_draft_amd import synthetic as syn
+    from dynamic_vocabulary_draft_amd.pipeline import DraftStep, StaticStep, to_dev
+
+    cfg = syn.CONFIGS[index]
     e = cfg.elem_bytes
     t_gen = time.perf_counter()
     cluster_of, _ = syn.make_clusters(cfg)
     W_host = syn.make_lm_head(cfg, cluster_of, threads=min(16, os.cpu_count() or 8))
-    log("W generated (%.1f s)" % (time.perf_counter() - t_gen))
+    log("%s: W generated (%.1f s)" % (cfg.name, time.perf_counter() - t_gen))
     W = to_dev(W_host)
-    wls = [syn.make_workload(args.config, instance=i, with_W=False) for i in range(args.instances)]
+    wls = [syn.make_workload(index, instance=i, with_W=False) for i in range(instances)]
     for wl in wls:
         wl.W = W_host
     static_ids = None
-    if args.static:
+    if static:
         if cfg.is_tree:
             raise SystemExit("--static drafts chains; pick a chain workload")
-        static_ids = syn.static_shortlist(cfg, args.static_size)
-        steps = [StaticStep(wl, static_ids, W=W, packed=args.static == "packed") for wl in wls]
+        static_ids = syn.static_shortlist(cfg, static_size)
+        steps = [StaticStep(wl, static_ids, W=W, packed=static == "packed") for wl in wls]
     else:
         steps = [DraftStep(wl, W=W) for wl in wls]
+    del wls
     npos = 1 if cfg.is_tree else cfg.T
-    if not args.no_replicas and not cfg.is_tree:
+    if replicas and not cfg.is_tree:
         for i, st in enumerate(steps):
-            base = st.head_matrix() if args.static else W
+            base = st.head_matrix() if static else W
             reps = [base if t == 0 else base.clone() for t in range(npos)]
             st.set_W_positions(reps)
-        log("head-matrix replicas: %d x %.2f GB" % (args.instances * npos,
+        log("head-matrix replicas: %d x %.2f GB" % (instances * npos,
                                                     reps[0].numel() * e / 1e9))
     del W_host
     torch.cuda.synchronize()
 
-    ev = HipEvents()
+    ev = N.HipEvents()
     stream = torch.cuda.Stream()  # a capturable (non-default) head stream
-    args.warmup = max(args.warmup, len(steps))  # every instance has run once
+    warmup = max(warmup, len(steps))  # every instance has run once
     with torch.cuda.stream(stream):
-        for k in range(args.warmup):
+        for k in range(warmup):
             steps[k % len(steps)].step(stream)
     torch.cuda.synchronize()
-    log("eager warmup done (%d steps)" % args.warmup)
+    log("eager warmup done (%d steps)" % warmup)
 
     # shortlist sizes per (instance, position): deterministic per instance
     sizes = []
@@ -574,13 +603,13 @@ def main():
         sizes.append(per)
         assert int(st.err_flag.item()) == 0
 
-    if args.pmc_probe:
+    if pmc_probe_file:
+        args = argparse.Namespace(probe_file=pmc_probe_file)
         return pmc_probe(args, cfg, steps, sizes, npos, stream, torch, np)
-    timed_events = True
     graphs, mode = [], "eager"
-    if not args.eager:
+    if not eager:
         # a few graphs per instance, replayed round-robin
-        n_graphs = max(len(steps), min(args.steps, 16) // len(steps) * len(steps))
+        n_graphs = max(len(steps), min(n_steps, 16) // len(steps) * len(steps))
         try:
             for g in range(n_graphs):
                 graphs.append(steps[g % len(steps)].capture(stream))
@@ -602,20 +631,32 @@ def main():
             st.step(stream)
         return sets
 
+    # per-step boundaries on the head stream (torch events see this stream)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    marks[0].record(stream)
     if mode == "hip-graph":
-        for k in range(args.steps):
+        for k in range(n_steps):
             graphs[k % len(graphs)].launch(stream)
+            marks[k + 1].record(stream)
     else:
-        ev_sets = eager_steps(args.steps, timed_events)
+        ev_sets = []
+        for k in range(n_steps):
+            st = steps[k % len(steps)]
+            sset = ev.array(2 * npos)
+            st.set_head_events(sset)
+            st.step(stream)
+            ev_sets.append(sset)
+            marks[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    log("timed %d steps in %.3f s (%s)" % (args.steps, wall, mode))
-    if timed_events and mode == "hip-graph":
+    step_ms = [marks[k].elapsed_time(marks[k + 1]) for k in range(n_steps)]
+    log("timed %d steps in %.3f s (%s)" % (n_steps, wall, mode))
+    if mode == "hip-graph":
         # HIP cannot time events recorded inside graphs: the head launches
         # are timed on the same steps launched eagerly (same kernels, data)
-        n_ev = min(args.steps, 120)
+        n_ev = min(n_steps, n_ev_max)
         torch.cuda.synchronize()
         ev_sets = eager_steps(n_ev, True)
         torch.cuda.synchronize()
@@ -626,82 +667,84 @@ def main():
 
     tokens_per_step = cfg.B * (cfg.tree_nodes if cfg.is_tree else cfg.T)
     hrows = cfg.tree_nodes if cfg.is_tree else 1  # head rows per shortlist
-    value = tokens_per_step * args.steps / wall
-    roof = None
-    head = None
-    if timed_events:
-        durs, nbytes, rows = [], [], []
-        for k in range(len(ev_sets)):
-            i = k % len(steps)
-            for t in range(npos):
-                durs.append(ev.elapsed_ms(ev_sets[k][2 * t], ev_sets[k][2 * t + 1]))
-                sz = sizes[i][t]
-                # every needed W row once, the ids, the hidden rows, the logits
-                nbytes.append(sz["union"] * cfg.d * e + sz["total"] * 4
-                              + cfg.B * hrows * cfg.d * e + sz["total"] * hrows * 4)
-                rows.append(sz["total"])
-        mean_ms = float(np.mean(durs))
-        achieved = float(np.sum(nbytes)) / (float(np.sum(durs)) * 1e-3) / 1e9
-        traffic = None
-        if os.path.exists(TRAFFIC_FILE):
-            with open(TRAFFIC_FILE) as f:
-                tr = json.load(f)
-            if tr.get("kernel_source_sha256") == head_source_sha() and \
-                    tr.get("workload") == cfg.name:
-                traffic = tr.get("bytes_per_launch")
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
-        mfma = cfg.dtype == syn.DT_BF16 and ((hrows == 1 and cfg.B >= 8) or hrows >= 8)
-        kname = ("head_gemv_kernel" if not mfma else
-                 "head_union_kernel (tile index written by the build)" if hrows == 1 else
-                 "head_gathered_kernel")
-        head = {"kernel": kname, "launches_timed": len(durs),
-                "mean_us": round(mean_ms * 1e3, 2),
-                "p10_us": round(float(np.percentile(durs, 10)) * 1e3, 2),
-                "p90_us": round(float(np.percentile(durs, 90)) * 1e3, 2),
-                "mean_rows": round(float(np.mean(rows)), 1),
-                "mean_algorithmic_bytes": round(float(np.mean(nbytes)), 0),
-                "head_only_tokens_per_s": round(cfg.B * hrows / (mean_ms * 1e-3), 1),
-                "w_replicas": not args.no_replicas,
-                "timed_on": "eager steps (HIP events stamped at each head's own kernel start "
-                             "and end)"}
+    value = tokens_per_step * n_steps / wall
+    durs, nbytes, rows, flops = [], [], [], []
+    for k in range(len(ev_sets)):
+        i = k % len(steps)
+        for t in range(npos):
+            durs.append(ev.elapsed_ms(ev_sets[k][2 * t], ev_sets[k][2 * t + 1]))
+            sz = sizes[i][t]
+            # every needed W row once, the ids, the hidden rows, the logits
+            nbytes.append(sz["union"] * cfg.d * e + sz["total"] * 4
+                          + cfg.B * hrows * cfg.d * e + sz["total"] * hrows * 4)
+            rows.append(sz["total"])
+            flops.append(2.0 * hrows * sz["total"] * cfg.d)
+    mean_ms = float(np.mean(durs))
+    achieved = float(np.sum(nbytes)) / (float(np.sum(durs)) * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256") == head_source_sha() and \
+                tr.get("workload") == cfg.name:
+            traffic = tr.get("bytes_per_launch")
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+    mfma = cfg.dtype == syn.DT_BF16 and ((hrows == 1 and cfg.B >= 8) or hrows >= 8)
+    kname = ("head_gemv_kernel" if not mfma else
+             "head_union_kernel (tile index written by the build)" if hrows == 1 else
+             "head_gathered_kernel")
+    head = {"kernel": kname, "launches_timed": len(durs),
+            "mean_us": round(mean_ms * 1e3, 2),
+            "p10_us": round(float(np.percentile(durs, 10)) * 1e3, 2),
+            "p90_us": round(float(np.percentile(durs, 90)) * 1e3, 2),
+            "mean_rows": round(float(np.mean(rows)), 1),
+            "mean_union_rows": round(float(np.mean([s["union"] for p in sizes for s in p])), 1),
+            "mean_algorithmic_bytes": round(float(np.mean(nbytes)), 0),
+            "hbm_frac": round(achieved / PEAK_HBM_GBS, 4),
+            "head_only_tokens_per_s": round(cfg.B * hrows / (mean_ms * 1e-3), 1),
+            "w_replicas": bool(replicas and not cfg.is_tree),
+            "timed_on": "eager steps (HIP events stamped at each head's own kernel start "
+                        "and end)"}
+    if hrows >= 8:
+        # a real dense contraction: 64 head rows against each gathered row
+        tf = float(np.sum(flops)) / (float(np.sum(durs)) * 1e-3) / 1e12
+        ai = float(np.sum(flops)) / float(np.sum(nbytes))
+        attain = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3)
+        head.update({"algorithmic_flops": round(float(np.mean(flops)), 0),
+                     "tflops": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "flop_per_byte": round(ai, 1),
+                     "attainable_tflops": round(attain, 1),
+                     "frac_of_attainable": round(tf / attain, 4)})
     for g in graphs:
         g.close()
+    for st in steps:
+        if hasattr(st, "close"):
+            st.close()
     ev.close()
-
-    out = {
-        "metric": "gathered-LM-head draft tokens/sec + HBM GB/s (% peak), V=128256 d=4096 bf16",
-        "value": round(value, 1), "unit": "draft tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == syn.DT_BF16 else "f32",
-        "data": "synthetic (seeded clustered-Gaussian W, N(0,1) hidden states, N(0,3) target "
-                "logits; %d instances rotated)" % args.instances,
-        "config": {"workload": cfg.name if static_ids is None else
-                   "%s, static %s |S|=%d" % (cfg.name, args.static, static_ids.shape[0]),
-                   "V": cfg.V, "d": cfg.d, "clusters": cfg.M,
-                   "batch": cfg.B, "depth": cfg.T, "tree_nodes": cfg.tree_nodes,
-                   "budget": list(cfg.budget), "router": "%d->%d->%d" % (cfg.d, cfg.r, cfg.M),
-                   "step": ("router+select+build for the %d roots, gathered head over the "
-                            "%d nodes of each tree + sample per node, target softmax over "
-                            "the %d nodes + tree verify" % (cfg.B, cfg.tree_nodes,
-                                                            cfg.tree_nodes + 1))
-                           if cfg.is_tree else
-                           ("router+select+build+gathered head+sample per position, "
-                            "target softmax + verify") if static_ids is None else
-                           ("static baseline: %s head over one fixed %d-token frequency-ranked "
-                            "shortlist + sample per position, target softmax + verify"
-                            % (args.static, static_ids.shape[0])),
-                   "launch": mode},
-        "roofline": roof,
-        "head": head,
-        "cpu_baseline": None,
-    }
-    if not args.no_cpu_baseline:
-        wl0 = syn.make_workload(args.config, instance=0)
-        out["cpu_baseline"] = cpu_baseline(wl0, args.cpu_seconds, static_ids)
-    print(json.dumps(out), flush=True)
+    config = {"workload": cfg.name if static_ids is None else
+              "%s, static %s |S|=%d" % (cfg.name, static, static_ids.shape[0]),
+              "V": cfg.V, "d": cfg.d, "clusters": cfg.M,
+              "batch": cfg.B, "depth": cfg.T, "tree_nodes": cfg.tree_nodes,
+              "budget": list(cfg.budget), "router": "%d->%d->%d" % (cfg.d, cfg.r, cfg.M),
+              "step": ("router+select+build for the %d roots, gathered head over the "
+                       "%d nodes of each tree + sample per node, target softmax over "
+                       "the %d nodes + tree verify" % (cfg.B, cfg.tree_nodes,
+                                                       cfg.tree_nodes + 1))
+                      if cfg.is_tree else
+                      ("router+select+build+gathered head+sample per position, "
+                       "target softmax + verify") if static_ids is None else
+                      ("static baseline: %s head over one fixed %d-token frequency-ranked "
+                       "shortlist + sample per position, target softmax + verify"
+                       % (static, static_ids.shape[0])),
+              "launch": mode}
+    return {"cfg": cfg, "static_ids": static_ids, "value": round(value, 1), "warmup": warmup,
+            "ms_per_step": round(wall * 1e3 / n_steps, 4),
+            "step_ms": {"median": round(float(np.median(step_ms)), 4),
+                        "p10": round(float(np.percentile(step_ms, 10)), 4),
+                        "p90": round(float(np.percentile(step_ms, 90)), 4),
+                        "timed_on": "events between consecutive steps on the head stream"},
+            "roofline": roof, "head": head, "config": config}
 
 
 if __name__ == "__main__":

@@ -3,7 +3,6 @@
 // Nothing here allocates device memory.
 #include <atomic>
 #include <new>
-#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -38,28 +37,6 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 ds_status hip_status(hipError_t e) { return e == hipSuccess ? DS_OK : DS_EHIP; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-// per-thread pool of timing-free events for ds_draft_chain
-struct EventPool {
-    std::vector<hipEvent_t> ev;
-    hipError_t ensure(size_t n)
-    {
-        while (ev.size() < n) {
-            hipEvent_t e;
-            hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
-            if (r != hipSuccess)
-                return r;
-            ev.push_back(e);
-        }
-        return hipSuccess;
-    }
-    ~EventPool()
-    {
-        for (hipEvent_t e : ev)
-            (void)hipEventDestroy(e);
-    }
-};
-thread_local EventPool g_events;
 
 ds_status check_router(ds_dtype dt, int n, int d, int r, int M, ds_act act, const void *h,
                        int64_t ldh, const void *W1, const void *b1, const void *W2,
@@ -524,6 +501,12 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
         if (a->head_events && (!a->head_events[2 * t] || !a->head_events[2 * t + 1]))
             return DS_EINVAL;
     }
+    if (!a->sync_events)
+        return DS_EINVAL;
+    for (int k = 0; k <= 2 * T; ++k)
+        if (!a->sync_events[k])
+            return DS_EINVAL;
+    hipEvent_t *const ev = a->sync_events;
 
     float *z = reinterpret_cast<float *>(a->ws);
     void *bws = reinterpret_cast<char *>(a->ws) + round_up(ds_router_workspace_bytes(B, a->r), 256);
@@ -535,10 +518,8 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
     const bool prebuilt = ds::head_mfma_applies(a->dtype == DS_BF16, a->V, a->d, B, 1);
     const size_t tslot = round_up(ds::tile_index_bytes(B, a->V), 256);
     // events: [0, T) build of position t done, [T, 2T) h[t+1] ready (token
-    // t-1 sampled), 2T fork
-    if (g_events.ensure(2 * (size_t)T + 1) != hipSuccess)
-        return DS_EHIP;
-    hipEvent_t fork = g_events.ev[2 * T];
+    // t-1 sampled) or router of t done, 2T fork
+    hipEvent_t fork = ev[2 * T];
     const bool bf16 = a->dtype == DS_BF16;
     const char *hb = reinterpret_cast<const char *>(a->h);
     hipError_t err = hipEventRecord(fork, hs);
@@ -586,21 +567,21 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
         // (token t-1 sampled), 2T fork
         for (int t = 0; t < T && err == hipSuccess; ++t) {
             if (t > 0)  // h[t] (H_{t-1}) exists once token t-2 is sampled
-                err = hipStreamWaitEvent(rs, g_events.ev[T + t - 1], 0);
+                err = hipStreamWaitEvent(rs, ev[T + t - 1], 0);
             if (err == hipSuccess)
                 err = router_at(rs, t);
             if (err == hipSuccess)
                 err = select_build_at(rs, t);
             if (err == hipSuccess)
-                err = hipEventRecord(g_events.ev[t], rs);
+                err = hipEventRecord(ev[t], rs);
             // h[t+1] (read by head t and by router t+1) is ready once token
             // t-1 is sampled: the record follows sample t-1 directly, before
             // the head stream waits for build t, so router t+1 may run
             // alongside head t
             if (err == hipSuccess)
-                err = hipEventRecord(g_events.ev[T + t], hs);
+                err = hipEventRecord(ev[T + t], hs);
             if (err == hipSuccess)
-                err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
+                err = hipStreamWaitEvent(hs, ev[t], 0);
             if (err == hipSuccess)
                 err = head_sample_at(t);
         }
@@ -616,20 +597,20 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
     if (err == hipSuccess)
         err = router_at(hs, 0);
     if (err == hipSuccess)
-        err = hipEventRecord(g_events.ev[T], hs);
+        err = hipEventRecord(ev[T], hs);
     for (int t = 0; t < T && err == hipSuccess; ++t) {
-        err = hipStreamWaitEvent(rs, g_events.ev[T + t], 0);
+        err = hipStreamWaitEvent(rs, ev[T + t], 0);
         if (err == hipSuccess)
             err = select_build_at(rs, t);
         if (err == hipSuccess)
-            err = hipEventRecord(g_events.ev[t], rs);
+            err = hipEventRecord(ev[t], rs);
         if (err == hipSuccess && t + 1 < T) {
             err = router_at(hs, t + 1);
             if (err == hipSuccess)
-                err = hipEventRecord(g_events.ev[T + t + 1], hs);
+                err = hipEventRecord(ev[T + t + 1], hs);
         }
         if (err == hipSuccess)
-            err = hipStreamWaitEvent(hs, g_events.ev[t], 0);
+            err = hipStreamWaitEvent(hs, ev[t], 0);
         if (err == hipSuccess)
             err = head_sample_at(t);
     }

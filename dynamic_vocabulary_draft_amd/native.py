@@ -50,7 +50,7 @@ class ChainArgs(C.Structure):
                 ("scores", _vp), ("sel", _vp), ("n_sel", _vp), ("sl_len", _vp),
                 ("sl_off", _vp), ("sl_ids", _vp), ("logits", _vp), ("q", _vp),
                 ("token", _vp), ("err_flag", _vp), ("ws", _vp), ("ws_bytes", _sz),
-                ("W_pos", _vp), ("head_events", _vp)]
+                ("W_pos", _vp), ("head_events", _vp), ("sync_events", _vp)]
 
 
 _SIGS = {
@@ -115,6 +115,49 @@ def _load() -> C.CDLL:
 
 
 lib = _load()
+
+
+class HipEvents:
+    """HIP events created and destroyed through the HIP runtime (torch's
+    Event objects only see torch's own streams, and the library takes raw
+    hipEvent_t handles).  ``array(n)`` returns a ctypes array of n new
+    handles; ``close()`` destroys every event made here."""
+
+    _hip = None
+
+    def __init__(self):
+        if HipEvents._hip is None:
+            hip = C.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+            hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+            hip.hipEventDestroy.argtypes = [C.c_void_p]
+            HipEvents._hip = hip
+        self.hip = HipEvents._hip
+        self.made = []
+
+    def array(self, n: int, timing: bool = True):
+        arr = (C.c_void_p * n)()
+        flags = 0 if timing else 2  # hipEventDisableTiming
+        for i in range(n):
+            e = C.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(C.byref(e), flags)
+            if rc != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+            arr[i] = e.value
+            self.made.append(e.value)
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = C.c_float()
+        rc = self.hip.hipEventElapsedTime(C.byref(ms), C.c_void_p(a), C.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(ms.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(C.c_void_p(e))
+        self.made = []
 
 
 def _p(t):

@@ -111,7 +111,27 @@ class DraftStep:
                     N.verify_tree_workspace_bytes(B, m, V, int(self.max_len[0])), device)
             else:
                 self.verify_ws = N.workspace(N.verify_workspace_bytes(B, T, V), device)
-        self._args = self._chain_args() if not cfg.is_tree else None
+        self._events = None
+        self._args = None
+        if not cfg.is_tree:
+            # stream-ordering events of ds_draft_chain (destroyed in close())
+            self._events = N.HipEvents()
+            self._sync = self._events.array(2 * T + 1, timing=False)
+            self._args = self._chain_args()
+            self._args.sync_events = ctypes.cast(self._sync, ctypes.c_void_p)
+
+    def close(self) -> None:
+        """Destroy the chain's HIP events (after the work that uses them)."""
+        if self._events is not None:
+            torch.cuda.synchronize(self.device)
+            self._events.close()
+            self._events = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
     # ------------------------------------------------------------------ chains
     def _chain_args(self) -> N.ChainArgs:

@@ -19,9 +19,9 @@
  *
  * Conventions for every call:
  *   - Every array pointer is a DEVICE pointer owned by the caller.  The
- *     library never allocates, frees or retains caller memory, and keeps no
- *     state between calls apart from a per-thread pool of HIP events used
- *     by ds_draft_chain and a per-device cache of the compute-unit count.
+ *     library never allocates, frees or retains caller memory.  It keeps
+ *     no state between calls apart from a per-device cache of the
+ *     compute-unit count (a read-only device attribute).
  *   - Calls only enqueue work on the given stream(s) and return; nothing
  *     synchronises with the host.
  *   - Argument errors are detected on the host before anything is enqueued
@@ -436,8 +436,15 @@ ds_status ds_router_train_step(hipStream_t s, const ds_router_train_args *a);
  * retire: in this mode the two router layers of position t+1 run on
  * head_stream just before head t (h[:, t+1] exists then), and only the
  * selection and build of position t+1 run on router_stream beside head t.  Every pointer is a device pointer except
- * max_rows, max_len, W_pos and head_events (host arrays).  On return all work is
+ * max_rows, max_len, W_pos, head_events and sync_events (host arrays).  On return all work is
  * enqueued and head_stream waits for everything enqueued on router_stream.
+ * Required field:
+ *   sync_events  host array [2T+1] of caller-created HIP events on the
+ *                streams' device (hipEventDisableTiming is enough), used to
+ *                order the two streams; a call records and waits on them, so
+ *                two calls that may be enqueued concurrently need their own
+ *                arrays.  The caller destroys them (after the enqueued work,
+ *                or after ds_capture_end when the call was captured).
  * Optional fields:
  *   W_pos        host array [T] of head matrices, one per position (drafters
  *                with a separate head per position, or copies of one head on
@@ -477,6 +484,7 @@ typedef struct {
     size_t ws_bytes;
     const void *const *W_pos;   /* HOST [T] or NULL                */
     hipEvent_t *head_events;    /* HOST [2T] or NULL               */
+    hipEvent_t *sync_events;    /* HOST [2T+1], required           */
 } ds_draft_chain_args;
 
 size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r, int64_t max_len);

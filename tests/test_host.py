@@ -146,6 +146,27 @@ def test_select_build_head_sample_verify_reject_bad_arguments(N):
     assert L.ds_draft_chain(None, None, None) == 1
     a = N.ChainArgs(B=0, T=6)
     assert L.ds_draft_chain(None, None, C.byref(a)) == 1
+
+
+def test_draft_chain_requires_sync_events(N):
+    """Arguments that pass every other check, with no stream-ordering
+    events: rejected on the host before anything is enqueued."""
+    L = N.lib
+    T, B = 2, 1
+    max_rows = (C.c_int64 * T)(1000, 1000)
+    max_len = (C.c_int64 * T)(1000, 1000)
+    f = FAKE.value
+    a = N.ChainArgs(B=B, T=T, V=5000, d=64, r=64, M=16, dtype=N.BF16, act=N.SILU,
+                    budget_kind=N.BUDGET_TOKENS, temperature=1.0, W=f, W1=f, b1=f, W2=f, b2=f,
+                    cluster_of=f, cluster_index=f, cluster_size=f, h=f, budget=f, u_draft=f,
+                    capacity=4000, max_rows=C.cast(max_rows, C.c_void_p),
+                    max_len=C.cast(max_len, C.c_void_p), scores=f, sel=f, n_sel=f, sl_len=f,
+                    sl_off=f, sl_ids=f, logits=f, q=f, token=f, err_flag=None, ws=f,
+                    ws_bytes=1 << 30)
+    assert L.ds_draft_chain(None, None, C.byref(a)) == 1
+    ev = (C.c_void_p * (2 * T + 1))(*([f] * (2 * T)), None)  # one handle missing
+    a.sync_events = C.cast(ev, C.c_void_p)
+    assert L.ds_draft_chain(None, None, C.byref(a)) == 1
     assert L.ds_capture_begin(None) == 1
     assert L.ds_capture_end(None, None) == 1
     assert L.ds_graph_launch(None, None) == 1
