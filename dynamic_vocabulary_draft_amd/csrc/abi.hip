@@ -2,6 +2,7 @@
 // sizes, dispatch to the kernel families, and the two-stream chain runner.
 // Nothing here allocates device memory.
 #include <atomic>
+#include <mutex>
 #include <new>
 
 #include "common.h"
@@ -134,6 +135,40 @@ ds_status check_verify(int B, int T, int V, const int32_t *draft, const int64_t 
     if (T > 64 || V > (1 << 20) || B > DS_MAX_GROUPS || (int64_t)B * T > (1ll << 30))
         return DS_ESHAPE;
     return DS_OK;
+}
+
+// Scratch of ds_verify_reject_noalloc: one copy per device, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[DS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxScratchDevices];
+
+// Device address of `scratch` on the current device (looked up on the
+// device's first call, then cached).
+hipError_t scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace
@@ -368,6 +403,25 @@ ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *dr
         return st;
     if (!ws || ws_bytes < ds_verify_workspace_bytes(B, T, V))
         return DS_EINVAL;
+    return hip_status(ds::verify_launch(s, B, T, V, draft, sl_off, sl_ids, q, p, u_acc, u_fin,
+                                        n_acc, out, ws));
+}
+
+ds_status ds_verify_reject_noalloc(hipStream_t s, int B, int T, int V, const int32_t *draft,
+                                   const int64_t *sl_off, const int32_t *sl_ids, const float *q,
+                                   const float *p, const float *u_acc, const float *u_fin,
+                                   int32_t *n_acc, int32_t *out)
+{
+    ds_status st = check_verify(B, T, V, draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out);
+    if (st != DS_OK)
+        return st;
+    if (ds::verify_ws_bytes(B, T, V) > (size_t)DS_NOALLOC_SCRATCH_BYTES)
+        return DS_ESHAPE;
+    void *ws = nullptr;
+    if (scratch_address(&ws) != hipSuccess)
+        return DS_EHIP;
+    // every scratch entry the two kernels read is written earlier in the
+    // same call (chunk sums, first rejected position): nothing to clear
     return hip_status(ds::verify_launch(s, B, T, V, draft, sl_off, sl_ids, q, p, u_acc, u_fin,
                                         n_acc, out, ws));
 }

@@ -84,6 +84,8 @@ _SIGS = {
     "ds_verify_workspace_bytes": (_sz, [_i, _i, _i]),
     "ds_verify_reject": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               _sz]),
+    "ds_verify_reject_noalloc": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp]),
     "ds_verify_tree_workspace_bytes": (_sz, [_i, _i, _i, _i64]),
     "ds_verify_tree": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
                             _vp, _vp, _vp, _sz]),
@@ -355,6 +357,16 @@ def verify_reject(draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out, ws, *, 
     _check("ds_verify_reject", lib.ds_verify_reject(
         _s(stream), B, T, V, _p(draft), _p(sl_off), _p(sl_ids), _p(q), _p(p), _p(u_acc),
         _p(u_fin), _p(n_acc), _p(out), _p(ws), _nbytes(ws)))
+
+
+def verify_reject_noalloc(draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out, *,
+                          stream=None):
+    """ds_verify_reject without a workspace (the library's static scratch)."""
+    T, B = draft.shape
+    V = p.shape[-1]
+    _check("ds_verify_reject_noalloc", lib.ds_verify_reject_noalloc(
+        _s(stream), B, T, V, _p(draft), _p(sl_off), _p(sl_ids), _p(q), _p(p), _p(u_acc),
+        _p(u_fin), _p(n_acc), _p(out)))
 
 
 def verify_tree_workspace_bytes(B: int, m: int, V: int, max_len: int) -> int:

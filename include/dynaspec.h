@@ -21,7 +21,8 @@
  *   - Every array pointer is a DEVICE pointer owned by the caller.  The
  *     library never allocates, frees or retains caller memory.  It keeps
  *     no state between calls apart from a per-device cache of the
- *     compute-unit count (a read-only device attribute).
+ *     compute-unit count (a read-only device attribute) and, for
+ *     ds_verify_reject_noalloc alone, its per-device scratch array.
  *   - Calls only enqueue work on the given stream(s) and return; nothing
  *     synchronises with the host.
  *   - Argument errors are detected on the host before anything is enqueued
@@ -305,6 +306,26 @@ ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *dr
                            const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                            const float *p, const float *u_acc, const float *u_fin,
                            int32_t *n_acc, int32_t *out, void *ws, size_t ws_bytes);
+
+/*
+ * Allocation-free ds_verify_reject, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, semantics, limits and outputs as
+ * ds_verify_reject, without the workspace: the kernels' scratch lives in a
+ * static device array of DS_NOALLOC_SCRATCH_BYTES that every GPU the library
+ * runs on holds until the process ends (its address is looked up once per
+ * device, on that device's first call; the current device must be the
+ * stream's).  The call allocates nothing.  It needs
+ * ds_verify_workspace_bytes(B, T, V) <= DS_NOALLOC_SCRATCH_BYTES (about
+ * B * ceil(V / 1024) <= 349000), else DS_ESHAPE.  All calls on one GPU share
+ * that GPU's array, so calls that may overlap on one GPU (other streams,
+ * other threads) race and give wrong results; serialise them.
+ */
+#define DS_NOALLOC_SCRATCH_BYTES (8u << 20)
+ds_status ds_verify_reject_noalloc(hipStream_t s, int B, int T, int V, const int32_t *draft,
+                                   const int64_t *sl_off, const int32_t *sl_ids, const float *q,
+                                   const float *p, const float *u_acc, const float *u_fin,
+                                   int32_t *n_acc, int32_t *out);
 
 /*
  * Tree verification by multi-step speculative sampling, which keeps the

@@ -143,6 +143,14 @@ def test_select_build_head_sample_verify_reject_bad_arguments(N):
     assert L.ds_verify_reject(*ver(V=(1 << 20) + 1)) == 3
     assert L.ds_verify_reject(*ver(draft=None)) == 1
     assert L.ds_verify_reject(*ver()) == 1  # workspace too small
+    # the allocation-free variant: same checks, plus its scratch limit
+    nver = lambda **kw: ver(**kw)[:-2]  # noqa: E731  (no workspace arguments)
+    assert L.ds_verify_reject_noalloc(*nver(T=65)) == 3
+    assert L.ds_verify_reject_noalloc(*nver(draft=None)) == 1
+    assert L.ds_verify_reject_noalloc(*nver(B=0)) == 1
+    assert L.ds_verify_reject_noalloc(*nver(B=1024, V=1 << 20)) == 3  # over the scratch
+    assert N.verify_workspace_bytes(1024, 3, 1 << 20) > (8 << 20)
+    assert N.verify_workspace_bytes(64, 5, 262144) <= (8 << 20)
     assert L.ds_draft_chain(None, None, None) == 1
     a = N.ChainArgs(B=0, T=6)
     assert L.ds_draft_chain(None, None, C.byref(a)) == 1
