@@ -354,6 +354,40 @@ def test_head_tree_tile_orders(N, oracle_lib, G, m, lo, hi):
     _logit_bar(got, ref, True)
 
 
+@pytest.mark.parametrize("G,m,d", [(8, 64, 264), (8, 100, 264), (5, 8, 4096), (1, 64, 264),
+                                   (8, 32, 520)])
+def test_head_tree_shared_rows(N, oracle_lib, G, m, d):
+    """Tree head over trees whose shortlists overlap heavily: a block of
+    tokens on every tree, blocks shared by pairs of neighbouring trees, and
+    scattered tokens of each tree alone; one pass of up to 64 head rows or
+    two (100 rows), one or two 32-row column blocks, d of one and several
+    phases.  Every logit is checked against the oracle."""
+    V = 20000
+    g = np.random.default_rng(G * 100 + m + d)
+    cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=50, dtype=syn.DT_BF16)
+    cluster_of, _ = _clusters(V, 50, 3)
+    W = syn.make_lm_head(cfg, cluster_of)
+    h = _store(g.standard_normal((G, m, d)).astype(np.float32), True)
+    perm = g.permutation(V)
+    common = perm[:1500]
+    pairs = [perm[1500 + 700 * k: 2200 + 700 * k] for k in range(G)]
+    rest = perm[1500 + 700 * G:]
+    ids = []
+    for k in range(G):
+        own = g.choice(rest, 900 + 137 * k, replace=False)
+        sel = [common, pairs[k], pairs[(k + 1) % G], own]
+        ids.append(np.unique(np.concatenate(sel)).astype(np.int32))
+    sl_off = np.concatenate([[0], np.cumsum([len(x) for x in ids])]).astype(np.int64)
+    sl_ids = np.concatenate(ids)
+    ref = oracle_lib.gathered_lm_head(W, h, sl_off, sl_ids)
+    logits = torch.full((m * int(sl_off[-1]),), float("nan"), device="cuda")
+    N.gathered_lm_head(to_dev(W), to_dev(h), to_dev(sl_off), to_dev(sl_ids),
+                       int(max(len(x) for x in ids)), logits)
+    got = _cpu(logits)
+    assert not np.isnan(got).any()
+    _logit_bar(got, ref, True)
+
+
 @pytest.mark.parametrize("G,m", [(3, 1), (16, 1), (3, 8)])
 def test_head_invalid_ids_are_nan(N, oracle_lib, G, m):
     """Ids outside [0, V) give NaN on every kernel path (GEMV, union, gathered);
