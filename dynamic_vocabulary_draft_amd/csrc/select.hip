@@ -3,16 +3,21 @@
 // "Key Novelty" and "Key Hyperparameters": a budget k_c(t) that decays with
 // the draft position).
 //
-// One workgroup per row.  The M (<= 4096) clusters are ranked with a bitonic
-// sort over 64-bit keys (order-preserving score bits, inverted for
-// descending order, above the cluster id), which realises the total order
-// (score desc, id asc) exactly.  Keys live in registers (one to four per
-// thread); compare-exchange partners closer than 64 positions are in the
-// same wave and are fetched with lane shuffles, only the wider strides go
-// through LDS with barriers.  The budget cut is one block-wide exclusive
-// scan of the ranked sizes: with a token budget, a cluster is taken iff the
-// tokens ranked before it fall short of the budget; the thread holding the
-// last taken cluster writes the count and the total.
+// One workgroup per row.  Every cluster gets a unique 64-bit key: the
+// order-preserving bits of its score, inverted so that ascending keys are
+// descending scores, above the cluster id; ascending keys are then exactly
+// the order (score desc, id asc).  The selection is a prefix of that order
+// ending at the first cluster where the running total reaches the target
+// (the budget's token count with the cluster sizes as weights, or its
+// cluster count with unit weights): with a token budget, a cluster is taken
+// iff the tokens ranked before it fall short of the budget.  That last key
+// is found without sorting, by a weighted radix search from the most
+// significant bits: per pass a 4096-bin LDS histogram (12 bits) of the
+// weights of the keys still in play, a block-wide scan for the bin where the
+// running total reaches the target, and the next 12 bits within that bin,
+// until one key is left (two passes for distinct scores).  Only the taken
+// clusters are then ranked, each by counting the taken keys below its own
+// (several threads per key), and written in that order.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,93 +33,145 @@ __device__ __forceinline__ uint32_t ordered_bits(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
-{
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    lo = __shfl_xor(lo, m);
-    hi = __shfl_xor(hi, m);
-    return ((uint64_t)hi << 32) | lo;
-}
+constexpr int kSelThreads = 1024;
+constexpr int kDigitBits = 12;
+constexpr int kBins = 1 << kDigitBits;  // 4 bins per thread
 
 template <int KPT>
-__global__ __launch_bounds__(1024) void select_kernel(int M, int P, const float *__restrict__ scores,
-                                                      const int32_t *__restrict__ cluster_size,
-                                                      int kind, const int32_t *__restrict__ budget,
-                                                      int32_t *__restrict__ sel,
-                                                      int32_t *__restrict__ n_sel,
-                                                      int32_t *__restrict__ sl_len)
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    int M, const float *__restrict__ scores, const int32_t *__restrict__ cluster_size, int kind,
+    const int32_t *__restrict__ budget, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
+    int32_t *__restrict__ sl_len)
 {
-    extern __shared__ uint64_t keys[];  // P entries
+    // weight histogram of one pass, then the taken keys
+    __shared__ unsigned long long s_hw[kBins];
+    __shared__ int s_hc[kBins];
     __shared__ int64_t scan_sh[kWave + 1];
-    const int row = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+    __shared__ int s_digit, s_cnt, s_ntake;
+    __shared__ long long s_below;
+    __shared__ unsigned long long s_kstar, s_tok;
+    const int row = blockIdx.x, tid = threadIdx.x;
     const float *s = scores + (int64_t)row * M;
-
+    const bool tokens = kind != DS_BUDGET_CLUSTERS;
     uint64_t k[KPT];
+    int64_t w[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        const int idx = tid + i * nt;
-        k[i] = idx < M ? ((uint64_t)(~ordered_bits(s[idx])) << 32) | (uint32_t)idx : ~0ull;
+        const int idx = tid + i * kSelThreads;
+        const bool in = idx < M;
+        k[i] = in ? ((uint64_t)(~ordered_bits(s[idx])) << 32) | (uint32_t)idx : ~0ull;
+        w[i] = in ? (tokens ? (int64_t)max(cluster_size[idx], 0) : 1) : 0;
     }
-    // bitonic sort, ascending keys == (score desc, id asc)
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            uint64_t partner[KPT];
-            if (stride >= kWave) {
-#pragma unroll
-                for (int i = 0; i < KPT; ++i)
-                    keys[tid + i * nt] = k[i];
-                __syncthreads();
-#pragma unroll
-                for (int i = 0; i < KPT; ++i)
-                    partner[i] = keys[(tid + i * nt) ^ stride];
-                __syncthreads();
-            } else {
-#pragma unroll
-                for (int i = 0; i < KPT; ++i)
-                    partner[i] = shfl_xor_u64(k[i], stride);
-            }
-#pragma unroll
-            for (int i = 0; i < KPT; ++i) {
-                const int idx = tid + i * nt;
-                const bool asc = (idx & size) == 0, lower = (idx & stride) == 0;
-                const uint64_t lo = k[i] < partner[i] ? k[i] : partner[i];
-                const uint64_t hi = k[i] < partner[i] ? partner[i] : k[i];
-                k[i] = (lower == asc) ? lo : hi;
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-        keys[tid + i * nt] = k[i];
-    __syncthreads();
-
     const int32_t bud = budget[row];
-    const int kclusters = bud < 1 ? 1 : (bud > M ? M : bud);
-    const int64_t btokens = bud < 1 ? 1 : (int64_t)bud;
-    __shared__ int s_take;
-    __shared__ long long s_total;
-    int64_t carry = 0;
-    for (int base = 0; base < M; base += nt) {  // uniform trip count
-        const int j = base + tid;
-        const int64_t v = j < M ? cluster_size[(uint32_t)keys[j]] : 0;
-        int64_t tot;
-        const int64_t excl = block_excl_scan_i64(v, scan_sh, &tot) + carry;
-        const bool take = j < M && (kind == DS_BUDGET_CLUSTERS ? j < kclusters : excl < btokens);
-        const bool next = j + 1 < M &&
-                          (kind == DS_BUDGET_CLUSTERS ? j + 1 < kclusters : excl + v < btokens);
-        if (take && !next) {  // the last cluster of the taken prefix
-            s_take = j + 1;
-            s_total = excl + v;
+    const int64_t target = tokens ? (bud < 1 ? 1 : (int64_t)bud) : (bud < 1 ? 1 : (bud > M ? M : bud));
+    if (tid == 0) {
+        s_ntake = 0;
+        s_tok = 0;
+    }
+
+    uint64_t kstar = ~0ull;  // the last taken key (all of them when the target is out of reach)
+    uint64_t prefix = 0;     // the key bits above `shift` fixed so far
+    int64_t below = 0;       // weight of the keys below that prefix
+    int shift = 64;
+    for (;;) {
+        const int bits = shift >= kDigitBits ? kDigitBits : shift;
+        shift -= bits;
+        const uint64_t dmask = ((uint64_t)1 << bits) - 1;
+#pragma unroll
+        for (int q = 0; q < kBins / kSelThreads; ++q) {
+            s_hw[tid + q * kSelThreads] = 0;
+            s_hc[tid + q * kSelThreads] = 0;
         }
-        carry += tot;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const bool cand = tid + i * kSelThreads < M &&
+                              (shift + bits == 64 || (k[i] >> (shift + bits)) == prefix);
+            if (cand) {
+                const int d = (int)((k[i] >> shift) & dmask);
+                if (w[i])
+                    atomicAdd(&s_hw[d], (unsigned long long)w[i]);
+                atomicAdd(&s_hc[d], 1);
+            }
+        }
+        __syncthreads();
+        // the first bin where below + (weights of the bins up to it) >= target
+        constexpr int BPT = kBins / kSelThreads;
+        int64_t bw[BPT], local = 0;
+#pragma unroll
+        for (int q = 0; q < BPT; ++q) {
+            bw[q] = (int64_t)s_hw[tid * BPT + q];
+            local += bw[q];
+        }
+        int64_t total;
+        int64_t run = below + block_excl_scan_i64(local, scan_sh, &total);
+        if (shift + bits == 64 && total < target)  // block-uniform: the whole order is taken
+            break;
+#pragma unroll
+        for (int q = 0; q < BPT; ++q) {
+            if (run < target && run + bw[q] >= target) {
+                s_digit = tid * BPT + q;
+                s_below = run;
+                s_cnt = s_hc[tid * BPT + q];
+            }
+            run += bw[q];
+        }
+        __syncthreads();
+        prefix = (prefix << bits) | (uint64_t)s_digit;
+        below = s_below;
+        if (s_cnt == 1 || shift == 0) {  // one key left in the bin: it is the cut
+#pragma unroll
+            for (int i = 0; i < KPT; ++i)
+                if (tid + i * kSelThreads < M && (k[i] >> shift) == prefix)
+                    s_kstar = k[i];
+            __syncthreads();
+            kstar = s_kstar;
+            break;
+        }
+        __syncthreads();  // every thread has read the pass's result
+    }
+
+    // the taken keys (k <= kstar) into LDS, in any order; their count and
+    // token total (integer sums: the same whatever the order)
+    uint64_t *taken = reinterpret_cast<uint64_t *>(s_hw);
+    static_assert(kBins >= kSelThreads * KPT, "room for every key");
+    __syncthreads();  // the histogram is no longer read
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int idx = tid + i * kSelThreads;
+        if (idx < M && k[i] <= kstar) {
+            taken[atomicAdd(&s_ntake, 1)] = k[i];
+            const int32_t sz = cluster_size[idx];
+            if (sz > 0)
+                atomicAdd(&s_tok, (unsigned long long)sz);
+        }
     }
     __syncthreads();
-    const int take = s_take;
-    for (int j = tid; j < M; j += nt)
-        sel[(int64_t)row * M + j] = j < take ? (int32_t)(uint32_t)keys[j] : -1;
+    const int nt = s_ntake;
+    int32_t *out = sel + (int64_t)row * M;
+    // rank of each taken key = the number of smaller taken keys: P threads
+    // per key (a power of two) each count a strided share, then add up
+    int P = 1;
+    while (P * 2 * nt <= kSelThreads && P < kWave)
+        P *= 2;
+    const int part = tid & (P - 1);
+    for (int a0 = 0; a0 < nt; a0 += kSelThreads / P) {  // block-uniform trip count
+        const int a = a0 + tid / P;
+        const uint64_t ka = a < nt ? taken[a] : 0ull;
+        int r = 0;
+        if (a < nt)
+            for (int j = part; j < nt; j += P)
+                r += taken[j] < ka;
+        for (int o = 1; o < P; o <<= 1)
+            r += __shfl_xor(r, o);
+        if (a < nt && part == 0)
+            out[r] = (int32_t)(uint32_t)ka;
+    }
+    for (int j = nt + tid; j < M; j += kSelThreads)
+        out[j] = -1;
     if (tid == 0) {
-        n_sel[row] = take;
-        sl_len[row] = (int32_t)s_total;
+        n_sel[row] = nt;
+        sl_len[row] = (int32_t)s_tok;
     }
 }
 
@@ -124,21 +181,16 @@ hipError_t select_launch(hipStream_t s, int n, int M, const float *scores,
                          const int32_t *cluster_size, int kind, const int32_t *budget,
                          int32_t *sel, int32_t *n_sel, int32_t *sl_len)
 {
-    int P = kWave;
-    while (P < M)
-        P <<= 1;
-    const int nt = P < 1024 ? P : 1024;
-    const int kpt = P / nt;
-    const size_t lds = (size_t)P * sizeof(uint64_t);
+    const int kpt = (M + kSelThreads - 1) / kSelThreads;  // M <= 4096
     if (kpt == 1)
-        hipLaunchKernelGGL(select_kernel<1>, dim3(n), dim3(nt), lds, s, M, P, scores, cluster_size,
-                           kind, budget, sel, n_sel, sl_len);
+        hipLaunchKernelGGL(select_kernel<1>, dim3(n), dim3(kSelThreads), 0, s, M, scores,
+                           cluster_size, kind, budget, sel, n_sel, sl_len);
     else if (kpt == 2)
-        hipLaunchKernelGGL(select_kernel<2>, dim3(n), dim3(nt), lds, s, M, P, scores, cluster_size,
-                           kind, budget, sel, n_sel, sl_len);
+        hipLaunchKernelGGL(select_kernel<2>, dim3(n), dim3(kSelThreads), 0, s, M, scores,
+                           cluster_size, kind, budget, sel, n_sel, sl_len);
     else
-        hipLaunchKernelGGL(select_kernel<4>, dim3(n), dim3(nt), lds, s, M, P, scores, cluster_size,
-                           kind, budget, sel, n_sel, sl_len);
+        hipLaunchKernelGGL(select_kernel<4>, dim3(n), dim3(kSelThreads), 0, s, M, scores,
+                           cluster_size, kind, budget, sel, n_sel, sl_len);
     return hipGetLastError();
 }
 

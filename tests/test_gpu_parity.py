@@ -118,6 +118,31 @@ def test_select_parity(N, oracle_lib, M, kind):
     assert np.array_equal(_cpu(sel), ref[0])
 
 
+@pytest.mark.parametrize("M", [100, 1024, 3000])
+def test_select_zero_sizes_and_ties(N, oracle_lib, M):
+    """Token budgets over clusters of which a third are empty, with tied
+    scores: the cut falls where the running size first reaches the budget,
+    empty clusters ranked before it are taken and those after it are not."""
+    g = np.random.default_rng(M + 11)
+    n = 12
+    s = g.integers(-3, 4, size=(n, M)).astype(np.float32)
+    s[n // 2:] = g.standard_normal((n - n // 2, M)).astype(np.float32)
+    size = g.integers(0, 60, size=M).astype(np.int32)
+    size[g.random(M) < 0.33] = 0
+    total = int(size.sum())
+    budget = np.array([0, 1, 2, 59, 60, 61, total // 7, total // 2, total - 1, total, total + 1,
+                       3], np.int32)
+    for kind in (syn.BUDGET_TOKENS, syn.BUDGET_CLUSTERS):
+        ref = oracle_lib.select_clusters(s, size, kind, budget)
+        sel = torch.empty(n, M, dtype=torch.int32, device="cuda")
+        n_sel = torch.empty(n, dtype=torch.int32, device="cuda")
+        sl_len = torch.empty(n, dtype=torch.int32, device="cuda")
+        N.select_clusters(to_dev(s), to_dev(size), kind, to_dev(budget), sel, n_sel, sl_len)
+        assert np.array_equal(_cpu(n_sel), ref[1])
+        assert np.array_equal(_cpu(sl_len), ref[2])
+        assert np.array_equal(_cpu(sel), ref[0])
+
+
 # ----------------------------------------------------------------------------
 # build_shortlist: bit-exact
 # ----------------------------------------------------------------------------
