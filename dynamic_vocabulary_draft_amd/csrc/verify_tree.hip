@@ -21,12 +21,25 @@
 // (u * q < p); every later test and the final draw differ from a sequential
 // fp64 evaluation by rounding order only.
 //
-// Two launches:
+// The chain at a node does not depend on how the walk reached it, and every
+// walk starts at the root, so the root's chain is precomputed on many
+// compute units (when the root has one or two children): after a rejection
+// of its first child the residual is max(0, p_0 - q_c1) on the shortlist,
+// after the second max(0, R_1 - P_1 q_c2).  Per 4096-token chunk, one pass
+// totals the mass off the shortlist, p_0 on it and R_1; a second pass, which
+// rebuilds P_1 from those totals in chunk order, totals R_2.  The walk then
+// tests the root's children from these normalisers and, when both are
+// rejected, finds the chunk holding the threshold from the chunk totals and
+// draws inside that chunk alone.  Below the root the walk is sequential.
+//
+// Four launches:
 //   bits: one workgroup per (32768 tokens, sequence) writes the shortlist's
 //         membership bitmap (bit y set iff token y is listed) and, per
 //         32-token word, the number of listed tokens before it, so the
 //         position of a listed token in the ascending shortlist is
 //         rank[word] + a popcount;
+//   root1, root2: the root's chunk totals (one workgroup per chunk and
+//         sequence);
 //   walk: one workgroup per sequence: every drafted node's shortlist
 //         position, u * q and target value at its parent go to LDS (a
 //         node's first test then needs no memory access), then the walk.
@@ -138,8 +151,7 @@ __device__ __forceinline__ double block_sum_f64(double v, double *sh)
         sh[threadIdx.x >> 6] = w;
     __syncthreads();
     double t = 0.0;
-#pragma unroll
-    for (int k = 0; k < kTreeWaves; ++k)
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k)
         t += sh[k];
     __syncthreads();
     return t;
@@ -290,20 +302,220 @@ __device__ __forceinline__ void draw_weights(const float *__restrict__ pu,
     }
 }
 
+// ---------------------------------------------------------------- root
+constexpr int kRootChunk = 4096;    // tokens per chunk of the root's passes
+constexpr int kRootThreads = 256;   // 16 tokens per thread
+constexpr int kRootMaxKids = 2;     // children handled by the precomputed chain
+
+__host__ __device__ inline int64_t root_chunks(int V) { return ((int64_t)V + kRootChunk - 1) / kRootChunk; }
+
+// per (sequence, chunk): mass off the shortlist, p_0 on it, sum R_1, sum R_2
+struct RootPart {
+    double off, sp, s1, s2;
+};
+
+__host__ __device__ inline size_t root_part_bytes(int B, int V)
+{
+    return ((size_t)B * (size_t)root_chunks(V) * sizeof(RootPart) + 255) / 256 * 256;
+}
+
+// residual update max(0, r - P q) without contraction into an fma (the
+// walk recomputes it and must get the same bits)
+__device__ __forceinline__ double resid(double r, double P, float q)
+{
+    const double t = __dmul_rn(P, (double)q);
+    return r > t ? __dsub_rn(r, t) : 0.0;
+}
+
+// the root's first two children (node numbers, in increasing order) and the
+// number of its children (capped at kRootMaxKids + 1); all threads
+__device__ void root_kids(const int32_t *__restrict__ parent_b, int m, int *s3, int *c1, int *c2,
+                          int *k)
+{
+    if (threadIdx.x == 0) {
+        s3[0] = INT_MAX;
+        s3[1] = INT_MAX;
+        s3[2] = 0;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x + 1; i <= m; i += blockDim.x)
+        if (parent_b[i - 1] == 0) {
+            atomicMin(&s3[0], i);
+            atomicAdd(&s3[2], 1);
+        }
+    __syncthreads();
+    const int a = s3[0];
+    for (int i = threadIdx.x + 1; i <= m; i += blockDim.x)
+        if (parent_b[i - 1] == 0 && i > a)
+            atomicMin(&s3[1], i);
+    __syncthreads();
+    *c1 = a;
+    *c2 = s3[1];
+    *k = min(s3[2], kRootMaxKids + 1);
+    __syncthreads();
+}
+
+// The shortlist entries with ids in [base, base + kRootChunk): membership
+// bits (from the sequence's bitmap) and the proposals q1 (and q2) of the
+// root's children at those ids, scattered into LDS (the entries are
+// positions rank[base/32] .. of the ascending shortlist); returns after a
+// barrier.
+__device__ void root_scatter(const uint32_t *__restrict__ bits_b, const uint32_t *__restrict__ rank_b,
+                             int V, int len, int64_t base, const float *__restrict__ q1,
+                             const float *__restrict__ q2, uint32_t *mem, float *q1d, float *q2d)
+{
+    const int64_t nw = tree_words(V);
+    const int64_t w0 = base >> 5;
+    for (int i = threadIdx.x; i < kRootChunk / 32; i += blockDim.x) {
+        const uint32_t wd = w0 + i < nw ? bits_b[w0 + i] : 0u;
+        mem[i] = wd;
+    }
+    __syncthreads();
+    // thread t handles words t, t + blockDim.x, ...: the first listed
+    // position of word i is rank[w0 + i]
+    for (int i = threadIdx.x; i < kRootChunk / 32; i += blockDim.x) {
+        uint32_t wd = mem[i];
+        if (!wd)
+            continue;
+        int j = (int)rank_b[w0 + i];
+        while (wd) {
+            const int bit = __ffs(wd) - 1;
+            wd &= wd - 1u;
+            if (j < len) {
+                const int o = 32 * i + bit;
+                q1d[o] = q1[j];
+                if (q2)
+                    q2d[o] = q2[j];
+            }
+            ++j;
+        }
+    }
+    __syncthreads();
+}
+
+// the chunk totals of sequence b into LDS (all threads load in parallel)
+__device__ __forceinline__ void root_parts_lds(const RootPart *__restrict__ pp, int nch, RootPart *lds)
+{
+    for (int c = threadIdx.x; c < nch; c += blockDim.x)
+        lds[c] = pp[c];
+    __syncthreads();
+}
+
+// P_1 (and the fresh flag: the residual had no mass, back to p_0), the
+// same sums in every kernel that needs them: chunk order, one thread's
+// sequence of adds
+__device__ __forceinline__ void root_p1(const RootPart *__restrict__ part, int nch, double *Poff,
+                                        double *P1, bool *fresh1)
+{
+    double off = 0.0, s1 = 0.0;
+    for (int c = 0; c < nch; ++c) {
+        off += part[c].off;
+        s1 += part[c].s1;
+    }
+    const double pn = off + s1;
+    *Poff = off;
+    *fresh1 = !(pn > 0.0);
+    *P1 = *fresh1 ? 1.0 : pn;
+}
+
+// the on-shortlist weight after the root's chain: R_1 (one child) or R_2
+__device__ __forceinline__ double root_R(double pv, float q1v, float q2v, int k, bool fresh1,
+                                         double P1)
+{
+    const double r1 = fresh1 ? pv : resid(pv, 1.0, q1v);
+    return k == 1 ? r1 : resid(r1, P1, q2v);
+}
+
+// PASS 1: off, sp, s1 per chunk; PASS 2: s2 per chunk (two children only)
+constexpr int kRootMaxChunks = 256;  // V <= 2^20
+
+template <int PASS>
+__global__ __launch_bounds__(kRootThreads) void root_pass_kernel(
+    int m, int V, int64_t max_len, const int32_t *__restrict__ parent,
+    const int64_t *__restrict__ sl_off, const float *__restrict__ q,
+    const float *__restrict__ p, const uint32_t *__restrict__ bits,
+    const uint32_t *__restrict__ rank, RootPart *__restrict__ part)
+{
+    __shared__ uint32_t mem[kRootChunk / 32];
+    __shared__ float q1d[kRootChunk], q2d[PASS == 2 ? kRootChunk : 1];
+    __shared__ RootPart s_part[PASS == 2 ? kRootMaxChunks : 1];
+    __shared__ int s3[3];
+    __shared__ double sh[kWave + 1];
+    const int b = blockIdx.y, nch = (int)gridDim.x;
+    const int64_t base = (int64_t)blockIdx.x * kRootChunk;
+    const int64_t off = sl_off[b], len64 = sl_off[b + 1] - off;
+    if (len64 < 0 || len64 > max_len)
+        return;  // the walk reports such a sequence
+    const int len = (int)len64;
+    int c1, c2, k;
+    root_kids(parent + (int64_t)b * m, m, s3, &c1, &c2, &k);
+    if (k < 1 || k > kRootMaxKids || (PASS == 2 && k != 2))
+        return;  // block-uniform; the walk takes the sequential path
+    RootPart *pb = part + (int64_t)b * nch;
+    double Poff = 0.0, P1 = 1.0;
+    bool fresh1 = true;
+    if (PASS == 2) {
+        root_parts_lds(pb, nch, s_part);
+        root_p1(s_part, nch, &Poff, &P1, &fresh1);
+    }
+    const float *qrow = q + (int64_t)m * off;
+    const int64_t nw = tree_words(V);
+    root_scatter(bits + (int64_t)b * nw, rank + (int64_t)b * nw, V, len, base,
+                 qrow + (int64_t)(c1 - 1) * len,
+                 PASS == 2 ? qrow + (int64_t)(c2 - 1) * len : nullptr, mem, q1d, q2d);
+    const float *pu = p + (int64_t)b * (m + 1) * V;
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0;
+#pragma unroll
+    for (int kk = 0; kk < kRootChunk / (4 * kRootThreads); ++kk) {
+        const int o0 = 4 * threadIdx.x + 4 * kRootThreads * kk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int o = o0 + e;
+            const int64_t y = base + o;
+            const double pv = y < V ? (double)pu[y] : 0.0;
+            const bool in = y < V && ((mem[o >> 5] >> (o & 31)) & 1u);
+            if (PASS == 1) {
+                a0 += in ? 0.0 : pv;
+                a1 += in ? pv : 0.0;
+                a2 += in ? resid(pv, 1.0, q1d[o]) : 0.0;
+            } else {
+                a2 += in ? root_R(pv, q1d[o], q2d[o], 2, fresh1, P1) : 0.0;
+            }
+        }
+    }
+    if (PASS == 1) {
+        a0 = block_sum_f64(a0, sh);
+        a1 = block_sum_f64(a1, sh);
+    }
+    a2 = block_sum_f64(a2, sh);
+    if (threadIdx.x == 0) {
+        if (PASS == 1) {
+            pb[blockIdx.x].off = a0;
+            pb[blockIdx.x].sp = a1;
+            pb[blockIdx.x].s1 = a2;
+        } else {
+            pb[blockIdx.x].s2 = a2;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
     int m, int V, int64_t max_len, bool vec, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ token, const int64_t *__restrict__ sl_off,
     const int32_t *__restrict__ sl_ids, const float *__restrict__ q, const float *__restrict__ p,
     const float *__restrict__ u_acc, const float *__restrict__ u_fin,
     const uint32_t *__restrict__ bits, const uint32_t *__restrict__ rank,
-    double *__restrict__ Rws, int32_t *__restrict__ n_acc, int32_t *__restrict__ out,
-    int32_t *__restrict__ path)
+    const RootPart *__restrict__ rpart, double *__restrict__ Rws, int32_t *__restrict__ n_acc,
+    int32_t *__restrict__ out, int32_t *__restrict__ path)
 {
     __shared__ int s_par[kTreeMaxNodes], s_pos[kTreeMaxNodes], s_tok[kTreeMaxNodes];
     __shared__ double s_lhs[kTreeMaxNodes], s_px[kTreeMaxNodes];
     __shared__ double s_woff[kTreeWaves], s_wt[kTreeWaves], s_w2[kTreeWaves];
     __shared__ double sh[kWave + 1];
     __shared__ int s_int[4];
+    __shared__ uint32_t s_mem[kRootChunk / 32];
+    __shared__ float s_q1[kRootChunk], s_q2[kRootChunk];
+    __shared__ RootPart s_part[kRootMaxChunks];
 
     const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int64_t nw = tree_words(V);
@@ -354,6 +566,119 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
     __syncthreads();
 
     int u = 0, n = 0;
+    // the root's chain from its precomputed chunk totals (one or two
+    // children); an accepted child continues the walk below
+    int c1, c2, kr;
+    root_kids(parent + (int64_t)b * m, m, s_int, &c1, &c2, &kr);
+    if (kr >= 1 && kr <= kRootMaxKids) {  // block-uniform
+        const int nch = (int)root_chunks(V);
+        root_parts_lds(rpart + (int64_t)b * nch, nch, s_part);
+        const RootPart *pp = s_part;
+        const float *qrow = q + (int64_t)m * off;
+        int acc = -1;
+        bool ffin = true;  // the final draw is from p_0 itself
+        double Poff = 0.0, P1 = 1.0;
+        bool fresh1 = true;
+        if (s_lhs[c1 - 1] < s_px[c1 - 1]) {
+            acc = c1;
+        } else {
+            root_p1(pp, nch, &Poff, &P1, &fresh1);
+            ffin = fresh1;
+            if (kr == 2) {
+                const int pos = s_pos[c2 - 1];
+                double rx = s_px[c2 - 1];
+                if (!fresh1)
+                    rx = (pos >= 0 ? resid(s_px[c2 - 1], 1.0, qrow[(int64_t)(c1 - 1) * len + pos])
+                                   : s_px[c2 - 1]) / P1;
+                if (s_lhs[c2 - 1] < rx) {
+                    acc = c2;
+                } else {
+                    double s2 = 0.0;
+                    for (int c = 0; c < nch; ++c)
+                        s2 += pp[c].s2;
+                    ffin = !(Poff + s2 > 0.0);
+                }
+            }
+        }
+        if (acc >= 0) {
+            if (tid == 0) {
+                ob[0] = s_tok[acc - 1];
+                pb[0] = acc;
+            }
+            n = 1;
+            u = acc;
+        } else {
+            // chunk totals of the final weights, the chunk holding u_fin *
+            // total (else the last chunk with mass), then that chunk's tokens
+            double pre = 0.0, tot = 0.0;
+            for (int c = 0; c < nch; ++c)
+                tot += pp[c].off + (ffin ? pp[c].sp : (kr == 1 ? pp[c].s1 : pp[c].s2));
+            const double thr = (double)u_fin[b] * tot;
+            int owner = -1, lastc = -1;
+            double run = 0.0;
+            for (int c = 0; c < nch; ++c) {
+                const double t = pp[c].off + (ffin ? pp[c].sp : (kr == 1 ? pp[c].s1 : pp[c].s2));
+                if (owner < 0 && run + t > thr) {
+                    owner = c;
+                    pre = run;
+                }
+                if (t > 0.0)
+                    lastc = c;
+                run += t;
+            }
+            const bool fb = owner < 0;
+            if (fb)
+                owner = lastc;
+            int32_t pick = -1;
+            if (owner >= 0) {
+                const int64_t cb = (int64_t)owner * kRootChunk;
+                root_scatter(bits_b, rank_b, V, len, cb, qrow + (int64_t)(c1 - 1) * len,
+                             kr == 2 ? qrow + (int64_t)(c2 - 1) * len : nullptr, s_mem, s_q1,
+                             s_q2);
+                const float *pu = p + (int64_t)b * (m + 1) * V;
+                constexpr int TPT = kRootChunk / kTreeThreads;  // 8 consecutive tokens
+                double w[TPT], mine = 0.0;
+#pragma unroll
+                for (int e = 0; e < TPT; ++e) {
+                    const int o = TPT * tid + e;
+                    const int64_t y = cb + o;
+                    const double pv = y < V ? (double)pu[y] : 0.0;
+                    const bool in = y < V && ((s_mem[o >> 5] >> (o & 31)) & 1u);
+                    w[e] = (!ffin && in) ? root_R(pv, s_q1[o], kr == 2 ? s_q2[o] : 0.f, kr, fresh1, P1)
+                                         : pv;
+                    mine += w[e];
+                }
+                double tot2;
+                double part = pre + block_excl_scan_f64(mine, sh, &tot2);
+                if (tid == 0) {
+                    s_int[0] = INT_MAX;
+                    s_int[1] = -1;
+                }
+                __syncthreads();
+                int found = INT_MAX, last = -1;
+#pragma unroll
+                for (int e = 0; e < TPT; ++e) {
+                    part += w[e];
+                    if (w[e] > 0.0) {
+                        last = (int)(cb + TPT * tid + e);
+                        if (found == INT_MAX && !fb && part > thr)
+                            found = last;
+                    }
+                }
+                if (found != INT_MAX)
+                    atomicMin(&s_int[0], found);
+                if (last >= 0)
+                    atomicMax(&s_int[1], last);
+                __syncthreads();
+                pick = s_int[0] != INT_MAX ? s_int[0] : s_int[1];
+            }
+            if (tid == 0) {
+                ob[0] = pick;
+                n_acc[b] = 0;
+            }
+            return;
+        }
+    }
     for (int visit = 0; visit <= m; ++visit) {  // u increases on every acceptance
         const float *pu = p + ((int64_t)b * (m + 1) + u) * V;
         bool fresh = true, have_off = false;
@@ -554,7 +879,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
 size_t verify_tree_ws_bytes(int B, int m, int V, int64_t max_len)
 {
     (void)m;
-    return tree_R_bytes(B, max_len) + 2 * tree_bits_bytes(B, V) + 256;
+    return tree_R_bytes(B, max_len) + 2 * tree_bits_bytes(B, V) + root_part_bytes(B, V) + 256;
 }
 
 hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
@@ -568,6 +893,8 @@ hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t 
     uint32_t *bits = reinterpret_cast<uint32_t *>(base + tree_R_bytes(B, max_len));
     uint32_t *rank = reinterpret_cast<uint32_t *>(base + tree_R_bytes(B, max_len) +
                                                   tree_bits_bytes(B, V));
+    RootPart *rpart = reinterpret_cast<RootPart *>(base + tree_R_bytes(B, max_len) +
+                                                   2 * tree_bits_bytes(B, V));
     const int bx = (V + kBitsTokens - 1) / kBitsTokens;
     const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
     hipError_t e = launch_timed(tree_bits_kernel, dim3((unsigned)bx, (unsigned)B),
@@ -575,9 +902,19 @@ hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t 
                                 bits, rank);
     if (e != hipSuccess)
         return e;
+    const dim3 rgrid((unsigned)root_chunks(V), (unsigned)B);
+    hipLaunchKernelGGL(root_pass_kernel<1>, rgrid, dim3(kRootThreads), 0, s, m, V, max_len, parent,
+                       sl_off, q, p, (const uint32_t *)bits, (const uint32_t *)rank, rpart);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(root_pass_kernel<2>, rgrid, dim3(kRootThreads), 0, s, m, V, max_len, parent,
+                       sl_off, q, p, (const uint32_t *)bits, (const uint32_t *)rank, rpart);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
     return launch_timed(verify_tree_kernel, dim3((unsigned)B), dim3(kTreeThreads), s, nullptr, t1,
                         m, V, max_len, vec, parent, token, sl_off, sl_ids, q, p, u_acc, u_fin,
-                        (const uint32_t *)bits, (const uint32_t *)rank, R, n_acc, out, path);
+                        (const uint32_t *)bits, (const uint32_t *)rank, (const RootPart *)rpart, R,
+                        n_acc, out, path);
 }
 
 }  // namespace ds

@@ -164,21 +164,43 @@ def test_verify_tree_invalid_and_off_shortlist_tokens(N, oracle_lib):
     _check(oracle_lib, c, _run(N, c), min_clean=B)
 
 
-def test_verify_tree_zero_mass_residual_falls_back_to_target(N, oracle_lib):
+@pytest.mark.parametrize("m", [1, 2, 3])
+def test_verify_tree_zero_mass_residual_falls_back_to_target(N, oracle_lib, m):
     """Proposal >= target everywhere (the target is the proposal with the
     drafted token's mass removed): the residual after the rejection has no
-    mass and the next tests and the draw use p_u itself."""
-    V, m, B = 700, 3, 2
+    mass and the next tests and the draw use p_u itself.  The root has one,
+    two (its chain precomputed over chunks) or three children (walked in
+    order on one compute unit)."""
+    V, B = 700, 2
     c = _tree_case(V, m, B, seed=3, lens=[V, V], topo="star")
     for b in range(B):
         q0 = c["q"][m * V * b: m * V * b + V]
-        c["q"][m * V * b + V: m * V * b + 3 * V] = np.tile(q0, 2)  # all three share q_1
+        for k in range(1, m):  # every child shares q_1
+            c["q"][m * V * b + k * V: m * V * b + (k + 1) * V] = q0
         c["token"][b, :] = c["token"][b, 0]
         for u in range(m + 1):
             c["p"][b, u] = q0
         c["p"][b, 0, c["token"][b, 0]] = 0.0
     n_ref = _check(oracle_lib, c, _run(N, c), min_clean=B)
     assert (n_ref == 0).all()
+
+
+@pytest.mark.parametrize("V", [3001, 151936])
+def test_verify_tree_root_second_child(N, oracle_lib, V):
+    """Binary trees whose root's first child is rejected (its uniform just
+    below 1) and whose second child is accepted wherever the residual left
+    by the first has mass at its token (uniform 0): the walk continues
+    below the root from the precomputed chain.  Then both rejected: the
+    draw from the root's residual."""
+    m, B = 15, 4
+    c = _tree_case(V, m, B, seed=31, lens=[min(V, 900), min(V, 2900), 17, min(V, 4500)],
+                   topo="binary", mode="correlated")
+    c["u_acc"][:, 0] = np.float32(1.0 - 2.0 ** -24)
+    c["u_acc"][:, 1] = np.float32(0.0)
+    n_ref = _check(oracle_lib, c, _run(N, c), min_clean=B - 1)
+    assert n_ref.max() >= 1
+    c["u_acc"][:, 1] = np.float32(1.0 - 2.0 ** -24)
+    _check(oracle_lib, c, _run(N, c), min_clean=B - 1)
 
 
 def test_verify_tree_long_shortlist_is_reported(N, oracle_lib):
