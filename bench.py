@@ -5,9 +5,10 @@ A step is the whole hot path over one batch: for each of T draft positions
 the router scores the clusters, the position's budget selects clusters, the
 shortlist is built, the gathered LM head projects the hidden state onto it
 and a draft token is sampled (router work of position t+1 on a second stream,
-overlapped with the head of position t); then the target distribution is the
-softmax of the target logits and the drafts are verified by rejection
-sampling.  Default workload: Llama-3-8B-shaped head, V=128256, d=4096, bf16,
+overlapped with the head of position t); then the drafts are verified by
+rejection sampling against the softmax of the target logits (the softmax's
+segment statistics, then the verification computing each target probability
+it reads).  Default workload: Llama-3-8B-shaped head, V=128256, d=4096, bf16,
 1024 Zipf-sized clusters, batch 1, depth 6, token budget 32768 -> 16384.
 
 Inputs are seeded and synthetic.  Steps rotate over several input instances
@@ -733,9 +734,9 @@ def run_draft(index, *, n_steps, warmup, instances, replicas, eager, static=None
                                                        cfg.tree_nodes + 1))
                       if cfg.is_tree else
                       ("router+select+build+gathered head+sample per position, "
-                       "target softmax + verify") if static_ids is None else
+                       "verify from target logits") if static_ids is None else
                       ("static baseline: %s head over one fixed %d-token frequency-ranked "
-                       "shortlist + sample per position, target softmax + verify"
+                       "shortlist + sample per position, verify from target logits"
                        % (static, static_ids.shape[0])),
               "launch": mode}
     return {"cfg": cfg, "static_ids": static_ids, "value": round(value, 1), "warmup": warmup,

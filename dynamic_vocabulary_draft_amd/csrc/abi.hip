@@ -407,6 +407,28 @@ ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *dr
                                         n_acc, out, ws));
 }
 
+size_t ds_verify_logits_workspace_bytes(int B, int T, int V)
+{
+    return B > 0 && T > 0 && V > 0 ? ds::verify_logits_ws_bytes(B, T, V) : 0;
+}
+
+ds_status ds_verify_reject_logits(hipStream_t s, int B, int T, int V, const int32_t *draft,
+                                  const int64_t *sl_off, const int32_t *sl_ids, const float *q,
+                                  const float *logits, const float *u_acc, const float *u_fin,
+                                  int32_t *n_acc, int32_t *out, void *ws, size_t ws_bytes)
+{
+    ds_status st =
+        check_verify(B, T, V, draft, sl_off, sl_ids, q, logits, u_acc, u_fin, n_acc, out);
+    if (st != DS_OK)
+        return st;
+    if ((int64_t)B * (T + 1) > 65535)  // one statistics row per target position
+        return DS_ESHAPE;
+    if (!ws || ws_bytes < ds_verify_logits_workspace_bytes(B, T, V))
+        return DS_EINVAL;
+    return hip_status(ds::verify_logits_launch(s, B, T, V, draft, sl_off, sl_ids, q, logits,
+                                               u_acc, u_fin, n_acc, out, ws));
+}
+
 ds_status ds_verify_reject_noalloc(hipStream_t s, int B, int T, int V, const int32_t *draft,
                                    const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                                    const float *p, const float *u_acc, const float *u_fin,

@@ -32,6 +32,67 @@ namespace ds {
 constexpr int kChunk = 1024;
 constexpr int kChunkThreads = 256;
 
+// exp(x) in fp64 by Tang's table-driven method (ACM TOMS 15(2), 1989):
+// x = (64n + j) ln2/64 + r with |r| <= ln2/128 (ln2/64 split in two parts,
+// so r is exact to ~1e-19), exp(x) = 2^n * 2^(j/64) * e^r, and e^r - 1 from
+// its Taylor series through r^5 (the next term is below 4e-17).  About 16
+// instructions against some 75 for the library routine; relative error at
+// most 2 fp64 ulp for x > -708 (below that the result is subnormal and its
+// absolute error under one subnormal ulp).  x below -1000 gives 0, NaN stays
+// NaN.  tab[j] = 2^(j/64), filled by fill_exp2_table.
+__device__ __forceinline__ double exp_tab(double x, const double *tab)
+{
+    constexpr double kInvL = 0x1.71547652b82fep+6;   // 64 / ln 2
+    constexpr double kL1 = 0x1.62e42fefa39efp-7;     // ln 2 / 64, leading part
+    constexpr double kL2 = 0x1.abc9e3b39803fp-62;    // ln 2 / 64 - kL1
+    x = x < -1000.0 ? -1000.0 : (x > 1000.0 ? 1000.0 : x);
+    const double kf = rint(x * kInvL);
+    double r = fma(-kf, kL1, x);
+    r = fma(-kf, kL2, r);
+    const int k = (int)kf;
+    const double t = tab[k & 63];
+    double q = fma(r, 1.0 / 120, 1.0 / 24);
+    q = fma(q, r, 1.0 / 6);
+    q = fma(q, r, 0.5);
+    const double pm1 = fma(q, r * r, r);  // e^r - 1
+    return ldexp(fma(t, pm1, t), k >> 6);
+}
+
+// tab[j] = 2^(j/64) in LDS, by the first wave; visible after the caller's
+// next barrier
+__device__ __forceinline__ void fill_exp2_table(double *tab)
+{
+    if (threadIdx.x < 64)
+        tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+}
+
+// The target softmax's row normaliser, rebuilt from its per-segment
+// statistics (segment maxima smax and sums of exp(l - smax), nseg of each):
+// M = the row max, rZ = 1 / sum_s ssum_s exp(smax_s - M), by one whole wave
+// in a fixed association (every lane gets the values).  Any kernel that
+// rebuilds it from the same statistics gets the same bits, so p_elem below
+// reproduces the softmax's output exactly.
+__device__ __forceinline__ void row_norm(const float *__restrict__ sm, const double *__restrict__ ss,
+                                         int64_t nseg, const double *tab, float *M, double *rZ)
+{
+    float m = -INFINITY;
+    for (int64_t c = lane_id(); c < nseg; c += kWave)
+        m = fmaxf(m, sm[c]);
+    m = wave_max(m);
+    double z = 0.0;
+    for (int64_t c = lane_id(); c < nseg; c += kWave)
+        z += ss[c] * exp_tab((double)sm[c] - (double)m, tab);
+    z = wave_sum_f64(z);
+    *M = m;
+    *rZ = 1.0 / z;  // p = w * (1/Z): within one fp32 ulp of w / Z
+}
+
+// p for logit l of a row with normaliser (M, rZ)
+__device__ __forceinline__ float p_elem(float l, float M, double rZ, const double *tab)
+{
+    return (float)(exp_tab((double)l - (double)M, tab) * rZ);
+}
+
 // chunk statistics kept in a caller workspace: [rows][nchmax] of each
 struct ChunkWs {
     float *cmax;

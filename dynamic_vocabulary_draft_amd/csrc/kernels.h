@@ -95,12 +95,24 @@ hipError_t sample_launch(hipStream_t s, int G, int m, const int64_t *sl_off,
 
 size_t softmax_ws_bytes(int64_t rows, int64_t V);
 hipError_t softmax_launch(hipStream_t s, int rows, int V, const float *logits, float *p, void *ws);
+// the softmax's first pass alone: per 4096-element segment of every row its
+// max (fp32) and sum of exp(l - max) (fp64), laid out in ws as
+// [rows][nseg] sums then [rows][nseg] maxima (softmax_ws_bytes)
+int64_t softmax_segments(int64_t V);
+hipError_t softmax_stats_launch(hipStream_t s, int rows, int V, const float *logits, void *ws);
 
 size_t verify_ws_bytes(int B, int T, int V);
 hipError_t verify_launch(hipStream_t s, int B, int T, int V, const int32_t *draft,
                          const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                          const float *p, const float *u_acc, const float *u_fin, int32_t *n_acc,
                          int32_t *out, void *ws);
+// the same verification from target logits: the softmax statistics pass,
+// then p computed where it is read (bit-identical to softmax_launch's p)
+size_t verify_logits_ws_bytes(int B, int T, int V);
+hipError_t verify_logits_launch(hipStream_t s, int B, int T, int V, const int32_t *draft,
+                                const int64_t *sl_off, const int32_t *sl_ids, const float *q,
+                                const float *logits, const float *u_acc, const float *u_fin,
+                                int32_t *n_acc, int32_t *out, void *ws);
 
 hipError_t dense_head_launch(hipStream_t s, int V, int d, const void *W, int n, const void *h,
                              float *logits, int64_t ldl, hipEvent_t t0 = nullptr,

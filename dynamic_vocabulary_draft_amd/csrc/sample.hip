@@ -65,40 +65,6 @@ __device__ __forceinline__ void load4(const float *__restrict__ l, int64_t j0, i
 // fp64 division, which leaves the value unchanged
 __device__ __forceinline__ double over_tau(double x, double tau) { return tau == 1.0 ? x : x / tau; }
 
-// exp(x) in fp64 by Tang's table-driven method (ACM TOMS 15(2), 1989):
-// x = (64n + j) ln2/64 + r with |r| <= ln2/128 (ln2/64 split in two parts,
-// so r is exact to ~1e-19), exp(x) = 2^n * 2^(j/64) * e^r, and e^r - 1 from
-// its Taylor series through r^5 (the next term is below 4e-17).  About 16
-// instructions against some 75 for the library routine; relative error at
-// most 2 fp64 ulp for x > -708 (below that the result is subnormal and its
-// absolute error under one subnormal ulp).  x below -1000 gives 0, NaN stays
-// NaN.  tab[j] = 2^(j/64), filled by fill_exp2_table.
-__device__ __forceinline__ double exp_tab(double x, const double *tab)
-{
-    constexpr double kInvL = 0x1.71547652b82fep+6;   // 64 / ln 2
-    constexpr double kL1 = 0x1.62e42fefa39efp-7;     // ln 2 / 64, leading part
-    constexpr double kL2 = 0x1.abc9e3b39803fp-62;    // ln 2 / 64 - kL1
-    x = x < -1000.0 ? -1000.0 : (x > 1000.0 ? 1000.0 : x);
-    const double kf = rint(x * kInvL);
-    double r = fma(-kf, kL1, x);
-    r = fma(-kf, kL2, r);
-    const int k = (int)kf;
-    const double t = tab[k & 63];
-    double q = fma(r, 1.0 / 120, 1.0 / 24);
-    q = fma(q, r, 1.0 / 6);
-    q = fma(q, r, 0.5);
-    const double pm1 = fma(q, r * r, r);  // e^r - 1
-    return ldexp(fma(t, pm1, t), k >> 6);
-}
-
-// tab[j] = 2^(j/64) in LDS, by the first wave; visible after the caller's
-// next barrier
-__device__ __forceinline__ void fill_exp2_table(double *tab)
-{
-    if (threadIdx.x < 64)
-        tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
-}
-
 // row max from the chunk maxima (order-independent), into every thread
 __device__ float row_max(const float *__restrict__ cmax, int nch, float *sh)
 {
@@ -321,7 +287,6 @@ hipError_t launch_norm(hipStream_t s, L layout, int64_t rows, int64_t max_len, c
 // Segment of kSeg elements per 256-thread workgroup; lane l of wave w holds
 // elements 1024 i + 256 w + 4 l + k (i, k < 4) of it (16-byte accesses).
 constexpr int kSeg = 4 * kChunk;
-constexpr int kSegPer = kSeg / kChunkThreads;  // elements per thread
 
 __device__ __forceinline__ void load_seg(const float *__restrict__ lr, int64_t j0, int64_t V,
                                          float v[4][4])
@@ -390,18 +355,10 @@ __global__ __launch_bounds__(kChunkThreads) void softmax_final_kernel(
     float v[4][4];
     load_seg(in + row * V, j0, V, v);
     fill_exp2_table(s_exp2);
-    const float *sm = smax + row * nseg;
-    const double *ss = ssum + row * nseg;
-    float M = -INFINITY;
-    for (int64_t c = lane_id(); c < nseg; c += kWave)
-        M = fmaxf(M, sm[c]);
-    M = wave_max(M);
     __syncthreads();  // the table
-    double z = 0.0;
-    for (int64_t c = lane_id(); c < nseg; c += kWave)
-        z += ss[c] * exp_tab((double)sm[c] - (double)M, s_exp2);
-    z = wave_sum_f64(z);
-    const double rZ = 1.0 / z;  // p = w * (1/Z): within one fp32 ulp of w / Z
+    float M;
+    double rZ;
+    row_norm(smax + row * nseg, ssum + row * nseg, nseg, s_exp2, &M, &rZ);
     float *pr = p + row * V;
     const bool vec = (reinterpret_cast<uintptr_t>(pr) & 15) == 0;
 #pragma unroll
@@ -410,7 +367,7 @@ __global__ __launch_bounds__(kChunkThreads) void softmax_final_kernel(
         float o[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            o[k] = (float)(exp_tab((double)v[i][k] - (double)M, s_exp2) * rZ);
+            o[k] = p_elem(v[i][k], M, rZ, s_exp2);
         if (vec && j + 3 < V) {
             *reinterpret_cast<float4 *>(pr + j) = make_float4(o[0], o[1], o[2], o[3]);
         } else {
@@ -446,7 +403,9 @@ size_t softmax_ws_bytes(int64_t rows, int64_t V)
     return (size_t)rows * (size_t)segments_for(V) * 12 + 256;
 }
 
-hipError_t softmax_launch(hipStream_t s, int rows, int V, const float *logits, float *p, void *ws)
+int64_t softmax_segments(int64_t V) { return segments_for(V); }
+
+hipError_t softmax_stats_launch(hipStream_t s, int rows, int V, const float *logits, void *ws)
 {
     const int64_t nseg = segments_for(V);
     double *ssum = reinterpret_cast<double *>(ws);
@@ -454,9 +413,18 @@ hipError_t softmax_launch(hipStream_t s, int rows, int V, const float *logits, f
     const dim3 grid((unsigned)nseg, (unsigned)rows);
     hipLaunchKernelGGL(softmax_stats_kernel, grid, dim3(kChunkThreads), 0, s, (int64_t)V, logits,
                        ssum, smax);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t softmax_launch(hipStream_t s, int rows, int V, const float *logits, float *p, void *ws)
+{
+    const int64_t nseg = segments_for(V);
+    double *ssum = reinterpret_cast<double *>(ws);
+    float *smax = reinterpret_cast<float *>(ssum + (size_t)rows * nseg);
+    hipError_t e = softmax_stats_launch(s, rows, V, logits, ws);
     if (e != hipSuccess)
         return e;
+    const dim3 grid((unsigned)nseg, (unsigned)rows);
     hipLaunchKernelGGL(softmax_final_kernel, grid, dim3(kChunkThreads), 0, s, (int64_t)V, logits,
                        (const double *)ssum, (const float *)smax, p);
     return hipGetLastError();

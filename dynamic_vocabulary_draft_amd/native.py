@@ -84,6 +84,9 @@ _SIGS = {
     "ds_verify_workspace_bytes": (_sz, [_i, _i, _i]),
     "ds_verify_reject": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               _sz]),
+    "ds_verify_logits_workspace_bytes": (_sz, [_i, _i, _i]),
+    "ds_verify_reject_logits": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _sz]),
     "ds_verify_reject_noalloc": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp]),
     "ds_verify_tree_workspace_bytes": (_sz, [_i, _i, _i, _i64]),
@@ -356,6 +359,20 @@ def verify_reject(draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out, ws, *, 
     V = p.shape[-1]
     _check("ds_verify_reject", lib.ds_verify_reject(
         _s(stream), B, T, V, _p(draft), _p(sl_off), _p(sl_ids), _p(q), _p(p), _p(u_acc),
+        _p(u_fin), _p(n_acc), _p(out), _p(ws), _nbytes(ws)))
+
+
+def verify_logits_workspace_bytes(B: int, T: int, V: int) -> int:
+    return int(lib.ds_verify_logits_workspace_bytes(B, T, V))
+
+
+def verify_reject_logits(draft, sl_off, sl_ids, q, logits, u_acc, u_fin, n_acc, out, ws, *,
+                         stream=None):
+    """ds_verify_reject from target logits [B][T+1][V]."""
+    T, B = draft.shape
+    V = logits.shape[-1]
+    _check("ds_verify_reject_logits", lib.ds_verify_reject_logits(
+        _s(stream), B, T, V, _p(draft), _p(sl_off), _p(sl_ids), _p(q), _p(logits), _p(u_acc),
         _p(u_fin), _p(n_acc), _p(out), _p(ws), _nbytes(ws)))
 
 

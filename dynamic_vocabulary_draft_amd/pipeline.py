@@ -3,7 +3,8 @@
 ``DraftStep`` owns the device buffers for one workload and enqueues:
   chains (batch B, depth T): ds_draft_chain (router/select/build of position
       t+1 on a second stream, overlapped with head + sample of position t),
-      then ds_target_softmax and ds_verify_reject on the head stream;
+      then ds_verify_reject_logits (verification straight from the target's
+      logits) on the head stream;
   trees (B sequences x m nodes sharing one shortlist): router, select and
       build for the B roots, then one gathered head with m rows per group and
       one sample per node, then ds_target_softmax over the m+1 nodes and
@@ -110,7 +111,7 @@ class DraftStep:
                 self.verify_ws = N.workspace(
                     N.verify_tree_workspace_bytes(B, m, V, int(self.max_len[0])), device)
             else:
-                self.verify_ws = N.workspace(N.verify_workspace_bytes(B, T, V), device)
+                self.verify_ws = N.workspace(N.verify_logits_workspace_bytes(B, T, V), device)
         self._events = None
         self._args = None
         if not cfg.is_tree:
@@ -186,14 +187,22 @@ class DraftStep:
         N.draft_chain(self._args, stream, self.router_stream)
 
     def verify(self, stream=None) -> None:
-        N.target_softmax(self.target_logits, self.p, self.softmax_ws, stream=stream)
         if self.cfg.is_tree:
+            N.target_softmax(self.target_logits, self.p, self.softmax_ws, stream=stream)
             N.verify_tree(self.parent, self.token, self.sl_off, self.sl_ids, self.q, self.p,
                           self.u_acc, self.u_fin, int(self.max_len[0]), self.n_acc, self.out,
                           self.path, self.verify_ws, stream=stream)
             return
-        N.verify_reject(self.token, self.sl_off, self.sl_ids, self.q, self.p, self.u_acc,
-                        self.u_fin, self.n_acc, self.out, self.verify_ws, stream=stream)
+        N.verify_reject_logits(self.token, self.sl_off, self.sl_ids, self.q, self.target_logits,
+                               self.u_acc, self.u_fin, self.n_acc, self.out, self.verify_ws,
+                               stream=stream)
+
+    def target_probs(self) -> torch.Tensor:
+        """The target probabilities the verification used (chains verify
+        from logits and write none: computed here, for inspection)."""
+        if not self.cfg.is_tree:
+            N.target_softmax(self.target_logits, self.p, self.softmax_ws)
+        return self.p
 
     def step(self, stream=None) -> None:
         self.draft(stream)
@@ -237,8 +246,8 @@ class DraftStep:
         r["logits"] = self.logits[: n * mm].cpu().numpy()
         r["q"] = self.q[: n * mm].cpu().numpy()
         if self.target_logits is not None:
-            r.update(p=self.p.cpu().numpy(), n_acc=self.n_acc.cpu().numpy(),
-                     out=self.out.cpu().numpy())
+            r.update(n_acc=self.n_acc.cpu().numpy(), out=self.out.cpu().numpy(),
+                     p=self.target_probs().cpu().numpy())
             if self.cfg.is_tree:
                 r["path"] = self.path.cpu().numpy()
         return r
@@ -290,7 +299,7 @@ class StaticStep:
             self.n_acc = torch.empty(B, **i32)
             self.out = torch.empty(B, T + 1, **i32)
             self.softmax_ws = N.workspace(N.softmax_workspace_bytes(B * (T + 1), V), device)
-            self.verify_ws = N.workspace(N.verify_workspace_bytes(B, T, V), device)
+            self.verify_ws = N.workspace(N.verify_logits_workspace_bytes(B, T, V), device)
         self._W_pos = None
         self._head_events = None
 
@@ -324,9 +333,14 @@ class StaticStep:
                                self.sample_ws, max_len=self.L, stream=stream)
 
     def verify(self, stream=None) -> None:
-        N.target_softmax(self.target_logits, self.p, self.softmax_ws, stream=stream)
-        N.verify_reject(self.token, self.sl_off, self.sl_ids, self.q, self.p, self.u_acc,
-                        self.u_fin, self.n_acc, self.out, self.verify_ws, stream=stream)
+        N.verify_reject_logits(self.token, self.sl_off, self.sl_ids, self.q, self.target_logits,
+                               self.u_acc, self.u_fin, self.n_acc, self.out, self.verify_ws,
+                               stream=stream)
+
+    def target_probs(self) -> torch.Tensor:
+        """The target probabilities (computed here, for inspection)."""
+        N.target_softmax(self.target_logits, self.p, self.softmax_ws)
+        return self.p
 
     def step(self, stream=None) -> None:
         self.draft(stream)
@@ -343,6 +357,6 @@ class StaticStep:
         r["logits"] = self.logits.cpu().numpy()
         r["q"] = self.q.cpu().numpy()
         if self.target_logits is not None:
-            r.update(p=self.p.cpu().numpy(), n_acc=self.n_acc.cpu().numpy(),
-                     out=self.out.cpu().numpy())
+            r.update(n_acc=self.n_acc.cpu().numpy(), out=self.out.cpu().numpy(),
+                     p=self.target_probs().cpu().numpy())
         return r

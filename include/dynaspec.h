@@ -308,6 +308,23 @@ ds_status ds_verify_reject(hipStream_t s, int B, int T, int V, const int32_t *dr
                            int32_t *n_acc, int32_t *out, void *ws, size_t ws_bytes);
 
 /*
+ * ds_verify_reject from the target's logits instead of its probabilities
+ * [same passages as ds_verify_reject].  logits [B][T+1][V] fp32; every
+ * p_t(y) the verification reads is the value ds_target_softmax would write
+ * for that row (the same segment statistics, row normaliser and rounding),
+ * so the outputs equal ds_target_softmax followed by ds_verify_reject, bit
+ * for bit, without writing or reading the B*(T+1)*V probabilities.  Limits
+ * as ds_verify_reject, and B*(T+1) <= 65535 (else DS_ESHAPE).
+ * ws >= ds_verify_logits_workspace_bytes(B, T, V) bytes (caller-owned, no
+ * state kept between calls).
+ */
+size_t ds_verify_logits_workspace_bytes(int B, int T, int V);
+ds_status ds_verify_reject_logits(hipStream_t s, int B, int T, int V, const int32_t *draft,
+                                  const int64_t *sl_off, const int32_t *sl_ids, const float *q,
+                                  const float *logits, const float *u_acc, const float *u_fin,
+                                  int32_t *n_acc, int32_t *out, void *ws, size_t ws_bytes);
+
+/*
  * Allocation-free ds_verify_reject, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments, semantics, limits and outputs as

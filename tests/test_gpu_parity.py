@@ -645,13 +645,13 @@ def _verify_case(oracle_lib, V, T, B, mode, seed):
         u_acc[:] = np.float32(1 - 2 ** -24)
     u_fin = syn.make_uniforms(syn.CONFIGS[0], 11, B, instance=seed)
     return dict(draft=draft.reshape(T, B), sl_off=sl_off, sl_ids=sl_ids, q=q, p=p, u_acc=u_acc,
-                u_fin=u_fin)
+                u_fin=u_fin), tl
 
 
 @pytest.mark.parametrize("V,T,B", [(8, 3, 64), (5000, 4, 16), (128256, 6, 4), (262144, 5, 3)])
 @pytest.mark.parametrize("mode", ["random", "accept_all", "reject_all", "correlated"])
 def test_verify_parity(N, oracle_lib, V, T, B, mode):
-    c = _verify_case(oracle_lib, V, T, B, mode, seed=V + T + B)
+    c, _ = _verify_case(oracle_lib, V, T, B, mode, seed=V + T + B)
     n_ref, out_ref, tie = oracle_lib.verify_reject(**c)
     n_acc = torch.empty(B, dtype=torch.int32, device="cuda")
     out = torch.empty(B, T + 1, dtype=torch.int32, device="cuda")
@@ -665,6 +665,39 @@ def test_verify_parity(N, oracle_lib, V, T, B, mode):
         assert (n_ref == T).all()
     if mode == "correlated":
         assert n_ref.mean() > 0.5
+
+
+@pytest.mark.parametrize("V,T,B", [(8, 3, 64), (5000, 4, 16), (128256, 6, 4), (262144, 5, 3),
+                                   (10001, 64, 3), (32000, 3, 200)])
+@pytest.mark.parametrize("mode", ["random", "reject_all", "correlated"])
+def test_verify_logits_parity(N, oracle_lib, V, T, B, mode):
+    """Verification from target logits: the same outputs as the target
+    softmax followed by verification over its probabilities (bit for bit,
+    every entry: the same p values are computed), and the oracle's
+    verification over those probabilities (exact outside the tie zone)."""
+    c, tl = _verify_case(oracle_lib, V, T, B, mode, seed=V + 7 * T + B)
+    dv = {k: to_dev(v) for k, v in c.items()}
+    lg = to_dev(tl)
+    p = torch.empty(B, T + 1, V, device="cuda")
+    N.target_softmax(lg, p, N.workspace(N.softmax_workspace_bytes(B * (T + 1), V)))
+    outs = []
+    for fused in (False, True):
+        n_acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        out = torch.full((B, T + 1), -7, dtype=torch.int32, device="cuda")
+        if fused:
+            N.verify_reject_logits(dv["draft"], dv["sl_off"], dv["sl_ids"], dv["q"], lg,
+                                   dv["u_acc"], dv["u_fin"], n_acc, out,
+                                   N.workspace(N.verify_logits_workspace_bytes(B, T, V)))
+        else:
+            N.verify_reject(dv["draft"], dv["sl_off"], dv["sl_ids"], dv["q"], p, dv["u_acc"],
+                            dv["u_fin"], n_acc, out,
+                            N.workspace(N.verify_workspace_bytes(B, T, V)))
+        outs.append((_cpu(n_acc), _cpu(out)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    c["p"] = _cpu(p)
+    n_ref, out_ref, tie = oracle_lib.verify_reject(**c)
+    assert np.array_equal(outs[1][0], n_ref)
+    assert np.array_equal(outs[1][1][~tie], out_ref[~tie])
 
 
 # ----------------------------------------------------------------------------

@@ -151,6 +151,13 @@ def test_select_build_head_sample_verify_reject_bad_arguments(N):
     assert L.ds_verify_reject_noalloc(*nver(B=1024, V=1 << 20)) == 3  # over the scratch
     assert N.verify_workspace_bytes(1024, 3, 1 << 20) > (8 << 20)
     assert N.verify_workspace_bytes(64, 5, 262144) <= (8 << 20)
+    # verification from logits: the same checks, plus one statistics row per
+    # target position
+    assert L.ds_verify_reject_logits(*ver(T=65)) == 3
+    assert L.ds_verify_reject_logits(*ver(p=None)) == 1
+    assert L.ds_verify_reject_logits(*ver(B=2048, T=32, ws_bytes=1 << 40)) == 3
+    assert L.ds_verify_reject_logits(*ver()) == 1  # workspace too small
+    assert N.verify_logits_workspace_bytes(2, 3, 100) >= N.verify_workspace_bytes(2, 3, 100) + 8 * 12
     assert L.ds_draft_chain(None, None, None) == 1
     a = N.ChainArgs(B=0, T=6)
     assert L.ds_draft_chain(None, None, C.byref(a)) == 1
