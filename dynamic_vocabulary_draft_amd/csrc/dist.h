@@ -38,14 +38,16 @@ constexpr int kChunkThreads = 256;
 // its Taylor series through r^5 (the next term is below 4e-17).  About 16
 // instructions against some 75 for the library routine; relative error at
 // most 2 fp64 ulp for x > -708 (below that the result is subnormal and its
-// absolute error under one subnormal ulp).  x below -1000 gives 0, NaN stays
-// NaN.  tab[j] = 2^(j/64), filled by fill_exp2_table.
+// absolute error under one subnormal ulp).  x below -1000 (-inf included)
+// gives exactly 0, NaN stays NaN.  Every caller passes x <= 0 (a value minus
+// a maximum), so there is no upper clamp: x above ~709 overflows to inf as
+// exp does, up to x ~ 2e7.  tab[j] = 2^(j/64), filled by fill_exp2_table.
 __device__ __forceinline__ double exp_tab(double x, const double *tab)
 {
     constexpr double kInvL = 0x1.71547652b82fep+6;   // 64 / ln 2
     constexpr double kL1 = 0x1.62e42fefa39efp-7;     // ln 2 / 64, leading part
     constexpr double kL2 = 0x1.abc9e3b39803fp-62;    // ln 2 / 64 - kL1
-    x = x < -1000.0 ? -1000.0 : (x > 1000.0 ? 1000.0 : x);
+    x = x < -1000.0 ? -1000.0 : x;
     const double kf = rint(x * kInvL);
     double r = fma(-kf, kL1, x);
     r = fma(-kf, kL2, r);

@@ -80,11 +80,14 @@ __device__ __forceinline__ void store_phase(uint16_t *lds, const u32x4 v[stage_n
 // (lane l: row l%32, pieces 4*(l/32) .. +3); a slice reaching past d zeroes
 // this lane's pieces at k >= d.  One wave's LDS operations execute in order,
 // so the wave's slice buffer needs no barrier.
-template <int NB>
+// With NP > 1 the slice multiplies NP staged B buffers, pstride elements
+// apart, into the same accumulators (one pass of A through the slice buffer).
+// LR: row stride of the staged B rows.
+template <int NB, int NP = 1, int LR = lds_row<NB>()>
 __device__ __forceinline__ void slice_mma(const u32x4 ld[4], uint16_t *aw, const uint16_t *lds,
-                                          int koff, int kabs, int d, f32x16 acc[NB])
+                                          int koff, int kabs, int d, f32x16 acc[NB],
+                                          int pstride = 0)
 {
-    constexpr int LR = lds_row<NB>();
     const int lane = lane_id();
     const int wr = lane >> 3, wp = lane & 7;
 #pragma unroll
@@ -103,14 +106,16 @@ __device__ __forceinline__ void slice_mma(const u32x4 ld[4], uint16_t *aw, const
     }
     const int kb = koff + 32 * hh;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const uint16_t *brow = lds + (nb * 32 + rr) * LR + kb;
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const u32x4 b = *reinterpret_cast<const u32x4 *>(brow + 8 * s);
-            acc[nb] = mfma(a[s], b, acc[nb]);
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint16_t *brow = lds + p * pstride + (nb * 32 + rr) * LR + kb;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const u32x4 b = *reinterpret_cast<const u32x4 *>(brow + 8 * s);
+                acc[nb] = mfma(a[s], b, acc[nb]);
+            }
         }
-    }
 }
 
 // acc[nb] = (this wave's 32 W rows) x (NB*32 staged B rows)^T over all d.
@@ -126,10 +131,15 @@ __device__ __forceinline__ void slice_mma(const u32x4 ld[4], uint16_t *aw, const
 // hidden-dimension sums changes, the same for every call.  The union head
 // rotates by tile; the gathered head's rows are scattered over the table
 // already and start at phase 0.
+// The ring's refill after the last group has no slice left to load: `tail`
+// >= 0 is the slice index it loads instead, one whose byte offset lies past
+// the buffer's range (the loads return zero without touching memory);
+// tail < 0 reloads the slices after the last (the next row's first bytes).
+constexpr int kTailOob = 1 << 24;  // slice offset 2^31 bytes, past any range < 2^31
 template <int NB, int NT, int AUX, class Src>
 __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], int d,
                                              uint16_t *lds, uint16_t *aw, int nrows, Src src,
-                                             f32x16 acc[NB], int rot)
+                                             f32x16 acc[NB], int rot, int tail)
 {
     constexpr int KP = phase_len<NB>(), NS = KP / kKs, GP = NS / 4;  // groups of 4 slices
     const int nsl = (d + kKs - 1) / kKs, nph = (d + KP - 1) / KP;
@@ -157,8 +167,11 @@ __device__ __forceinline__ void rows_times_b(rsrc_t w, const uint32_t voff[4], i
             if (ks >= nsl)
                 break;  // only in the last phase
             // first slice of the next group: the next in this phase, else the
-            // next phase's first (past the end: a slice whose data goes unused)
-            const int kn = (gi < GP - 1 || j + 1 == nph) ? ks + 4 : phn * NS;
+            // next phase's first (after the last group: `tail`, whose data
+            // goes unused)
+            const bool fin = j + 1 == nph && (gi == GP - 1 || ks + 4 >= nsl);
+            const int kn = fin && tail >= 0 ? tail
+                                            : ((gi < GP - 1 || j + 1 == nph) ? ks + 4 : phn * NS);
             if (gi == GP - 1) {
                 load_phase<NB, NT>(hv, phn * KP, d, nrows, src);
                 // keep these loads ahead of the ring reloads below: the switch
@@ -364,8 +377,9 @@ __device__ __forceinline__ void union_tile(int V, int d, const uint16_t *__restr
         voff[i] = (uint32_t)((32 * wave + (lane >> 3) + 8 * i) * d * 2 + 16 * (lane & 7));
     f32x16 acc[NB];
     auto hsrc = [&](int r) { return h + (int64_t)(g0 + r) * ldh_g; };
+    // the range is at most 256 rows x 16 KB: the tail slice reads nothing
     rows_times_b<NB, 64 * WV, kNonTemporal>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc,
-                                            acc, tile * kPhaseRot);
+                                            acc, tile * kPhaseRot, kTailOob);
 
     // epilogue: the (row, group) pairs on the group's shortlist.  A group's
     // entries for the block's WV tiles are one contiguous run of its logits;
@@ -438,7 +452,11 @@ __device__ __forceinline__ void gathered_tile(rsrc_t w, int V, int d, int m, int
         voff[i] = (uint32_t)__shfl(yrow, (lane >> 3) + 8 * i) * (uint32_t)d * 2u +
                   16u * (lane & 7);
     f32x16 acc[NB];
-    rows_times_b<NB, 64 * WV, kCached>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc, 0);
+    // the range is all of W: the tail slice reads nothing when offsets below
+    // 2^31 cover it (voff + 2^31 stays below 2^32)
+    const int tail = (int64_t)V * d * 2 <= (1ll << 31) ? kTailOob : -1;
+    rows_times_b<NB, 64 * WV, kCached>(w, voff, d, lds, lds_a + wave * kASlice, mm, hsrc, acc, 0,
+                                       tail);
     // epilogue: column = head row (node), row = shortlist entry; the entry
     // of accumulator row i was loaded by lanes i and i + 32
 #pragma unroll
@@ -617,6 +635,34 @@ constexpr int kRouterWin = 256;  // k-window (4 slices)
 constexpr int kRouterCols = 64;  // inputs per column pass
 constexpr int kRouterMaxWin = 8192 / kRouterWin;  // d <= 8192
 
+// part[c][row0 + i] = this workgroup's sums for input c and weight row i
+// (i < rows, c < ncols).  Register q of lane l holds weight row 8*(q/4) +
+// 4*(l/32) + q%4 of the wave's 32 and input (l%32) + 32*nb; the tile passes
+// through the wave's share of `buf` (NB*32 x 33 floats) so that each input's
+// 32 rows go out as one 128-byte store.
+template <int NB>
+__device__ __forceinline__ void store_part(const f32x16 acc[NB], float *buf, float *part, int ld,
+                                           int row0, int rows, int ncols)
+{
+    constexpr int LB = 33;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    float *wb = buf + wave * NB * 32 * LB;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            wb[(nb * 32 + (lane & 31)) * LB + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)] =
+                acc[nb][q];
+    // one wave's LDS operations complete in order: no barrier before reading
+    const int i = lane & 31, row = 32 * wave + i;
+#pragma unroll
+    for (int cc = 0; cc < NB * 16; ++cc) {
+        const int c = 2 * cc + (lane >> 5);
+        if (c < ncols && row < rows)
+            part[(int64_t)c * ld + row0 + row] = wb[c * LB + i];
+    }
+}
+
 template <int NB>
 __global__ __launch_bounds__(256) void router_l1_kernel(int n, int d, int r,
                                                         const uint16_t *__restrict__ W1,
@@ -627,6 +673,7 @@ __global__ __launch_bounds__(256) void router_l1_kernel(int n, int d, int r,
     static_assert(phase_len<NB>() >= kRouterWin, "the window is one staged phase");
     __shared__ __attribute__((aligned(16))) uint16_t lds[NB * 32 * lds_row<NB>()];
     __shared__ __attribute__((aligned(16))) uint16_t lds_a[4 * kASlice];
+    static_assert(sizeof(lds) >= 4 * NB * 32 * 33 * sizeof(float), "partial tile buffer");
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int row0 = blockIdx.x * 128, win = blockIdx.y;
     const int k0 = win * kRouterWin, klen = min(kRouterWin, d - k0);
@@ -658,19 +705,9 @@ __global__ __launch_bounds__(256) void router_l1_kernel(int n, int d, int r,
     for (int sl = 0; sl < 4; ++sl)
         if (sl < nsl)
             slice_mma<NB>(ld[sl], lds_a + wave * kASlice, lds, sl * kKs, sl * kKs, klen, acc);
-    // register q of lane l: weight row 8*(q/4) + 4*(l/32) + q%4 of the wave's
-    // 32, input (l%32) + 32*nb
-    float *pw = part + (int64_t)win * kRouterCols * r;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int c = nb * 32 + (lane & 31);
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int i = 32 * wave + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-            if (c < ncols && i < rows)
-                pw[(int64_t)c * r + row0 + i] = acc[nb][q];
-        }
-    }
+    __syncthreads();  // every wave is done with the staged inputs
+    store_part<NB>(acc, reinterpret_cast<float *>(lds), part + (int64_t)win * kRouterCols * r, r,
+                   row0, rows, ncols);
 }
 
 // z[c0 + c][i] = act(sum over windows w in order of part[w][c][i] + b1[i])
@@ -682,9 +719,18 @@ __global__ __launch_bounds__(256) void router_l1_finish(int r, int nwin, int c0,
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= (int64_t)ncols * r)
         return;
+    // windows in order; eight loads in flight at a time
     float s = 0.f;
-    for (int w = 0; w < nwin; ++w)
-        s += part[(int64_t)w * kRouterCols * r + q];
+    for (int w0 = 0; w0 < nwin; w0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = w0 + i < nwin ? part[(int64_t)(w0 + i) * kRouterCols * r + q] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (w0 + i < nwin)
+                s += v[i];
+    }
     if (b1)
         s += __uint_as_float((uint32_t)b1[q % r] << 16);
     if (act == DS_RELU)
@@ -692,6 +738,89 @@ __global__ __launch_bounds__(256) void router_l1_finish(int r, int nwin, int c0,
     else if (act == DS_SILU)
         s = s / (1.f + expf(-s));
     z[(int64_t)c0 * r + q] = s;
+}
+
+// ------------------------------------------------------- router, layer 2
+// scores = W2 z + b2 for the same batches, z fp32.  Each z value splits
+// exactly into three bf16 pieces: hi = bf16(z), mid = bf16(z - hi), lo =
+// z - hi - mid (both differences are exact in fp32 and lo has at most 8
+// significant bits), so W2 z = W2 hi + W2 mid + W2 lo is a bf16 contraction
+// with exact products, accumulated in fp32 as in the first layer.  A
+// workgroup takes 128 rows of W2 and one k-window of NSW slices, stages the
+// three pieces of the window for up to 64 inputs in LDS and multiplies each
+// W2 slice with all three; part[w][c][o] as in the first layer, summed by
+// router_l1_finish (no activation).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite x
+}
+
+__device__ __forceinline__ void split3(float z, uint32_t &hi, uint32_t &mid, uint32_t &lo)
+{
+    hi = bf16_rne_bits(z);
+    const float r1 = z - __uint_as_float(hi << 16);
+    mid = bf16_rne_bits(r1);
+    const float r2 = r1 - __uint_as_float(mid << 16);
+    lo = bf16_rne_bits(r2);  // exact: r2 has at most 8 significant bits
+}
+
+template <int NB, int NSW>
+__global__ __launch_bounds__(256) void router_l2_kernel(int n, int r, int M,
+                                                        const uint16_t *__restrict__ W2,
+                                                        const float *__restrict__ z, int c0,
+                                                        float *__restrict__ part)
+{
+    constexpr int KW = NSW * kKs, LR = KW + 8, PS = NB * 32 * LR;  // piece stride
+    constexpr int LDS_U16 = 3 * PS > 4 * NB * 32 * 33 * 2 ? 3 * PS : 4 * NB * 32 * 33 * 2;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_U16];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_a[4 * kASlice];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int row0 = blockIdx.x * 128, win = blockIdx.y;
+    const int k0 = win * KW, klen = min(KW, r - k0);
+    const int rows = min(128, M - row0), ncols = min(kRouterCols, n - c0);
+    const rsrc_t w = make_rsrc(W2 + (int64_t)row0 * r + k0,
+                               (uint32_t)((rows - 1) * r * 2 + klen * 2));
+    uint32_t voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        voff[i] = (uint32_t)((32 * wave + (lane >> 3) + 8 * i) * r * 2 + 16 * (lane & 7));
+    u32x4 ld[NSW][4];
+#pragma unroll
+    for (int sl = 0; sl < NSW; ++sl)
+        load_a<kNonTemporal>(w, voff, sl * kKs, ld[sl]);
+    // the window's inputs, 4 values per thread and step (r % 8 == 0: whole
+    // float4s); columns past ncols and k past klen stage zeros
+    constexpr int Q = KW / 4;  // float4s per input row
+#pragma unroll
+    for (int it = 0; it < NB * 32 * Q / 256; ++it) {
+        const int p = threadIdx.x + 256 * it;
+        const int c = p / Q, kk = (p % Q) * 4;
+        float4 v = {0.f, 0.f, 0.f, 0.f};
+        if (c < ncols && kk < klen)
+            v = *reinterpret_cast<const float4 *>(z + (int64_t)(c0 + c) * r + k0 + kk);
+        uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
+        split3(v.x, h0, m0, l0);
+        split3(v.y, h1, m1, l1);
+        split3(v.z, h2, m2, l2);
+        split3(v.w, h3, m3, l3);
+        uint16_t *dst = lds + c * LR + kk;
+        *reinterpret_cast<uint2 *>(dst) = uint2{h0 | (h1 << 16), h2 | (h3 << 16)};
+        *reinterpret_cast<uint2 *>(dst + PS) = uint2{m0 | (m1 << 16), m2 | (m3 << 16)};
+        *reinterpret_cast<uint2 *>(dst + 2 * PS) = uint2{l0 | (l1 << 16), l2 | (l3 << 16)};
+    }
+    __syncthreads();
+    f32x16 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = f32x16{};
+#pragma unroll
+    for (int sl = 0; sl < NSW; ++sl)
+        slice_mma<NB, 3, LR>(ld[sl], lds_a + wave * kASlice, lds, sl * kKs, sl * kKs, klen, acc,
+                             PS);
+    __syncthreads();
+    store_part<NB>(acc, reinterpret_cast<float *>(lds), part + (int64_t)win * kRouterCols * M, M,
+                   row0, rows, ncols);
 }
 
 }  // namespace
@@ -859,6 +988,63 @@ hipError_t router_l1_mfma_launch(hipStream_t s, int n, int d, int r, int act, co
         hipLaunchKernelGGL(router_l1_finish, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s,
                            r, nwin, c0, nc, (const float *)part,
                            reinterpret_cast<const uint16_t *>(b1), act, z);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+// layer 2 on the matrix cores: bf16 W2, r % 8 == 0, and the window
+// partials of a column pass fit the first layer's partial buffer
+static int router_l2_slices(int r, int M)
+{
+    if (r % 8)
+        return 0;
+    for (int nsw = 1; nsw <= 2; ++nsw) {
+        const size_t need = (size_t)((r + nsw * kKs - 1) / (nsw * kKs)) * kRouterCols * M *
+                            sizeof(float);
+        if (need <= router_l1_ws_bytes(r))
+            return nsw;
+    }
+    return 0;
+}
+
+bool router_l2_mfma_applies(int r, int M) { return router_l2_slices(r, M) > 0; }
+
+hipError_t router_l2_mfma_launch(hipStream_t s, int n, int r, int M, const void *z_,
+                                 const void *W2, const void *b2, float *scores, float *part)
+{
+    const int nsw = router_l2_slices(r, M);
+    if (nsw == 0)
+        return hipErrorInvalidValue;
+    const int nwin = (r + nsw * kKs - 1) / (nsw * kKs);
+    const dim3 grid((unsigned)((M + 127) / 128), (unsigned)nwin);
+    const uint16_t *Wb = reinterpret_cast<const uint16_t *>(W2);
+    const float *z = reinterpret_cast<const float *>(z_);
+    for (int c0 = 0; c0 < n; c0 += kRouterCols) {
+        const int nc = n - c0 < kRouterCols ? n - c0 : kRouterCols;
+        if (nsw == 1) {
+            if (nc > 32)
+                hipLaunchKernelGGL((router_l2_kernel<2, 1>), grid, dim3(256), 0, s, n, r, M, Wb, z,
+                                   c0, part);
+            else
+                hipLaunchKernelGGL((router_l2_kernel<1, 1>), grid, dim3(256), 0, s, n, r, M, Wb, z,
+                                   c0, part);
+        } else {
+            if (nc > 32)
+                hipLaunchKernelGGL((router_l2_kernel<2, 2>), grid, dim3(256), 0, s, n, r, M, Wb, z,
+                                   c0, part);
+            else
+                hipLaunchKernelGGL((router_l2_kernel<1, 2>), grid, dim3(256), 0, s, n, r, M, Wb, z,
+                                   c0, part);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        const int64_t cnt = (int64_t)nc * M;
+        hipLaunchKernelGGL(router_l1_finish, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s,
+                           M, nwin, c0, nc, (const float *)part,
+                           reinterpret_cast<const uint16_t *>(b2), -1, scores);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }

@@ -19,6 +19,12 @@ hipError_t router_launch(hipStream_t s, bool bf16, int n, int d, int r, int M, i
 size_t router_l1_ws_bytes(int r);
 hipError_t router_l1_mfma_launch(hipStream_t s, int n, int d, int r, int act, const void *h,
                                  int64_t ldh, const void *W1, const void *b1, float *z, float *part);
+// second layer on the matrix cores (bf16 W2, r % 8 == 0, window partials
+// within router_l1_ws_bytes(r)): scores = W2 z + b2, z fp32 split exactly
+// into three bf16 pieces; part as above
+bool router_l2_mfma_applies(int r, int M);
+hipError_t router_l2_mfma_launch(hipStream_t s, int n, int r, int M, const void *z,
+                                 const void *W2, const void *b2, float *scores, float *part);
 
 hipError_t select_launch(hipStream_t s, int n, int M, const float *scores,
                          const int32_t *cluster_size, int kind, const int32_t *budget,

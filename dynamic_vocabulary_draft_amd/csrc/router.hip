@@ -181,13 +181,13 @@ hipError_t router_launch(hipStream_t s, bool bf16, int n, int d, int r, int M, i
                          const void *W2, const void *b2, float *scores, float *z)
 {
     hipError_t e;
+    float *part = reinterpret_cast<float *>(
+        reinterpret_cast<char *>(z) + ((size_t)n * (size_t)r * sizeof(float) + 255) / 256 * 256);
     // layer 1: z = act(W1 h + b1).  A batch of bf16 inputs is a dense
     // contraction: matrix cores, split over k (the GEMV below re-reads each
     // weight row once per 8 inputs); else the GEMV with act encoded as
     // act + 1 (0 = identity)
     if (bf16 && n >= kRouterMfmaMin) {
-        float *part = reinterpret_cast<float *>(
-            reinterpret_cast<char *>(z) + ((size_t)n * (size_t)r * sizeof(float) + 255) / 256 * 256);
         e = router_l1_mfma_launch(s, n, d, r, act, h, ldh, W1, b1, z, part);
     } else {
         e = bf16 ? launch_gemv<true, true>(s, n, d, r, W1, b1, h, ldh, act + 1, z, r)
@@ -195,7 +195,11 @@ hipError_t router_launch(hipStream_t s, bool bf16, int n, int d, int r, int M, i
     }
     if (e != hipSuccess)
         return e;
-    // layer 2: scores = W2 z + b2 (z is fp32)
+    // layer 2: scores = W2 z + b2 (z is fp32).  A batch re-reads every W2
+    // row once per 8 inputs in the GEMV, and reads z once per W2 row: on
+    // the matrix cores (z split exactly into bf16 pieces) instead
+    if (bf16 && n >= kRouterMfmaMin && router_l2_mfma_applies(r, M))
+        return router_l2_mfma_launch(s, n, r, M, z, W2, b2, scores, part);
     return bf16 ? launch_gemv<true, false>(s, n, r, M, W2, b2, z, r, 0, scores, M)
                 : launch_gemv<false, false>(s, n, r, M, W2, b2, z, r, 0, scores, M);
 }

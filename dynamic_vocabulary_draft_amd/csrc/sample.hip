@@ -328,9 +328,11 @@ __global__ __launch_bounds__(kChunkThreads) void softmax_stats_kernel(int64_t V,
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
+            // computed for every element and selected (no branch per
+            // element); adding an exact 0 leaves the sum unchanged
             const float x = v[i][k];
-            if (j0 + i * kChunk + k < V && x != -INFINITY)
-                acc += exp_tab((double)x - (double)mseg, s_exp2);
+            const double e = exp_tab((double)x - (double)mseg, s_exp2);
+            acc += (j0 + i * kChunk + k < V && x != -INFINITY) ? e : 0.0;
         }
     acc = wave_sum_f64(acc);
     if (lane_id() == 0)

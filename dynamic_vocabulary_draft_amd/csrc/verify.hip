@@ -4,18 +4,21 @@
 // exact; summary page, "Pipeline Flow: Rejection Sampling Verification"; the
 // accept / residual / bonus rules are textbook speculative sampling).
 //
-// Two launches, one workgroup per (1024-token chunk of V, sequence):
-//   sum:    the workgroup's four waves run the T accept tests (the draft
-//           token is found in its ascending shortlist with a three-round
-//           wave search; the exact fp64 test u*q < p) and take the first
-//           rejected position t*; for a rejection the chunk's residual
-//           weights max(0, p - q) (q of the shortlist entries inside the
-//           chunk scattered into LDS) and the plain p weights are summed;
-//           after T acceptances the bonus position's p is summed;
-//   final:  every workgroup rebuilds the same prefixes and total (the
-//           residual, or p when the residual has no mass); the owner of the
-//           threshold u_fin * total walks its chunk and writes the drawn
-//           token; chunk 0 writes the accepted tokens, -1 padding and n_acc.
+// Three launches:
+//   prep:   one workgroup per sequence: its waves run the T accept
+//           tests (the draft token is found in its ascending shortlist with
+//           a three-round wave search; the exact fp64 test u*q < p) and take
+//           the first rejected position t*; after a rejection one pass over
+//           the rejected row's shortlist records where each 1024-token chunk
+//           of V starts in it;
+//   sum:    one wave per (chunk, sequence): for a rejection the chunk's
+//           residual weights max(0, p - q) (q of the chunk's shortlist
+//           entries scattered into the wave's LDS array) and the plain p
+//           weights are summed; after T acceptances the bonus position's p;
+//   final:  one workgroup per sequence: the chunk prefixes and total (the
+//           residual, or p when the residual has no mass), the chunk owning
+//           the threshold u_fin * total, the walk of that chunk, the drawn
+//           token, the accepted tokens, -1 padding and n_acc.
 #include <float.h>
 
 #include "common.h"
@@ -31,13 +34,35 @@ constexpr int kMaxRows = 65;       // T + 1 <= 65
 struct VerifyWs {
     ChunkWs ch;
     int32_t *tstar;  // [B]: first rejected position (T if none)
+    int32_t *cbeg;   // [B][nchV+1]: first entry of chunk c in the rejected row's shortlist
+    float *rowM;     // [B] (logits): normaliser of row t* ...
+    double *rowZ;    // [B] ... and its 1 / Z
 };
+
+__host__ __device__ inline size_t verify_ws_layout(int B, int64_t nchV, size_t off[4])
+{
+    size_t o = (chunk_ws_bytes(B, nchV) + 255) / 256 * 256;
+    off[0] = o;                                           // tstar
+    o += ((size_t)B * 4 + 255) / 256 * 256;
+    off[1] = o;                                           // cbeg
+    o += ((size_t)B * (size_t)(nchV + 1) * 4 + 255) / 256 * 256;
+    off[2] = o;                                           // rowM
+    o += ((size_t)B * 4 + 255) / 256 * 256;
+    off[3] = o;                                           // rowZ
+    return o + (size_t)B * 8;
+}
 
 __host__ __device__ inline VerifyWs verify_ws(void *ws, int B, int64_t nchV)
 {
+    size_t off[4];
+    verify_ws_layout(B, nchV, off);
+    char *p = reinterpret_cast<char *>(ws);
     VerifyWs w;
     w.ch = chunk_ws(ws, B, nchV);
-    w.tstar = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ws) + chunk_ws_bytes(B, nchV));
+    w.tstar = reinterpret_cast<int32_t *>(p + off[0]);
+    w.cbeg = reinterpret_cast<int32_t *>(p + off[1]);
+    w.rowM = reinterpret_cast<float *>(p + off[2]);
+    w.rowZ = reinterpret_cast<double *>(p + off[3]);
     return w;
 }
 
@@ -60,17 +85,25 @@ struct Target {
     }
 };
 
+// One target row and (LOGITS) its normaliser
+template <bool LOGITS>
+struct RowP {
+    const float *r;
+    float M;
+    double rZ;
+    const double *tab;
+};
+
 // LOGITS: every row's normaliser of sequence b into LDS (wave w: rows w,
-// w + 4, ...) and the exp table; returns after a barrier
+// w + 4, ...); the exp table must be filled and visible.  Returns after a
+// barrier.
 template <bool LOGITS>
 __device__ __forceinline__ void target_norms(int b, int T, const float *__restrict__ smax,
                                              const double *__restrict__ ssum, int64_t nseg,
-                                             float *sM, double *srZ, double *tab)
+                                             float *sM, double *srZ, const double *tab)
 {
     if (!LOGITS)
         return;
-    fill_exp2_table(tab);
-    __syncthreads();
     const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     for (int t = wave; t <= T; t += nw) {
         const int64_t r = (int64_t)b * (T + 1) + t;
@@ -113,42 +146,93 @@ __device__ int first_rejection(int B, int T, int V, int b, const int32_t *__rest
     return *s_rej;
 }
 
-// The chunk's q values (shortlist entries with token ids in [base, base+1024))
-// scattered into a dense LDS array; returns after a barrier.
-__device__ void scatter_q(const int32_t *__restrict__ S, const float *__restrict__ qrow,
-                          int64_t len, int64_t base, float *qd, int64_t *s_rng)
+// Per-sequence preparation, one workgroup per sequence: the accept tests,
+// t*, the normaliser of row t* (logits) and, after a rejection, where each
+// 1024-token chunk of V starts in the rejected row's ascending shortlist
+// (cbeg[c] = first entry with id >= 1024 c, len if none; found in one pass:
+// entry k starts every chunk c with ids[k-1] < 1024 c <= ids[k]).
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepPer = 16;  // shortlist entries per thread and pass
+
+template <bool LOGITS>
+__global__ __launch_bounds__(kPrepThreads) void verify_prep_kernel(
+    int B, int T, int V, const int32_t *__restrict__ draft, const int64_t *__restrict__ sl_off,
+    const int32_t *__restrict__ sl_ids, const float *__restrict__ q, const float *__restrict__ p,
+    const float *__restrict__ smax, const double *__restrict__ ssum, int64_t nseg,
+    const float *__restrict__ u_acc, int64_t nchV, void *ws)
 {
-    for (int i = threadIdx.x; i < kChunk; i += blockDim.x)
-        qd[i] = 0.0f;
-    if ((threadIdx.x >> 6) == 0) {
-        const int64_t a = wave_lower_bound(S, len, (int32_t)base);
-        const int64_t e = wave_lower_bound(S, len, (int32_t)min(base + kChunk, (int64_t)INT32_MAX));
-        if (lane_id() == 0) {
-            s_rng[0] = a;
-            s_rng[1] = e;
+    __shared__ int s_rej;
+    __shared__ float sM[LOGITS ? kMaxRows : 1];
+    __shared__ double srZ[LOGITS ? kMaxRows : 1], tab[LOGITS ? 64 : 1];
+    const int b = blockIdx.x;
+    VerifyWs w = verify_ws(ws, B, nchV);
+    if (LOGITS) {
+        fill_exp2_table(tab);
+        __syncthreads();
+    }
+    target_norms<LOGITS>(b, T, smax, ssum, nseg, sM, srZ, tab);
+    const Target<LOGITS> tg{p, (int64_t)V, T, sM, srZ, tab};
+    const int tstar =
+        first_rejection<LOGITS>(B, T, V, b, draft, sl_off, sl_ids, q, tg, u_acc, &s_rej);
+    if (threadIdx.x == 0) {
+        w.tstar[b] = tstar;
+        if (LOGITS) {
+            w.rowM[b] = sM[tstar];
+            w.rowZ[b] = srZ[tstar];
         }
     }
-    __syncthreads();
-    for (int64_t k = s_rng[0] + threadIdx.x; k < s_rng[1]; k += blockDim.x) {
-        const int64_t o = (int64_t)S[k] - base;
-        if (o >= 0 && o < kChunk)
-            qd[o] = qrow[k];
+    if (tstar == T)
+        return;
+    const int64_t row = (int64_t)tstar * B + b;
+    const int64_t lo = sl_off[row], len = sl_off[row + 1] - lo;
+    const int32_t *S = sl_ids + lo;
+    int32_t *cb = w.cbeg + (int64_t)b * (nchV + 1);
+    // each thread takes kPrepPer consecutive entries (and the one before),
+    // all loaded before any is used: a pass covers 16K entries
+    for (int64_t k0 = (int64_t)threadIdx.x * kPrepPer; k0 <= len;
+         k0 += (int64_t)blockDim.x * kPrepPer) {
+        int32_t v[kPrepPer + 1];  // v[i] = S[k0 - 1 + i]
+#pragma unroll
+        for (int i = 0; i <= kPrepPer; ++i) {
+            const int64_t k = k0 - 1 + i;
+            v[i] = (k >= 0 && k < len) ? S[k] : 0;
+        }
+#pragma unroll
+        for (int i = 1; i <= kPrepPer; ++i) {
+            const int64_t k = k0 - 1 + i;  // entry k starts chunks c_lo .. c_hi
+            if (k > len)
+                break;
+            const int64_t prev = k > 0 ? (int64_t)v[i - 1] : -1;
+            const int64_t c_lo = prev < 0 ? 0 : prev / kChunk + 1;
+            const int64_t c_hi =
+                k < len ? (v[i] < 0 ? -1 : min((int64_t)v[i] / kChunk, nchV)) : nchV;
+            for (int64_t c = c_lo; c <= c_hi; ++c)
+                cb[c] = (int32_t)k;
+        }
     }
-    __syncthreads();
 }
 
-// weights of this lane's four tokens: family 0 = residual (or bonus p),
-// family 1 = plain p of the rejected position
+// this lane's four raw target values (p, or logits) of tokens y0 .. y0+3
+__device__ __forceinline__ void lane_raw(const float *__restrict__ r, int64_t y0, int V,
+                                         float x[4])
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        x[k] = y0 + k < V ? r[y0 + k] : 0.f;
+}
+
+// weights of this lane's four tokens from their raw values: family 0 =
+// residual (or bonus p), family 1 = plain p of the rejected position
 template <bool LOGITS>
-__device__ __forceinline__ void lane_weights(const Target<LOGITS> &tg, const float *__restrict__ pt,
-                                             int t, int64_t y0, int V, const float *qd,
-                                             int64_t local0, bool resid, double w0[4],
-                                             double w1[4])
+__device__ __forceinline__ void lane_weights(const RowP<LOGITS> &rp, const float x[4], int64_t y0,
+                                             int V, const float *qd, int64_t local0, bool resid,
+                                             double w0[4], double w1[4])
 {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int64_t y = y0 + k;
-        const double pv = y < V ? (double)tg.at(pt, t, y) : 0.0;
+        const double pv =
+            y < V ? (double)(LOGITS ? p_elem(x[k], rp.M, rp.rZ, rp.tab) : x[k]) : 0.0;
         w1[k] = pv;
         if (resid) {
             const double r = y < V ? pv - (double)qd[local0 + k] : 0.0;
@@ -159,72 +243,110 @@ __device__ __forceinline__ void lane_weights(const Target<LOGITS> &tg, const flo
     }
 }
 
-template <bool LOGITS>
-__global__ __launch_bounds__(kChunkThreads) void verify_sum_kernel(
-    int B, int T, int V, const int32_t *__restrict__ draft, const int64_t *__restrict__ sl_off,
-    const int32_t *__restrict__ sl_ids, const float *__restrict__ q, const float *__restrict__ p,
-    const float *__restrict__ smax, const double *__restrict__ ssum, int64_t nseg,
-    const float *__restrict__ u_acc, int64_t nchV, void *ws)
+// The chunk's entries [a, e) of the rejected row's shortlist (ids in
+// [base, base + 1024)) scattered into the dense array qd (zeroed first) by
+// `nt` threads with index i; the caller orders the writes before the reads.
+__device__ __forceinline__ void scatter_q(const int32_t *__restrict__ S,
+                                          const float *__restrict__ qrow, int64_t a, int64_t e,
+                                          int64_t base, float *qd, int i, int nt, bool zero)
 {
-    __shared__ float qd[kChunk];
-    __shared__ int64_t s_rng[2];
-    __shared__ double s_w0[4], s_w1[4];
-    __shared__ int s_rej;
-    __shared__ float sM[LOGITS ? kMaxRows : 1];
-    __shared__ double srZ[LOGITS ? kMaxRows : 1], tab[LOGITS ? 64 : 1];
-    const int b = blockIdx.y;
-    const int64_t c = blockIdx.x;
-    VerifyWs w = verify_ws(ws, B, nchV);
-    target_norms<LOGITS>(b, T, smax, ssum, nseg, sM, srZ, tab);
-    const Target<LOGITS> tg{p, (int64_t)V, T, sM, srZ, tab};
-    const int tstar =
-        first_rejection<LOGITS>(B, T, V, b, draft, sl_off, sl_ids, q, tg, u_acc, &s_rej);
-    if (c == 0 && threadIdx.x == 0)
-        w.tstar[b] = tstar;
-    const float *pt = tg.row(b, tstar);
-    const bool resid = tstar < T;
-    const int64_t base = c * kChunk;
-    if (resid) {
-        const int64_t row = (int64_t)tstar * B + b;
-        const int64_t lo = sl_off[row];
-        scatter_q(sl_ids + lo, q + lo, sl_off[row + 1] - lo, base, qd, s_rng);
-    }
-    const int64_t local0 = (threadIdx.x >> 6) * 256 + lane_id() * 4;
-    double w0[4], w1[4];
-    lane_weights<LOGITS>(tg, pt, tstar, base + local0, V, qd, local0, resid, w0, w1);
-    double i0, i1;
-    double t0 = wave_chunk_sum(w0, &i0), t1 = wave_chunk_sum(w1, &i1);
-    if (lane_id() == 0) {
-        s_w0[threadIdx.x >> 6] = t0;
-        s_w1[threadIdx.x >> 6] = t1;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        w.ch.csum[(int64_t)b * nchV + c] = ((s_w0[0] + s_w0[1]) + s_w0[2]) + s_w0[3];
-        w.ch.csum2[(int64_t)b * nchV + c] = ((s_w1[0] + s_w1[1]) + s_w1[2]) + s_w1[3];
+    if (zero)
+        for (int k = i; k < kChunk; k += nt)
+            qd[k] = 0.0f;
+    for (int64_t k = a + i; k < e; k += nt) {
+        const int64_t o = (int64_t)S[k] - base;
+        if (o >= 0 && o < kChunk)
+            qd[o] = qrow[k];
     }
 }
 
+// the chunk's entry range [a, e), clamped to the row (cbeg comes from the
+// shortlist itself; the clamp keeps a malformed list in bounds)
+__device__ __forceinline__ void chunk_range(const int32_t *cb, int64_t c, int64_t len, int64_t *a,
+                                            int64_t *e)
+{
+    int64_t x = cb[c], y = cb[c + 1];
+    x = x < 0 ? 0 : (x > len ? len : x);
+    y = y < x ? x : (y > len ? len : y);
+    *a = x;
+    *e = y;
+}
+
+// Chunk sums: wave w of workgroup x takes chunk 4x + w of sequence blockIdx.y
+// (its 1024 tokens as four 256-token parts, each summed as in the final
+// walk: four-term lane sums, the wave's inclusive scan, then the parts in
+// order).  The q values of the chunk go through the wave's own LDS array.
+template <bool LOGITS>
+__global__ __launch_bounds__(kChunkThreads) void verify_sum_kernel(
+    int B, int T, int V, const int64_t *__restrict__ sl_off, const int32_t *__restrict__ sl_ids,
+    const float *__restrict__ q, const float *__restrict__ p, int64_t nchV, void *ws)
+{
+    __shared__ float qd_all[4][kChunk];
+    __shared__ double tab[LOGITS ? 64 : 1];
+    const int b = blockIdx.y, wave = threadIdx.x >> 6, lane = lane_id();
+    VerifyWs w = verify_ws(ws, B, nchV);
+    if (LOGITS) {
+        fill_exp2_table(tab);
+        __syncthreads();
+    }
+    const int64_t c = (int64_t)blockIdx.x * 4 + wave;
+    if (c >= nchV)
+        return;  // no barrier follows
+    const int tstar = w.tstar[b];
+    const bool resid = tstar < T;
+    const RowP<LOGITS> rp{p + ((int64_t)b * (T + 1) + tstar) * V, LOGITS ? w.rowM[b] : 0.f,
+                          LOGITS ? w.rowZ[b] : 0.0, tab};
+    const int64_t base = c * kChunk;
+    float *qd = qd_all[wave];
+    float x[4][4];  // loaded before the scatter so that both are in flight
+#pragma unroll
+    for (int part = 0; part < 4; ++part)
+        lane_raw(rp.r, base + part * 256 + lane * 4, V, x[part]);
+    if (resid) {
+        const int64_t row = (int64_t)tstar * B + b;
+        const int64_t lo = sl_off[row], len = sl_off[row + 1] - lo;
+        int64_t a, e;
+        chunk_range(w.cbeg + (int64_t)b * (nchV + 1), c, len, &a, &e);
+        scatter_q(sl_ids + lo, q + lo, a, e, base, qd, lane, kWave, true);
+    }
+    // one wave's LDS operations complete in order: the scatter is visible
+    double t0 = 0.0, t1 = 0.0;
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+        const int64_t local0 = part * 256 + lane * 4;
+        double w0[4], w1[4], i0, i1;
+        lane_weights<LOGITS>(rp, x[part], base + local0, V, qd, local0, resid, w0, w1);
+        const double s0 = wave_chunk_sum(w0, &i0), s1 = wave_chunk_sum(w1, &i1);
+        t0 = part == 0 ? s0 : t0 + s0;
+        t1 = part == 0 ? s1 : t1 + s1;
+    }
+    if (lane == 0) {
+        w.ch.csum[(int64_t)b * nchV + c] = t0;
+        w.ch.csum2[(int64_t)b * nchV + c] = t1;
+    }
+}
+
+// One workgroup per sequence: the prefix over the chunk sums (the residual,
+// or p when the residual has no mass), the chunk owning u_fin * total, the
+// walk of that chunk, and the outputs.
 template <bool LOGITS>
 __global__ __launch_bounds__(kChunkThreads) void verify_final_kernel(
     int B, int T, int V, const int32_t *__restrict__ draft, const int64_t *__restrict__ sl_off,
     const int32_t *__restrict__ sl_ids, const float *__restrict__ q, const float *__restrict__ p,
-    const float *__restrict__ smax, const double *__restrict__ ssum, int64_t nseg,
     const float *__restrict__ u_fin, int64_t nchV, const void *ws, int32_t *__restrict__ n_acc,
     int32_t *__restrict__ out)
 {
     __shared__ double P[kMaxVChunks], S[kMaxVChunks];
     __shared__ float qd[kChunk];
-    __shared__ int64_t s_rng[2];
     __shared__ double s_wt[4];
     __shared__ double s_total;
     __shared__ int s_owner, s_fallback;
     __shared__ int64_t s_pick[2];
-    __shared__ float sM[LOGITS ? kMaxRows : 1];
-    __shared__ double srZ[LOGITS ? kMaxRows : 1], tab[LOGITS ? 64 : 1];
-    const int b = blockIdx.y;
-    const int64_t c = blockIdx.x;
+    __shared__ double tab[LOGITS ? 64 : 1];
+    const int b = blockIdx.x;
     VerifyWs w = verify_ws(const_cast<void *>(ws), B, nchV);
+    if (LOGITS)
+        fill_exp2_table(tab);  // ordered by the barriers below
     const int tstar = w.tstar[b];
     const int nch = (int)nchV;
     const double *cs0 = w.ch.csum + (int64_t)b * nchV;
@@ -240,27 +362,33 @@ __global__ __launch_bounds__(kChunkThreads) void verify_final_kernel(
     const double thr = (double)u_fin[b] * Z;
     owner_chunk(P, S, nch, thr, &s_owner, &s_fallback);
     int32_t *ob = out + (int64_t)b * (T + 1);
-    if (c == 0) {
-        for (int k = threadIdx.x; k <= T; k += blockDim.x)
-            if (k != tstar || s_owner < 0)
-                ob[k] = k < tstar ? draft[(int64_t)k * B + b] : -1;
-        if (threadIdx.x == 0)
-            n_acc[b] = tstar;
-    }
-    if (c != s_owner)
+    const int owner = s_owner;
+    for (int k = threadIdx.x; k <= T; k += blockDim.x)
+        if (k != tstar || owner < 0)
+            ob[k] = k < tstar ? draft[(int64_t)k * B + b] : -1;
+    if (threadIdx.x == 0)
+        n_acc[b] = tstar;
+    if (owner < 0)
         return;
-    target_norms<LOGITS>(b, T, smax, ssum, nseg, sM, srZ, tab);
-    const Target<LOGITS> tg{p, (int64_t)V, T, sM, srZ, tab};
-    const float *pt = tg.row(b, tstar);
-    const int64_t base = c * kChunk;
+    const RowP<LOGITS> rp{p + ((int64_t)b * (T + 1) + tstar) * V, LOGITS ? w.rowM[b] : 0.f,
+                          LOGITS ? w.rowZ[b] : 0.0, tab};
+    const int64_t c = owner, base = c * kChunk;
+    const int64_t local0 = (threadIdx.x >> 6) * 256 + lane_id() * 4;
+    float x[4];
+    lane_raw(rp.r, base + local0, V, x);
     if (resid && !use_p) {
         const int64_t row = (int64_t)tstar * B + b;
-        const int64_t lo = sl_off[row];
-        scatter_q(sl_ids + lo, q + lo, sl_off[row + 1] - lo, base, qd, s_rng);
+        const int64_t lo = sl_off[row], len = sl_off[row + 1] - lo;
+        int64_t a, e;
+        chunk_range(w.cbeg + (int64_t)b * (nchV + 1), c, len, &a, &e);
+        for (int k = threadIdx.x; k < kChunk; k += blockDim.x)
+            qd[k] = 0.0f;
+        __syncthreads();
+        scatter_q(sl_ids + lo, q + lo, a, e, base, qd, threadIdx.x, blockDim.x, false);
+        __syncthreads();
     }
-    const int64_t local0 = (threadIdx.x >> 6) * 256 + lane_id() * 4;
     double w0[4], w1[4];
-    lane_weights<LOGITS>(tg, pt, tstar, base + local0, V, qd, local0, resid && !use_p, w0, w1);
+    lane_weights<LOGITS>(rp, x, base + local0, V, qd, local0, resid && !use_p, w0, w1);
     double incl;
     double tot = wave_chunk_sum(w0, &incl);
     if (lane_id() == 0)
@@ -280,15 +408,18 @@ hipError_t verify_kernels(hipStream_t s, int B, int T, int V, const int32_t *dra
                           void *ws)
 {
     const int64_t nchV = chunks_for(V);
-    dim3 grid((unsigned)nchV, (unsigned)B);
-    hipLaunchKernelGGL(verify_sum_kernel<LOGITS>, grid, dim3(kChunkThreads), 0, s, B, T, V, draft,
-                       sl_off, sl_ids, q, x, smax, ssum, nseg, u_acc, nchV, ws);
+    hipLaunchKernelGGL(verify_prep_kernel<LOGITS>, dim3((unsigned)B), dim3(kPrepThreads), 0, s,
+                       B, T, V, draft, sl_off, sl_ids, q, x, smax, ssum, nseg, u_acc, nchV, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(verify_final_kernel<LOGITS>, grid, dim3(kChunkThreads), 0, s, B, T, V,
-                       draft, sl_off, sl_ids, q, x, smax, ssum, nseg, u_fin, nchV,
-                       (const void *)ws, n_acc, out);
+    hipLaunchKernelGGL(verify_sum_kernel<LOGITS>, dim3((unsigned)((nchV + 3) / 4), (unsigned)B),
+                       dim3(kChunkThreads), 0, s, B, T, V, sl_off, sl_ids, q, x, nchV, ws);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(verify_final_kernel<LOGITS>, dim3((unsigned)B), dim3(kChunkThreads), 0, s,
+                       B, T, V, draft, sl_off, sl_ids, q, x, u_fin, nchV, (const void *)ws, n_acc,
+                       out);
     return hipGetLastError();
 }
 
@@ -297,7 +428,8 @@ hipError_t verify_kernels(hipStream_t s, int B, int T, int V, const int32_t *dra
 size_t verify_ws_bytes(int B, int T, int V)
 {
     (void)T;
-    return chunk_ws_bytes(B, chunks_for(V)) + (size_t)B * sizeof(int32_t) + 256;
+    size_t off[4];
+    return verify_ws_layout(B, chunks_for(V), off) + 256;
 }
 
 hipError_t verify_launch(hipStream_t s, int B, int T, int V, const int32_t *draft,

@@ -72,6 +72,10 @@ def _cpu(t):
     (True, syn.ACT_SILU, 8, 264, 136, 100),
     (True, syn.ACT_SILU, 32, 4096, 1024, 1024),
     (True, syn.ACT_RELU, 70, 520, 200, 64),
+    # second layer on the matrix cores: two-slice windows (M = 4096), and a
+    # shape whose window partials do not fit (the vector path)
+    (True, syn.ACT_SILU, 16, 512, 1024, 4096),
+    (True, syn.ACT_RELU, 12, 256, 64, 4096),
 ])
 def test_router_parity(N, oracle_lib, bf16, act, n, d, r, M):
     g = np.random.default_rng(100 + d)
