@@ -25,6 +25,8 @@
 // so results are reproducible bit for bit.
 #pragma once
 
+#include <float.h>
+
 #include "common.h"
 
 namespace ds {
@@ -93,6 +95,81 @@ __device__ __forceinline__ void row_norm(const float *__restrict__ sm, const dou
 __device__ __forceinline__ float p_elem(float l, float M, double rZ, const double *tab)
 {
     return (float)(exp_tab((double)l - (double)M, tab) * rZ);
+}
+
+// this lane's four consecutive elements (-FLT_MAX past the row end); one
+// 16-byte load when the row base is 16-byte aligned (j0 is a multiple of 4)
+__device__ __forceinline__ void load4(const float *__restrict__ l, int64_t j0, int64_t len,
+                                      float v[4])
+{
+    const bool vec = (reinterpret_cast<uintptr_t>(l) & 15) == 0;
+    if (vec && j0 + 3 < len) {
+        const float4 q = *reinterpret_cast<const float4 *>(l + j0);
+        v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        v[k] = j0 + k < len ? l[j0 + k] : -FLT_MAX;
+}
+
+// Target softmax segments: kSeg elements per 256-thread workgroup; lane l
+// of wave w holds elements 1024 i + 256 w + 4 l + k (i, k < 4) of it.
+constexpr int kSeg = 4 * kChunk;
+
+__device__ __forceinline__ void load_seg(const float *__restrict__ lr, int64_t j0, int64_t V,
+                                         float v[4][4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        load4(lr, j0 + i * kChunk, V, v[i]);
+}
+
+// Statistics of segment `seg` of one row of V logits, by the whole
+// (256-thread) workgroup: its max (fp32, exact) and the sum of exp(l - max)
+// over it in fp64, in a fixed association (each lane's 16 terms in order,
+// the wave butterfly, the four wave sums in order); -inf logits weigh 0.
+// Thread 0 writes *sum_out and *max_out.
+__device__ __forceinline__ void segment_stats(int64_t V, const float *__restrict__ row,
+                                              int64_t seg, double *sum_out, float *max_out)
+{
+    __shared__ float s_m[4];
+    __shared__ double s_s[4];
+    __shared__ double s_exp2[64];
+    const int64_t j0 = seg * kSeg + (threadIdx.x >> 6) * 256 + lane_id() * 4;
+    float v[4][4];
+    load_seg(row, j0, V, v);
+    fill_exp2_table(s_exp2);
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            m = fmaxf(m, v[i][k]);  // -FLT_MAX past V
+    m = wave_max(m);
+    if (lane_id() == 0)
+        s_m[threadIdx.x >> 6] = m;
+    __syncthreads();  // also orders the table
+    const float mseg = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            // computed for every element and selected (no branch per
+            // element); adding an exact 0 leaves the sum unchanged
+            const float x = v[i][k];
+            const double e = exp_tab((double)x - (double)mseg, s_exp2);
+            acc += (j0 + i * kChunk + k < V && x != -INFINITY) ? e : 0.0;
+        }
+    acc = wave_sum_f64(acc);
+    if (lane_id() == 0)
+        s_s[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        *sum_out = ((s_s[0] + s_s[1]) + s_s[2]) + s_s[3];
+        *max_out = mseg;
+    }
 }
 
 // chunk statistics kept in a caller workspace: [rows][nchmax] of each
@@ -303,6 +380,39 @@ __device__ inline int64_t wave_lower_bound(const int32_t *__restrict__ S, int64_
     const int64_t idx = lo + lane;
     const bool lt = idx < hi && S[idx] < x;
     return lo + __popcll(__ballot(lt));
+}
+
+// wave_lower_bound for two keys x0 <= x1 at once (the loads of both
+// searches of a round are issued together): *r0, *r1 as two calls would give.
+__device__ inline void wave_lower_bound2(const int32_t *__restrict__ S, int64_t len, int32_t x0,
+                                         int32_t x1, int64_t *r0, int64_t *r1)
+{
+    const int lane = lane_id();
+    int64_t lo0 = 0, hi0 = len, lo1 = 0, hi1 = len;
+    while (hi0 - lo0 > kWave || hi1 - lo1 > kWave) {
+        const bool a0 = hi0 - lo0 > kWave, a1 = hi1 - lo1 > kWave;  // wave-uniform
+        const int64_t st0 = (hi0 - lo0 + kWave - 1) / kWave, st1 = (hi1 - lo1 + kWave - 1) / kWave;
+        const int64_t i0 = lo0 + (int64_t)lane * st0, i1 = lo1 + (int64_t)lane * st1;
+        const bool in0 = a0 && i0 < hi0, in1 = a1 && i1 < hi1;
+        const int32_t v0 = in0 ? S[i0] : 0, v1 = in1 ? S[i1] : 0;
+        if (a0) {
+            const int k = __popcll(__ballot(in0 && v0 < x0));
+            const int64_t nlo = k > 0 ? lo0 + (int64_t)(k - 1) * st0 + 1 : lo0;
+            hi0 = min(hi0, lo0 + (int64_t)k * st0);
+            lo0 = nlo;
+        }
+        if (a1) {
+            const int k = __popcll(__ballot(in1 && v1 < x1));
+            const int64_t nlo = k > 0 ? lo1 + (int64_t)(k - 1) * st1 + 1 : lo1;
+            hi1 = min(hi1, lo1 + (int64_t)k * st1);
+            lo1 = nlo;
+        }
+    }
+    const int64_t i0 = lo0 + lane, i1 = lo1 + lane;
+    const bool in0 = i0 < hi0, in1 = i1 < hi1;
+    const int32_t v0 = in0 ? S[i0] : 0, v1 = in1 ? S[i1] : 0;
+    *r0 = lo0 + __popcll(__ballot(in0 && v0 < x0));
+    *r1 = lo1 + __popcll(__ballot(in1 && v1 < x1));
 }
 
 }  // namespace ds

@@ -45,22 +45,6 @@ struct Ragged {
     }
 };
 
-// this lane's four consecutive elements (-FLT_MAX past the row end); one
-// 16-byte load when the row base is 16-byte aligned (j0 is a multiple of 4)
-__device__ __forceinline__ void load4(const float *__restrict__ l, int64_t j0, int64_t len,
-                                      float v[4])
-{
-    const bool vec = (reinterpret_cast<uintptr_t>(l) & 15) == 0;
-    if (vec && j0 + 3 < len) {
-        const float4 q = *reinterpret_cast<const float4 *>(l + j0);
-        v[0] = q.x, v[1] = q.y, v[2] = q.z, v[3] = q.w;
-        return;
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        v[k] = j0 + k < len ? l[j0 + k] : -FLT_MAX;
-}
-
 // (x) / T; T = 1 (the usual case, and always for the target) skips the
 // fp64 division, which leaves the value unchanged
 __device__ __forceinline__ double over_tau(double x, double tau) { return tau == 1.0 ? x : x / tau; }
@@ -284,64 +268,15 @@ hipError_t launch_norm(hipStream_t s, L layout, int64_t rows, int64_t max_len, c
 }
 
 // ------------------------------------------------------------ target softmax
-// Segment of kSeg elements per 256-thread workgroup; lane l of wave w holds
-// elements 1024 i + 256 w + 4 l + k (i, k < 4) of it (16-byte accesses).
-constexpr int kSeg = 4 * kChunk;
-
-__device__ __forceinline__ void load_seg(const float *__restrict__ lr, int64_t j0, int64_t V,
-                                         float v[4][4])
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        load4(lr, j0 + i * kChunk, V, v[i]);
-}
-
-// Segment max (fp32, exact) and the sum of exp(l - max) over the segment in
-// fp64, in a fixed association (each lane's 16 terms in order, the wave
-// butterfly, the four wave sums in order).  -inf logits weigh 0.
+// Segment statistics (segment_stats in dist.h), one workgroup per segment.
 __global__ __launch_bounds__(kChunkThreads) void softmax_stats_kernel(int64_t V,
                                                                       const float *__restrict__ in,
                                                                       double *__restrict__ ssum,
                                                                       float *__restrict__ smax)
 {
-    __shared__ float s_m[4];
-    __shared__ double s_s[4];
-    __shared__ double s_exp2[64];
     const int64_t row = blockIdx.y, nseg = gridDim.x;
-    const int64_t j0 = (int64_t)blockIdx.x * kSeg + (threadIdx.x >> 6) * 256 + lane_id() * 4;
-    float v[4][4];
-    load_seg(in + row * V, j0, V, v);
-    fill_exp2_table(s_exp2);
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            m = fmaxf(m, v[i][k]);  // -FLT_MAX past V
-    m = wave_max(m);
-    if (lane_id() == 0)
-        s_m[threadIdx.x >> 6] = m;
-    __syncthreads();  // also orders the table
-    const float mseg = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-    double acc = 0.0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            // computed for every element and selected (no branch per
-            // element); adding an exact 0 leaves the sum unchanged
-            const float x = v[i][k];
-            const double e = exp_tab((double)x - (double)mseg, s_exp2);
-            acc += (j0 + i * kChunk + k < V && x != -INFINITY) ? e : 0.0;
-        }
-    acc = wave_sum_f64(acc);
-    if (lane_id() == 0)
-        s_s[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        ssum[row * nseg + blockIdx.x] = ((s_s[0] + s_s[1]) + s_s[2]) + s_s[3];
-        smax[row * nseg + blockIdx.x] = mseg;
-    }
+    segment_stats(V, in + row * V, blockIdx.x, &ssum[row * nseg + blockIdx.x],
+                  &smax[row * nseg + blockIdx.x]);
 }
 
 // p = exp(l - M) * (1 / Z), M the row max, Z = sum over segments of

@@ -334,7 +334,7 @@ ds_status ds_verify_reject_logits(hipStream_t s, int B, int T, int V, const int3
  * device, on that device's first call; the current device must be the
  * stream's).  The call allocates nothing.  It needs
  * ds_verify_workspace_bytes(B, T, V) <= DS_NOALLOC_SCRATCH_BYTES (about
- * B * ceil(V / 1024) <= 299000), else DS_ESHAPE.  All calls on one GPU share
+ * B * ceil(V / 1024) <= 1040000), else DS_ESHAPE.  All calls on one GPU share
  * that GPU's array, so calls that may overlap on one GPU (other streams,
  * other threads) race and give wrong results; serialise them.
  */

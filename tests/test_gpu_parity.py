@@ -671,6 +671,34 @@ def test_verify_parity(N, oracle_lib, V, T, B, mode):
         assert n_ref.mean() > 0.5
 
 
+def test_verify_residual_without_mass(N, oracle_lib):
+    """Rejections whose residual max(0, p - q) has no mass draw from p_t
+    itself: p_0 = q_0 / 2 on the shortlist (sequences 0-2) rejects for
+    u = 0.9 and leaves no residual; an all-zero p_0 (sequence 3) has nothing
+    to draw (-1)."""
+    V, T, B = 5000, 3, 4
+    c, _ = _verify_case(oracle_lib, V, T, B, "random", seed=77)
+    p = c["p"].copy()
+    for b in range(B):
+        p[b, 0] = 0.0
+        if b < 3:
+            lo, hi = c["sl_off"][b], c["sl_off"][b + 1]
+            p[b, 0, c["sl_ids"][lo:hi]] = 0.5 * c["q"][lo:hi]
+    c["p"] = p
+    c["u_acc"] = c["u_acc"].copy()
+    c["u_acc"][0] = 0.9
+    n_ref, out_ref, tie = oracle_lib.verify_reject(**c)
+    assert (n_ref == 0).all() and out_ref[3, 0] == -1 and (out_ref[:3, 0] >= 0).all()
+    n_acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, T + 1, dtype=torch.int32, device="cuda")
+    dv = {k: to_dev(v) for k, v in c.items()}
+    N.verify_reject(dv["draft"], dv["sl_off"], dv["sl_ids"], dv["q"], dv["p"], dv["u_acc"],
+                    dv["u_fin"], n_acc, out, N.workspace(N.verify_workspace_bytes(B, T, V)))
+    assert np.array_equal(_cpu(n_acc), n_ref)
+    got = _cpu(out)
+    assert np.array_equal(got[~tie], out_ref[~tie])
+
+
 @pytest.mark.parametrize("V,T,B", [(8, 3, 64), (5000, 4, 16), (128256, 6, 4), (262144, 5, 3),
                                    (10001, 64, 3), (32000, 3, 200)])
 @pytest.mark.parametrize("mode", ["random", "reject_all", "correlated"])

@@ -58,7 +58,7 @@ def test_workspace_queries(N):
     assert N.sample_workspace_bytes(1, 1, 1024) == 24 + 256
     assert N.sample_workspace_bytes(3, 4, 1025) == 12 * 2 * 24 + 256
     assert N.softmax_workspace_bytes(7, 128256) == 7 * 32 * 12 + 256  # 4096-entry segments
-    assert N.verify_workspace_bytes(2, 6, 128256) >= 2 * 126 * 24 + 2 * 4
+    assert N.verify_workspace_bytes(2, 6, 128256) >= 2 * 126 * 8 + 2 * 16  # chunk sums, t*, row norms
     assert N.draft_chain_workspace_bytes(1, 6, 128256, 1024, 55734) >= 4096 + 256
     # batched chains: two 32-token tile-index slots (8 bytes per tile and row)
     tiles = (128256 + 31) // 32 + 1
