@@ -11,6 +11,7 @@ power of two, empty and single-entry shortlists).
 import numpy as np
 import pytest
 import torch
+from tie_checks import check_sample_ties, check_verify_ties
 
 import oracle
 from dynamic_vocabulary_draft_amd import synthetic as syn
@@ -532,6 +533,7 @@ def test_sample_parity(N, oracle_lib, lens, m, tau):
                        max_len=max(lens), m=m)
     got = _cpu(token)
     assert np.array_equal(got[~tie], tok_ref[~tie])
+    check_sample_ties(got, tok_ref, tie, sl_off, sl_ids, q_ref, m)
     _ulp_bar(_cpu(q), q_ref)
 
 
@@ -552,6 +554,7 @@ def test_sample_many_rows_bit_exact(N, oracle_lib):
                        max_len=L)
     got = _cpu(token)
     assert np.array_equal(got[~tie], tok_ref[~tie])
+    check_sample_ties(got, tok_ref, tie, sl_off, ids, q_ref)
     assert tie.sum() <= 2
 
 
@@ -577,6 +580,7 @@ def test_sample_multi_chunk_workgroups(N, oracle_lib, rows, maxlen, tau):
                        ws, max_len=int(lens.max()))
     got = _cpu(token)
     assert np.array_equal(got[~tie], tok_ref[~tie])
+    check_sample_ties(got, tok_ref, tie, sl_off, sl_ids, q_ref)
     _ulp_bar(_cpu(q), q_ref)
 
 
@@ -665,6 +669,8 @@ def test_verify_parity(N, oracle_lib, V, T, B, mode):
     assert np.array_equal(_cpu(n_acc), n_ref)  # accept decisions are exact
     got = _cpu(out)
     assert np.array_equal(got[~tie], out_ref[~tie])
+    check_verify_ties(got, out_ref, n_ref, tie, c["draft"], c["sl_off"], c["sl_ids"], c["q"],
+                      c["p"])
     if mode == "accept_all":
         assert (n_ref == T).all()
     if mode == "correlated":
@@ -697,6 +703,8 @@ def test_verify_residual_without_mass(N, oracle_lib):
     assert np.array_equal(_cpu(n_acc), n_ref)
     got = _cpu(out)
     assert np.array_equal(got[~tie], out_ref[~tie])
+    check_verify_ties(got, out_ref, n_ref, tie, c["draft"], c["sl_off"], c["sl_ids"], c["q"],
+                      c["p"])
 
 
 @pytest.mark.parametrize("V,T,B", [(8, 3, 64), (5000, 4, 16), (128256, 6, 4), (262144, 5, 3),
@@ -730,6 +738,8 @@ def test_verify_logits_parity(N, oracle_lib, V, T, B, mode):
     n_ref, out_ref, tie = oracle_lib.verify_reject(**c)
     assert np.array_equal(outs[1][0], n_ref)
     assert np.array_equal(outs[1][1][~tie], out_ref[~tie])
+    check_verify_ties(outs[1][1], out_ref, n_ref, tie, c["draft"], c["sl_off"], c["sl_ids"],
+                      c["q"], c["p"])
 
 
 # ----------------------------------------------------------------------------

@@ -13,6 +13,7 @@ on sampled entries (the oracle cannot do 10^11 fp64 MACs in seconds).
 import numpy as np
 import pytest
 import torch
+from tie_checks import check_sample_ties, check_verify_ties
 
 import oracle
 from oracle import pipeline as opipe
@@ -105,6 +106,7 @@ def check_stagewise(wl, r, head_samples=None, seed=0, tau=1.0):
                                               tau)
         got_tok = r["token"].reshape(-1) if cfg.is_tree else r["token"][t]
         assert np.array_equal(got_tok[~tie], tok[~tie])
+        check_sample_ties(got_tok, tok, tie, loc_off, loc_ids, q, m)
         _ulp(r["q"][m * lo:m * hi], q)
     if "p" in r:
         _ulp(r["p"], oracle.target_softmax(wl.target_logits))
@@ -120,6 +122,8 @@ def check_stagewise(wl, r, head_samples=None, seed=0, tau=1.0):
                                                wl.u_acc, wl.u_fin)
         assert np.array_equal(r["n_acc"], n_acc)
         assert np.array_equal(r["out"][~tie], out[~tie])
+        check_verify_ties(r["out"], out, n_acc, tie, r["token"], r["sl_off"], r["sl_ids"], r["q"],
+                          r["p"])
 
 
 def check_from_scratch(wl, r, tau=1.0):
@@ -132,14 +136,26 @@ def check_from_scratch(wl, r, tau=1.0):
     ok_rows = np.ones((npos, B), bool)
     for t in range(npos):
         for b in range(B):
-            k = ref["n_sel"][t][b]
-            same = (r["n_sel"][t][b] == k and
-                    np.array_equal(r["sel"][t][b, :k], ref["sel"][t][b, :k]))
-            if not same:
-                s = np.sort(ref["scores"][t][b])[::-1]
-                gaps = np.abs(np.diff(s[: min(len(s), k + 2)]))
-                assert gaps.min() < 2 * router_err + 1e-30, "selection differs outside a tie zone"
-                ok_rows[t, b] = False
+            k, kg = int(ref["n_sel"][t][b]), int(r["n_sel"][t][b])
+            rs, gs = ref["sel"][t][b, :k], r["sel"][t][b, :kg]
+            if kg == k and np.array_equal(gs, rs):
+                continue
+            # the first rank where the two selections differ: the clusters
+            # there must be within the router's error of each other in the
+            # oracle's scores (else the GPU ranked them wrongly)
+            sc = np.asarray(ref["scores"][t][b], np.float64)
+            n = min(k, kg)
+            diff = np.flatnonzero(rs[:n] != gs[:n])
+            # equal prefixes decide the next cluster alike: a count that
+            # differs after them is no ranking tie
+            assert diff.size, "selection counts differ after the same ranked prefix"
+            i = int(diff[0])
+            c_ref, c_gpu = int(rs[i]), int(gs[i])
+            assert abs(sc[c_ref] - sc[c_gpu]) < 2 * router_err + 1e-30, \
+                "selection differs at rank %d outside a tie zone" % i
+            ok_rows[t, b] = False
+    # the excuse is for rare near-ties, not a share of the rows
+    assert (~ok_rows).sum() <= max(1, ok_rows.size // 8), "too many rows in tie zones"
     if cfg.is_tree:
         tok_ok = ~ref["tie"].reshape(B, -1) & ok_rows[0][:, None]
         assert np.array_equal(r["token"][tok_ok], ref["token"].reshape(B, -1)[tok_ok])
