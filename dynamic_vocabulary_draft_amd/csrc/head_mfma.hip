@@ -308,35 +308,135 @@ __global__ __launch_bounds__(256) void union_index_kernel(int G, int nt, int V,
     }
 }
 
-// one 32*WV-row tile of W (tile index `tile`) against the column pass
+// Union tiles are walked back to back by each workgroup of a persistent
+// grid.  A tile's W ring (its first four slices) is issued ahead, by the
+// previous tile's last slice group in place of refills that would have no
+// slice left to load: the next tile's first W bytes are in flight while
+// this tile's epilogue runs, and no tile starts its K loop on a cold ring.
+template <int NB, int NT>
+struct Ring {
+    u32x4 hv[stage_n<NT>()];
+    u32x4 r0[4], r1[4], r2[4], r3[4];
+};
+
+// the phase the walk of union tile `tile` starts at (rotation by tile)
+__device__ __forceinline__ int union_ph0(int tile, int d, int KP)
+{
+    const int nsl = (d + kKs - 1) / kKs, nph = (d + KP - 1) / KP;
+    return nsl == nph * (KP / kKs) ? (tile * kPhaseRot) % nph : 0;
+}
+
+// W rows y0 .. y0+tile_rows-1 of a union tile (rows past V read zero; never
+// written)
+template <int WV>
+__device__ __forceinline__ rsrc_t union_rsrc(const uint16_t *W, int V, int d, int tile)
+{
+    const int64_t y0 = (int64_t)tile * tile_rows<WV>();
+    const int64_t rows = min((int64_t)tile_rows<WV>(), (int64_t)V - y0);
+    return make_rsrc(W + y0 * d, (uint32_t)(rows * d * 2));
+}
+
+// the first B phase (hidden vectors, from L2) and the first four W slices
+template <int NB, int NT, class Src>
+__device__ __forceinline__ void ring_prime(Ring<NB, NT> &rg, rsrc_t w, const uint32_t voff[4],
+                                           int d, int nrows, Src src, int ph0)
+{
+    constexpr int KP = phase_len<NB>(), NS = KP / kKs;
+    load_phase<NB, NT>(rg.hv, ph0 * KP, d, nrows, src);
+    __builtin_amdgcn_sched_barrier(0);  // B loads first, as in the loop
+    load_a<kNonTemporal>(w, voff, (ph0 * NS + 0) * kKs, rg.r0);
+    load_a<kNonTemporal>(w, voff, (ph0 * NS + 1) * kKs, rg.r1);
+    load_a<kNonTemporal>(w, voff, (ph0 * NS + 2) * kKs, rg.r2);
+    load_a<kNonTemporal>(w, voff, (ph0 * NS + 3) * kKs, rg.r3);
+}
+
+// rows_times_b for a primed ring; the last group's refills load the next
+// tile's first slices (wn, ph0n) when has_next, else nothing (a slice past
+// the buffer range); after the loop, the next tile's first B phase.
+template <int NB, int NT, class Src>
+__device__ __forceinline__ void union_rows_times_b(Ring<NB, NT> &rg, rsrc_t w, rsrc_t wn,
+                                                   const uint32_t voff[4], int d, uint16_t *lds,
+                                                   uint16_t *aw, int nrows, Src src,
+                                                   f32x16 acc[NB], int ph0, int ph0n,
+                                                   bool has_next)
+{
+    constexpr int KP = phase_len<NB>(), NS = KP / kKs, GP = NS / 4;
+    const int nsl = (d + kKs - 1) / kKs, nph = (d + KP - 1) / KP;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = f32x16{};
+    for (int j = 0; j < nph; ++j) {
+        const int ph = j + ph0 < nph ? j + ph0 : j + ph0 - nph;
+        const int phn = j + 1 + ph0 < nph ? j + 1 + ph0 : j + 1 + ph0 - nph;
+        __syncthreads();  // every wave is done with the previous phase (or tile)
+        store_phase<NB, NT>(lds, rg.hv, ph * KP, d, nrows);
+        __syncthreads();
+#pragma unroll
+        for (int gi = 0; gi < GP; ++gi) {
+            const int ks = ph * NS + 4 * gi;
+            if (ks >= nsl)
+                break;  // only in the last phase
+            const bool fin = j + 1 == nph && (gi == GP - 1 || ks + 4 >= nsl);
+            const int kn = fin ? (has_next ? ph0n * NS : kTailOob)
+                               : (gi < GP - 1 ? ks + 4 : phn * NS);
+            const rsrc_t wr = fin && has_next ? wn : w;
+            if (gi == GP - 1 && j + 1 < nph) {
+                load_phase<NB, NT>(rg.hv, phn * KP, d, nrows, src);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            slice_mma<NB>(rg.r0, aw, lds, (4 * gi + 0) * kKs, (ks + 0) * kKs, d, acc);
+            load_a<kNonTemporal>(wr, voff, (kn + 0) * kKs, rg.r0);
+            slice_mma<NB>(rg.r1, aw, lds, (4 * gi + 1) * kKs, (ks + 1) * kKs, d, acc);
+            load_a<kNonTemporal>(wr, voff, (kn + 1) * kKs, rg.r1);
+            slice_mma<NB>(rg.r2, aw, lds, (4 * gi + 2) * kKs, (ks + 2) * kKs, d, acc);
+            load_a<kNonTemporal>(wr, voff, (kn + 2) * kKs, rg.r2);
+            slice_mma<NB>(rg.r3, aw, lds, (4 * gi + 3) * kKs, (ks + 3) * kKs, d, acc);
+            load_a<kNonTemporal>(wr, voff, (kn + 3) * kKs, rg.r3);
+        }
+    }
+    if (has_next)
+        load_phase<NB, NT>(rg.hv, ph0n * KP, d, nrows, src);
+}
+
+// does any shortlist of the column pass touch union tile `tile`?  (every
+// thread; barriers inside)
+template <int WV>
+__device__ __forceinline__ bool union_tile_any(int G, int g0, int ng,
+                                               const int64_t *__restrict__ sl_off,
+                                               const TileIx *__restrict__ tix, int nt, int tile,
+                                               int *s_any)
+{
+    const int64_t y0 = (int64_t)tile * tile_rows<WV>();
+    __syncthreads();  // the previous reader of *s_any is done
+    if (threadIdx.x == 0)
+        *s_any = 0;
+    __syncthreads();
+    for (int q = threadIdx.x; q < ng * WV; q += blockDim.x) {
+        const int g = g0 + q / WV, t = (int)(y0 >> 5) + q % WV;
+        if (t < nt && sl_off[g + 1] > sl_off[g] && tix[(int64_t)g * (nt + 1) + t].mask != 0u)
+            *s_any = 1;
+    }
+    __syncthreads();
+    return *s_any != 0;
+}
+
+// one 32*WV-row tile of W (tile index `tile`, ring primed) against the
+// column pass; primes the ring for `next` when has_next
 template <int NB, int WV>
 __device__ __forceinline__ void union_tile(int V, int d, const uint16_t *__restrict__ W, int G,
                                            int g0, const uint16_t *__restrict__ h, int64_t ldh_g,
                                            const int64_t *__restrict__ sl_off,
                                            const TileIx *__restrict__ tix, int nt,
-                                           float *__restrict__ logits, int tile)
+                                           float *__restrict__ logits, int tile, int next,
+                                           bool has_next, Ring<NB, 64 * WV> &rg,
+                                           uint16_t *lds_all)
 {
     constexpr int kTileRows = tile_rows<WV>();
-    __shared__ __attribute__((aligned(16))) uint16_t lds_all[lds_bytes<NB, WV>() / 2];
     uint16_t *lds = lds_all, *lds_a = lds_all + NB * 32 * lds_row<NB>();
-    __shared__ int s_any;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int ng = min(NB * 32, G - g0);  // groups of this column pass
     const int64_t y0 = (int64_t)tile * kTileRows;
     const int t32 = (int)(y0 >> 5) + wave;  // this wave's 32-token tile
-
-    // skip tiles no shortlist touches
-    if (threadIdx.x == 0)
-        s_any = 0;
-    __syncthreads();
-    for (int q = threadIdx.x; q < ng * WV; q += blockDim.x) {
-        const int g = g0 + q / WV, t = (int)(y0 >> 5) + q % WV;
-        if (t < nt && sl_off[g + 1] > sl_off[g] && tix[(int64_t)g * (nt + 1) + t].mask != 0u)
-            s_any = 1;
-    }
-    __syncthreads();
-    if (!s_any)
-        return;
 
     // where this lane's groups put the tile's logits, fetched before the
     // K loop (lane l, column block nb: group g0 + 32*nb + l%32); wave 0
@@ -368,18 +468,18 @@ __device__ __forceinline__ void union_tile(int V, int d, const uint16_t *__restr
         }
     }
 
-    // the block's W rows y0 .. y0+kTileRows-1 (rows past V read zero; never written)
-    const int64_t rows = min((int64_t)kTileRows, (int64_t)V - y0);
-    const rsrc_t w = make_rsrc(W + y0 * d, (uint32_t)(rows * d * 2));
     uint32_t voff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         voff[i] = (uint32_t)((32 * wave + (lane >> 3) + 8 * i) * d * 2 + 16 * (lane & 7));
     f32x16 acc[NB];
     auto hsrc = [&](int r) { return h + (int64_t)(g0 + r) * ldh_g; };
-    // the range is at most 256 rows x 16 KB: the tail slice reads nothing
-    rows_times_b<NB, 64 * WV, kNonTemporal>(w, voff, d, lds, lds_a + wave * kASlice, ng, hsrc,
-                                            acc, tile * kPhaseRot, kTailOob);
+    // the ranges are at most 256 rows x 16 KB: the tail slice reads nothing
+    union_rows_times_b<NB, 64 * WV>(rg, union_rsrc<WV>(W, V, d, tile),
+                                    union_rsrc<WV>(W, V, d, has_next ? next : tile), voff, d, lds,
+                                    lds_a + wave * kASlice, ng, hsrc, acc,
+                                    union_ph0(tile, d, phase_len<NB>()),
+                                    union_ph0(next, d, phase_len<NB>()), has_next);
 
     // epilogue: the (row, group) pairs on the group's shortlist.  A group's
     // entries for the block's WV tiles are one contiguous run of its logits;
@@ -420,9 +520,54 @@ __global__ __launch_bounds__(64 * WV) void head_union_kernel(int V, int d, const
                                                          const TileIx *__restrict__ tix, int nt,
                                                          float *__restrict__ logits, int ntiles)
 {
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        union_tile<NB, WV>(V, d, W, G, g0, h, ldh_g, sl_off, tix, nt, logits, tile);
-        __syncthreads();  // the tile's epilogue is done with the shared buffers
+    __shared__ __attribute__((aligned(16))) uint16_t lds_all[lds_bytes<NB, WV>() / 2];
+    __shared__ int s_any;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int ng = min(NB * 32, G - g0);
+    uint32_t voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        voff[i] = (uint32_t)((32 * wave + (lane >> 3) + 8 * i) * d * 2 + 16 * (lane & 7));
+    Ring<NB, 64 * WV> rg;
+    int tile = blockIdx.x;
+    if (tile >= ntiles)
+        return;
+    // tiles no shortlist touches are skipped (and never primed).  CROSS:
+    // the ring for the next tile is primed by this one (measured: the
+    // 64-group Gemma-shaped head 348 -> 344 us; the 32-group Llama-shaped
+    // head, 4-wave tiles with less register room, 179 -> 181 us without
+    // its B phase primed, so it primes per tile)
+    constexpr bool CROSS = NB == 2;
+    auto hsrc = [&](int r) { return h + (int64_t)(g0 + r) * ldh_g; };
+    if constexpr (!CROSS) {  // each tile primes its own ring
+        for (; tile < ntiles; tile += gridDim.x)
+            if (union_tile_any<WV>(G, g0, ng, sl_off, tix, nt, tile, &s_any)) {
+                ring_prime<NB, 64 * WV>(rg, union_rsrc<WV>(W, V, d, tile), voff, d, ng, hsrc,
+                                        union_ph0(tile, d, phase_len<NB>()));
+                union_tile<NB, WV>(V, d, W, G, g0, h, ldh_g, sl_off, tix, nt, logits, tile, tile,
+                                   false, rg, lds_all);
+                __syncthreads();  // the tile's epilogue is done with the shared buffers
+            }
+        return;
+    }
+    bool any = union_tile_any<WV>(G, g0, ng, sl_off, tix, nt, tile, &s_any);
+    if (any)
+        ring_prime<NB, 64 * WV>(rg, union_rsrc<WV>(W, V, d, tile), voff, d, ng, hsrc,
+                                union_ph0(tile, d, phase_len<NB>()));
+    while (tile < ntiles) {
+        const int next = tile + (int)gridDim.x;
+        const bool any_next =
+            next < ntiles && union_tile_any<WV>(G, g0, ng, sl_off, tix, nt, next, &s_any);
+        if (any) {
+            union_tile<NB, WV>(V, d, W, G, g0, h, ldh_g, sl_off, tix, nt, logits, tile, next,
+                               any_next, rg, lds_all);
+            __syncthreads();  // the tile's epilogue is done with the shared buffers
+        } else if (any_next) {
+            ring_prime<NB, 64 * WV>(rg, union_rsrc<WV>(W, V, d, next), voff, d, ng, hsrc,
+                                    union_ph0(next, d, phase_len<NB>()));
+        }
+        tile = next;
+        any = any_next;
     }
 }
 
