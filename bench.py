@@ -212,6 +212,82 @@ def traffic_from(args):
     print(json.dumps(out))
 
 
+def overlap_from(args):
+    """Concurrency with the gathered head in a rocprofv3 kernel trace (the
+    SQLite results file of `rocprofv3 --kernel-trace`): for every other
+    kernel, its launches, mean duration, the share of its time during which
+    a head kernel was running, and the share of its launches that
+    overlapped a head at all.  Printed as a markdown table."""
+    import re
+    import sqlite3
+
+    con = sqlite3.connect(args.overlap_from)
+    rows = con.execute("select name, start, end from kernels order by start").fetchall()
+    con.close()
+
+    def short(n):
+        n = n.replace("void ", "").replace("ds::(anonymous namespace)::", "")
+        return re.split(r"[<(]", n)[0]
+
+    heads = [(a, b) for n, a, b in rows if short(n).startswith("head_")]
+    stats = {}
+    for n, a, b in rows:
+        k = short(n)
+        if k.startswith("head_") or "rocclr" in n or "at::" in n:
+            continue
+        ov = 0
+        for ha, hb in heads:  # sorted by start; heads do not overlap each other
+            if hb <= a:
+                continue
+            if ha >= b:
+                break
+            ov += min(b, hb) - max(a, ha)
+        d = stats.setdefault(k, [0, 0.0, 0.0, 0])
+        d[0] += 1
+        d[1] += (b - a) / 1e3
+        d[2] += ov / 1e3
+        d[3] += ov > 0
+    hk = sorted({short(n) for n, _, _ in rows if short(n).startswith("head_")})
+    print("| kernel | launches | mean us | time beside a head | launches beside a head |")
+    print("|---|---:|---:|---:|---:|")
+    for k, (cnt, tot, ov, anyc) in sorted(stats.items(), key=lambda x: -x[1][1]):
+        print("| %s | %d | %.2f | %.0f%% | %.0f%% |" % (k, cnt, tot / cnt, 100 * ov / tot,
+                                                       100 * anyc / cnt))
+    hs = [(b - a) / 1e3 for a, b in heads]
+    print("\nhead kernels (%s): %d launches, mean %.2f us" % (", ".join(hk), len(hs),
+                                                            sum(hs) / max(1, len(hs))))
+
+
+def stats_from(args):
+    """The kernel statistics CSV of `rocprofv3 --stats` as a markdown table
+    (kernel, calls, mean / min / max / total microseconds, share)."""
+    import csv
+    import re
+
+    with open(args.stats_from) as f:
+        rows = list(csv.DictReader(f))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    print("| kernel | calls | avg us | min us | max us | total us | % |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        n = re.sub(r"^void ", "", r["Name"])
+        n = n.replace("ds::(anonymous namespace)::", "").replace("ds::", "")
+        depth, cut = 0, len(n)  # drop the parameter list
+        for i, ch in enumerate(n):
+            if ch == "<":
+                depth += 1
+            elif ch == ">":
+                depth -= 1
+            elif ch == "(" and depth == 0:
+                cut = i
+                break
+        n = n[:cut] if cut < 60 else n[:60] + "..."
+        print("| %s | %s | %.2f | %.2f | %.2f | %.1f | %.2f |" % (
+            n, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3,
+            100 * float(r["TotalDurationNs"]) / tot))
+
+
 PEAK_BF16_TFLOPS = 2500.0
 
 
@@ -455,6 +531,12 @@ def main():
     ap.add_argument("--traffic-out", default=None,
                     help="where --traffic-from writes (default: the file the default bench "
                          "line reads its traffic from; give another path for other workloads)")
+    ap.add_argument("--stats-from", metavar="KERNEL_STATS_CSV",
+                    help="print a rocprofv3 --stats kernel_stats.csv as a markdown table, "
+                         "and exit")
+    ap.add_argument("--overlap-from", metavar="RESULTS_DB",
+                    help="print, from a rocprofv3 --kernel-trace results database, how much "
+                         "of every kernel's time ran beside a head kernel, and exit")
     ap.add_argument("--probe-file", default=os.path.join(ROOT, "pmc_probe.json"),
                     help="where --pmc-probe writes (and --traffic-from reads) the launch list")
     ap.add_argument("--static", choices=["gathered", "packed"],
@@ -478,6 +560,10 @@ def main():
 
     if args.traffic_from:
         return traffic_from(args)
+    if args.overlap_from:
+        return overlap_from(args)
+    if args.stats_from:
+        return stats_from(args)
     if args.kmeans:
         if args.gpus != 1:
             print("bench.py measures one GPU only", file=sys.stderr)
