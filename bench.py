@@ -259,13 +259,25 @@ def overlap_from(args):
 
 
 def stats_from(args):
-    """The kernel statistics CSV of `rocprofv3 --stats` as a markdown table
-    (kernel, calls, mean / min / max / total microseconds, share)."""
+    """Kernel statistics as a markdown table (kernel, calls, mean / min / max
+    / total microseconds, share): from the kernel_stats.csv of `rocprofv3
+    --stats`, or aggregated from the kernels of a results database (.db)."""
     import csv
     import re
 
-    with open(args.stats_from) as f:
-        rows = list(csv.DictReader(f))
+    if args.stats_from.endswith(".db"):
+        import sqlite3
+
+        con = sqlite3.connect(args.stats_from)
+        agg = con.execute("select name, count(*), avg(end - start), min(end - start), "
+                          "max(end - start), sum(end - start) from kernels group by name"
+                          ).fetchall()
+        con.close()
+        rows = [{"Name": n, "Calls": c, "AverageNs": a, "MinNs": lo, "MaxNs": hi,
+                 "TotalDurationNs": t} for n, c, a, lo, hi, t in agg]
+    else:
+        with open(args.stats_from) as f:
+            rows = list(csv.DictReader(f))
     tot = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
     print("| kernel | calls | avg us | min us | max us | total us | % |")
     print("|---|---:|---:|---:|---:|---:|---:|")
@@ -531,9 +543,9 @@ def main():
     ap.add_argument("--traffic-out", default=None,
                     help="where --traffic-from writes (default: the file the default bench "
                          "line reads its traffic from; give another path for other workloads)")
-    ap.add_argument("--stats-from", metavar="KERNEL_STATS_CSV",
-                    help="print a rocprofv3 --stats kernel_stats.csv as a markdown table, "
-                         "and exit")
+    ap.add_argument("--stats-from", metavar="STATS_CSV_OR_DB",
+                    help="print kernel statistics (a rocprofv3 --stats kernel_stats.csv, or a "
+                         "--kernel-trace results database) as a markdown table, and exit")
     ap.add_argument("--overlap-from", metavar="RESULTS_DB",
                     help="print, from a rocprofv3 --kernel-trace results database, how much "
                          "of every kernel's time ran beside a head kernel, and exit")
