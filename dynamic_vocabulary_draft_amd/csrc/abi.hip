@@ -474,6 +474,35 @@ ds_status ds_verify_tree(hipStream_t s, int B, int m, int V, const int32_t *pare
                                              u_acc, u_fin, max_len, n_acc, out, path, ws));
 }
 
+size_t ds_verify_tree_logits_workspace_bytes(int B, int m, int V, int64_t max_len)
+{
+    if (B <= 0 || m <= 0 || V <= 0 || max_len <= 0)
+        return 0;
+    return ds::verify_tree_logits_ws_bytes(B, m, V, max_len);
+}
+
+ds_status ds_verify_tree_logits(hipStream_t s, int B, int m, int V, const int32_t *parent,
+                                const int32_t *token, const int64_t *sl_off,
+                                const int32_t *sl_ids, const float *q, const float *logits,
+                                const float *u_acc, const float *u_fin, int64_t max_len,
+                                int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
+                                size_t ws_bytes)
+{
+    if (!parent || !token || !sl_off || !sl_ids || !q || !logits || !u_acc || !u_fin || !n_acc ||
+        !out || !path)
+        return DS_EINVAL;
+    if (B <= 0 || m <= 0 || V <= 0 || max_len <= 0)
+        return DS_EINVAL;
+    if (m > DS_MAX_TREE_NODES || V > (1 << 20) || B > DS_MAX_GROUPS || max_len > (1 << 24) ||
+        (int64_t)B * (m + 1) > 65535)
+        return DS_ESHAPE;
+    if (!ws || ws_bytes < ds_verify_tree_logits_workspace_bytes(B, m, V, max_len))
+        return DS_EINVAL;
+    return hip_status(ds::verify_tree_logits_launch(s, B, m, V, parent, token, sl_off, sl_ids, q,
+                                                    logits, u_acc, u_fin, max_len, n_acc, out,
+                                                    path, ws));
+}
+
 ds_status ds_dense_lm_head(hipStream_t s, int V, int d, const void *W, int n, const void *h,
                            float *logits, int64_t ldl, hipEvent_t *events)
 {

@@ -132,6 +132,16 @@ hipError_t router_train_launch(hipStream_t s, int n, int d, int r, int M, int ac
                                float *db1, float *dW2, float *db2, double *loss, void *ws);
 
 size_t verify_tree_ws_bytes(int B, int m, int V, int64_t max_len);
+// tree verification from target logits [B][m+1][V]: the softmax statistics
+// pass, the row normalisers, then the same kernels with every target value
+// taken as the softmax would write it
+size_t verify_tree_logits_ws_bytes(int B, int m, int V, int64_t max_len);
+hipError_t verify_tree_logits_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
+                                     const int32_t *token, const int64_t *sl_off,
+                                     const int32_t *sl_ids, const float *q, const float *logits,
+                                     const float *u_acc, const float *u_fin, int64_t max_len,
+                                     int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
+                                     hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
                               const int32_t *token, const int64_t *sl_off, const int32_t *sl_ids,
                               const float *q, const float *p, const float *u_acc,

@@ -81,6 +81,43 @@ __host__ __device__ inline size_t tree_bits_bytes(int B, int V)
     return ((size_t)B * (size_t)tree_words(V) * 4 + 255) / 256 * 256;
 }
 
+// A target row: p itself, or (LOGITS) target logits with the row's softmax
+// normaliser (M, rZ) rebuilt from the softmax's segment statistics, each
+// value taken as p_elem (the bits the target softmax writes).  tab: the exp
+// table in LDS (LOGITS).
+template <bool LOGITS>
+struct TRow {
+    float M;
+    double rZ;
+    const double *tab;
+    __device__ __forceinline__ float operator()(float x) const
+    {
+        return LOGITS ? p_elem(x, M, rZ, tab) : x;
+    }
+};
+
+// Row normalisers of the B*(m+1) target rows, one wave per row
+__global__ __launch_bounds__(256) void tree_norms_kernel(int rows, int64_t nseg,
+                                                         const float *__restrict__ smax,
+                                                         const double *__restrict__ ssum,
+                                                         float *__restrict__ nM,
+                                                         double *__restrict__ nZ)
+{
+    __shared__ double tab[64];
+    fill_exp2_table(tab);
+    __syncthreads();
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows)
+        return;
+    float M;
+    double rZ;
+    row_norm(smax + (int64_t)r * nseg, ssum + (int64_t)r * nseg, nseg, tab, &M, &rZ);
+    if (lane_id() == 0) {
+        nM[r] = M;
+        nZ[r] = rZ;
+    }
+}
+
 __global__ __launch_bounds__(kBitsThreads) void tree_bits_kernel(
     int V, int64_t max_len, const int64_t *__restrict__ sl_off, const int32_t *__restrict__ sl_ids,
     uint32_t *__restrict__ bits, uint32_t *__restrict__ rank)
@@ -160,20 +197,21 @@ __device__ __forceinline__ double block_sum_f64(double v, double *sh)
 // four consecutive target values from y0 (y0 % 4 == 0); zero at or beyond
 // lim (<= V).  The loads are unconditional (clamped addresses), so no
 // branch separates them from the loads issued around them.
+template <bool LOGITS>
 __device__ __forceinline__ void load4(const float *__restrict__ pu, int64_t y0, int64_t lim, int V,
-                                      bool vec, float v[4])
+                                      bool vec, const TRow<LOGITS> &tv, float v[4])
 {
     if (vec) {  // V % 4 == 0 and pu 16-byte aligned: one dwordx4 load
         typedef float f32x4 __attribute__((ext_vector_type(4)));
         const f32x4 t = reinterpret_cast<const f32x4 *>(pu)[min(y0, (int64_t)V - 4) >> 2];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            v[e] = y0 + e < lim ? t[e] : 0.f;
+            v[e] = y0 + e < lim ? tv(t[e]) : 0.f;
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float t = pu[min(y0 + e, (int64_t)V - 1)];
-            v[e] = y0 + e < lim ? t : 0.0f;
+            v[e] = y0 + e < lim ? tv(t) : 0.0f;
         }
     }
 }
@@ -198,10 +236,10 @@ __device__ __forceinline__ int rank_at(const uint32_t *__restrict__ rank_b, int6
 // into s_wsum[w] the target mass off the shortlist (OFF) or all of it.
 // Branch-free fp64 accumulation: on one compute unit the conversions and
 // adds cost as much as the loads.
-template <bool OFF>
+template <bool OFF, bool LOGITS>
 __device__ __forceinline__ void slice_pass(const float *__restrict__ pu,
                                            const uint32_t *__restrict__ bits_b, int V, Slices sl,
-                                           bool vec, double *s_wsum)
+                                           bool vec, const TRow<LOGITS> &tv, double *s_wsum)
 {
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int64_t a = sl.lo(wave, V), e = sl.hi(wave, V);
@@ -213,7 +251,7 @@ __device__ __forceinline__ void slice_pass(const float *__restrict__ pu,
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int64_t y0 = y00 + 4 * kWave * k;
-            load4(pu, y0, e, V, vec, v[k]);
+            load4(pu, y0, e, V, vec, tv, v[k]);
             if (OFF)
                 wd[k] = bits_b[min(y0, (int64_t)V - 1) >> 5];
         }
@@ -233,11 +271,12 @@ __device__ __forceinline__ void slice_pass(const float *__restrict__ pu,
 
 // R <- max(0, R - P q_c) over the shortlist (R read as p_u at the listed
 // ids when fresh; ids outside [0, V) carry no mass); returns sum R.
+template <bool LOGITS>
 __device__ __forceinline__ double residual_update(const float *__restrict__ pu,
                                                   const int32_t *__restrict__ S,
                                                   const float *__restrict__ qc, int len, int V,
                                                   bool fresh, double P, double *__restrict__ R,
-                                                  double *sh)
+                                                  const TRow<LOGITS> &tv, double *sh)
 {
     constexpr int U = 16;
     double acc = 0.0;
@@ -253,7 +292,7 @@ __device__ __forceinline__ double residual_update(const float *__restrict__ pu,
                 const int32_t y = S[j];
                 const bool ok = y >= 0 && y < V;
                 const float t = pu[ok ? y : 0];
-                r[k] = ok ? (double)t : 0.0;
+                r[k] = ok ? (double)tv(t) : 0.0;
             } else {
                 r[k] = R[j];
             }
@@ -275,14 +314,16 @@ __device__ __forceinline__ double residual_update(const float *__restrict__ pu,
 // Weights of the four tokens y0 .. y0+3 (zero at or beyond lim) in the
 // final draw: the target off the shortlist, R on it (p_u everywhere when
 // fresh).
+template <bool LOGITS>
 __device__ __forceinline__ void draw_weights(const float *__restrict__ pu,
                                              const uint32_t *__restrict__ bits_b,
                                              const uint32_t *__restrict__ rank_b,
                                              const double *__restrict__ R, int len, int64_t y0,
-                                             int64_t lim, int V, bool vec, bool fresh, double w[4])
+                                             int64_t lim, int V, bool vec, bool fresh,
+                                             const TRow<LOGITS> &tv, double w[4])
 {
     float v[4];
-    load4(pu, y0, lim, V, vec, v);
+    load4(pu, y0, lim, V, vec, tv, v);
     if (fresh) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -429,13 +470,17 @@ __device__ __forceinline__ double root_R(double pv, float q1v, float q2v, int k,
 // PASS 1: off, sp, s1 per chunk; PASS 2: s2 per chunk (two children only)
 constexpr int kRootMaxChunks = 256;  // V <= 2^20
 
-template <int PASS>
+template <int PASS, bool LOGITS>
 __global__ __launch_bounds__(kRootThreads) void root_pass_kernel(
     int m, int V, int64_t max_len, const int32_t *__restrict__ parent,
     const int64_t *__restrict__ sl_off, const float *__restrict__ q,
-    const float *__restrict__ p, const uint32_t *__restrict__ bits,
-    const uint32_t *__restrict__ rank, RootPart *__restrict__ part)
+    const float *__restrict__ p, const float *__restrict__ nM, const double *__restrict__ nZ,
+    const uint32_t *__restrict__ bits, const uint32_t *__restrict__ rank,
+    RootPart *__restrict__ part)
 {
+    __shared__ double tab[LOGITS ? 64 : 1];
+    if (LOGITS)
+        fill_exp2_table(tab);  // ordered by the barriers in root_kids
     __shared__ uint32_t mem[kRootChunk / 32];
     __shared__ float q1d[kRootChunk], q2d[PASS == 2 ? kRootChunk : 1];
     __shared__ RootPart s_part[PASS == 2 ? kRootMaxChunks : 1];
@@ -464,6 +509,8 @@ __global__ __launch_bounds__(kRootThreads) void root_pass_kernel(
                  qrow + (int64_t)(c1 - 1) * len,
                  PASS == 2 ? qrow + (int64_t)(c2 - 1) * len : nullptr, mem, q1d, q2d);
     const float *pu = p + (int64_t)b * (m + 1) * V;
+    const int64_t r0 = (int64_t)b * (m + 1);
+    const TRow<LOGITS> tv{LOGITS ? nM[r0] : 0.f, LOGITS ? nZ[r0] : 0.0, tab};
     double a0 = 0.0, a1 = 0.0, a2 = 0.0;
 #pragma unroll
     for (int kk = 0; kk < kRootChunk / (4 * kRootThreads); ++kk) {
@@ -472,7 +519,7 @@ __global__ __launch_bounds__(kRootThreads) void root_pass_kernel(
         for (int e = 0; e < 4; ++e) {
             const int o = o0 + e;
             const int64_t y = base + o;
-            const double pv = y < V ? (double)pu[y] : 0.0;
+            const double pv = y < V ? (double)tv(pu[y]) : 0.0;
             const bool in = y < V && ((mem[o >> 5] >> (o & 31)) & 1u);
             if (PASS == 1) {
                 a0 += in ? 0.0 : pv;
@@ -499,10 +546,12 @@ __global__ __launch_bounds__(kRootThreads) void root_pass_kernel(
     }
 }
 
+template <bool LOGITS>
 __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
     int m, int V, int64_t max_len, bool vec, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ token, const int64_t *__restrict__ sl_off,
     const int32_t *__restrict__ sl_ids, const float *__restrict__ q, const float *__restrict__ p,
+    const float *__restrict__ nM, const double *__restrict__ nZ,
     const float *__restrict__ u_acc, const float *__restrict__ u_fin,
     const uint32_t *__restrict__ bits, const uint32_t *__restrict__ rank,
     const RootPart *__restrict__ rpart, double *__restrict__ Rws, int32_t *__restrict__ n_acc,
@@ -516,8 +565,18 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
     __shared__ uint32_t s_mem[kRootChunk / 32];
     __shared__ float s_q1[kRootChunk], s_q2[kRootChunk];
     __shared__ RootPart s_part[kRootMaxChunks];
+    __shared__ double tab[LOGITS ? 64 : 1];
 
     const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    if (LOGITS) {
+        fill_exp2_table(tab);
+        __syncthreads();
+    }
+    // target row u of this sequence and its value conversion
+    auto trow = [&](int u) {
+        const int64_t r = (int64_t)b * (m + 1) + u;
+        return TRow<LOGITS>{LOGITS ? nM[r] : 0.f, LOGITS ? nZ[r] : 0.0, tab};
+    };
     const int64_t nw = tree_words(V);
     const uint32_t *bits_b = bits + (int64_t)b * nw, *rank_b = rank + (int64_t)b * nw;
     double *R = Rws + (int64_t)b * max_len;
@@ -561,7 +620,9 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
         s_tok[i - 1] = x;
         s_pos[i - 1] = pos;
         s_lhs[i - 1] = (double)ua * qx;
-        s_px[i - 1] = (valid && linked) ? (double)p[((int64_t)b * (m + 1) + par) * V + x] : 0.0;
+        s_px[i - 1] = (valid && linked)
+                          ? (double)trow(par)(p[((int64_t)b * (m + 1) + par) * V + x])
+                          : 0.0;
     }
     __syncthreads();
 
@@ -636,13 +697,14 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
                              kr == 2 ? qrow + (int64_t)(c2 - 1) * len : nullptr, s_mem, s_q1,
                              s_q2);
                 const float *pu = p + (int64_t)b * (m + 1) * V;
+                const TRow<LOGITS> tv0 = trow(0);
                 constexpr int TPT = kRootChunk / kTreeThreads;  // 8 consecutive tokens
                 double w[TPT], mine = 0.0;
 #pragma unroll
                 for (int e = 0; e < TPT; ++e) {
                     const int o = TPT * tid + e;
                     const int64_t y = cb + o;
-                    const double pv = y < V ? (double)pu[y] : 0.0;
+                    const double pv = y < V ? (double)tv0(pu[y]) : 0.0;
                     const bool in = y < V && ((s_mem[o >> 5] >> (o & 31)) & 1u);
                     w[e] = (!ffin && in) ? root_R(pv, s_q1[o], kr == 2 ? s_q2[o] : 0.f, kr, fresh1, P1)
                                          : pv;
@@ -681,6 +743,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
     }
     for (int visit = 0; visit <= m; ++visit) {  // u increases on every acceptance
         const float *pu = p + ((int64_t)b * (m + 1) + u) * V;
+        const TRow<LOGITS> tv = trow(u);
         bool fresh = true, have_off = false;
         double P = 1.0, Poff = 0.0;
         int acc = -1;
@@ -696,7 +759,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
                 break;
             }
             if (!have_off) {
-                slice_pass<true>(pu, bits_b, V, sl, vec, s_woff);
+                slice_pass<true>(pu, bits_b, V, sl, vec, tv, s_woff);
                 __syncthreads();  // (also orders this test's reads of R)
                 Poff = 0.0;
 #pragma unroll
@@ -707,7 +770,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
                 __syncthreads();  // every thread has read R for this test
             }
             const float *qc = q + (int64_t)m * off + (int64_t)(c - 1) * len;
-            const double sr = residual_update(pu, S, qc, len, V, fresh, P, R, sh);
+            const double sr = residual_update(pu, S, qc, len, V, fresh, P, R, tv, sh);
             const double Pn = Poff + sr;
             if (Pn > 0.0) {
                 P = Pn;
@@ -730,7 +793,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
         // final draw from r over all V (inverse CDF): slice totals, the
         // owning slice, the owning thread's segment of it, its token
         if (fresh) {  // r is p_u: slice totals of the row
-            slice_pass<false>(pu, bits_b, V, sl, vec, s_wt);
+            slice_pass<false>(pu, bits_b, V, sl, vec, tv, s_wt);
         } else {  // wave w adds R over the listed ids of its slice
             const int j0 = rank_at(rank_b, sl.lo(wave, V), V, rank_end);
             const int j1 = rank_at(rank_b, sl.hi(wave, V), V, rank_end);
@@ -790,7 +853,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
                 for (int k = 0; k < G; ++k) {
                     const int64_t y0 = a + (int64_t)(g + k) * 4 * kWave + 4 * lane;
                     draw_weights(pu, bits_b, rank_b, R, len, y0, g + k < r1 ? e : 0, V, vec,
-                                 fresh, w[k]);
+                                 fresh, tv, w[k]);
                 }
 #pragma unroll
                 for (int k = 0; k < G; ++k)
@@ -821,7 +884,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
                     for (int k = 0; k < G; ++k) {
                         const int64_t y0 = a + (int64_t)(g + k) * 4 * kWave + 4 * lane;
                         draw_weights(pu, bits_b, rank_b, R, len, y0, g + k < r1 ? e : 0, V, vec,
-                                     fresh, w[k]);
+                                     fresh, tv, w[k]);
                     }
 #pragma unroll
                     for (int k = 0; k < G; ++k)
@@ -838,7 +901,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
                 for (int r = rw0; r < rw1; ++r) {
                     const int64_t y0 = a + (int64_t)r * 4 * kWave + 4 * lane;
                     double w[4];
-                    draw_weights(pu, bits_b, rank_b, R, len, y0, e, V, vec, fresh, w);
+                    draw_weights(pu, bits_b, rank_b, R, len, y0, e, V, vec, fresh, tv, w);
                     const double lsum = ((w[0] + w[1]) + w[2]) + w[3];
                     const double incl = wave_incl_scan_f64(lsum);
                     double part = run + (incl - lsum);
@@ -882,11 +945,14 @@ size_t verify_tree_ws_bytes(int B, int m, int V, int64_t max_len)
     return tree_R_bytes(B, max_len) + 2 * tree_bits_bytes(B, V) + root_part_bytes(B, V) + 256;
 }
 
-hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
-                              const int32_t *token, const int64_t *sl_off, const int32_t *sl_ids,
-                              const float *q, const float *p, const float *u_acc,
-                              const float *u_fin, int64_t max_len, int32_t *n_acc, int32_t *out,
-                              int32_t *path, void *ws, hipEvent_t t0, hipEvent_t t1)
+namespace {
+
+template <bool LOGITS>
+hipError_t tree_kernels(hipStream_t s, int B, int m, int V, const int32_t *parent,
+                        const int32_t *token, const int64_t *sl_off, const int32_t *sl_ids,
+                        const float *q, const float *x, const float *nM, const double *nZ,
+                        const float *u_acc, const float *u_fin, int64_t max_len, int32_t *n_acc,
+                        int32_t *out, int32_t *path, void *ws, hipEvent_t t0, hipEvent_t t1)
 {
     char *base = reinterpret_cast<char *>(ws);
     double *R = reinterpret_cast<double *>(base);
@@ -896,25 +962,74 @@ hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t 
     RootPart *rpart = reinterpret_cast<RootPart *>(base + tree_R_bytes(B, max_len) +
                                                    2 * tree_bits_bytes(B, V));
     const int bx = (V + kBitsTokens - 1) / kBitsTokens;
-    const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+    const bool vec = V % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
     hipError_t e = launch_timed(tree_bits_kernel, dim3((unsigned)bx, (unsigned)B),
                                 dim3(kBitsThreads), s, t0, nullptr, V, max_len, sl_off, sl_ids,
                                 bits, rank);
     if (e != hipSuccess)
         return e;
     const dim3 rgrid((unsigned)root_chunks(V), (unsigned)B);
-    hipLaunchKernelGGL(root_pass_kernel<1>, rgrid, dim3(kRootThreads), 0, s, m, V, max_len, parent,
-                       sl_off, q, p, (const uint32_t *)bits, (const uint32_t *)rank, rpart);
+    hipLaunchKernelGGL((root_pass_kernel<1, LOGITS>), rgrid, dim3(kRootThreads), 0, s, m, V,
+                       max_len, parent, sl_off, q, x, nM, nZ, (const uint32_t *)bits,
+                       (const uint32_t *)rank, rpart);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(root_pass_kernel<2>, rgrid, dim3(kRootThreads), 0, s, m, V, max_len, parent,
-                       sl_off, q, p, (const uint32_t *)bits, (const uint32_t *)rank, rpart);
+    hipLaunchKernelGGL((root_pass_kernel<2, LOGITS>), rgrid, dim3(kRootThreads), 0, s, m, V,
+                       max_len, parent, sl_off, q, x, nM, nZ, (const uint32_t *)bits,
+                       (const uint32_t *)rank, rpart);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    return launch_timed(verify_tree_kernel, dim3((unsigned)B), dim3(kTreeThreads), s, nullptr, t1,
-                        m, V, max_len, vec, parent, token, sl_off, sl_ids, q, p, u_acc, u_fin,
-                        (const uint32_t *)bits, (const uint32_t *)rank, (const RootPart *)rpart, R,
-                        n_acc, out, path);
+    return launch_timed(verify_tree_kernel<LOGITS>, dim3((unsigned)B), dim3(kTreeThreads), s,
+                        nullptr, t1, m, V, max_len, vec, parent, token, sl_off, sl_ids, q, x, nM,
+                        nZ, u_acc, u_fin, (const uint32_t *)bits, (const uint32_t *)rank,
+                        (const RootPart *)rpart, R, n_acc, out, path);
+}
+
+}  // namespace
+
+hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
+                              const int32_t *token, const int64_t *sl_off, const int32_t *sl_ids,
+                              const float *q, const float *p, const float *u_acc,
+                              const float *u_fin, int64_t max_len, int32_t *n_acc, int32_t *out,
+                              int32_t *path, void *ws, hipEvent_t t0, hipEvent_t t1)
+{
+    return tree_kernels<false>(s, B, m, V, parent, token, sl_off, sl_ids, q, p, nullptr, nullptr,
+                               u_acc, u_fin, max_len, n_acc, out, path, ws, t0, t1);
+}
+
+// the tree workspace, the row normalisers, then the softmax statistics
+size_t verify_tree_logits_ws_bytes(int B, int m, int V, int64_t max_len)
+{
+    const size_t rows = (size_t)B * (m + 1);
+    return (verify_tree_ws_bytes(B, m, V, max_len) + 255) / 256 * 256 + rows * 8 +
+           (rows * 4 + 255) / 256 * 256 + softmax_ws_bytes((int64_t)rows, V);
+}
+
+hipError_t verify_tree_logits_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
+                                     const int32_t *token, const int64_t *sl_off,
+                                     const int32_t *sl_ids, const float *q, const float *logits,
+                                     const float *u_acc, const float *u_fin, int64_t max_len,
+                                     int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
+                                     hipEvent_t t0, hipEvent_t t1)
+{
+    const int rows = B * (m + 1);
+    char *b = reinterpret_cast<char *>(ws) + (verify_tree_ws_bytes(B, m, V, max_len) + 255) /
+                                                 256 * 256;
+    double *nZ = reinterpret_cast<double *>(b);
+    float *nM = reinterpret_cast<float *>(b + (size_t)rows * 8);
+    char *sws = b + (size_t)rows * 8 + ((size_t)rows * 4 + 255) / 256 * 256;
+    hipError_t e = softmax_stats_launch(s, rows, V, logits, sws);
+    if (e != hipSuccess)
+        return e;
+    const int64_t nseg = softmax_segments(V);
+    const double *ssum = reinterpret_cast<const double *>(sws);
+    const float *smax = reinterpret_cast<const float *>(ssum + (size_t)rows * nseg);
+    hipLaunchKernelGGL(tree_norms_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
+                       rows, nseg, smax, ssum, nM, nZ);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    return tree_kernels<true>(s, B, m, V, parent, token, sl_off, sl_ids, q, logits, nM, nZ,
+                              u_acc, u_fin, max_len, n_acc, out, path, ws, t0, t1);
 }
 
 }  // namespace ds

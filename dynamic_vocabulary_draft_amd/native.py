@@ -89,6 +89,9 @@ _SIGS = {
                                      _vp, _sz]),
     "ds_verify_reject_noalloc": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp]),
+    "ds_verify_tree_logits_workspace_bytes": (_sz, [_i, _i, _i, _i64]),
+    "ds_verify_tree_logits": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _i64, _vp, _vp, _vp, _vp, _sz]),
     "ds_verify_tree_workspace_bytes": (_sz, [_i, _i, _i, _i64]),
     "ds_verify_tree": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp,
                             _vp, _vp, _vp, _sz]),
@@ -398,6 +401,21 @@ def verify_tree(parent, token, sl_off, sl_ids, q, p, u_acc, u_fin, max_len, n_ac
     V = p.shape[-1]
     _check("ds_verify_tree", lib.ds_verify_tree(
         _s(stream), B, m, V, _p(parent), _p(token), _p(sl_off), _p(sl_ids), _p(q), _p(p),
+        _p(u_acc), _p(u_fin), int(max_len), _p(n_acc), _p(out), _p(path), _p(ws),
+        _nbytes(ws)))
+
+
+def verify_tree_logits_workspace_bytes(B: int, m: int, V: int, max_len: int) -> int:
+    return int(lib.ds_verify_tree_logits_workspace_bytes(B, m, V, max_len))
+
+
+def verify_tree_logits(parent, token, sl_off, sl_ids, q, logits, u_acc, u_fin, max_len, n_acc,
+                       out, path, ws, *, stream=None):
+    """verify_tree from target logits [B][m+1][V]."""
+    B, m = parent.shape
+    V = logits.shape[-1]
+    _check("ds_verify_tree_logits", lib.ds_verify_tree_logits(
+        _s(stream), B, m, V, _p(parent), _p(token), _p(sl_off), _p(sl_ids), _p(q), _p(logits),
         _p(u_acc), _p(u_fin), int(max_len), _p(n_acc), _p(out), _p(path), _p(ws),
         _nbytes(ws)))
 

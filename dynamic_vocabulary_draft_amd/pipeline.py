@@ -7,8 +7,8 @@
       logits) on the head stream;
   trees (B sequences x m nodes sharing one shortlist): router, select and
       build for the B roots, then one gathered head with m rows per group and
-      one sample per node, then ds_target_softmax over the m+1 nodes and
-      ds_verify_tree.
+      one sample per node, then ds_verify_tree_logits (from the target
+      logits of the m+1 nodes).
 PyTorch only allocates memory and provides the streams.
 """
 from __future__ import annotations
@@ -109,7 +109,7 @@ class DraftStep:
                 self.parent = dev(wl.parent)
                 self.path = torch.empty(B, m, **i32)
                 self.verify_ws = N.workspace(
-                    N.verify_tree_workspace_bytes(B, m, V, int(self.max_len[0])), device)
+                    N.verify_tree_logits_workspace_bytes(B, m, V, int(self.max_len[0])), device)
             else:
                 self.verify_ws = N.workspace(N.verify_logits_workspace_bytes(B, T, V), device)
         self._events = None
@@ -188,20 +188,19 @@ class DraftStep:
 
     def verify(self, stream=None) -> None:
         if self.cfg.is_tree:
-            N.target_softmax(self.target_logits, self.p, self.softmax_ws, stream=stream)
-            N.verify_tree(self.parent, self.token, self.sl_off, self.sl_ids, self.q, self.p,
-                          self.u_acc, self.u_fin, int(self.max_len[0]), self.n_acc, self.out,
-                          self.path, self.verify_ws, stream=stream)
+            N.verify_tree_logits(self.parent, self.token, self.sl_off, self.sl_ids, self.q,
+                                 self.target_logits, self.u_acc, self.u_fin,
+                                 int(self.max_len[0]), self.n_acc, self.out, self.path,
+                                 self.verify_ws, stream=stream)
             return
         N.verify_reject_logits(self.token, self.sl_off, self.sl_ids, self.q, self.target_logits,
                                self.u_acc, self.u_fin, self.n_acc, self.out, self.verify_ws,
                                stream=stream)
 
     def target_probs(self) -> torch.Tensor:
-        """The target probabilities the verification used (chains verify
-        from logits and write none: computed here, for inspection)."""
-        if not self.cfg.is_tree:
-            N.target_softmax(self.target_logits, self.p, self.softmax_ws)
+        """The target probabilities the verification used (it works from the
+        logits and writes none: computed here, for inspection)."""
+        N.target_softmax(self.target_logits, self.p, self.softmax_ws)
         return self.p
 
     def step(self, stream=None) -> None:

@@ -389,6 +389,24 @@ ds_status ds_verify_tree(hipStream_t s, int B, int m, int V, const int32_t *pare
                          size_t ws_bytes);
 
 /*
+ * ds_verify_tree from the target's logits instead of its probabilities
+ * [same passages as ds_verify_tree].  logits [B][m+1][V] fp32; every target
+ * value the walk reads is the one ds_target_softmax would write for that
+ * row (the same segment statistics, row normaliser and rounding), so the
+ * outputs equal ds_target_softmax followed by ds_verify_tree, bit for bit,
+ * without writing or reading the B*(m+1)*V probabilities.  Limits as
+ * ds_verify_tree, and B*(m+1) <= 65535 (else DS_ESHAPE).
+ * ws >= ds_verify_tree_logits_workspace_bytes(B, m, V, max_len) bytes.
+ */
+size_t ds_verify_tree_logits_workspace_bytes(int B, int m, int V, int64_t max_len);
+ds_status ds_verify_tree_logits(hipStream_t s, int B, int m, int V, const int32_t *parent,
+                                const int32_t *token, const int64_t *sl_off,
+                                const int32_t *sl_ids, const float *q, const float *logits,
+                                const float *u_acc, const float *u_fin, int64_t max_len,
+                                int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
+                                size_t ws_bytes);
+
+/*
  * Dense LM head of the full drafter over every token, the O(|V| d)
  * projection the shortlist avoids [S "Comparison to Prior Work": EAGLE's
  * O(|V| d) head; "Modeling": the full drafter whose top-L gives the

@@ -224,3 +224,54 @@ def test_verify_tree_qwen3_shape(N, oracle_lib):
         n_ref = _check(oracle_lib, c, _run(N, c), min_clean=2)
         if mode == "first":
             assert n_ref.max() >= 3
+
+
+def _run_logits(N, c, tl, max_len=None):
+    """ds_verify_tree_logits on target logits tl [B][m+1][V]."""
+    B, m = c["parent"].shape
+    V = tl.shape[-1]
+    lens = np.diff(c["sl_off"])
+    max_len = int(max(1, lens.max())) if max_len is None else max_len
+    dv = {k: to_dev(np.asarray(v)) for k, v in c.items() if k != "p"}
+    if dv["sl_ids"].numel() == 0:
+        dv["sl_ids"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if dv["q"].numel() == 0:
+        dv["q"] = torch.zeros(1, dtype=torch.float32, device="cuda")
+    n_acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((B, m + 1), -7, dtype=torch.int32, device="cuda")
+    path = torch.full((B, m), -7, dtype=torch.int32, device="cuda")
+    ws = N.workspace(N.verify_tree_logits_workspace_bytes(B, m, V, max_len))
+    ws.fill_(0x5A)  # no initialisation is needed
+    N.verify_tree_logits(dv["parent"], dv["token"], dv["sl_off"], dv["sl_ids"], dv["q"],
+                         to_dev(tl), dv["u_acc"], dv["u_fin"], max_len, n_acc, out, path, ws)
+    torch.cuda.synchronize()
+    return n_acc.cpu().numpy(), out.cpu().numpy(), path.cpu().numpy()
+
+
+@pytest.mark.parametrize("V,m,B,lens,topo,mode", [
+    (5000, 24, 6, [700, 1, 0, 2500, 4999, 1200], "random", "correlated"),
+    (5000, 24, 6, [700, 1, 0, 2500, 4999, 1200], "star", "random"),
+    (3001, 12, 4, [300, 2999, 17, 1000], "chain", "first"),
+    (151936, 64, 3, [24576, 24000, 25000], "binary", "first"),
+    (151936, 64, 3, [24576, 24000, 25000], "binary", "correlated"),
+])
+def test_verify_tree_logits_parity(N, oracle_lib, V, m, B, lens, topo, mode):
+    """Tree verification from target logits: the same outputs as the target
+    softmax followed by verification over its probabilities (bit for bit,
+    every sequence: the same target values are computed), and the oracle's
+    verification over those probabilities outside its tie flags.  The
+    logits are the logs of the case's target rows, so walks go as deep."""
+    c = _tree_case(V, m, B, seed=V + m + len(mode), lens=lens, topo=topo, mode=mode)
+    tl = np.log(np.maximum(c["p"].astype(np.float64), 1e-30)).astype(np.float32)
+    tl[0, 0, :7] = -np.inf  # tokens the target rules out
+    rows = B * (m + 1)
+    p = torch.empty(B, m + 1, V, device="cuda")
+    N.target_softmax(to_dev(tl), p, N.workspace(N.softmax_workspace_bytes(rows, V)))
+    c["p"] = p.cpu().numpy()
+    ref = _run(N, c)
+    got = _run_logits(N, c, tl)
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a, b)
+    n_ref = _check(oracle_lib, c, got, min_clean=max(1, B - 2))
+    if mode == "first":
+        assert n_ref.max() >= 2

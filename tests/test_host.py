@@ -158,6 +158,18 @@ def test_select_build_head_sample_verify_reject_bad_arguments(N):
     assert L.ds_verify_reject_logits(*ver(B=2048, T=32, ws_bytes=1 << 40)) == 3
     assert L.ds_verify_reject_logits(*ver()) == 1  # workspace too small
     assert N.verify_logits_workspace_bytes(2, 3, 100) >= N.verify_workspace_bytes(2, 3, 100) + 8 * 12
+    # tree verification from logits: argument and shape checks
+    tv = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
+        ("s", None), ("B", 2), ("m", 3), ("V", 100), ("parent", FAKE), ("token", FAKE),
+        ("sl_off", FAKE), ("sl_ids", FAKE), ("q", FAKE), ("logits", FAKE), ("u_acc", FAKE),
+        ("u_fin", FAKE), ("max_len", 50), ("n_acc", FAKE), ("out", FAKE), ("path", FAKE),
+        ("ws", FAKE), ("ws_bytes", 0)]]
+    assert L.ds_verify_tree_logits(*tv(logits=None)) == 1
+    assert L.ds_verify_tree_logits(*tv(m=0)) == 1
+    assert L.ds_verify_tree_logits(*tv(B=2048, m=64, ws_bytes=1 << 40)) == 3  # B*(m+1) rows
+    assert L.ds_verify_tree_logits(*tv()) == 1  # workspace too small
+    assert (N.verify_tree_logits_workspace_bytes(2, 3, 100, 50)
+            > N.verify_tree_workspace_bytes(2, 3, 100, 50))
     assert L.ds_draft_chain(None, None, None) == 1
     a = N.ChainArgs(B=0, T=6)
     assert L.ds_draft_chain(None, None, C.byref(a)) == 1
