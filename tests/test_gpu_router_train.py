@@ -154,10 +154,11 @@ def test_router_train_step(N, oracle_lib, shape, act, h_bf16):
         assert np.array_equal(g2[k], g[k]) and np.array_equal(p2[k], p[k])
 
 
-@pytest.mark.parametrize("V,d,n", [(5000, 256, 37), (20011, 1024, 300), (1000, 64, 1)])
+@pytest.mark.parametrize("V,d,n", [(5000, 256, 37), (20011, 1024, 300), (1000, 64, 1),
+                                   (3000, 192, 40)])
 def test_dense_lm_head_parity(N, oracle_lib, V, d, n):
     """The dense head over all V against the oracle (bf16 bar 2e-2), on
-    ragged row and column tiles."""
+    ragged row and column tiles and one to sixteen 64-wide slices."""
     g = np.random.default_rng(V + n)
     W = syn.f32_to_bf16_bits((g.standard_normal((V, d)) * 0.05).astype(np.float32))
     h = syn.f32_to_bf16_bits(g.standard_normal((n, d)).astype(np.float32))
