@@ -624,20 +624,33 @@ __device__ __forceinline__ void gathered_tile(rsrc_t w, int V, int d, int m, int
 // overshoots by up to one cluster: 24.6K to 51K entries on the Qwen-shaped
 // 8-tree workload), so a fixed number of workgroups per group would leave
 // the longest group's workgroups running alone.
-//   up to kTreeMixGroups groups: tile-index-major (tile t of every group
-//     that has one, in group order, then tile t+1): the groups walk their
-//     shortlists side by side, and while all G = 8 have tiles, group g stays
-//     on XCD g (its hidden rows in that L2).  Every workgroup rebuilds in
-//     LDS the tile counts and C(t) = the number of tiles before index t.
+//   up to kTreeMixGroups groups and kTreeMergeTiles tiles: merged by token
+//     id (the tiles of all groups ordered by the id of their first entry,
+//     ties to the lower group; each shortlist ascends, so this merges G
+//     sorted lists), the list cut into 8 slices of consecutive tiles, and
+//     slice x walked by the workgroups of XCD x.  Groups' shortlists
+//     overlap (the 8-tree workload's rows sit on 2.0 shortlists on average):
+//     a row that several groups share falls in one slice, and the tiles
+//     that read it run at about the same time on one XCD, so it is fetched
+//     from HBM once and then read from that XCD's L2.  Every workgroup
+//     rebuilds the order in LDS (each tile's rank: its index in its group
+//     plus binary searches in the other groups' first ids).
+//   else up to kTreeMixGroups groups: tile-index-major (tile t of every
+//     group that has one, in group order, then tile t+1): the groups walk
+//     their shortlists side by side.  Every workgroup rebuilds in LDS the
+//     tile counts and C(t) = the number of tiles before index t.
 //   up to kTreeLdsGroups groups: group-major (tile t of group g is entry
 //     tpre[g] + t, tpre = exclusive prefix of the tile counts, in LDS).
 //   above: each group keeps tiles_stride workgroups of its own.
 // Measured on the 8-tree workload (mean over four input instances): a fixed
 // share of workgroups per group 436 us, group-major 424 us, tile-index-major
-// 373 us.
+// 373 us (338 us later); merged with XCD slices 301 us and 1.17 GB fetched
+// per launch against 1.93 GB (the same merged order dealt round-robin over
+// the XCDs: 349 us, 2.02 GB).
 constexpr int kTreeMixGroups = 64;
 constexpr int kTreeMixTiles = 4096;  // tile indices covered by C in LDS
 constexpr int kTreeLdsGroups = 4096;
+constexpr int kTreeMergeTiles = 4096;  // tiles of all groups in the merged order
 
 template <int NB, int WV>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) void head_gathered_kernel(int V, int d, const uint16_t *__restrict__ W,
@@ -659,6 +672,91 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
     uint16_t *lds = lds_all, *lds_a = lds_all + NB * 32 * lds_row<NB>();
     const int mm = min(m - n0, NB * 32);  // head rows n0 .. n0+mm-1 in this pass
     const rsrc_t w = make_rsrc(W, (uint32_t)((int64_t)V * d * 2));  // V*d*2 < 4 GiB
+    if (G <= kTreeMixGroups) {  // block-uniform: the merged order when it applies
+        __shared__ int32_t s_mpre[kTreeMixGroups + 1];  // exclusive prefix of tile counts
+        __shared__ int32_t s_f[kTreeMergeTiles];        // first token id of every tile
+        if (threadIdx.x == 0) {
+            int32_t run = 0;
+            for (int g = 0; g < G; ++g) {
+                s_mpre[g] = run;
+                const int64_t len = sl_off[g + 1] - sl_off[g];
+                const int64_t c = len > 0 ? (len + kTileRows - 1) / kTileRows : 0;
+                run = (int32_t)min((int64_t)run + c, (int64_t)kTreeMergeTiles + 1);
+            }
+            s_mpre[G] = run;
+        }
+        __syncthreads();
+        const int total = s_mpre[G];
+        if (total <= kTreeMergeTiles) {
+            auto group_of = [&](int i) {  // group of tile i: last g with s_mpre[g] <= i
+                int lo = 0, hi = G;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_mpre[mid] <= i)
+                        lo = mid;
+                    else
+                        hi = mid;
+                }
+                return lo;
+            };
+            for (int i = threadIdx.x; i < total; i += NT) {
+                const int g = group_of(i);
+                s_f[i] = sl_ids[sl_off[g] + (int64_t)(i - s_mpre[g]) * kTileRows];
+            }
+            __syncthreads();
+            // the merge needs each group's first ids strictly increasing (a
+            // shortlist in ascending token order); else the tile-index order
+            int bad = 0;
+            for (int i = threadIdx.x; i < total; i += NT) {
+                const int g = group_of(i);
+                bad |= i > s_mpre[g] && s_f[i - 1] >= s_f[i];
+            }
+            if (!__syncthreads_or(bad)) {
+                // rank of tile (g, t): t plus, for every other group h, its
+                // tiles with a smaller first id (ties: lower group first)
+                int32_t *s_ord = s_tpre;
+                for (int i = threadIdx.x; i < total; i += NT) {
+                    const int g = group_of(i);
+                    const int32_t f = s_f[i];
+                    int rank = i - s_mpre[g];
+                    for (int hg = 0; hg < G; ++hg) {
+                        if (hg == g)
+                            continue;
+                        int lo = s_mpre[hg], hi = s_mpre[hg + 1];
+                        while (lo < hi) {
+                            const int mid = (lo + hi) >> 1;
+                            const int32_t fm = s_f[mid];
+                            if (fm < f || (hg < g && fm == f))
+                                lo = mid + 1;
+                            else
+                                hi = mid;
+                        }
+                        rank += lo - s_mpre[hg];
+                    }
+                    s_ord[rank] = i;
+                }
+                __syncthreads();
+                // XCD x (blocks b with b % 8 == x, dealt round-robin) walks
+                // slice x of the merged list: the groups' tiles over one
+                // eighth of the token ids, so a row that several groups
+                // share is fetched once into that XCD's L2
+                const int b = blockIdx.x, nb = gridDim.x;
+                int64_t k0 = b, k1 = total, ks = nb;
+                if (nb % 8 == 0) {
+                    const int x = b % 8;
+                    k0 = (int64_t)x * total / 8 + b / 8;
+                    k1 = (int64_t)(x + 1) * total / 8;
+                    ks = nb / 8;
+                }
+                for (int64_t k = k0; k < k1; k += ks) {
+                    const int i = s_ord[k], g = group_of(i);
+                    gathered_tile<NB, WV>(w, V, d, m, n0, mm, h, ldh_g, sl_off, sl_ids, logits,
+                                          lds, lds_a, g, i - s_mpre[g]);
+                }
+                return;
+            }
+        }
+    }
     if (G <= kTreeMixGroups) {  // block-uniform; s_tpre holds C(t), then the tile counts
         int32_t *s_cnt = s_tpre + kTreeMixTiles + 1;
         __shared__ int s_tmax;
@@ -1048,7 +1146,10 @@ hipError_t gathered_passes(hipStream_t s, int V, int d, const uint16_t *Wb, int 
     const int64_t slots = (8 / WV) * (int64_t)device_cu_count();
     int64_t per_group = (max_rows + tile_rows<WV>() - 1) / tile_rows<WV>();
     int64_t blocks;
-    if (G <= kTreeLdsGroups) {  // one list of all groups' tiles: at most this many
+    if (G <= kTreeMixGroups) {  // the merged list: every compute unit (XCD slices when a multiple of 8)
+        blocks = slots;
+        per_group = 1;  // unused
+    } else if (G <= kTreeLdsGroups) {  // one list of all groups' tiles: at most this many
         blocks = per_group + G;
         if (blocks > slots)
             blocks = slots;
