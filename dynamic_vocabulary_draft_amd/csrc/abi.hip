@@ -553,6 +553,15 @@ ds_status ds_router_train_step(hipStream_t s, const ds_router_train_args *a)
         a->W1, a->b1, a->W2, a->b2, a->dW1, a->db1, a->dW2, a->db2, a->loss, a->ws));
 }
 
+// batched chains with a one-pass second router layer: two slots (positions
+// alternate) for that layer's window partials, which the selection adds up
+static size_t chain_part_bytes(int B, int r)
+{
+    return B >= ds::kRouterMfmaMin && B <= ds::kRouterPassCols
+               ? 2 * round_up(ds::router_l1_ws_bytes(r), 256)
+               : 0;
+}
+
 size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r, int64_t max_len)
 {
     if (B <= 0 || T <= 0 || V <= 0 || r <= 0 || max_len <= 0)
@@ -562,7 +571,7 @@ size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r, int64_t max_le
     const size_t tix = B >= ds::kUnionMinGroups ? 2 * round_up(ds::tile_index_bytes(B, V), 256) : 0;
     return round_up(ds_router_workspace_bytes(B, r), 256) +
            round_up(ds::build_ws_bytes(B, V), 256) + round_up(ds::sample_ws_bytes(B, max_len), 256) +
-           tix;
+           tix + chain_part_bytes(B, r);
 }
 
 ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_args *a)
@@ -630,16 +639,34 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
     hipError_t err = hipEventRecord(fork, hs);
     if (err == hipSuccess)
         err = hipStreamWaitEvent(rs, fork, 0);
+    // batched: the second router layer stops at its window partials (slot
+    // t % 2) and the selection on router_stream adds them up, so its finish
+    // leaves head_stream; slot t % 2 is rewritten by router t + 2, which
+    // head_stream runs after waiting for build t
+    const bool split = prebuilt && chain_part_bytes(B, a->r) > 0 &&
+                       ds::router_split_applies(bf16, B, a->r, a->M);
+    const size_t pslot = round_up(ds::router_l1_ws_bytes(a->r), 256);
+    float *part2 = reinterpret_cast<float *>(tws + (prebuilt ? 2 * tslot : 0));
+    const int nwin2 = split ? ds::router_l2_windows(a->r, a->M) : 0;
     auto router_at = [&](hipStream_t st, int t) {  // router layers of position t (reads h[:, t])
         const int64_t rb = (int64_t)t * B;
+        if (split)
+            return ds::router_launch_split(st, B, a->d, a->r, a->M, a->act,
+                                           hb + (size_t)t * a->d * e, ldh, a->W1, a->b1, a->W2, z,
+                                           part2 + (t & 1) * (pslot / sizeof(float)));
         return ds::router_launch(st, bf16, B, a->d, a->r, a->M, a->act, hb + (size_t)t * a->d * e,
                                  ldh, a->W1, a->b1, a->W2, a->b2, a->scores + rb * a->M, z);
     };
     auto select_build_at = [&](hipStream_t st, int t) {
         const int64_t rb = (int64_t)t * B;
-        hipError_t r = ds::select_launch(st, B, a->M, a->scores + rb * a->M, a->cluster_size,
-                                         a->budget_kind, a->budget + rb, a->sel + rb * a->M,
-                                         a->n_sel + rb, a->sl_len + rb);
+        hipError_t r =
+            split ? ds::select_partials_launch(st, B, a->M, part2 + (t & 1) * (pslot / sizeof(float)),
+                                               nwin2, a->b2, a->scores + rb * a->M, a->cluster_size,
+                                               a->budget_kind, a->budget + rb, a->sel + rb * a->M,
+                                               a->n_sel + rb, a->sl_len + rb)
+                  : ds::select_launch(st, B, a->M, a->scores + rb * a->M, a->cluster_size,
+                                      a->budget_kind, a->budget + rb, a->sel + rb * a->M,
+                                      a->n_sel + rb, a->sl_len + rb);
         if (r == hipSuccess)
             r = ds::build_launch(st, B, a->M, a->V, a->sel + rb * a->M, a->n_sel + rb,
                                  a->cluster_of, a->cluster_index, a->capacity, a->sl_off + rb,

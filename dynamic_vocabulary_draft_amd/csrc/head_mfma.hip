@@ -875,7 +875,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
 // router_l1_finish adds the windows in order.  Passes run in stream order
 // and reuse part.
 constexpr int kRouterWin = 256;  // k-window (4 slices)
-constexpr int kRouterCols = 64;  // inputs per column pass
+constexpr int kRouterCols = kRouterPassCols;  // inputs per column pass
 constexpr int kRouterMaxWin = 8192 / kRouterWin;  // d <= 8192
 
 // part[c][row0 + i] = this workgroup's sums for input c and weight row i
@@ -1257,34 +1257,58 @@ static int router_l2_slices(int r, int M)
 
 bool router_l2_mfma_applies(int r, int M) { return router_l2_slices(r, M) > 0; }
 
+int router_l2_windows(int r, int M)
+{
+    const int nsw = router_l2_slices(r, M);
+    return nsw ? (r + nsw * kKs - 1) / (nsw * kKs) : 0;
+}
+
+// the second layer's window partials of column pass c0 into part
+static hipError_t router_l2_pass(hipStream_t s, int n, int r, int M, int nsw, const float *z,
+                                 const uint16_t *Wb, int c0, float *part)
+{
+    const dim3 grid((unsigned)((M + 127) / 128), (unsigned)router_l2_windows(r, M));
+    const int nc = n - c0 < kRouterCols ? n - c0 : kRouterCols;
+    if (nsw == 1) {
+        if (nc > 32)
+            hipLaunchKernelGGL((router_l2_kernel<2, 1>), grid, dim3(256), 0, s, n, r, M, Wb, z, c0,
+                               part);
+        else
+            hipLaunchKernelGGL((router_l2_kernel<1, 1>), grid, dim3(256), 0, s, n, r, M, Wb, z, c0,
+                               part);
+    } else {
+        if (nc > 32)
+            hipLaunchKernelGGL((router_l2_kernel<2, 2>), grid, dim3(256), 0, s, n, r, M, Wb, z, c0,
+                               part);
+        else
+            hipLaunchKernelGGL((router_l2_kernel<1, 2>), grid, dim3(256), 0, s, n, r, M, Wb, z, c0,
+                               part);
+    }
+    return hipGetLastError();
+}
+
+hipError_t router_l2_mfma_partials(hipStream_t s, int n, int r, int M, const void *z,
+                                   const void *W2, float *part)
+{
+    const int nsw = router_l2_slices(r, M);
+    if (nsw == 0 || n > kRouterCols)
+        return hipErrorInvalidValue;
+    return router_l2_pass(s, n, r, M, nsw, reinterpret_cast<const float *>(z),
+                          reinterpret_cast<const uint16_t *>(W2), 0, part);
+}
+
 hipError_t router_l2_mfma_launch(hipStream_t s, int n, int r, int M, const void *z_,
                                  const void *W2, const void *b2, float *scores, float *part)
 {
     const int nsw = router_l2_slices(r, M);
     if (nsw == 0)
         return hipErrorInvalidValue;
-    const int nwin = (r + nsw * kKs - 1) / (nsw * kKs);
-    const dim3 grid((unsigned)((M + 127) / 128), (unsigned)nwin);
+    const int nwin = router_l2_windows(r, M);
     const uint16_t *Wb = reinterpret_cast<const uint16_t *>(W2);
     const float *z = reinterpret_cast<const float *>(z_);
     for (int c0 = 0; c0 < n; c0 += kRouterCols) {
         const int nc = n - c0 < kRouterCols ? n - c0 : kRouterCols;
-        if (nsw == 1) {
-            if (nc > 32)
-                hipLaunchKernelGGL((router_l2_kernel<2, 1>), grid, dim3(256), 0, s, n, r, M, Wb, z,
-                                   c0, part);
-            else
-                hipLaunchKernelGGL((router_l2_kernel<1, 1>), grid, dim3(256), 0, s, n, r, M, Wb, z,
-                                   c0, part);
-        } else {
-            if (nc > 32)
-                hipLaunchKernelGGL((router_l2_kernel<2, 2>), grid, dim3(256), 0, s, n, r, M, Wb, z,
-                                   c0, part);
-            else
-                hipLaunchKernelGGL((router_l2_kernel<1, 2>), grid, dim3(256), 0, s, n, r, M, Wb, z,
-                                   c0, part);
-        }
-        hipError_t e = hipGetLastError();
+        hipError_t e = router_l2_pass(s, n, r, M, nsw, z, Wb, c0, part);
         if (e != hipSuccess)
             return e;
         const int64_t cnt = (int64_t)nc * M;

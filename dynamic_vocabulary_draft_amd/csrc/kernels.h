@@ -25,7 +25,33 @@ hipError_t router_l1_mfma_launch(hipStream_t s, int n, int d, int r, int act, co
 bool router_l2_mfma_applies(int r, int M);
 hipError_t router_l2_mfma_launch(hipStream_t s, int n, int r, int M, const void *z,
                                  const void *W2, const void *b2, float *scores, float *part);
+// inputs per column pass of the matrix-core router layers
+constexpr int kRouterPassCols = 64;
+// the second layer's k-windows (0: not on the matrix cores) and, for one
+// column pass (n <= kRouterPassCols), its window partials alone:
+// part[w][c][o] for window w < router_l2_windows(r, M), input c, score o
+// (row stride M, window stride kRouterPassCols * M); score o of input c is
+// then the sum over w in order, plus b2[o] -- what router_l2_mfma_launch's
+// finish computes
+int router_l2_windows(int r, int M);
+hipError_t router_l2_mfma_partials(hipStream_t s, int n, int r, int M, const void *z,
+                                   const void *W2, float *part);
+// the router up to the second layer's window partials (bf16, kRouterMfmaMin
+// <= n <= kRouterPassCols, second layer on the matrix cores): z as in
+// router_launch, the partials into part2 (router_l1_ws_bytes(r) bytes
+// suffice); select_partials_launch adds them up
+bool router_split_applies(bool bf16, int n, int r, int M);
+hipError_t router_launch_split(hipStream_t s, int n, int d, int r, int M, int act, const void *h,
+                               int64_t ldh, const void *W1, const void *b1, const void *W2,
+                               float *z, float *part2);
 
+// selection from the router's second-layer window partials (nwin windows,
+// layout of router_l2_mfma_partials, bias b2): every score is formed in the
+// order of router_l2_mfma_launch's finish, written to scores, and selected
+hipError_t select_partials_launch(hipStream_t s, int n, int M, const float *part, int nwin,
+                                  const void *b2, float *scores, const int32_t *cluster_size,
+                                  int kind, const int32_t *budget, int32_t *sel, int32_t *n_sel,
+                                  int32_t *sl_len);
 hipError_t select_launch(hipStream_t s, int n, int M, const float *scores,
                          const int32_t *cluster_size, int kind, const int32_t *budget,
                          int32_t *sel, int32_t *n_sel, int32_t *sl_len);

@@ -204,4 +204,30 @@ hipError_t router_launch(hipStream_t s, bool bf16, int n, int d, int r, int M, i
                 : launch_gemv<false, false>(s, n, r, M, W2, b2, z, r, 0, scores, M);
 }
 
+// the partials are read beside the batched head: only when they are small
+// (measured: 2 MB at 32 inputs, M = 1024 saved 10 us per step; 8 MB at 64
+// inputs, M = 2048 slowed the head beside them and cost 7 us)
+constexpr size_t kSplitMaxBytes = (size_t)2 << 20;
+
+bool router_split_applies(bool bf16, int n, int r, int M)
+{
+    const int nwin = router_l2_windows(r, M);
+    return bf16 && n >= kRouterMfmaMin && n <= kRouterPassCols && nwin > 0 &&
+           (size_t)nwin * (size_t)n * (size_t)M * sizeof(float) <= kSplitMaxBytes;
+}
+
+hipError_t router_launch_split(hipStream_t s, int n, int d, int r, int M, int act, const void *h,
+                               int64_t ldh, const void *W1, const void *b1, const void *W2,
+                               float *z, float *part2)
+{
+    if (!router_split_applies(true, n, r, M))
+        return hipErrorInvalidValue;
+    float *part = reinterpret_cast<float *>(
+        reinterpret_cast<char *>(z) + ((size_t)n * (size_t)r * sizeof(float) + 255) / 256 * 256);
+    hipError_t e = router_l1_mfma_launch(s, n, d, r, act, h, ldh, W1, b1, z, part);
+    if (e != hipSuccess)
+        return e;
+    return router_l2_mfma_partials(s, n, r, M, z, W2, part2);
+}
+
 }  // namespace ds

@@ -37,11 +37,16 @@ constexpr int kSelThreads = 1024;
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;  // 4 bins per thread
 
-template <int KPT>
+// PART: the scores are the router's second-layer window partials
+// wpart[w][row][idx] (nwin windows, window stride kRouterPassCols * M) added
+// in window order plus the bias, exactly as the router's finish adds them;
+// they are written to sc_out and selected from
+template <int KPT, bool PART>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
-    int M, const float *__restrict__ scores, const int32_t *__restrict__ cluster_size, int kind,
-    const int32_t *__restrict__ budget, int32_t *__restrict__ sel, int32_t *__restrict__ n_sel,
-    int32_t *__restrict__ sl_len)
+    int M, const float *__restrict__ scores, const float *__restrict__ wpart, int nwin,
+    const uint16_t *__restrict__ b2, float *__restrict__ sc_out,
+    const int32_t *__restrict__ cluster_size, int kind, const int32_t *__restrict__ budget,
+    int32_t *__restrict__ sel, int32_t *__restrict__ n_sel, int32_t *__restrict__ sl_len)
 {
     // weight histogram of one pass, then the taken keys
     __shared__ unsigned long long s_hw[kBins];
@@ -51,7 +56,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     __shared__ long long s_below;
     __shared__ unsigned long long s_kstar, s_tok;
     const int row = blockIdx.x, tid = threadIdx.x;
-    const float *s = scores + (int64_t)row * M;
+    const float *s = PART ? nullptr : scores + (int64_t)row * M;
     const bool tokens = kind != DS_BUDGET_CLUSTERS;
     uint64_t k[KPT];
     int64_t w[KPT];
@@ -59,7 +64,28 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     for (int i = 0; i < KPT; ++i) {
         const int idx = tid + i * kSelThreads;
         const bool in = idx < M;
-        k[i] = in ? ((uint64_t)(~ordered_bits(s[idx])) << 32) | (uint32_t)idx : ~0ull;
+        float sc = 0.f;
+        if (PART) {
+            if (in) {
+                const float *pp = wpart + (int64_t)row * M + idx;
+                for (int w0 = 0; w0 < nwin; w0 += 8) {  // eight loads in flight
+                    float v[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        v[j] = w0 + j < nwin ? pp[(int64_t)(w0 + j) * kRouterPassCols * M] : 0.f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (w0 + j < nwin)
+                            sc += v[j];
+                }
+                if (b2)
+                    sc += __uint_as_float((uint32_t)b2[idx] << 16);
+                sc_out[(int64_t)row * M + idx] = sc;
+            }
+        } else if (in) {
+            sc = s[idx];
+        }
+        k[i] = in ? ((uint64_t)(~ordered_bits(sc)) << 32) | (uint32_t)idx : ~0ull;
         w[i] = in ? (tokens ? (int64_t)max(cluster_size[idx], 0) : 1) : 0;
     }
     const int32_t bud = budget[row];
@@ -177,21 +203,44 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
 }  // namespace
 
+namespace {
+
+template <bool PART>
+hipError_t select_any(hipStream_t s, int n, int M, const float *scores, const float *part,
+                      int nwin, const uint16_t *b2, float *sc_out, const int32_t *cluster_size,
+                      int kind, const int32_t *budget, int32_t *sel, int32_t *n_sel,
+                      int32_t *sl_len)
+{
+    const int kpt = (M + kSelThreads - 1) / kSelThreads;  // M <= 4096
+    if (kpt == 1)
+        hipLaunchKernelGGL((select_kernel<1, PART>), dim3(n), dim3(kSelThreads), 0, s, M, scores,
+                           part, nwin, b2, sc_out, cluster_size, kind, budget, sel, n_sel, sl_len);
+    else if (kpt == 2)
+        hipLaunchKernelGGL((select_kernel<2, PART>), dim3(n), dim3(kSelThreads), 0, s, M, scores,
+                           part, nwin, b2, sc_out, cluster_size, kind, budget, sel, n_sel, sl_len);
+    else
+        hipLaunchKernelGGL((select_kernel<4, PART>), dim3(n), dim3(kSelThreads), 0, s, M, scores,
+                           part, nwin, b2, sc_out, cluster_size, kind, budget, sel, n_sel, sl_len);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t select_launch(hipStream_t s, int n, int M, const float *scores,
                          const int32_t *cluster_size, int kind, const int32_t *budget,
                          int32_t *sel, int32_t *n_sel, int32_t *sl_len)
 {
-    const int kpt = (M + kSelThreads - 1) / kSelThreads;  // M <= 4096
-    if (kpt == 1)
-        hipLaunchKernelGGL(select_kernel<1>, dim3(n), dim3(kSelThreads), 0, s, M, scores,
-                           cluster_size, kind, budget, sel, n_sel, sl_len);
-    else if (kpt == 2)
-        hipLaunchKernelGGL(select_kernel<2>, dim3(n), dim3(kSelThreads), 0, s, M, scores,
-                           cluster_size, kind, budget, sel, n_sel, sl_len);
-    else
-        hipLaunchKernelGGL(select_kernel<4>, dim3(n), dim3(kSelThreads), 0, s, M, scores,
-                           cluster_size, kind, budget, sel, n_sel, sl_len);
-    return hipGetLastError();
+    return select_any<false>(s, n, M, scores, nullptr, 0, nullptr, nullptr, cluster_size, kind,
+                             budget, sel, n_sel, sl_len);
+}
+
+hipError_t select_partials_launch(hipStream_t s, int n, int M, const float *part, int nwin,
+                                  const void *b2, float *scores, const int32_t *cluster_size,
+                                  int kind, const int32_t *budget, int32_t *sel, int32_t *n_sel,
+                                  int32_t *sl_len)
+{
+    return select_any<true>(s, n, M, nullptr, part, nwin, reinterpret_cast<const uint16_t *>(b2),
+                            scores, cluster_size, kind, budget, sel, n_sel, sl_len);
 }
 
 }  // namespace ds

@@ -491,9 +491,14 @@ ds_status ds_router_train_step(hipStream_t s, const ds_router_train_args *a);
  * every compute unit busy, so kernels beside it wait for its workgroups to
  * retire: in this mode the two router layers of position t+1 run on
  * head_stream just before head t (h[:, t+1] exists then), and only the
- * selection and build of position t+1 run on router_stream beside head t.  Every pointer is a device pointer except
- * max_rows, max_len, W_pos, head_events and sync_events (host arrays).  On return all work is
- * enqueued and head_stream waits for everything enqueued on router_stream.
+ * selection and build of position t+1 run on router_stream beside head t.
+ * When B <= 64 and the second layer's k-window partial sums of a position
+ * fit 2 MB, head_stream stops at those partials and the selection adds them
+ * (in window order, then b2, as ds_router_score does; the same scores are
+ * written), so the layer's finishing pass leaves head_stream.  Every
+ * pointer is a device pointer except max_rows, max_len, W_pos, head_events
+ * and sync_events (host arrays).  On return all work is enqueued and
+ * head_stream waits for everything enqueued on router_stream.
  * Required field:
  *   sync_events  host array [2T+1] of caller-created HIP events on the
  *                streams' device (hipEventDisableTiming is enough), used to
