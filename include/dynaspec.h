@@ -179,8 +179,9 @@ ds_status ds_build_shortlist(hipStream_t s, int n, int M, int V, const int32_t *
  * G >= 8 single-row groups (batched drafting) walk W once in token order on
  * the matrix cores and write only shortlisted (row, group) pairs -- this
  * path requires every shortlist to be ascending; bf16 heads with m >= 8
- * (tree drafting) run a gathered matrix-core GEMM per group; everything
- * else streams the shortlisted rows as a GEMV.
+ * (tree drafting) run a gathered matrix-core GEMM per group (shortlists in
+ * any order; ascending ones let rows shared by several groups be read from
+ * HBM once); everything else streams the shortlisted rows as a GEMV.
  */
 size_t ds_head_workspace_bytes(int G, int m, int V);
 ds_status ds_gathered_lm_head(hipStream_t s, ds_dtype dt, int V, int d, const void *W, int G,

@@ -418,6 +418,40 @@ def test_head_tree_shared_rows(N, oracle_lib, G, m, d):
     _logit_bar(got, ref, True)
 
 
+@pytest.mark.parametrize("kind", ["identical", "unsorted", "descending", "one_long"])
+def test_head_tree_merge_edges(N, oracle_lib, kind):
+    """Edge cases of the tree head's tile list merged by token id: every
+    group with the same shortlist (every tile's first id tied across the
+    groups: ties go to the lower group), shortlists not in ascending order
+    (the merge does not apply and the tile-index order runs instead), and
+    one long group among short ones.  Every logit is checked."""
+    V, d, G, m = 30000, 264, 8, 16
+    g = np.random.default_rng({"identical": 1, "unsorted": 2, "descending": 3, "one_long": 4}[kind])
+    cfg = syn.shrink(syn.CONFIGS[1], V=V, d=d, M=50, dtype=syn.DT_BF16)
+    cluster_of, _ = _clusters(V, 50, 3)
+    W = syn.make_lm_head(cfg, cluster_of)
+    h = _store(g.standard_normal((G, m, d)).astype(np.float32), True)
+    if kind == "identical":
+        one = np.sort(g.choice(V, 3000, replace=False)).astype(np.int32)
+        ids = [one] * G
+    elif kind == "one_long":
+        ids = [np.sort(g.choice(V, 300 if k else 20000, replace=False)).astype(np.int32)
+               for k in range(G)]
+    else:
+        ids = [np.sort(g.choice(V, 2000 + 300 * k, replace=False)).astype(np.int32)
+               for k in range(G)]
+        ids = [x[g.permutation(len(x))] if kind == "unsorted" else x[::-1].copy() for x in ids]
+    sl_off = np.concatenate([[0], np.cumsum([len(x) for x in ids])]).astype(np.int64)
+    sl_ids = np.concatenate(ids)
+    ref = oracle_lib.gathered_lm_head(W, h, sl_off, sl_ids)
+    logits = torch.full((m * int(sl_off[-1]),), float("nan"), device="cuda")
+    N.gathered_lm_head(to_dev(W), to_dev(h), to_dev(sl_off), to_dev(sl_ids),
+                       int(max(len(x) for x in ids)), logits)
+    got = _cpu(logits)
+    assert not np.isnan(got).any()
+    _logit_bar(got, ref, True)
+
+
 @pytest.mark.parametrize("G,m", [(3, 1), (16, 1), (3, 8)])
 def test_head_invalid_ids_are_nan(N, oracle_lib, G, m):
     """Ids outside [0, V) give NaN on every kernel path (GEMV, union, gathered);
