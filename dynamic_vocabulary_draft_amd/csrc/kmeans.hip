@@ -170,10 +170,28 @@ __device__ __forceinline__ u32x4 frag(const uint16_t *t, int row, int s)
     return *reinterpret_cast<const u32x4 *>(t + row * kSlice + ((p ^ swz(row)) << 3));
 }
 
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+// 16 bytes per lane from the buffer (offset voff + soff) straight into LDS:
+// the wave's 64 lanes fill 1 KB from lds on, in lane order
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint16_t *lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+// wait until this wave's vector memory operations (LDS loads included) are done
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // STORE = false: the assignment (argmax epilogue into best); STORE = true:
 // the plain product, out[c][y] = W[y] . C[c] (row stride ldo), which is the
 // dense LM head when C holds hidden vectors.
-template <bool STORE, int TC>
+// DMA (an even number of 64-wide slices): the slices go from L2 straight
+// into LDS (buffer loads with the LDS destination), not through registers
+// and LDS writes: two LDS stages, each wave's eight 1-KB loads of slice t+1
+// issued before the products of slice t, one barrier per slice (which
+// waits for them).  A load's 64 lanes fill 1 KB of LDS in lane order (8 rows
+// of 128 bytes), so each lane fetches the global piece that the swizzle
+// puts at its slot.  The stages are separate LDS arrays, so the compiler
+// sees that the products' reads cannot alias the loads in flight.
+template <bool STORE, int TC, bool DMA = false>
 __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d, const uint16_t *__restrict__ W,
                                                             int M, const uint16_t *__restrict__ C,
                                                             int RT, int CT,
@@ -181,9 +199,12 @@ __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d
                                                             float *__restrict__ out, int64_t ldo)
 {
     constexpr int WCOLS = TC / 2, JT = WCOLS / 32;  // columns per wave, its 32-wide tiles
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(kTileR + TC) * kSlice];
     const int b = blockIdx.x;
-    const int rt = (b / (8 * CT)) * 8 + (b % 8), ct = (b / 8) % CT;  // a row tile stays on one XCD
+    // a row tile stays on one XCD; the tile indices are read back as scalars
+    // (the divisions go through vector registers; buffer descriptors built
+    // from them must be scalar)
+    const int rt = __builtin_amdgcn_readfirstlane((b / (8 * CT)) * 8 + (b % 8));
+    const int ct = __builtin_amdgcn_readfirstlane((b / 8) % CT);
     if (rt >= RT)
         return;
     const int lane = lane_id(), wave = threadIdx.x >> 6, wr = wave >> 1, wc = wave & 1;  // 4 x 2 waves
@@ -199,6 +220,103 @@ __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d
         for (int j = 0; j < JT; ++j)
             acc[i][j] = f32x16{};
     const int nsl = d / kSlice;
+    if constexpr (DMA) {
+        // two stages, each an A tile and a B tile, four separate arrays: the
+        // compiler then tells every read from the loads in flight (an offset
+        // folded into a constant loses that)
+        __shared__ __attribute__((aligned(1024))) uint16_t sa0[kTileR * kSlice];
+        __shared__ __attribute__((aligned(1024))) uint16_t sb0[TC * kSlice];
+        __shared__ __attribute__((aligned(1024))) uint16_t sa1[kTileR * kSlice];
+        __shared__ __attribute__((aligned(1024))) uint16_t sb1[TC * kSlice];
+        const int wv = __builtin_amdgcn_readfirstlane(wave);  // LDS destinations are scalar
+        // load q of this wave fills rows 8 * (8q + wave) .. +8 of a tile
+        constexpr int QA = kTileR / 64, QB = TC / 64;
+        uint32_t voa[QA], vob[QB];
+#pragma unroll
+        for (int q = 0; q < QA; ++q) {
+            const int row = 8 * (8 * q + wv) + (lane >> 3);
+            voa[q] = (uint32_t)row * (uint32_t)d * 2u + 16u * (uint32_t)((lane & 7) ^ swz(row));
+        }
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+            const int row = 8 * (8 * q + wv) + (lane >> 3);
+            vob[q] = (uint32_t)row * (uint32_t)d * 2u + 16u * (uint32_t)((lane & 7) ^ swz(row));
+        }
+#define KMD_LOAD(SA, SB, T)                                                                 \
+    {                                                                                       \
+        const int k0_ = min((T), nsl - 1) * kSlice;                                         \
+        _Pragma("unroll") for (int q = 0; q < QA; ++q)                                      \
+            lds_load16(ra, (SA) + (8 * q + wv) * 8 * kSlice, voa[q], 2 * k0_);              \
+        _Pragma("unroll") for (int q = 0; q < QB; ++q)                                      \
+            lds_load16(rb, (SB) + (8 * q + wv) * 8 * kSlice, vob[q], 2 * k0_);              \
+    }
+// the operands of piece st + 1 are read while piece st is multiplied (two
+// register sets), one read between consecutive products
+#define KMD_READ(SA, SB, ST, FA, FB)                                                        \
+    {                                                                                       \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
+            FA[i] = frag((SA), wr * 64 + i * 32 + (lane & 31), (ST));                       \
+        _Pragma("unroll") for (int j = 0; j < JT; ++j)                                      \
+            FB[j] = frag((SB), wc * WCOLS + j * 32 + (lane & 31), (ST));                    \
+    }
+#define KMD_MUL(FA, FB)                                                                     \
+    {                                                                                       \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i)                                       \
+            _Pragma("unroll") for (int j = 0; j < JT; ++j)                                  \
+                acc[i][j] = mfma(FA[i], FB[j], acc[i][j]);                                  \
+    }
+#define KMD_PRODUCTS(SA, SB)                                                                \
+    {                                                                                       \
+        u32x4 fa0_[2], fb0_[JT], fa1_[2], fb1_[JT];                                         \
+        KMD_READ(SA, SB, 0, fa0_, fb0_)                                                     \
+        KMD_READ(SA, SB, 1, fa1_, fb1_)                                                     \
+        KMD_MUL(fa0_, fb0_)                                                                 \
+        KMD_READ(SA, SB, 2, fa0_, fb0_)                                                     \
+        KMD_MUL(fa1_, fb1_)                                                                 \
+        KMD_READ(SA, SB, 3, fa1_, fb1_)                                                     \
+        KMD_MUL(fa0_, fb0_)                                                                 \
+        KMD_MUL(fa1_, fb1_)                                                                 \
+        /* order: piece 0's reads, then each of the first three pieces'   */                \
+        /* products with the next piece's reads one by one between them   */                \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 + JT, 0);                             \
+        _Pragma("unroll") for (int g = 0; g < 3; ++g)                                       \
+        {                                                                                   \
+            _Pragma("unroll") for (int k = 0; k < 2 + JT; ++k)                              \
+            {                                                                               \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          \
+            }                                                                               \
+            __builtin_amdgcn_sched_group_barrier(0x008, JT - 2, 0);                         \
+        }                                                                                   \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * JT, 0);                             \
+    }
+        // a wave's LDS loads must have landed before the barrier that lets
+        // the other waves read them (the barrier itself does not wait)
+#define KMD_SYNC                                  \
+    {                                             \
+        wait_vmem();                              \
+        __syncthreads();                          \
+    }
+        KMD_LOAD(sa0, sb0, 0)
+        KMD_SYNC
+        for (int t = 0; t < nsl; t += 2) {  // nsl is even (the launcher checks)
+            // the scheduler would sink the loads below the products
+            KMD_LOAD(sa1, sb1, t + 1)
+            __builtin_amdgcn_sched_barrier(0);
+            KMD_PRODUCTS(sa0, sb0)
+            KMD_SYNC  // stage 1 loaded by every wave; stage 0 read by every wave
+            KMD_LOAD(sa0, sb0, t + 2)
+            __builtin_amdgcn_sched_barrier(0);
+            KMD_PRODUCTS(sa1, sb1)
+            KMD_SYNC
+        }
+#undef KMD_SYNC
+#undef KMD_PRODUCTS
+#undef KMD_MUL
+#undef KMD_READ
+#undef KMD_LOAD
+    } else {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][(kTileR + TC) * kSlice];
     constexpr int NA = kTileR * 8 / kAsgThreads, NB = TC * 8 / kAsgThreads;
     // register ring of one slice (a 256-column slice holds enough MFMA work
     // to cover a memory round trip; 128-column tiles needed two slices in
@@ -248,6 +366,7 @@ __global__ __launch_bounds__(kAsgThreads) void kmeans_assign_kernel(int V, int d
         KM_STEP(t, a0, b0)
 #undef KM_STEP
 #undef KM_LOAD
+    }
     // epilogue: register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 of
     // the 32 x 32 tile, column l%32
     if constexpr (STORE) {
@@ -627,10 +746,17 @@ hipError_t kmeans_assign_launch(hipStream_t s, int V, int d, const void *W, int 
         return e;
     const int RT = (V + kTileR - 1) / kTileR, CT = (M + kTileC - 1) / kTileC;
     const int RTp = (RT + 7) / 8 * 8;  // row tiles padded to whole XCD rounds
-    e = launch_timed(kmeans_assign_kernel<false, kTileC>, dim3((unsigned)((int64_t)RTp * CT)), dim3(kAsgThreads), s, t0, t1,
-                     V, d, reinterpret_cast<const uint16_t *>(W), M,
-                     reinterpret_cast<const uint16_t *>(C), RT, CT, best, (float *)nullptr,
-                     (int64_t)0);
+    const dim3 grid((unsigned)((int64_t)RTp * CT));
+    if ((d / kSlice) % 2 == 0)
+        e = launch_timed(kmeans_assign_kernel<false, kTileC, true>, grid, dim3(kAsgThreads), s, t0,
+                         t1, V, d, reinterpret_cast<const uint16_t *>(W), M,
+                         reinterpret_cast<const uint16_t *>(C), RT, CT, best, (float *)nullptr,
+                         (int64_t)0);
+    else
+        e = launch_timed(kmeans_assign_kernel<false, kTileC>, grid, dim3(kAsgThreads), s, t0, t1,
+                         V, d, reinterpret_cast<const uint16_t *>(W), M,
+                         reinterpret_cast<const uint16_t *>(C), RT, CT, best, (float *)nullptr,
+                         (int64_t)0);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(assign_finalize_kernel, dim3(fb), dim3(256), 0, s, V,
@@ -687,6 +813,9 @@ hipError_t dense_head_launch(hipStream_t s, int V, int d, const void *W, int n, 
 {
     const int RT = (V + kTileR - 1) / kTileR, CT = (n + kTileC - 1) / kTileC;
     const int RTp = (RT + 7) / 8 * 8;
+    // the register ring keeps two slices of W in flight against one for the
+    // LDS-direct loads; W streams from HBM once here (one column tile), and
+    // the ring measured as fast or faster
     return launch_timed(kmeans_assign_kernel<true, kTileC>, dim3((unsigned)((int64_t)RTp * CT)),
                         dim3(kAsgThreads), s, t0, t1, V, d, reinterpret_cast<const uint16_t *>(W),
                         n, reinterpret_cast<const uint16_t *>(h), RT, CT,
