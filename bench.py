@@ -568,6 +568,9 @@ def main():
     ap.add_argument("--no-extra", dest="extra", action="store_false",
                     help="skip the other full-size workloads after the default one")
     ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--q-mode", choices=("stats", "dense"), default="stats",
+                    help="draft sampler output: per-row statistics (verification recomputes "
+                         "q; the default) or the q array")
     args = ap.parse_args()
 
     if args.traffic_from:
@@ -598,7 +601,8 @@ def main():
     r = run_draft(args.config, n_steps=args.steps, warmup=args.warmup,
                   instances=args.instances, replicas=not args.no_replicas, eager=args.eager,
                   static=args.static, static_size=args.static_size,
-                  pmc_probe_file=args.probe_file if args.pmc_probe else None)
+                  pmc_probe_file=args.probe_file if args.pmc_probe else None,
+                  q_mode=args.q_mode)
     if r is None:  # --pmc-probe
         return
     cfg, static_ids = r["cfg"], r["static_ids"]
@@ -630,7 +634,7 @@ def main():
         for k in (2, 3, 4):
             torch.cuda.empty_cache()
             x = run_draft(k, n_steps=args.extra_steps, warmup=4, instances=2, replicas=False,
-                          eager=args.eager)
+                          eager=args.eager, q_mode=args.q_mode)
             extra[x["cfg"].name] = {
                 "draft_tokens_per_s": x["value"], "ms_per_step": x["ms_per_step"],
                 "step_ms": x["step_ms"], "steps": args.extra_steps, "instances": 2,
@@ -640,7 +644,7 @@ def main():
 
 
 def run_draft(index, *, n_steps, warmup, instances, replicas, eager, static=None,
-              static_size=32768, pmc_probe_file=None, n_ev_max=120):
+              static_size=32768, pmc_probe_file=None, n_ev_max=120, q_mode="stats"):
     """Time n_steps whole draft steps (plus verification) of workload
     `index` and the head kernels inside them; returns the figures (or None
     after a --pmc-probe run)."""
@@ -668,7 +672,7 @@ def run_draft(index, *, n_steps, warmup, instances, replicas, eager, static=None
         static_ids = syn.static_shortlist(cfg, static_size)
         steps = [StaticStep(wl, static_ids, W=W, packed=static == "packed") for wl in wls]
     else:
-        steps = [DraftStep(wl, W=W) for wl in wls]
+        steps = [DraftStep(wl, W=W, q_mode=q_mode) for wl in wls]
     del wls
     npos = 1 if cfg.is_tree else cfg.T
     if replicas and not cfg.is_tree:
@@ -836,7 +840,9 @@ def run_draft(index, *, n_steps, warmup, instances, replicas, eager, static=None
                       ("static baseline: %s head over one fixed %d-token frequency-ranked "
                        "shortlist + sample per position, verify from target logits"
                        % (static, static_ids.shape[0])),
-              "launch": mode}
+              "launch": mode,
+              "draft_q": ("row statistics (q recomputed where verification reads it)"
+                          if q_mode == "stats" and static_ids is None else "written")}
     return {"cfg": cfg, "static_ids": static_ids, "value": round(value, 1), "warmup": warmup,
             "ms_per_step": round(wall * 1e3 / n_steps, 4),
             "step_ms": {"median": round(float(np.median(step_ms)), 4),

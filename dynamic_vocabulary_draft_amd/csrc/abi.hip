@@ -1,6 +1,7 @@
 // C-ABI of the shortlisted draft head: host-side argument checks, workspace
 // sizes, dispatch to the kernel families, and the two-stream chain runner.
 // Nothing here allocates device memory.
+#include <cstddef>
 #include <atomic>
 #include <mutex>
 #include <new>
@@ -371,6 +372,29 @@ ds_status ds_shortlist_sample(hipStream_t s, int G, int m, const int64_t *sl_off
                                         max_len, ws));
 }
 
+static_assert(sizeof(ds_qstats) == sizeof(ds::QStats) && offsetof(ds_qstats, M) == 0 &&
+                  offsetof(ds_qstats, rZ) == offsetof(ds::QStats, rZ),
+              "row statistics layout");
+
+ds_status ds_shortlist_sample_stats(hipStream_t s, int G, int m, const int64_t *sl_off,
+                                    const int32_t *sl_ids, const float *logits,
+                                    float temperature, const float *u, int64_t max_len,
+                                    int32_t *token, ds_qstats *qstats, void *ws, size_t ws_bytes)
+{
+    if (!qstats || !(temperature > 0.0f))
+        return DS_EINVAL;
+    // check_sample wants a q pointer: the statistics take its place
+    ds_status st = check_sample(G, m, sl_off, sl_ids, logits, temperature, u, max_len, token,
+                                reinterpret_cast<float *>(qstats));
+    if (st != DS_OK)
+        return st;
+    if (!ws || ws_bytes < ds_sample_workspace_bytes(G, m, max_len))
+        return DS_EINVAL;
+    return hip_status(ds::sample_stats_launch(s, G, m, sl_off, sl_ids, logits, temperature, u,
+                                              token, reinterpret_cast<ds::QStats *>(qstats),
+                                              max_len, ws));
+}
+
 size_t ds_softmax_workspace_bytes(int rows, int V)
 {
     return rows > 0 && V > 0 ? ds::softmax_ws_bytes(rows, V) : 0;
@@ -427,6 +451,30 @@ ds_status ds_verify_reject_logits(hipStream_t s, int B, int T, int V, const int3
         return DS_EINVAL;
     return hip_status(ds::verify_logits_launch(s, B, T, V, draft, sl_off, sl_ids, q, logits,
                                                u_acc, u_fin, n_acc, out, ws));
+}
+
+ds_status ds_verify_reject_logits_qstats(hipStream_t s, int B, int T, int V,
+                                         const int32_t *draft, const int64_t *sl_off,
+                                         const int32_t *sl_ids, const float *draft_logits,
+                                         const ds_qstats *qstats, float temperature,
+                                         const float *logits, const float *u_acc,
+                                         const float *u_fin, int32_t *n_acc, int32_t *out,
+                                         void *ws, size_t ws_bytes)
+{
+    if (!qstats || !(temperature > 0.0f) || temperature > 3.0e38f)
+        return DS_EINVAL;
+    ds_status st = check_verify(B, T, V, draft, sl_off, sl_ids, draft_logits, logits, u_acc,
+                                u_fin, n_acc, out);
+    if (st != DS_OK)
+        return st;
+    if ((int64_t)B * (T + 1) > 65535)  // one statistics row per target position
+        return DS_ESHAPE;
+    if (!ws || ws_bytes < ds_verify_logits_workspace_bytes(B, T, V))
+        return DS_EINVAL;
+    return hip_status(ds::verify_logits_qstats_launch(
+        s, B, T, V, draft, sl_off, sl_ids, draft_logits,
+        reinterpret_cast<const ds::QStats *>(qstats), temperature, logits, u_acc, u_fin, n_acc,
+        out, ws));
 }
 
 ds_status ds_verify_reject_noalloc(hipStream_t s, int B, int T, int V, const int32_t *draft,
@@ -501,6 +549,33 @@ ds_status ds_verify_tree_logits(hipStream_t s, int B, int m, int V, const int32_
     return hip_status(ds::verify_tree_logits_launch(s, B, m, V, parent, token, sl_off, sl_ids, q,
                                                     logits, u_acc, u_fin, max_len, n_acc, out,
                                                     path, ws));
+}
+
+ds_status ds_verify_tree_logits_qstats(hipStream_t s, int B, int m, int V,
+                                       const int32_t *parent, const int32_t *token,
+                                       const int64_t *sl_off, const int32_t *sl_ids,
+                                       const float *draft_logits, const ds_qstats *qstats,
+                                       float temperature, const float *logits,
+                                       const float *u_acc, const float *u_fin, int64_t max_len,
+                                       int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
+                                       size_t ws_bytes)
+{
+    if (!qstats || !(temperature > 0.0f) || temperature > 3.0e38f)
+        return DS_EINVAL;
+    if (!parent || !token || !sl_off || !sl_ids || !draft_logits || !logits || !u_acc || !u_fin ||
+        !n_acc || !out || !path)
+        return DS_EINVAL;
+    if (B <= 0 || m <= 0 || V <= 0 || max_len <= 0)
+        return DS_EINVAL;
+    if (m > DS_MAX_TREE_NODES || V > (1 << 20) || B > DS_MAX_GROUPS || max_len > (1 << 24) ||
+        (int64_t)B * (m + 1) > 65535)
+        return DS_ESHAPE;
+    if (!ws || ws_bytes < ds_verify_tree_logits_workspace_bytes(B, m, V, max_len))
+        return DS_EINVAL;
+    return hip_status(ds::verify_tree_logits_qstats_launch(
+        s, B, m, V, parent, token, sl_off, sl_ids, draft_logits,
+        reinterpret_cast<const ds::QStats *>(qstats), temperature, logits, u_acc, u_fin, max_len,
+        n_acc, out, path, ws));
 }
 
 ds_status ds_dense_lm_head(hipStream_t s, int V, int d, const void *W, int n, const void *h,
@@ -580,7 +655,10 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
         return DS_EINVAL;
     const int B = a->B, T = a->T;
     if (B <= 0 || T <= 0 || !a->max_rows || !a->max_len || !a->budget || !a->u_draft ||
-        !a->token || !a->q)
+        !a->token)
+        return DS_EINVAL;
+    // q, or (temperature > 0) the rows' statistics in its place
+    if (!a->q && !(a->qstats && a->temperature > 0.0f))
         return DS_EINVAL;
     const size_t e = a->dtype == DS_BF16 ? 2 : 4;
     const int64_t ldh = (int64_t)(T + 1) * a->d;  // h is [B][T+1][d]
@@ -689,9 +767,14 @@ ds_status ds_draft_chain(hipStream_t hs, hipStream_t rs, const ds_draft_chain_ar
             r = ds::head_launch(hs, bf16, a->V, a->d, Wt, B, 1, hb + (size_t)(t + 1) * a->d * e,
                                 ldh, a->sl_off + rb, a->sl_ids, a->max_rows[t], a->logits, nullptr,
                                 h0, h1);
-        if (r == hipSuccess)
+        if (r == hipSuccess && a->q)
             r = ds::sample_launch(hs, B, 1, a->sl_off + rb, a->sl_ids, a->logits, a->temperature,
                                   a->u_draft + rb, a->token + rb, a->q, a->max_len[t], sws);
+        else if (r == hipSuccess)
+            r = ds::sample_stats_launch(hs, B, 1, a->sl_off + rb, a->sl_ids, a->logits,
+                                        a->temperature, a->u_draft + rb, a->token + rb,
+                                        reinterpret_cast<ds::QStats *>(a->qstats) + rb,
+                                        a->max_len[t], sws);
         return r;
     };
     if (!prebuilt) {

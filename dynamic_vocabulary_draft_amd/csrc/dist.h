@@ -28,6 +28,7 @@
 #include <float.h>
 
 #include "common.h"
+#include "kernels.h"
 
 namespace ds {
 
@@ -95,6 +96,40 @@ __device__ __forceinline__ void row_norm(const float *__restrict__ sm, const dou
 __device__ __forceinline__ float p_elem(float l, float M, double rZ, const double *tab)
 {
     return (float)(exp_tab((double)l - (double)M, tab) * rZ);
+}
+
+// (x) / T; T = 1 (the usual case, and always for the target) skips the
+// fp64 division, which leaves the value unchanged
+__device__ __forceinline__ double over_tau(double x, double tau) { return tau == 1.0 ? x : x / tau; }
+
+// a draft row's weight of logit l relative to its max M, exp((l - M) / T)
+__device__ __forceinline__ double draft_w(float l, double M, double tau, const double *tab)
+{
+    return exp_tab(over_tau((double)l - M, tau), tab);
+}
+// q for draft logit l of a row with statistics (M, rZ): the sampler's q
+__device__ __forceinline__ float q_elem(float l, float M, double rZ, double tau, const double *tab)
+{
+    return (float)(draft_w(l, (double)M, tau, tab) * rZ);
+}
+
+// q of one draft row from its stored values: the values themselves, or
+// (QL) draft logits turned into q with the row's statistics
+template <bool QL>
+struct QRow {
+    float M;
+    double rZ, tau;
+    const double *tab;
+    __device__ __forceinline__ float operator()(float x) const
+    {
+        return QL ? q_elem(x, M, rZ, tau, tab) : x;
+    }
+};
+template <bool QL>
+__device__ __forceinline__ QRow<QL> q_row(const QStats *qs, int64_t row, double qtau,
+                                          const double *tab)
+{
+    return QL ? QRow<QL>{qs[row].M, qs[row].rZ, qtau, tab} : QRow<QL>{0.f, 0.0, 0.0, tab};
 }
 
 // this lane's four consecutive elements (-FLT_MAX past the row end); one

@@ -124,6 +124,21 @@ size_t sample_ws_bytes(int64_t rows, int64_t max_len);
 hipError_t sample_launch(hipStream_t s, int G, int m, const int64_t *sl_off,
                          const int32_t *sl_ids, const float *logits, float temperature,
                          const float *u, int32_t *token, float *q, int64_t max_len, void *ws);
+// A draft row's statistics in place of its q (temperature > 0): q_j =
+// (float)(exp((l_j - M) / T) * rZ) from the row's logits l, the same
+// expression and the same bits as the sampler's q (q_elem in dist.h).  An
+// empty row has rZ = 0.
+struct QStats {
+    float M;
+    int32_t pad;
+    double rZ;
+};
+// the draw of sample_launch without writing q: one workgroup per row after
+// the chunk statistics; the row's statistics go to qs[row]
+hipError_t sample_stats_launch(hipStream_t s, int G, int m, const int64_t *sl_off,
+                               const int32_t *sl_ids, const float *logits, float temperature,
+                               const float *u, int32_t *token, QStats *qs, int64_t max_len,
+                               void *ws);
 
 size_t softmax_ws_bytes(int64_t rows, int64_t V);
 hipError_t softmax_launch(hipStream_t s, int rows, int V, const float *logits, float *p, void *ws);
@@ -145,6 +160,14 @@ hipError_t verify_logits_launch(hipStream_t s, int B, int T, int V, const int32_
                                 const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                                 const float *logits, const float *u_acc, const float *u_fin,
                                 int32_t *n_acc, int32_t *out, void *ws);
+// the same with q taken from the draft logits and their rows' statistics
+// (sample_stats_launch; draft row t * B + b), workspace as verify_logits
+hipError_t verify_logits_qstats_launch(hipStream_t s, int B, int T, int V, const int32_t *draft,
+                                       const int64_t *sl_off, const int32_t *sl_ids,
+                                       const float *draft_logits, const QStats *qs,
+                                       float temperature, const float *logits,
+                                       const float *u_acc, const float *u_fin, int32_t *n_acc,
+                                       int32_t *out, void *ws);
 
 hipError_t dense_head_launch(hipStream_t s, int V, int d, const void *W, int n, const void *h,
                              float *logits, int64_t ldl, hipEvent_t t0 = nullptr,
@@ -168,6 +191,18 @@ hipError_t verify_tree_logits_launch(hipStream_t s, int B, int m, int V, const i
                                      const float *u_acc, const float *u_fin, int64_t max_len,
                                      int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
                                      hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+// tree verification with q from the draft logits and their rows' statistics
+// (sample_stats_launch; draft row b * m + node), workspace as
+// verify_tree_logits
+hipError_t verify_tree_logits_qstats_launch(hipStream_t s, int B, int m, int V,
+                                            const int32_t *parent, const int32_t *token,
+                                            const int64_t *sl_off, const int32_t *sl_ids,
+                                            const float *draft_logits, const QStats *qs,
+                                            float temperature, const float *logits,
+                                            const float *u_acc, const float *u_fin,
+                                            int64_t max_len, int32_t *n_acc, int32_t *out,
+                                            int32_t *path, void *ws, hipEvent_t t0 = nullptr,
+                                            hipEvent_t t1 = nullptr);
 hipError_t verify_tree_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
                               const int32_t *token, const int64_t *sl_off, const int32_t *sl_ids,
                               const float *q, const float *p, const float *u_acc,

@@ -45,9 +45,6 @@ struct Ragged {
     }
 };
 
-// (x) / T; T = 1 (the usual case, and always for the target) skips the
-// fp64 division, which leaves the value unchanged
-__device__ __forceinline__ double over_tau(double x, double tau) { return tau == 1.0 ? x : x / tau; }
 
 // row max from the chunk maxima (order-independent), into every thread
 __device__ float row_max(const float *__restrict__ cmax, int nch, float *sh)
@@ -206,8 +203,7 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             if (j0 + k < len)
-                out[off + j0 + k] =
-                    (float)(exp_tab(over_tau((double)v[r][k] - mx, tau), s_exp2) * rZ);
+                out[off + j0 + k] = q_elem(v[r][k], mxf, rZ, tau, s_exp2);
     }
     if (!PICK)
         return;
@@ -224,7 +220,7 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
         if (c0 + r == c) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                wt[k] = j0 + k < len ? exp_tab(over_tau((double)v[r][k] - mx, tau), s_exp2) : 0.0;
+                wt[k] = j0 + k < len ? draft_w(v[r][k], mx, tau, s_exp2) : 0.0;
         }
     double incl;
     double tot = wave_chunk_sum(wt, &incl);
@@ -232,6 +228,67 @@ __global__ __launch_bounds__(kChunkThreads) void norm_final_kernel(
         s_wt[threadIdx.x >> 6] = tot;
     __syncthreads();
     int64_t pick = chunk_walk(wt, j0, s_wt, incl, P[c], thr, s_fallback != 0, s_pick);
+    if (threadIdx.x == 0)
+        token[row] = sl_ids[ids_off + (pick < 0 ? 0 : pick)];
+}
+
+// The draw without q (tau > 0): one workgroup per row rebuilds the row's
+// statistics exactly as norm_final_kernel does, stores (M, 1 / Z), and walks
+// the chunk holding u * Z with the same weights, so the token is the one
+// norm_final_kernel draws and q_elem of the logits gives its q bit for bit.
+template <class L>
+__global__ __launch_bounds__(kChunkThreads) void norm_pick_kernel(
+    L layout, const float *__restrict__ in, double tau, int64_t nchmax, const void *ws,
+    int64_t rows, const int32_t *__restrict__ sl_ids, const float *__restrict__ u,
+    int32_t *__restrict__ token, QStats *__restrict__ qs)
+{
+    __shared__ double P[kMaxRowChunks], S[kMaxRowChunks], S2[kMaxRowChunks];
+    __shared__ double s_wt[4];
+    __shared__ double s_total;
+    __shared__ float s_f[4];
+    __shared__ int s_owner, s_fallback;
+    __shared__ int64_t s_pick[2];
+    __shared__ double s_exp2[64];
+    const int64_t row = blockIdx.x;
+    int64_t off, len, ids_off;
+    layout.locate(row, &off, &len, &ids_off);
+    if (len <= 0) {
+        if (threadIdx.x == 0) {
+            token[row] = -1;
+            qs[row] = QStats{0.0f, 0, 0.0};
+        }
+        return;
+    }
+    ChunkWs w = chunk_ws(const_cast<void *>(ws), rows, nchmax);
+    const int nch = (int)min(chunks_for(len), nchmax);  // rows beyond max_len: in bounds
+    const float *cmax = w.cmax + row * nchmax;
+    const double *csum = w.csum + row * nchmax;
+    fill_exp2_table(s_exp2);  // ordered before its use by the barrier in row_max
+    const float mxf = row_max(cmax, nch, s_f);
+    const double mx = (double)mxf;
+    rescaled_sums(cmax, csum, nch, mx, tau, s_exp2, S2);
+    const double Z = row_prefix(S2, nch, P, S, &s_total);
+    const double rZ = 1.0 / Z;
+    if (threadIdx.x == 0)
+        qs[row] = QStats{mxf, 0, rZ};
+    const double thr = (double)u[row] * Z;
+    owner_chunk(P, S, nch, thr, &s_owner, &s_fallback);
+    const int64_t c = s_owner;
+    if (c < 0)
+        return;  // as in norm_final_kernel: no chunk with mass
+    const int64_t j0 = c * kChunk + (threadIdx.x >> 6) * 256 + lane_id() * 4;
+    float v[4];
+    load4(in + off, j0, len, v);
+    double wt[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        wt[k] = j0 + k < len ? draft_w(v[k], mx, tau, s_exp2) : 0.0;
+    double incl;
+    const double tot = wave_chunk_sum(wt, &incl);
+    if (lane_id() == 0)
+        s_wt[threadIdx.x >> 6] = tot;
+    __syncthreads();
+    const int64_t pick = chunk_walk(wt, j0, s_wt, incl, P[c], thr, s_fallback != 0, s_pick);
     if (threadIdx.x == 0)
         token[row] = sl_ids[ids_off + (pick < 0 ? 0 : pick)];
 }
@@ -335,6 +392,36 @@ hipError_t sample_launch(hipStream_t s, int G, int m, const int64_t *sl_off,
     Ragged layout{sl_off, m};
     return launch_norm<Ragged, true>(s, layout, (int64_t)G * m, max_len, logits,
                                      (double)temperature, ws, sl_ids, u, token, q);
+}
+
+hipError_t sample_stats_launch(hipStream_t s, int G, int m, const int64_t *sl_off,
+                               const int32_t *sl_ids, const float *logits, float temperature,
+                               const float *u, int32_t *token, QStats *qs, int64_t max_len,
+                               void *ws)
+{
+    Ragged layout{sl_off, m};
+    const int64_t rows = (int64_t)G * m;
+    const int64_t nchmax = chunks_for(max_len > 0 ? max_len : 1);
+    const double tau = (double)temperature;
+    // the chunk statistics as in launch_norm (their values do not depend on
+    // the chunks per workgroup)
+    const int R = rows >= 256 && nchmax >= 16 ? 2 : (nchmax >= 64 && rows * nchmax / 4 >= 2048 ? 4 : 1);
+    const dim3 grid((unsigned)((nchmax + R - 1) / R), (unsigned)rows);
+    if (R == 2)
+        hipLaunchKernelGGL((norm_stats_kernel<Ragged, 2>), grid, dim3(kChunkThreads), 0, s, layout,
+                           logits, tau, nchmax, ws, rows);
+    else if (R == 4)
+        hipLaunchKernelGGL((norm_stats_kernel<Ragged, 4>), grid, dim3(kChunkThreads), 0, s, layout,
+                           logits, tau, nchmax, ws, rows);
+    else
+        hipLaunchKernelGGL((norm_stats_kernel<Ragged, 1>), grid, dim3(kChunkThreads), 0, s, layout,
+                           logits, tau, nchmax, ws, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((norm_pick_kernel<Ragged>), dim3((unsigned)rows), dim3(kChunkThreads), 0, s,
+                       layout, logits, tau, nchmax, (const void *)ws, rows, sl_ids, u, token, qs);
+    return hipGetLastError();
 }
 
 static int64_t segments_for(int64_t V) { return (V + kSeg - 1) / kSeg; }

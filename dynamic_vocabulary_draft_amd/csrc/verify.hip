@@ -80,20 +80,25 @@ struct RowP {
 
 // One workgroup per sequence: (logits) every target row's normaliser, the T
 // accept tests (wave t: position t, t + 16, ...) and t*.
-template <bool LOGITS>
+// QL: q is recomputed from the draft logits (q points to them) and each
+// draft row's statistics qs (temperature qtau), bit for bit the sampler's q.
+template <bool LOGITS, bool QL>
 __global__ __launch_bounds__(kPrepThreads) void verify_prep_kernel(
     int B, int T, int V, const int32_t *__restrict__ draft, const int64_t *__restrict__ sl_off,
     const int32_t *__restrict__ sl_ids, const float *__restrict__ q, const float *__restrict__ p,
     const float *__restrict__ smax, const double *__restrict__ ssum, int64_t nseg,
-    const float *__restrict__ u_acc, int64_t nchV, void *ws)
+    const float *__restrict__ u_acc, int64_t nchV, void *ws, const QStats *__restrict__ qs,
+    double qtau)
 {
     __shared__ int s_rej;
     __shared__ float sM[LOGITS ? kMaxRows : 1];
-    __shared__ double srZ[LOGITS ? kMaxRows : 1], tab[LOGITS ? 64 : 1];
+    __shared__ double srZ[LOGITS ? kMaxRows : 1], tab[LOGITS || QL ? 64 : 1];
     const int b = blockIdx.x, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     VerifyWs w = verify_ws(ws, B, nchV);
     if (threadIdx.x == 0)
         s_rej = T;
+    if (QL && !LOGITS)
+        fill_exp2_table(tab);  // ordered by the barrier below
     if (LOGITS) {
         fill_exp2_table(tab);
         __syncthreads();
@@ -118,7 +123,10 @@ __global__ __launch_bounds__(kPrepThreads) void verify_prep_kernel(
         const float px_raw = xin ? p[((int64_t)b * (T + 1) + t) * V + x] : 0.f;
         const int64_t j = wave_lower_bound(sl_ids + lo, len, x);
         const bool found = j < len && sl_ids[lo + j] == x;
-        const double qx = found ? (double)q[lo + j] : 0.0;
+        double qx = 0.0;
+        if (found)
+            qx = QL ? (double)q_elem(q[lo + j], qs[row].M, qs[row].rZ, qtau, tab)
+                    : (double)q[lo + j];
         double px = 0.0;
         if (xin)
             px = LOGITS ? (double)p_elem(px_raw, sM[t], srZ[t], tab) : (double)px_raw;
@@ -170,16 +178,19 @@ __device__ __forceinline__ void lane_weights(const RowP<LOGITS> &rp, const float
 // [base, base + 1024)) scattered into the dense array qd by `nt` threads
 // with index i; the caller zeroes qd first and orders the writes before the
 // reads.
+// qf maps a stored value to q (identity, or q_elem of a draft logit).
+template <class QF>
 __device__ __forceinline__ void scatter_q(const int32_t *__restrict__ S,
                                           const float *__restrict__ qrow, int64_t a, int64_t e,
-                                          int64_t base, float *qd, int i, int nt)
+                                          int64_t base, float *qd, int i, int nt, QF qf)
 {
     for (int64_t k = a + i; k < e; k += nt) {
         const int64_t o = (int64_t)S[k] - base;
         if (o >= 0 && o < kChunk)
-            qd[o] = qrow[k];
+            qd[o] = qf(qrow[k]);
     }
 }
+
 
 // the chunk's entries [a, e) of an ascending shortlist S of length len:
 // ids in [base, base + 1024), by one wave
@@ -212,16 +223,17 @@ __device__ __forceinline__ double wave_chunk_total(const RowP<LOGITS> &rp, const
 }
 
 // Chunk sums: wave w of workgroup x takes chunk 4x + w of sequence blockIdx.y.
-template <bool LOGITS>
+template <bool LOGITS, bool QL>
 __global__ __launch_bounds__(kChunkThreads) void verify_sum_kernel(
     int B, int T, int V, const int64_t *__restrict__ sl_off, const int32_t *__restrict__ sl_ids,
-    const float *__restrict__ q, const float *__restrict__ p, int64_t nchV, void *ws)
+    const float *__restrict__ q, const float *__restrict__ p, int64_t nchV, void *ws,
+    const QStats *__restrict__ qs, double qtau)
 {
     __shared__ float qd_all[4][kChunk];
-    __shared__ double tab[LOGITS ? 64 : 1];
+    __shared__ double tab[LOGITS || QL ? 64 : 1];
     const int b = blockIdx.y, wave = threadIdx.x >> 6, lane = lane_id();
     VerifyWs w = verify_ws(ws, B, nchV);
-    if (LOGITS) {
+    if (LOGITS || QL) {
         fill_exp2_table(tab);
         __syncthreads();
     }
@@ -245,7 +257,7 @@ __global__ __launch_bounds__(kChunkThreads) void verify_sum_kernel(
         chunk_range(sl_ids + lo, len, base, &a, &e);
         for (int k = lane; k < kChunk; k += kWave)
             qd[k] = 0.0f;
-        scatter_q(sl_ids + lo, q + lo, a, e, base, qd, lane, kWave);
+        scatter_q(sl_ids + lo, q + lo, a, e, base, qd, lane, kWave, q_row<QL>(qs, row, qtau, tab));
     }
     // one wave's LDS operations complete in order: the scatter is visible
     const double t = wave_chunk_total<LOGITS>(rp, x, base, V, qd, resid);
@@ -253,12 +265,12 @@ __global__ __launch_bounds__(kChunkThreads) void verify_sum_kernel(
         w.csum[(int64_t)b * nchV + c] = t;
 }
 
-template <bool LOGITS>
+template <bool LOGITS, bool QL>
 __global__ __launch_bounds__(kChunkThreads) void verify_final_kernel(
     int B, int T, int V, const int32_t *__restrict__ draft, const int64_t *__restrict__ sl_off,
     const int32_t *__restrict__ sl_ids, const float *__restrict__ q, const float *__restrict__ p,
     const float *__restrict__ u_fin, int64_t nchV, const void *ws, int32_t *__restrict__ n_acc,
-    int32_t *__restrict__ out)
+    int32_t *__restrict__ out, const QStats *__restrict__ qs, double qtau)
 {
     __shared__ double P[kMaxVChunks], S[kMaxVChunks];
     __shared__ float qd[kChunk];
@@ -266,10 +278,10 @@ __global__ __launch_bounds__(kChunkThreads) void verify_final_kernel(
     __shared__ double s_total;
     __shared__ int s_owner, s_fallback;
     __shared__ int64_t s_pick[2];
-    __shared__ double tab[LOGITS ? 64 : 1];
+    __shared__ double tab[LOGITS || QL ? 64 : 1];
     const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = lane_id();
     VerifyWs w = verify_ws(const_cast<void *>(ws), B, nchV);
-    if (LOGITS)
+    if (LOGITS || QL)
         fill_exp2_table(tab);  // ordered by the barrier in row_prefix
     const int tstar = w.tstar[b];
     const int nch = (int)nchV;
@@ -323,7 +335,8 @@ __global__ __launch_bounds__(kChunkThreads) void verify_final_kernel(
         for (int k = threadIdx.x; k < kChunk; k += blockDim.x)
             qd[k] = 0.0f;
         __syncthreads();
-        scatter_q(sl_ids + lo, q + lo, s_rng[0], s_rng[1], base, qd, threadIdx.x, blockDim.x);
+        scatter_q(sl_ids + lo, q + lo, s_rng[0], s_rng[1], base, qd, threadIdx.x, blockDim.x,
+                  q_row<QL>(qs, row, qtau, tab));
         __syncthreads();
     }
     double w0[4];
@@ -339,29 +352,30 @@ __global__ __launch_bounds__(kChunkThreads) void verify_final_kernel(
         ob[tstar] = (int32_t)pick;
 }
 
-template <bool LOGITS>
+template <bool LOGITS, bool QL = false>
 hipError_t verify_kernels(hipStream_t s, int B, int T, int V, const int32_t *draft,
                           const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                           const float *x, float *smax, double *ssum, int64_t nseg,
                           const float *u_acc, const float *u_fin, int32_t *n_acc, int32_t *out,
-                          void *ws)
+                          void *ws, const QStats *qs = nullptr, double qtau = 1.0)
 {
     const int64_t nchV = chunks_for(V);
     hipError_t e;
     if (LOGITS && (e = softmax_stats_launch(s, B * (T + 1), V, x, ssum)) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(verify_prep_kernel<LOGITS>, dim3((unsigned)B), dim3(kPrepThreads), 0, s,
-                       B, T, V, draft, sl_off, sl_ids, q, x, (const float *)smax,
-                       (const double *)ssum, nseg, u_acc, nchV, ws);
+    hipLaunchKernelGGL((verify_prep_kernel<LOGITS, QL>), dim3((unsigned)B), dim3(kPrepThreads), 0,
+                       s, B, T, V, draft, sl_off, sl_ids, q, x, (const float *)smax,
+                       (const double *)ssum, nseg, u_acc, nchV, ws, qs, qtau);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(verify_sum_kernel<LOGITS>, dim3((unsigned)((nchV + 3) / 4), (unsigned)B),
-                       dim3(kChunkThreads), 0, s, B, T, V, sl_off, sl_ids, q, x, nchV, ws);
+    hipLaunchKernelGGL((verify_sum_kernel<LOGITS, QL>),
+                       dim3((unsigned)((nchV + 3) / 4), (unsigned)B), dim3(kChunkThreads), 0, s, B,
+                       T, V, sl_off, sl_ids, q, x, nchV, ws, qs, qtau);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(verify_final_kernel<LOGITS>, dim3((unsigned)B), dim3(kChunkThreads), 0, s,
-                       B, T, V, draft, sl_off, sl_ids, q, x, u_fin, nchV, (const void *)ws, n_acc,
-                       out);
+    hipLaunchKernelGGL((verify_final_kernel<LOGITS, QL>), dim3((unsigned)B), dim3(kChunkThreads),
+                       0, s, B, T, V, draft, sl_off, sl_ids, q, x, u_fin, nchV, (const void *)ws,
+                       n_acc, out, qs, qtau);
     return hipGetLastError();
 }
 
@@ -402,6 +416,23 @@ hipError_t verify_logits_launch(hipStream_t s, int B, int T, int V, const int32_
     float *smax = reinterpret_cast<float *>(ssum + (size_t)rows * nseg);
     return verify_kernels<true>(s, B, T, V, draft, sl_off, sl_ids, q, logits, smax, ssum, nseg,
                                 u_acc, u_fin, n_acc, out, ws);
+}
+
+hipError_t verify_logits_qstats_launch(hipStream_t s, int B, int T, int V, const int32_t *draft,
+                                       const int64_t *sl_off, const int32_t *sl_ids,
+                                       const float *draft_logits, const QStats *qs,
+                                       float temperature, const float *logits,
+                                       const float *u_acc, const float *u_fin, int32_t *n_acc,
+                                       int32_t *out, void *ws)
+{
+    const int rows = B * (T + 1);
+    char *sws = reinterpret_cast<char *>(ws) + align256(verify_ws_bytes(B, T, V));
+    const int64_t nseg = softmax_segments(V);
+    double *ssum = reinterpret_cast<double *>(sws);
+    float *smax = reinterpret_cast<float *>(ssum + (size_t)rows * nseg);
+    return verify_kernels<true, true>(s, B, T, V, draft, sl_off, sl_ids, draft_logits, logits,
+                                      smax, ssum, nseg, u_acc, u_fin, n_acc, out, ws, qs,
+                                      (double)temperature);
 }
 
 }  // namespace ds

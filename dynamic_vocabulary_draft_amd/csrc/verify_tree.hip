@@ -271,12 +271,12 @@ __device__ __forceinline__ void slice_pass(const float *__restrict__ pu,
 
 // R <- max(0, R - P q_c) over the shortlist (R read as p_u at the listed
 // ids when fresh; ids outside [0, V) carry no mass); returns sum R.
-template <bool LOGITS>
+template <bool LOGITS, class QF>
 __device__ __forceinline__ double residual_update(const float *__restrict__ pu,
                                                   const int32_t *__restrict__ S,
                                                   const float *__restrict__ qc, int len, int V,
                                                   bool fresh, double P, double *__restrict__ R,
-                                                  const TRow<LOGITS> &tv, double *sh)
+                                                  const TRow<LOGITS> &tv, double *sh, QF qf)
 {
     constexpr int U = 16;
     double acc = 0.0;
@@ -287,7 +287,7 @@ __device__ __forceinline__ double residual_update(const float *__restrict__ pu,
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int j = min(j0 + k * kTreeThreads, len - 1);
-            qv[k] = qc[j];
+            qv[k] = qc[j];  // turned into q below
             if (fresh) {
                 const int32_t y = S[j];
                 const bool ok = y >= 0 && y < V;
@@ -300,7 +300,7 @@ __device__ __forceinline__ double residual_update(const float *__restrict__ pu,
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int j = j0 + k * kTreeThreads;
-            const double t = P * (double)qv[k];
+            const double t = P * (double)qf(qv[k]);
             const double nr = r[k] > t ? r[k] - t : 0.0;
             if (j < len) {
                 R[j] = nr;
@@ -401,9 +401,11 @@ __device__ void root_kids(const int32_t *__restrict__ parent_b, int m, int *s3, 
 // root's children at those ids, scattered into LDS (the entries are
 // positions rank[base/32] .. of the ascending shortlist); returns after a
 // barrier.
+template <bool QL>
 __device__ void root_scatter(const uint32_t *__restrict__ bits_b, const uint32_t *__restrict__ rank_b,
                              int V, int len, int64_t base, const float *__restrict__ q1,
-                             const float *__restrict__ q2, uint32_t *mem, float *q1d, float *q2d)
+                             const float *__restrict__ q2, uint32_t *mem, float *q1d, float *q2d,
+                             QRow<QL> f1, QRow<QL> f2)
 {
     const int64_t nw = tree_words(V);
     const int64_t w0 = base >> 5;
@@ -424,9 +426,9 @@ __device__ void root_scatter(const uint32_t *__restrict__ bits_b, const uint32_t
             wd &= wd - 1u;
             if (j < len) {
                 const int o = 32 * i + bit;
-                q1d[o] = q1[j];
+                q1d[o] = f1(q1[j]);
                 if (q2)
-                    q2d[o] = q2[j];
+                    q2d[o] = f2(q2[j]);
             }
             ++j;
         }
@@ -470,16 +472,18 @@ __device__ __forceinline__ double root_R(double pv, float q1v, float q2v, int k,
 // PASS 1: off, sp, s1 per chunk; PASS 2: s2 per chunk (two children only)
 constexpr int kRootMaxChunks = 256;  // V <= 2^20
 
-template <int PASS, bool LOGITS>
+// QL: q is recomputed from the draft logits (q points to them) and the
+// draft rows' statistics qs (row b * m + node), bit for bit the sampler's q
+template <int PASS, bool LOGITS, bool QL>
 __global__ __launch_bounds__(kRootThreads) void root_pass_kernel(
     int m, int V, int64_t max_len, const int32_t *__restrict__ parent,
     const int64_t *__restrict__ sl_off, const float *__restrict__ q,
     const float *__restrict__ p, const float *__restrict__ nM, const double *__restrict__ nZ,
     const uint32_t *__restrict__ bits, const uint32_t *__restrict__ rank,
-    RootPart *__restrict__ part)
+    RootPart *__restrict__ part, const QStats *__restrict__ qs, double qtau)
 {
-    __shared__ double tab[LOGITS ? 64 : 1];
-    if (LOGITS)
+    __shared__ double tab[LOGITS || QL ? 64 : 1];
+    if (LOGITS || QL)
         fill_exp2_table(tab);  // ordered by the barriers in root_kids
     __shared__ uint32_t mem[kRootChunk / 32];
     __shared__ float q1d[kRootChunk], q2d[PASS == 2 ? kRootChunk : 1];
@@ -505,9 +509,11 @@ __global__ __launch_bounds__(kRootThreads) void root_pass_kernel(
     }
     const float *qrow = q + (int64_t)m * off;
     const int64_t nw = tree_words(V);
-    root_scatter(bits + (int64_t)b * nw, rank + (int64_t)b * nw, V, len, base,
-                 qrow + (int64_t)(c1 - 1) * len,
-                 PASS == 2 ? qrow + (int64_t)(c2 - 1) * len : nullptr, mem, q1d, q2d);
+    root_scatter<QL>(bits + (int64_t)b * nw, rank + (int64_t)b * nw, V, len, base,
+                     qrow + (int64_t)(c1 - 1) * len,
+                     PASS == 2 ? qrow + (int64_t)(c2 - 1) * len : nullptr, mem, q1d, q2d,
+                     q_row<QL>(qs, (int64_t)b * m + c1 - 1, qtau, tab),
+                     q_row<QL>(qs, (int64_t)b * m + (PASS == 2 ? c2 : c1) - 1, qtau, tab));
     const float *pu = p + (int64_t)b * (m + 1) * V;
     const int64_t r0 = (int64_t)b * (m + 1);
     const TRow<LOGITS> tv{LOGITS ? nM[r0] : 0.f, LOGITS ? nZ[r0] : 0.0, tab};
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(kRootThreads) void root_pass_kernel(
     }
 }
 
-template <bool LOGITS>
+template <bool LOGITS, bool QL>
 __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
     int m, int V, int64_t max_len, bool vec, const int32_t *__restrict__ parent,
     const int32_t *__restrict__ token, const int64_t *__restrict__ sl_off,
@@ -555,7 +561,8 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
     const float *__restrict__ u_acc, const float *__restrict__ u_fin,
     const uint32_t *__restrict__ bits, const uint32_t *__restrict__ rank,
     const RootPart *__restrict__ rpart, double *__restrict__ Rws, int32_t *__restrict__ n_acc,
-    int32_t *__restrict__ out, int32_t *__restrict__ path)
+    int32_t *__restrict__ out, int32_t *__restrict__ path, const QStats *__restrict__ qs,
+    double qtau)
 {
     __shared__ int s_par[kTreeMaxNodes], s_pos[kTreeMaxNodes], s_tok[kTreeMaxNodes];
     __shared__ double s_lhs[kTreeMaxNodes], s_px[kTreeMaxNodes];
@@ -565,13 +572,15 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
     __shared__ uint32_t s_mem[kRootChunk / 32];
     __shared__ float s_q1[kRootChunk], s_q2[kRootChunk];
     __shared__ RootPart s_part[kRootMaxChunks];
-    __shared__ double tab[LOGITS ? 64 : 1];
+    __shared__ double tab[LOGITS || QL ? 64 : 1];
 
     const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    if (LOGITS) {
+    if (LOGITS || QL) {
         fill_exp2_table(tab);
         __syncthreads();
     }
+    // draft row of node i (1-based): its q conversion
+    auto qrow_f = [&](int i) { return q_row<QL>(qs, (int64_t)b * m + i - 1, qtau, tab); };
     // target row u of this sequence and its value conversion
     auto trow = [&](int u) {
         const int64_t r = (int64_t)b * (m + 1) + u;
@@ -615,7 +624,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
                 pos = min(len - 1, (int)rank_b[x >> 5] + (int)__popc(w & ((1u << (x & 31)) - 1u)));
         }
         const double qx =
-            pos >= 0 ? (double)q[(int64_t)m * off + (int64_t)(i - 1) * len + pos] : 0.0;
+            pos >= 0 ? (double)qrow_f(i)(q[(int64_t)m * off + (int64_t)(i - 1) * len + pos]) : 0.0;
         s_par[i - 1] = linked ? par : -1;
         s_tok[i - 1] = x;
         s_pos[i - 1] = pos;
@@ -649,7 +658,8 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
                 const int pos = s_pos[c2 - 1];
                 double rx = s_px[c2 - 1];
                 if (!fresh1)
-                    rx = (pos >= 0 ? resid(s_px[c2 - 1], 1.0, qrow[(int64_t)(c1 - 1) * len + pos])
+                    rx = (pos >= 0 ? resid(s_px[c2 - 1], 1.0,
+                                           qrow_f(c1)(qrow[(int64_t)(c1 - 1) * len + pos]))
                                    : s_px[c2 - 1]) / P1;
                 if (s_lhs[c2 - 1] < rx) {
                     acc = c2;
@@ -693,9 +703,9 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
             int32_t pick = -1;
             if (owner >= 0) {
                 const int64_t cb = (int64_t)owner * kRootChunk;
-                root_scatter(bits_b, rank_b, V, len, cb, qrow + (int64_t)(c1 - 1) * len,
-                             kr == 2 ? qrow + (int64_t)(c2 - 1) * len : nullptr, s_mem, s_q1,
-                             s_q2);
+                root_scatter<QL>(bits_b, rank_b, V, len, cb, qrow + (int64_t)(c1 - 1) * len,
+                                 kr == 2 ? qrow + (int64_t)(c2 - 1) * len : nullptr, s_mem, s_q1,
+                                 s_q2, qrow_f(c1), qrow_f(kr == 2 ? c2 : c1));
                 const float *pu = p + (int64_t)b * (m + 1) * V;
                 const TRow<LOGITS> tv0 = trow(0);
                 constexpr int TPT = kRootChunk / kTreeThreads;  // 8 consecutive tokens
@@ -770,7 +780,7 @@ __global__ __launch_bounds__(kTreeThreads) void verify_tree_kernel(
                 __syncthreads();  // every thread has read R for this test
             }
             const float *qc = q + (int64_t)m * off + (int64_t)(c - 1) * len;
-            const double sr = residual_update(pu, S, qc, len, V, fresh, P, R, tv, sh);
+            const double sr = residual_update(pu, S, qc, len, V, fresh, P, R, tv, sh, qrow_f(c));
             const double Pn = Poff + sr;
             if (Pn > 0.0) {
                 P = Pn;
@@ -947,12 +957,13 @@ size_t verify_tree_ws_bytes(int B, int m, int V, int64_t max_len)
 
 namespace {
 
-template <bool LOGITS>
+template <bool LOGITS, bool QL = false>
 hipError_t tree_kernels(hipStream_t s, int B, int m, int V, const int32_t *parent,
                         const int32_t *token, const int64_t *sl_off, const int32_t *sl_ids,
                         const float *q, const float *x, const float *nM, const double *nZ,
                         const float *u_acc, const float *u_fin, int64_t max_len, int32_t *n_acc,
-                        int32_t *out, int32_t *path, void *ws, hipEvent_t t0, hipEvent_t t1)
+                        int32_t *out, int32_t *path, void *ws, hipEvent_t t0, hipEvent_t t1,
+                        const QStats *qs = nullptr, double qtau = 1.0)
 {
     char *base = reinterpret_cast<char *>(ws);
     double *R = reinterpret_cast<double *>(base);
@@ -969,20 +980,20 @@ hipError_t tree_kernels(hipStream_t s, int B, int m, int V, const int32_t *paren
     if (e != hipSuccess)
         return e;
     const dim3 rgrid((unsigned)root_chunks(V), (unsigned)B);
-    hipLaunchKernelGGL((root_pass_kernel<1, LOGITS>), rgrid, dim3(kRootThreads), 0, s, m, V,
+    hipLaunchKernelGGL((root_pass_kernel<1, LOGITS, QL>), rgrid, dim3(kRootThreads), 0, s, m, V,
                        max_len, parent, sl_off, q, x, nM, nZ, (const uint32_t *)bits,
-                       (const uint32_t *)rank, rpart);
+                       (const uint32_t *)rank, rpart, qs, qtau);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    hipLaunchKernelGGL((root_pass_kernel<2, LOGITS>), rgrid, dim3(kRootThreads), 0, s, m, V,
+    hipLaunchKernelGGL((root_pass_kernel<2, LOGITS, QL>), rgrid, dim3(kRootThreads), 0, s, m, V,
                        max_len, parent, sl_off, q, x, nM, nZ, (const uint32_t *)bits,
-                       (const uint32_t *)rank, rpart);
+                       (const uint32_t *)rank, rpart, qs, qtau);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    return launch_timed(verify_tree_kernel<LOGITS>, dim3((unsigned)B), dim3(kTreeThreads), s,
+    return launch_timed(verify_tree_kernel<LOGITS, QL>, dim3((unsigned)B), dim3(kTreeThreads), s,
                         nullptr, t1, m, V, max_len, vec, parent, token, sl_off, sl_ids, q, x, nM,
                         nZ, u_acc, u_fin, (const uint32_t *)bits, (const uint32_t *)rank,
-                        (const RootPart *)rpart, R, n_acc, out, path);
+                        (const RootPart *)rpart, R, n_acc, out, path, qs, qtau);
 }
 
 }  // namespace
@@ -1005,12 +1016,14 @@ size_t verify_tree_logits_ws_bytes(int B, int m, int V, int64_t max_len)
            (rows * 4 + 255) / 256 * 256 + softmax_ws_bytes((int64_t)rows, V);
 }
 
-hipError_t verify_tree_logits_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
-                                     const int32_t *token, const int64_t *sl_off,
-                                     const int32_t *sl_ids, const float *q, const float *logits,
-                                     const float *u_acc, const float *u_fin, int64_t max_len,
-                                     int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
-                                     hipEvent_t t0, hipEvent_t t1)
+// QL: q from the draft logits (q points to them) and the rows' statistics qs
+template <bool QL>
+static hipError_t tree_logits_kernels(hipStream_t s, int B, int m, int V, const int32_t *parent,
+                               const int32_t *token, const int64_t *sl_off,
+                               const int32_t *sl_ids, const float *q, const float *logits,
+                               const float *u_acc, const float *u_fin, int64_t max_len,
+                               int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
+                               hipEvent_t t0, hipEvent_t t1, const QStats *qs, double qtau)
 {
     const int rows = B * (m + 1);
     char *b = reinterpret_cast<char *>(ws) + (verify_tree_ws_bytes(B, m, V, max_len) + 255) /
@@ -1028,8 +1041,33 @@ hipError_t verify_tree_logits_launch(hipStream_t s, int B, int m, int V, const i
                        rows, nseg, smax, ssum, nM, nZ);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
-    return tree_kernels<true>(s, B, m, V, parent, token, sl_off, sl_ids, q, logits, nM, nZ,
-                              u_acc, u_fin, max_len, n_acc, out, path, ws, t0, t1);
+    return tree_kernels<true, QL>(s, B, m, V, parent, token, sl_off, sl_ids, q, logits, nM, nZ,
+                                  u_acc, u_fin, max_len, n_acc, out, path, ws, t0, t1, qs, qtau);
+}
+
+hipError_t verify_tree_logits_launch(hipStream_t s, int B, int m, int V, const int32_t *parent,
+                                     const int32_t *token, const int64_t *sl_off,
+                                     const int32_t *sl_ids, const float *q, const float *logits,
+                                     const float *u_acc, const float *u_fin, int64_t max_len,
+                                     int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
+                                     hipEvent_t t0, hipEvent_t t1)
+{
+    return tree_logits_kernels<false>(s, B, m, V, parent, token, sl_off, sl_ids, q, logits, u_acc,
+                                      u_fin, max_len, n_acc, out, path, ws, t0, t1, nullptr, 1.0);
+}
+
+hipError_t verify_tree_logits_qstats_launch(hipStream_t s, int B, int m, int V,
+                                            const int32_t *parent, const int32_t *token,
+                                            const int64_t *sl_off, const int32_t *sl_ids,
+                                            const float *draft_logits, const QStats *qs,
+                                            float temperature, const float *logits,
+                                            const float *u_acc, const float *u_fin,
+                                            int64_t max_len, int32_t *n_acc, int32_t *out,
+                                            int32_t *path, void *ws, hipEvent_t t0, hipEvent_t t1)
+{
+    return tree_logits_kernels<true>(s, B, m, V, parent, token, sl_off, sl_ids, draft_logits,
+                                     logits, u_acc, u_fin, max_len, n_acc, out, path, ws, t0, t1,
+                                     qs, (double)temperature);
 }
 
 }  // namespace ds

@@ -50,7 +50,8 @@ class ChainArgs(C.Structure):
                 ("scores", _vp), ("sel", _vp), ("n_sel", _vp), ("sl_len", _vp),
                 ("sl_off", _vp), ("sl_ids", _vp), ("logits", _vp), ("q", _vp),
                 ("token", _vp), ("err_flag", _vp), ("ws", _vp), ("ws_bytes", _sz),
-                ("W_pos", _vp), ("head_events", _vp), ("sync_events", _vp)]
+                ("W_pos", _vp), ("head_events", _vp), ("sync_events", _vp),
+                ("qstats", _vp)]
 
 
 _SIGS = {
@@ -79,6 +80,12 @@ _SIGS = {
                               _sz]),
     "ds_sample_workspace_bytes": (_sz, [_i, _i, _i64]),
     "ds_shortlist_sample": (_i, [_vp, _i, _i, _vp, _vp, _vp, _f, _vp, _i64, _vp, _vp, _vp, _sz]),
+    "ds_shortlist_sample_stats": (_i, [_vp, _i, _i, _vp, _vp, _vp, _f, _vp, _i64, _vp, _vp, _vp,
+                                       _sz]),
+    "ds_verify_reject_logits_qstats": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _f, _vp,
+                                            _vp, _vp, _vp, _vp, _vp, _sz]),
+    "ds_verify_tree_logits_qstats": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp,
+                                          _vp, _vp, _i64, _vp, _vp, _vp, _vp, _sz]),
     "ds_softmax_workspace_bytes": (_sz, [_i, _i]),
     "ds_target_softmax": (_i, [_vp, _i, _i, _vp, _vp, _vp, _sz]),
     "ds_verify_workspace_bytes": (_sz, [_i, _i, _i]),
@@ -351,6 +358,24 @@ def shortlist_sample(sl_off, sl_ids, logits, temperature, u, token, q, ws, *, ma
         int(max_len), _p(token), _p(q), _p(ws), _nbytes(ws)))
 
 
+# bytes of one row's statistics (ds_qstats: fp32 M, padding, fp64 1 / Z)
+QSTATS_BYTES = 16
+
+
+def qstats_buffer(rows: int, device="cuda") -> torch.Tensor:
+    """Storage for `rows` ds_qstats records."""
+    return torch.empty(max(rows, 1) * QSTATS_BYTES, dtype=torch.uint8, device=device)
+
+
+def shortlist_sample_stats(sl_off, sl_ids, logits, temperature, u, token, qstats, ws, *,
+                           max_len, m=1, stream=None):
+    """ds_shortlist_sample without q: tokens and per-row statistics."""
+    G = sl_off.shape[0] - 1
+    _check("ds_shortlist_sample_stats", lib.ds_shortlist_sample_stats(
+        _s(stream), G, m, _p(sl_off), _p(sl_ids), _p(logits), float(temperature), _p(u),
+        int(max_len), _p(token), _p(qstats), _p(ws), _nbytes(ws)))
+
+
 def target_softmax(logits, p, ws, *, stream=None):
     V = logits.shape[-1]
     _check("ds_target_softmax", lib.ds_target_softmax(
@@ -377,6 +402,17 @@ def verify_reject_logits(draft, sl_off, sl_ids, q, logits, u_acc, u_fin, n_acc, 
     _check("ds_verify_reject_logits", lib.ds_verify_reject_logits(
         _s(stream), B, T, V, _p(draft), _p(sl_off), _p(sl_ids), _p(q), _p(logits), _p(u_acc),
         _p(u_fin), _p(n_acc), _p(out), _p(ws), _nbytes(ws)))
+
+
+def verify_reject_logits_qstats(draft, sl_off, sl_ids, draft_logits, qstats, temperature,
+                                logits, u_acc, u_fin, n_acc, out, ws, *, stream=None):
+    """verify_reject_logits with q from the draft logits and row statistics."""
+    T, B = draft.shape
+    V = logits.shape[-1]
+    _check("ds_verify_reject_logits_qstats", lib.ds_verify_reject_logits_qstats(
+        _s(stream), B, T, V, _p(draft), _p(sl_off), _p(sl_ids), _p(draft_logits), _p(qstats),
+        float(temperature), _p(logits), _p(u_acc), _p(u_fin), _p(n_acc), _p(out), _p(ws),
+        _nbytes(ws)))
 
 
 def verify_reject_noalloc(draft, sl_off, sl_ids, q, p, u_acc, u_fin, n_acc, out, *,
@@ -418,6 +454,18 @@ def verify_tree_logits(parent, token, sl_off, sl_ids, q, logits, u_acc, u_fin, m
         _s(stream), B, m, V, _p(parent), _p(token), _p(sl_off), _p(sl_ids), _p(q), _p(logits),
         _p(u_acc), _p(u_fin), int(max_len), _p(n_acc), _p(out), _p(path), _p(ws),
         _nbytes(ws)))
+
+
+def verify_tree_logits_qstats(parent, token, sl_off, sl_ids, draft_logits, qstats, temperature,
+                              logits, u_acc, u_fin, max_len, n_acc, out, path, ws, *,
+                              stream=None):
+    """verify_tree_logits with q from the draft logits and row statistics."""
+    B, m = parent.shape
+    V = logits.shape[-1]
+    _check("ds_verify_tree_logits_qstats", lib.ds_verify_tree_logits_qstats(
+        _s(stream), B, m, V, _p(parent), _p(token), _p(sl_off), _p(sl_ids), _p(draft_logits),
+        _p(qstats), float(temperature), _p(logits), _p(u_acc), _p(u_fin), int(max_len),
+        _p(n_acc), _p(out), _p(path), _p(ws), _nbytes(ws)))
 
 
 def dense_lm_head(W, h, logits, *, stream=None, events=None):

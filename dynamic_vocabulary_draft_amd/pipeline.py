@@ -57,11 +57,23 @@ def shortlist_bounds(cfg: syn.Config, cluster_size: np.ndarray) -> np.ndarray:
 
 
 class DraftStep:
+    """One draft step (chain or tree) and its verification from target
+    logits.  ``q_mode``: "dense" writes the draft distribution q (the
+    sampler's output, read back by verification and by host()); "stats"
+    (temperature > 0) writes each draft row's statistics instead and
+    verification recomputes q from the draft logits, bit for bit the same
+    values, so tokens and verification outputs are those of "dense"."""
+
     def __init__(self, wl: syn.Workload, device="cuda", W: torch.Tensor | None = None,
-                 temperature: float = 1.0):
+                 temperature: float = 1.0, q_mode: str = "dense"):
         cfg = self.cfg = wl.cfg
         self.device = device
         self.temperature = float(temperature)
+        if q_mode not in ("dense", "stats"):
+            raise ValueError("q_mode is 'dense' or 'stats'")
+        if q_mode == "stats" and not self.temperature > 0.0:
+            raise ValueError("q_mode 'stats' needs a temperature > 0")
+        self.q_mode = q_mode
         dev = lambda a: to_dev(a, device)  # noqa: E731
         self.W = W if W is not None else dev(wl.W)
         R = wl.router
@@ -91,7 +103,10 @@ class DraftStep:
         self.sl_ids = torch.empty(max(self.capacity, 1), **i32)
         m = cfg.tree_nodes
         self.logits = torch.empty(max(self.capacity * m, 1), **f32)
-        self.q = torch.empty(max(self.capacity * m, 1), **f32)
+        if q_mode == "dense":
+            self.q, self.qstats = torch.empty(max(self.capacity * m, 1), **f32), None
+        else:  # one ds_qstats record per draft row
+            self.q, self.qstats = None, N.qstats_buffer(B * m if cfg.is_tree else T * B, device)
         self.token = torch.empty((B, m) if cfg.is_tree else (T, B), **i32)
         nbytes = N.draft_chain_workspace_bytes(B, T, V, cfg.r, int(self.max_len.max()))
         if cfg.is_tree:
@@ -150,7 +165,8 @@ class DraftStep:
             scores=p(self.scores), sel=p(self.sel),
             n_sel=p(self.n_sel), sl_len=p(self.sl_len), sl_off=p(self.sl_off),
             sl_ids=p(self.sl_ids), logits=p(self.logits), q=p(self.q), token=p(self.token),
-            err_flag=p(self.err_flag), ws=p(self.ws), ws_bytes=self.ws.numel())
+            err_flag=p(self.err_flag), ws=p(self.ws), ws_bytes=self.ws.numel(),
+            qstats=p(self.qstats))
 
     def set_W(self, W: torch.Tensor) -> None:
         """Point the head at another (identical) copy of W."""
@@ -187,11 +203,25 @@ class DraftStep:
         N.draft_chain(self._args, stream, self.router_stream)
 
     def verify(self, stream=None) -> None:
+        stats = self.q_mode == "stats"
         if self.cfg.is_tree:
+            if stats:
+                N.verify_tree_logits_qstats(self.parent, self.token, self.sl_off, self.sl_ids,
+                                            self.logits, self.qstats, self.temperature,
+                                            self.target_logits, self.u_acc, self.u_fin,
+                                            int(self.max_len[0]), self.n_acc, self.out,
+                                            self.path, self.verify_ws, stream=stream)
+                return
             N.verify_tree_logits(self.parent, self.token, self.sl_off, self.sl_ids, self.q,
                                  self.target_logits, self.u_acc, self.u_fin,
                                  int(self.max_len[0]), self.n_acc, self.out, self.path,
                                  self.verify_ws, stream=stream)
+            return
+        if stats:
+            N.verify_reject_logits_qstats(self.token, self.sl_off, self.sl_ids, self.logits,
+                                          self.qstats, self.temperature, self.target_logits,
+                                          self.u_acc, self.u_fin, self.n_acc, self.out,
+                                          self.verify_ws, stream=stream)
             return
         N.verify_reject_logits(self.token, self.sl_off, self.sl_ids, self.q, self.target_logits,
                                self.u_acc, self.u_fin, self.n_acc, self.out, self.verify_ws,
@@ -230,6 +260,11 @@ class DraftStep:
         N.gathered_lm_head(self.W, self.h[:, 1:], self.sl_off, self.sl_ids, self.max_rows[0],
                            self.logits, self.head_ws, G=B, m=m, ldh_g=(1 + m) * d,
                            stream=stream, events=None if ev is None else (ev[0], ev[1]))
+        if self.q_mode == "stats":
+            N.shortlist_sample_stats(self.sl_off, self.sl_ids, self.logits, self.temperature,
+                                     self.u_draft, self.token, self.qstats, self.ws,
+                                     max_len=int(self.max_len[0]), m=m, stream=stream)
+            return
         N.shortlist_sample(self.sl_off, self.sl_ids, self.logits, self.temperature,
                            self.u_draft, self.token, self.q, self.ws,
                            max_len=int(self.max_len[0]), m=m, stream=stream)
@@ -243,7 +278,12 @@ class DraftStep:
         r["sl_ids"] = self.sl_ids[:n].cpu().numpy()
         mm = self.cfg.tree_nodes
         r["logits"] = self.logits[: n * mm].cpu().numpy()
-        r["q"] = self.q[: n * mm].cpu().numpy()
+        if self.q is not None:
+            r["q"] = self.q[: n * mm].cpu().numpy()
+        else:  # fp32 M at byte 0, fp64 1/Z at byte 8 of each 16-byte record
+            raw = self.qstats.cpu().numpy()
+            r["qstats_M"] = raw.view(np.float32)[0::4].copy()
+            r["qstats_rZ"] = raw.view(np.float64)[1::2].copy()
         if self.target_logits is not None:
             r.update(n_acc=self.n_acc.cpu().numpy(), out=self.out.cpu().numpy(),
                      p=self.target_probs().cpu().numpy())

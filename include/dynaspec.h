@@ -277,6 +277,29 @@ ds_status ds_shortlist_sample(hipStream_t s, int G, int m, const int64_t *sl_off
                               size_t ws_bytes);
 
 /*
+ * ds_shortlist_sample without writing q, for temperature > 0 [same passages
+ * as ds_shortlist_sample]: the same token per row, and per row its
+ * statistics in place of q, qstats[row] = {M, rZ}, such that the q value
+ * ds_shortlist_sample writes for logit l_j of the row is exactly
+ * (float)(exp((l_j - M) / T) * rZ) evaluated as the library does (fp64
+ * exponent); the verifiers' _qstats forms recompute q that way, bit for
+ * bit.  Empty rows give token -1 and rZ = 0.  temperature must be > 0 (else
+ * DS_EINVAL); other arguments, limits and the workspace as
+ * ds_shortlist_sample.  Writes G*m tokens and G*m statistics, not the
+ * sum over rows of |S_g| q values.
+ */
+typedef struct {
+    float M;
+    int32_t pad;
+    double rZ;
+} ds_qstats;
+ds_status ds_shortlist_sample_stats(hipStream_t s, int G, int m, const int64_t *sl_off,
+                                    const int32_t *sl_ids, const float *logits,
+                                    float temperature, const float *u, int64_t max_len,
+                                    int32_t *token, ds_qstats *qstats, void *ws,
+                                    size_t ws_bytes);
+
+/*
  * Full-vocabulary target distribution p = softmax(target logits) per row
  * (fp64 exponent and sum, fp32 output) [A: the target verifies over the full
  * vocabulary].  logits and p are [rows][V] fp32, V <= 2^20.
@@ -324,6 +347,24 @@ ds_status ds_verify_reject_logits(hipStream_t s, int B, int T, int V, const int3
                                   const int64_t *sl_off, const int32_t *sl_ids, const float *q,
                                   const float *logits, const float *u_acc, const float *u_fin,
                                   int32_t *n_acc, int32_t *out, void *ws, size_t ws_bytes);
+
+/*
+ * ds_verify_reject_logits with q given by the draft logits and their rows'
+ * statistics instead of the q array [same passages as ds_verify_reject]:
+ * draft_logits in the sampler's layout (m = 1), qstats [T*B] from
+ * ds_shortlist_sample_stats over them with the same temperature (> 0).
+ * Every q value the verification reads is recomputed from its logit and row
+ * statistics, which gives the value ds_shortlist_sample writes, so the
+ * outputs equal ds_verify_reject_logits given that q, bit for bit.  Limits
+ * and workspace as ds_verify_reject_logits.
+ */
+ds_status ds_verify_reject_logits_qstats(hipStream_t s, int B, int T, int V,
+                                         const int32_t *draft, const int64_t *sl_off,
+                                         const int32_t *sl_ids, const float *draft_logits,
+                                         const ds_qstats *qstats, float temperature,
+                                         const float *logits, const float *u_acc,
+                                         const float *u_fin, int32_t *n_acc, int32_t *out,
+                                         void *ws, size_t ws_bytes);
 
 /*
  * Allocation-free ds_verify_reject, for callers that cannot allocate device
@@ -406,6 +447,24 @@ ds_status ds_verify_tree_logits(hipStream_t s, int B, int m, int V, const int32_
                                 const float *u_acc, const float *u_fin, int64_t max_len,
                                 int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
                                 size_t ws_bytes);
+
+/*
+ * ds_verify_tree_logits with q given by the draft logits and their rows'
+ * statistics instead of the q array [same passages as ds_verify_tree]:
+ * draft_logits in the sampler's layout (group b, head row = node), qstats
+ * [B*m] from ds_shortlist_sample_stats over them with the same temperature
+ * (> 0).  The outputs equal ds_verify_tree_logits given the q that
+ * ds_shortlist_sample writes, bit for bit.  Limits and workspace as
+ * ds_verify_tree_logits.
+ */
+ds_status ds_verify_tree_logits_qstats(hipStream_t s, int B, int m, int V,
+                                       const int32_t *parent, const int32_t *token,
+                                       const int64_t *sl_off, const int32_t *sl_ids,
+                                       const float *draft_logits, const ds_qstats *qstats,
+                                       float temperature, const float *logits,
+                                       const float *u_acc, const float *u_fin, int64_t max_len,
+                                       int32_t *n_acc, int32_t *out, int32_t *path, void *ws,
+                                       size_t ws_bytes);
 
 /*
  * Dense LM head of the full drafter over every token, the O(|V| d)
@@ -516,6 +575,11 @@ ds_status ds_router_train_step(hipStream_t s, const ds_router_train_args *a);
  *                stamped at the start of the first and the end of the last
  *                head kernel of position t (the kernels' own begin and end,
  *                so hipEventElapsedTime gives the head's execution time).
+ *   qstats       [T*B] row statistics; when q is NULL (temperature > 0) the
+ *                sampler writes these instead of q, as
+ *                ds_shortlist_sample_stats does (the same tokens), for
+ *                ds_verify_reject_logits_qstats.  One of q and qstats is
+ *                required.
  */
 typedef struct {
     int B, T, V, d, r, M;
@@ -547,6 +611,7 @@ typedef struct {
     const void *const *W_pos;   /* HOST [T] or NULL                */
     hipEvent_t *head_events;    /* HOST [2T] or NULL               */
     hipEvent_t *sync_events;    /* HOST [2T+1], required           */
+    ds_qstats *qstats;          /* [T][B], used when q is NULL     */
 } ds_draft_chain_args;
 
 size_t ds_draft_chain_workspace_bytes(int B, int T, int V, int r, int64_t max_len);

@@ -175,6 +175,44 @@ def test_select_build_head_sample_verify_reject_bad_arguments(N):
     assert L.ds_draft_chain(None, None, C.byref(a)) == 1
 
 
+def test_row_statistics_entry_points_reject_bad_arguments(N):
+    """The sampler and verifiers that take per-row draft statistics in place
+    of q: a positive temperature and the statistics are required; the other
+    checks are those of the q forms."""
+    L = N.lib
+    smp = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
+        ("s", None), ("G", 2), ("m", 1), ("sl_off", FAKE), ("sl_ids", FAKE), ("logits", FAKE),
+        ("tau", C.c_float(1.0)), ("u", FAKE), ("max_len", 100), ("token", FAKE),
+        ("qstats", FAKE), ("ws", FAKE), ("ws_bytes", 0)]]
+    assert L.ds_shortlist_sample_stats(*smp(tau=C.c_float(0.0))) == 1  # argmax keeps q
+    assert L.ds_shortlist_sample_stats(*smp(qstats=None)) == 1
+    assert L.ds_shortlist_sample_stats(*smp(max_len=(1 << 20) + 1)) == 3
+    assert L.ds_shortlist_sample_stats(*smp()) == 1  # workspace too small
+    ver = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
+        ("s", None), ("B", 2), ("T", 3), ("V", 100), ("draft", FAKE), ("sl_off", FAKE),
+        ("sl_ids", FAKE), ("dl", FAKE), ("qstats", FAKE), ("tau", C.c_float(1.0)),
+        ("logits", FAKE), ("u_acc", FAKE), ("u_fin", FAKE), ("n_acc", FAKE), ("out", FAKE),
+        ("ws", FAKE), ("ws_bytes", 0)]]
+    assert L.ds_verify_reject_logits_qstats(*ver(qstats=None)) == 1
+    assert L.ds_verify_reject_logits_qstats(*ver(tau=C.c_float(0.0))) == 1
+    assert L.ds_verify_reject_logits_qstats(*ver(dl=None)) == 1
+    assert L.ds_verify_reject_logits_qstats(*ver(T=65)) == 3
+    assert L.ds_verify_reject_logits_qstats(*ver(B=2048, T=32, ws_bytes=1 << 40)) == 3
+    assert L.ds_verify_reject_logits_qstats(*ver()) == 1  # workspace too small
+    tv = lambda **kw: [kw.get(k, v) for k, v in [  # noqa: E731
+        ("s", None), ("B", 2), ("m", 3), ("V", 100), ("parent", FAKE), ("token", FAKE),
+        ("sl_off", FAKE), ("sl_ids", FAKE), ("dl", FAKE), ("qstats", FAKE),
+        ("tau", C.c_float(1.0)), ("logits", FAKE), ("u_acc", FAKE), ("u_fin", FAKE),
+        ("max_len", 50), ("n_acc", FAKE), ("out", FAKE), ("path", FAKE), ("ws", FAKE),
+        ("ws_bytes", 0)]]
+    assert L.ds_verify_tree_logits_qstats(*tv(qstats=None)) == 1
+    assert L.ds_verify_tree_logits_qstats(*tv(tau=C.c_float(float("nan")))) == 1
+    assert L.ds_verify_tree_logits_qstats(*tv(m=0)) == 1
+    assert L.ds_verify_tree_logits_qstats(*tv(B=2048, m=64, ws_bytes=1 << 40)) == 3
+    assert L.ds_verify_tree_logits_qstats(*tv()) == 1  # workspace too small
+    assert C.sizeof(N.ChainArgs) == N.ChainArgs.qstats.offset + 8  # the last field
+
+
 def test_draft_chain_requires_sync_events(N):
     """Arguments that pass every other check, with no stream-ordering
     events: rejected on the host before anything is enqueued."""
@@ -191,6 +229,13 @@ def test_draft_chain_requires_sync_events(N):
                     sl_off=f, sl_ids=f, logits=f, q=f, token=f, err_flag=None, ws=f,
                     ws_bytes=1 << 30)
     assert L.ds_draft_chain(None, None, C.byref(a)) == 1
+    a.q = None  # no q: the row statistics are then required, with temperature > 0
+    ev_ok = (C.c_void_p * (2 * T + 1))(*([f] * (2 * T + 1)))
+    a.sync_events = C.cast(ev_ok, C.c_void_p)
+    assert L.ds_draft_chain(None, None, C.byref(a)) == 1
+    a.qstats, a.temperature = f, 0.0
+    assert L.ds_draft_chain(None, None, C.byref(a)) == 1
+    a.q, a.qstats, a.temperature, a.sync_events = f, None, 1.0, None
     ev = (C.c_void_p * (2 * T + 1))(*([f] * (2 * T)), None)  # one handle missing
     a.sync_events = C.cast(ev, C.c_void_p)
     assert L.ds_draft_chain(None, None, C.byref(a)) == 1
