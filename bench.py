@@ -670,7 +670,8 @@ def run_draft(index, *, n_steps, warmup, instances, replicas, eager, static=None
         if cfg.is_tree:
             raise SystemExit("--static drafts chains; pick a chain workload")
         static_ids = syn.static_shortlist(cfg, static_size)
-        steps = [StaticStep(wl, static_ids, W=W, packed=static == "packed") for wl in wls]
+        steps = [StaticStep(wl, static_ids, W=W, packed=static == "packed", q_mode=q_mode)
+                 for wl in wls]
     else:
         steps = [DraftStep(wl, W=W, q_mode=q_mode) for wl in wls]
     del wls
@@ -842,7 +843,7 @@ def run_draft(index, *, n_steps, warmup, instances, replicas, eager, static=None
                        % (static, static_ids.shape[0])),
               "launch": mode,
               "draft_q": ("row statistics (q recomputed where verification reads it)"
-                          if q_mode == "stats" and static_ids is None else "written")}
+                          if q_mode == "stats" else "written")}
     return {"cfg": cfg, "static_ids": static_ids, "value": round(value, 1), "warmup": warmup,
             "ms_per_step": round(wall * 1e3 / n_steps, 4),
             "step_ms": {"median": round(float(np.median(step_ms)), 4),

@@ -303,11 +303,14 @@ class StaticStep:
 
     def __init__(self, wl: syn.Workload, static_ids: np.ndarray, device="cuda",
                  W: torch.Tensor | None = None, packed: bool = False,
-                 temperature: float = 1.0):
+                 temperature: float = 1.0, q_mode: str = "dense"):
         cfg = self.cfg = wl.cfg
         assert not cfg.is_tree, "the static step drafts chains"
         self.device = device
         self.temperature = float(temperature)
+        if q_mode not in ("dense", "stats") or (q_mode == "stats" and not self.temperature > 0):
+            raise ValueError("q_mode is 'dense', or 'stats' with a temperature > 0")
+        self.q_mode = q_mode
         self.packed = packed
         dev = lambda a: to_dev(a, device)  # noqa: E731
         B, T, V, d = cfg.B, cfg.T, cfg.V, cfg.d
@@ -328,7 +331,10 @@ class StaticStep:
             N.pack_rows(self.W, self.static_ids, self.slab)
             self.head_ids = dev(np.tile(np.arange(L, dtype=np.int32), T * B))
         self.logits = torch.empty(max(T * B * L, 1), **f32)
-        self.q = torch.empty(max(T * B * L, 1), **f32)
+        if q_mode == "dense":
+            self.q, self.qstats = torch.empty(max(T * B * L, 1), **f32), None
+        else:
+            self.q, self.qstats = None, N.qstats_buffer(T * B, device)
         self.token = torch.empty(T, B, **i32)
         self.err_flag = torch.zeros(1, **i32)
         self.head_ws = N.workspace(N.head_workspace_bytes(B, 1, L if packed else V), device)
@@ -367,11 +373,23 @@ class StaticStep:
                                self.logits, self.head_ws, G=B, m=1, ldh_g=(T + 1) * d,
                                stream=stream,
                                events=None if ev is None else (ev[2 * t], ev[2 * t + 1]))
+            if self.q_mode == "stats":
+                N.shortlist_sample_stats(self.sl_off[rb:rb + B + 1], self.sl_ids, self.logits,
+                                         self.temperature, self.u_draft[t], self.token[t],
+                                         self.qstats[rb * N.QSTATS_BYTES:], self.sample_ws,
+                                         max_len=self.L, stream=stream)
+                continue
             N.shortlist_sample(self.sl_off[rb:rb + B + 1], self.sl_ids, self.logits,
                                self.temperature, self.u_draft[t], self.token[t], self.q,
                                self.sample_ws, max_len=self.L, stream=stream)
 
     def verify(self, stream=None) -> None:
+        if self.q_mode == "stats":
+            N.verify_reject_logits_qstats(self.token, self.sl_off, self.sl_ids, self.logits,
+                                          self.qstats, self.temperature, self.target_logits,
+                                          self.u_acc, self.u_fin, self.n_acc, self.out,
+                                          self.verify_ws, stream=stream)
+            return
         N.verify_reject_logits(self.token, self.sl_off, self.sl_ids, self.q, self.target_logits,
                                self.u_acc, self.u_fin, self.n_acc, self.out, self.verify_ws,
                                stream=stream)
@@ -394,7 +412,8 @@ class StaticStep:
         r = {k: getattr(self, k).cpu().numpy() for k in ("sl_off", "token", "err_flag")}
         r["sl_ids"] = self.sl_ids.cpu().numpy()
         r["logits"] = self.logits.cpu().numpy()
-        r["q"] = self.q.cpu().numpy()
+        if self.q is not None:
+            r["q"] = self.q.cpu().numpy()
         if self.target_logits is not None:
             r.update(n_acc=self.n_acc.cpu().numpy(), out=self.out.cpu().numpy(),
                      p=self.target_probs().cpu().numpy())

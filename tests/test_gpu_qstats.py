@@ -148,3 +148,19 @@ def test_sample_stats_empty_and_ragged_rows():
         rZ = raw.view(np.float64)[1::2]
         assert (tok_s.cpu().numpy()[2:4] == -1).all() and (rZ[2:4] == 0.0).all()
         assert (rZ[[0, 1, 4, 5, 6, 7]] > 0.0).all()
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_static_stats_step_matches_q_step(packed):
+    """The static baseline with the row-statistics sampler: the same tokens
+    and verification outputs as with q."""
+    from dynamic_vocabulary_draft_amd.pipeline import StaticStep
+    cfg = _configs()["small-bf16-b3"]
+    wl = syn.make_workload(cfg.index, cfg=cfg)
+    ids = syn.static_shortlist(cfg, cfg.V // 3)
+    res = {}
+    for mode in ("dense", "stats"):
+        step = StaticStep(wl, ids, packed=packed, q_mode=mode)
+        step.step()
+        res[mode] = step.host()
+    _same(res["dense"], res["stats"], ("token", "logits", "n_acc", "out"))
