@@ -603,7 +603,8 @@ typedef struct {
     int32_t *n_sel, *sl_len;    /* [T][B]                          */
     int64_t *sl_off;            /* [T*B+1], sl_off[0] read as base */
     int32_t *sl_ids;            /* [capacity]                      */
-    float *logits, *q;          /* [capacity]                      */
+    float *logits;              /* [capacity]                      */
+    float *q;                   /* [capacity], or NULL: qstats     */
     int32_t *token;             /* [T][B]                          */
     int32_t *err_flag;          /* 1 int32 or NULL                 */
     void *ws;                   /* ds_draft_chain_workspace_bytes  */
