@@ -66,7 +66,7 @@ def _q_from_stats(r, cfg, tau):
 KEYS = ("token", "sl_off", "sl_ids", "logits", "n_acc", "out", "path")
 
 
-@pytest.mark.parametrize("tau", [1.0, 0.7])
+@pytest.mark.parametrize("tau", [1.0, 0.7, 0.1, 2.5])
 @pytest.mark.parametrize("name", list(_configs()))
 def test_stats_step_matches_q_step(name, tau):
     cfg = _configs()[name]
