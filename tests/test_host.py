@@ -337,6 +337,24 @@ def test_traffic_from_scales_counters(tmp_path):
     assert t["launches"] == 2 and t["workload"] == "w"
 
 
+def test_committed_traffic_matches_head_sources():
+    """The committed head traffic counters were taken from the GEMV head's
+    current sources for the default workload, so the default bench line
+    reports `roofline.traffic` (bench.py drops it when the hash or the
+    workload differs).  An edit to those sources needs new counters."""
+    import json
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    assert t["kernel_source_sha256"] == bench.head_source_sha(), \
+        "head sources changed since the traffic counters were taken"
+    assert t["workload"] == syn.CONFIGS[1].name
+    assert t["head_kernel"] == "head_gemv_kernel"
+    assert 1.0 <= t["traffic_over_algorithmic"] < 1.05
+
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py measures one GPU: asked for more it says so and exits
     non-zero before touching a device."""
