@@ -21,15 +21,16 @@ Printed: one JSON line (value = draft tokens/s of the whole step), with
 duration; the duration comes from HIP events stamped at the head kernels'
 own start and end, on eager replays of the timed steps, since events cannot
 be timed inside graphs) and `cpu_baseline` (the CPU oracle, one core, on a
-bounded sample of the same workload).  `roofline.traffic` is the head's
-measured HBM bytes per launch when profiles/head_gemv_traffic.json was made
-from the current head sources for this workload (see --pmc-probe).
+bounded sample of the same workload).  `roofline.traffic` (in the line and
+in each workload of its `extra` block) is the head's measured HBM bytes per
+launch when that workload's file under profiles/ (TRAFFIC_FILES) was made
+from the current sources of its head kernel (see --pmc-probe).
 
-HBM traffic of the head (two profiler passes, then one parse):
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -- python3 bench.py --pmc-probe
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -- python3 bench.py --pmc-probe
+HBM traffic of a workload's head (two profiler passes, then one parse):
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -- python3 bench.py --config C --pmc-probe
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -- python3 bench.py --config C --pmc-probe
     python3 bench.py --traffic-from OUT/fetch OUT/write
-(all three with the same --probe-file)
+(all three with the same --probe-file; the parse writes the workload's file)
 The probe runs eager steps of the workload, then a 1 GiB device-to-device
 copy; each counter of the head is scaled by known bytes / the counter of
 that copy.
@@ -49,20 +50,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "head_gemv_traffic.json")
-# the GEMV head's translation unit: the traffic counters hold while it is unchanged
-HEAD_SOURCES = ["dynamic_vocabulary_draft_amd/csrc/head.hip",
-                "dynamic_vocabulary_draft_amd/csrc/common.h",
-                "dynamic_vocabulary_draft_amd/csrc/kernels.h"]
+# committed HBM traffic counters of each workload's head (--traffic-from)
+TRAFFIC_FILES = {1: "head_gemv_traffic.json", 2: "head_union_traffic_llama3-8b-b32.json",
+                 3: "head_gathered_traffic_qwen3-8b-8x64.json",
+                 4: "head_union_traffic_gemma3-12b-b64.json"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", TRAFFIC_FILES[1])
+# each head kernel's translation unit: its counters hold while it is unchanged
+_CSRC = "dynamic_vocabulary_draft_amd/csrc/"
+_MFMA_SOURCES = [_CSRC + f for f in ("head_mfma.hip", "mfma_tile.h", "common.h", "kernels.h")]
+HEAD_SOURCES = {"head_gemv_kernel": [_CSRC + f for f in ("head.hip", "common.h", "kernels.h")],
+                "head_union_kernel": _MFMA_SOURCES, "head_gathered_kernel": _MFMA_SOURCES}
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def head_source_sha() -> str:
+def head_source_sha(kernel: str = "head_gemv_kernel") -> str:
     h = hashlib.sha256()
-    for f in HEAD_SOURCES:
+    for f in HEAD_SOURCES[kernel]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -128,6 +134,15 @@ def head_kernel_name(cfg) -> str:
     return "head_gemv_kernel"
 
 
+def traffic_file(workload: str):
+    """The committed traffic counters of this workload's head, or None."""
+    from dynamic_vocabulary_draft_amd import synthetic as syn
+    for i, name in TRAFFIC_FILES.items():
+        if syn.CONFIGS[i].name == workload:
+            return os.path.join(ROOT, "profiles", name)
+    return None
+
+
 def pmc_probe(args, cfg, steps, sizes, npos, stream, torch, np):
     """Eager steps over every (instance, position), then a plain copy of
     COPY_BYTES; writes the algorithmic bytes of each head launch, in launch
@@ -153,7 +168,7 @@ def pmc_probe(args, cfg, steps, sizes, npos, stream, torch, np):
     with open(args.probe_file, "w") as f:
         json.dump({"workload": cfg.name, "head_kernel": head_kernel_name(cfg),
                    "launch_bytes": launch_bytes, "copy_bytes": COPY_BYTES,
-                   "kernel_source_sha256": head_source_sha()}, f)
+                   "kernel_source_sha256": head_source_sha(head_kernel_name(cfg))}, f)
     log("pmc probe: %d head launches, copy of %d bytes" % (len(launch_bytes), COPY_BYTES))
 
 
@@ -206,7 +221,10 @@ def traffic_from(args):
         "copy_write_kib": per["WRITE_SIZE"]["copy_kib"],
     })
     out["traffic_over_algorithmic"] = round(out["bytes_per_launch"] / alg, 4)
-    with open(args.traffic_out or TRAFFIC_FILE, "w") as f:
+    dest = args.traffic_out or traffic_file(probe["workload"])
+    if dest is None:
+        raise SystemExit("no committed traffic file for %s: give --traffic-out" % probe["workload"])
+    with open(dest, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
@@ -541,8 +559,8 @@ def main():
                     help="turn two rocprofv3 --pmc outputs of --pmc-probe into "
                          "profiles/head_gemv_traffic.json and exit")
     ap.add_argument("--traffic-out", default=None,
-                    help="where --traffic-from writes (default: the file the default bench "
-                         "line reads its traffic from; give another path for other workloads)")
+                    help="where --traffic-from writes (default: the file the bench line "
+                         "reads the probed workload's traffic from)")
     ap.add_argument("--stats-from", metavar="STATS_CSV_OR_DB",
                     help="print kernel statistics (a rocprofv3 --stats kernel_stats.csv, or a "
                          "--kernel-trace results database) as a markdown table, and exit")
@@ -786,11 +804,12 @@ def run_draft(index, *, n_steps, warmup, instances, replicas, eager, static=None
     mean_ms = float(np.mean(durs))
     achieved = float(np.sum(nbytes)) / (float(np.sum(durs)) * 1e-3) / 1e9
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    tfile = traffic_file(cfg.name)
+    if tfile is not None and os.path.exists(tfile):
+        with open(tfile) as f:
             tr = json.load(f)
-        if tr.get("kernel_source_sha256") == head_source_sha() and \
-                tr.get("workload") == cfg.name:
+        if tr.get("kernel_source_sha256") == head_source_sha(head_kernel_name(cfg)) and \
+                tr.get("workload") == cfg.name and tr.get("head_kernel") == head_kernel_name(cfg):
             traffic = tr.get("bytes_per_launch")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
