@@ -63,16 +63,21 @@ __device__ float row_max(const float *__restrict__ cmax, int nch, float *sh)
 }
 
 // chunk max m_c, first index of it, and the chunk sum of exp((l - m_c)/T);
-// a workgroup handles R consecutive chunks of a row, all loads issued first
+// a workgroup handles R consecutive chunks of a row: all loads issued first,
+// then each step done for the R chunks side by side, so the workgroup waits
+// at two barriers in all rather than three per chunk.  Per chunk the
+// reductions are those of block_chunk_max and wave_chunk_sum (the same
+// values and summation order as one chunk at a time).
 template <class L, int R>
 __global__ __launch_bounds__(kChunkThreads) void norm_stats_kernel(L layout,
                                                                    const float *__restrict__ in,
                                                                    double tau, int64_t nchmax,
                                                                    void *ws, int64_t rows)
 {
-    __shared__ float s_max[4];
-    __shared__ int s_idx[4];
-    __shared__ double s_wt[4];
+    constexpr int NW = kChunkThreads / kWave;
+    __shared__ float s_max[R][NW];
+    __shared__ int s_idx[R][NW];
+    __shared__ double s_wt[R][NW];
     __shared__ double s_exp2[64];
     const int64_t row = blockIdx.y, c0 = (int64_t)blockIdx.x * R;
     int64_t off, len, ids_off;
@@ -80,38 +85,73 @@ __global__ __launch_bounds__(kChunkThreads) void norm_stats_kernel(L layout,
     if (c0 * kChunk >= len)
         return;
     ChunkWs w = chunk_ws(ws, rows, nchmax);
-    const int64_t jl = (threadIdx.x >> 6) * 256 + lane_id() * 4;  // lane's offset in a chunk
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int64_t jl = wave * 256 + lane * 4;  // lane's offset in a chunk
     float v[R][4];
 #pragma unroll
     for (int r = 0; r < R; ++r)
         load4(in + off, (c0 + r) * kChunk + jl, len, v[r]);
-    fill_exp2_table(s_exp2);  // ordered before its use by the barrier in the loop
+    fill_exp2_table(s_exp2);  // ordered before its use by the first barrier
+    // chunks c0 .. c0+nr-1 hold entries (block-uniform)
+    const int nr = (int)min((int64_t)R, min(nchmax, (len + kChunk - 1) / kChunk) - c0);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int64_t c = c0 + r;
-        if (c * kChunk >= len || c >= nchmax)
+        if (r >= nr)
             break;
-        const int64_t j0 = c * kChunk + jl;
-        __syncthreads();  // the previous chunk's use of the shared scratch is over
-        block_chunk_max(v[r], j0, s_max, s_idx, &w.cmax[row * nchmax + c],
-                        &w.cidx[row * nchmax + c]);
-        if (tau == 0.0)
-            continue;
-        float mc = s_max[0];  // block_chunk_max ends after a barrier
-        for (int i = 1; i < 4; ++i)
-            mc = fmaxf(mc, s_max[i]);
+        float m = v[r][0];
+        int idx = 0;
+#pragma unroll
+        for (int k = 1; k < 4; ++k)
+            if (v[r][k] > m) {
+                m = v[r][k];
+                idx = k;
+            }
+        const float wm = wave_max(m);
+        const uint64_t bal = __ballot(m == wm);
+        const int first = __shfl((int)((c0 + r) * kChunk + jl + idx),
+                                 __ffsll((unsigned long long)bal) - 1);
+        if (lane == 0) {
+            s_max[r][wave] = wm;
+            s_idx[r][wave] = first;
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < nr) {  // thread r: chunk c0 + r, the first wave's index on ties
+        const int r = (int)threadIdx.x;
+        float bm = s_max[r][0];
+        int bi = s_idx[r][0];
+        for (int q = 1; q < NW; ++q)
+            if (s_max[r][q] > bm) {
+                bm = s_max[r][q];
+                bi = s_idx[r][q];
+            }
+        w.cmax[row * nchmax + c0 + r] = bm;
+        w.cidx[row * nchmax + c0 + r] = bi;
+    }
+    if (tau == 0.0)
+        return;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r >= nr)
+            break;
+        float mc = s_max[r][0];
+        for (int q = 1; q < NW; ++q)
+            mc = fmaxf(mc, s_max[r][q]);
+        const int64_t j0 = (c0 + r) * kChunk + jl;
         double wt[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             wt[k] = j0 + k < len ? exp_tab(over_tau((double)v[r][k] - (double)mc, tau), s_exp2)
                                  : 0.0;
         double incl;
-        double tot = wave_chunk_sum(wt, &incl);
-        if (lane_id() == 0)
-            s_wt[threadIdx.x >> 6] = tot;
-        __syncthreads();
-        if (threadIdx.x == 0)
-            w.csum[row * nchmax + c] = ((s_wt[0] + s_wt[1]) + s_wt[2]) + s_wt[3];
+        const double tot = wave_chunk_sum(wt, &incl);
+        if (lane == 0)
+            s_wt[r][wave] = tot;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < nr) {
+        const int r = (int)threadIdx.x;
+        w.csum[row * nchmax + c0 + r] = ((s_wt[r][0] + s_wt[r][1]) + s_wt[r][2]) + s_wt[r][3];
     }
 }
 
